@@ -1,0 +1,205 @@
+"""Unpacked evaluation of verify rows and the head's row statistics
+(test infrastructure only).
+
+What a verify row must equal (paper §3.2, Def. 1; App. B.1 proof; project page
+"Verify pass"): the row of a depth-d node y_{1:d} is the target's next-token
+distribution p(. | x o b o y_{1:d}); packing and ancestor-only masking change
+the layout of the pass, never a row's conditioning.  So the oracle evaluates
+every node on its own explicit token sequence b, y_1, .., y_d placed after the
+cached prefix x, causally, with no tree and no mask matrix.
+
+The pages do not define the target's layers.  The reading used here is an
+attention-only residual stack over the given shapes:
+  layer input   h = E[token] at the first layer (one embedding row per token)
+  per layer     q = h Wq^T, k = h Wk^T, v = h Wv^T, split into heads of size D
+                q and k rotated by rotate-half RoPE at absolute position
+                P + (index in the sequence), from the given cos/sin tables
+                query head g reads KV head floor(g / (Hq / Hkv))
+                a = softmax(q k^T / sqrt(D)) v over [prefix keys, own keys <= pos]
+                h' = h + concat_g(a_g) Wo^T
+  logits        z = h_last W_head^T
+Storage points of bf16 runs (values that a real engine keeps in bf16): the
+K/V entry of every sequence position and each layer's output h'.  The oracle
+rounds there and computes in float64 everywhere else.
+
+Row statistics (paper §3.1 greedy argmax; App. B.1 top-2 gap; §6 and the
+project page's entropy law: next-token entropy H at the round root, in nats):
+argmax (lowest token id on exact ties), top-1 logit, gap = top-1 minus the best
+logit of any other token, and H = -sum_v p(v) ln p(v) with p = softmax(z).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .numerics import decode, store
+
+
+def rope(x: np.ndarray, pos: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """Rotate-half rotary embedding of x [..., n, H, D] at positions pos [n]:
+    for i < D/2, (x_i, x_{i+D/2}) -> (x_i c - x_{i+D/2} s, x_{i+D/2} c + x_i s)
+    with c, s = cos/sin tables at (pos, i)."""
+    half = x.shape[-1] // 2
+    c = cos[pos][:, None, :]
+    s = sin[pos][:, None, :]
+    x1 = x[..., :half]
+    x2 = x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+class TargetModel:
+    """Float64 view of the synthetic target's tensors, decoded on demand."""
+
+    def __init__(self, inp: dict, cache_head: bool = False):
+        cfg = inp["cfg"]
+        self.cfg = cfg
+        self.dtype = cfg.dtype
+        self.V, self.d = cfg.V, cfg.d_model
+        self.Hq, self.Hkv, self.D = cfg.Hq, cfg.Hkv, cfg.D
+        self.n_layers = cfg.n_layers
+        self._inp = inp
+        self.kv_offsets = np.asarray(inp["kv_offsets"], dtype=np.int64)
+        self.prefix_len = np.asarray(inp["prefix_len"], dtype=np.int64)
+        self.cos = np.asarray(inp["rope_cos"], dtype=np.float64)
+        self.sin = np.asarray(inp["rope_sin"], dtype=np.float64)
+        self._head64 = decode(inp["w_head"], self.dtype) if cache_head else None
+        self._layer_cache: dict = {}
+
+    # ---------------------------------------------------------------- tensors
+    def embed_rows(self, tokens) -> np.ndarray:
+        return decode(self._inp["embed"][np.asarray(tokens, dtype=np.int64)], self.dtype)
+
+    def layer(self, li: int) -> dict:
+        if li not in self._layer_cache:
+            lw = self._inp["layers"][li]
+            self._layer_cache = {li: {k: decode(lw[k], self.dtype)
+                                      for k in ("wq", "wk", "wv", "wo")}}
+        return self._layer_cache[li]
+
+    def prefix_kv(self, li: int, s: int):
+        lw = self._inp["layers"][li]
+        a, b = int(self.kv_offsets[s]), int(self.kv_offsets[s + 1])
+        return decode(lw["k_cache"][a:b], self.dtype), decode(lw["v_cache"][a:b], self.dtype)
+
+    def logits(self, h: np.ndarray, chunk: int = 8192) -> np.ndarray:
+        """z = h W_head^T in float64, over vocabulary chunks."""
+        h = np.atleast_2d(np.asarray(h, dtype=np.float64))
+        z = np.empty((h.shape[0], self.V), dtype=np.float64)
+        for a in range(0, self.V, chunk):
+            b = min(a + chunk, self.V)
+            w = self._head64[a:b] if self._head64 is not None else \
+                decode(self._inp["w_head"][a:b], self.dtype)
+            z[:, a:b] = h @ w.T
+        return z
+
+    # ------------------------------------------------------------- one layer
+    def project(self, li: int, h: np.ndarray, pos: np.ndarray):
+        """q (rotated), k (rotated, stored), v (stored) of rows h at positions pos."""
+        w = self.layer(li)
+        n = h.shape[0]
+        q = (h @ w["wq"].T).reshape(n, self.Hq, self.D)
+        k = (h @ w["wk"].T).reshape(n, self.Hkv, self.D)
+        v = (h @ w["wv"].T).reshape(n, self.Hkv, self.D)
+        q = rope(q, pos, self.cos, self.sin)
+        k = store(rope(k, pos, self.cos, self.sin), self.dtype)
+        v = store(v, self.dtype)
+        return q, k, v
+
+    def attend(self, q: np.ndarray, keys: np.ndarray, vals: np.ndarray) -> np.ndarray:
+        """Softmax attention of one position's query heads q [Hq][D] over an
+        explicit key/value sequence [T][Hkv][D]; returns [Hq][D]."""
+        G = self.Hq // self.Hkv
+        out = np.empty((self.Hq, self.D))
+        for g in range(self.Hq):
+            kv = g // G
+            sc = keys[:, kv, :] @ q[g] / np.sqrt(self.D)
+            p = np.exp(sc - sc.max())
+            p /= p.sum()
+            out[g] = p @ vals[:, kv, :]
+        return out
+
+    def residual(self, li: int, h: np.ndarray, a: np.ndarray) -> np.ndarray:
+        w = self.layer(li)
+        return store(h + a.reshape(a.shape[0], -1) @ w["wo"].T, self.dtype)
+
+
+def evaluate_paths(model: TargetModel, s: int, root: int, paths: list) -> dict:
+    """Evaluate every node of a prefix-closed set of token paths (the root is the
+    empty path ()) on its own explicit sequence after sequence s's prefix.
+
+    Layer by layer, every node's query attends to the prefix keys followed by the
+    keys of its own path (root, y_1, .., y_d), i.e. exactly the causal sequence
+    x o b o y_{1:d}; no other node is visible.  Returns per-layer attention
+    outputs ``attn[l]`` [n][Hq*D], per-layer outputs ``h[l]`` [n][d] and the
+    final hidden rows ``final`` [n][d], all float64, in the order of ``paths``."""
+    index = {p: i for i, p in enumerate(paths)}
+    if () not in index:
+        raise ValueError("paths must contain the root ()")
+    n = len(paths)
+    tokens = [root if p == () else p[-1] for p in paths]
+    P = int(model.prefix_len[s])
+    pos = np.array([P + len(p) for p in paths], dtype=np.int64)
+    chains = [[index[p[:j]] for j in range(len(p) + 1)] for p in paths]
+    h = model.embed_rows(tokens)
+    attn_all, h_all = [], []
+    for li in range(model.n_layers):
+        q, k, v = model.project(li, h, pos)
+        Kp, Vp = model.prefix_kv(li, s)
+        a = np.empty((n, model.Hq, model.D))
+        for i in range(n):
+            keys = np.concatenate([Kp, k[chains[i]]], axis=0)
+            vals = np.concatenate([Vp, v[chains[i]]], axis=0)
+            a[i] = model.attend(q[i], keys, vals)
+        attn_all.append(a.reshape(n, -1))
+        h = model.residual(li, h, a)
+        h_all.append(h)
+    return {"attn": attn_all, "h": h_all, "final": h}
+
+
+class Decoder:
+    """Plain autoregressive decoding of one sequence after its cached prefix:
+    each ``extend(token)`` appends one position, evaluates it through every layer
+    against the prefix and the sequence's own earlier positions, and returns the
+    position's logits."""
+
+    def __init__(self, model: TargetModel, s: int):
+        self.m = model
+        self.s = s
+        self.P = int(model.prefix_len[s])
+        self.keys = [[] for _ in range(model.n_layers)]
+        self.vals = [[] for _ in range(model.n_layers)]
+        self.kv = [model.prefix_kv(li, s) for li in range(model.n_layers)]
+        self.final = None
+
+    def extend(self, token: int) -> np.ndarray:
+        m = self.m
+        pos = np.array([self.P + len(self.keys[0])], dtype=np.int64)
+        h = m.embed_rows([token])
+        for li in range(m.n_layers):
+            q, k, v = m.project(li, h, pos)
+            self.keys[li].append(k[0])
+            self.vals[li].append(v[0])
+            Kp, Vp = self.kv[li]
+            keys = np.concatenate([Kp, np.stack(self.keys[li])], axis=0)
+            vals = np.concatenate([Vp, np.stack(self.vals[li])], axis=0)
+            a = m.attend(q[0], keys, vals)[None]
+            h = m.residual(li, h, a)
+        self.final = h[0]
+        return m.logits(h)[0]
+
+
+def row_stats(z: np.ndarray):
+    """argmax (lowest id on exact ties), top-1 logit, top-2 gap and entropy (nats)
+    of every row of logits z [n][V]."""
+    z = np.atleast_2d(np.asarray(z, dtype=np.float64))
+    am = np.argmax(z, axis=1)
+    rows = np.arange(z.shape[0])
+    top1 = z[rows, am]
+    other = z.copy()
+    other[rows, am] = -np.inf
+    second = other.max(axis=1)
+    gap = top1 - second
+    lse = top1 + np.log(np.exp(z - top1[:, None]).sum(axis=1))
+    lp = z - lse[:, None]
+    p = np.exp(lp)
+    H = -np.where(p > 0, p * lp, 0.0).sum(axis=1)
+    return am.astype(np.int64), top1, gap, H
