@@ -1,0 +1,212 @@
+/*
+ * glance.h -- C ABI of the per-round verify path of one-pass block drafting with
+ * tree-verified acceptance, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources.  "The paper" is "Vision Is Not Overhead: One-Pass Block Drafting for
+ * Lossless Speculative Decoding in Vision-Language Models" (arXiv 2609.00355);
+ * "the project page" is the GLANCE project page.  A round starts from a cached
+ * prefix x and a pending root token b (paper §3.1).  The draft head gives one
+ * marginal q_j over the vocabulary at every offset j = 1..L (paper §3.2,
+ * Assumption 1); the N prefixes of highest plug-in score prod_j q_j(y_j) form a
+ * prefix-closed tree S (paper §3.2 Def. 1, §4.2; project page "Verify pass");
+ * one ancestor-masked target pass gives every node's row p(. | x o b o y_{1:d});
+ * the walk commits the target's greedy tokens Y_{1:A(S)} and emits the next
+ * greedy token as the new root (paper Def. 1; App. B.1 proof of Theorem 1).
+ *
+ * Conventions shared by every call.
+ *   - Every pointer argument is a DEVICE pointer unless marked (host).
+ *   - Every call is asynchronous in stream order on `stream` (a hipStream_t;
+ *     NULL means the default stream).  No call synchronises the host.
+ *   - The caller owns every buffer.  The library allocates nothing and keeps no
+ *     state between calls; scratch memory is the caller's workspace `ws` of at
+ *     least the size the matching *_ws() function returns, aligned to 256 bytes.
+ *     Calls that share a workspace must not overlap in time.
+ *   - Arguments are checked on the host before anything is enqueued.  On error
+ *     nothing is launched and a negative glance_status is returned;
+ *     glance_last_error() then describes it (per thread).
+ *   - Device buffers must be 16-byte aligned.
+ *   - dtype GLANCE_F32: every floating tensor is float32.  GLANCE_BF16: stored
+ *     tensors (draft logits, embeddings, weights, caches, hidden rows) are
+ *     bfloat16; products accumulate in float32; softmax, logits and statistics
+ *     are float32.
+ *   - Verify rows of a round: row 0 is the root b, rows 1..|S| the tree nodes in
+ *     breadth-first order (depth, then parent row, then token id), rows past
+ *     n_valid are padding.  A batch of nseq rounds stores its rows back to back,
+ *     n_rows = N + 1 per round (row r of round s is global row s*n_rows + r).
+ */
+#ifndef GLANCE_H
+#define GLANCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GLANCE_F32 = 0, GLANCE_BF16 = 1 } glance_dtype;
+
+typedef enum {
+  GLANCE_OK = 0,
+  GLANCE_ERR_INVALID_ARG = -1, /* a size, count or pointer is out of range     */
+  GLANCE_ERR_ALIGNMENT = -2,   /* a device pointer is not 16-byte aligned       */
+  GLANCE_ERR_WORKSPACE = -3,   /* ws is NULL, too small or not 256-byte aligned */
+  GLANCE_ERR_UNSUPPORTED = -4, /* a shape this build does not implement         */
+  GLANCE_ERR_HIP = -5          /* a HIP launch failed                           */
+} glance_status;
+
+#define GLANCE_MAX_L 16     /* offsets per block (the paper uses B = 16, L = 15) */
+#define GLANCE_MAX_ROWS 64  /* N + 1 verify rows per round, one 64-bit mask word */
+
+/* ---------------------------------------------------------------- step 1 + 2 --
+ * glance_build_tree: log-softmax of every draft marginal, the best tokens of each
+ * offset, and the top-N prefix-closed tree with its verify-row layout.
+ *
+ * Defines (paper §3.2 Assumption 1 and Def. 1; §4.2; project page "Verify
+ * pass"): S = the N prefixes y_{1:d}, 1 <= d <= L, of highest plug-in score,
+ * ranked in the log domain by score(y_{1:d}) = sum_{j<=d} log q_j(y_j), with
+ * log q_j(v) = (z_jv - max_w z_jw) - ln sum_w exp(z_jw - max_w z_jw), all in
+ * float32, the score accumulated in depth order.  Equal scores: smaller depth
+ * first, then the parent selected earlier, then the token ranked earlier within
+ * its offset (larger logit, then smaller token id).  Prefixes whose score is
+ * -inf are never selected, so |S| < N is possible.
+ *
+ *   draft_logits [nseq][L][V]   dtype; the draft head's logits z_j
+ *   root_token   [nseq]         int32 in [0, V): b of each round (row 0)
+ *   N            tree budget, 0 <= N <= GLANCE_MAX_ROWS - 1 (the root is extra)
+ * Outputs ([nseq][N+1] each, row layout above; padding rows: parent -1, depth 0,
+ * token -1, anc 0, score -inf):
+ *   parent   int32   parent row (-1 for the root)
+ *   depth    int32   d of the node (0 for the root)
+ *   token    int32   last token y_d (b for the root)
+ *   anc      uint64  bit j set iff row j is the row itself or one of its
+ *                    ancestors (the root row is an ancestor of every row)
+ *   score    float   the node's log plug-in score (0 for the root)
+ *   n_valid  [nseq] int32: 1 + |S|
+ * Limits: 1 <= L <= GLANCE_MAX_L, 2 <= V <= 2^20, nseq >= 1.
+ */
+glance_status glance_build_tree(const void* draft_logits, int32_t dtype,
+                                const int32_t* root_token, int32_t nseq, int32_t L,
+                                int32_t V, int32_t N, int32_t* parent, int32_t* depth,
+                                int32_t* token, uint64_t* anc, float* score,
+                                int32_t* n_valid, void* ws, size_t ws_bytes,
+                                void* stream);
+
+size_t glance_build_tree_ws(int32_t nseq, int32_t L, int32_t V, int32_t N);
+
+/* -------------------------------------------------------------------- step 3 --
+ * glance_tree_attn: one target layer over every verify row of nseq rounds, as a
+ * single packed pass with ancestor-only masking.
+ *
+ * Defines (paper §3.2 Def. 1; App. B.1 proof: ancestor-only masking and token
+ * packing change the attention layout, not a row's conditioning): the output of
+ * row i equals that of the last position of the explicit causal sequence
+ * x o b o y_{1:d(i)}.  The layer, whose internals the pages do not give, is an
+ * attention-only residual block:
+ *   q = h Wq^T, k = h Wk^T, v = h Wv^T split in heads of D; q and k rotated by
+ *   rotate-half RoPE at position P_s + depth(i); query head g reads KV head
+ *   g / (Hq / Hkv); a = softmax(q k^T / sqrt(D)) v over the round's prefix keys
+ *   and the keys of the rows j with bit j of anc[i] set;
+ *   h_out = h_in + concat_g(a_g) Wo^T.
+ * bf16 runs round to bf16 at the storage points: each row's new K and V entries
+ * and h_out.
+ *
+ *   layer        weights and prefix cache of this layer (struct below)
+ *   embed        [V][d_model] dtype or NULL.  If not NULL the layer input of row
+ *                i is embed[token[i]] (first layer) and h_in is ignored.
+ *   token        [nseq*n_rows] int32 (tree output; -1 marks a padding row)
+ *   h_in         [nseq*n_rows][d_model] dtype, or NULL when embed is given
+ *   h_out        [nseq*n_rows][d_model] dtype; padding rows are written as 0
+ *   kv_offsets   [nseq+1] int64: round s's prefix is cache rows
+ *                [kv_offsets[s], kv_offsets[s+1]); P_s = the difference >= 0
+ *   max_prefix   (host) an upper bound of every P_s, used to size the launch
+ *   depth, anc   [nseq*n_rows] tree outputs
+ *   rope_cos/sin [n_pos][D/2] float32 cos/sin of the rotary angles; they must
+ *                cover every position P_s + depth (n_pos > max_prefix is checked;
+ *                positions past the table are clamped to its last row)
+ *   attn_out     [nseq*n_rows][Hq*D] float32 or NULL: concat_g(a_g) per row
+ *   tree_k/v     [nseq*n_rows][Hkv][D] dtype or NULL: the rows' new cache
+ *                entries (k after RoPE)
+ * Limits: Hq % Hkv == 0; 1 <= n_rows <= GLANCE_MAX_ROWS.  bf16: D == 128,
+ * d_model % 256 == 0, Hq*D % 256 == 0.  f32: D <= 128 even, max_prefix <= 8192.
+ */
+typedef struct {
+  const void* wq;      /* [Hq*D][d_model]  (out x in, row-major) */
+  const void* wk;      /* [Hkv*D][d_model]                        */
+  const void* wv;      /* [Hkv*D][d_model]                        */
+  const void* wo;      /* [d_model][Hq*D]                         */
+  const void* k_cache; /* [sum P][Hkv][D], keys already rotated   */
+  const void* v_cache; /* [sum P][Hkv][D]                         */
+} glance_attn_layer;
+
+glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype,
+                               const void* embed, const int32_t* token, const void* h_in,
+                               void* h_out, const int64_t* kv_offsets, int64_t max_prefix,
+                               const int32_t* depth, const uint64_t* anc,
+                               const float* rope_cos, const float* rope_sin, int32_t n_pos,
+                               int32_t nseq, int32_t n_rows, int32_t d_model, int32_t Hq,
+                               int32_t Hkv, int32_t D, float* attn_out, void* tree_k,
+                               void* tree_v, void* ws, size_t ws_bytes, void* stream);
+
+size_t glance_tree_attn_ws(int32_t nseq, int32_t n_rows, int64_t max_prefix,
+                           int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D);
+
+/* -------------------------------------------------------------------- step 4 --
+ * glance_verify_head: LM head of the verify rows with a fused row epilogue.
+ *
+ * Defines: z = h W_head^T (float32 accumulation).  Per row: the greedy token
+ * argmax_v z_v (paper §3.1; the smallest token id on exact ties), its logit top1,
+ * the top-2 gap top1 - max_{v != argmax} z_v (paper App. B.1, gamma_k; 0 on an
+ * exact tie), and the next-token entropy H = -sum_v p_v ln p_v of p =
+ * softmax(z), in nats (paper §6 and the project page's entropy law: H at the
+ * round root is row 0 of each round).
+ *
+ *   h        [R][d_model] dtype (final hidden rows)
+ *   w_head   [V][d_model] dtype (out x in)
+ *   argmax   [R] int32; top1, gap, entropy [R] float
+ *   logits   [R][V] float32 or NULL
+ * Limits: R >= 1, V >= 2.  bf16: d_model % 256 == 0.
+ */
+glance_status glance_verify_head(const void* h, const void* w_head, int32_t dtype,
+                                 int32_t R, int32_t d_model, int32_t V, int32_t* argmax,
+                                 float* top1, float* gap, float* entropy, float* logits,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+size_t glance_verify_head_ws(int32_t R, int32_t V, int32_t d_model, int32_t dtype);
+
+/* -------------------------------------------------------------------- step 5 --
+ * glance_accept_walk: the greedy accept walk of every round.
+ *
+ * Defines (paper §3.2 Def. 1; App. B.1 proof): from the root row r = 0, with
+ * y = argmax[r]: if a row c < n_valid has parent r and token y, commit y and
+ * descend to c; otherwise emit y as the new root and stop.  This yields
+ * A(S) = max{k : Y_{1:j} in S for all j <= k}, the committed Y_{1:A(S)} and the
+ * new root Y_{A(S)+1}; a round commits A(S) + 1 tokens (paper §3.1, Eq. (1)).
+ * Sibling tokens are distinct, so at most one child matches.
+ *
+ *   parent, token [nseq*n_rows], n_valid [nseq]: tree outputs
+ *   argmax, gap   [nseq*n_rows]: verify-head outputs
+ *   gap_flag      a round is flagged when a visited row has gap <= gap_flag
+ *                 (near-ties, where packed and unpacked evaluation may pick
+ *                 different tokens; paper Theorem 1); <= 0 disables flagging
+ * Outputs: n_accept [nseq] = A(S); out_tokens [nseq][L+1] (entries 0..A-1 the
+ * committed tokens, entry A the new root, the rest -1); path_rows [nseq][L+1]
+ * (entry k = the row whose argmax gave out_tokens[k], the rest -1);
+ * flagged [nseq] (0/1).
+ * Limits: 1 <= L <= GLANCE_MAX_L, 1 <= n_rows <= GLANCE_MAX_ROWS.
+ */
+glance_status glance_accept_walk(const int32_t* parent, const int32_t* token,
+                                 const int32_t* n_valid, const int32_t* argmax,
+                                 const float* gap, int32_t nseq, int32_t n_rows, int32_t L,
+                                 float gap_flag, int32_t* n_accept, int32_t* out_tokens,
+                                 int32_t* path_rows, int32_t* flagged, void* stream);
+
+/* ------------------------------------------------------------------ helpers -- */
+const char* glance_status_string(int32_t status); /* static text (host)       */
+const char* glance_last_error(void);              /* this thread's last error */
+int32_t glance_abi_version(void);                 /* 1                        */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GLANCE_H */

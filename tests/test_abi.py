@@ -1,0 +1,133 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+entry point include/glance.h declares with the binding's signatures, and
+rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tree_verified_block_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "glance.h")
+
+OK_PTR = 0x100000  # 16-byte aligned stand-in; every call below fails validation first
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(glance_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from tree_verified_block_amd import build
+        build.build(verbose=False)
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert set(names) == set(_lib.SIGNATURES), (names, sorted(_lib.SIGNATURES))
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_helpers(lib):
+    assert lib.glance_abi_version() == 1
+    assert lib.glance_status_string(0) == b"ok"
+    assert b"workspace" in lib.glance_status_string(-3)
+    assert lib.glance_build_tree_ws(1, 15, 151936, 63) > 0
+    assert lib.glance_build_tree_ws(0, 15, 151936, 63) == 0
+    assert lib.glance_verify_head_ws(64, 151936, 4096, 1) >= 64 * 1187 * 5 * 4
+    assert lib.glance_tree_attn_ws(1, 64, 1024, 4096, 32, 8, 128) > 0
+
+
+def _tree(lib, **kw):
+    a = dict(logits=OK_PTR, dtype=1, root=OK_PTR, nseq=1, L=15, V=151936, N=63, out=OK_PTR,
+             ws=OK_PTR * 16, ws_bytes=1 << 40)
+    a.update(kw)
+    o = a["out"]
+    return lib.glance_build_tree(a["logits"], a["dtype"], a["root"], a["nseq"], a["L"], a["V"],
+                                 a["N"], o, o, o, o, o, o, a["ws"], a["ws_bytes"], None)
+
+
+def test_build_tree_rejects_bad_arguments(lib):
+    assert _tree(lib, nseq=0) == -1
+    assert _tree(lib, L=0) == -1
+    assert _tree(lib, L=17) == -1
+    assert _tree(lib, V=1) == -1
+    assert _tree(lib, N=64) == -1
+    assert _tree(lib, N=-1) == -1
+    assert _tree(lib, dtype=7) == -1
+    assert _tree(lib, logits=None) == -1
+    assert b"draft_logits" in lib.glance_last_error()
+    assert _tree(lib, logits=OK_PTR + 2) == -2
+    assert _tree(lib, out=OK_PTR + 4) == -2
+    assert _tree(lib, ws=None) == -3
+    assert _tree(lib, ws=OK_PTR + 16) == -3          # not 256-byte aligned
+    assert _tree(lib, ws_bytes=16) == -3
+    assert b"needed" in lib.glance_last_error()
+
+
+def _head(lib, **kw):
+    a = dict(h=OK_PTR, w=OK_PTR, dtype=1, R=64, d=4096, V=151936, out=OK_PTR, ws=OK_PTR * 16,
+             ws_bytes=1 << 40)
+    a.update(kw)
+    o = a["out"]
+    return lib.glance_verify_head(a["h"], a["w"], a["dtype"], a["R"], a["d"], a["V"], o, o, o, o,
+                                  None, a["ws"], a["ws_bytes"], None)
+
+
+def test_verify_head_rejects_bad_arguments(lib):
+    assert _head(lib, R=0) == -1
+    assert _head(lib, V=1) == -1
+    assert _head(lib, d=4000) == -4       # bf16 needs d_model % 256 == 0
+    assert _head(lib, w=OK_PTR + 8) == -2
+    assert _head(lib, ws_bytes=100) == -3
+
+
+def _attn(lib, **kw):
+    a = dict(dtype=1, embed=OK_PTR, h_in=None, nseq=1, n_rows=64, d=4096, Hq=32, Hkv=8, D=128,
+             max_prefix=1024, n_pos=2048, ws=OK_PTR * 16, ws_bytes=1 << 40, layer=OK_PTR)
+    a.update(kw)
+    lay = _lib.GlanceAttnLayer(*(a["layer"],) * 6)
+    p = OK_PTR
+    return lib.glance_tree_attn(ctypes.byref(lay), a["dtype"], a["embed"], p, a["h_in"], p, p,
+                                a["max_prefix"], p, p, p, p, a["n_pos"], a["nseq"], a["n_rows"],
+                                a["d"], a["Hq"], a["Hkv"], a["D"], None, None, None, a["ws"],
+                                a["ws_bytes"], None)
+
+
+def test_tree_attn_rejects_bad_arguments(lib):
+    assert _attn(lib, n_rows=65) == -1
+    assert _attn(lib, Hq=30) == -1            # not a multiple of Hkv
+    assert _attn(lib, D=64) == -4             # bf16 path is head_dim 128
+    assert _attn(lib, embed=None) == -1       # neither embed nor h_in
+    assert _attn(lib, n_pos=100) == -1
+    assert _attn(lib, layer=OK_PTR + 2) == -2
+    assert _attn(lib, dtype=0, max_prefix=9000, n_pos=10000) == -4
+    assert _attn(lib, ws_bytes=1000) == -3
+
+
+def test_accept_walk_rejects_bad_arguments(lib):
+    p = OK_PTR
+    assert lib.glance_accept_walk(p, p, p, p, p, 0, 64, 15, 1e-3, p, p, p, p, None) == -1
+    assert lib.glance_accept_walk(p, p, p, p, p, 1, 65, 15, 1e-3, p, p, p, p, None) == -1
+    assert lib.glance_accept_walk(p, p, p, p, p, 1, 64, 0, 1e-3, p, p, p, p, None) == -1
+    assert lib.glance_accept_walk(None, p, p, p, p, 1, 64, 15, 1e-3, p, p, p, p, None) == -1
+    assert lib.glance_accept_walk(p, p, p, p, p + 4, 1, 64, 15, 1e-3, p, p, p, p, None) == -2
+
+
+def test_binding_requires_built_library(tmp_path):
+    """The binding never falls back: a missing library raises."""
+    with pytest.raises(RuntimeError, match="missing"):
+        saved = _lib._lib
+        _lib._lib = None
+        try:
+            _lib.load(str(tmp_path / "nope.so"))
+        finally:
+            _lib._lib = saved

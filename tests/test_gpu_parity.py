@@ -1,0 +1,116 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on seeded
+synthetic rounds.  Every test needs an MI355X."""
+import numpy as np
+import pytest
+
+from oracle import model as mdl, round as orr, tree as tr
+from synth import gen_round, make_config
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(inp, r=0, logits=True):
+    from tree_verified_block_amd.round import DeviceRound
+    dev = DeviceRound(inp, keep_layers=True, want_logits=logits)
+    dev.set_round(r)
+    dev.run()
+    return dev.fetch()
+
+
+def _round_parity(inp, r, exact="beam", greedy=True):
+    cfg = inp["cfg"]
+    gpu = _run(inp, r)
+    model = inp.setdefault("_oracle_model", mdl.TargetModel(inp))
+    rd = inp["rounds"][r]
+    report = {}
+    for s in range(cfg.nseq):
+        root = int(rd["root"][s])
+        if "draft_logits" in rd:
+            ot = orr.build_tree(rd["draft_logits"][s], cfg.dtype, root, cfg.N, exact)
+            paths = parity.check_tree(gpu, s, ot, ot["logq"], cfg.N, cfg.L, report)
+        else:
+            paths = parity.gpu_paths(gpu["parent"][s], gpu["token"][s], gpu["n_valid"][s])
+        ev = mdl.evaluate_paths(model, s, root, paths)
+        z = model.logits(ev["final"])
+        am, gap = parity.check_rows(gpu, ev, z, s, cfg.N + 1, cfg.dtype, report)
+        g = orr.continuation(model, s, root, paths[1:], cfg.L) if greedy else None
+        parity.check_walk(gpu, s, paths, am, gap, cfg.L, report, g)
+    print(f"[parity] {cfg.name} seed={inp['seed']} round={r}: {report}", flush=True)
+    return gpu, report
+
+
+@pytest.mark.parametrize("seed", [1000, 1001, 1002])
+def test_tiny_round_brute_force(seed):
+    """Tiny fp32 round; the oracle's tree is the full enumeration."""
+    _round_parity(gen_round(make_config("tiny"), seed), 0, exact="brute")
+
+
+@pytest.mark.parametrize("seed", range(1000, 1006))
+def test_tiny_widehead_round(seed):
+    _round_parity(gen_round(make_config("tiny_widehead"), seed), 0)
+
+
+def test_tiny_empty_tree():
+    inp = gen_round(make_config("tiny_widehead", N=0), 1000)
+    gpu, _ = _round_parity(inp, 0)
+    assert gpu["n_valid"][0] == 1 and gpu["n_accept"][0] == 0
+    assert gpu["out_tokens"][0][0] == gpu["argmax"][0]
+
+
+@pytest.mark.parametrize("name,seed", [("mini_bf16", 1), ("mini_bf16", 2),
+                                       ("mini_bf16_ragged", 3), ("mini_bf16_ragged", 4)])
+def test_mini_bf16_round(name, seed):
+    _round_parity(gen_round(make_config(name), seed), 0)
+
+
+def test_mini_copy_regime_accepts_planted_run():
+    inp = gen_round(make_config("mini_bf16_copy"), 3)
+    for r, rd in enumerate(inp["rounds"]):
+        gpu, _ = _round_parity(inp, r)
+        assert int(gpu["n_accept"][0]) == rd["G"]
+        assert int(gpu["out_tokens"][0][rd["G"]]) == rd["break_token"]
+
+
+def test_mini_given_topology_multilayer():
+    """Random prefix-closed topology (no draft), three stacked layers."""
+    cfg = make_config("mini_bf16_ragged", draft="topology", n_layers=3, nseq=2, N=63, L=15)
+    _round_parity(gen_round(cfg, 9), 0)
+
+
+def test_determinism():
+    """Two launches give identical bits (also a race check of the LDS code)."""
+    from tree_verified_block_amd.round import DeviceRound
+    inp = gen_round(make_config("mini_bf16_ragged"), 5)
+    dev = DeviceRound(inp, keep_layers=True, want_logits=True)
+    dev.set_round(0)
+    dev.run()
+    a = dev.fetch()
+    dev.run()
+    b = dev.fetch()
+    for k in ("parent", "token", "anc", "score", "argmax", "top1", "gap", "entropy", "logits",
+              "n_accept", "out_tokens", "h_final"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_non_ancestor_rows_do_not_leak():
+    """Changing the token of a leaf changes no other row's output bits."""
+    from tree_verified_block_amd.round import DeviceRound
+    cfg = make_config("mini_bf16_ragged", draft="topology", nseq=1, N=40, L=7)
+    inp = gen_round(cfg, 11)
+    dev = DeviceRound(inp, keep_layers=True)
+    dev.set_round(0)
+    dev.run()
+    a = dev.fetch()
+    rd = inp["rounds"][0]
+    parent = rd["parent"][0]
+    leaf = max(i for i in range(1, cfg.N + 1) if i not in set(parent.tolist()))
+    tok = dev.tree["token"].clone()
+    tok[0, leaf] = (tok[0, leaf] + 1) % cfg.V
+    dev.tree["token"].copy_(tok)
+    dev.step_attn()
+    dev.step_head()
+    b = dev.fetch()
+    keep = [i for i in range(cfg.N + 1) if i != leaf]
+    assert np.array_equal(a["h_final"][keep], b["h_final"][keep])
+    assert not np.array_equal(a["h_final"][leaf], b["h_final"][leaf])

@@ -1,0 +1,103 @@
+"""Torch-tensor front end of the C ABI: the same four calls, argument
+marshalling only (device pointers, sizes, the current HIP stream).  Every step
+runs in libglance's HIP kernels; PyTorch only provides memory and streams."""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import GLANCE_BF16, GLANCE_F32, GlanceAttnLayer
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return GLANCE_F32
+    if t.dtype == torch.bfloat16:
+        return GLANCE_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ step 1 + 2
+def build_tree_ws_bytes(nseq: int, L: int, V: int, N: int) -> int:
+    return _lib.load().glance_build_tree_ws(nseq, L, V, N)
+
+
+def tree_outputs(nseq: int, N: int, device) -> dict:
+    R = N + 1
+    return {
+        "parent": torch.empty((nseq, R), dtype=torch.int32, device=device),
+        "depth": torch.empty((nseq, R), dtype=torch.int32, device=device),
+        "token": torch.empty((nseq, R), dtype=torch.int32, device=device),
+        "anc": torch.empty((nseq, R), dtype=torch.int64, device=device),
+        "score": torch.empty((nseq, R), dtype=torch.float32, device=device),
+        "n_valid": torch.empty((nseq,), dtype=torch.int32, device=device),
+    }
+
+
+def glance_build_tree(draft_logits, root_token, N, out, ws, stream=None):
+    nseq, L, V = draft_logits.shape
+    _lib.call("glance_build_tree", _ptr(draft_logits), dtype_code(draft_logits),
+              _ptr(root_token), nseq, L, V, N, _ptr(out["parent"]), _ptr(out["depth"]),
+              _ptr(out["token"]), _ptr(out["anc"]), _ptr(out["score"]), _ptr(out["n_valid"]),
+              _ptr(ws), ws.numel(), _stream(stream))
+    return out
+
+
+# ---------------------------------------------------------------------- step 3
+def tree_attn_ws_bytes(nseq, n_rows, max_prefix, d_model, Hq, Hkv, D) -> int:
+    return _lib.load().glance_tree_attn_ws(nseq, n_rows, max_prefix, d_model, Hq, Hkv, D)
+
+
+def glance_tree_attn(layer: dict, dtype: int, embed, token, h_in, h_out, kv_offsets,
+                     max_prefix: int, depth, anc, rope_cos, rope_sin, nseq: int, n_rows: int,
+                     d_model: int, Hq: int, Hkv: int, D: int, ws, attn_out=None, tree_k=None,
+                     tree_v=None, stream=None):
+    lay = GlanceAttnLayer(_ptr(layer["wq"]), _ptr(layer["wk"]), _ptr(layer["wv"]),
+                          _ptr(layer["wo"]), _ptr(layer["k_cache"]), _ptr(layer["v_cache"]))
+    _lib.call("glance_tree_attn", ctypes.byref(lay), dtype, _ptr(embed), _ptr(token),
+              _ptr(h_in), _ptr(h_out), _ptr(kv_offsets), int(max_prefix), _ptr(depth),
+              _ptr(anc), _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], nseq, n_rows,
+              d_model, Hq, Hkv, D, _ptr(attn_out), _ptr(tree_k), _ptr(tree_v), _ptr(ws),
+              ws.numel(), _stream(stream))
+
+
+# ---------------------------------------------------------------------- step 4
+def verify_head_ws_bytes(R, V, d_model, dtype) -> int:
+    return _lib.load().glance_verify_head_ws(R, V, d_model, dtype)
+
+
+def glance_verify_head(h, w_head, argmax, top1, gap, entropy, ws, logits=None, stream=None):
+    R, d_model = h.shape
+    V = w_head.shape[0]
+    _lib.call("glance_verify_head", _ptr(h), _ptr(w_head), dtype_code(w_head), R, d_model, V,
+              _ptr(argmax), _ptr(top1), _ptr(gap), _ptr(entropy), _ptr(logits), _ptr(ws),
+              ws.numel(), _stream(stream))
+
+
+# ---------------------------------------------------------------------- step 5
+def glance_accept_walk(parent, token, n_valid, argmax, gap, nseq, n_rows, L, gap_flag,
+                       n_accept, out_tokens, path_rows, flagged, stream=None):
+    _lib.call("glance_accept_walk", _ptr(parent), _ptr(token), _ptr(n_valid), _ptr(argmax),
+              _ptr(gap), nseq, n_rows, L, float(gap_flag), _ptr(n_accept), _ptr(out_tokens),
+              _ptr(path_rows), _ptr(flagged), _stream(stream))

@@ -1,0 +1,450 @@
+// Packed, ancestor-masked GQA attention of the verify rows (step 3).
+//
+// Paper §3.2 Def. 1 and App. B.1 (proof of Theorem 1): packing the tree into
+// one pass with ancestor-only masking changes the attention layout, not a row's
+// conditioning, so the row of node i attends to the cached prefix of its round
+// plus exactly the tree rows j that are i itself or its ancestors (bit j of
+// anc[i]), which is the causal sequence x o b o y_{1:d(i)}.
+//
+// bf16 path (head_dim 128, gfx950 MFMA v_mfma_f32_32x32x16_bf16).  Grid
+// (prefix splits + 1, Hkv x query blocks, rounds), 512 threads: the queries of
+// one KV head are its Hq/Hkv query heads times the round's rows (<= 256 per
+// work-group, 32 per wave).  Split c streams prefix keys [c*split, (c+1)*split)
+// in blocks of 64: K is staged in LDS as [key][dim], V transposed as [dim][key];
+// each wave forms S^T = K Q^T (one query per lane, so the row max and sum of the
+// online softmax stay inside a lane and its partner lane l^32), rounds P to bf16
+// into its own LDS tile and accumulates O^T += V^T P^T.  The extra split n_split
+// takes the round's tree rows as keys: their K (rotated) and V come from the
+// fp32 projection, rounded to bf16 (a storage point), masked by anc.  Each
+// (split, query) leaves (max, sum, unnormalised O); attn_combine merges them.
+//
+// fp32 path (tiny shapes): one work-group per (row, query head), scores in LDS,
+// plain fp32 loops.
+#include "common.h"
+#include "kernels.h"
+
+namespace glance {
+
+namespace {
+
+constexpr int kAThreads = 512;
+constexpr int kQWave = 32;
+constexpr int kQBlock = 256;
+constexpr int kKB = 64;
+constexpr int kHD = 128;         // head_dim of the bf16 path
+constexpr int kKPad = kHD + 8;   // Ks row stride (bf16)
+constexpr int kVPad = kKB + 8;   // Vt / Ps row stride (bf16)
+constexpr int kRec = kHD + 4;    // partial record: m, l, -, -, o[128]
+
+// position P + depth of a row, clamped into the cos/sin tables
+__device__ __forceinline__ int row_pos(const AttnArgs& a, int P, int row) {
+  const int p = P + a.depth[row];
+  return p < a.n_pos - 1 ? p : a.n_pos - 1;
+}
+
+__device__ __forceinline__ float rope_pair(const float* x, int i, int half, float c, float s) {
+  // rotate-half: (x_i, x_{i+half}) -> (x_i c - x_{i+half} s, x_{i+half} c + x_i s)
+  return i < half ? x[i] * c - x[i + half] * s : x[i] * c + x[i - half] * s;
+}
+
+__global__ __launch_bounds__(kAThreads) void tree_attn_bf16_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kKB][kKPad];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[kHD][kVPad];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[kAThreads / kWave][kQWave][kVPad];
+
+  const int c = blockIdx.x, s = blockIdx.z;
+  const int h = blockIdx.y % a.Hkv, qb = blockIdx.y / a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int Qn = a.n_rows * G;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 31, g = l >> 5;
+  const bool tree_split = (c == a.n_split);
+  const int64_t kv0 = a.kv_offsets[s];
+  const int P = static_cast<int>(a.kv_offsets[s + 1] - kv0);
+  const int nq_total = (a.Hq + 2 * a.Hkv) * kHD;
+
+  // ---- this lane's query: q index, row, head; rotated and rounded to bf16
+  const int q = qb * kQBlock + w * kQWave + j;
+  const bool qvalid = q < Qn;
+  const int r = qvalid ? q / G : 0;
+  const int qh = h * G + (qvalid ? q % G : 0);
+  const int grow = s * a.n_rows + r;
+  const bool qlive = qvalid && a.token[grow] >= 0;
+  const uint64_t qanc = qvalid ? a.anc[grow] : 0ull;
+  bf16x8 qf[8];
+  {
+    const int pos = row_pos(a, P, grow);
+    const float* xq = a.qkv + static_cast<size_t>(grow) * nq_total + qh * kHD;
+    const float* cs = a.rope_cos + static_cast<size_t>(pos) * (kHD / 2);
+    const float* sn = a.rope_sin + static_cast<size_t>(pos) * (kHD / 2);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      uint16_t e[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int i = ks * 16 + 8 * g + t;
+        const int ii = i & (kHD / 2 - 1);
+        e[t] = qlive ? f32_to_bf16(rope_pair(xq, i, kHD / 2, cs[ii], sn[ii])) : 0;
+      }
+      uint4 u;
+      u.x = e[0] | (static_cast<uint32_t>(e[1]) << 16);
+      u.y = e[2] | (static_cast<uint32_t>(e[3]) << 16);
+      u.z = e[4] | (static_cast<uint32_t>(e[5]) << 16);
+      u.w = e[6] | (static_cast<uint32_t>(e[7]) << 16);
+      qf[ks] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+
+  int kbeg, kend;
+  if (tree_split) {
+    kbeg = 0;
+    kend = a.n_rows;
+  } else {
+    kbeg = c * a.split;
+    kend = min(kbeg + a.split, P);
+  }
+  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(kHD));
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 acc_o[4] = {};
+
+  for (int k0 = kbeg; k0 < kend; k0 += kKB) {
+    // ---- stage K [key][dim] and V^T [dim][key] for keys k0 .. k0+63
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int kr = pass * 32 + (tid >> 4);
+      const int col = (tid & 15) * 8;
+      const int key = k0 + kr;
+      uint16_t kv[8], vv[8];
+      if (key < kend) {
+        if (!tree_split) {
+          const size_t off = (static_cast<size_t>(kv0 + key) * a.Hkv + h) * kHD + col;
+          const uint4 ku = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_cache) + off);
+          const uint4 vu = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v_cache) + off);
+          const uint32_t kw[4] = {ku.x, ku.y, ku.z, ku.w};
+          const uint32_t vw[4] = {vu.x, vu.y, vu.z, vu.w};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            kv[2 * t] = kw[t] & 0xFFFF;
+            kv[2 * t + 1] = kw[t] >> 16;
+            vv[2 * t] = vw[t] & 0xFFFF;
+            vv[2 * t + 1] = vw[t] >> 16;
+          }
+        } else {
+          const int trow = s * a.n_rows + key;
+          const int pos = row_pos(a, P, trow);
+          const float* xk = a.qkv + static_cast<size_t>(trow) * nq_total + a.Hq * kHD + h * kHD;
+          const float* xv = xk + a.Hkv * kHD;
+          const float* cs = a.rope_cos + static_cast<size_t>(pos) * (kHD / 2);
+          const float* sn = a.rope_sin + static_cast<size_t>(pos) * (kHD / 2);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int i = col + t;
+            const int ii = i & (kHD / 2 - 1);
+            kv[t] = f32_to_bf16(rope_pair(xk, i, kHD / 2, cs[ii], sn[ii]));
+            vv[t] = f32_to_bf16(xv[i]);
+          }
+          if (qb == 0) {
+            const size_t o = (static_cast<size_t>(trow) * a.Hkv + h) * kHD + col;
+            if (a.tree_k) {
+              uint16_t* tk = static_cast<uint16_t*>(a.tree_k) + o;
+#pragma unroll
+              for (int t = 0; t < 8; ++t) tk[t] = kv[t];
+            }
+            if (a.tree_v) {
+              uint16_t* tv = static_cast<uint16_t*>(a.tree_v) + o;
+#pragma unroll
+              for (int t = 0; t < 8; ++t) tv[t] = vv[t];
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) kv[t] = vv[t] = 0;
+      }
+      uint4 ku;
+      ku.x = kv[0] | (static_cast<uint32_t>(kv[1]) << 16);
+      ku.y = kv[2] | (static_cast<uint32_t>(kv[3]) << 16);
+      ku.z = kv[4] | (static_cast<uint32_t>(kv[5]) << 16);
+      ku.w = kv[6] | (static_cast<uint32_t>(kv[7]) << 16);
+      *reinterpret_cast<uint4*>(&Ks[kr][col]) = ku;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) Vt[col + t][kr] = vv[t];
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T for 64 keys x this wave's 32 queries
+    f32x16 acc_s[2] = {};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Ks[kb * 32 + j][ks * 16 + 8 * g]);
+        acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], acc_s[kb], 0, 0, 0);
+      }
+    }
+    // element v of acc_s[kb]: key k0 + 32 kb + 8 (v/4) + 4 g + v%4, query j
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = k0 + kb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+        bool vis = key < kend;
+        if (tree_split) vis = vis && ((qanc >> key) & 1ull);
+        const float sv = vis ? acc_s[kb][v] * scale_log2 : -INFINITY;
+        acc_s[kb][v] = sv;
+        mloc = fmaxf(mloc, sv);
+      }
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+    const float m_new = fmaxf(m_run, mloc);
+    float rowsum = 0.f;
+    uint16_t pb[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = (m_new == -INFINITY) ? 0.f : exp2f(acc_s[kb][v] - m_new);
+        pb[kb][v] = f32_to_bf16(p);
+        rowsum += bf16_to_f32(pb[kb][v]);
+      }
+    }
+    rowsum += __shfl_xor(rowsum, 32, kWave);
+    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+    l_run = l_run * alpha + rowsum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
+    // P (bf16) -> this wave's LDS tile, [query][key]
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        uint2 u;
+        u.x = pb[kb][4 * vg] | (static_cast<uint32_t>(pb[kb][4 * vg + 1]) << 16);
+        u.y = pb[kb][4 * vg + 2] | (static_cast<uint32_t>(pb[kb][4 * vg + 3]) << 16);
+        *reinterpret_cast<uint2*>(&Ps[w][j][kb * 32 + 8 * vg + 4 * g]) = u;
+      }
+    }
+    __syncthreads();
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Vt[db * 32 + j][ks * 16 + 8 * g]);
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&Ps[w][j][ks * 16 + 8 * g]);
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc_o[db], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- partial record of (split, query): m (log2 units), l, unnormalised O
+  if (qvalid) {
+    float* rec = a.part +
+                 ((static_cast<size_t>(s) * a.Hkv + h) * (a.n_split + 1) + c) * static_cast<size_t>(Qn) * kRec +
+                 static_cast<size_t>(q) * kRec;
+    if (g == 0) {
+      rec[0] = m_run;
+      rec[1] = l_run;
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        const int dim = db * 32 + 8 * vg + 4 * g;
+        *reinterpret_cast<float4*>(rec + 4 + dim) =
+            make_float4(acc_o[db][4 * vg], acc_o[db][4 * vg + 1], acc_o[db][4 * vg + 2], acc_o[db][4 * vg + 3]);
+      }
+  }
+}
+
+// Merge the split partials of every (row, query head) into the attention output.
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  const int grow = blockIdx.x;
+  const int s = grow / a.n_rows, r = grow % a.n_rows;
+  const int G = a.Hq / a.Hkv;
+  const int Qn = a.n_rows * G;
+  const bool live = a.token[grow] >= 0;
+  const int HD = a.Hq * kHD;
+  for (int e = threadIdx.x * 4; e < HD; e += 256 * 4) {
+    const int qh = e / kHD, dim = e % kHD;
+    const int h = qh / G, q = r * G + qh % G;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (live) {
+      const float* base = a.part + (static_cast<size_t>(s) * a.Hkv + h) * (a.n_split + 1) *
+                                       static_cast<size_t>(Qn) * kRec;
+      float M = -INFINITY;
+      for (int c = 0; c <= a.n_split; ++c) {
+        const float* rec = base + (static_cast<size_t>(c) * Qn + q) * kRec;
+        if (rec[1] > 0.f) M = fmaxf(M, rec[0]);
+      }
+      float Ls = 0.f;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int c = 0; c <= a.n_split; ++c) {
+        const float* rec = base + (static_cast<size_t>(c) * Qn + q) * kRec;
+        if (rec[1] > 0.f) {
+          const float f = exp2f(rec[0] - M);
+          Ls += rec[1] * f;
+          const float4 v = *reinterpret_cast<const float4*>(rec + 4 + dim);
+          acc.x += v.x * f;
+          acc.y += v.y * f;
+          acc.z += v.z * f;
+          acc.w += v.w * f;
+        }
+      }
+      const float inv = 1.f / Ls;
+      o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+    const size_t off = static_cast<size_t>(grow) * HD + e;
+    if (a.attn_out) *reinterpret_cast<float4*>(a.attn_out + off) = o;
+    uint2 u;
+    u.x = f32_to_bf16(o.x) | (static_cast<uint32_t>(f32_to_bf16(o.y)) << 16);
+    u.y = f32_to_bf16(o.z) | (static_cast<uint32_t>(f32_to_bf16(o.w)) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.attn_x) + off) = u;
+  }
+}
+
+// ------------------------------------------------------------------ fp32 path
+constexpr int kF32MaxKeys = 8192 + GLANCE_MAX_ROWS;
+
+__global__ __launch_bounds__(128) void tree_attn_f32_kernel(AttnArgs a) {
+  __shared__ float sc[kF32MaxKeys];
+  __shared__ float qs[kHD];
+  __shared__ float red[2];
+  const int grow = blockIdx.x, qh = blockIdx.y;
+  const int s = grow / a.n_rows;
+  const int G = a.Hq / a.Hkv, h = qh / G, D = a.D, half = D / 2;
+  const int nq_total = (a.Hq + 2 * a.Hkv) * D;
+  const int tid = threadIdx.x;
+  float* ox = static_cast<float*>(a.attn_x) + static_cast<size_t>(grow) * a.Hq * D + qh * D;
+  if (a.token[grow] < 0) {
+    for (int d = tid; d < D; d += 128) {
+      ox[d] = 0.f;
+      if (a.attn_out) a.attn_out[static_cast<size_t>(grow) * a.Hq * D + qh * D + d] = 0.f;
+    }
+    return;
+  }
+  const int64_t kv0 = a.kv_offsets[s];
+  const int P = static_cast<int>(a.kv_offsets[s + 1] - kv0);
+  const uint64_t anc = a.anc[grow];
+  {
+    const int pos = row_pos(a, P, grow);
+    const float* xq = a.qkv + static_cast<size_t>(grow) * nq_total + qh * D;
+    for (int i = tid; i < D; i += 128) {
+      const int ii = i % half;
+      qs[i] = rope_pair(xq, i, half, a.rope_cos[static_cast<size_t>(pos) * half + ii],
+                        a.rope_sin[static_cast<size_t>(pos) * half + ii]);
+    }
+  }
+  __syncthreads();
+  const int T = P + a.n_rows;
+  const float scale = 1.f / sqrtf(static_cast<float>(D));
+  float mx = -INFINITY;
+  for (int t = tid; t < T; t += 128) {
+    float dot = -INFINITY;
+    if (t < P) {
+      const float* k = static_cast<const float*>(a.k_cache) + (static_cast<size_t>(kv0 + t) * a.Hkv + h) * D;
+      float acc = 0.f;
+      for (int i = 0; i < D; ++i) acc = fmaf(qs[i], k[i], acc);
+      dot = acc * scale;
+    } else {
+      const int tr = t - P;
+      if ((anc >> tr) & 1ull) {
+        const int trow = s * a.n_rows + tr;
+        const int pos = row_pos(a, P, trow);
+        const float* xk = a.qkv + static_cast<size_t>(trow) * nq_total + a.Hq * D + h * D;
+        float acc = 0.f;
+        for (int i = 0; i < D; ++i) {
+          const int ii = i % half;
+          const float kr = rope_pair(xk, i, half, a.rope_cos[static_cast<size_t>(pos) * half + ii],
+                                     a.rope_sin[static_cast<size_t>(pos) * half + ii]);
+          acc = fmaf(qs[i], kr, acc);
+        }
+        dot = acc * scale;
+      }
+    }
+    sc[t] = dot;
+    mx = fmaxf(mx, dot);
+  }
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(red[0], red[1]);
+  __syncthreads();
+  float sum = 0.f;
+  for (int t = tid; t < T; t += 128) {
+    const float p = sc[t] == -INFINITY ? 0.f : expf(sc[t] - mx);
+    sc[t] = p;
+    sum += p;
+  }
+  sum = wave_sum(sum);
+  if ((tid & 63) == 0) red[tid >> 6] = sum;
+  __syncthreads();
+  sum = red[0] + red[1];
+  for (int d = tid; d < D; d += 128) {
+    float acc = 0.f;
+    for (int t = 0; t < T; ++t) {
+      const float p = sc[t];
+      if (p == 0.f) continue;
+      float v;
+      if (t < P)
+        v = static_cast<const float*>(a.v_cache)[(static_cast<size_t>(kv0 + t) * a.Hkv + h) * D + d];
+      else
+        v = a.qkv[static_cast<size_t>(s * a.n_rows + (t - P)) * nq_total + (a.Hq + a.Hkv) * D + h * D + d];
+      acc = fmaf(p, v, acc);
+    }
+    const float o = acc / sum;
+    ox[d] = o;
+    if (a.attn_out) a.attn_out[static_cast<size_t>(grow) * a.Hq * D + qh * D + d] = o;
+  }
+  // this row's own cache entries, written once per KV head
+  if (qh % G == 0) {
+    const int pos = row_pos(a, P, grow);
+    const float* xk = a.qkv + static_cast<size_t>(grow) * nq_total + a.Hq * D + h * D;
+    for (int i = tid; i < D; i += 128) {
+      const size_t o = (static_cast<size_t>(grow) * a.Hkv + h) * D + i;
+      const int ii = i % half;
+      if (a.tree_k)
+        static_cast<float*>(a.tree_k)[o] = rope_pair(xk, i, half, a.rope_cos[static_cast<size_t>(pos) * half + ii],
+                                                     a.rope_sin[static_cast<size_t>(pos) * half + ii]);
+      if (a.tree_v) static_cast<float*>(a.tree_v)[o] = xk[a.Hkv * D + i];
+    }
+  }
+}
+
+}  // namespace
+
+int attn_split_len(int64_t max_prefix, int nseq, int Hkv) {
+  (void)max_prefix;
+  (void)nseq;
+  (void)Hkv;
+  return 128;
+}
+
+size_t attn_part_floats(int nseq, int n_rows, int Hq, int Hkv, int D, int n_split) {
+  (void)D;
+  const size_t Qn = static_cast<size_t>(n_rows) * (Hq / Hkv);
+  return static_cast<size_t>(nseq) * Hkv * (n_split + 1) * Qn * kRec;
+}
+
+glance_status launch_tree_attention(const AttnArgs& a, hipStream_t st) {
+  if (a.dtype == GLANCE_BF16) {
+    const int Qn = a.n_rows * (a.Hq / a.Hkv);
+    const int nqb = (Qn + kQBlock - 1) / kQBlock;
+    dim3 grid(a.n_split + 1, a.Hkv * nqb, a.nseq);
+    tree_attn_bf16_kernel<<<grid, kAThreads, 0, st>>>(a);
+    GLANCE_LAUNCH_CHECK();
+    attn_combine_kernel<<<a.nseq * a.n_rows, 256, 0, st>>>(a);
+    GLANCE_LAUNCH_CHECK();
+  } else {
+    dim3 grid(a.nseq * a.n_rows, a.Hq);
+    tree_attn_f32_kernel<<<grid, 128, 0, st>>>(a);
+    GLANCE_LAUNCH_CHECK();
+  }
+  return GLANCE_OK;
+}
+
+}  // namespace glance

@@ -1,0 +1,361 @@
+// C ABI of libglance: argument validation, workspace layout and the launch
+// sequence of each step.  Every check runs on the host before anything is
+// enqueued; on error nothing is launched.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace glance {
+
+namespace {
+
+thread_local std::string g_last_error;
+
+glance_status fail(glance_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+#define REQUIRE(cond, ...)                                               \
+  do {                                                                   \
+    if (!(cond)) return fail(GLANCE_ERR_INVALID_ARG, __VA_ARGS__);       \
+  } while (0)
+#define REQUIRE_PTR(p)                                                   \
+  do {                                                                   \
+    if ((p) == nullptr) return fail(GLANCE_ERR_INVALID_ARG, "%s is NULL", #p); \
+    if (!aligned16(p)) return fail(GLANCE_ERR_ALIGNMENT, "%s is not 16-byte aligned", #p); \
+  } while (0)
+#define REQUIRE_ALIGNED_OR_NULL(p)                                       \
+  do {                                                                   \
+    if ((p) != nullptr && !aligned16(p))                                 \
+      return fail(GLANCE_ERR_ALIGNMENT, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+glance_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return GLANCE_OK;
+  if (ws == nullptr) return fail(GLANCE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(GLANCE_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(GLANCE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  return GLANCE_OK;
+}
+
+// ---------------------------------------------------------------- tree_attn ws
+struct AttnWs {
+  int n_split = 0, split = 0;
+  size_t off_qkv = 0, off_part = 0, off_x = 0, bytes = 0;
+};
+
+AttnWs attn_ws_layout(int dtype, int nseq, int n_rows, int64_t max_prefix, int d_model, int Hq,
+                      int Hkv, int D) {
+  (void)d_model;
+  AttnWs w;
+  const size_t R = static_cast<size_t>(nseq) * n_rows;
+  const size_t nqkv = static_cast<size_t>(Hq + 2 * Hkv) * D;
+  size_t off = 0;
+  w.off_qkv = off;
+  off += round256(R * nqkv * sizeof(float));
+  if (dtype == GLANCE_BF16) {
+    w.split = attn_split_len(max_prefix, nseq, Hkv);
+    w.n_split = static_cast<int>((max_prefix + w.split - 1) / w.split);
+    w.off_part = off;
+    off += round256(attn_part_floats(nseq, n_rows, Hq, Hkv, D, w.n_split) * sizeof(float));
+  }
+  w.off_x = off;
+  off += round256(R * Hq * D * (dtype == GLANCE_BF16 ? 2 : 4));
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace
+
+glance_status hip_fail(hipError_t e) {
+  g_last_error = std::string("HIP error: ") + hipGetErrorString(e);
+  return GLANCE_ERR_HIP;
+}
+
+}  // namespace glance
+
+using namespace glance;
+
+extern "C" {
+
+const char* glance_status_string(int32_t status) {
+  switch (status) {
+    case GLANCE_OK: return "ok";
+    case GLANCE_ERR_INVALID_ARG: return "invalid argument";
+    case GLANCE_ERR_ALIGNMENT: return "misaligned device pointer";
+    case GLANCE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case GLANCE_ERR_UNSUPPORTED: return "unsupported shape";
+    case GLANCE_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+const char* glance_last_error(void) { return g_last_error.c_str(); }
+
+int32_t glance_abi_version(void) { return 1; }
+
+// ------------------------------------------------------------------ step 1+2
+size_t glance_build_tree_ws(int32_t nseq, int32_t L, int32_t V, int32_t N) {
+  (void)N;
+  if (nseq < 1 || L < 1 || L > GLANCE_MAX_L || V < 2 || V > (1 << 20)) return 0;
+  return tree_ws_layout(nseq, L, V).bytes;
+}
+
+glance_status glance_build_tree(const void* draft_logits, int32_t dtype,
+                                const int32_t* root_token, int32_t nseq, int32_t L,
+                                int32_t V, int32_t N, int32_t* parent, int32_t* depth,
+                                int32_t* token, uint64_t* anc, float* score,
+                                int32_t* n_valid, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  REQUIRE(dtype == GLANCE_F32 || dtype == GLANCE_BF16, "dtype %d is not GLANCE_F32/BF16", dtype);
+  REQUIRE(nseq >= 1, "nseq = %d < 1", nseq);
+  REQUIRE(L >= 1 && L <= GLANCE_MAX_L, "L = %d outside [1, %d]", L, GLANCE_MAX_L);
+  REQUIRE(V >= 2 && V <= (1 << 20), "V = %d outside [2, 2^20]", V);
+  REQUIRE(N >= 0 && N <= GLANCE_MAX_ROWS - 1, "N = %d outside [0, %d]", N, GLANCE_MAX_ROWS - 1);
+  REQUIRE_PTR(draft_logits);
+  REQUIRE_PTR(root_token);
+  REQUIRE_PTR(parent);
+  REQUIRE_PTR(depth);
+  REQUIRE_PTR(token);
+  REQUIRE_PTR(anc);
+  REQUIRE_PTR(score);
+  REQUIRE_PTR(n_valid);
+  const TreeWs w = tree_ws_layout(nseq, L, V);
+  glance_status st = check_ws(ws, ws_bytes, w.bytes);
+  if (st != GLANCE_OK) return st;
+  return launch_build_tree(draft_logits, dtype, root_token, nseq, L, V, N, parent, depth, token,
+                           anc, score, n_valid, ws, static_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------------------------- step 3
+size_t glance_tree_attn_ws(int32_t nseq, int32_t n_rows, int64_t max_prefix, int32_t d_model,
+                           int32_t Hq, int32_t Hkv, int32_t D) {
+  if (nseq < 1 || n_rows < 1 || n_rows > GLANCE_MAX_ROWS || max_prefix < 0 || Hkv < 1 ||
+      Hq < Hkv || D < 2)
+    return 0;
+  // the larger of the two dtypes' layouts, so one size fits either
+  const AttnWs a = attn_ws_layout(GLANCE_BF16, nseq, n_rows, max_prefix, d_model, Hq, Hkv, D);
+  const AttnWs b = attn_ws_layout(GLANCE_F32, nseq, n_rows, max_prefix, d_model, Hq, Hkv, D);
+  return a.bytes > b.bytes ? a.bytes : b.bytes;
+}
+
+glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, const void* embed,
+                               const int32_t* token, const void* h_in, void* h_out,
+                               const int64_t* kv_offsets, int64_t max_prefix,
+                               const int32_t* depth, const uint64_t* anc,
+                               const float* rope_cos, const float* rope_sin, int32_t n_pos,
+                               int32_t nseq, int32_t n_rows, int32_t d_model, int32_t Hq,
+                               int32_t Hkv, int32_t D, float* attn_out, void* tree_k,
+                               void* tree_v, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  REQUIRE(layer != nullptr, "layer is NULL");
+  REQUIRE(dtype == GLANCE_F32 || dtype == GLANCE_BF16, "dtype %d is not GLANCE_F32/BF16", dtype);
+  REQUIRE(nseq >= 1, "nseq = %d < 1", nseq);
+  REQUIRE(n_rows >= 1 && n_rows <= GLANCE_MAX_ROWS, "n_rows = %d outside [1, %d]", n_rows,
+          GLANCE_MAX_ROWS);
+  REQUIRE(Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
+  REQUIRE(d_model >= 1, "d_model = %d < 1", d_model);
+  REQUIRE(max_prefix >= 0, "max_prefix < 0");
+  REQUIRE(embed != nullptr || h_in != nullptr, "both embed and h_in are NULL");
+  REQUIRE(n_pos > max_prefix, "n_pos = %d must exceed max_prefix", n_pos);
+  if (dtype == GLANCE_BF16) {
+    if (D != 128) return fail(GLANCE_ERR_UNSUPPORTED, "bf16 tree attention needs D = 128 (got %d)", D);
+    if (d_model % 256 != 0 || (Hq * D) % 256 != 0)
+      return fail(GLANCE_ERR_UNSUPPORTED, "bf16 needs d_model and Hq*D multiples of 256");
+  } else {
+    if (D < 2 || D > 128 || D % 2 != 0)
+      return fail(GLANCE_ERR_UNSUPPORTED, "fp32 tree attention needs even D <= 128 (got %d)", D);
+    if (max_prefix > 8192)
+      return fail(GLANCE_ERR_UNSUPPORTED, "fp32 tree attention needs max_prefix <= 8192");
+  }
+  REQUIRE_PTR(layer->wq);
+  REQUIRE_PTR(layer->wk);
+  REQUIRE_PTR(layer->wv);
+  REQUIRE_PTR(layer->wo);
+  REQUIRE_PTR(layer->k_cache);
+  REQUIRE_PTR(layer->v_cache);
+  REQUIRE_ALIGNED_OR_NULL(embed);
+  REQUIRE_ALIGNED_OR_NULL(h_in);
+  REQUIRE_PTR(token);
+  REQUIRE_PTR(h_out);
+  REQUIRE_PTR(kv_offsets);
+  REQUIRE_PTR(depth);
+  REQUIRE_PTR(anc);
+  REQUIRE_PTR(rope_cos);
+  REQUIRE_PTR(rope_sin);
+  REQUIRE_ALIGNED_OR_NULL(attn_out);
+  REQUIRE_ALIGNED_OR_NULL(tree_k);
+  REQUIRE_ALIGNED_OR_NULL(tree_v);
+  const AttnWs w = attn_ws_layout(dtype, nseq, n_rows, max_prefix, d_model, Hq, Hkv, D);
+  glance_status st = check_ws(ws, ws_bytes, w.bytes);
+  if (st != GLANCE_OK) return st;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  float* qkv = reinterpret_cast<float*>(base + w.off_qkv);
+  void* attn_x = base + w.off_x;
+  const int R = nseq * n_rows;
+  const int qd = Hq * D, kd = Hkv * D;
+
+  // 1. q, k, v of every row (layer input: embedding rows or h_in)
+  GemmArgs g{};
+  g.x = embed ? embed : h_in;
+  g.gather = embed ? token : nullptr;
+  g.w.w[0] = layer->wq;
+  g.w.w[1] = layer->wk;
+  g.w.w[2] = layer->wv;
+  g.w.n_end[0] = qd;
+  g.w.n_end[1] = qd + kd;
+  g.w.n_end[2] = qd + 2 * kd;
+  g.w.nseg = 3;
+  g.M = R;
+  g.N = qd + 2 * kd;
+  g.K = d_model;
+  g.epi = EPI_STORE_F32;
+  g.out_f32 = qkv;
+  st = dtype == GLANCE_BF16 ? launch_gemm_bf16(g, hs) : launch_gemm_f32(g, hs);
+  if (st != GLANCE_OK) return st;
+
+  // 2. attention over prefix + ancestors
+  AttnArgs a{};
+  a.dtype = dtype;
+  a.qkv = qkv;
+  a.k_cache = layer->k_cache;
+  a.v_cache = layer->v_cache;
+  a.kv_offsets = kv_offsets;
+  a.depth = depth;
+  a.anc = anc;
+  a.token = token;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.n_pos = n_pos;
+  a.nseq = nseq;
+  a.n_rows = n_rows;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.max_prefix = max_prefix;
+  a.split = w.split;
+  a.n_split = w.n_split;
+  a.part = reinterpret_cast<float*>(base + w.off_part);
+  a.attn_out = attn_out;
+  a.attn_x = attn_x;
+  a.tree_k = tree_k;
+  a.tree_v = tree_v;
+  st = launch_tree_attention(a, hs);
+  if (st != GLANCE_OK) return st;
+
+  // 3. h_out = h_in + attn Wo^T (padding rows -> 0)
+  GemmArgs o{};
+  o.x = attn_x;
+  o.gather = nullptr;
+  o.w.w[0] = layer->wo;
+  o.w.n_end[0] = d_model;
+  o.w.nseg = 1;
+  o.M = R;
+  o.N = d_model;
+  o.K = qd;
+  o.epi = EPI_RESID;
+  o.resid = embed ? embed : h_in;
+  o.resid_tok = token;
+  o.resid_by_token = embed != nullptr;
+  o.out_res = h_out;
+  return dtype == GLANCE_BF16 ? launch_gemm_bf16(o, hs) : launch_gemm_f32(o, hs);
+}
+
+// ------------------------------------------------------------------- step 4
+size_t glance_verify_head_ws(int32_t R, int32_t V, int32_t d_model, int32_t dtype) {
+  (void)d_model;
+  if (R < 1 || V < 2) return 0;
+  if (dtype == GLANCE_BF16)
+    return round256(static_cast<size_t>(R) * gemm_bf16_n_tiles(V) * 5 * sizeof(float));
+  return round256(static_cast<size_t>(R) * V * sizeof(float));
+}
+
+glance_status glance_verify_head(const void* h, const void* w_head, int32_t dtype, int32_t R,
+                                 int32_t d_model, int32_t V, int32_t* argmax, float* top1,
+                                 float* gap, float* entropy, float* logits, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  REQUIRE(dtype == GLANCE_F32 || dtype == GLANCE_BF16, "dtype %d is not GLANCE_F32/BF16", dtype);
+  REQUIRE(R >= 1, "R = %d < 1", R);
+  REQUIRE(V >= 2, "V = %d < 2", V);
+  REQUIRE(d_model >= 1, "d_model = %d < 1", d_model);
+  if (dtype == GLANCE_BF16 && d_model % 256 != 0)
+    return fail(GLANCE_ERR_UNSUPPORTED, "bf16 head needs d_model %% 256 == 0 (got %d)", d_model);
+  REQUIRE_PTR(h);
+  REQUIRE_PTR(w_head);
+  REQUIRE_PTR(argmax);
+  REQUIRE_PTR(top1);
+  REQUIRE_PTR(gap);
+  REQUIRE_PTR(entropy);
+  REQUIRE_ALIGNED_OR_NULL(logits);
+  const size_t need = glance_verify_head_ws(R, V, d_model, dtype);
+  glance_status st = check_ws(ws, ws_bytes, need);
+  if (st != GLANCE_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  GemmArgs g{};
+  g.x = h;
+  g.w.w[0] = w_head;
+  g.w.n_end[0] = V;
+  g.w.nseg = 1;
+  g.M = R;
+  g.N = V;
+  g.K = d_model;
+  g.epi = EPI_HEAD;
+  if (dtype == GLANCE_BF16) {
+    g.part = static_cast<float*>(ws);
+    g.logits = logits;
+    st = launch_gemm_bf16(g, hs);
+    if (st != GLANCE_OK) return st;
+    return launch_head_merge(g.part, gemm_bf16_n_tiles(V), R, argmax, top1, gap, entropy, hs);
+  }
+  g.logits = logits ? logits : static_cast<float*>(ws);
+  st = launch_gemm_f32(g, hs);
+  if (st != GLANCE_OK) return st;
+  return launch_head_rowstats_f32(g.logits, R, V, argmax, top1, gap, entropy, hs);
+}
+
+// ------------------------------------------------------------------- step 5
+glance_status glance_accept_walk(const int32_t* parent, const int32_t* token,
+                                 const int32_t* n_valid, const int32_t* argmax, const float* gap,
+                                 int32_t nseq, int32_t n_rows, int32_t L, float gap_flag,
+                                 int32_t* n_accept, int32_t* out_tokens, int32_t* path_rows,
+                                 int32_t* flagged, void* stream) {
+  g_last_error.clear();
+  REQUIRE(nseq >= 1, "nseq = %d < 1", nseq);
+  REQUIRE(n_rows >= 1 && n_rows <= GLANCE_MAX_ROWS, "n_rows = %d outside [1, %d]", n_rows,
+          GLANCE_MAX_ROWS);
+  REQUIRE(L >= 1 && L <= GLANCE_MAX_L, "L = %d outside [1, %d]", L, GLANCE_MAX_L);
+  REQUIRE_PTR(parent);
+  REQUIRE_PTR(token);
+  REQUIRE_PTR(n_valid);
+  REQUIRE_PTR(argmax);
+  REQUIRE_PTR(gap);
+  REQUIRE_PTR(n_accept);
+  REQUIRE_PTR(out_tokens);
+  REQUIRE_PTR(path_rows);
+  REQUIRE_PTR(flagged);
+  return launch_accept_walk(parent, token, n_valid, argmax, gap, nseq, n_rows, L, gap_flag,
+                            n_accept, out_tokens, path_rows, flagged,
+                            static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Internal launchers of libglance; the C ABI in glance.cpp validates every
+// argument before calling these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "glance.h"
+
+namespace glance {
+
+// ------------------------------------------------------------------ tree.hip
+struct TreeWs {
+  int chunk = 0, ipt = 0, nch = 0;
+  size_t off_cstat = 0, off_ccand = 0, off_logq = 0, off_id = 0, bytes = 0;
+};
+TreeWs tree_ws_layout(int nseq, int L, int V);
+glance_status launch_build_tree(const void* logits, int dtype, const int32_t* root, int nseq,
+                                int L, int V, int N, int32_t* parent, int32_t* depth,
+                                int32_t* token, uint64_t* anc, float* score,
+                                int32_t* n_valid, void* ws, hipStream_t st);
+
+// ------------------------------------------------------------------ gemm.hip
+// C = X W^T with X [M][K] (rows optionally gathered by token id) and W the
+// concatenation along N of up to three [n_i][K] row-major segments.
+struct GemmSeg {
+  const void* w[3];
+  int n_end[3];  // cumulative row counts
+  int nseg;
+};
+enum GemmEpi { EPI_STORE_F32 = 0, EPI_RESID = 1, EPI_HEAD = 2 };
+struct GemmArgs {
+  const void* x;          // [M][K]
+  const int32_t* gather;  // NULL or [M] token ids (row m of X = x[gather[m]], -1 = zero row)
+  GemmSeg w;
+  int M, N, K;
+  int epi;
+  float* out_f32;          // EPI_STORE_F32: [M][N]
+  const void* resid;       // EPI_RESID: residual rows, [M][N] or a table indexed by token
+  const int32_t* resid_tok;  // EPI_RESID: [M] token ids; rows with token < 0 are written as 0
+  bool resid_by_token;     // residual row m is resid[resid_tok[m]] (else resid[m])
+  void* out_res;           // EPI_RESID: [M][N] in the storage dtype
+  float* part;             // EPI_HEAD: [M][n_tiles] partial statistics (5 floats)
+  float* logits;           // EPI_HEAD: optional [M][N]
+};
+int gemm_bf16_n_tiles(int N);
+glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
+glance_status launch_gemm_f32(const GemmArgs& a, hipStream_t st);
+// Row statistics of the head from bf16 partials, or from full fp32 logits.
+glance_status launch_head_merge(const float* part, int n_tiles, int R, int32_t* argmax,
+                                float* top1, float* gap, float* entropy, hipStream_t st);
+glance_status launch_head_rowstats_f32(const float* logits, int R, int V, int32_t* argmax,
+                                       float* top1, float* gap, float* entropy,
+                                       hipStream_t st);
+
+// ------------------------------------------------------------------ attn.hip
+struct AttnArgs {
+  int dtype;
+  const float* qkv;        // [R][(Hq + 2 Hkv) D] fp32 projections (before RoPE)
+  const void* k_cache;     // [sum P][Hkv][D]
+  const void* v_cache;
+  const int64_t* kv_offsets;
+  const int32_t* depth;
+  const uint64_t* anc;
+  const int32_t* token;    // -1 marks padding rows
+  const float* rope_cos;
+  const float* rope_sin;
+  int n_pos;               // table rows; positions past the table are clamped to its end
+  int nseq, n_rows, Hq, Hkv, D;
+  int64_t max_prefix;
+  int split;               // prefix keys per split work-group
+  int n_split;             // prefix splits (the tree keys form split n_split)
+  float* part;             // partial (m, l, o[D]) per split and query
+  float* attn_out;         // NULL or [R][Hq D] fp32
+  void* attn_x;            // [R][Hq D] storage dtype: input of the output projection
+  void* tree_k;            // NULL or [R][Hkv][D]
+  void* tree_v;
+};
+int attn_split_len(int64_t max_prefix, int nseq, int Hkv);
+size_t attn_part_floats(int nseq, int n_rows, int Hq, int Hkv, int D, int n_split);
+glance_status launch_tree_attention(const AttnArgs& a, hipStream_t st);
+
+// ------------------------------------------------------------------ walk.hip
+glance_status launch_accept_walk(const int32_t* parent, const int32_t* token,
+                                 const int32_t* n_valid, const int32_t* argmax,
+                                 const float* gap, int nseq, int n_rows, int L, float gap_flag,
+                                 int32_t* n_accept, int32_t* out_tokens, int32_t* path_rows,
+                                 int32_t* flagged, hipStream_t st);
+
+}  // namespace glance

@@ -1,0 +1,66 @@
+// Step 5: the greedy accept walk (paper §3.2 Def. 1; App. B.1, proof of
+// Theorem 1).  From the root row, with y the row's greedy token: if the row has
+// a child carrying y, commit y and descend; otherwise emit y as the next root
+// and stop.  The walk visits at most L + 1 rows, so one wavefront per round
+// does it: lane c holds row c's parent and token, and a child lookup is one
+// ballot.
+#include "common.h"
+#include "kernels.h"
+
+namespace glance {
+
+namespace {
+
+__global__ __launch_bounds__(kWave) void accept_walk_kernel(
+    const int32_t* __restrict__ parent, const int32_t* __restrict__ token,
+    const int32_t* __restrict__ n_valid, const int32_t* __restrict__ argmax,
+    const float* __restrict__ gap, int n_rows, int L, float gap_flag,
+    int32_t* __restrict__ n_accept, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ path_rows, int32_t* __restrict__ flagged) {
+  const int s = blockIdx.x, lane = lane_id();
+  const size_t rb = static_cast<size_t>(s) * n_rows;
+  const int nv = n_valid[s];
+  const bool mine = lane < nv && lane < n_rows;
+  const int my_parent = mine ? parent[rb + lane] : -2;
+  const int my_token = mine ? token[rb + lane] : -2;
+  const int my_arg = mine ? argmax[rb + lane] : -1;
+  const float my_gap = mine ? gap[rb + lane] : INFINITY;
+  int r = 0, a = 0, flag = 0;
+  for (;;) {
+    const int y = __shfl(my_arg, r, kWave);
+    const float gp = __shfl(my_gap, r, kWave);
+    if (gap_flag > 0.f && gp <= gap_flag) flag = 1;
+    if (lane == 0) {
+      out_tokens[static_cast<size_t>(s) * (L + 1) + a] = y;
+      path_rows[static_cast<size_t>(s) * (L + 1) + a] = r;
+    }
+    const unsigned long long hit = __ballot(lane > 0 && my_parent == r && my_token == y);
+    if (hit == 0ull || a >= L) break;
+    r = __ffsll(static_cast<long long>(hit)) - 1;
+    ++a;
+  }
+  for (int k = a + 1 + lane; k <= L; k += kWave) {
+    out_tokens[static_cast<size_t>(s) * (L + 1) + k] = -1;
+    path_rows[static_cast<size_t>(s) * (L + 1) + k] = -1;
+  }
+  if (lane == 0) {
+    n_accept[s] = a;
+    flagged[s] = flag;
+  }
+}
+
+}  // namespace
+
+glance_status launch_accept_walk(const int32_t* parent, const int32_t* token,
+                                 const int32_t* n_valid, const int32_t* argmax,
+                                 const float* gap, int nseq, int n_rows, int L, float gap_flag,
+                                 int32_t* n_accept, int32_t* out_tokens, int32_t* path_rows,
+                                 int32_t* flagged, hipStream_t st) {
+  accept_walk_kernel<<<nseq, kWave, 0, st>>>(parent, token, n_valid, argmax, gap, n_rows, L,
+                                              gap_flag, n_accept, out_tokens, path_rows,
+                                              flagged);
+  GLANCE_LAUNCH_CHECK();
+  return GLANCE_OK;
+}
+
+}  // namespace glance

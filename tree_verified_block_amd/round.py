@@ -1,0 +1,141 @@
+"""One verify round on the device: the synthetic workload's tensors uploaded once
+into HBM, output and workspace buffers allocated once, and the four C-ABI calls
+launched in stream order (steps 1-2, one tree-attention call per layer, the LM
+head, the walk)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import api
+from ._lib import GLANCE_BF16, GLANCE_F32
+
+GAP_FLAG = 1e-3
+
+
+def to_device(x: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Stored synthetic tensor -> device tensor (bf16 bit patterns -> bfloat16)."""
+    if dtype == "bf16" and x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+
+
+class DeviceRound:
+    def __init__(self, inp: dict, device="cuda", keep_layers: bool = False,
+                 want_logits: bool = False):
+        cfg = inp["cfg"]
+        self.cfg = cfg
+        self.inp = inp
+        self.device = device
+        self.dt = GLANCE_BF16 if cfg.dtype == "bf16" else GLANCE_F32
+        dt = cfg.dtype
+        self.nseq, self.L, self.N, self.V = cfg.nseq, cfg.L, cfg.N, cfg.V
+        self.n_rows = cfg.N + 1
+        self.R = self.nseq * self.n_rows
+        d = cfg.d_model
+        self.embed = to_device(inp["embed"], dt, device)
+        self.w_head = to_device(inp["w_head"], dt, device)
+        self.layers = [{k: to_device(v, dt, device) for k, v in lw.items()} for lw in inp["layers"]]
+        self.kv_offsets = torch.from_numpy(inp["kv_offsets"].astype(np.int64)).to(device)
+        self.max_prefix = int(inp["prefix_len"].max())
+        self.rope_cos = torch.from_numpy(inp["rope_cos"]).to(device)
+        self.rope_sin = torch.from_numpy(inp["rope_sin"]).to(device)
+        self.tree = api.tree_outputs(self.nseq, self.N, device)
+        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        self.h = [torch.empty((self.R, d), dtype=tdt, device=device) for _ in range(2)]
+        self.keep_layers = keep_layers
+        HD = cfg.Hq * cfg.D
+        n_keep = cfg.n_layers if keep_layers else 0
+        self.attn_out = [torch.empty((self.R, HD), dtype=torch.float32, device=device)
+                         for _ in range(n_keep)]
+        self.h_layers = [torch.empty((self.R, d), dtype=tdt, device=device) for _ in range(n_keep)]
+        self.tree_k = torch.empty((self.R, cfg.Hkv, cfg.D), dtype=tdt, device=device)
+        self.tree_v = torch.empty((self.R, cfg.Hkv, cfg.D), dtype=tdt, device=device)
+        self.argmax = torch.empty(self.R, dtype=torch.int32, device=device)
+        self.top1 = torch.empty(self.R, dtype=torch.float32, device=device)
+        self.gap = torch.empty(self.R, dtype=torch.float32, device=device)
+        self.entropy = torch.empty(self.R, dtype=torch.float32, device=device)
+        self.logits = (torch.empty((self.R, self.V), dtype=torch.float32, device=device)
+                       if want_logits else None)
+        self.n_accept = torch.empty(self.nseq, dtype=torch.int32, device=device)
+        self.out_tokens = torch.empty((self.nseq, self.L + 1), dtype=torch.int32, device=device)
+        self.path_rows = torch.empty((self.nseq, self.L + 1), dtype=torch.int32, device=device)
+        self.flagged = torch.empty(self.nseq, dtype=torch.int32, device=device)
+        self.ws_tree = api.workspace(api.build_tree_ws_bytes(self.nseq, self.L, self.V, self.N), device)
+        self.ws_attn = api.workspace(api.tree_attn_ws_bytes(self.nseq, self.n_rows, self.max_prefix, d,
+                                                            cfg.Hq, cfg.Hkv, cfg.D), device)
+        self.ws_head = api.workspace(api.verify_head_ws_bytes(self.R, self.V, d, self.dt), device)
+        self.draft = None
+        self.root = None
+        self.given_tree = cfg.draft == "topology"
+
+    def set_round(self, r: int):
+        rd = self.inp["rounds"][r]
+        self.root = torch.from_numpy(rd["root"].astype(np.int32)).to(self.device)
+        if self.given_tree:
+            self.tree["parent"].copy_(torch.from_numpy(rd["parent"]))
+            self.tree["depth"].copy_(torch.from_numpy(rd["depth"]))
+            self.tree["token"].copy_(torch.from_numpy(rd["token"]))
+            self.tree["anc"].copy_(torch.from_numpy(rd["anc"].view(np.int64)))
+            self.tree["score"].zero_()
+            self.tree["n_valid"].fill_(self.n_rows)
+        else:
+            self.draft = to_device(rd["draft_logits"], self.cfg.dtype, self.device)
+
+    # -------------------------------------------------------------- the path
+    def step_tree(self, stream=None):
+        if not self.given_tree:
+            api.glance_build_tree(self.draft, self.root, self.N, self.tree, self.ws_tree, stream)
+
+    def step_attn(self, stream=None):
+        cfg = self.cfg
+        t = self.tree
+        for li, lw in enumerate(self.layers):
+            h_in = None if li == 0 else self.h[(li - 1) % 2]
+            h_out = self.h[li % 2]
+            api.glance_tree_attn(lw, self.dt, self.embed if li == 0 else None, t["token"], h_in,
+                                 h_out, self.kv_offsets, self.max_prefix, t["depth"], t["anc"],
+                                 self.rope_cos, self.rope_sin, self.nseq, self.n_rows,
+                                 cfg.d_model, cfg.Hq, cfg.Hkv, cfg.D, self.ws_attn,
+                                 attn_out=self.attn_out[li] if self.keep_layers else None,
+                                 tree_k=self.tree_k, tree_v=self.tree_v, stream=stream)
+            if self.keep_layers:
+                self.h_layers[li].copy_(h_out)
+
+    @property
+    def h_final(self):
+        return self.h[(self.cfg.n_layers - 1) % 2]
+
+    def step_head(self, stream=None):
+        api.glance_verify_head(self.h_final, self.w_head, self.argmax, self.top1, self.gap,
+                               self.entropy, self.ws_head, logits=self.logits, stream=stream)
+
+    def step_walk(self, stream=None, gap_flag=GAP_FLAG):
+        t = self.tree
+        api.glance_accept_walk(t["parent"], t["token"], t["n_valid"], self.argmax, self.gap,
+                               self.nseq, self.n_rows, self.L, gap_flag, self.n_accept,
+                               self.out_tokens, self.path_rows, self.flagged, stream)
+
+    def run(self, stream=None):
+        self.step_tree(stream)
+        self.step_attn(stream)
+        self.step_head(stream)
+        self.step_walk(stream)
+
+    def fetch(self) -> dict:
+        torch.cuda.synchronize()
+        out = {k: v.cpu().numpy() for k, v in self.tree.items()}
+        out["anc"] = out["anc"].view(np.uint64)
+        out.update(argmax=self.argmax.cpu().numpy(), top1=self.top1.cpu().numpy(),
+                   gap=self.gap.cpu().numpy(), entropy=self.entropy.cpu().numpy(),
+                   n_accept=self.n_accept.cpu().numpy(), out_tokens=self.out_tokens.cpu().numpy(),
+                   path_rows=self.path_rows.cpu().numpy(), flagged=self.flagged.cpu().numpy())
+        out["h_final"] = self.h_final.float().cpu().numpy()
+        if self.logits is not None:
+            out["logits"] = self.logits.cpu().numpy()
+        if self.keep_layers:
+            out["attn_out"] = [a.cpu().numpy() for a in self.attn_out]
+            out["h_layers"] = [h.float().cpu().numpy() for h in self.h_layers]
+        out["tree_k"] = self.tree_k.float().cpu().numpy()
+        out["tree_v"] = self.tree_v.float().cpu().numpy()
+        return out
