@@ -1,0 +1,157 @@
+"""Benchmark of the verify round on one MI355X.
+
+A step is one whole round (steps 1-5: tree build, one packed tree-attention
+layer, LM head with its epilogue, accept walk) over device-resident synthetic
+inputs of the 8B-shaped single-layer workload: d_model 4096, 32 query / 8 KV
+heads, head_dim 128, V 151936, L 15, N 63, a 1024-token prefix, bf16 storage.
+Prints one JSON line: rounds/s, per-step microseconds and HBM fractions
+(HIP events on the launch stream), the roofline of the dominant kernel (the LM
+head) and the CPU oracle timed on a sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verify rounds/s at N=63, L=15, V=151936 (8B shape); % of HBM peak per kernel"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor peak
+
+
+def step_bytes(cfg, P: int) -> dict:
+    """Algorithmic HBM bytes of each step of one round (each tensor moved once)."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    R = cfg.nseq * (cfg.N + 1)
+    d, HD, KD = cfg.d_model, cfg.Hq * cfg.D, cfg.Hkv * cfg.D
+    tree = cfg.nseq * cfg.L * cfg.V * es + R * 28
+    attn_layer = ((HD + 2 * KD) * d + d * HD) * es + 2 * P * KD * es * cfg.nseq + 2 * R * d * es
+    attn = cfg.n_layers * attn_layer
+    head = cfg.V * d * es + R * d * es + R * 16
+    walk = R * 16 + cfg.nseq * (cfg.L + 1) * 8
+    return {"build_tree": tree, "tree_attn": attn, "verify_head": head, "accept_walk": walk}
+
+
+def cpu_baseline(inp, r: int) -> dict:
+    """The CPU oracle as it stands, on one round of the same workload: log-softmax,
+    exact top-N tree, every verify row by unpacked evaluation, head statistics and
+    the walk (the independent greedy re-decode is left out of the sample)."""
+    from threadpoolctl import threadpool_info
+    from oracle import round as orr
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    t0 = time.perf_counter()
+    orr.oracle_round(inp, r, exact="beam", continuation_check=False)
+    dt = time.perf_counter() - t0
+    return {"value": 1.0 / dt, "unit": "rounds/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"1 round of {inp['cfg'].name} (steps 1-5, float64 NumPy), {dt:.1f} s",
+            "host_cpu": platform.processor() or platform.machine(),
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="qwen8b_1layer")
+    ap.add_argument("--seed", type=int, default=2000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe-copy", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    from synth import gen_round, make_config
+    from tree_verified_block_amd.round import DeviceRound, to_device
+
+    cfg = make_config(args.config)
+    t0 = time.perf_counter()
+    inp = gen_round(cfg, args.seed)
+    print(f"[bench] generated {cfg.name} in {time.perf_counter() - t0:.1f} s", file=sys.stderr,
+          flush=True)
+    dev = DeviceRound(inp, device="cuda")
+    dev.set_round(0)
+    drafts = [to_device(rd["draft_logits"], cfg.dtype, "cuda") for rd in inp["rounds"]
+              if "draft_logits" in rd]
+    stream = torch.cuda.current_stream()
+
+    def one_step(i, ev=None):
+        if drafts:
+            dev.draft = drafts[i % len(drafts)]
+        if ev:
+            ev[0].record(stream)
+        dev.step_tree()
+        if ev:
+            ev[1].record(stream)
+        dev.step_attn()
+        if ev:
+            ev[2].record(stream)
+        dev.step_head()
+        if ev:
+            ev[3].record(stream)
+        dev.step_walk()
+        if ev:
+            ev[4].record(stream)
+
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K whole rounds, events between the steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    names = ["build_tree", "tree_attn", "verify_head", "accept_walk"]
+    us = {n: float(np.mean([e[k].elapsed_time(e[k + 1]) for e in evs]) * 1e3)
+          for k, n in enumerate(names)}
+    P = int(inp["prefix_len"].max())
+    nbytes = step_bytes(cfg, P)
+    per_kernel = {n: {"us": round(us[n], 2), "bytes": nbytes[n],
+                      "hbm_frac": round(nbytes[n] / (us[n] * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)}
+                  for n in names}
+    total_bytes = sum(nbytes.values())
+    ms = wall / args.steps * 1e3
+    head_gbs = nbytes["verify_head"] / (us["verify_head"] * 1e-6) / 1e9
+    out = {
+        "metric": METRIC, "value": round(args.steps / wall, 2), "unit": "rounds/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16"
+        if cfg.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.n_layers} tree-attention layer(s), d_model "
+                   f"{cfg.d_model}, {cfg.Hq}q/{cfg.Hkv}kv heads x {cfg.D}, V {cfg.V}, L {cfg.L}, "
+                   f"N {cfg.N}, prefix {P}, nseq {cfg.nseq}", "seed": args.seed},
+        "round_hbm_frac": round(total_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+        "round_bytes": total_bytes,
+        "per_kernel": per_kernel,
+        "roofline": {"bound": "hbm", "kernel": "verify_head (LM head GEMM + row merge)",
+                     "achieved": round(head_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(head_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if args.probe_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, 0)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
