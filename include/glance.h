@@ -83,7 +83,8 @@ typedef enum {
  *                    ancestors (the root row is an ancestor of every row)
  *   score    float   the node's log plug-in score (0 for the root)
  *   n_valid  [nseq] int32: 1 + |S|
- * Limits: 1 <= L <= GLANCE_MAX_L, 2 <= V <= 2^20, nseq >= 1.
+ * Limits: 1 <= L <= GLANCE_MAX_L, nseq >= 1, 2 <= V <= 2^18 (bf16) or 2^17
+ * (fp32); larger V returns GLANCE_ERR_UNSUPPORTED.
  */
 glance_status glance_build_tree(const void* draft_logits, int32_t dtype,
                                 const int32_t* root_token, int32_t nseq, int32_t L,

@@ -14,8 +14,8 @@
 // each wave forms S^T = K Q^T (one query per lane, so the row max and sum of the
 // online softmax stay inside a lane and its partner lane l^32), rounds P to bf16
 // into its own LDS tile and accumulates O^T += V^T P^T.  The extra split n_split
-// takes the round's tree rows as keys: their K (rotated) and V come from the
-// fp32 projection, rounded to bf16 (a storage point), masked by anc.  Each
+// takes the round's tree rows as keys: the rotated bf16 K and bf16 V rows the
+// q/k/v projection wrote (a storage point), masked by anc.  Each
 // (split, query) leaves (max, sum, unnormalised O); attn_combine merges them.
 //
 // fp32 path (tiny shapes): one work-group per (row, query head), scores in LDS,
@@ -60,7 +60,6 @@ __global__ __launch_bounds__(kAThreads) void tree_attn_bf16_kernel(AttnArgs a) {
   const bool tree_split = (c == a.n_split);
   const int64_t kv0 = a.kv_offsets[s];
   const int P = static_cast<int>(a.kv_offsets[s + 1] - kv0);
-  const int nq_total = (a.Hq + 2 * a.Hkv) * kHD;
 
   // ---- this lane's query: q index, row, head; rotated and rounded to bf16
   const int q = qb * kQBlock + w * kQWave + j;
@@ -72,24 +71,11 @@ __global__ __launch_bounds__(kAThreads) void tree_attn_bf16_kernel(AttnArgs a) {
   const uint64_t qanc = qvalid ? a.anc[grow] : 0ull;
   bf16x8 qf[8];
   {
-    const int pos = row_pos(a, P, grow);
-    const float* xq = a.qkv + static_cast<size_t>(grow) * nq_total + qh * kHD;
-    const float* cs = a.rope_cos + static_cast<size_t>(pos) * (kHD / 2);
-    const float* sn = a.rope_sin + static_cast<size_t>(pos) * (kHD / 2);
+    const uint16_t* xq = static_cast<const uint16_t*>(a.q) + static_cast<size_t>(grow) * a.Hq * kHD + qh * kHD;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      uint16_t e[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int i = ks * 16 + 8 * g + t;
-        const int ii = i & (kHD / 2 - 1);
-        e[t] = qlive ? f32_to_bf16(rope_pair(xq, i, kHD / 2, cs[ii], sn[ii])) : 0;
-      }
-      uint4 u;
-      u.x = e[0] | (static_cast<uint32_t>(e[1]) << 16);
-      u.y = e[2] | (static_cast<uint32_t>(e[3]) << 16);
-      u.z = e[4] | (static_cast<uint32_t>(e[5]) << 16);
-      u.w = e[6] | (static_cast<uint32_t>(e[7]) << 16);
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (qlive) u = *reinterpret_cast<const uint4*>(xq + ks * 16 + 8 * g);
       qf[ks] = __builtin_bit_cast(bf16x8, u);
     }
   }
@@ -115,46 +101,22 @@ __global__ __launch_bounds__(kAThreads) void tree_attn_bf16_kernel(AttnArgs a) {
       const int key = k0 + kr;
       uint16_t kv[8], vv[8];
       if (key < kend) {
-        if (!tree_split) {
-          const size_t off = (static_cast<size_t>(kv0 + key) * a.Hkv + h) * kHD + col;
-          const uint4 ku = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_cache) + off);
-          const uint4 vu = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v_cache) + off);
-          const uint32_t kw[4] = {ku.x, ku.y, ku.z, ku.w};
-          const uint32_t vw[4] = {vu.x, vu.y, vu.z, vu.w};
+        const uint16_t* kb = tree_split ? static_cast<const uint16_t*>(a.tree_k)
+                                        : static_cast<const uint16_t*>(a.k_cache);
+        const uint16_t* vb = tree_split ? static_cast<const uint16_t*>(a.tree_v)
+                                        : static_cast<const uint16_t*>(a.v_cache);
+        const int64_t krow = tree_split ? static_cast<int64_t>(s) * a.n_rows + key : kv0 + key;
+        const size_t off = (static_cast<size_t>(krow) * a.Hkv + h) * kHD + col;
+        const uint4 ku = load_stream(kb + off);
+        const uint4 vu = load_stream(vb + off);
+        const uint32_t kw[4] = {ku.x, ku.y, ku.z, ku.w};
+        const uint32_t vw[4] = {vu.x, vu.y, vu.z, vu.w};
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            kv[2 * t] = kw[t] & 0xFFFF;
-            kv[2 * t + 1] = kw[t] >> 16;
-            vv[2 * t] = vw[t] & 0xFFFF;
-            vv[2 * t + 1] = vw[t] >> 16;
-          }
-        } else {
-          const int trow = s * a.n_rows + key;
-          const int pos = row_pos(a, P, trow);
-          const float* xk = a.qkv + static_cast<size_t>(trow) * nq_total + a.Hq * kHD + h * kHD;
-          const float* xv = xk + a.Hkv * kHD;
-          const float* cs = a.rope_cos + static_cast<size_t>(pos) * (kHD / 2);
-          const float* sn = a.rope_sin + static_cast<size_t>(pos) * (kHD / 2);
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const int i = col + t;
-            const int ii = i & (kHD / 2 - 1);
-            kv[t] = f32_to_bf16(rope_pair(xk, i, kHD / 2, cs[ii], sn[ii]));
-            vv[t] = f32_to_bf16(xv[i]);
-          }
-          if (qb == 0) {
-            const size_t o = (static_cast<size_t>(trow) * a.Hkv + h) * kHD + col;
-            if (a.tree_k) {
-              uint16_t* tk = static_cast<uint16_t*>(a.tree_k) + o;
-#pragma unroll
-              for (int t = 0; t < 8; ++t) tk[t] = kv[t];
-            }
-            if (a.tree_v) {
-              uint16_t* tv = static_cast<uint16_t*>(a.tree_v) + o;
-#pragma unroll
-              for (int t = 0; t < 8; ++t) tv[t] = vv[t];
-            }
-          }
+        for (int t = 0; t < 4; ++t) {
+          kv[2 * t] = kw[t] & 0xFFFF;
+          kv[2 * t + 1] = kw[t] >> 16;
+          vv[2 * t] = vw[t] & 0xFFFF;
+          vv[2 * t + 1] = vw[t] >> 16;
         }
       } else {
 #pragma unroll
@@ -261,50 +223,42 @@ __global__ __launch_bounds__(kAThreads) void tree_attn_bf16_kernel(AttnArgs a) {
   }
 }
 
-// Merge the split partials of every (row, query head) into the attention output.
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  const int grow = blockIdx.x;
+// Merge the split partials of every (row, query head) into the attention output:
+// one work-group per row and query head, one thread per head dimension, splits
+// folded in order with a running maximum.
+__global__ __launch_bounds__(kHD) void attn_combine_kernel(AttnArgs a) {
+  const int grow = blockIdx.x, qh = blockIdx.y, dim = threadIdx.x;
   const int s = grow / a.n_rows, r = grow % a.n_rows;
   const int G = a.Hq / a.Hkv;
   const int Qn = a.n_rows * G;
-  const bool live = a.token[grow] >= 0;
-  const int HD = a.Hq * kHD;
-  for (int e = threadIdx.x * 4; e < HD; e += 256 * 4) {
-    const int qh = e / kHD, dim = e % kHD;
-    const int h = qh / G, q = r * G + qh % G;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (live) {
-      const float* base = a.part + (static_cast<size_t>(s) * a.Hkv + h) * (a.n_split + 1) *
-                                       static_cast<size_t>(Qn) * kRec;
-      float M = -INFINITY;
-      for (int c = 0; c <= a.n_split; ++c) {
-        const float* rec = base + (static_cast<size_t>(c) * Qn + q) * kRec;
-        if (rec[1] > 0.f) M = fmaxf(M, rec[0]);
-      }
-      float Ls = 0.f;
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int c = 0; c <= a.n_split; ++c) {
-        const float* rec = base + (static_cast<size_t>(c) * Qn + q) * kRec;
-        if (rec[1] > 0.f) {
-          const float f = exp2f(rec[0] - M);
-          Ls += rec[1] * f;
-          const float4 v = *reinterpret_cast<const float4*>(rec + 4 + dim);
-          acc.x += v.x * f;
-          acc.y += v.y * f;
-          acc.z += v.z * f;
-          acc.w += v.w * f;
-        }
-      }
-      const float inv = 1.f / Ls;
-      o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  const int h = qh / G, q = r * G + qh % G;
+  float o = 0.f;
+  if (a.token[grow] >= 0) {
+    const float* rec = a.part + ((static_cast<size_t>(s) * a.Hkv + h) * (a.n_split + 1) *
+                                     static_cast<size_t>(Qn) + q) * kRec;
+    const size_t stride = static_cast<size_t>(Qn) * kRec;
+    const int ns = a.n_split + 1;
+    // pass 1: the largest split maximum (splits without keys have l = 0)
+    float M = -INFINITY;
+#pragma unroll 8
+    for (int c = 0; c < ns; ++c) {
+      const float m = rec[c * stride], l = rec[c * stride + 1];
+      M = fmaxf(M, l > 0.f ? m : -INFINITY);
     }
-    const size_t off = static_cast<size_t>(grow) * HD + e;
-    if (a.attn_out) *reinterpret_cast<float4*>(a.attn_out + off) = o;
-    uint2 u;
-    u.x = f32_to_bf16(o.x) | (static_cast<uint32_t>(f32_to_bf16(o.y)) << 16);
-    u.y = f32_to_bf16(o.z) | (static_cast<uint32_t>(f32_to_bf16(o.w)) << 16);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.attn_x) + off) = u;
+    // pass 2: rescaled sums, loads independent of each other
+    float Ls = 0.f, acc = 0.f;
+#pragma unroll 8
+    for (int c = 0; c < ns; ++c) {
+      const float m = rec[c * stride], l = rec[c * stride + 1], v = rec[c * stride + 4 + dim];
+      const float f = l > 0.f ? exp2f(m - M) : 0.f;
+      Ls += l * f;
+      acc += v * f;
+    }
+    o = acc / Ls;
   }
+  const size_t off = static_cast<size_t>(grow) * a.Hq * kHD + qh * kHD + dim;
+  if (a.attn_out) a.attn_out[off] = o;
+  static_cast<uint16_t*>(a.attn_x)[off] = f32_to_bf16(o);
 }
 
 // ------------------------------------------------------------------ fp32 path
@@ -437,7 +391,7 @@ glance_status launch_tree_attention(const AttnArgs& a, hipStream_t st) {
     dim3 grid(a.n_split + 1, a.Hkv * nqb, a.nseq);
     tree_attn_bf16_kernel<<<grid, kAThreads, 0, st>>>(a);
     GLANCE_LAUNCH_CHECK();
-    attn_combine_kernel<<<a.nseq * a.n_rows, 256, 0, st>>>(a);
+    attn_combine_kernel<<<dim3(a.nseq * a.n_rows, a.Hq), kHD, 0, st>>>(a);
     GLANCE_LAUNCH_CHECK();
   } else {
     dim3 grid(a.nseq * a.n_rows, a.Hq);

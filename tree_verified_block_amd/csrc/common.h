@@ -14,6 +14,16 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr int kWave = 64;
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load of data that is read once (weights, caches, draft logits): the
+// non-temporal hint keeps it from displacing reused lines in L2 and MALL and
+// streams noticeably faster from HBM.
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ------------------------------------------------------------------ bfloat16
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -51,21 +61,27 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int d = 32; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
   return v;
 }
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
-  return v;
-}
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) {
-    unsigned long long o = __shfl_xor(v, d, kWave);
-    v = o > v ? o : v;
-  }
-  return v;
-}
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Wave-wide unsigned max through DPP row shifts and row broadcasts (gfx9
+// family): after row_shr 1/2/4/8 each lane holds the max of its row prefix,
+// row_bcast:15 and row_bcast:31 carry rows 0..2 forward, lane 63 ends with the
+// maximum of all 64 lanes.  Lanes that receive no source keep 0, the identity.
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x142, 0xA, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x143, 0xC, 0xF, false)));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+__device__ __forceinline__ int readlane_i(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
 
 // -------------------------------------------------------------- launch checks
 #define GLANCE_LAUNCH_CHECK()                                   \

@@ -1,24 +1,30 @@
-// Skinny GEMMs of the verify pass: C = X W^T for the few verify rows X
-// [M][K] against a streamed weight matrix W [N][K] (out x in), with the
-// epilogue fused:
-//   EPI_STORE_F32  the QKV projection (fp32 out, RoPE is applied by the
-//                  attention kernel that reads it);
-//   EPI_RESID      the output projection plus residual, rounded to the storage
-//                  dtype (a storage point of the layer);
-//   EPI_HEAD       the LM head: per row and per 128-column tile, the partial
-//                  (max, argmax, second max, sum e^(z-max), sum e^(z-max)(z-max)),
-//                  merged by head_merge into argmax, top-1, top-2 gap and entropy
-//                  (paper §3.1 greedy token; App. B.1 top-2 gap; §6 root entropy).
+// Skinny GEMMs of the verify pass: C = X W^T for the few verify rows X [M][K]
+// against a streamed weight matrix W [N][K] (out x in), with the epilogue fused:
+//   EPI_QKV    the q/k/v projection: q and k rotated (rotate-half RoPE at the
+//              row's position), q, k, v rounded to bf16 (k and v are the rows'
+//              new cache entries, a storage point);
+//   EPI_RESID  the output projection plus residual, rounded to bf16 (the
+//              layer's output, a storage point);
+//   EPI_HEAD   the LM head: per row, partial (max, argmax, second max,
+//              sum e^(z-max), sum e^(z-max)(z-max)) of the work-group's columns,
+//              merged by head_merge into argmax, top-1, top-2 gap and entropy
+//              (paper §3.1 greedy token; App. B.1 top-2 gap; §6 root entropy).
 //
-// bf16 path (gfx950 MFMA v_mfma_f32_32x32x16_bf16): a 256-thread work-group
-// owns a 128 (N) x 64 (M) output tile.  Each wave streams its 32 weight rows
-// straight from HBM into registers (one 16-byte load per lane per 16-deep
-// k-step, a whole 256-deep chunk prefetched ahead), while the 64 activation rows
-// of the chunk are staged once per work-group in LDS (double-buffered, rows
-// padded by 16 bytes against bank conflicts).  At M <= 64 the weight stream is
-// the whole cost (64 flop per weight byte, below the MFMA ridge), so the kernel
-// is judged against HBM bandwidth.  Work-group ids are mapped so that the
-// M-tiles of one N-tile land on the same XCD back to back and share its L2.
+// bf16 path, gfx950 MFMA v_mfma_f32_16x16x32_bf16.  W is cut into 16-row blocks
+// (the MFMA A operand: lane l holds row l%16, k = 8(l/16)..+7 of a 32-deep step).
+// A 256-thread work-group is 4 waves; each wave owns B blocks of one K-slice
+// (S slices per work-group: S = 1 for the LM head, S = 4 for the small
+// projections so that hundreds of work-groups share their few thousand rows).
+// The loop runs over K outermost: every 64-deep chunk of the 64 activation rows
+// is staged once in LDS and shared by the work-group, while each wave streams
+// its blocks' weights from HBM straight into a ring of registers (the loads of
+// chunk c + DEPTH are issued before chunk c waits on its LDS barrier) and keeps
+// all its accumulators in registers.  At M <= 64 the weight
+// stream is the whole cost (64 flop per weight byte, far below the MFMA ridge),
+// so the kernel is judged against HBM bandwidth.  Blocks are dealt round-robin
+// over all waves of the grid (9496 blocks over 2048 waves for V = 151936), and
+// the M-tiles of one weight range are placed on the same XCD back to back so
+// that the weights are fetched from HBM once per XCD L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -27,11 +33,10 @@ namespace glance {
 namespace {
 
 constexpr int kGThreads = 256;
-constexpr int kTileN = 128;
 constexpr int kTileM = 64;
-constexpr int kKc = 256;          // K chunk staged per step
-constexpr int kXPad = kKc + 8;    // LDS row stride (bf16 elements)
-constexpr int kKSteps = kKc / 16;
+constexpr int kKc = 64;            // K chunk staged per step
+constexpr int kXP = kKc + 8;       // LDS row stride (bf16), padded against bank conflicts
+constexpr int kXS = kTileM * kXP;  // one staged sub-chunk (elements)
 
 struct HeadPart {
   float m;   // max logit
@@ -94,6 +99,7 @@ __device__ __forceinline__ HeadPart shfl_part(const HeadPart& p, int src) {
   return r;
 }
 
+
 __device__ __forceinline__ const uint16_t* x_row_ptr(const GemmArgs& a, int m) {
   if (m >= a.M) return nullptr;
   if (a.gather) {
@@ -104,157 +110,275 @@ __device__ __forceinline__ const uint16_t* x_row_ptr(const GemmArgs& a, int m) {
   return static_cast<const uint16_t*>(a.x) + static_cast<size_t>(m) * a.K;
 }
 
+// W row of row i (0..15) of block b.  For EPI_QKV the q and k blocks pair head
+// dims so that rows i and i+8 are RoPE partners: block j of a head holds dims
+// 8j..8j+7 and 64+8j..64+8j+7.
 template <int EPI>
-__global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a, int nNT, int nMT) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kTileM][kXPad];
-  __shared__ HeadPart red[4][kTileM];
+__device__ __forceinline__ int block_row(const GemmArgs& a, int b, int i) {
+  if constexpr (EPI == EPI_QKV) {
+    const int nq = a.Hq * 8, nk = a.Hkv * 8;
+    if (b < nq + nk) {
+      const int base = b < nq ? 0 : a.Hq * 128;
+      const int bb = b < nq ? b : b - nq;
+      const int dim = (i < 8) ? 8 * (bb & 7) + i : 64 + 8 * (bb & 7) + (i - 8);
+      return base + (bb >> 3) * 128 + dim;
+    }
+    return (a.Hq + a.Hkv) * 128 + (b - nq - nk) * 16 + i;
+  } else {
+    return b * 16 + i;
+  }
+}
 
-  const int b = blockIdx.x;
-  const int xcd = b & 7, kk = b >> 3;
+__device__ __forceinline__ const uint16_t* w_row_ptr(const GemmArgs& a, int row) {
+  int start = 0, sidx = 0;
+  while (sidx < a.w.nseg - 1 && row >= a.w.n_end[sidx]) start = a.w.n_end[sidx++];
+  return static_cast<const uint16_t*>(a.w.w[sidx]) + static_cast<size_t>(row - start) * a.K;
+}
+
+__device__ __forceinline__ uint2 pack4_bf16(float x0, float x1, float x2, float x3) {
+  uint2 u;
+  u.x = static_cast<uint32_t>(f32_to_bf16(x0)) | (static_cast<uint32_t>(f32_to_bf16(x1)) << 16);
+  u.y = static_cast<uint32_t>(f32_to_bf16(x2)) | (static_cast<uint32_t>(f32_to_bf16(x3)) << 16);
+  return u;
+}
+
+template <int EPI, int B, int S, int DEPTH>
+__global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a, int NB, int NG,
+                                                                 int nWG, int nMT) {
+  constexpr int GPW = 4 / S;  // block groups per work-group
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2 * S * kXS];
+  __shared__ HeadPart hred[4][kTileM];
+
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, kk = bid >> 3;
   const int mt = kk % nMT;
-  const int nt = (kk / nMT) * 8 + xcd;
-  if (nt >= nNT) return;
-  const int n0 = nt * kTileN, m0 = mt * kTileM;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 31, g = l >> 5;
+  const int wg = (kk / nMT) * 8 + xcd;
+  if (wg >= nWG) return;
+  const int m0 = mt * kTileM;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+  const int q = w % S, gi = w / S;
+  const int G = wg * GPW + gi;
+  const int Ks = a.K / S;
+  const int kbase = q * Ks;
+  const int nck = Ks / kKc;
 
-  // this lane's weight row (clamped into range; outputs past N are masked)
-  int wrow = n0 + w * 32 + li;
-  if (wrow > a.N - 1) wrow = a.N - 1;
-  const uint16_t* wp;
-  {
-    int start = 0, sidx = 0;
-    while (sidx < a.w.nseg - 1 && wrow >= a.w.n_end[sidx]) start = a.w.n_end[sidx++];
-    wp = static_cast<const uint16_t*>(a.w.w[sidx]) + static_cast<size_t>(wrow - start) * a.K + 8 * g;
+  // this wave's blocks
+  int blk[B];
+  bool bval[B];
+  const uint16_t* wp[B];
+#pragma unroll
+  for (int t = 0; t < B; ++t) {
+    blk[t] = G + t * NG;
+    bval[t] = G < NG && blk[t] < NB;
+    int row = bval[t] ? block_row<EPI>(a, blk[t], lr) : 0;
+    if (row > a.N - 1) row = a.N - 1;
+    wp[t] = w_row_ptr(a, row) + kbase + 8 * lg;
   }
 
-  // activation rows this thread copies into LDS: rows tid/32 + 8 p, 16 bytes at col (tid%32)*8
-  const uint16_t* xr[8];
+  // activation rows this thread stages: S sub-chunks x 64 rows x 8 pieces of 16 B
+  const uint16_t* xr[2 * S];
+  int xoff[2 * S], xlds[2 * S];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) xr[p] = x_row_ptr(a, m0 + p * 8 + (tid >> 5));
-  const int xc = (tid & 31) * 8;
+  for (int e = 0; e < 2 * S; ++e) {
+    const int idx = e * kGThreads + tid;
+    const int sub = idx >> 9, r = (idx >> 3) & 63, cc = (idx & 7) * 8;
+    xr[e] = x_row_ptr(a, m0 + r);
+    xoff[e] = sub * Ks + cc;
+    xlds[e] = sub * kXS + r * kXP + cc;
+  }
 
-  const int nch = a.K / kKc;
-  f32x16 acc0 = {}, acc1 = {};
-  uint4 wcur[kKSteps], wnext[kKSteps];
-  uint4 xnext[8];
-
-  // prologue: chunk 0
+  f32x4 acc[B][4];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
+  for (int t = 0; t < B; ++t)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[t][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // weight ring of DEPTH + 1 chunk slots: the loads of chunk c + DEPTH are issued
+  // before chunk c waits on the LDS barrier, so they overlap both
+  constexpr int RS = DEPTH + 1;
+  uint4 wbuf[RS][B][2];
+  auto wload = [&](int c, uint4 (&dst)[B][2]) {
+#pragma unroll
+    for (int t = 0; t < B; ++t)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) dst[t][s] = *reinterpret_cast<const uint4*>(wp[t] + c * kKc + s * 32);
+  };
+
+  // prologue: X chunk 0 -> LDS stage 0, W chunks 0 .. DEPTH-1 -> registers
+#pragma unroll
+  for (int e = 0; e < 2 * S; ++e) {
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (xr[p]) v = *reinterpret_cast<const uint4*>(xr[p] + xc);
-    *reinterpret_cast<uint4*>(&xs[0][p * 8 + (tid >> 5)][xc]) = v;
+    if (xr[e]) v = *reinterpret_cast<const uint4*>(xr[e] + xoff[e]);
+    *reinterpret_cast<uint4*>(&xs[xlds[e]]) = v;
   }
 #pragma unroll
-  for (int s = 0; s < kKSteps; ++s) wcur[s] = *reinterpret_cast<const uint4*>(wp + s * 16);
+  for (int d = 0; d < DEPTH; ++d)
+    if (d < nck) wload(d, wbuf[d]);
 
-  for (int c = 0; c < nch; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < nch;
-    if (more) {
-      const int k1 = (c + 1) * kKc;
+  for (int c0 = 0; c0 < nck; c0 += RS) {
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        xnext[p] = make_uint4(0, 0, 0, 0);
-        if (xr[p]) xnext[p] = *reinterpret_cast<const uint4*>(xr[p] + k1 + xc);
-      }
+    for (int u = 0; u < RS; ++u) {
+      const int c = c0 + u;
+      if (c < nck) {
+        if (c + DEPTH < nck) wload(c + DEPTH, wbuf[(u + DEPTH) % RS]);
+        const int st = c & 1;
+        const bool more = c + 1 < nck;
+        uint4 xn[2 * S];
+        if (more) {
 #pragma unroll
-      for (int s = 0; s < kKSteps; ++s)
-        wnext[s] = *reinterpret_cast<const uint4*>(wp + k1 + s * 16);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < kKSteps; ++s) {
-      const bf16x8 av = __builtin_bit_cast(bf16x8, wcur[s]);
-      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(&xs[buf][li][s * 16 + 8 * g]);
-      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(&xs[buf][32 + li][s * 16 + 8 * g]);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b0, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b1, acc1, 0, 0, 0);
-    }
-    if (more) {
-#pragma unroll
-      for (int p = 0; p < 8; ++p)
-        *reinterpret_cast<uint4*>(&xs[buf ^ 1][p * 8 + (tid >> 5)][xc]) = xnext[p];
-#pragma unroll
-      for (int s = 0; s < kKSteps; ++s) wcur[s] = wnext[s];
-    }
-  }
-
-  // ------------------------------------------------------------- epilogues
-  // acc element v of this lane: output row n = n0 + 32 w + 8 (v/4) + 4 g + v%4,
-  // activation row m = m0 + li (acc0) or m0 + 32 + li (acc1).
-  const int nb = n0 + w * 32 + 4 * g;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const f32x16 acc = h ? acc1 : acc0;
-    const int m = m0 + h * 32 + li;
-    if constexpr (EPI == EPI_STORE_F32) {
-      if (m < a.M) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = nb + 8 * q;
-          if (n < a.N) {
-            float4 o = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
-            *reinterpret_cast<float4*>(a.out_f32 + static_cast<size_t>(m) * a.N + n) = o;
+          for (int e = 0; e < 2 * S; ++e) {
+            xn[e] = make_uint4(0, 0, 0, 0);
+            if (xr[e]) xn[e] = *reinterpret_cast<const uint4*>(xr[e] + xoff[e] + (c + 1) * kKc);
           }
         }
-      }
-    } else if constexpr (EPI == EPI_RESID) {
-      if (m < a.M) {
-        const uint16_t* rp = nullptr;
-        const int tok = a.resid_tok[m];
-        if (tok >= 0)
-          rp = static_cast<const uint16_t*>(a.resid) +
-               static_cast<size_t>(a.resid_by_token ? tok : m) * a.N;
-        uint16_t* op = static_cast<uint16_t*>(a.out_res) + static_cast<size_t>(m) * a.N;
+        __syncthreads();
+        const uint16_t* xq = xs + (st * S + q) * kXS;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = nb + 8 * q;
-          if (n < a.N) {
-            uint2 o = make_uint2(0, 0);
-            if (rp) {
-              const uint2 r = *reinterpret_cast<const uint2*>(rp + n);
-              const float r0 = bf16_to_f32(static_cast<uint16_t>(r.x & 0xFFFF));
-              const float r1 = bf16_to_f32(static_cast<uint16_t>(r.x >> 16));
-              const float r2 = bf16_to_f32(static_cast<uint16_t>(r.y & 0xFFFF));
-              const float r3 = bf16_to_f32(static_cast<uint16_t>(r.y >> 16));
-              o.x = static_cast<uint32_t>(f32_to_bf16(r0 + acc[4 * q])) |
-                    (static_cast<uint32_t>(f32_to_bf16(r1 + acc[4 * q + 1])) << 16);
-              o.y = static_cast<uint32_t>(f32_to_bf16(r2 + acc[4 * q + 2])) |
-                    (static_cast<uint32_t>(f32_to_bf16(r3 + acc[4 * q + 3])) << 16);
-            }
-            *reinterpret_cast<uint2*>(op + n) = o;
+        for (int s = 0; s < 2; ++s) {
+          bf16x8 bx[4];
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+            bx[mb] = *reinterpret_cast<const bf16x8*>(xq + (mb * 16 + lr) * kXP + s * 32 + 8 * lg);
+#pragma unroll
+          for (int t = 0; t < B; ++t) {
+            const bf16x8 av = __builtin_bit_cast(bf16x8, wbuf[u][t][s]);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+              acc[t][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bx[mb], acc[t][mb], 0, 0, 0);
           }
         }
-      }
-    } else {  // EPI_HEAD
-      HeadPart p = head_empty();
+        if (more) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int n = nb + 8 * (v >> 2) + (v & 3);
-        if (n < a.N) {
-          p = head_combine(p, head_elem(acc[v], n));
-          if (a.logits && m < a.M) a.logits[static_cast<size_t>(m) * a.N + n] = acc[v];
+          for (int e = 0; e < 2 * S; ++e)
+            *reinterpret_cast<uint4*>(&xs[(st ^ 1) * S * kXS + xlds[e]]) = xn[e];
         }
       }
-      p = head_combine(p, shfl_part(p, l ^ 32));
-      if (g == 0) red[w][h * 32 + li] = p;
     }
   }
+
+  // ------------------------------------------------------------------ epilogues
+  // acc[t][mb][v]: row i = 4 lg + v of block blk[t], activation row m0 + 16 mb + lr.
   if constexpr (EPI == EPI_HEAD) {
+    HeadPart hp[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) hp[mb] = head_empty();
+#pragma unroll
+    for (int t = 0; t < B; ++t) {
+      if (!bval[t]) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int n = blk[t] * 16 + 4 * lg + v;
+        if (n < a.N) {
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) {
+            hp[mb] = head_combine(hp[mb], head_elem(acc[t][mb][v], n));
+            const int m = m0 + mb * 16 + lr;
+            if (a.logits && m < a.M) a.logits[static_cast<size_t>(m) * a.N + n] = acc[t][mb][v];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      hp[mb] = head_combine(hp[mb], shfl_part(hp[mb], l ^ 16));
+      hp[mb] = head_combine(hp[mb], shfl_part(hp[mb], l ^ 32));
+      if (lg == 0) hred[w][mb * 16 + lr] = hp[mb];
+    }
     __syncthreads();
     if (tid < kTileM) {
-      HeadPart p = red[0][tid];
+      HeadPart p = hred[0][tid];
 #pragma unroll
-      for (int q = 1; q < 4; ++q) p = head_combine(p, red[q][tid]);
+      for (int ww = 1; ww < 4; ++ww) p = head_combine(p, hred[ww][tid]);
       const int m = m0 + tid;
       if (m < a.M) {
-        float* o = a.part + (static_cast<size_t>(m) * nNT + nt) * 5;
+        float* o = a.part + (static_cast<size_t>(m) * nWG + wg) * 5;
         o[0] = p.m;
         o[1] = __int_as_float(p.am);
         o[2] = p.m2;
         o[3] = p.s;
         o[4] = p.t;
+      }
+    }
+  } else {
+    // sum the S K-slice partials of each block in LDS (fixed order), then write
+    static_assert(B == 1, "projection epilogues take one block per wave");
+    float* red = reinterpret_cast<float*>(xs);  // [GPW][S][16][64]
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        red[((gi * S + q) * 16 + 4 * lg + v) * 64 + mb * 16 + lr] = acc[0][mb][v];
+    __syncthreads();
+    if (!bval[0]) return;
+    const int lt = q * 64 + l;  // thread index within the block group (S*64 threads)
+    const float* rg = red + gi * S * 1024;
+    auto sumq = [&](int i, int m) {
+      float x = 0.f;
+#pragma unroll
+      for (int qq = 0; qq < S; ++qq) x += rg[(qq * 16 + i) * 64 + m];
+      return x;
+    };
+    if constexpr (EPI == EPI_RESID) {
+      // 16 rows x 64 activations = 256 items of 4 consecutive columns
+      for (int it = lt; it < 256; it += S * 64) {
+        const int m = it & 63, i0 = (it >> 6) * 4;
+        const int gm = m0 + m;
+        if (gm >= a.M) continue;
+        const int n = blk[0] * 16 + i0;
+        if (n >= a.N) continue;
+        float x[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) x[v] = sumq(i0 + v, m);
+        uint2 o = make_uint2(0, 0);
+        const int tok = a.resid_tok[gm];
+        if (tok >= 0) {
+          const uint16_t* rp = static_cast<const uint16_t*>(a.resid) +
+                               static_cast<size_t>(a.resid_by_token ? tok : gm) * a.N + n;
+          const uint2 r = *reinterpret_cast<const uint2*>(rp);
+          o = pack4_bf16(bf16_to_f32(r.x & 0xFFFF) + x[0], bf16_to_f32(r.x >> 16) + x[1],
+                         bf16_to_f32(r.y & 0xFFFF) + x[2], bf16_to_f32(r.y >> 16) + x[3]);
+        }
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out_res) + static_cast<size_t>(gm) * a.N + n) = o;
+      }
+    } else {  // EPI_QKV
+      const int b = blk[0];
+      const int nq = a.Hq * 8, nk = a.Hkv * 8;
+      if (b < nq + nk) {
+        // q or k block: rows i < 8 are dims 8j+i, rows 8+i their RoPE partners 64+8j+i
+        const int bb = b < nq ? b : b - nq;
+        const int head = bb >> 3, j8 = (bb & 7) * 8;
+        for (int it = lt; it < 128; it += S * 64) {
+          const int m = it & 63, i0 = (it >> 6) * 4;
+          const int gm = m0 + m;
+          if (gm >= a.M) continue;
+          const int sq = gm / a.n_rows;
+          int pos = static_cast<int>(a.kv_offsets[sq + 1] - a.kv_offsets[sq]) + a.depth[gm];
+          if (pos > a.n_pos - 1) pos = a.n_pos - 1;
+          float lo[4], hi[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int d = j8 + i0 + v;
+            const float c = a.rope_cos[static_cast<size_t>(pos) * 64 + d];
+            const float sn = a.rope_sin[static_cast<size_t>(pos) * 64 + d];
+            const float x1 = sumq(i0 + v, m), x2 = sumq(8 + i0 + v, m);
+            lo[v] = x1 * c - x2 * sn;
+            hi[v] = x2 * c + x1 * sn;
+          }
+          uint16_t* op = b < nq ? static_cast<uint16_t*>(a.q_out) + static_cast<size_t>(gm) * a.Hq * 128
+                                : static_cast<uint16_t*>(a.k_out) + static_cast<size_t>(gm) * a.Hkv * 128;
+          op += head * 128 + j8 + i0;
+          *reinterpret_cast<uint2*>(op) = pack4_bf16(lo[0], lo[1], lo[2], lo[3]);
+          *reinterpret_cast<uint2*>(op + 64) = pack4_bf16(hi[0], hi[1], hi[2], hi[3]);
+        }
+      } else {
+        const int vr = (b - nq - nk) * 16;  // first v row of the block
+        for (int it = lt; it < 256; it += S * 64) {
+          const int m = it & 63, i0 = (it >> 6) * 4;
+          const int gm = m0 + m;
+          if (gm >= a.M) continue;
+          uint16_t* op = static_cast<uint16_t*>(a.v_out) + static_cast<size_t>(gm) * a.Hkv * 128 + vr + i0;
+          *reinterpret_cast<uint2*>(op) = pack4_bf16(sumq(i0, m), sumq(i0 + 1, m), sumq(i0 + 2, m), sumq(i0 + 3, m));
+        }
       }
     }
   }
@@ -353,22 +477,46 @@ __global__ __launch_bounds__(256) void head_rowstats_f32_kernel(const float* __r
 
 }  // namespace
 
-int gemm_bf16_n_tiles(int N) { return (N + kTileN - 1) / kTileN; }
+namespace {
+constexpr int kHeadB = 5;      // weight blocks per wave in the LM head
+constexpr int kHeadWaves = 2048;  // waves the LM head grid aims for (256 CUs x 8)
+
+struct HeadGrid {
+  int NB, NG, nWG;
+};
+HeadGrid head_grid(int N) {
+  HeadGrid g;
+  g.NB = (N + 15) / 16;
+  int ng = g.NB < kHeadWaves ? g.NB : kHeadWaves;
+  const int need = (g.NB + kHeadB - 1) / kHeadB;
+  if (ng < need) ng = need;
+  g.NG = ng;
+  g.nWG = (ng + 3) / 4;
+  return g;
+}
+}  // namespace
+
+int gemm_bf16_head_parts(int N) { return head_grid(N).nWG; }
 
 glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
-  const int nNT = gemm_bf16_n_tiles(a.N);
   const int nMT = (a.M + kTileM - 1) / kTileM;
-  const int grid = ((nNT + 7) / 8) * 8 * nMT;
-  switch (a.epi) {
-    case EPI_STORE_F32:
-      gemm_bf16_kernel<EPI_STORE_F32><<<grid, kGThreads, 0, st>>>(a, nNT, nMT);
-      break;
-    case EPI_RESID:
-      gemm_bf16_kernel<EPI_RESID><<<grid, kGThreads, 0, st>>>(a, nNT, nMT);
-      break;
-    default:
-      gemm_bf16_kernel<EPI_HEAD><<<grid, kGThreads, 0, st>>>(a, nNT, nMT);
-      break;
+  if (a.epi == EPI_HEAD) {
+    const HeadGrid g = head_grid(a.N);
+    const int grid = ((g.nWG + 7) / 8) * 8 * nMT;
+    gemm_bf16_kernel<EPI_HEAD, kHeadB, 1, 1><<<grid, kGThreads, 0, st>>>(a, g.NB, g.NG, g.nWG, nMT);
+  } else {
+    // one 16-row block per work-group, its K split over the 4 waves
+    int NB;
+    if (a.epi == EPI_QKV)
+      NB = (a.Hq + 2 * a.Hkv) * 8;
+    else
+      NB = (a.N + 15) / 16;
+    const int nWG = NB;
+    const int grid = ((nWG + 7) / 8) * 8 * nMT;
+    if (a.epi == EPI_QKV)
+      gemm_bf16_kernel<EPI_QKV, 1, 4, 3><<<grid, kGThreads, 0, st>>>(a, NB, NB, nWG, nMT);
+    else
+      gemm_bf16_kernel<EPI_RESID, 1, 4, 3><<<grid, kGThreads, 0, st>>>(a, NB, NB, nWG, nMT);
   }
   GLANCE_LAUNCH_CHECK();
   return GLANCE_OK;

@@ -58,7 +58,7 @@ glance_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
 // ---------------------------------------------------------------- tree_attn ws
 struct AttnWs {
   int n_split = 0, split = 0;
-  size_t off_qkv = 0, off_part = 0, off_x = 0, bytes = 0;
+  size_t off_qkv = 0, off_q = 0, off_k = 0, off_v = 0, off_part = 0, off_x = 0, bytes = 0;
 };
 
 AttnWs attn_ws_layout(int dtype, int nseq, int n_rows, int64_t max_prefix, int d_model, int Hq,
@@ -66,18 +66,24 @@ AttnWs attn_ws_layout(int dtype, int nseq, int n_rows, int64_t max_prefix, int d
   (void)d_model;
   AttnWs w;
   const size_t R = static_cast<size_t>(nseq) * n_rows;
-  const size_t nqkv = static_cast<size_t>(Hq + 2 * Hkv) * D;
   size_t off = 0;
-  w.off_qkv = off;
-  off += round256(R * nqkv * sizeof(float));
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += round256(bytes);
+    return o;
+  };
   if (dtype == GLANCE_BF16) {
+    w.off_q = take(R * Hq * D * 2);
+    w.off_k = take(R * Hkv * D * 2);
+    w.off_v = take(R * Hkv * D * 2);
     w.split = attn_split_len(max_prefix, nseq, Hkv);
     w.n_split = static_cast<int>((max_prefix + w.split - 1) / w.split);
-    w.off_part = off;
-    off += round256(attn_part_floats(nseq, n_rows, Hq, Hkv, D, w.n_split) * sizeof(float));
+    w.off_part = take(attn_part_floats(nseq, n_rows, Hq, Hkv, D, w.n_split) * sizeof(float));
+    w.off_x = take(R * Hq * D * 2);
+  } else {
+    w.off_qkv = take(R * static_cast<size_t>(Hq + 2 * Hkv) * D * sizeof(float));
+    w.off_x = take(R * Hq * D * sizeof(float));
   }
-  w.off_x = off;
-  off += round256(R * Hq * D * (dtype == GLANCE_BF16 ? 2 : 4));
   w.bytes = off;
   return w;
 }
@@ -114,7 +120,7 @@ int32_t glance_abi_version(void) { return 1; }
 // ------------------------------------------------------------------ step 1+2
 size_t glance_build_tree_ws(int32_t nseq, int32_t L, int32_t V, int32_t N) {
   (void)N;
-  if (nseq < 1 || L < 1 || L > GLANCE_MAX_L || V < 2 || V > (1 << 20)) return 0;
+  if (nseq < 1 || L < 1 || L > GLANCE_MAX_L || V < 2 || V > (1 << 18)) return 0;
   return tree_ws_layout(nseq, L, V).bytes;
 }
 
@@ -127,8 +133,10 @@ glance_status glance_build_tree(const void* draft_logits, int32_t dtype,
   REQUIRE(dtype == GLANCE_F32 || dtype == GLANCE_BF16, "dtype %d is not GLANCE_F32/BF16", dtype);
   REQUIRE(nseq >= 1, "nseq = %d < 1", nseq);
   REQUIRE(L >= 1 && L <= GLANCE_MAX_L, "L = %d outside [1, %d]", L, GLANCE_MAX_L);
-  REQUIRE(V >= 2 && V <= (1 << 20), "V = %d outside [2, 2^20]", V);
+  REQUIRE(V >= 2, "V = %d < 2", V);
   REQUIRE(N >= 0 && N <= GLANCE_MAX_ROWS - 1, "N = %d outside [0, %d]", N, GLANCE_MAX_ROWS - 1);
+  if (V > (dtype == GLANCE_BF16 ? (1 << 18) : (1 << 17)))
+    return fail(GLANCE_ERR_UNSUPPORTED, "V = %d above 2^18 (bf16) / 2^17 (fp32)", V);
   REQUIRE_PTR(draft_logits);
   REQUIRE_PTR(root_token);
   REQUIRE_PTR(parent);
@@ -209,10 +217,13 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
-  float* qkv = reinterpret_cast<float*>(base + w.off_qkv);
   void* attn_x = base + w.off_x;
   const int R = nseq * n_rows;
   const int qd = Hq * D, kd = Hkv * D;
+  if (dtype == GLANCE_BF16) {
+    if (tree_k == nullptr) tree_k = base + w.off_k;
+    if (tree_v == nullptr) tree_v = base + w.off_v;
+  }
 
   // 1. q, k, v of every row (layer input: embedding rows or h_in)
   GemmArgs g{};
@@ -228,15 +239,32 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
   g.M = R;
   g.N = qd + 2 * kd;
   g.K = d_model;
-  g.epi = EPI_STORE_F32;
-  g.out_f32 = qkv;
-  st = dtype == GLANCE_BF16 ? launch_gemm_bf16(g, hs) : launch_gemm_f32(g, hs);
+  if (dtype == GLANCE_BF16) {
+    g.epi = EPI_QKV;
+    g.Hq = Hq;
+    g.Hkv = Hkv;
+    g.q_out = base + w.off_q;
+    g.k_out = tree_k;
+    g.v_out = tree_v;
+    g.kv_offsets = kv_offsets;
+    g.depth = depth;
+    g.n_rows = n_rows;
+    g.rope_cos = rope_cos;
+    g.rope_sin = rope_sin;
+    g.n_pos = n_pos;
+    st = launch_gemm_bf16(g, hs);
+  } else {
+    g.epi = EPI_STORE_F32;
+    g.out_f32 = reinterpret_cast<float*>(base + w.off_qkv);
+    st = launch_gemm_f32(g, hs);
+  }
   if (st != GLANCE_OK) return st;
 
   // 2. attention over prefix + ancestors
   AttnArgs a{};
   a.dtype = dtype;
-  a.qkv = qkv;
+  a.qkv = reinterpret_cast<const float*>(base + w.off_qkv);
+  a.q = base + w.off_q;
   a.k_cache = layer->k_cache;
   a.v_cache = layer->v_cache;
   a.kv_offsets = kv_offsets;
@@ -285,7 +313,7 @@ size_t glance_verify_head_ws(int32_t R, int32_t V, int32_t d_model, int32_t dtyp
   (void)d_model;
   if (R < 1 || V < 2) return 0;
   if (dtype == GLANCE_BF16)
-    return round256(static_cast<size_t>(R) * gemm_bf16_n_tiles(V) * 5 * sizeof(float));
+    return round256(static_cast<size_t>(R) * gemm_bf16_head_parts(V) * 5 * sizeof(float));
   return round256(static_cast<size_t>(R) * V * sizeof(float));
 }
 
@@ -325,7 +353,7 @@ glance_status glance_verify_head(const void* h, const void* w_head, int32_t dtyp
     g.logits = logits;
     st = launch_gemm_bf16(g, hs);
     if (st != GLANCE_OK) return st;
-    return launch_head_merge(g.part, gemm_bf16_n_tiles(V), R, argmax, top1, gap, entropy, hs);
+    return launch_head_merge(g.part, gemm_bf16_head_parts(V), R, argmax, top1, gap, entropy, hs);
   }
   g.logits = logits ? logits : static_cast<float*>(ws);
   st = launch_gemm_f32(g, hs);

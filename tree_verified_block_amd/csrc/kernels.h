@@ -12,8 +12,8 @@ namespace glance {
 
 // ------------------------------------------------------------------ tree.hip
 struct TreeWs {
-  int chunk = 0, ipt = 0, nch = 0;
-  size_t off_cstat = 0, off_ccand = 0, off_logq = 0, off_id = 0, bytes = 0;
+  int nch = 0, chunk = 0;  // chunks per offset row and logits per chunk
+  size_t off_cstat = 0, off_clist = 0, off_logq = 0, off_id = 0, bytes = 0;
 };
 TreeWs tree_ws_layout(int nseq, int L, int V);
 glance_status launch_build_tree(const void* logits, int dtype, const int32_t* root, int nseq,
@@ -29,7 +29,7 @@ struct GemmSeg {
   int n_end[3];  // cumulative row counts
   int nseg;
 };
-enum GemmEpi { EPI_STORE_F32 = 0, EPI_RESID = 1, EPI_HEAD = 2 };
+enum GemmEpi { EPI_STORE_F32 = 0, EPI_RESID = 1, EPI_HEAD = 2, EPI_QKV = 3 };
 struct GemmArgs {
   const void* x;          // [M][K]
   const int32_t* gather;  // NULL or [M] token ids (row m of X = x[gather[m]], -1 = zero row)
@@ -41,10 +41,23 @@ struct GemmArgs {
   const int32_t* resid_tok;  // EPI_RESID: [M] token ids; rows with token < 0 are written as 0
   bool resid_by_token;     // residual row m is resid[resid_tok[m]] (else resid[m])
   void* out_res;           // EPI_RESID: [M][N] in the storage dtype
-  float* part;             // EPI_HEAD: [M][n_tiles] partial statistics (5 floats)
+  float* part;             // EPI_HEAD: [M][n_part] partial statistics (5 floats)
   float* logits;           // EPI_HEAD: optional [M][N]
+  // EPI_QKV (bf16, head_dim 128): W = [Wq; Wk; Wv]; q and k rotated at the row's
+  // position, everything rounded to bf16.
+  int Hq, Hkv;
+  void* q_out;             // [M][Hq*128]
+  void* k_out;             // [M][Hkv][128]
+  void* v_out;             // [M][Hkv][128]
+  const int64_t* kv_offsets;
+  const int32_t* depth;
+  int n_rows;
+  const float* rope_cos;
+  const float* rope_sin;
+  int n_pos;
 };
-int gemm_bf16_n_tiles(int N);
+// Number of per-row partial records the bf16 LM-head GEMM leaves (the merge input).
+int gemm_bf16_head_parts(int N);
 glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
 glance_status launch_gemm_f32(const GemmArgs& a, hipStream_t st);
 // Row statistics of the head from bf16 partials, or from full fp32 logits.
@@ -57,7 +70,8 @@ glance_status launch_head_rowstats_f32(const float* logits, int R, int V, int32_
 // ------------------------------------------------------------------ attn.hip
 struct AttnArgs {
   int dtype;
-  const float* qkv;        // [R][(Hq + 2 Hkv) D] fp32 projections (before RoPE)
+  const float* qkv;        // fp32 path: [R][(Hq + 2 Hkv) D] projections (before RoPE)
+  const void* q;           // bf16 path: [R][Hq D] rotated queries (tree K/V in tree_k/v)
   const void* k_cache;     // [sum P][Hkv][D]
   const void* v_cache;
   const int64_t* kv_offsets;
@@ -74,7 +88,7 @@ struct AttnArgs {
   float* part;             // partial (m, l, o[D]) per split and query
   float* attn_out;         // NULL or [R][Hq D] fp32
   void* attn_x;            // [R][Hq D] storage dtype: input of the output projection
-  void* tree_k;            // NULL or [R][Hkv][D]
+  void* tree_k;            // [R][Hkv][D]: written by the fp32 path (if not NULL), read by bf16
   void* tree_v;
 };
 int attn_split_len(int64_t max_prefix, int nseq, int Hkv);

@@ -10,18 +10,29 @@
 // Only the K_j = min(N - j + 1, V) best tokens of offset j can appear at depth j:
 // a depth-j node of rank r is preceded by its r - 1 better siblings and its j - 1
 // ancestors, all of which must also be in S.  So each offset keeps <= 63 tokens.
+// Tokens are ranked by the key (logit desc, token id asc); keys are distinct.
 //
 // Kernels
-//   lsm_chunk   grid (chunks, L, nseq) x 256: per chunk of one offset's logits,
-//               the chunk maximum, sum exp(z - max), and the chunk's K_j best
-//               tokens by an LDS radix select on the key (logit, -token id).
-//   lsm_merge   grid (L, nseq) x 256: merges the chunks of one offset into
-//               log q_j(v) = (z_v - max) - ln(sum exp(z - max)) for its K_j best
-//               tokens, ordered by (logit desc, token id asc).
-//   build_tree  grid nseq x 64: one wavefront runs best-first selection over the
-//               ranked lists (each lane holds one frontier prefix; a pop is a
-//               wave-wide max), then lays the nodes out breadth-first and builds
-//               the ancestor masks.
+//   lsm_chunk   grid (chunks, L, nseq) x 256.  One chunk (4096 bf16 or 2048 fp32
+//               logits) of one offset row, held in registers after one wave of
+//               16-byte streaming loads: the chunk maximum, the sum of
+//               exp(z - max) and the chunk's K best keys, sorted (block_topk).
+//   lsm_merge   grid (L, nseq) x 256.  Combines the chunk statistics into the
+//               row's max and ln(sum exp), selects the K best of the <= 64 chunk
+//               lists (block_topk again) and writes them as
+//               log q_j(v) = (z_v - max) - ln(sum exp(z - max)) with their ids.
+//   build_tree  grid nseq x 256.  The ranked lists go to LDS; wave 0 runs
+//               best-first selection: lane 0 is the root and lane i the i-th
+//               selected node; every lane holds the best not-yet-selected child
+//               of its node, so a selection is one wave max and touches two
+//               lanes.  Finally the nodes are laid out breadth-first with their
+//               ancestor masks.
+//
+// block_topk finds the K largest of the keys a block holds in registers: the
+// K-th largest of the per-thread best keys, T, bounds the K-th largest key from
+// below (K threads each hold a key >= T), so only keys >= T (about K of them)
+// are gathered to LDS and ranked exactly by counting; when more than kCap keys
+// reach T (massive ties) an exact 8-bit radix select runs instead.
 #include "common.h"
 #include "kernels.h"
 
@@ -29,7 +40,6 @@ namespace glance {
 
 namespace {
 
-constexpr int kTopThreads = 256;
 constexpr int kSlots = 64;  // candidate slots per (offset, chunk); K_j <= 63
 
 __device__ __forceinline__ int k_of(int N, int V, int j) {
@@ -43,75 +53,133 @@ __device__ __forceinline__ unsigned long long make_comp(float v, uint32_t idx) {
          static_cast<unsigned long long>(0xFFFFFFFFu - idx);
 }
 
-// Block-wide radix select over 64-bit keys held in registers (IPT per thread).
-// Returns T such that exactly K of the valid keys are >= T, or 0 when at most K
-// keys are valid (then every valid key is selected).  Keys are distinct.
-template <int IPT>
-__device__ unsigned long long block_threshold(const unsigned long long (&comp)[IPT],
-                                              const bool (&ok)[IPT], int K, int n_ok,
-                                              unsigned* hist, unsigned long long* s_prefix,
-                                              int* s_krem, int* s_done) {
-  if (n_ok <= K) return 0ull;
+constexpr int kChunkThreads = 256;
+constexpr int kCap = 1024;      // candidates gathered above the threshold
+constexpr int kChunkVecs = 2;   // 16-byte vectors per thread per chunk
+constexpr int kMergeItems = 16; // list entries per thread in the merge (nch <= 64)
+
+// Shared memory of block_topk.
+template <int NT>
+struct TopkSmem {
+  unsigned long long bests[NT];
+  unsigned long long cand[kCap];
+  unsigned hist[256];
+  unsigned long long prefix, T;
+  int krem, done, count;
+};
+
+// Rank of key k among n keys of an LDS array (the number of larger keys),
+// reading 2 keys per 16-byte load, 8 in flight.
+__device__ __forceinline__ int count_greater(const unsigned long long* a, int n,
+                                             unsigned long long k) {
+  int rank = 0;
+  int o = 0;
+  for (; o + 8 <= n; o += 8) {
+    ulonglong2 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const ulonglong2*>(a + o + 2 * u);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rank += (v[u].x > k ? 1 : 0) + (v[u].y > k ? 1 : 0);
+  }
+  for (; o < n; ++o) rank += a[o] > k ? 1 : 0;
+  return rank;
+}
+
+// The K (<= 63) largest of the distinct nonzero keys held by the block's
+// threads (IPT per thread, 0 = no key), written to sel[0..63] sorted
+// descending (0 where fewer exist).  The K-th largest per-thread best key T
+// bounds the K-th largest key from below (K threads each hold a key >= T), so
+// only keys >= T are gathered (about K of them) and ranked exactly by counting.
+// If more than kCap keys are >= T (many ties), an exact radix select runs.
+template <int NT, int IPT>
+__device__ void block_topk(const unsigned long long (&items)[IPT], int K, unsigned long long* sel,
+                           TopkSmem<NT>& sm) {
+  const int tid = threadIdx.x, lane = lane_id();
+  unsigned long long best = 0ull;
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) best = items[i] > best ? items[i] : best;
+  for (int i = tid; i < kSlots; i += NT) sel[i] = 0ull;
+  sm.bests[tid] = best;
+  if (tid == 0) {
+    sm.count = 0;
+    sm.T = 0ull;
+  }
+  const int n_ok = __syncthreads_count(best != 0ull);
+  if (K <= 0) return;
+  if (n_ok > K && best != 0ull && count_greater(sm.bests, NT, best) == K - 1) sm.T = best;
+  __syncthreads();
+  const unsigned long long T = sm.T;
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    if (items[i] != 0ull && items[i] >= T) {
+      const int slot = atomicAdd(&sm.count, 1);
+      if (slot < kCap) sm.cand[slot] = items[i];
+    }
+  }
+  __syncthreads();
+  const int C = sm.count;
+  if (C <= kCap) {
+    for (int e = tid; e < C; e += NT) {
+      const unsigned long long k = sm.cand[e];
+      const int rank = count_greater(sm.cand, C, k);
+      if (rank < K) sel[rank] = k;
+    }
+    __syncthreads();
+    return;
+  }
+  // exact radix select over every key
+  __syncthreads();
+  if (tid == 0) sm.count = 0;
   unsigned long long prefix = 0ull, mask = 0ull;
   int krem = K;
   for (int shift = 56; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0u;
+    for (int i = tid; i < 256; i += NT) sm.hist[i] = 0u;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < IPT; ++i)
-      if (ok[i] && (comp[i] & mask) == prefix)
-        atomicAdd(&hist[(comp[i] >> shift) & 255ull], 1u);
+      if (items[i] != 0ull && (items[i] & mask) == prefix)
+        atomicAdd(&sm.hist[(items[i] >> shift) & 255ull], 1u);
     __syncthreads();
-    if (threadIdx.x < kWave) {
-      const int lane = threadIdx.x;
-      unsigned c[4];
+    if (tid < kWave) {
+      unsigned cc[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) c[b] = hist[4 * lane + b];
-      const unsigned s = c[0] + c[1] + c[2] + c[3];
-      unsigned inc = s;
+      for (int b = 0; b < 4; ++b) cc[b] = sm.hist[4 * lane + b];
+      const unsigned sc = cc[0] + cc[1] + cc[2] + cc[3];
+      unsigned inc = sc;
 #pragma unroll
       for (int d = 1; d < kWave; d <<= 1) {
         unsigned o = __shfl_down(inc, d, kWave);
         if (lane + d < kWave) inc += o;
       }
-      unsigned above = inc - s;  // keys in the bins of higher lanes
+      unsigned above = inc - sc;
 #pragma unroll
       for (int b = 3; b >= 0; --b) {
-        if (above < static_cast<unsigned>(krem) && static_cast<unsigned>(krem) <= above + c[b]) {
-          *s_prefix = prefix | (static_cast<unsigned long long>(4 * lane + b) << shift);
-          *s_krem = krem - static_cast<int>(above);
-          *s_done = (c[b] == static_cast<unsigned>(krem) - above) ? 1 : 0;
+        if (above < static_cast<unsigned>(krem) && static_cast<unsigned>(krem) <= above + cc[b]) {
+          sm.prefix = prefix | (static_cast<unsigned long long>(4 * lane + b) << shift);
+          sm.krem = krem - static_cast<int>(above);
+          sm.done = (cc[b] == static_cast<unsigned>(krem) - above) ? 1 : 0;
         }
-        above += c[b];
+        above += cc[b];
       }
     }
     __syncthreads();
-    prefix = *s_prefix;
-    krem = *s_krem;
-    const int done = *s_done;
+    prefix = sm.prefix;
+    krem = sm.krem;
+    const int done = sm.done;
     mask |= 0xFFull << shift;
     __syncthreads();
     if (done) break;
   }
-  return prefix;
-}
-
-// Descending sort of one wavefront's 64 keys (one per lane), bitonic network.
-__device__ __forceinline__ unsigned long long wave_sort_desc(unsigned long long key) {
-  const int lane = lane_id();
 #pragma unroll
-  for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      unsigned long long other = __shfl_xor(key, j, kWave);
-      const bool desc_seg = (lane & k) == 0;
-      const bool lower = (lane & j) == 0;
-      const unsigned long long hi = key > other ? key : other;
-      const unsigned long long lo = key > other ? other : key;
-      key = (lower == desc_seg) ? hi : lo;
+  for (int i = 0; i < IPT; ++i) {
+    if (items[i] != 0ull && items[i] >= prefix) {
+      const int slot = atomicAdd(&sm.count, 1);
+      if (slot < kSlots) sm.cand[slot] = items[i];
     }
   }
-  return key;
+  __syncthreads();
+  if (tid < K) sel[count_greater(sm.cand, K, sm.cand[tid])] = sm.cand[tid];
+  __syncthreads();
 }
 
 template <typename T>
@@ -121,171 +189,148 @@ __device__ __forceinline__ float load_logit<float>(const float* p) { return *p; 
 template <>
 __device__ __forceinline__ float load_logit<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
 
-template <typename T, int IPT>
-__global__ __launch_bounds__(kTopThreads) void lsm_chunk_kernel(
-    const T* __restrict__ logits, int L, int V, int N, int chunk, int nch,
-    float* __restrict__ cstat, unsigned long long* __restrict__ ccand) {
-  __shared__ unsigned hist[256];
-  __shared__ unsigned long long s_prefix;
-  __shared__ int s_krem, s_done, s_count;
-  __shared__ float red[kTopThreads / kWave];
-  __shared__ int redi[kTopThreads / kWave];
-
-  const int j = blockIdx.y, s = blockIdx.z, c = blockIdx.x;
-  const int row = s * L + j;
-  const int K = k_of(N, V, j);
-  const T* base = logits + static_cast<size_t>(row) * V;
-  const int c0 = c * chunk;
-  const int c1 = min(c0 + chunk, V);
-  const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
-
-  float v[IPT];
-  bool ok[IPT];
-  unsigned long long comp[IPT];
-  float mx = -INFINITY;
-  int cnt = 0;
-#pragma unroll
-  for (int i = 0; i < IPT; ++i) {
-    const int idx = c0 + i * kTopThreads + tid;
-    ok[i] = idx < c1;
-    v[i] = ok[i] ? load_logit<T>(base + idx) : -INFINITY;
-    comp[i] = make_comp(v[i], static_cast<uint32_t>(idx));
-    mx = fmaxf(mx, v[i]);
-    cnt += ok[i] ? 1 : 0;
-  }
-  // chunk maximum
-  mx = wave_max(mx);
-  if (lane == 0) red[w] = mx;
-  cnt = wave_sum_i(cnt);
-  if (lane == 0) redi[w] = cnt;
-  __syncthreads();
-  float cmax = red[0];
-  int n_ok = redi[0];
-#pragma unroll
-  for (int i = 1; i < kTopThreads / kWave; ++i) {
-    cmax = fmaxf(cmax, red[i]);
-    n_ok += redi[i];
-  }
-  __syncthreads();
-  // sum exp(z - chunk max), fixed reduction order
-  float sum = 0.f;
-  if (cmax != -INFINITY) {
-#pragma unroll
-    for (int i = 0; i < IPT; ++i) sum += ok[i] ? expf(v[i] - cmax) : 0.f;
-  }
-  sum = wave_sum(sum);
-  if (lane == 0) red[w] = sum;
-  __syncthreads();
-  if (tid == 0) {
-    float t = 0.f;
-    for (int i = 0; i < kTopThreads / kWave; ++i) t += red[i];
-    float* st = cstat + (static_cast<size_t>(row) * nch + c) * 2;
-    st[0] = cmax;
-    st[1] = t;
-  }
-  // the chunk's K best (logit desc, token id asc)
-  unsigned long long* out = ccand + (static_cast<size_t>(row) * nch + c) * kSlots;
-  if (tid < kSlots) out[tid] = 0ull;  // slot 0 = empty
-  if (tid == 0) s_count = 0;
-  __syncthreads();
-  if (K > 0) {
-    const unsigned long long T0 =
-        block_threshold<IPT>(comp, ok, K, n_ok, hist, &s_prefix, &s_krem, &s_done);
-#pragma unroll
-    for (int i = 0; i < IPT; ++i) {
-      if (ok[i] && comp[i] >= T0) {
-        const int slot = atomicAdd(&s_count, 1);
-        out[slot] = comp[i];
-      }
-    }
-  }
-}
-
-template <int IPT>
-__global__ __launch_bounds__(kTopThreads) void lsm_merge_kernel(
-    int L, int V, int N, int nch, const float* __restrict__ cstat,
-    const unsigned long long* __restrict__ ccand, float* __restrict__ top_logq,
-    int32_t* __restrict__ top_id) {
-  __shared__ unsigned hist[256];
-  __shared__ unsigned long long s_prefix;
-  __shared__ int s_krem, s_done, s_count;
-  __shared__ int redi[kTopThreads / kWave];
-  __shared__ float s_M, s_lnS;
+// One chunk of kChunkThreads * kChunkVecs * E logits (E per 16 bytes) of one
+// offset row; every load is issued before any is used.
+template <typename T>
+__global__ __launch_bounds__(kChunkThreads) void lsm_chunk_kernel(
+    const T* __restrict__ logits, int L, int V, int N, int nch,
+    float* __restrict__ cstat, unsigned long long* __restrict__ clist) {
+  constexpr int E = 16 / sizeof(T);
+  constexpr int IPT = kChunkVecs * E;
+  __shared__ float redf[kChunkThreads / kWave];
+  __shared__ float s_M;
+  __shared__ __attribute__((aligned(16))) TopkSmem<kChunkThreads> sm;
   __shared__ unsigned long long sel[kSlots];
 
-  const int j = blockIdx.x, s = blockIdx.y;
-  const int row = s * L + j;
+  const int c = blockIdx.x, j = blockIdx.y, sq = blockIdx.z;
+  const int row = sq * L + j;
   const int K = k_of(N, V, j);
   const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
-  const float* st = cstat + static_cast<size_t>(row) * nch * 2;
-  if (tid == 0) {
-    float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, st[2 * c]);
-    float S = 0.f;
-    if (M != -INFINITY)
-      for (int c = 0; c < nch; ++c)
-        if (st[2 * c + 1] > 0.f) S += st[2 * c + 1] * expf(st[2 * c] - M);
-    s_M = M;
-    s_lnS = logf(S);
-    s_count = 0;
-  }
-  const unsigned long long* cand = ccand + static_cast<size_t>(row) * nch * kSlots;
-  const int total = nch * kSlots;
-  unsigned long long comp[IPT];
-  bool ok[IPT];
-  int cnt = 0;
+  const T* base = logits + static_cast<size_t>(row) * V;
+  const int c0 = c * kChunkThreads * IPT;
+  const bool vec = (V % E) == 0;
+
+  float z[IPT];
+  int idx[IPT];
+  if (vec) {
+    uint4 u[kChunkVecs];
 #pragma unroll
-  for (int i = 0; i < IPT; ++i) {
-    const int e = i * kTopThreads + tid;
-    comp[i] = e < total ? cand[e] : 0ull;
-    ok[i] = comp[i] != 0ull;
-    cnt += ok[i] ? 1 : 0;
-  }
-  cnt = wave_sum_i(cnt);
-  if (lane == 0) redi[w] = cnt;
-  if (tid < kSlots) sel[tid] = 0ull;
-  __syncthreads();
-  int n_ok = 0;
+    for (int v = 0; v < kChunkVecs; ++v) {
+      const int e0 = c0 + (v * kChunkThreads + tid) * E;
+      u[v] = e0 < V ? load_stream(base + e0) : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
-  for (int i = 0; i < kTopThreads / kWave; ++i) n_ok += redi[i];
-  if (K > 0) {
-    const unsigned long long T0 =
-        block_threshold<IPT>(comp, ok, K, n_ok, hist, &s_prefix, &s_krem, &s_done);
+    for (int v = 0; v < kChunkVecs; ++v) {
+      const int e0 = c0 + (v * kChunkThreads + tid) * E;
+      const uint32_t wd[4] = {u[v].x, u[v].y, u[v].z, u[v].w};
 #pragma unroll
-    for (int i = 0; i < IPT; ++i) {
-      if (ok[i] && comp[i] >= T0) {
-        const int slot = atomicAdd(&s_count, 1);
-        sel[slot] = comp[i];
+      for (int e = 0; e < E; ++e) {
+        idx[v * E + e] = e0 + e;
+        float x;
+        if constexpr (sizeof(T) == 2)
+          x = bf16_to_f32(static_cast<uint16_t>(e & 1 ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xFFFF));
+        else
+          x = __uint_as_float(wd[e]);
+        z[v * E + e] = e0 < V ? x : -INFINITY;
       }
     }
+  } else {
+#pragma unroll
+    for (int e = 0; e < IPT; ++e) {
+      idx[e] = c0 + e * kChunkThreads + tid;
+      z[e] = idx[e] < V ? load_logit<T>(base + idx[e]) : -INFINITY;
+    }
+  }
+
+  // running max, rescaled sum of exp, keys (logit desc, token id asc)
+  float m = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < IPT; ++e) m = fmaxf(m, z[e]);
+  float sum = 0.f;
+  unsigned long long keys[IPT];
+#pragma unroll
+  for (int e = 0; e < IPT; ++e) {
+    const bool ok = idx[e] < V;
+    if (ok && z[e] != -INFINITY) sum += expf(z[e] - m);
+    keys[e] = ok ? make_comp(z[e], static_cast<uint32_t>(idx[e])) : 0ull;
+  }
+  const float wm = wave_max(m);
+  if (lane == 0) redf[w] = wm;
+  __syncthreads();
+  if (tid == 0) {
+    float M = redf[0];
+    for (int i = 1; i < kChunkThreads / kWave; ++i) M = fmaxf(M, redf[i]);
+    s_M = M;
   }
   __syncthreads();
+  const float M = s_M;
+  float part = (M == -INFINITY || m == -INFINITY) ? 0.f : sum * expf(m - M);
+  part = wave_sum(part);
+  __syncthreads();
+  if (lane == 0) redf[w] = part;
+  __syncthreads();
+  if (tid == 0) {
+    float S = 0.f;
+    for (int i = 0; i < kChunkThreads / kWave; ++i) S += redf[i];
+    float* st = cstat + (static_cast<size_t>(row) * nch + c) * 2;
+    st[0] = M;
+    st[1] = S;
+  }
+  block_topk<kChunkThreads, IPT>(keys, K, sel, sm);
+  if (tid < kSlots) clist[(static_cast<size_t>(row) * nch + c) * kSlots + tid] = sel[tid];
+}
+
+// Merge of one offset's sorted chunk lists into its K best, as log q.
+__global__ __launch_bounds__(kChunkThreads) void lsm_merge_kernel(
+    int L, int V, int N, int nch, const float* __restrict__ cstat,
+    const unsigned long long* __restrict__ clist, float* __restrict__ top_logq,
+    int32_t* __restrict__ top_id) {
+  __shared__ __attribute__((aligned(16))) TopkSmem<kChunkThreads> sm;
+  __shared__ unsigned long long sel[kSlots];
+  __shared__ float s_M, s_lnS;
+  const int j = blockIdx.x, sq = blockIdx.y;
+  const int row = sq * L + j;
+  const int K = k_of(N, V, j);
+  const int tid = threadIdx.x;
+  const size_t rowc = static_cast<size_t>(row) * nch;
+  const unsigned long long* lists = clist + rowc * kSlots;
+  const int n = nch * kSlots;
+  unsigned long long items[kMergeItems];
+#pragma unroll
+  for (int i = 0; i < kMergeItems; ++i) {
+    const int e = i * kChunkThreads + tid;
+    items[i] = e < n ? lists[e] : 0ull;
+  }
   if (tid < kWave) {
-    const unsigned long long key = wave_sort_desc(sel[tid]);
-    const float M = s_M, lnS = s_lnS;
+    // row maximum and ln(sum exp(z - max)) from the chunk statistics (<= 64)
+    const int c = tid;
+    const float cm = c < nch ? cstat[(rowc + c) * 2] : -INFINITY;
+    const float cs = c < nch ? cstat[(rowc + c) * 2 + 1] : 0.f;
+    const float M = wave_max(cm);
+    float t = (M == -INFINITY || cs <= 0.f) ? 0.f : cs * expf(cm - M);
+    t = wave_sum(t);
+    if (tid == 0) {
+      s_M = M;
+      s_lnS = logf(t);
+    }
+  }
+  block_topk<kChunkThreads, kMergeItems>(items, K, sel, sm);
+  if (tid < kSlots) {
+    const unsigned long long k = sel[tid];
     float lq = -INFINITY;
     int id = -1;
-    if (key != 0ull && tid < K) {
-      const float z = key_float(static_cast<uint32_t>(key >> 32));
-      id = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
-      lq = (M == -INFINITY) ? -INFINITY : (z - M) - lnS;
+    if (k != 0ull) {
+      const float zz = key_float(static_cast<uint32_t>(k >> 32));
+      const float M = s_M;
+      id = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(k));
+      lq = (M == -INFINITY || zz == -INFINITY) ? -INFINITY : (zz - M) - s_lnS;
     }
     top_logq[static_cast<size_t>(row) * kSlots + tid] = lq;
     top_id[static_cast<size_t>(row) * kSlots + tid] = id;
   }
 }
 
-// Frontier key of the best-first search: higher score first, then smaller
-// depth, then the earlier-selected parent, then the better-ranked token.
-__device__ __forceinline__ unsigned long long frontier_key(float score, int depth, int ppop,
-                                                           int rank) {
-  const uint32_t tie = (static_cast<uint32_t>(depth) << 16) |
-                       (static_cast<uint32_t>(ppop + 1) << 8) | static_cast<uint32_t>(rank);
-  return (static_cast<unsigned long long>(float_key(score)) << 32) |
-         static_cast<unsigned long long>(0xFFFFFFFFu - tie);
-}
-
-__global__ __launch_bounds__(kWave) void build_tree_kernel(
+__global__ __launch_bounds__(4 * kWave) void build_tree_kernel(
     const float* __restrict__ top_logq, const int32_t* __restrict__ top_id,
     const int32_t* __restrict__ root_token, int L, int V, int N, int32_t* __restrict__ parent,
     int32_t* __restrict__ depth_out, int32_t* __restrict__ token_out,
@@ -293,80 +338,87 @@ __global__ __launch_bounds__(kWave) void build_tree_kernel(
     int32_t* __restrict__ n_valid_out) {
   __shared__ float lq[GLANCE_MAX_L][kSlots];
   __shared__ int tk[GLANCE_MAX_L][kSlots];
-  __shared__ float pop_score[kSlots];
-  __shared__ int row_of_pop[kSlots];
+  __shared__ int row_of_lane[kSlots];
   __shared__ unsigned long long anc_row[kSlots];
 
-  const int s = blockIdx.x, lane = lane_id();
-  const int R = N + 1;
-  for (int j = 0; j < L; ++j) {
-    lq[j][lane] = top_logq[(static_cast<size_t>(s) * L + j) * kSlots + lane];
-    tk[j][lane] = top_id[(static_cast<size_t>(s) * L + j) * kSlots + lane];
+  const int s = blockIdx.x, lane = lane_id(), wv = threadIdx.x / kWave;
+
+  // the ranked lists of every offset
+  {
+    float vq[GLANCE_MAX_L * kSlots / (4 * kWave)];
+    int vt[GLANCE_MAX_L * kSlots / (4 * kWave)];
+#pragma unroll
+    for (int u = 0; u < GLANCE_MAX_L * kSlots / (4 * kWave); ++u) {
+      const int e = u * 4 * kWave + threadIdx.x;
+      vq[u] = e < L * kSlots ? top_logq[static_cast<size_t>(s) * L * kSlots + e] : -INFINITY;
+      vt[u] = e < L * kSlots ? top_id[static_cast<size_t>(s) * L * kSlots + e] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < GLANCE_MAX_L * kSlots / (4 * kWave); ++u) {
+      const int e = u * 4 * kWave + threadIdx.x;
+      lq[e / kSlots][e % kSlots] = vq[u];
+      tk[e / kSlots][e % kSlots] = vt[u];
+    }
   }
   __syncthreads();
+  if (wv != 0) return;  // the rest is one wavefront; no block barrier follows
 
-  // ---- best-first selection: lane holds one frontier prefix (key 0 = empty)
-  bool has = false;
-  float f_score = 0.f;
-  int f_depth = 0, f_ppop = -1, f_rank = 0;
-  if (lane == 0 && N > 0 && k_of(N, V, 0) > 0 && lq[0][0] != -INFINITY) {
-    has = true;
-    f_score = 0.f + lq[0][0];
-    f_depth = 1;
-  }
-  // popped node fields (lane i keeps node i)
+  // ---- best-first selection.  Lane 0 is the root, lane i the i-th selected
+  // node; each lane offers the best not-yet-selected child of its node (the
+  // next entry of the next offset's ranked list).  Equal scores: smaller depth,
+  // then the earlier-selected parent (smaller lane); one offer per lane.
+  const int R = N + 1;
+  const float fq = lane < L ? lq[lane][0] : -INFINITY;  // first entry of each offset
   float n_score = 0.f;
-  int n_depth = 0, n_ppop = -1, n_token = -1;
+  int n_depth = 0, n_par = -1, n_rank = 0, n_next = 0;
+  float c_score = 0.f, nx_q = -INFINITY;
+  uint32_t c_hi = 0u;
+  // the candidate is child n_next of this node with log q `q`; prefetch the next one
+  auto offer = [&](float q) {
+    c_hi = 0u;
+    if (n_depth < L && n_next < k_of(N, V, n_depth) && q != -INFINITY) {
+      c_score = n_score + q;
+      c_hi = float_key(c_score);
+    }
+    const int nn = n_next + 1;
+    nx_q = (n_depth < L && nn < kSlots) ? lq[n_depth][nn] : -INFINITY;
+  };
+  if (lane == 0) offer(fq);
   int n_pop = 0;
-  for (int i = 0; i < N; ++i) {
-    const unsigned long long key = has ? frontier_key(f_score, f_depth, f_ppop, f_rank) : 0ull;
-    const unsigned long long best = wave_max_u64(key);
-    if (best == 0ull) break;
-    const unsigned long long win_mask = __ballot(key == best);
-    const int win = __ffsll(static_cast<long long>(win_mask)) - 1;
-    const float w_score = __shfl(f_score, win, kWave);
-    const int w_depth = __shfl(f_depth, win, kWave);
-    const int w_ppop = __shfl(f_ppop, win, kWave);
-    const int w_rank = __shfl(f_rank, win, kWave);
-    const int w_token = tk[w_depth - 1][w_rank];
+  for (int i = 1; i <= N; ++i) {
+    const uint32_t mh = wave_umax(c_hi);
+    if (mh == 0u) break;
+    unsigned long long cm = __ballot(c_hi == mh);
+    if (__popcll(cm) > 1) {  // equal scores: the smallest child depth, then the lowest lane
+      const uint32_t lo = (c_hi == mh) ? ~static_cast<uint32_t>(n_depth) : 0u;
+      const uint32_t ml = wave_umax(lo);
+      cm = __ballot(c_hi == mh && ~static_cast<uint32_t>(n_depth) == ml);
+    }
+    const int p = __ffsll(static_cast<long long>(cm)) - 1;
+    const float w_score = readlane_f(c_score, p);
+    const int w_depth = readlane_i(n_depth, p) + 1;
+    const int w_rank = readlane_i(n_next, p);
+    const float q0 = readlane_f(fq, w_depth < L ? w_depth : 0);
     if (lane == i) {
       n_score = w_score;
       n_depth = w_depth;
-      n_ppop = w_ppop;
-      n_token = w_token;
-      pop_score[i] = w_score;
+      n_par = p;
+      n_rank = w_rank;
+      n_next = 0;
+      offer(w_depth < L ? q0 : -INFINITY);
     }
-    // the winner's slot takes its next sibling
-    if (lane == win) {
-      const int r2 = w_rank + 1;
-      const int jd = w_depth - 1;
-      if (r2 < k_of(N, V, jd) && lq[jd][r2] != -INFINITY) {
-        const float ps = (w_ppop < 0) ? 0.f : pop_score[w_ppop];
-        f_score = ps + lq[jd][r2];
-        f_rank = r2;
-      } else {
-        has = false;
-      }
+    if (lane == p) {
+      ++n_next;
+      offer(nx_q);
     }
-    // the popped node's first child takes the lowest empty slot
-    if (w_depth < L && k_of(N, V, w_depth) > 0 && lq[w_depth][0] != -INFINITY) {
-      const unsigned long long empty = __ballot(!has);
-      const int tgt = __ffsll(static_cast<long long>(empty)) - 1;
-      if (lane == tgt) {
-        has = true;
-        f_score = w_score + lq[w_depth][0];
-        f_depth = w_depth + 1;
-        f_ppop = i;
-        f_rank = 0;
-      }
-    }
-    __syncthreads();
-    n_pop = i + 1;
+    n_pop = i;
   }
 
   // ---- breadth-first layout: rows by (depth, parent row, token id)
+  const int n_token = (lane >= 1 && lane <= n_pop) ? tk[n_depth - 1][n_rank] : -1;
   const size_t ob = static_cast<size_t>(s) * R;
   if (lane == 0) {
+    row_of_lane[0] = 0;
     anc_row[0] = 1ull;
     parent[ob] = -1;
     depth_out[ob] = 0;
@@ -375,26 +427,24 @@ __global__ __launch_bounds__(kWave) void build_tree_kernel(
     score_out[ob] = 0.f;
     n_valid_out[s] = n_pop + 1;
   }
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();  // one wave: LDS is in order
   int base = 1;
   for (int d = 1; d <= L; ++d) {
-    const bool in_level = lane < n_pop && n_depth == d;
+    const bool in_level = lane >= 1 && lane <= n_pop && n_depth == d;
     const unsigned long long lvl = __ballot(in_level);
     if (lvl == 0ull) break;
-    const int prow = in_level ? (n_ppop < 0 ? 0 : row_of_pop[n_ppop]) : 0;
-    const unsigned long long mykey =
-        (static_cast<unsigned long long>(prow) << 32) | static_cast<uint32_t>(n_token);
+    const int prow = in_level ? row_of_lane[n_par] : 0;
     int rank = 0;
-    unsigned long long m = lvl;
-    while (m) {
-      const int jl = __ffsll(static_cast<long long>(m)) - 1;
-      m &= m - 1;
-      const unsigned long long other = __shfl(mykey, jl, kWave);
-      rank += (other < mykey) ? 1 : 0;
+    unsigned long long mm = lvl;
+    while (mm) {
+      const int jl = __ffsll(static_cast<long long>(mm)) - 1;
+      mm &= mm - 1;
+      const int op = readlane_i(prow, jl), ot = readlane_i(n_token, jl);
+      rank += (op < prow || (op == prow && ot < n_token)) ? 1 : 0;
     }
     if (in_level) {
       const int r = base + rank;
-      row_of_pop[lane] = r;
+      row_of_lane[lane] = r;
       const unsigned long long a = anc_row[prow] | (1ull << r);
       anc_row[r] = a;
       parent[ob + r] = prow;
@@ -404,9 +454,8 @@ __global__ __launch_bounds__(kWave) void build_tree_kernel(
       score_out[ob + r] = n_score;
     }
     base += __popcll(lvl);
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();  // one wave: LDS is in order
   }
-  // padding rows
   for (int r = n_pop + 1 + lane; r < R; r += kWave) {
     parent[ob + r] = -1;
     depth_out[ob + r] = 0;
@@ -421,28 +470,18 @@ __global__ __launch_bounds__(kWave) void build_tree_kernel(
 // Host side -------------------------------------------------------------------
 TreeWs tree_ws_layout(int nseq, int L, int V) {
   TreeWs w;
-  // chunk size: 4096 logits (16 per thread) while V <= 64 chunks of it, else
-  // 16384 (64 per thread); V <= 2^20 keeps the chunk count <= 64.
-  if (V <= 64 * 4096) {
-    w.chunk = 4096;
-    w.ipt = 16;
-  } else {
-    w.chunk = 16384;
-    w.ipt = 64;
-  }
+  // chunks of 256 threads x 2 vectors of 16 bytes: 4096 bf16 or 2048 fp32
+  // logits; the merge takes up to 64 chunks per row (V <= 2^18 bf16, 2^17 fp32)
+  w.chunk = kChunkThreads * kChunkVecs * 4;
   w.nch = (V + w.chunk - 1) / w.chunk;
-  const size_t rows = static_cast<size_t>(nseq) * L;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    size_t o = off;
-    off += (bytes + 255) & ~static_cast<size_t>(255);
-    return o;
-  };
-  w.off_cstat = take(rows * w.nch * 2 * sizeof(float));
-  w.off_ccand = take(rows * w.nch * kSlots * sizeof(unsigned long long));
-  w.off_logq = take(rows * kSlots * sizeof(float));
-  w.off_id = take(rows * kSlots * sizeof(int32_t));
-  w.bytes = off;
+  const size_t r = static_cast<size_t>(nseq) * L;
+  auto up = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
+  const int nch_max = w.nch;
+  w.off_cstat = 0;
+  w.off_clist = up(r * nch_max * 2 * sizeof(float));
+  w.off_logq = w.off_clist + up(r * nch_max * kSlots * sizeof(unsigned long long));
+  w.off_id = w.off_logq + up(r * kSlots * sizeof(float));
+  w.bytes = w.off_id + up(r * kSlots * sizeof(int32_t));
   return w;
 }
 
@@ -453,28 +492,24 @@ glance_status launch_build_tree(const void* logits, int dtype, const int32_t* ro
   const TreeWs w = tree_ws_layout(nseq, L, V);
   char* base = static_cast<char*>(ws);
   float* cstat = reinterpret_cast<float*>(base + w.off_cstat);
-  unsigned long long* ccand = reinterpret_cast<unsigned long long*>(base + w.off_ccand);
+  unsigned long long* clist = reinterpret_cast<unsigned long long*>(base + w.off_clist);
+  // chunk size in logits: 256 threads x 2 x 16 bytes
+  const int E = dtype == GLANCE_BF16 ? 8 : 4;
+  const int nch = (V + kChunkThreads * kChunkVecs * E - 1) / (kChunkThreads * kChunkVecs * E);
+  dim3 ga(nch, L, nseq);
+  if (dtype == GLANCE_BF16)
+    lsm_chunk_kernel<uint16_t><<<ga, kChunkThreads, 0, st>>>(static_cast<const uint16_t*>(logits), L, V, N,
+                                                             nch, cstat, clist);
+  else
+    lsm_chunk_kernel<float><<<ga, kChunkThreads, 0, st>>>(static_cast<const float*>(logits), L, V, N, nch,
+                                                          cstat, clist);
+  GLANCE_LAUNCH_CHECK();
   float* logq = reinterpret_cast<float*>(base + w.off_logq);
   int32_t* id = reinterpret_cast<int32_t*>(base + w.off_id);
-  dim3 ga(w.nch, L, nseq);
-  if (dtype == GLANCE_BF16) {
-    const uint16_t* z = static_cast<const uint16_t*>(logits);
-    if (w.ipt == 16)
-      lsm_chunk_kernel<uint16_t, 16><<<ga, kTopThreads, 0, st>>>(z, L, V, N, w.chunk, w.nch, cstat, ccand);
-    else
-      lsm_chunk_kernel<uint16_t, 64><<<ga, kTopThreads, 0, st>>>(z, L, V, N, w.chunk, w.nch, cstat, ccand);
-  } else {
-    const float* z = static_cast<const float*>(logits);
-    if (w.ipt == 16)
-      lsm_chunk_kernel<float, 16><<<ga, kTopThreads, 0, st>>>(z, L, V, N, w.chunk, w.nch, cstat, ccand);
-    else
-      lsm_chunk_kernel<float, 64><<<ga, kTopThreads, 0, st>>>(z, L, V, N, w.chunk, w.nch, cstat, ccand);
-  }
+  lsm_merge_kernel<<<dim3(L, nseq), kChunkThreads, 0, st>>>(L, V, N, nch, cstat, clist, logq, id);
   GLANCE_LAUNCH_CHECK();
-  lsm_merge_kernel<16><<<dim3(L, nseq), kTopThreads, 0, st>>>(L, V, N, w.nch, cstat, ccand, logq, id);
-  GLANCE_LAUNCH_CHECK();
-  build_tree_kernel<<<nseq, kWave, 0, st>>>(logq, id, root, L, V, N, parent, depth, token, anc,
-                                            score, n_valid);
+  build_tree_kernel<<<nseq, 4 * kWave, 0, st>>>(logq, id, root, L, V, N, parent, depth, token, anc,
+                                                score, n_valid);
   GLANCE_LAUNCH_CHECK();
   return GLANCE_OK;
 }
