@@ -146,7 +146,12 @@ template <int EPI, int B, int S, int DEPTH>
 __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a, int NB, int NG,
                                                                  int nWG, int nMT) {
   constexpr int GPW = 4 / S;  // block groups per work-group
+  // The LM head streams its weights with full-line non-temporal loads and
+  // transposes them to the MFMA layout through a per-wave LDS tile; the
+  // projections load the MFMA layout directly.
+  constexpr bool CW = EPI == EPI_HEAD;
   __shared__ __attribute__((aligned(16))) uint16_t xs[2 * S * kXS];
+  __shared__ __attribute__((aligned(16))) uint16_t wtile[CW ? 4 * B * 16 * kXP : 8];
   __shared__ HeadPart hred[4][kTileM];
 
   const int bid = blockIdx.x;
@@ -161,18 +166,25 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a, int
   const int Ks = a.K / S;
   const int kbase = q * Ks;
   const int nck = Ks / kKc;
+  uint16_t* wt = wtile + (CW ? w * B * 16 * kXP : 0);
 
-  // this wave's blocks
+  // this wave's blocks.  Weight load i of a block (i = 0, 1) per chunk: in the
+  // MFMA operand layout, rows lr at k = 32 i + 8 lg; coalesced (CW), rows
+  // 8 i + l/8 at k = 8 (l%8), i.e. eight full 128-byte row segments per load.
   int blk[B];
   bool bval[B];
-  const uint16_t* wp[B];
+  const uint16_t* wp[B][2];
 #pragma unroll
   for (int t = 0; t < B; ++t) {
     blk[t] = G + t * NG;
     bval[t] = G < NG && blk[t] < NB;
-    int row = bval[t] ? block_row<EPI>(a, blk[t], lr) : 0;
-    if (row > a.N - 1) row = a.N - 1;
-    wp[t] = w_row_ptr(a, row) + kbase + 8 * lg;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ri = CW ? 8 * i + (l >> 3) : lr;
+      int row = bval[t] ? block_row<EPI>(a, blk[t], ri) : 0;
+      if (row > a.N - 1) row = a.N - 1;
+      wp[t][i] = w_row_ptr(a, row) + kbase + (CW ? 8 * (l & 7) : 32 * i + 8 * lg);
+    }
   }
 
   // activation rows this thread stages: S sub-chunks x 64 rows x 8 pieces of 16 B
@@ -192,46 +204,66 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a, int
   for (int t = 0; t < B; ++t)
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) acc[t][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // weight ring of DEPTH + 1 chunk slots: the loads of chunk c + DEPTH are issued
-  // before chunk c waits on the LDS barrier, so they overlap both
+  // Rings of DEPTH + 1 chunk slots in registers for the weights and for the
+  // activation chunks on their way to LDS.  Iteration c issues the activation
+  // loads of chunk c + DEPTH, then the weight loads of chunk c + DEPTH, and at
+  // its end stores chunk c + 1 to the other LDS stage.  Loads complete in issue
+  // order, so every wait is for data that is due anyway: DEPTH chunks stay in
+  // flight through the barriers.
   constexpr int RS = DEPTH + 1;
+  static_assert(RS % 2 == 0, "ring slots and LDS stages must unroll together");
   uint4 wbuf[RS][B][2];
+  uint4 xbuf[RS][2 * S];
   auto wload = [&](int c, uint4 (&dst)[B][2]) {
 #pragma unroll
     for (int t = 0; t < B; ++t)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) dst[t][s] = *reinterpret_cast<const uint4*>(wp[t] + c * kKc + s * 32);
+      for (int i = 0; i < 2; ++i) {
+        if constexpr (CW)
+          dst[t][i] = load_stream(wp[t][i] + c * kKc);
+        else
+          dst[t][i] = *reinterpret_cast<const uint4*>(wp[t][i] + c * kKc);
+      }
+  };
+  auto xload = [&](int c, uint4 (&dst)[2 * S]) {
+#pragma unroll
+    for (int e = 0; e < 2 * S; ++e) {
+      dst[e] = make_uint4(0, 0, 0, 0);
+      if (xr[e]) dst[e] = *reinterpret_cast<const uint4*>(xr[e] + xoff[e] + c * kKc);
+    }
   };
 
-  // prologue: X chunk 0 -> LDS stage 0, W chunks 0 .. DEPTH-1 -> registers
+  // prologue: X chunk 0 -> LDS stage 0; X chunks 1 .. DEPTH-1 and W chunks
+  // 0 .. DEPTH-1 -> registers, each W chunk after the X chunk due before it
+  xload(0, xbuf[0]);
 #pragma unroll
-  for (int e = 0; e < 2 * S; ++e) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (xr[e]) v = *reinterpret_cast<const uint4*>(xr[e] + xoff[e]);
-    *reinterpret_cast<uint4*>(&xs[xlds[e]]) = v;
-  }
+  for (int e = 0; e < 2 * S; ++e) *reinterpret_cast<uint4*>(&xs[xlds[e]]) = xbuf[0][e];
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
+  for (int d = 0; d < DEPTH; ++d) {
+    if (d + 1 < DEPTH && d + 1 < nck) xload(d + 1, xbuf[d + 1]);
     if (d < nck) wload(d, wbuf[d]);
+  }
 
   for (int c0 = 0; c0 < nck; c0 += RS) {
 #pragma unroll
     for (int u = 0; u < RS; ++u) {
       const int c = c0 + u;
       if (c < nck) {
-        if (c + DEPTH < nck) wload(c + DEPTH, wbuf[(u + DEPTH) % RS]);
-        const int st = c & 1;
-        const bool more = c + 1 < nck;
-        uint4 xn[2 * S];
-        if (more) {
+        if (c + DEPTH < nck) {
+          xload(c + DEPTH, xbuf[(u + DEPTH) % RS]);
+          wload(c + DEPTH, wbuf[(u + DEPTH) % RS]);
+        }
+        if constexpr (CW) {
+          // this wave's weight chunk into its LDS tile, row-major (same-wave
+          // LDS accesses complete in order, so no barrier is needed)
 #pragma unroll
-          for (int e = 0; e < 2 * S; ++e) {
-            xn[e] = make_uint4(0, 0, 0, 0);
-            if (xr[e]) xn[e] = *reinterpret_cast<const uint4*>(xr[e] + xoff[e] + (c + 1) * kKc);
-          }
+          for (int t = 0; t < B; ++t)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+              *reinterpret_cast<uint4*>(wt + (t * 16 + 8 * i + (l >> 3)) * kXP + 8 * (l & 7)) = wbuf[u][t][i];
         }
         __syncthreads();
-        const uint16_t* xq = xs + (st * S + q) * kXS;
+        const uint16_t* xq = xs + ((u & 1) * S + q) * kXS;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           bf16x8 bx[4];
@@ -240,16 +272,20 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a, int
             bx[mb] = *reinterpret_cast<const bf16x8*>(xq + (mb * 16 + lr) * kXP + s * 32 + 8 * lg);
 #pragma unroll
           for (int t = 0; t < B; ++t) {
-            const bf16x8 av = __builtin_bit_cast(bf16x8, wbuf[u][t][s]);
+            bf16x8 av;
+            if constexpr (CW)
+              av = *reinterpret_cast<const bf16x8*>(wt + (t * 16 + lr) * kXP + s * 32 + 8 * lg);
+            else
+              av = __builtin_bit_cast(bf16x8, wbuf[u][t][s]);
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
               acc[t][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bx[mb], acc[t][mb], 0, 0, 0);
           }
         }
-        if (more) {
+        if (c + 1 < nck) {
 #pragma unroll
           for (int e = 0; e < 2 * S; ++e)
-            *reinterpret_cast<uint4*>(&xs[(st ^ 1) * S * kXS + xlds[e]]) = xn[e];
+            *reinterpret_cast<uint4*>(&xs[((u + 1) & 1) * S * kXS + xlds[e]]) = xbuf[(u + 1) % RS][e];
         }
       }
     }
