@@ -100,14 +100,24 @@ __device__ __forceinline__ HeadPart shfl_part(const HeadPart& p, int src) {
 }
 
 
-__device__ __forceinline__ const uint16_t* x_row_ptr(const GemmArgs& a, int m) {
-  if (m >= a.M) return nullptr;
-  if (a.gather) {
-    const int tok = a.gather[m];
-    if (tok < 0) return nullptr;
-    return static_cast<const uint16_t*>(a.x) + static_cast<size_t>(tok) * a.K;
+// Activation row m of X (a gathered embedding row when a.gather is set).  Rows
+// past M and gathered rows with token < 0 are zero: they get row 0's address
+// (always valid) and a zero mask, so their loads need no branch.
+__device__ __forceinline__ void x_row_masked(const GemmArgs& a, int m, const uint16_t*& p,
+                                             uint32_t& mask) {
+  int row = m;
+  bool ok = m < a.M;
+  if (ok && a.gather) {
+    row = a.gather[m];
+    ok = row >= 0;
   }
-  return static_cast<const uint16_t*>(a.x) + static_cast<size_t>(m) * a.K;
+  if (!ok) row = 0;
+  p = static_cast<const uint16_t*>(a.x) + static_cast<size_t>(row) * a.K;
+  mask = ok ? 0xFFFFFFFFu : 0u;
+}
+
+__device__ __forceinline__ uint4 mask4(uint4 v, uint32_t mask) {
+  return make_uint4(v.x & mask, v.y & mask, v.z & mask, v.w & mask);
 }
 
 // W row of row i (0..15) of block b.  For EPI_QKV the q and k blocks pair head
@@ -135,23 +145,23 @@ __device__ __forceinline__ const uint16_t* w_row_ptr(const GemmArgs& a, int row)
   return static_cast<const uint16_t*>(a.w.w[sidx]) + static_cast<size_t>(row - start) * a.K;
 }
 
-__device__ __forceinline__ uint2 pack4_bf16(float x0, float x1, float x2, float x3) {
-  uint2 u;
-  u.x = static_cast<uint32_t>(f32_to_bf16(x0)) | (static_cast<uint32_t>(f32_to_bf16(x1)) << 16);
-  u.y = static_cast<uint32_t>(f32_to_bf16(x2)) | (static_cast<uint32_t>(f32_to_bf16(x3)) << 16);
-  return u;
-}
-
-template <int EPI, int B, int S, int DEPTH>
-__global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a, int NB, int NG,
+// ------------------------------------------------------------------ LM head
+// Work-group = 4 waves over one 64-row activation tile; wave G owns blocks
+// G, G + NG, ... (B of them).  Each weight chunk (64 deep) of a block is loaded
+// with two full-line non-temporal loads (rows 8 i + l/8, k = 8 (l%8)), written
+// to the wave's own LDS tile and read back in the MFMA operand layout (row
+// l%16, k = 32 s + 8 (l/16)).  Same-wave LDS accesses complete in order, so the
+// tile needs no barrier.  The activation chunk is staged in LDS for all waves.
+// Rings of DEPTH + 1 chunk slots in registers hold the weights and the
+// activation chunks on their way to LDS: iteration c issues the activation and
+// then the weight loads of chunk c + DEPTH and at its end stores activation
+// chunk c + 1 to the other LDS stage.  Loads complete in issue order, so every
+// wait is for data that is due anyway.
+template <int B, int DEPTH>
+__global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int NB, int NG,
                                                                  int nWG, int nMT) {
-  constexpr int GPW = 4 / S;  // block groups per work-group
-  // The LM head streams its weights with full-line non-temporal loads and
-  // transposes them to the MFMA layout through a per-wave LDS tile; the
-  // projections load the MFMA layout directly.
-  constexpr bool CW = EPI == EPI_HEAD;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2 * S * kXS];
-  __shared__ __attribute__((aligned(16))) uint16_t wtile[CW ? 4 * B * 16 * kXP : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2 * kXS];
+  __shared__ __attribute__((aligned(16))) uint16_t wtile[4 * B * 16 * kXP];
   __shared__ HeadPart hred[4][kTileM];
 
   const int bid = blockIdx.x;
@@ -161,16 +171,10 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a, int
   if (wg >= nWG) return;
   const int m0 = mt * kTileM;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
-  const int q = w % S, gi = w / S;
-  const int G = wg * GPW + gi;
-  const int Ks = a.K / S;
-  const int kbase = q * Ks;
-  const int nck = Ks / kKc;
-  uint16_t* wt = wtile + (CW ? w * B * 16 * kXP : 0);
+  const int G = wg * 4 + w;
+  const int nck = a.K / kKc;
+  uint16_t* wt = wtile + w * B * 16 * kXP;
 
-  // this wave's blocks.  Weight load i of a block (i = 0, 1) per chunk: in the
-  // MFMA operand layout, rows lr at k = 32 i + 8 lg; coalesced (CW), rows
-  // 8 i + l/8 at k = 8 (l%8), i.e. eight full 128-byte row segments per load.
   int blk[B];
   bool bval[B];
   const uint16_t* wp[B][2];
@@ -180,23 +184,22 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a, int
     bval[t] = G < NG && blk[t] < NB;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int ri = CW ? 8 * i + (l >> 3) : lr;
-      int row = bval[t] ? block_row<EPI>(a, blk[t], ri) : 0;
+      int row = bval[t] ? blk[t] * 16 + 8 * i + (l >> 3) : 0;
       if (row > a.N - 1) row = a.N - 1;
-      wp[t][i] = w_row_ptr(a, row) + kbase + (CW ? 8 * (l & 7) : 32 * i + 8 * lg);
+      wp[t][i] = w_row_ptr(a, row) + 8 * (l & 7);
     }
   }
-
-  // activation rows this thread stages: S sub-chunks x 64 rows x 8 pieces of 16 B
-  const uint16_t* xr[2 * S];
-  int xoff[2 * S], xlds[2 * S];
+  // activation pieces this thread stages: 64 rows x 8 pieces of 16 B per chunk
+  const uint16_t* xr[2];
+  uint32_t xm[2];
+  int xlds[2];
 #pragma unroll
-  for (int e = 0; e < 2 * S; ++e) {
+  for (int e = 0; e < 2; ++e) {
     const int idx = e * kGThreads + tid;
-    const int sub = idx >> 9, r = (idx >> 3) & 63, cc = (idx & 7) * 8;
-    xr[e] = x_row_ptr(a, m0 + r);
-    xoff[e] = sub * Ks + cc;
-    xlds[e] = sub * kXS + r * kXP + cc;
+    const int r = idx >> 3, cc = (idx & 7) * 8;
+    x_row_masked(a, m0 + r, xr[e], xm[e]);
+    xr[e] += cc;
+    xlds[e] = r * kXP + cc;
   }
 
   f32x4 acc[B][4];
@@ -204,66 +207,48 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a, int
   for (int t = 0; t < B; ++t)
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) acc[t][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Rings of DEPTH + 1 chunk slots in registers for the weights and for the
-  // activation chunks on their way to LDS.  Iteration c issues the activation
-  // loads of chunk c + DEPTH, then the weight loads of chunk c + DEPTH, and at
-  // its end stores chunk c + 1 to the other LDS stage.  Loads complete in issue
-  // order, so every wait is for data that is due anyway: DEPTH chunks stay in
-  // flight through the barriers.
   constexpr int RS = DEPTH + 1;
   static_assert(RS % 2 == 0, "ring slots and LDS stages must unroll together");
   uint4 wbuf[RS][B][2];
-  uint4 xbuf[RS][2 * S];
+  uint4 xbuf[RS][2];
   auto wload = [&](int c, uint4 (&dst)[B][2]) {
 #pragma unroll
     for (int t = 0; t < B; ++t)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if constexpr (CW)
-          dst[t][i] = load_stream(wp[t][i] + c * kKc);
-        else
-          dst[t][i] = *reinterpret_cast<const uint4*>(wp[t][i] + c * kKc);
-      }
+      for (int i = 0; i < 2; ++i) dst[t][i] = load_stream(wp[t][i] + c * kKc);
   };
-  auto xload = [&](int c, uint4 (&dst)[2 * S]) {
+  // raw loads; the row mask is applied when the chunk is written to LDS
+  auto xload = [&](int c, uint4 (&dst)[2]) {
 #pragma unroll
-    for (int e = 0; e < 2 * S; ++e) {
-      dst[e] = make_uint4(0, 0, 0, 0);
-      if (xr[e]) dst[e] = *reinterpret_cast<const uint4*>(xr[e] + xoff[e] + c * kKc);
-    }
+    for (int e = 0; e < 2; ++e) dst[e] = *reinterpret_cast<const uint4*>(xr[e] + c * kKc);
   };
 
-  // prologue: X chunk 0 -> LDS stage 0; X chunks 1 .. DEPTH-1 and W chunks
-  // 0 .. DEPTH-1 -> registers, each W chunk after the X chunk due before it
+  // nck is a multiple of RS; loads past the last chunk are clamped to it, so no
+  // load is conditional (a conditional load would make the compiler's wait
+  // counts conservative and drain the ring every chunk)
   xload(0, xbuf[0]);
 #pragma unroll
-  for (int e = 0; e < 2 * S; ++e) *reinterpret_cast<uint4*>(&xs[xlds[e]]) = xbuf[0][e];
+  for (int e = 0; e < 2; ++e) *reinterpret_cast<uint4*>(&xs[xlds[e]]) = mask4(xbuf[0][e], xm[e]);
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) {
-    if (d + 1 < DEPTH && d + 1 < nck) xload(d + 1, xbuf[d + 1]);
-    if (d < nck) wload(d, wbuf[d]);
+    if (d + 1 < DEPTH) xload(min(d + 1, nck - 1), xbuf[d + 1]);
+    wload(min(d, nck - 1), wbuf[d]);
   }
-
   for (int c0 = 0; c0 < nck; c0 += RS) {
 #pragma unroll
     for (int u = 0; u < RS; ++u) {
       const int c = c0 + u;
-      if (c < nck) {
-        if (c + DEPTH < nck) {
-          xload(c + DEPTH, xbuf[(u + DEPTH) % RS]);
-          wload(c + DEPTH, wbuf[(u + DEPTH) % RS]);
-        }
-        if constexpr (CW) {
-          // this wave's weight chunk into its LDS tile, row-major (same-wave
-          // LDS accesses complete in order, so no barrier is needed)
+      {
+        const int cn = min(c + DEPTH, nck - 1);
+        xload(cn, xbuf[(u + DEPTH) % RS]);
+        wload(cn, wbuf[(u + DEPTH) % RS]);
 #pragma unroll
-          for (int t = 0; t < B; ++t)
+        for (int t = 0; t < B; ++t)
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-              *reinterpret_cast<uint4*>(wt + (t * 16 + 8 * i + (l >> 3)) * kXP + 8 * (l & 7)) = wbuf[u][t][i];
-        }
+          for (int i = 0; i < 2; ++i)
+            *reinterpret_cast<uint4*>(wt + (t * 16 + 8 * i + (l >> 3)) * kXP + 8 * (l & 7)) = wbuf[u][t][i];
         __syncthreads();
-        const uint16_t* xq = xs + ((u & 1) * S + q) * kXS;
+        const uint16_t* xq = xs + (u & 1) * kXS;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           bf16x8 bx[4];
@@ -272,150 +257,250 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a, int
             bx[mb] = *reinterpret_cast<const bf16x8*>(xq + (mb * 16 + lr) * kXP + s * 32 + 8 * lg);
 #pragma unroll
           for (int t = 0; t < B; ++t) {
-            bf16x8 av;
-            if constexpr (CW)
-              av = *reinterpret_cast<const bf16x8*>(wt + (t * 16 + lr) * kXP + s * 32 + 8 * lg);
-            else
-              av = __builtin_bit_cast(bf16x8, wbuf[u][t][s]);
+            const bf16x8 av = *reinterpret_cast<const bf16x8*>(wt + (t * 16 + lr) * kXP + s * 32 + 8 * lg);
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
               acc[t][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bx[mb], acc[t][mb], 0, 0, 0);
           }
         }
-        if (c + 1 < nck) {
+        // (after the last chunk this stores a clamped copy nobody reads)
 #pragma unroll
-          for (int e = 0; e < 2 * S; ++e)
-            *reinterpret_cast<uint4*>(&xs[((u + 1) & 1) * S * kXS + xlds[e]]) = xbuf[(u + 1) % RS][e];
-        }
+        for (int e = 0; e < 2; ++e)
+          *reinterpret_cast<uint4*>(&xs[((u + 1) & 1) * kXS + xlds[e]]) = mask4(xbuf[(u + 1) % RS][e], xm[e]);
       }
     }
   }
 
-  // ------------------------------------------------------------------ epilogues
-  // acc[t][mb][v]: row i = 4 lg + v of block blk[t], activation row m0 + 16 mb + lr.
-  if constexpr (EPI == EPI_HEAD) {
-    HeadPart hp[4];
+  // acc[t][mb][v]: vocabulary row blk[t]*16 + 4 lg + v, activation row m0 + 16 mb + lr
+  HeadPart hp[4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) hp[mb] = head_empty();
+  for (int mb = 0; mb < 4; ++mb) hp[mb] = head_empty();
 #pragma unroll
-    for (int t = 0; t < B; ++t) {
-      if (!bval[t]) continue;
+  for (int t = 0; t < B; ++t) {
+    if (!bval[t]) continue;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int n = blk[t] * 16 + 4 * lg + v;
-        if (n < a.N) {
+    for (int v = 0; v < 4; ++v) {
+      const int n = blk[t] * 16 + 4 * lg + v;
+      if (n < a.N) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          hp[mb] = head_combine(hp[mb], head_elem(acc[t][mb][v], n));
+          const int m = m0 + mb * 16 + lr;
+          if (a.logits && m < a.M) a.logits[static_cast<size_t>(m) * a.N + n] = acc[t][mb][v];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    hp[mb] = head_combine(hp[mb], shfl_part(hp[mb], l ^ 16));
+    hp[mb] = head_combine(hp[mb], shfl_part(hp[mb], l ^ 32));
+    if (lg == 0) hred[w][mb * 16 + lr] = hp[mb];
+  }
+  __syncthreads();
+  if (tid < kTileM) {
+    HeadPart p = hred[0][tid];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) p = head_combine(p, hred[ww][tid]);
+    const int m = m0 + tid;
+    if (m < a.M) {
+      float* o = a.part + (static_cast<size_t>(m) * nWG + wg) * 5;
+      o[0] = p.m;
+      o[1] = __int_as_float(p.am);
+      o[2] = p.m2;
+      o[3] = p.s;
+      o[4] = p.t;
+    }
+  }
+}
+
+// -------------------------------------------------------------- projections
+// Split-K in two kernels.  proj_bf16: work-group (group g, slice q, tile mt)
+// computes blocks 4g .. 4g+3 (one per wave, MFMA-layout weight loads) over the
+// K-slice q of S and stores the fp32 partial; the activation chunk in LDS is
+// shared by the four blocks, so the activations are read once per 64 weight
+// rows.  All S x nMT work-groups of a group run on the same XCD.  proj_reduce:
+// one thread per (block, activation row) sums the S partials in slice order
+// (deterministic) and applies the epilogue.
+template <int EPI, int DEPTH>
+__global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int NB, int NGr,
+                                                                 int S, int nMT) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2 * kXS];
+
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, kk = bid >> 3;
+  const int mt = kk % nMT;
+  const int q = (kk / nMT) % S;
+  const int g = (kk / (nMT * S)) * 8 + xcd;
+  if (g >= NGr) return;
+  const int m0 = mt * kTileM;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+  const int b = g * 4 + w;
+  const bool bv = b < NB;
+  const int Ks = a.K / S;
+  const int kbase = q * Ks;
+  const int nck = Ks / kKc;
+
+  int row = bv ? block_row<EPI>(a, b, lr) : 0;
+  if (row > a.N - 1) row = a.N - 1;
+  const uint16_t* wp = w_row_ptr(a, row) + kbase + 8 * lg;
+  const uint16_t* xr[2];
+  uint32_t xm[2];
+  int xlds[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int idx = e * kGThreads + tid;
+    const int r = idx >> 3, cc = (idx & 7) * 8;
+    x_row_masked(a, m0 + r, xr[e], xm[e]);
+    xr[e] += kbase + cc;
+    xlds[e] = r * kXP + cc;
+  }
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int RS = DEPTH + 1;
+  static_assert(RS % 2 == 0, "ring slots and LDS stages must unroll together");
+  uint4 wbuf[RS][2];
+  uint4 xbuf[RS][2];
+  auto wload = [&](int c, uint4 (&dst)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dst[i] = *reinterpret_cast<const uint4*>(wp + c * kKc + 32 * i);
+  };
+  // raw loads; the row mask is applied when the chunk is written to LDS
+  auto xload = [&](int c, uint4 (&dst)[2]) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) dst[e] = *reinterpret_cast<const uint4*>(xr[e] + c * kKc);
+  };
+
+  // nck is a multiple of RS; loads past the last chunk are clamped to it, so no
+  // load is conditional (a conditional load would make the compiler's wait
+  // counts conservative and drain the ring every chunk)
+  xload(0, xbuf[0]);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) *reinterpret_cast<uint4*>(&xs[xlds[e]]) = mask4(xbuf[0][e], xm[e]);
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    if (d + 1 < DEPTH) xload(min(d + 1, nck - 1), xbuf[d + 1]);
+    wload(min(d, nck - 1), wbuf[d]);
+  }
+  for (int c0 = 0; c0 < nck; c0 += RS) {
+#pragma unroll
+    for (int u = 0; u < RS; ++u) {
+      const int c = c0 + u;
+      {
+        const int cn = min(c + DEPTH, nck - 1);
+        xload(cn, xbuf[(u + DEPTH) % RS]);
+        wload(cn, wbuf[(u + DEPTH) % RS]);
+        __syncthreads();
+        const uint16_t* xq = xs + (u & 1) * kXS;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8 av = __builtin_bit_cast(bf16x8, wbuf[u][s]);
 #pragma unroll
           for (int mb = 0; mb < 4; ++mb) {
-            hp[mb] = head_combine(hp[mb], head_elem(acc[t][mb][v], n));
-            const int m = m0 + mb * 16 + lr;
-            if (a.logits && m < a.M) a.logits[static_cast<size_t>(m) * a.N + n] = acc[t][mb][v];
+            const bf16x8 bx = *reinterpret_cast<const bf16x8*>(xq + (mb * 16 + lr) * kXP + s * 32 + 8 * lg);
+            acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bx, acc[mb], 0, 0, 0);
           }
         }
+        // (after the last chunk this stores a clamped copy nobody reads)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          *reinterpret_cast<uint4*>(&xs[((u + 1) & 1) * kXS + xlds[e]]) = mask4(xbuf[(u + 1) % RS][e], xm[e]);
       }
     }
+  }
+
+  // partial of this wave's block: [16 block rows][64 activation rows]
+  const size_t grp = static_cast<size_t>(mt) * NGr + g;
+  float* pp = a.kpart + ((grp * S + q) * 4 + w) * 1024;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      hp[mb] = head_combine(hp[mb], shfl_part(hp[mb], l ^ 16));
-      hp[mb] = head_combine(hp[mb], shfl_part(hp[mb], l ^ 32));
-      if (lg == 0) hred[w][mb * 16 + lr] = hp[mb];
-    }
-    __syncthreads();
-    if (tid < kTileM) {
-      HeadPart p = hred[0][tid];
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int ww = 1; ww < 4; ++ww) p = head_combine(p, hred[ww][tid]);
-      const int m = m0 + tid;
-      if (m < a.M) {
-        float* o = a.part + (static_cast<size_t>(m) * nWG + wg) * 5;
-        o[0] = p.m;
-        o[1] = __int_as_float(p.am);
-        o[2] = p.m2;
-        o[3] = p.s;
-        o[4] = p.t;
+    for (int v = 0; v < 4; ++v) pp[(4 * lg + v) * 64 + mb * 16 + lr] = acc[mb][v];
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kGThreads) void proj_reduce_kernel(GemmArgs a, int NB, int NGr, int S) {
+  const int grp = blockIdx.x;  // mt * NGr + g
+  const int mt = grp / NGr, g = grp - mt * NGr;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int b = g * 4 + w;
+  if (b >= NB) return;
+  const int m0 = mt * kTileM;
+  // lane l: activation row m0 + l of block b
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = 0.f;
+  for (int qq = 0; qq < S; ++qq) {
+    const float* src = a.kpart + ((static_cast<size_t>(grp) * S + qq) * 4 + w) * 1024;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] += src[i * 64 + l];
+  }
+  const int gm = m0 + l;
+  if (gm >= a.M) return;
+  if constexpr (EPI == EPI_RESID) {
+    const int n = b * 16;
+    uint4 o[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+    const int tok = a.resid_tok[gm];
+    if (tok >= 0) {
+      const uint16_t* rp = static_cast<const uint16_t*>(a.resid) +
+                           static_cast<size_t>(a.resid_by_token ? tok : gm) * a.N + n;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 r = *reinterpret_cast<const uint4*>(rp + 8 * h);
+        const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+        uint32_t ow[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float lo = bf16_to_f32(rw[j] & 0xFFFF) + x[8 * h + 2 * j];
+          const float hi = bf16_to_f32(rw[j] >> 16) + x[8 * h + 2 * j + 1];
+          ow[j] = static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+        }
+        o[h] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
       }
     }
-  } else {
-    // sum the S K-slice partials of each block in LDS (fixed order), then write
-    static_assert(B == 1, "projection epilogues take one block per wave");
-    float* red = reinterpret_cast<float*>(xs);  // [GPW][S][16][64]
-    __syncthreads();
+    uint4* op = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out_res) + static_cast<size_t>(gm) * a.N + n);
+    op[0] = o[0];
+    op[1] = o[1];
+  } else {  // EPI_QKV
+    const int nq = a.Hq * 8, nk = a.Hkv * 8;
+    if (b < nq + nk) {
+      // rows i < 8 are head dims 8j + i, rows 8 + i their RoPE partners 64 + 8j + i
+      const int bb = b < nq ? b : b - nq;
+      const int head = bb >> 3, j8 = (bb & 7) * 8;
+      const int sq = gm / a.n_rows;
+      int pos = static_cast<int>(a.kv_offsets[sq + 1] - a.kv_offsets[sq]) + a.depth[gm];
+      if (pos > a.n_pos - 1) pos = a.n_pos - 1;
+      uint32_t lw[4], hw[4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+      for (int j = 0; j < 4; ++j) {
+        float lo[2], hi[2];
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        red[((gi * S + q) * 16 + 4 * lg + v) * 64 + mb * 16 + lr] = acc[0][mb][v];
-    __syncthreads();
-    if (!bval[0]) return;
-    const int lt = q * 64 + l;  // thread index within the block group (S*64 threads)
-    const float* rg = red + gi * S * 1024;
-    auto sumq = [&](int i, int m) {
-      float x = 0.f;
-#pragma unroll
-      for (int qq = 0; qq < S; ++qq) x += rg[(qq * 16 + i) * 64 + m];
-      return x;
-    };
-    if constexpr (EPI == EPI_RESID) {
-      // 16 rows x 64 activations = 256 items of 4 consecutive columns
-      for (int it = lt; it < 256; it += S * 64) {
-        const int m = it & 63, i0 = (it >> 6) * 4;
-        const int gm = m0 + m;
-        if (gm >= a.M) continue;
-        const int n = blk[0] * 16 + i0;
-        if (n >= a.N) continue;
-        float x[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) x[v] = sumq(i0 + v, m);
-        uint2 o = make_uint2(0, 0);
-        const int tok = a.resid_tok[gm];
-        if (tok >= 0) {
-          const uint16_t* rp = static_cast<const uint16_t*>(a.resid) +
-                               static_cast<size_t>(a.resid_by_token ? tok : gm) * a.N + n;
-          const uint2 r = *reinterpret_cast<const uint2*>(rp);
-          o = pack4_bf16(bf16_to_f32(r.x & 0xFFFF) + x[0], bf16_to_f32(r.x >> 16) + x[1],
-                         bf16_to_f32(r.y & 0xFFFF) + x[2], bf16_to_f32(r.y >> 16) + x[3]);
+        for (int h = 0; h < 2; ++h) {
+          const int i = 2 * j + h;
+          const float c = a.rope_cos[static_cast<size_t>(pos) * 64 + j8 + i];
+          const float sn = a.rope_sin[static_cast<size_t>(pos) * 64 + j8 + i];
+          lo[h] = x[i] * c - x[i + 8] * sn;
+          hi[h] = x[i + 8] * c + x[i] * sn;
         }
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out_res) + static_cast<size_t>(gm) * a.N + n) = o;
+        lw[j] = static_cast<uint32_t>(f32_to_bf16(lo[0])) | (static_cast<uint32_t>(f32_to_bf16(lo[1])) << 16);
+        hw[j] = static_cast<uint32_t>(f32_to_bf16(hi[0])) | (static_cast<uint32_t>(f32_to_bf16(hi[1])) << 16);
       }
-    } else {  // EPI_QKV
-      const int b = blk[0];
-      const int nq = a.Hq * 8, nk = a.Hkv * 8;
-      if (b < nq + nk) {
-        // q or k block: rows i < 8 are dims 8j+i, rows 8+i their RoPE partners 64+8j+i
-        const int bb = b < nq ? b : b - nq;
-        const int head = bb >> 3, j8 = (bb & 7) * 8;
-        for (int it = lt; it < 128; it += S * 64) {
-          const int m = it & 63, i0 = (it >> 6) * 4;
-          const int gm = m0 + m;
-          if (gm >= a.M) continue;
-          const int sq = gm / a.n_rows;
-          int pos = static_cast<int>(a.kv_offsets[sq + 1] - a.kv_offsets[sq]) + a.depth[gm];
-          if (pos > a.n_pos - 1) pos = a.n_pos - 1;
-          float lo[4], hi[4];
+      uint16_t* op = b < nq ? static_cast<uint16_t*>(a.q_out) + static_cast<size_t>(gm) * a.Hq * 128
+                            : static_cast<uint16_t*>(a.k_out) + static_cast<size_t>(gm) * a.Hkv * 128;
+      op += head * 128 + j8;
+      *reinterpret_cast<uint4*>(op) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      *reinterpret_cast<uint4*>(op + 64) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    } else {
+      const int vr = (b - nq - nk) * 16;  // first v dim of the block
+      uint32_t ow[8];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int d = j8 + i0 + v;
-            const float c = a.rope_cos[static_cast<size_t>(pos) * 64 + d];
-            const float sn = a.rope_sin[static_cast<size_t>(pos) * 64 + d];
-            const float x1 = sumq(i0 + v, m), x2 = sumq(8 + i0 + v, m);
-            lo[v] = x1 * c - x2 * sn;
-            hi[v] = x2 * c + x1 * sn;
-          }
-          uint16_t* op = b < nq ? static_cast<uint16_t*>(a.q_out) + static_cast<size_t>(gm) * a.Hq * 128
-                                : static_cast<uint16_t*>(a.k_out) + static_cast<size_t>(gm) * a.Hkv * 128;
-          op += head * 128 + j8 + i0;
-          *reinterpret_cast<uint2*>(op) = pack4_bf16(lo[0], lo[1], lo[2], lo[3]);
-          *reinterpret_cast<uint2*>(op + 64) = pack4_bf16(hi[0], hi[1], hi[2], hi[3]);
-        }
-      } else {
-        const int vr = (b - nq - nk) * 16;  // first v row of the block
-        for (int it = lt; it < 256; it += S * 64) {
-          const int m = it & 63, i0 = (it >> 6) * 4;
-          const int gm = m0 + m;
-          if (gm >= a.M) continue;
-          uint16_t* op = static_cast<uint16_t*>(a.v_out) + static_cast<size_t>(gm) * a.Hkv * 128 + vr + i0;
-          *reinterpret_cast<uint2*>(op) = pack4_bf16(sumq(i0, m), sumq(i0 + 1, m), sumq(i0 + 2, m), sumq(i0 + 3, m));
-        }
-      }
+      for (int j = 0; j < 8; ++j)
+        ow[j] = static_cast<uint32_t>(f32_to_bf16(x[2 * j])) | (static_cast<uint32_t>(f32_to_bf16(x[2 * j + 1])) << 16);
+      uint4* op = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.v_out) + static_cast<size_t>(gm) * a.Hkv * 128 + vr);
+      op[0] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      op[1] = make_uint4(ow[4], ow[5], ow[6], ow[7]);
     }
   }
 }
@@ -534,25 +619,62 @@ HeadGrid head_grid(int N) {
 
 int gemm_bf16_head_parts(int N) { return head_grid(N).nWG; }
 
+int proj_ksplit(int K, int NB) {
+  // about one work-group per CU: S ~ 256 / (number of 4-block groups), taken as a
+  // divisor of half the chunk count (each slice an even number of chunks)
+  const int nch = K / kKc;
+  const int NGr = (NB + 3) / 4;
+  int target = 256 / NGr;
+  if (target < 1) target = 1;
+  int S = 1;
+  for (int c = 1; c <= nch / 2; ++c)
+    if ((nch / 2) % c == 0 && c <= target) S = c;
+  return S;
+}
+
+int proj_blocks(const GemmArgs& a) {
+  return a.epi == EPI_QKV ? (a.Hq + 2 * a.Hkv) * 8 : (a.N + 15) / 16;
+}
+
+size_t proj_part_floats(int M, int NB, int K) {
+  const int nMT = (M + kTileM - 1) / kTileM;
+  const int NGr = (NB + 3) / 4;
+  return static_cast<size_t>(nMT) * NGr * proj_ksplit(K, NB) * 4 * 1024;
+}
+
 glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   const int nMT = (a.M + kTileM - 1) / kTileM;
   if (a.epi == EPI_HEAD) {
     const HeadGrid g = head_grid(a.N);
     const int grid = ((g.nWG + 7) / 8) * 8 * nMT;
-    gemm_bf16_kernel<EPI_HEAD, kHeadB, 1, 1><<<grid, kGThreads, 0, st>>>(a, g.NB, g.NG, g.nWG, nMT);
+    head_bf16_kernel<kHeadB, 1><<<grid, kGThreads, 0, st>>>(a, g.NB, g.NG, g.nWG, nMT);
   } else {
-    // one 16-row block per work-group, its K split over the 4 waves
-    int NB;
-    if (a.epi == EPI_QKV)
-      NB = (a.Hq + 2 * a.Hkv) * 8;
-    else
-      NB = (a.N + 15) / 16;
-    const int nWG = NB;
-    const int grid = ((nWG + 7) / 8) * 8 * nMT;
-    if (a.epi == EPI_QKV)
-      gemm_bf16_kernel<EPI_QKV, 1, 4, 3><<<grid, kGThreads, 0, st>>>(a, NB, NB, nWG, nMT);
-    else
-      gemm_bf16_kernel<EPI_RESID, 1, 4, 3><<<grid, kGThreads, 0, st>>>(a, NB, NB, nWG, nMT);
+    const int NB = proj_blocks(a);
+    const int NGr = (NB + 3) / 4;
+    const int S = proj_ksplit(a.K, NB);
+    const int grid = ((NGr + 7) / 8) * 8 * S * nMT;
+    // ring depth: the largest of 8, 4, 2 slots dividing the slice's chunk count
+    const int nck = a.K / S / kKc;
+    const int rs = nck % 8 == 0 ? 8 : nck % 4 == 0 ? 4 : 2;
+    if (a.epi == EPI_QKV) {
+      if (rs == 8)
+        proj_bf16_kernel<EPI_QKV, 7><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
+      else if (rs == 4)
+        proj_bf16_kernel<EPI_QKV, 3><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
+      else
+        proj_bf16_kernel<EPI_QKV, 1><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
+      GLANCE_LAUNCH_CHECK();
+      proj_reduce_kernel<EPI_QKV><<<NGr * nMT, kGThreads, 0, st>>>(a, NB, NGr, S);
+    } else {
+      if (rs == 8)
+        proj_bf16_kernel<EPI_RESID, 7><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
+      else if (rs == 4)
+        proj_bf16_kernel<EPI_RESID, 3><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
+      else
+        proj_bf16_kernel<EPI_RESID, 1><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
+      GLANCE_LAUNCH_CHECK();
+      proj_reduce_kernel<EPI_RESID><<<NGr * nMT, kGThreads, 0, st>>>(a, NB, NGr, S);
+    }
   }
   GLANCE_LAUNCH_CHECK();
   return GLANCE_OK;

@@ -3,6 +3,7 @@
 // enqueued; on error nothing is launched.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -59,11 +60,11 @@ glance_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
 struct AttnWs {
   int n_split = 0, split = 0;
   size_t off_qkv = 0, off_q = 0, off_k = 0, off_v = 0, off_part = 0, off_x = 0, bytes = 0;
+  size_t off_kpart = 0;
 };
 
 AttnWs attn_ws_layout(int dtype, int nseq, int n_rows, int64_t max_prefix, int d_model, int Hq,
                       int Hkv, int D) {
-  (void)d_model;
   AttnWs w;
   const size_t R = static_cast<size_t>(nseq) * n_rows;
   size_t off = 0;
@@ -80,6 +81,11 @@ AttnWs attn_ws_layout(int dtype, int nseq, int n_rows, int64_t max_prefix, int d
     w.n_split = static_cast<int>((max_prefix + w.split - 1) / w.split);
     w.off_part = take(attn_part_floats(nseq, n_rows, Hq, Hkv, D, w.n_split) * sizeof(float));
     w.off_x = take(R * Hq * D * 2);
+    // split-K scratch shared by the q/k/v and output projections
+    const int M = static_cast<int>(R);
+    const int nb_qkv = (Hq + 2 * Hkv) * 8, nb_o = (d_model + 15) / 16;
+    const size_t pf = std::max(proj_part_floats(M, nb_qkv, d_model), proj_part_floats(M, nb_o, Hq * D));
+    w.off_kpart = take(pf * sizeof(float));
   } else {
     w.off_qkv = take(R * static_cast<size_t>(Hq + 2 * Hkv) * D * sizeof(float));
     w.off_x = take(R * Hq * D * sizeof(float));
@@ -220,6 +226,7 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
   void* attn_x = base + w.off_x;
   const int R = nseq * n_rows;
   const int qd = Hq * D, kd = Hkv * D;
+  float* kpart = reinterpret_cast<float*>(base + w.off_kpart);
   if (dtype == GLANCE_BF16) {
     if (tree_k == nullptr) tree_k = base + w.off_k;
     if (tree_v == nullptr) tree_v = base + w.off_v;
@@ -252,6 +259,7 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
     g.rope_cos = rope_cos;
     g.rope_sin = rope_sin;
     g.n_pos = n_pos;
+    g.kpart = kpart;
     st = launch_gemm_bf16(g, hs);
   } else {
     g.epi = EPI_STORE_F32;
@@ -305,6 +313,7 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
   o.resid_tok = token;
   o.resid_by_token = embed != nullptr;
   o.out_res = h_out;
+  o.kpart = kpart;
   return dtype == GLANCE_BF16 ? launch_gemm_bf16(o, hs) : launch_gemm_f32(o, hs);
 }
 

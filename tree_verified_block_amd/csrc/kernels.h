@@ -55,10 +55,17 @@ struct GemmArgs {
   const float* rope_cos;
   const float* rope_sin;
   int n_pos;
+  // EPI_QKV / EPI_RESID (bf16): split-K partials
+  float* kpart;
 };
 // Number of per-row partial records the bf16 LM-head GEMM leaves (the merge input).
 int gemm_bf16_head_parts(int N);
 glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
+// Scratch of the bf16 projections: number of 16-row weight blocks, K-split and
+// partial floats for M activation rows.
+int proj_blocks(const GemmArgs& a);
+int proj_ksplit(int K, int NB);
+size_t proj_part_floats(int M, int NB, int K);
 glance_status launch_gemm_f32(const GemmArgs& a, hipStream_t st);
 // Row statistics of the head from bf16 partials, or from full fp32 logits.
 glance_status launch_head_merge(const float* part, int n_tiles, int R, int32_t* argmax,
