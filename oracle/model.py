@@ -122,7 +122,8 @@ class TargetModel:
         return store(h + a.reshape(a.shape[0], -1) @ w["wo"].T, self.dtype)
 
 
-def evaluate_paths(model: TargetModel, s: int, root: int, paths: list) -> dict:
+def evaluate_paths(model: TargetModel, s: int, root: int, paths: list,
+                   layer_inputs: list | None = None) -> dict:
     """Evaluate every node of a prefix-closed set of token paths (the root is the
     empty path ()) on its own explicit sequence after sequence s's prefix.
 
@@ -130,7 +131,12 @@ def evaluate_paths(model: TargetModel, s: int, root: int, paths: list) -> dict:
     keys of its own path (root, y_1, .., y_d), i.e. exactly the causal sequence
     x o b o y_{1:d}; no other node is visible.  Returns per-layer attention
     outputs ``attn[l]`` [n][Hq*D], per-layer outputs ``h[l]`` [n][d] and the
-    final hidden rows ``final`` [n][d], all float64, in the order of ``paths``."""
+    final hidden rows ``final`` [n][d], all float64, in the order of ``paths``.
+
+    ``layer_inputs[l]`` (l >= 1), when given, replaces the rows entering layer l
+    (in the order of ``paths``): each layer is then evaluated on exactly the
+    inputs another implementation fed to it, which isolates that layer's error
+    from the drift that bf16 storage accumulates over a deep stack."""
     index = {p: i for i, p in enumerate(paths)}
     if () not in index:
         raise ValueError("paths must contain the root ()")
@@ -142,6 +148,8 @@ def evaluate_paths(model: TargetModel, s: int, root: int, paths: list) -> dict:
     h = model.embed_rows(tokens)
     attn_all, h_all = [], []
     for li in range(model.n_layers):
+        if layer_inputs is not None and li > 0 and layer_inputs[li] is not None:
+            h = np.asarray(layer_inputs[li], dtype=np.float64)
         q, k, v = model.project(li, h, pos)
         Kp, Vp = model.prefix_kv(li, s)
         a = np.empty((n, model.Hq, model.D))

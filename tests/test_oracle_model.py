@@ -161,6 +161,27 @@ def test_tree_rows_equal_token_by_token_decoding(name, seed):
         np.testing.assert_allclose(dec.final, ev["final"][i], rtol=1e-12, atol=1e-14)
 
 
+def test_teacher_forced_layers_reproduce_free_running():
+    """Feeding every layer the rows the oracle itself produced before it gives
+    back the free-running result exactly; feeding a perturbed layer input moves
+    that layer and the ones after it, and no earlier one."""
+    inp = gen_round(make_config("mini_bf16_ragged", n_layers=3), 3)
+    cfg = inp["cfg"]
+    model = mdl.TargetModel(inp)
+    root = int(inp["rounds"][0]["root"][0])
+    t = orr.build_tree(inp["rounds"][0]["draft_logits"][0], cfg.dtype, root, cfg.N)
+    free = mdl.evaluate_paths(model, 0, root, t["order"])
+    feeds = [None] + [free["h"][li - 1] for li in range(1, cfg.n_layers)]
+    tf = mdl.evaluate_paths(model, 0, root, t["order"], layer_inputs=feeds)
+    for li in range(cfg.n_layers):
+        assert np.array_equal(tf["h"][li], free["h"][li])
+        assert np.array_equal(tf["attn"][li], free["attn"][li])
+    feeds[2] = free["h"][1] * 1.01
+    moved = mdl.evaluate_paths(model, 0, root, t["order"], layer_inputs=feeds)
+    assert np.array_equal(moved["h"][1], free["h"][1])
+    assert not np.allclose(moved["attn"][2], free["attn"][2])
+
+
 def test_rows_ignore_non_ancestors():
     """A row depends on its own path only: changing the other nodes leaves it
     unchanged (paper App. B.1: masking changes the layout, not the conditioning)."""
