@@ -12,8 +12,8 @@ namespace glance {
 
 // ------------------------------------------------------------------ tree.hip
 struct TreeWs {
-  int nch = 0, chunk = 0;  // chunks per offset row and logits per chunk
-  size_t off_cstat = 0, off_clist = 0, off_logq = 0, off_id = 0, bytes = 0;
+  // per-chunk (max, sum exp) [nseq*L][16] and sorted key lists [nseq*L][16][64]
+  size_t off_cstat = 0, off_clist = 0, bytes = 0;
 };
 TreeWs tree_ws_layout(int nseq, int L, int V);
 glance_status launch_build_tree(const void* logits, int dtype, const int32_t* root, int nseq,

@@ -13,26 +13,21 @@
 // Tokens are ranked by the key (logit desc, token id asc); keys are distinct.
 //
 // Kernels
-//   lsm_chunk   grid (chunks, L, nseq) x 256.  One chunk (4096 bf16 or 2048 fp32
-//               logits) of one offset row, held in registers after one wave of
-//               16-byte streaming loads: the chunk maximum, the sum of
-//               exp(z - max) and the chunk's K best keys, sorted (block_topk).
-//   lsm_merge   grid (L, nseq) x 256.  Combines the chunk statistics into the
-//               row's max and ln(sum exp), selects the K best of the <= 64 chunk
-//               lists (block_topk again) and writes them as
-//               log q_j(v) = (z_v - max) - ln(sum exp(z - max)) with their ids.
+//   lsm_row     grid (L, nseq) x 1024: one offset row per work-group.  Pass 1
+//               streams the row once from HBM (each thread's running max, sum of
+//               exp and best key); the K-th largest of the 1024 per-thread best
+//               keys, T, bounds the row's K-th largest key from below (K threads
+//               each hold a key >= T), and is found by sorting each wave's bests
+//               and merging the sorted lists pairwise.  Pass 2 re-reads the row
+//               from L2 and gathers the keys >= T (about K of them), ranked
+//               exactly by counting.  Output: log q_j(v) = (z_v - max) -
+//               ln(sum exp(z - max)) of the K best tokens, in rank order.
 //   build_tree  grid nseq x 256.  The ranked lists go to LDS; wave 0 runs
 //               best-first selection: lane 0 is the root and lane i the i-th
 //               selected node; every lane holds the best not-yet-selected child
 //               of its node, so a selection is one wave max and touches two
 //               lanes.  Finally the nodes are laid out breadth-first with their
 //               ancestor masks.
-//
-// block_topk finds the K largest of the keys a block holds in registers: the
-// K-th largest of the per-thread best keys, T, bounds the K-th largest key from
-// below (K threads each hold a key >= T), so only keys >= T (about K of them)
-// are gathered to LDS and ranked exactly by counting; when more than kCap keys
-// reach T (massive ties) an exact 8-bit radix select runs instead.
 #include "common.h"
 #include "kernels.h"
 
@@ -54,19 +49,10 @@ __device__ __forceinline__ unsigned long long make_comp(float v, uint32_t idx) {
 }
 
 constexpr int kChunkThreads = 256;
-constexpr int kCap = 1024;      // candidates gathered above the threshold
-constexpr int kChunkVecs = 2;   // 16-byte vectors per thread per chunk
-constexpr int kMergeItems = 16; // list entries per thread in the merge (nch <= 64)
-
-// Shared memory of block_topk.
-template <int NT>
-struct TopkSmem {
-  unsigned long long bests[NT];
-  unsigned long long cand[kCap];
-  unsigned hist[256];
-  unsigned long long prefix, T;
-  int krem, done, count;
-};
+constexpr int kChunkWaves = kChunkThreads / kWave;
+constexpr int kMaxVec = 8;       // 16-byte vectors per thread
+constexpr int kMaxChunks = 16;   // chunk lists per offset row
+constexpr int kCap = 2048;       // candidates gathered above the threshold
 
 // Rank of key k among n keys of an LDS array (the number of larger keys),
 // reading 2 keys per 16-byte load, 8 in flight.
@@ -85,101 +71,49 @@ __device__ __forceinline__ int count_greater(const unsigned long long* a, int n,
   return rank;
 }
 
-// The K (<= 63) largest of the distinct nonzero keys held by the block's
-// threads (IPT per thread, 0 = no key), written to sel[0..63] sorted
-// descending (0 where fewer exist).  The K-th largest per-thread best key T
-// bounds the K-th largest key from below (K threads each hold a key >= T), so
-// only keys >= T are gathered (about K of them) and ranked exactly by counting.
-// If more than kCap keys are >= T (many ties), an exact radix select runs.
-template <int NT, int IPT>
-__device__ void block_topk(const unsigned long long (&items)[IPT], int K, unsigned long long* sel,
-                           TopkSmem<NT>& sm) {
-  const int tid = threadIdx.x, lane = lane_id();
-  unsigned long long best = 0ull;
+// Ranks (numbers of larger keys) of two keys among n keys of an LDS array that
+// every lane reads in step (broadcast reads, 8 keys in flight).
+__device__ __forceinline__ void rank2(const unsigned long long* a, int n, unsigned long long x,
+                                      unsigned long long y, int& rx, int& ry) {
+  rx = 0;
+  ry = 0;
+  int o = 0;
+  for (; o + 8 <= n; o += 8) {
+    ulonglong2 v[4];
 #pragma unroll
-  for (int i = 0; i < IPT; ++i) best = items[i] > best ? items[i] : best;
-  for (int i = tid; i < kSlots; i += NT) sel[i] = 0ull;
-  sm.bests[tid] = best;
-  if (tid == 0) {
-    sm.count = 0;
-    sm.T = 0ull;
-  }
-  const int n_ok = __syncthreads_count(best != 0ull);
-  if (K <= 0) return;
-  if (n_ok > K && best != 0ull && count_greater(sm.bests, NT, best) == K - 1) sm.T = best;
-  __syncthreads();
-  const unsigned long long T = sm.T;
+    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const ulonglong2*>(a + o + 2 * u);
 #pragma unroll
-  for (int i = 0; i < IPT; ++i) {
-    if (items[i] != 0ull && items[i] >= T) {
-      const int slot = atomicAdd(&sm.count, 1);
-      if (slot < kCap) sm.cand[slot] = items[i];
+    for (int u = 0; u < 4; ++u) {
+      rx += (v[u].x > x ? 1 : 0) + (v[u].y > x ? 1 : 0);
+      ry += (v[u].x > y ? 1 : 0) + (v[u].y > y ? 1 : 0);
     }
   }
-  __syncthreads();
-  const int C = sm.count;
-  if (C <= kCap) {
-    for (int e = tid; e < C; e += NT) {
-      const unsigned long long k = sm.cand[e];
-      const int rank = count_greater(sm.cand, C, k);
-      if (rank < K) sel[rank] = k;
-    }
-    __syncthreads();
-    return;
+  for (; o < n; ++o) {
+    rx += a[o] > x ? 1 : 0;
+    ry += a[o] > y ? 1 : 0;
   }
-  // exact radix select over every key
-  __syncthreads();
-  if (tid == 0) sm.count = 0;
-  unsigned long long prefix = 0ull, mask = 0ull;
-  int krem = K;
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += NT) sm.hist[i] = 0u;
-    __syncthreads();
+}
+
+__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
+  return a > b ? a : b;
+}
+__device__ __forceinline__ unsigned long long umin64(unsigned long long a, unsigned long long b) {
+  return a > b ? b : a;
+}
+
+// Descending sort of one wavefront's 64 keys (one per lane): bitonic network.
+__device__ __forceinline__ unsigned long long wave_sort_desc(unsigned long long key) {
+  const int lane = lane_id();
 #pragma unroll
-    for (int i = 0; i < IPT; ++i)
-      if (items[i] != 0ull && (items[i] & mask) == prefix)
-        atomicAdd(&sm.hist[(items[i] >> shift) & 255ull], 1u);
-    __syncthreads();
-    if (tid < kWave) {
-      unsigned cc[4];
+  for (int k = 2; k <= kWave; k <<= 1) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) cc[b] = sm.hist[4 * lane + b];
-      const unsigned sc = cc[0] + cc[1] + cc[2] + cc[3];
-      unsigned inc = sc;
-#pragma unroll
-      for (int d = 1; d < kWave; d <<= 1) {
-        unsigned o = __shfl_down(inc, d, kWave);
-        if (lane + d < kWave) inc += o;
-      }
-      unsigned above = inc - sc;
-#pragma unroll
-      for (int b = 3; b >= 0; --b) {
-        if (above < static_cast<unsigned>(krem) && static_cast<unsigned>(krem) <= above + cc[b]) {
-          sm.prefix = prefix | (static_cast<unsigned long long>(4 * lane + b) << shift);
-          sm.krem = krem - static_cast<int>(above);
-          sm.done = (cc[b] == static_cast<unsigned>(krem) - above) ? 1 : 0;
-        }
-        above += cc[b];
-      }
-    }
-    __syncthreads();
-    prefix = sm.prefix;
-    krem = sm.krem;
-    const int done = sm.done;
-    mask |= 0xFFull << shift;
-    __syncthreads();
-    if (done) break;
-  }
-#pragma unroll
-  for (int i = 0; i < IPT; ++i) {
-    if (items[i] != 0ull && items[i] >= prefix) {
-      const int slot = atomicAdd(&sm.count, 1);
-      if (slot < kSlots) sm.cand[slot] = items[i];
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const unsigned long long o = __shfl_xor(key, j, kWave);
+      const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
+      key = keep_max ? umax64(key, o) : umin64(key, o);
     }
   }
-  __syncthreads();
-  if (tid < K) sel[count_greater(sm.cand, K, sm.cand[tid])] = sm.cand[tid];
-  __syncthreads();
+  return key;
 }
 
 template <typename T>
@@ -189,149 +123,209 @@ __device__ __forceinline__ float load_logit<float>(const float* p) { return *p; 
 template <>
 __device__ __forceinline__ float load_logit<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
 
-// One chunk of kChunkThreads * kChunkVecs * E logits (E per 16 bytes) of one
-// offset row; every load is issued before any is used.
-template <typename T>
+// One chunk of an offset row: 256 threads x NV vectors of 16 bytes, every load
+// issued before any is used.  Writes the chunk's maximum and sum of
+// exp(z - max) and its K best keys, sorted descending (0 where fewer exist).
+// Threshold: wave w sorts its 64 per-thread best keys and takes the k-th
+// largest, k = ceil(K/4); the minimum T over the four waves is a lower bound of
+// the chunk's K-th largest key (each wave holds k keys >= T).  Only keys >= T
+// (about K of them) are gathered to LDS and ranked exactly by counting; more
+// than kCap of them (massive ties) switches to an exact 8-bit radix select.
+template <typename T, int NV>
 __global__ __launch_bounds__(kChunkThreads) void lsm_chunk_kernel(
-    const T* __restrict__ logits, int L, int V, int N, int nch,
-    float* __restrict__ cstat, unsigned long long* __restrict__ clist) {
+    const T* __restrict__ logits, int L, int V, int N, int nch, float2* __restrict__ cstat,
+    unsigned long long* __restrict__ clist) {
   constexpr int E = 16 / sizeof(T);
-  constexpr int IPT = kChunkVecs * E;
-  __shared__ float redf[kChunkThreads / kWave];
-  __shared__ float s_M;
-  __shared__ __attribute__((aligned(16))) TopkSmem<kChunkThreads> sm;
+  constexpr int IPT = NV * E;
+  __shared__ __attribute__((aligned(16))) unsigned long long cand[kCap];
   __shared__ unsigned long long sel[kSlots];
+  __shared__ unsigned long long wt[kChunkWaves];
+  __shared__ float red_m[kChunkWaves], red_s[kChunkWaves];
+  __shared__ unsigned hist[256];
+  __shared__ int s_count, s_krem, s_done;
+  __shared__ unsigned long long s_prefix;
 
   const int c = blockIdx.x, j = blockIdx.y, sq = blockIdx.z;
   const int row = sq * L + j;
   const int K = k_of(N, V, j);
   const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
   const T* base = logits + static_cast<size_t>(row) * V;
-  const int c0 = c * kChunkThreads * IPT;
-  const bool vec = (V % E) == 0;
+  const int c0 = c * kChunkThreads * IPT;  // first logit of the chunk
 
+  // element e: vector path token idx0 + (e/E)*256*E + e%E (V % E == 0), else
+  // token idx0 + e*256; token ids increase with e
+  const bool vec = V % E == 0;
+  const int idx0 = vec ? c0 + tid * E : c0 + tid;
+  auto tok = [&](int e) { return vec ? idx0 + (e / E) * kChunkThreads * E + (e % E) : idx0 + e * kChunkThreads; };
   float z[IPT];
-  int idx[IPT];
+  bool ok[IPT];
   if (vec) {
-    uint4 u[kChunkVecs];
+    uint4 u[NV];
 #pragma unroll
-    for (int v = 0; v < kChunkVecs; ++v) {
-      const int e0 = c0 + (v * kChunkThreads + tid) * E;
-      u[v] = e0 < V ? load_stream(base + e0) : make_uint4(0, 0, 0, 0);
+    for (int b = 0; b < NV; ++b) {
+      const int i = idx0 + b * kChunkThreads * E;
+      u[b] = i < V ? *reinterpret_cast<const uint4*>(base + i) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int v = 0; v < kChunkVecs; ++v) {
-      const int e0 = c0 + (v * kChunkThreads + tid) * E;
-      const uint32_t wd[4] = {u[v].x, u[v].y, u[v].z, u[v].w};
+    for (int b = 0; b < NV; ++b) {
+      const bool vb = idx0 + b * kChunkThreads * E < V;
+      const uint32_t wd[4] = {u[b].x, u[b].y, u[b].z, u[b].w};
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        idx[v * E + e] = e0 + e;
-        float x;
         if constexpr (sizeof(T) == 2)
-          x = bf16_to_f32(static_cast<uint16_t>(e & 1 ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xFFFF));
+          z[b * E + e] = bf16_to_f32(static_cast<uint16_t>(e & 1 ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xFFFF));
         else
-          x = __uint_as_float(wd[e]);
-        z[v * E + e] = e0 < V ? x : -INFINITY;
+          z[b * E + e] = __uint_as_float(wd[e]);
+        ok[b * E + e] = vb;
       }
     }
   } else {
 #pragma unroll
     for (int e = 0; e < IPT; ++e) {
-      idx[e] = c0 + e * kChunkThreads + tid;
-      z[e] = idx[e] < V ? load_logit<T>(base + idx[e]) : -INFINITY;
+      const int i = idx0 + e * kChunkThreads;
+      ok[e] = i < V;
+      z[e] = ok[e] ? load_logit<T>(base + i) : 0.f;
     }
   }
 
-  // running max, rescaled sum of exp, keys (logit desc, token id asc)
-  float m = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < IPT; ++e) m = fmaxf(m, z[e]);
-  float sum = 0.f;
-  unsigned long long keys[IPT];
+  // running max and best (strict comparison: the smallest id wins a tie)
+  float m = -INFINITY, bz = -INFINITY;
+  int bi = -1;
 #pragma unroll
   for (int e = 0; e < IPT; ++e) {
-    const bool ok = idx[e] < V;
-    if (ok && z[e] != -INFINITY) sum += expf(z[e] - m);
-    keys[e] = ok ? make_comp(z[e], static_cast<uint32_t>(idx[e])) : 0ull;
+    if (ok[e]) {
+      m = fmaxf(m, z[e]);
+      if (bi < 0 || z[e] > bz) {
+        bz = z[e];
+        bi = tok(e);
+      }
+    }
   }
-  const float wm = wave_max(m);
-  if (lane == 0) redf[w] = wm;
-  __syncthreads();
-  if (tid == 0) {
-    float M = redf[0];
-    for (int i = 1; i < kChunkThreads / kWave; ++i) M = fmaxf(M, redf[i]);
-    s_M = M;
-  }
-  __syncthreads();
-  const float M = s_M;
-  float part = (M == -INFINITY || m == -INFINITY) ? 0.f : sum * expf(m - M);
-  part = wave_sum(part);
-  __syncthreads();
-  if (lane == 0) redf[w] = part;
-  __syncthreads();
-  if (tid == 0) {
-    float S = 0.f;
-    for (int i = 0; i < kChunkThreads / kWave; ++i) S += redf[i];
-    float* st = cstat + (static_cast<size_t>(row) * nch + c) * 2;
-    st[0] = M;
-    st[1] = S;
-  }
-  block_topk<kChunkThreads, IPT>(keys, K, sel, sm);
-  if (tid < kSlots) clist[(static_cast<size_t>(row) * nch + c) * kSlots + tid] = sel[tid];
-}
-
-// Merge of one offset's sorted chunk lists into its K best, as log q.
-__global__ __launch_bounds__(kChunkThreads) void lsm_merge_kernel(
-    int L, int V, int N, int nch, const float* __restrict__ cstat,
-    const unsigned long long* __restrict__ clist, float* __restrict__ top_logq,
-    int32_t* __restrict__ top_id) {
-  __shared__ __attribute__((aligned(16))) TopkSmem<kChunkThreads> sm;
-  __shared__ unsigned long long sel[kSlots];
-  __shared__ float s_M, s_lnS;
-  const int j = blockIdx.x, sq = blockIdx.y;
-  const int row = sq * L + j;
-  const int K = k_of(N, V, j);
-  const int tid = threadIdx.x;
-  const size_t rowc = static_cast<size_t>(row) * nch;
-  const unsigned long long* lists = clist + rowc * kSlots;
-  const int n = nch * kSlots;
-  unsigned long long items[kMergeItems];
+  // sum of exp(z - m) through the hardware exp2 (z - m <= 0)
+  float s = 0.f;
+  if (m != -INFINITY) {
 #pragma unroll
-  for (int i = 0; i < kMergeItems; ++i) {
-    const int e = i * kChunkThreads + tid;
-    items[i] = e < n ? lists[e] : 0ull;
+    for (int e = 0; e < IPT; ++e)
+      if (ok[e]) s += __builtin_amdgcn_exp2f((z[e] - m) * 1.4426950408889634f);
   }
-  if (tid < kWave) {
-    // row maximum and ln(sum exp(z - max)) from the chunk statistics (<= 64)
-    const int c = tid;
-    const float cm = c < nch ? cstat[(rowc + c) * 2] : -INFINITY;
-    const float cs = c < nch ? cstat[(rowc + c) * 2 + 1] : 0.f;
-    const float M = wave_max(cm);
-    float t = (M == -INFINITY || cs <= 0.f) ? 0.f : cs * expf(cm - M);
-    t = wave_sum(t);
-    if (tid == 0) {
-      s_M = M;
-      s_lnS = logf(t);
+  const unsigned long long best = bi >= 0 ? make_comp(bz, static_cast<uint32_t>(bi)) : 0ull;
+
+  const float wm = wave_max(m);
+  float part = (wm == -INFINITY || m == -INFINITY) ? 0.f : s * __builtin_amdgcn_exp2f((m - wm) * 1.4426950408889634f);
+  part = wave_sum(part);
+  // this wave's k-th largest best, k = ceil(K/4)
+  const int kw = (K + kChunkWaves - 1) / kChunkWaves;
+  const unsigned long long srt = wave_sort_desc(best);
+  if (lane == 0) {
+    red_m[w] = wm;
+    red_s[w] = part;
+  }
+  if (kw > 0 && lane == kw - 1) wt[w] = srt;
+  if (tid < kSlots) sel[tid] = 0ull;
+  if (tid == 0) s_count = 0;
+  __syncthreads();
+  if (tid == 0) {
+    float M = -INFINITY;
+    for (int i = 0; i < kChunkWaves; ++i) M = fmaxf(M, red_m[i]);
+    float S = 0.f;
+    for (int i = 0; i < kChunkWaves; ++i)
+      if (red_m[i] != -INFINITY) S += red_s[i] * __builtin_amdgcn_exp2f((red_m[i] - M) * 1.4426950408889634f);
+    cstat[static_cast<size_t>(row) * nch + c] = make_float2(M, S);
+  }
+  unsigned long long* out = clist + (static_cast<size_t>(row) * nch + c) * kSlots;
+  if (K <= 0) {
+    if (tid < kSlots) out[tid] = 0ull;
+    return;
+  }
+  unsigned long long Tk = wt[0];
+#pragma unroll
+  for (int i = 1; i < kChunkWaves; ++i) Tk = umin64(Tk, wt[i]);
+  // (Tk == 0 when a wave holds fewer than k keys: every key is gathered)
+#pragma unroll
+  for (int e = 0; e < IPT; ++e) {
+    if (ok[e]) {
+      const unsigned long long key = make_comp(z[e], static_cast<uint32_t>(tok(e)));
+      if (key >= Tk) {
+        const int slot = atomicAdd(&s_count, 1);
+        if (slot < kCap) cand[slot] = key;
+      }
     }
   }
-  block_topk<kChunkThreads, kMergeItems>(items, K, sel, sm);
-  if (tid < kSlots) {
-    const unsigned long long k = sel[tid];
-    float lq = -INFINITY;
-    int id = -1;
-    if (k != 0ull) {
-      const float zz = key_float(static_cast<uint32_t>(k >> 32));
-      const float M = s_M;
-      id = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(k));
-      lq = (M == -INFINITY || zz == -INFINITY) ? -INFINITY : (zz - M) - s_lnS;
+  __syncthreads();
+  const int C = s_count;
+  if (C <= kCap) {
+    for (int e = tid; e < C; e += kChunkThreads) {
+      const unsigned long long k = cand[e];
+      const int rank = count_greater(cand, C, k);
+      if (rank < K) sel[rank] = k;
     }
-    top_logq[static_cast<size_t>(row) * kSlots + tid] = lq;
-    top_id[static_cast<size_t>(row) * kSlots + tid] = id;
+  } else {
+    // exact radix select of the K-th largest key, 8 bits at a time
+    unsigned long long prefix = 0ull, mask = 0ull;
+    int krem = K;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      for (int i = tid; i < 256; i += kChunkThreads) hist[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < IPT; ++e) {
+        if (ok[e]) {
+          const unsigned long long key = make_comp(z[e], static_cast<uint32_t>(tok(e)));
+          if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255ull], 1u);
+        }
+      }
+      __syncthreads();
+      if (tid < kWave) {
+        unsigned cc[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) cc[b] = hist[4 * lane + b];
+        const unsigned sc = cc[0] + cc[1] + cc[2] + cc[3];
+        unsigned above = sc;  // keys in this lane's bins and all higher bins
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+          const unsigned o = __shfl_down(above, d, kWave);
+          if (lane + d < kWave) above += o;
+        }
+        above -= sc;
+#pragma unroll
+        for (int b = 3; b >= 0; --b) {
+          if (above < static_cast<unsigned>(krem) && static_cast<unsigned>(krem) <= above + cc[b]) {
+            s_prefix = prefix | (static_cast<unsigned long long>(4 * lane + b) << shift);
+            s_krem = krem - static_cast<int>(above);
+            s_done = cc[b] == static_cast<unsigned>(krem) - above ? 1 : 0;
+          }
+          above += cc[b];
+        }
+      }
+      __syncthreads();
+      prefix = s_prefix;
+      krem = s_krem;
+      const int done = s_done;
+      mask |= 0xFFull << shift;
+      __syncthreads();
+      if (done) break;
+    }
+    // exactly K keys are >= prefix (keys are distinct)
+    if (tid == 0) s_count = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < IPT; ++e) {
+      if (ok[e]) {
+        const unsigned long long key = make_comp(z[e], static_cast<uint32_t>(tok(e)));
+        if (key >= prefix) {
+          const int slot = atomicAdd(&s_count, 1);
+          if (slot < kSlots) cand[slot] = key;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < K) sel[count_greater(cand, K, cand[tid])] = cand[tid];
   }
+  __syncthreads();
+  if (tid < kSlots) out[tid] = sel[tid];
 }
 
-__global__ __launch_bounds__(4 * kWave) void build_tree_kernel(
-    const float* __restrict__ top_logq, const int32_t* __restrict__ top_id,
+__global__ __launch_bounds__(kMaxChunks * kWave) void build_tree_kernel(
+    const float2* __restrict__ cstat, const unsigned long long* __restrict__ clist, int nch,
     const int32_t* __restrict__ root_token, int L, int V, int N, int32_t* __restrict__ parent,
     int32_t* __restrict__ depth_out, int32_t* __restrict__ token_out,
     uint64_t* __restrict__ anc_out, float* __restrict__ score_out,
@@ -343,21 +337,72 @@ __global__ __launch_bounds__(4 * kWave) void build_tree_kernel(
 
   const int s = blockIdx.x, lane = lane_id(), wv = threadIdx.x / kWave;
 
-  // the ranked lists of every offset
-  {
-    float vq[GLANCE_MAX_L * kSlots / (4 * kWave)];
-    int vt[GLANCE_MAX_L * kSlots / (4 * kWave)];
+  // ---- wave j ranks offset j from its chunk lists (sorted, lane l holds entry
+  // l of each).  With k = ceil(K / nch), the K-th largest of the lists' k
+  // leading entries, T, bounds the offset's K-th largest key from below (K
+  // keys >= T among them); the entries >= T, a prefix of each list, are
+  // gathered (about K) and ranked exactly by counting.
+  // per offset: up to 128 leading entries, then up to nch * 64 candidates
+  __shared__ __attribute__((aligned(16))) unsigned long long mcand[GLANCE_MAX_L][128 + kMaxChunks * kSlots];
+  __shared__ unsigned long long mthr[GLANCE_MAX_L];
+  if (wv < L) {
+    const int j = wv;
+    const size_t row = static_cast<size_t>(s) * L + j;
+    const int K = k_of(N, V, j);
+    unsigned long long e[kMaxChunks];
 #pragma unroll
-    for (int u = 0; u < GLANCE_MAX_L * kSlots / (4 * kWave); ++u) {
-      const int e = u * 4 * kWave + threadIdx.x;
-      vq[u] = e < L * kSlots ? top_logq[static_cast<size_t>(s) * L * kSlots + e] : -INFINITY;
-      vt[u] = e < L * kSlots ? top_id[static_cast<size_t>(s) * L * kSlots + e] : -1;
+    for (int c = 0; c < kMaxChunks; ++c)
+      e[c] = c < nch ? clist[(row * nch + c) * kSlots + lane] : 0ull;
+    const float2 st = lane < nch ? cstat[row * nch + lane] : make_float2(-INFINITY, 0.f);
+    const float M = wave_max(st.x);
+    float t = (M == -INFINITY || st.y <= 0.f) ? 0.f : st.y * __builtin_amdgcn_exp2f((st.x - M) * 1.4426950408889634f);
+    t = wave_sum(t);
+    const float lnS = logf(t);
+    unsigned long long* mc = mcand[j];
+    const int kc = K > 0 ? (K + nch - 1) / nch : 1;
+    const int n1 = nch * kc;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+      if (c < nch && lane < kc) mc[c * kc + lane] = e[c];
+    if (lane == 0) mthr[j] = 0ull;
+    __builtin_amdgcn_wave_barrier();  // one wave: LDS is in order
+    for (int x0 = 0; x0 < n1; x0 += 2 * kWave) {
+      const int xa = x0 + lane, xb = x0 + kWave + lane;
+      const unsigned long long va = xa < n1 ? mc[xa] : 0ull, vb = xb < n1 ? mc[xb] : 0ull;
+      int ra, rb;
+      rank2(mc, n1, va, vb, ra, rb);
+      if (xa < n1 && va != 0ull && ra == K - 1) mthr[j] = va;
+      if (xb < n1 && vb != 0ull && rb == K - 1) mthr[j] = vb;
     }
+    __builtin_amdgcn_wave_barrier();
+    const unsigned long long Tm = mthr[j];  // 0 when fewer than K leading entries: take all
+    unsigned long long* cs = mc + 128;
+    int C = 0;
 #pragma unroll
-    for (int u = 0; u < GLANCE_MAX_L * kSlots / (4 * kWave); ++u) {
-      const int e = u * 4 * kWave + threadIdx.x;
-      lq[e / kSlots][e % kSlots] = vq[u];
-      tk[e / kSlots][e % kSlots] = vt[u];
+    for (int c = 0; c < kMaxChunks; ++c) {
+      const bool take = c < nch && e[c] != 0ull && e[c] >= Tm;
+      const unsigned long long bal = __ballot(take);
+      if (take) cs[C + __popcll(bal & ((1ull << lane) - 1ull))] = e[c];
+      C += __popcll(bal);
+    }
+    lq[j][lane] = -INFINITY;
+    tk[j][lane] = -1;
+    __builtin_amdgcn_wave_barrier();
+    for (int x0 = 0; x0 < C; x0 += 2 * kWave) {
+      const int xa = x0 + lane, xb = x0 + kWave + lane;
+      const unsigned long long va = xa < C ? cs[xa] : 0ull, vb = xb < C ? cs[xb] : 0ull;
+      int ra, rb;
+      rank2(cs, C, va, vb, ra, rb);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const unsigned long long k = h ? vb : va;
+        const int rank = h ? rb : ra;
+        if ((h ? xb : xa) < C && rank < K) {
+          const float zz = key_float(static_cast<uint32_t>(k >> 32));
+          lq[j][rank] = (M == -INFINITY || zz == -INFINITY) ? -INFINITY : (zz - M) - lnS;
+          tk[j][rank] = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(k));
+        }
+      }
     }
   }
   __syncthreads();
@@ -366,24 +411,26 @@ __global__ __launch_bounds__(4 * kWave) void build_tree_kernel(
   // ---- best-first selection.  Lane 0 is the root, lane i the i-th selected
   // node; each lane offers the best not-yet-selected child of its node (the
   // next entry of the next offset's ranked list).  Equal scores: smaller depth,
-  // then the earlier-selected parent (smaller lane); one offer per lane.
+  // then the earlier-selected parent (smaller lane); one offer per lane.  The
+  // loop body is branch-free per lane: the winner p and the new node i update
+  // through selects, and the log q after each new offer is read from LDS one
+  // iteration ahead of its first possible use.
   const int R = N + 1;
   const float fq = lane < L ? lq[lane][0] : -INFINITY;  // first entry of each offset
-  float n_score = 0.f;
-  int n_depth = 0, n_par = -1, n_rank = 0, n_next = 0;
-  float c_score = 0.f, nx_q = -INFINITY;
-  uint32_t c_hi = 0u;
-  // the candidate is child n_next of this node with log q `q`; prefetch the next one
-  auto offer = [&](float q) {
-    c_hi = 0u;
-    if (n_depth < L && n_next < k_of(N, V, n_depth) && q != -INFINITY) {
-      c_score = n_score + q;
-      c_hi = float_key(c_score);
-    }
-    const int nn = n_next + 1;
-    nx_q = (n_depth < L && nn < kSlots) ? lq[n_depth][nn] : -INFINITY;
-  };
-  if (lane == 0) offer(fq);
+  const int kd = lane < L ? k_of(N, V, lane) : 0;        // entries of each offset's list
+  float n_score = 0.f;   // this node's score
+  int n_depth = 0, n_par = -1, n_rank = 0;
+  int n_next = 0;        // rank of the offered child in list n_depth
+  float c_score = 0.f;   // the offered child's score
+  uint32_t c_hi = 0u;    // its order key (0: no offer)
+  float nx_q = -INFINITY;  // log q of the child after the offered one
+  if (lane == 0 && L > 0) {
+    c_score = fq;
+    c_hi = (kd > 0 && fq != -INFINITY) ? float_key(fq) : 0u;
+    nx_q = lq[0][1];
+  }
+  float pend = -INFINITY;
+  bool upd = false;
   int n_pop = 0;
   for (int i = 1; i <= N; ++i) {
     const uint32_t mh = wave_umax(c_hi);
@@ -398,19 +445,30 @@ __global__ __launch_bounds__(4 * kWave) void build_tree_kernel(
     const float w_score = readlane_f(c_score, p);
     const int w_depth = readlane_i(n_depth, p) + 1;
     const int w_rank = readlane_i(n_next, p);
-    const float q0 = readlane_f(fq, w_depth < L ? w_depth : 0);
-    if (lane == i) {
-      n_score = w_score;
-      n_depth = w_depth;
-      n_par = p;
-      n_rank = w_rank;
-      n_next = 0;
-      offer(w_depth < L ? q0 : -INFINITY);
-    }
-    if (lane == p) {
-      ++n_next;
-      offer(nx_q);
-    }
+    const int wl_ = w_depth < L ? w_depth : 0;
+    const float q0 = readlane_f(fq, wl_);
+    const int k0 = readlane_i(kd, wl_);
+    nx_q = upd ? pend : nx_q;
+    const bool isp = lane == p, isi = lane == i;
+    // lane p: its next child; lane i: the new node's first child
+    const int np = n_next + 1;
+    const float sp = n_score + nx_q;
+    const bool okp = n_depth < L && np < k_of(N, V, n_depth) && nx_q != -INFINITY;
+    const float si = w_score + q0;
+    const bool oki = w_depth < L && k0 > 0 && q0 != -INFINITY;
+    const uint32_t kp = okp ? float_key(sp) : 0u;
+    const uint32_t ki = oki ? float_key(si) : 0u;
+    n_score = isi ? w_score : n_score;
+    n_depth = isi ? w_depth : n_depth;
+    n_par = isi ? p : n_par;
+    n_rank = isi ? w_rank : n_rank;
+    n_next = isi ? 0 : (isp ? np : n_next);
+    c_score = isi ? si : (isp ? sp : c_score);
+    c_hi = isi ? ki : (isp ? kp : c_hi);
+    // log q of the child after the new offer (used from the next iteration on)
+    upd = isp || isi;
+    const int rr = n_next + 1;
+    pend = (n_depth < L && rr < kSlots) ? lq[n_depth < L ? n_depth : 0][rr < kSlots ? rr : 0] : -INFINITY;
     n_pop = i;
   }
 
@@ -468,20 +526,35 @@ __global__ __launch_bounds__(4 * kWave) void build_tree_kernel(
 }  // namespace
 
 // Host side -------------------------------------------------------------------
+namespace {
+template <typename T>
+void launch_chunks(int nv, dim3 ga, const T* logits, int L, int V, int N, int nch, float2* cstat,
+                   unsigned long long* clist, hipStream_t st) {
+  switch (nv) {
+#define GLANCE_CHUNK_CASE(n) \
+  case n: lsm_chunk_kernel<T, n><<<ga, kChunkThreads, 0, st>>>(logits, L, V, N, nch, cstat, clist); break;
+    GLANCE_CHUNK_CASE(1)
+    GLANCE_CHUNK_CASE(2)
+    GLANCE_CHUNK_CASE(3)
+    GLANCE_CHUNK_CASE(4)
+    GLANCE_CHUNK_CASE(5)
+    GLANCE_CHUNK_CASE(6)
+    GLANCE_CHUNK_CASE(7)
+    GLANCE_CHUNK_CASE(8)
+#undef GLANCE_CHUNK_CASE
+    default: break;
+  }
+}
+}  // namespace
+
 TreeWs tree_ws_layout(int nseq, int L, int V) {
+  (void)V;
   TreeWs w;
-  // chunks of 256 threads x 2 vectors of 16 bytes: 4096 bf16 or 2048 fp32
-  // logits; the merge takes up to 64 chunks per row (V <= 2^18 bf16, 2^17 fp32)
-  w.chunk = kChunkThreads * kChunkVecs * 4;
-  w.nch = (V + w.chunk - 1) / w.chunk;
   const size_t r = static_cast<size_t>(nseq) * L;
   auto up = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
-  const int nch_max = w.nch;
   w.off_cstat = 0;
-  w.off_clist = up(r * nch_max * 2 * sizeof(float));
-  w.off_logq = w.off_clist + up(r * nch_max * kSlots * sizeof(unsigned long long));
-  w.off_id = w.off_logq + up(r * kSlots * sizeof(float));
-  w.bytes = w.off_id + up(r * kSlots * sizeof(int32_t));
+  w.off_clist = up(r * kMaxChunks * sizeof(float2));
+  w.bytes = w.off_clist + up(r * kMaxChunks * kSlots * sizeof(unsigned long long));
   return w;
 }
 
@@ -491,25 +564,23 @@ glance_status launch_build_tree(const void* logits, int dtype, const int32_t* ro
                                 int32_t* n_valid, void* ws, hipStream_t st) {
   const TreeWs w = tree_ws_layout(nseq, L, V);
   char* base = static_cast<char*>(ws);
-  float* cstat = reinterpret_cast<float*>(base + w.off_cstat);
+  float2* cstat = reinterpret_cast<float2*>(base + w.off_cstat);
   unsigned long long* clist = reinterpret_cast<unsigned long long*>(base + w.off_clist);
-  // chunk size in logits: 256 threads x 2 x 16 bytes
+  // at most kMaxChunks chunks of 256 threads x nv vectors per offset row
   const int E = dtype == GLANCE_BF16 ? 8 : 4;
-  const int nch = (V + kChunkThreads * kChunkVecs * E - 1) / (kChunkThreads * kChunkVecs * E);
-  dim3 ga(nch, L, nseq);
+  const int per_vec = kChunkThreads * E;
+  int nv = (V + per_vec * kMaxChunks - 1) / (per_vec * kMaxChunks);
+  if (nv < 1) nv = 1;
+  if (nv > kMaxVec) return GLANCE_ERR_UNSUPPORTED;
+  const int nch = (V + per_vec * nv - 1) / (per_vec * nv);
+  const dim3 ga(nch, L, nseq);
   if (dtype == GLANCE_BF16)
-    lsm_chunk_kernel<uint16_t><<<ga, kChunkThreads, 0, st>>>(static_cast<const uint16_t*>(logits), L, V, N,
-                                                             nch, cstat, clist);
+    launch_chunks<uint16_t>(nv, ga, static_cast<const uint16_t*>(logits), L, V, N, nch, cstat, clist, st);
   else
-    lsm_chunk_kernel<float><<<ga, kChunkThreads, 0, st>>>(static_cast<const float*>(logits), L, V, N, nch,
-                                                          cstat, clist);
+    launch_chunks<float>(nv, ga, static_cast<const float*>(logits), L, V, N, nch, cstat, clist, st);
   GLANCE_LAUNCH_CHECK();
-  float* logq = reinterpret_cast<float*>(base + w.off_logq);
-  int32_t* id = reinterpret_cast<int32_t*>(base + w.off_id);
-  lsm_merge_kernel<<<dim3(L, nseq), kChunkThreads, 0, st>>>(L, V, N, nch, cstat, clist, logq, id);
-  GLANCE_LAUNCH_CHECK();
-  build_tree_kernel<<<nseq, 4 * kWave, 0, st>>>(logq, id, root, L, V, N, parent, depth, token, anc,
-                                                score, n_valid);
+  build_tree_kernel<<<nseq, kMaxChunks * kWave, 0, st>>>(cstat, clist, nch, root, L, V, N, parent,
+                                                          depth, token, anc, score, n_valid);
   GLANCE_LAUNCH_CHECK();
   return GLANCE_OK;
 }
