@@ -9,14 +9,15 @@
 // bf16 path (head_dim 128, gfx950 MFMA v_mfma_f32_32x32x16_bf16).  Grid
 // (prefix splits + 1, Hkv x query blocks, rounds), 512 threads: the queries of
 // one KV head are its Hq/Hkv query heads times the round's rows (<= 256 per
-// work-group, 32 per wave).  Split c streams prefix keys [c*split, (c+1)*split)
-// in blocks of 64: K is staged in LDS as [key][dim], V transposed as [dim][key];
-// each wave forms S^T = K Q^T (one query per lane, so the row max and sum of the
-// online softmax stay inside a lane and its partner lane l^32), rounds P to bf16
-// into its own LDS tile and accumulates O^T += V^T P^T.  The extra split n_split
-// takes the round's tree rows as keys: the rotated bf16 K and bf16 V rows the
-// q/k/v projection wrote (a storage point), masked by anc.  Each
-// (split, query) leaves (max, sum, unnormalised O); attn_combine merges them.
+// work-group, 32 per wave).  Split c takes prefix keys [c*128, (c+1)*128) as
+// one tile: the query, K and V loads are all issued before any is used; K is
+// staged in LDS as [key][dim], V transposed as [dim][key]; each wave forms
+// S^T = K Q^T (one query per lane, so the row max and sum stay inside a lane
+// and its partner lane l^32), rounds P to bf16 into its own LDS tile and forms
+// O^T = V^T P^T.  The extra split n_split takes the round's tree rows as keys:
+// the rotated bf16 K and bf16 V rows the q/k/v projection wrote (a storage
+// point), masked by anc.  Each (split, query) leaves (max, sum, unnormalised
+// O); attn_combine merges them.
 //
 // fp32 path (tiny shapes): one work-group per (row, query head), scores in LDS,
 // plain fp32 loops.
@@ -30,10 +31,9 @@ namespace {
 constexpr int kAThreads = 512;
 constexpr int kQWave = 32;
 constexpr int kQBlock = 256;
-constexpr int kKB = 64;
+constexpr int kKT = 128;         // keys per work-group tile (one prefix split)
 constexpr int kHD = 128;         // head_dim of the bf16 path
-constexpr int kKPad = kHD + 8;   // Ks row stride (bf16)
-constexpr int kVPad = kKB + 8;   // Vt / Ps row stride (bf16)
+constexpr int kTPad = 136;       // row stride of the K, V^T and P tiles (bf16)
 constexpr int kRec = kHD + 4;    // partial record: m, l, -, -, o[128]
 
 // position P + depth of a row, clamped into the cos/sin tables
@@ -48,9 +48,9 @@ __device__ __forceinline__ float rope_pair(const float* x, int i, int half, floa
 }
 
 __global__ __launch_bounds__(kAThreads) void tree_attn_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kKB][kKPad];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kHD][kVPad];
-  __shared__ __attribute__((aligned(16))) uint16_t Ps[kAThreads / kWave][kQWave][kVPad];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kKT][kTPad];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[kHD][kTPad];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[kAThreads / kWave][kQWave][kTPad];
 
   const int c = blockIdx.x, s = blockIdx.z;
   const int h = blockIdx.y % a.Hkv, qb = blockIdx.y / a.Hkv;
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kAThreads) void tree_attn_bf16_kernel(AttnArgs a) {
   const int64_t kv0 = a.kv_offsets[s];
   const int P = static_cast<int>(a.kv_offsets[s + 1] - kv0);
 
-  // ---- this lane's query: q index, row, head; rotated and rounded to bf16
+  // ---- this lane's query: q index, row, head (rotated and rounded by the projection)
   const int q = qb * kQBlock + w * kQWave + j;
   const bool qvalid = q < Qn;
   const int r = qvalid ? q / G : 0;
@@ -69,6 +69,18 @@ __global__ __launch_bounds__(kAThreads) void tree_attn_bf16_kernel(AttnArgs a) {
   const int grow = s * a.n_rows + r;
   const bool qlive = qvalid && a.token[grow] >= 0;
   const uint64_t qanc = qvalid ? a.anc[grow] : 0ull;
+
+  int kbeg, kend;
+  if (tree_split) {
+    kbeg = 0;
+    kend = a.n_rows;
+  } else {
+    kbeg = c * a.split;
+    kend = min(kbeg + a.split, P);
+  }
+  const int nk = kend - kbeg;  // <= kKT keys in this tile
+
+  // ---- every load of the tile issued up front: the query, then K and V
   bf16x8 qf[8];
   {
     const uint16_t* xq = static_cast<const uint16_t*>(a.q) + static_cast<size_t>(grow) * a.Hq * kHD + qh * kHD;
@@ -79,128 +91,103 @@ __global__ __launch_bounds__(kAThreads) void tree_attn_bf16_kernel(AttnArgs a) {
       qf[ks] = __builtin_bit_cast(bf16x8, u);
     }
   }
-
-  int kbeg, kend;
-  if (tree_split) {
-    kbeg = 0;
-    kend = a.n_rows;
-  } else {
-    kbeg = c * a.split;
-    kend = min(kbeg + a.split, P);
-  }
-  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(kHD));
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x16 acc_o[4] = {};
-
-  for (int k0 = kbeg; k0 < kend; k0 += kKB) {
-    // ---- stage K [key][dim] and V^T [dim][key] for keys k0 .. k0+63
+  constexpr int kPass = kKT * (kHD / 8) / kAThreads;  // 16-byte pieces per thread
+  uint4 kb_[kPass], vb_[kPass];
+  {
+    const uint16_t* kbase = tree_split ? static_cast<const uint16_t*>(a.tree_k)
+                                       : static_cast<const uint16_t*>(a.k_cache);
+    const uint16_t* vbase = tree_split ? static_cast<const uint16_t*>(a.tree_v)
+                                       : static_cast<const uint16_t*>(a.v_cache);
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const int kr = pass * 32 + (tid >> 4);
-      const int col = (tid & 15) * 8;
-      const int key = k0 + kr;
-      uint16_t kv[8], vv[8];
-      if (key < kend) {
-        const uint16_t* kb = tree_split ? static_cast<const uint16_t*>(a.tree_k)
-                                        : static_cast<const uint16_t*>(a.k_cache);
-        const uint16_t* vb = tree_split ? static_cast<const uint16_t*>(a.tree_v)
-                                        : static_cast<const uint16_t*>(a.v_cache);
-        const int64_t krow = tree_split ? static_cast<int64_t>(s) * a.n_rows + key : kv0 + key;
+    for (int pass = 0; pass < kPass; ++pass) {
+      const int idx = pass * kAThreads + tid;
+      const int kr = idx >> 4, col = (idx & 15) * 8;
+      kb_[pass] = make_uint4(0, 0, 0, 0);
+      vb_[pass] = make_uint4(0, 0, 0, 0);
+      if (kr < nk) {
+        const int64_t krow = tree_split ? static_cast<int64_t>(s) * a.n_rows + kr : kv0 + kbeg + kr;
         const size_t off = (static_cast<size_t>(krow) * a.Hkv + h) * kHD + col;
-        const uint4 ku = load_stream(kb + off);
-        const uint4 vu = load_stream(vb + off);
-        const uint32_t kw[4] = {ku.x, ku.y, ku.z, ku.w};
-        const uint32_t vw[4] = {vu.x, vu.y, vu.z, vu.w};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          kv[2 * t] = kw[t] & 0xFFFF;
-          kv[2 * t + 1] = kw[t] >> 16;
-          vv[2 * t] = vw[t] & 0xFFFF;
-          vv[2 * t + 1] = vw[t] >> 16;
-        }
-      } else {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) kv[t] = vv[t] = 0;
+        kb_[pass] = load_stream(kbase + off);
+        vb_[pass] = load_stream(vbase + off);
       }
-      uint4 ku;
-      ku.x = kv[0] | (static_cast<uint32_t>(kv[1]) << 16);
-      ku.y = kv[2] | (static_cast<uint32_t>(kv[3]) << 16);
-      ku.z = kv[4] | (static_cast<uint32_t>(kv[5]) << 16);
-      ku.w = kv[6] | (static_cast<uint32_t>(kv[7]) << 16);
-      *reinterpret_cast<uint4*>(&Ks[kr][col]) = ku;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) Vt[col + t][kr] = vv[t];
     }
-    __syncthreads();
+  }
+  // K as [key][dim]; V transposed to [dim][key], its 8-key blocks XOR-swizzled by
+  // the dim's 8-row block so that the transposing stores spread over the banks
+#pragma unroll
+  for (int pass = 0; pass < kPass; ++pass) {
+    const int idx = pass * kAThreads + tid;
+    const int kr = idx >> 4, col = (idx & 15) * 8;
+    *reinterpret_cast<uint4*>(&Ks[kr][col]) = kb_[pass];
+    const uint32_t vw[4] = {vb_[pass].x, vb_[pass].y, vb_[pass].z, vb_[pass].w};
+    const int kcol = 8 * ((kr >> 3) ^ ((col >> 3) & 15)) + (kr & 7);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      Vt[col + 2 * t][kcol] = static_cast<uint16_t>(vw[t] & 0xFFFF);
+      Vt[col + 2 * t + 1][kcol] = static_cast<uint16_t>(vw[t] >> 16);
+    }
+  }
+  __syncthreads();
 
-    // ---- S^T = K Q^T for 64 keys x this wave's 32 queries
-    f32x16 acc_s[2] = {};
+  // ---- S^T = K Q^T: kKT keys x this wave's 32 queries
+  f32x16 acc_s[kKT / 32] = {};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < kKT / 32; ++kb) {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Ks[kb * 32 + j][ks * 16 + 8 * g]);
-        acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], acc_s[kb], 0, 0, 0);
-      }
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Ks[kb * 32 + j][ks * 16 + 8 * g]);
+      acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], acc_s[kb], 0, 0, 0);
     }
-    // element v of acc_s[kb]: key k0 + 32 kb + 8 (v/4) + 4 g + v%4, query j
-    float mloc = -INFINITY;
+  }
+  // element v of acc_s[kb]: key kb*32 + 8 (v/4) + 4 g + v%4 of the tile, query j
+  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(kHD));
+  float m = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < kKT / 32; ++kb) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = k0 + kb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-        bool vis = key < kend;
-        if (tree_split) vis = vis && ((qanc >> key) & 1ull);
-        const float sv = vis ? acc_s[kb][v] * scale_log2 : -INFINITY;
-        acc_s[kb][v] = sv;
-        mloc = fmaxf(mloc, sv);
-      }
+    for (int v = 0; v < 16; ++v) {
+      const int key = kb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+      bool vis = key < nk;
+      if (tree_split) vis = vis && ((qanc >> key) & 1ull);
+      const float sv = vis ? acc_s[kb][v] * scale_log2 : -INFINITY;
+      acc_s[kb][v] = sv;
+      m = fmaxf(m, sv);
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-    const float m_new = fmaxf(m_run, mloc);
-    float rowsum = 0.f;
-    uint16_t pb[2][16];
+  }
+  m = fmaxf(m, __shfl_xor(m, 32, kWave));
+  float lsum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < kKT / 32; ++kb) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = (m_new == -INFINITY) ? 0.f : exp2f(acc_s[kb][v] - m_new);
-        pb[kb][v] = f32_to_bf16(p);
-        rowsum += bf16_to_f32(pb[kb][v]);
+    for (int vg = 0; vg < 4; ++vg) {
+      uint16_t pb[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float p = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(acc_s[kb][4 * vg + t] - m);
+        pb[t] = f32_to_bf16(p);
+        lsum += bf16_to_f32(pb[t]);
       }
+      uint2 u;
+      u.x = pb[0] | (static_cast<uint32_t>(pb[1]) << 16);
+      u.y = pb[2] | (static_cast<uint32_t>(pb[3]) << 16);
+      *reinterpret_cast<uint2*>(&Ps[w][j][kb * 32 + 8 * vg + 4 * g]) = u;
     }
-    rowsum += __shfl_xor(rowsum, 32, kWave);
-    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
-    l_run = l_run * alpha + rowsum;
-    m_run = m_new;
+  }
+  lsum += __shfl_xor(lsum, 32, kWave);
+  __builtin_amdgcn_wave_barrier();  // the wave's own P tile: same-wave LDS accesses are in order
+
+  // ---- O^T = V^T P^T
+  f32x16 acc_o[4] = {};
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 4; ++db) {
+    const int dim = db * 32 + j;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
-    // P (bf16) -> this wave's LDS tile, [query][key]
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int vg = 0; vg < 4; ++vg) {
-        uint2 u;
-        u.x = pb[kb][4 * vg] | (static_cast<uint32_t>(pb[kb][4 * vg + 1]) << 16);
-        u.y = pb[kb][4 * vg + 2] | (static_cast<uint32_t>(pb[kb][4 * vg + 3]) << 16);
-        *reinterpret_cast<uint2*>(&Ps[w][j][kb * 32 + 8 * vg + 4 * g]) = u;
-      }
+    for (int ks = 0; ks < kKT / 16; ++ks) {
+      const int kblk = (ks * 16 + 8 * g) >> 3;
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Vt[dim][8 * (kblk ^ ((dim >> 3) & 15))]);
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&Ps[w][j][ks * 16 + 8 * g]);
+      acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc_o[db], 0, 0, 0);
     }
-    __syncthreads();
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Vt[db * 32 + j][ks * 16 + 8 * g]);
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&Ps[w][j][ks * 16 + 8 * g]);
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc_o[db], 0, 0, 0);
-      }
-    }
-    __syncthreads();
   }
 
   // ---- partial record of (split, query): m (log2 units), l, unnormalised O
@@ -209,8 +196,8 @@ __global__ __launch_bounds__(kAThreads) void tree_attn_bf16_kernel(AttnArgs a) {
                  ((static_cast<size_t>(s) * a.Hkv + h) * (a.n_split + 1) + c) * static_cast<size_t>(Qn) * kRec +
                  static_cast<size_t>(q) * kRec;
     if (g == 0) {
-      rec[0] = m_run;
-      rec[1] = l_run;
+      rec[0] = m;
+      rec[1] = lsum;
     }
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -225,7 +212,7 @@ __global__ __launch_bounds__(kAThreads) void tree_attn_bf16_kernel(AttnArgs a) {
 
 // Merge the split partials of every (row, query head) into the attention output:
 // one work-group per row and query head, one thread per head dimension, splits
-// folded in order with a running maximum.
+// folded in order in batches of 16 with a running maximum.
 __global__ __launch_bounds__(kHD) void attn_combine_kernel(AttnArgs a) {
   const int grow = blockIdx.x, qh = blockIdx.y, dim = threadIdx.x;
   const int s = grow / a.n_rows, r = grow % a.n_rows;
@@ -238,21 +225,33 @@ __global__ __launch_bounds__(kHD) void attn_combine_kernel(AttnArgs a) {
                                      static_cast<size_t>(Qn) + q) * kRec;
     const size_t stride = static_cast<size_t>(Qn) * kRec;
     const int ns = a.n_split + 1;
-    // pass 1: the largest split maximum (splits without keys have l = 0)
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int c = 0; c < ns; ++c) {
-      const float m = rec[c * stride], l = rec[c * stride + 1];
-      M = fmaxf(M, l > 0.f ? m : -INFINITY);
-    }
-    // pass 2: rescaled sums, loads independent of each other
-    float Ls = 0.f, acc = 0.f;
-#pragma unroll 8
-    for (int c = 0; c < ns; ++c) {
-      const float m = rec[c * stride], l = rec[c * stride + 1], v = rec[c * stride + 4 + dim];
-      const float f = l > 0.f ? exp2f(m - M) : 0.f;
-      Ls += l * f;
-      acc += v * f;
+    // 16 splits at a time: every load of the batch issued first, then the
+    // batch maximum, then the rescaled sums
+    float M = -INFINITY, Ls = 0.f, acc = 0.f;
+    for (int c0 = 0; c0 < ns; c0 += 16) {
+      float mm[16], ll[16], vv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const size_t cc = static_cast<size_t>(min(c0 + u, ns - 1)) * stride;
+        mm[u] = rec[cc];
+        ll[u] = rec[cc + 1];
+        vv[u] = rec[cc + 4 + dim];
+      }
+      float Mb = M;
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (c0 + u < ns && ll[u] > 0.f) Mb = fmaxf(Mb, mm[u]);
+      const float fo = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mb);
+      Ls *= fo;
+      acc *= fo;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        // splits without visible keys have l = 0 and contribute nothing
+        const float f = (c0 + u < ns && ll[u] > 0.f) ? __builtin_amdgcn_exp2f(mm[u] - Mb) : 0.f;
+        Ls += ll[u] * f;
+        acc += vv[u] * f;
+      }
+      M = Mb;
     }
     o = acc / Ls;
   }
@@ -375,7 +374,7 @@ int attn_split_len(int64_t max_prefix, int nseq, int Hkv) {
   (void)max_prefix;
   (void)nseq;
   (void)Hkv;
-  return 128;
+  return kKT;  // one tile per split work-group
 }
 
 size_t attn_part_floats(int nseq, int n_rows, int Hq, int Hkv, int D, int n_split) {
