@@ -330,7 +330,7 @@ __global__ __launch_bounds__(kMaxChunks * kWave) void build_tree_kernel(
     int32_t* __restrict__ depth_out, int32_t* __restrict__ token_out,
     uint64_t* __restrict__ anc_out, float* __restrict__ score_out,
     int32_t* __restrict__ n_valid_out) {
-  __shared__ float lq[GLANCE_MAX_L][kSlots];
+  __shared__ float lq[GLANCE_MAX_L + 1][kSlots];  // row L: -inf (depth-L nodes have no children)
   __shared__ int tk[GLANCE_MAX_L][kSlots];
   __shared__ int row_of_lane[kSlots];
   __shared__ unsigned long long anc_row[kSlots];
@@ -345,6 +345,7 @@ __global__ __launch_bounds__(kMaxChunks * kWave) void build_tree_kernel(
   // per offset: up to 128 leading entries, then up to nch * 64 candidates
   __shared__ __attribute__((aligned(16))) unsigned long long mcand[GLANCE_MAX_L][128 + kMaxChunks * kSlots];
   __shared__ unsigned long long mthr[GLANCE_MAX_L];
+  if (wv == 0) lq[L][lane] = -INFINITY;
   if (wv < L) {
     const int j = wv;
     const size_t row = static_cast<size_t>(s) * L + j;
@@ -416,19 +417,15 @@ __global__ __launch_bounds__(kMaxChunks * kWave) void build_tree_kernel(
   // through selects, and the log q after each new offer is read from LDS one
   // iteration ahead of its first possible use.
   const int R = N + 1;
-  const float fq = lane < L ? lq[lane][0] : -INFINITY;  // first entry of each offset
-  const int kd = lane < L ? k_of(N, V, lane) : 0;        // entries of each offset's list
+  // order keys: float_key(score) - float_key(-inf), so no offer (score -inf) is 0
+  constexpr uint32_t kNegInfKey = 0x007FFFFFu;
+  const float fq = lane <= L ? lq[lane][0] : -INFINITY;  // first entry of each offset
   float n_score = 0.f;   // this node's score
-  int n_depth = 0, n_par = -1, n_rank = 0;
-  int n_next = 0;        // rank of the offered child in list n_depth
-  float c_score = 0.f;   // the offered child's score
-  uint32_t c_hi = 0u;    // its order key (0: no offer)
-  float nx_q = -INFINITY;  // log q of the child after the offered one
-  if (lane == 0 && L > 0) {
-    c_score = fq;
-    c_hi = (kd > 0 && fq != -INFINITY) ? float_key(fq) : 0u;
-    nx_q = lq[0][1];
-  }
+  int n_dn = 0;          // depth << 8 | rank of the offered child in list `depth`
+  int n_par = -1, n_rank = 0;
+  float c_score = lane == 0 ? fq : 0.f;  // the offered child's score
+  uint32_t c_hi = lane == 0 ? float_key(fq) - kNegInfKey : 0u;
+  float nx_q = lane == 0 ? lq[0][1] : -INFINITY;  // log q of the child after the offered one
   float pend = -INFINITY;
   bool upd = false;
   int n_pop = 0;
@@ -437,40 +434,36 @@ __global__ __launch_bounds__(kMaxChunks * kWave) void build_tree_kernel(
     if (mh == 0u) break;
     unsigned long long cm = __ballot(c_hi == mh);
     if (__popcll(cm) > 1) {  // equal scores: the smallest child depth, then the lowest lane
-      const uint32_t lo = (c_hi == mh) ? ~static_cast<uint32_t>(n_depth) : 0u;
+      const uint32_t lo = (c_hi == mh) ? ~static_cast<uint32_t>(n_dn >> 8) : 0u;
       const uint32_t ml = wave_umax(lo);
-      cm = __ballot(c_hi == mh && ~static_cast<uint32_t>(n_depth) == ml);
+      cm = __ballot(c_hi == mh && ~static_cast<uint32_t>(n_dn >> 8) == ml);
     }
     const int p = __ffsll(static_cast<long long>(cm)) - 1;
     const float w_score = readlane_f(c_score, p);
-    const int w_depth = readlane_i(n_depth, p) + 1;
-    const int w_rank = readlane_i(n_next, p);
-    const int wl_ = w_depth < L ? w_depth : 0;
-    const float q0 = readlane_f(fq, wl_);
-    const int k0 = readlane_i(kd, wl_);
+    const int w_dn = readlane_i(n_dn, p);
+    const int w_depth = (w_dn >> 8) + 1;
+    const float q0 = readlane_f(fq, w_depth);
     nx_q = upd ? pend : nx_q;
     const bool isp = lane == p, isi = lane == i;
-    // lane p: its next child; lane i: the new node's first child
-    const int np = n_next + 1;
+    // lane p: its next child; lane i: the new node's first child (a -inf log q,
+    // past a list's end or below depth L, gives key 0: no offer)
     const float sp = n_score + nx_q;
-    const bool okp = n_depth < L && np < k_of(N, V, n_depth) && nx_q != -INFINITY;
     const float si = w_score + q0;
-    const bool oki = w_depth < L && k0 > 0 && q0 != -INFINITY;
-    const uint32_t kp = okp ? float_key(sp) : 0u;
-    const uint32_t ki = oki ? float_key(si) : 0u;
+    const uint32_t kp = float_key(sp) - kNegInfKey;
+    const uint32_t ki = float_key(si) - kNegInfKey;
     n_score = isi ? w_score : n_score;
-    n_depth = isi ? w_depth : n_depth;
     n_par = isi ? p : n_par;
-    n_rank = isi ? w_rank : n_rank;
-    n_next = isi ? 0 : (isp ? np : n_next);
+    n_rank = isi ? (w_dn & 255) : n_rank;
+    n_dn = isi ? (w_depth << 8) : (isp ? n_dn + 1 : n_dn);
     c_score = isi ? si : (isp ? sp : c_score);
     c_hi = isi ? ki : (isp ? kp : c_hi);
-    // log q of the child after the new offer (used from the next iteration on)
+    // log q of the child after the new offer, used from the next iteration on
     upd = isp || isi;
-    const int rr = n_next + 1;
-    pend = (n_depth < L && rr < kSlots) ? lq[n_depth < L ? n_depth : 0][rr < kSlots ? rr : 0] : -INFINITY;
+    const int rr = (n_dn & 255) + 1;
+    pend = lq[n_dn >> 8][rr < kSlots ? rr : kSlots - 1];
     n_pop = i;
   }
+  const int n_depth = n_dn >> 8;
 
   // ---- breadth-first layout: rows by (depth, parent row, token id)
   const int n_token = (lane >= 1 && lane <= n_pop) ? tk[n_depth - 1][n_rank] : -1;
