@@ -420,25 +420,12 @@ __global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int
     for (int v = 0; v < 4; ++v) pp[(4 * lg + v) * 64 + mb * 16 + lr] = acc[mb][v];
 }
 
+// Epilogue of one 16-row weight block for activation row gm: x[i] is the
+// block's row i (of the summed K slices).  q/k blocks are rotated (rows i and
+// 8+i are RoPE partners), v rows copied, output-projection rows added to the
+// residual; everything is rounded to bf16.
 template <int EPI>
-__global__ __launch_bounds__(kGThreads) void proj_reduce_kernel(GemmArgs a, int NB, int NGr, int S) {
-  const int grp = blockIdx.x;  // mt * NGr + g
-  const int mt = grp / NGr, g = grp - mt * NGr;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int b = g * 4 + w;
-  if (b >= NB) return;
-  const int m0 = mt * kTileM;
-  // lane l: activation row m0 + l of block b
-  float x[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = 0.f;
-  for (int qq = 0; qq < S; ++qq) {
-    const float* src = a.kpart + ((static_cast<size_t>(grp) * S + qq) * 4 + w) * 1024;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] += src[i * 64 + l];
-  }
-  const int gm = m0 + l;
-  if (gm >= a.M) return;
+__device__ __forceinline__ void proj_store(const GemmArgs& a, int b, int gm, const float (&x)[16]) {
   if constexpr (EPI == EPI_RESID) {
     const int n = b * 16;
     uint4 o[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
@@ -503,6 +490,28 @@ __global__ __launch_bounds__(kGThreads) void proj_reduce_kernel(GemmArgs a, int 
       op[1] = make_uint4(ow[4], ow[5], ow[6], ow[7]);
     }
   }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kGThreads) void proj_reduce_kernel(GemmArgs a, int NB, int NGr, int S) {
+  const int grp = blockIdx.x;  // mt * NGr + g
+  const int mt = grp / NGr, g = grp - mt * NGr;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int b = g * 4 + w;
+  if (b >= NB) return;
+  const int m0 = mt * kTileM;
+  // lane l: activation row m0 + l of block b
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = 0.f;
+  for (int qq = 0; qq < S; ++qq) {
+    const float* src = a.kpart + ((static_cast<size_t>(grp) * S + qq) * 4 + w) * 1024;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] += src[i * 64 + l];
+  }
+  const int gm = m0 + l;
+  if (gm >= a.M) return;
+  proj_store<EPI>(a, b, gm, x);
 }
 
 __global__ __launch_bounds__(256) void head_merge_kernel(const float* __restrict__ part, int nNT,
