@@ -20,7 +20,10 @@
  *   - The caller owns every buffer.  The library allocates nothing and keeps no
  *     state between calls; scratch memory is the caller's workspace `ws` of at
  *     least the size the matching *_ws() function returns, aligned to 256 bytes.
- *     Calls that share a workspace must not overlap in time.
+ *     A workspace must be zero-filled before its first use: it holds arrival
+ *     counters of work-groups that split one reduction, and every call returns
+ *     them to zero before it completes, so a workspace stays ready for the next
+ *     call.  Calls that share a workspace must not overlap in time.
  *   - Arguments are checked on the host before anything is enqueued.  On error
  *     nothing is launched and a negative glance_status is returned;
  *     glance_last_error() then describes it (per thread).

@@ -35,7 +35,9 @@ def dtype_code(t: torch.Tensor) -> int:
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    """A zero-filled workspace (the library's arrival counters start at zero and
+    every call leaves them at zero)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 # ------------------------------------------------------------------ step 1 + 2

@@ -151,17 +151,22 @@ __device__ __forceinline__ const uint16_t* w_row_ptr(const GemmArgs& a, int row)
 // with two full-line non-temporal loads (rows 8 i + l/8, k = 8 (l%8)), written
 // to the wave's own LDS tile and read back in the MFMA operand layout (row
 // l%16, k = 32 s + 8 (l/16)).  Same-wave LDS accesses complete in order, so the
-// tile needs no barrier.  The activation chunk is staged in LDS for all waves.
-// Rings of DEPTH + 1 chunk slots in registers hold the weights and the
-// activation chunks on their way to LDS: iteration c issues the activation and
-// then the weight loads of chunk c + DEPTH and at its end stores activation
-// chunk c + 1 to the other LDS stage.  Loads complete in issue order, so every
-// wait is for data that is due anyway.
-template <int B, int DEPTH>
+// tile needs no barrier.  The activation chunks are staged in LDS for all
+// waves in a ring of 2 SB one-chunk stages: SB chunks are computed between two
+// barriers while the next SB chunks are loaded and written to the other half,
+// so the waves meet once per SB chunks (a barrier per chunk costs several
+// percent of the weight stream: the waves wait for the slowest one's loads).
+// LDS rows are 128 bytes, unpadded, with the 16-byte unit XOR-swizzled by the
+// row's low 3 bits against bank conflicts.  The weights of chunk c + 1 are
+// loaded into a second register slot while chunk c is computed.
+__device__ __forceinline__ int swz(int row, int unit) { return row * kKc + 8 * (unit ^ (row & 7)); }
+
+template <int B, int SB>
 __global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int NB, int NG,
                                                                  int nWG, int nMT) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2 * kXS];
-  __shared__ __attribute__((aligned(16))) uint16_t wtile[4 * B * 16 * kXP];
+  constexpr int XST = kTileM * kKc;  // one activation stage (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2 * SB * XST];
+  __shared__ __attribute__((aligned(16))) uint16_t wtile[4 * B * 16 * kKc];
   __shared__ HeadPart hred[4][kTileM];
 
   const int bid = blockIdx.x;
@@ -173,7 +178,7 @@ __global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
   const int G = wg * 4 + w;
   const int nck = a.K / kKc;
-  uint16_t* wt = wtile + w * B * 16 * kXP;
+  uint16_t* wt = wtile + w * B * 16 * kKc;
 
   int blk[B];
   bool bval[B];
@@ -189,17 +194,17 @@ __global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int
       wp[t][i] = w_row_ptr(a, row) + 8 * (l & 7);
     }
   }
-  // activation pieces this thread stages: 64 rows x 8 pieces of 16 B per chunk
+  // activation pieces this thread stages: 64 rows x 8 units of 16 B per chunk.
+  // Rows past M read row 0 unmasked: their results are never stored.
   const uint16_t* xr[2];
-  uint32_t xm[2];
   int xlds[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int idx = e * kGThreads + tid;
-    const int r = idx >> 3, cc = (idx & 7) * 8;
-    x_row_masked(a, m0 + r, xr[e], xm[e]);
-    xr[e] += cc;
-    xlds[e] = r * kXP + cc;
+    const int r = idx >> 3, cc = idx & 7;
+    const int row = m0 + r < a.M ? m0 + r : 0;
+    xr[e] = static_cast<const uint16_t*>(a.x) + static_cast<size_t>(row) * a.K + 8 * cc;
+    xlds[e] = swz(r, cc);
   }
 
   f32x4 acc[B][4];
@@ -207,89 +212,125 @@ __global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int
   for (int t = 0; t < B; ++t)
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) acc[t][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  constexpr int RS = DEPTH + 1;
-  static_assert(RS % 2 == 0, "ring slots and LDS stages must unroll together");
-  uint4 wbuf[RS][B][2];
-  uint4 xbuf[RS][2];
+  uint4 wbuf[2][B][2];
+  uint4 xb[SB][2];
   auto wload = [&](int c, uint4 (&dst)[B][2]) {
 #pragma unroll
     for (int t = 0; t < B; ++t)
 #pragma unroll
       for (int i = 0; i < 2; ++i) dst[t][i] = load_stream(wp[t][i] + c * kKc);
   };
-  // raw loads; the row mask is applied when the chunk is written to LDS
   auto xload = [&](int c, uint4 (&dst)[2]) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) dst[e] = *reinterpret_cast<const uint4*>(xr[e] + c * kKc);
   };
+  auto xstore = [&](int stage, const uint4 (&src)[2]) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) *reinterpret_cast<uint4*>(&xs[stage * XST + xlds[e]]) = src[e];
+  };
 
-  // nck is a multiple of RS; loads past the last chunk are clamped to it, so no
+  // nck is a multiple of SB; loads past the last chunk are clamped to it, so no
   // load is conditional (a conditional load would make the compiler's wait
-  // counts conservative and drain the ring every chunk)
-  xload(0, xbuf[0]);
+  // counts conservative and drain the loads in flight)
 #pragma unroll
-  for (int e = 0; e < 2; ++e) *reinterpret_cast<uint4*>(&xs[xlds[e]]) = mask4(xbuf[0][e], xm[e]);
+  for (int j = 0; j < SB; ++j) xload(j, xb[j]);
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) {
-    if (d + 1 < DEPTH) xload(min(d + 1, nck - 1), xbuf[d + 1]);
-    wload(min(d, nck - 1), wbuf[d]);
-  }
-  for (int c0 = 0; c0 < nck; c0 += RS) {
+  for (int j = 0; j < SB; ++j) xstore(j, xb[j]);
+  wload(0, wbuf[0]);
+  __syncthreads();
+  for (int c0 = 0; c0 < nck; c0 += SB) {
+    const int half = (c0 / SB) & 1;  // stage half holding chunks c0 .. c0 + SB - 1
 #pragma unroll
-    for (int u = 0; u < RS; ++u) {
+    for (int j = 0; j < SB; ++j) xload(min(c0 + SB + j, nck - 1), xb[j]);
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
       const int c = c0 + u;
-      {
-        const int cn = min(c + DEPTH, nck - 1);
-        xload(cn, xbuf[(u + DEPTH) % RS]);
-        wload(cn, wbuf[(u + DEPTH) % RS]);
+      wload(min(c + 1, nck - 1), wbuf[(u + 1) & 1]);
 #pragma unroll
-        for (int t = 0; t < B; ++t)
+      for (int t = 0; t < B; ++t)
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
-            *reinterpret_cast<uint4*>(wt + (t * 16 + 8 * i + (l >> 3)) * kXP + 8 * (l & 7)) = wbuf[u][t][i];
-        __syncthreads();
-        const uint16_t* xq = xs + (u & 1) * kXS;
+        for (int i = 0; i < 2; ++i)
+          *reinterpret_cast<uint4*>(wt + swz(t * 16 + 8 * i + (l >> 3), l & 7)) = wbuf[u & 1][t][i];
+      const uint16_t* xq = xs + (half * SB + u) * XST;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          bf16x8 bx[4];
+      for (int s = 0; s < 2; ++s) {
+        bf16x8 bx[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) bx[mb] = *reinterpret_cast<const bf16x8*>(xq + swz(mb * 16 + lr, 4 * s + lg));
+#pragma unroll
+        for (int t = 0; t < B; ++t) {
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(wt + swz(t * 16 + lr, 4 * s + lg));
 #pragma unroll
           for (int mb = 0; mb < 4; ++mb)
-            bx[mb] = *reinterpret_cast<const bf16x8*>(xq + (mb * 16 + lr) * kXP + s * 32 + 8 * lg);
-#pragma unroll
-          for (int t = 0; t < B; ++t) {
-            const bf16x8 av = *reinterpret_cast<const bf16x8*>(wt + (t * 16 + lr) * kXP + s * 32 + 8 * lg);
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-              acc[t][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bx[mb], acc[t][mb], 0, 0, 0);
-          }
+            acc[t][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bx[mb], acc[t][mb], 0, 0, 0);
         }
-        // (after the last chunk this stores a clamped copy nobody reads)
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          *reinterpret_cast<uint4*>(&xs[((u + 1) & 1) * kXS + xlds[e]]) = mask4(xbuf[(u + 1) % RS][e], xm[e]);
       }
     }
+    // the next SB chunks go to the other half, whose last reads came before the
+    // previous barrier (after the last chunk these are clamped copies nobody reads)
+#pragma unroll
+    for (int j = 0; j < SB; ++j) xstore((half ^ 1) * SB + j, xb[j]);
+    __syncthreads();
   }
 
-  // acc[t][mb][v]: vocabulary row blk[t]*16 + 4 lg + v, activation row m0 + 16 mb + lr
+  // acc[t][mb][v]: vocabulary row blk[t]*16 + 4 lg + v, activation row m0 + 16 mb + lr.
+  // Per lane and activation row: max, its smallest token id and the best other
+  // logit in one select-only pass (rows are visited in increasing token order, so
+  // a strict comparison keeps the smallest id; rows past the vocabulary enter as
+  // -inf), then the two sums relative to that max.
+  bool nval[B][4];
+#pragma unroll
+  for (int t = 0; t < B; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) nval[t][v] = bval[t] & (blk[t] * 16 + 4 * lg + v < a.N);
   HeadPart hp[4];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) hp[mb] = head_empty();
+  for (int mb = 0; mb < 4; ++mb) {
+    float mx = -INFINITY, m2 = -INFINITY;
+    int am = 0x7FFFFFFF;
 #pragma unroll
-  for (int t = 0; t < B; ++t) {
-    if (!bval[t]) continue;
+    for (int t = 0; t < B; ++t)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int n = blk[t] * 16 + 4 * lg + v;
-      if (n < a.N) {
+      for (int v = 0; v < 4; ++v) {
+        const float z = nval[t][v] ? acc[t][mb][v] : -INFINITY;
+        const bool gt = z > mx;
+        m2 = gt ? mx : fmaxf(m2, z);
+        am = gt ? blk[t] * 16 + 4 * lg + v : am;
+        mx = gt ? z : mx;
+      }
+    // d = z - max, kept finite so that e * d is 0 for absent rows (e = 0)
+    const float ms = mx == -INFINITY ? 0.f : mx;
+    float sum = 0.f, tsum = 0.f;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          hp[mb] = head_combine(hp[mb], head_elem(acc[t][mb][v], n));
-          const int m = m0 + mb * 16 + lr;
-          if (a.logits && m < a.M) a.logits[static_cast<size_t>(m) * a.N + n] = acc[t][mb][v];
+    for (int t = 0; t < B; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float z = nval[t][v] ? acc[t][mb][v] : -INFINITY;
+        const float d = fmaxf(z - ms, -1e30f);
+        const float e = __builtin_amdgcn_exp2f(d * 1.4426950408889634f);
+        sum += e;
+        tsum = fmaf(e, d, tsum);
+      }
+    hp[mb].m = mx;
+    hp[mb].am = am;
+    hp[mb].m2 = m2;
+    hp[mb].s = sum;
+    hp[mb].t = tsum;
+  }
+  if (a.logits) {
+#pragma unroll
+    for (int t = 0; t < B; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int n = blk[t] * 16 + 4 * lg + v;
+        if (bval[t] && n < a.N) {
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) {
+            const int m = m0 + mb * 16 + lr;
+            if (m < a.M) a.logits[static_cast<size_t>(m) * a.N + n] = acc[t][mb][v];
+          }
         }
       }
-    }
   }
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
@@ -315,13 +356,85 @@ __global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int
 }
 
 // -------------------------------------------------------------- projections
-// Split-K in two kernels.  proj_bf16: work-group (group g, slice q, tile mt)
-// computes blocks 4g .. 4g+3 (one per wave, MFMA-layout weight loads) over the
-// K-slice q of S and stores the fp32 partial; the activation chunk in LDS is
-// shared by the four blocks, so the activations are read once per 64 weight
-// rows.  All S x nMT work-groups of a group run on the same XCD.  proj_reduce:
-// one thread per (block, activation row) sums the S partials in slice order
-// (deterministic) and applies the epilogue.
+// Epilogue of one 16-row weight block for activation row gm: x[i] is the
+// block's row i (of the summed K slices).  q/k blocks are rotated (rows i and
+// 8+i are RoPE partners), v rows copied, output-projection rows added to the
+// residual; everything is rounded to bf16.
+template <int EPI>
+__device__ __forceinline__ void proj_store(const GemmArgs& a, int b, int gm, const float (&x)[16]) {
+  if constexpr (EPI == EPI_RESID) {
+    const int n = b * 16;
+    uint4 o[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+    const int tok = a.resid_tok[gm];
+    if (tok >= 0) {
+      const uint16_t* rp = static_cast<const uint16_t*>(a.resid) +
+                           static_cast<size_t>(a.resid_by_token ? tok : gm) * a.N + n;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 r = *reinterpret_cast<const uint4*>(rp + 8 * h);
+        const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+        uint32_t ow[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float lo = bf16_to_f32(rw[j] & 0xFFFF) + x[8 * h + 2 * j];
+          const float hi = bf16_to_f32(rw[j] >> 16) + x[8 * h + 2 * j + 1];
+          ow[j] = static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+        }
+        o[h] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      }
+    }
+    uint4* op = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out_res) + static_cast<size_t>(gm) * a.N + n);
+    op[0] = o[0];
+    op[1] = o[1];
+  } else {  // EPI_QKV
+    const int nq = a.Hq * 8, nk = a.Hkv * 8;
+    if (b < nq + nk) {
+      // rows i < 8 are head dims 8j + i, rows 8 + i their RoPE partners 64 + 8j + i
+      const int bb = b < nq ? b : b - nq;
+      const int head = bb >> 3, j8 = (bb & 7) * 8;
+      const int sq = gm / a.n_rows;
+      int pos = static_cast<int>(a.kv_offsets[sq + 1] - a.kv_offsets[sq]) + a.depth[gm];
+      if (pos > a.n_pos - 1) pos = a.n_pos - 1;
+      uint32_t lw[4], hw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float lo[2], hi[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int i = 2 * j + h;
+          const float c = a.rope_cos[static_cast<size_t>(pos) * 64 + j8 + i];
+          const float sn = a.rope_sin[static_cast<size_t>(pos) * 64 + j8 + i];
+          lo[h] = x[i] * c - x[i + 8] * sn;
+          hi[h] = x[i + 8] * c + x[i] * sn;
+        }
+        lw[j] = static_cast<uint32_t>(f32_to_bf16(lo[0])) | (static_cast<uint32_t>(f32_to_bf16(lo[1])) << 16);
+        hw[j] = static_cast<uint32_t>(f32_to_bf16(hi[0])) | (static_cast<uint32_t>(f32_to_bf16(hi[1])) << 16);
+      }
+      uint16_t* op = b < nq ? static_cast<uint16_t*>(a.q_out) + static_cast<size_t>(gm) * a.Hq * 128
+                            : static_cast<uint16_t*>(a.k_out) + static_cast<size_t>(gm) * a.Hkv * 128;
+      op += head * 128 + j8;
+      *reinterpret_cast<uint4*>(op) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      *reinterpret_cast<uint4*>(op + 64) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    } else {
+      const int vr = (b - nq - nk) * 16;  // first v dim of the block
+      uint32_t ow[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        ow[j] = static_cast<uint32_t>(f32_to_bf16(x[2 * j])) | (static_cast<uint32_t>(f32_to_bf16(x[2 * j + 1])) << 16);
+      uint4* op = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.v_out) + static_cast<size_t>(gm) * a.Hkv * 128 + vr);
+      op[0] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      op[1] = make_uint4(ow[4], ow[5], ow[6], ow[7]);
+    }
+  }
+}
+
+// Split-K in one kernel: work-group (group g, slice q, tile mt) computes blocks
+// 4g .. 4g+3 (one per wave, MFMA-layout weight loads) over the K-slice q of S
+// and stores the fp32 partial; the activation chunk in LDS is shared by the four
+// blocks, so the activations are read once per 64 weight rows.  The last of the
+// group's S work-groups to finish sums the partials, one thread per (block,
+// activation row), and applies the epilogue.  The S x nMT work-groups of a
+// group are dealt to the same XCD.
 template <int EPI, int DEPTH>
 __global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int NB, int NGr,
                                                                  int S, int nMT) {
@@ -411,103 +524,42 @@ __global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int
     }
   }
 
-  // partial of this wave's block: [16 block rows][64 activation rows]
+  // partial of this wave's block: [16 block rows][64 activation rows], stored
+  // with device-coherent stores; the group's last work-group to arrive sums the
+  // S slices in slice order (deterministic) and applies the epilogue.  Only the
+  // counter and the partials are shared, both through device-scope atomic
+  // accesses (write-through stores and coherent loads), and every store has
+  // completed before the arrival is counted, so no cache write-back is needed.
   const size_t grp = static_cast<size_t>(mt) * NGr + g;
   float* pp = a.kpart + ((grp * S + q) * 4 + w) * 1024;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) pp[(4 * lg + v) * 64 + mb * 16 + lr] = acc[mb][v];
-}
-
-// Epilogue of one 16-row weight block for activation row gm: x[i] is the
-// block's row i (of the summed K slices).  q/k blocks are rotated (rows i and
-// 8+i are RoPE partners), v rows copied, output-projection rows added to the
-// residual; everything is rounded to bf16.
-template <int EPI>
-__device__ __forceinline__ void proj_store(const GemmArgs& a, int b, int gm, const float (&x)[16]) {
-  if constexpr (EPI == EPI_RESID) {
-    const int n = b * 16;
-    uint4 o[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-    const int tok = a.resid_tok[gm];
-    if (tok >= 0) {
-      const uint16_t* rp = static_cast<const uint16_t*>(a.resid) +
-                           static_cast<size_t>(a.resid_by_token ? tok : gm) * a.N + n;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint4 r = *reinterpret_cast<const uint4*>(rp + 8 * h);
-        const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
-        uint32_t ow[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float lo = bf16_to_f32(rw[j] & 0xFFFF) + x[8 * h + 2 * j];
-          const float hi = bf16_to_f32(rw[j] >> 16) + x[8 * h + 2 * j + 1];
-          ow[j] = static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
-        }
-        o[h] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-      }
-    }
-    uint4* op = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out_res) + static_cast<size_t>(gm) * a.N + n);
-    op[0] = o[0];
-    op[1] = o[1];
-  } else {  // EPI_QKV
-    const int nq = a.Hq * 8, nk = a.Hkv * 8;
-    if (b < nq + nk) {
-      // rows i < 8 are head dims 8j + i, rows 8 + i their RoPE partners 64 + 8j + i
-      const int bb = b < nq ? b : b - nq;
-      const int head = bb >> 3, j8 = (bb & 7) * 8;
-      const int sq = gm / a.n_rows;
-      int pos = static_cast<int>(a.kv_offsets[sq + 1] - a.kv_offsets[sq]) + a.depth[gm];
-      if (pos > a.n_pos - 1) pos = a.n_pos - 1;
-      uint32_t lw[4], hw[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float lo[2], hi[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int i = 2 * j + h;
-          const float c = a.rope_cos[static_cast<size_t>(pos) * 64 + j8 + i];
-          const float sn = a.rope_sin[static_cast<size_t>(pos) * 64 + j8 + i];
-          lo[h] = x[i] * c - x[i + 8] * sn;
-          hi[h] = x[i + 8] * c + x[i] * sn;
-        }
-        lw[j] = static_cast<uint32_t>(f32_to_bf16(lo[0])) | (static_cast<uint32_t>(f32_to_bf16(lo[1])) << 16);
-        hw[j] = static_cast<uint32_t>(f32_to_bf16(hi[0])) | (static_cast<uint32_t>(f32_to_bf16(hi[1])) << 16);
-      }
-      uint16_t* op = b < nq ? static_cast<uint16_t*>(a.q_out) + static_cast<size_t>(gm) * a.Hq * 128
-                            : static_cast<uint16_t*>(a.k_out) + static_cast<size_t>(gm) * a.Hkv * 128;
-      op += head * 128 + j8;
-      *reinterpret_cast<uint4*>(op) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-      *reinterpret_cast<uint4*>(op + 64) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    } else {
-      const int vr = (b - nq - nk) * 16;  // first v dim of the block
-      uint32_t ow[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        ow[j] = static_cast<uint32_t>(f32_to_bf16(x[2 * j])) | (static_cast<uint32_t>(f32_to_bf16(x[2 * j + 1])) << 16);
-      uint4* op = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.v_out) + static_cast<size_t>(gm) * a.Hkv * 128 + vr);
-      op[0] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-      op[1] = make_uint4(ow[4], ow[5], ow[6], ow[7]);
-    }
+    for (int v = 0; v < 4; ++v)
+      __hip_atomic_store(pp + (4 * lg + v) * 64 + mb * 16 + lr, acc[mb][v], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);
+  __shared__ int s_last;
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned old = __hip_atomic_fetch_add(a.kcnt + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == static_cast<unsigned>(S - 1);
+    if (last) __hip_atomic_store(a.kcnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last;
   }
-}
-
-template <int EPI>
-__global__ __launch_bounds__(kGThreads) void proj_reduce_kernel(GemmArgs a, int NB, int NGr, int S) {
-  const int grp = blockIdx.x;  // mt * NGr + g
-  const int mt = grp / NGr, g = grp - mt * NGr;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int b = g * 4 + w;
-  if (b >= NB) return;
-  const int m0 = mt * kTileM;
-  // lane l: activation row m0 + l of block b
+  __syncthreads();
+  if (!s_last || !bv) return;
+  // thread (w, l): activation row m0 + l of block b
   float x[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) x[i] = 0.f;
   for (int qq = 0; qq < S; ++qq) {
-    const float* src = a.kpart + ((static_cast<size_t>(grp) * S + qq) * 4 + w) * 1024;
+    const float* src = a.kpart + ((grp * S + qq) * 4 + w) * 1024 + l;
+    float y[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] += src[i * 64 + l];
+    for (int i = 0; i < 16; ++i) y[i] = __hip_atomic_load(src + i * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] += y[i];
   }
   const int gm = m0 + l;
   if (gm >= a.M) return;
@@ -615,13 +667,14 @@ struct HeadGrid {
   int NB, NG, nWG;
 };
 HeadGrid head_grid(int N) {
+  // the fewest waves (at most kHeadWaves while blocks per wave <= kHeadB) that
+  // give every wave the same number of blocks, up to one
   HeadGrid g;
   g.NB = (N + 15) / 16;
-  int ng = g.NB < kHeadWaves ? g.NB : kHeadWaves;
-  const int need = (g.NB + kHeadB - 1) / kHeadB;
-  if (ng < need) ng = need;
-  g.NG = ng;
-  g.nWG = (ng + 3) / 4;
+  int per = (g.NB + kHeadWaves - 1) / kHeadWaves;
+  if (per > kHeadB) per = kHeadB;
+  g.NG = (g.NB + per - 1) / per;
+  g.nWG = (g.NG + 3) / 4;
   return g;
 }
 }  // namespace
@@ -651,12 +704,17 @@ size_t proj_part_floats(int M, int NB, int K) {
   return static_cast<size_t>(nMT) * NGr * proj_ksplit(K, NB) * 4 * 1024;
 }
 
+size_t proj_counters(int M, int NB) {
+  const int nMT = (M + kTileM - 1) / kTileM;
+  return static_cast<size_t>(nMT) * ((NB + 3) / 4);
+}
+
 glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   const int nMT = (a.M + kTileM - 1) / kTileM;
   if (a.epi == EPI_HEAD) {
     const HeadGrid g = head_grid(a.N);
     const int grid = ((g.nWG + 7) / 8) * 8 * nMT;
-    head_bf16_kernel<kHeadB, 1><<<grid, kGThreads, 0, st>>>(a, g.NB, g.NG, g.nWG, nMT);
+    head_bf16_kernel<kHeadB, 2><<<grid, kGThreads, 0, st>>>(a, g.NB, g.NG, g.nWG, nMT);
   } else {
     const int NB = proj_blocks(a);
     const int NGr = (NB + 3) / 4;
@@ -672,8 +730,6 @@ glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
         proj_bf16_kernel<EPI_QKV, 3><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
       else
         proj_bf16_kernel<EPI_QKV, 1><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
-      GLANCE_LAUNCH_CHECK();
-      proj_reduce_kernel<EPI_QKV><<<NGr * nMT, kGThreads, 0, st>>>(a, NB, NGr, S);
     } else {
       if (rs == 8)
         proj_bf16_kernel<EPI_RESID, 7><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
@@ -681,8 +737,6 @@ glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
         proj_bf16_kernel<EPI_RESID, 3><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
       else
         proj_bf16_kernel<EPI_RESID, 1><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
-      GLANCE_LAUNCH_CHECK();
-      proj_reduce_kernel<EPI_RESID><<<NGr * nMT, kGThreads, 0, st>>>(a, NB, NGr, S);
     }
   }
   GLANCE_LAUNCH_CHECK();

@@ -60,7 +60,7 @@ glance_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
 struct AttnWs {
   int n_split = 0, split = 0;
   size_t off_qkv = 0, off_q = 0, off_k = 0, off_v = 0, off_part = 0, off_x = 0, bytes = 0;
-  size_t off_kpart = 0;
+  size_t off_kpart = 0, off_kcnt = 0;
 };
 
 AttnWs attn_ws_layout(int dtype, int nseq, int n_rows, int64_t max_prefix, int d_model, int Hq,
@@ -86,6 +86,8 @@ AttnWs attn_ws_layout(int dtype, int nseq, int n_rows, int64_t max_prefix, int d
     const int nb_qkv = (Hq + 2 * Hkv) * 8, nb_o = (d_model + 15) / 16;
     const size_t pf = std::max(proj_part_floats(M, nb_qkv, d_model), proj_part_floats(M, nb_o, Hq * D));
     w.off_kpart = take(pf * sizeof(float));
+    // arrival counters of the split-K groups (each projection returns them to zero)
+    w.off_kcnt = take(std::max(proj_counters(M, nb_qkv), proj_counters(M, nb_o)) * sizeof(unsigned));
   } else {
     w.off_qkv = take(R * static_cast<size_t>(Hq + 2 * Hkv) * D * sizeof(float));
     w.off_x = take(R * Hq * D * sizeof(float));
@@ -227,6 +229,7 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
   const int R = nseq * n_rows;
   const int qd = Hq * D, kd = Hkv * D;
   float* kpart = reinterpret_cast<float*>(base + w.off_kpart);
+  unsigned* kcnt = reinterpret_cast<unsigned*>(base + w.off_kcnt);
   if (dtype == GLANCE_BF16) {
     if (tree_k == nullptr) tree_k = base + w.off_k;
     if (tree_v == nullptr) tree_v = base + w.off_v;
@@ -260,6 +263,7 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
     g.rope_sin = rope_sin;
     g.n_pos = n_pos;
     g.kpart = kpart;
+    g.kcnt = kcnt;
     st = launch_gemm_bf16(g, hs);
   } else {
     g.epi = EPI_STORE_F32;
@@ -314,6 +318,7 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
   o.resid_by_token = embed != nullptr;
   o.out_res = h_out;
   o.kpart = kpart;
+  o.kcnt = kcnt;
   return dtype == GLANCE_BF16 ? launch_gemm_bf16(o, hs) : launch_gemm_f32(o, hs);
 }
 

@@ -55,17 +55,20 @@ struct GemmArgs {
   const float* rope_cos;
   const float* rope_sin;
   int n_pos;
-  // EPI_QKV / EPI_RESID (bf16): split-K partials
+  // EPI_QKV / EPI_RESID (bf16): split-K partials and one arrival counter per
+  // group of work-groups (zero before the call; the call leaves them zero)
   float* kpart;
+  unsigned* kcnt;
 };
 // Number of per-row partial records the bf16 LM-head GEMM leaves (the merge input).
 int gemm_bf16_head_parts(int N);
 glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
-// Scratch of the bf16 projections: number of 16-row weight blocks, K-split and
-// partial floats for M activation rows.
+// Scratch of the bf16 projections: number of 16-row weight blocks, K-split,
+// partial floats and arrival counters for M activation rows.
 int proj_blocks(const GemmArgs& a);
 int proj_ksplit(int K, int NB);
 size_t proj_part_floats(int M, int NB, int K);
+size_t proj_counters(int M, int NB);
 glance_status launch_gemm_f32(const GemmArgs& a, hipStream_t st);
 // Row statistics of the head from bf16 partials, or from full fp32 logits.
 glance_status launch_head_merge(const float* part, int n_tiles, int R, int32_t* argmax,

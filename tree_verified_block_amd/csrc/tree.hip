@@ -36,6 +36,7 @@ namespace glance {
 namespace {
 
 constexpr int kSlots = 64;  // candidate slots per (offset, chunk); K_j <= 63
+constexpr int kLqRow = 72;  // LDS row of a ranked list: 64 entries and -inf padding
 
 __device__ __forceinline__ int k_of(int N, int V, int j) {
   int k = N - j;
@@ -140,6 +141,7 @@ __global__ __launch_bounds__(kChunkThreads) void lsm_chunk_kernel(
   __shared__ __attribute__((aligned(16))) unsigned long long cand[kCap];
   __shared__ unsigned long long sel[kSlots];
   __shared__ unsigned long long wt[kChunkWaves];
+  __shared__ int wcnt[kChunkWaves];
   __shared__ float red_m[kChunkWaves], red_s[kChunkWaves];
   __shared__ unsigned hist[256];
   __shared__ int s_count, s_krem, s_done;
@@ -222,7 +224,6 @@ __global__ __launch_bounds__(kChunkThreads) void lsm_chunk_kernel(
   }
   if (kw > 0 && lane == kw - 1) wt[w] = srt;
   if (tid < kSlots) sel[tid] = 0ull;
-  if (tid == 0) s_count = 0;
   __syncthreads();
   if (tid == 0) {
     float M = -INFINITY;
@@ -241,18 +242,32 @@ __global__ __launch_bounds__(kChunkThreads) void lsm_chunk_kernel(
 #pragma unroll
   for (int i = 1; i < kChunkWaves; ++i) Tk = umin64(Tk, wt[i]);
   // (Tk == 0 when a wave holds fewer than k keys: every key is gathered)
+  // Slots: a wave-inclusive scan of the per-thread counts places each thread's
+  // keys after those of the lower lanes, the waves' totals after the lower waves.
+  int cnt = 0;
+#pragma unroll
+  for (int e = 0; e < IPT; ++e)
+    cnt += (ok[e] && make_comp(z[e], static_cast<uint32_t>(tok(e))) >= Tk) ? 1 : 0;
+  const int incl = wave_incl_sum(cnt);
+  if (lane == kWave - 1) wcnt[w] = incl;
+  __syncthreads();
+  int slot = incl - cnt, C = 0;
+#pragma unroll
+  for (int i = 0; i < kChunkWaves; ++i) {
+    slot += i < w ? wcnt[i] : 0;
+    C += wcnt[i];
+  }
 #pragma unroll
   for (int e = 0; e < IPT; ++e) {
     if (ok[e]) {
       const unsigned long long key = make_comp(z[e], static_cast<uint32_t>(tok(e)));
       if (key >= Tk) {
-        const int slot = atomicAdd(&s_count, 1);
         if (slot < kCap) cand[slot] = key;
+        ++slot;
       }
     }
   }
   __syncthreads();
-  const int C = s_count;
   if (C <= kCap) {
     for (int e = tid; e < C; e += kChunkThreads) {
       const unsigned long long k = cand[e];
@@ -330,10 +345,10 @@ __global__ __launch_bounds__(kMaxChunks * kWave) void build_tree_kernel(
     int32_t* __restrict__ depth_out, int32_t* __restrict__ token_out,
     uint64_t* __restrict__ anc_out, float* __restrict__ score_out,
     int32_t* __restrict__ n_valid_out) {
-  __shared__ float lq[GLANCE_MAX_L + 1][kSlots];  // row L: -inf (depth-L nodes have no children)
+  // ranked log q per offset, -inf past the list (reads reach entry 65); row L is
+  // all -inf (depth-L nodes have no children)
+  __shared__ float lq[GLANCE_MAX_L + 1][kLqRow];
   __shared__ int tk[GLANCE_MAX_L][kSlots];
-  __shared__ int row_of_lane[kSlots];
-  __shared__ unsigned long long anc_row[kSlots];
 
   const int s = blockIdx.x, lane = lane_id(), wv = threadIdx.x / kWave;
 
@@ -345,7 +360,10 @@ __global__ __launch_bounds__(kMaxChunks * kWave) void build_tree_kernel(
   // per offset: up to 128 leading entries, then up to nch * 64 candidates
   __shared__ __attribute__((aligned(16))) unsigned long long mcand[GLANCE_MAX_L][128 + kMaxChunks * kSlots];
   __shared__ unsigned long long mthr[GLANCE_MAX_L];
-  if (wv == 0) lq[L][lane] = -INFINITY;
+  if (wv == 0) {
+    lq[L][lane] = -INFINITY;
+    if (lane < kLqRow - kSlots) lq[L][kSlots + lane] = -INFINITY;
+  }
   if (wv < L) {
     const int j = wv;
     const size_t row = static_cast<size_t>(s) * L + j;
@@ -371,7 +389,12 @@ __global__ __launch_bounds__(kMaxChunks * kWave) void build_tree_kernel(
       const int xa = x0 + lane, xb = x0 + kWave + lane;
       const unsigned long long va = xa < n1 ? mc[xa] : 0ull, vb = xb < n1 ? mc[xb] : 0ull;
       int ra, rb;
-      rank2(mc, n1, va, vb, ra, rb);
+      if (x0 + kWave < n1) {
+        rank2(mc, n1, va, vb, ra, rb);
+      } else {  // one key per lane left
+        ra = count_greater(mc, n1, va);
+        rb = K;
+      }
       if (xa < n1 && va != 0ull && ra == K - 1) mthr[j] = va;
       if (xb < n1 && vb != 0ull && rb == K - 1) mthr[j] = vb;
     }
@@ -387,13 +410,19 @@ __global__ __launch_bounds__(kMaxChunks * kWave) void build_tree_kernel(
       C += __popcll(bal);
     }
     lq[j][lane] = -INFINITY;
+    if (lane < kLqRow - kSlots) lq[j][kSlots + lane] = -INFINITY;
     tk[j][lane] = -1;
     __builtin_amdgcn_wave_barrier();
     for (int x0 = 0; x0 < C; x0 += 2 * kWave) {
       const int xa = x0 + lane, xb = x0 + kWave + lane;
       const unsigned long long va = xa < C ? cs[xa] : 0ull, vb = xb < C ? cs[xb] : 0ull;
       int ra, rb;
-      rank2(cs, C, va, vb, ra, rb);
+      if (x0 + kWave < C) {
+        rank2(cs, C, va, vb, ra, rb);
+      } else {
+        ra = count_greater(cs, C, va);
+        rb = K;
+      }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const unsigned long long k = h ? vb : va;
@@ -411,66 +440,82 @@ __global__ __launch_bounds__(kMaxChunks * kWave) void build_tree_kernel(
 
   // ---- best-first selection.  Lane 0 is the root, lane i the i-th selected
   // node; each lane offers the best not-yet-selected child of its node (the
-  // next entry of the next offset's ranked list).  Equal scores: smaller depth,
-  // then the earlier-selected parent (smaller lane); one offer per lane.  The
-  // loop body is branch-free per lane: the winner p and the new node i update
-  // through selects, and the log q after each new offer is read from LDS one
-  // iteration ahead of its first possible use.
+  // next entry of the list of its depth).  Equal scores: smaller depth, then the
+  // earlier-selected parent (smaller lane); a lane offers one child at a time.
+  // Scores are sums of log q <= 0, so the order key of a score v is
+  // 0x7F800000 - bits(|v|): larger scores give larger keys, -inf (no offer)
+  // gives 0, and the key maps back to -|v| on the scalar unit.  Per iteration
+  // only the winner p and the new node i change, from scalar values; every lane
+  // re-reads the log q after its offered child, so the read is issued one
+  // iteration ahead of its use.
+  // Lane state: st = depth << 16 | own rank << 8 | rank of the offered child.
   const int R = N + 1;
-  // order keys: float_key(score) - float_key(-inf), so no offer (score -inf) is 0
-  constexpr uint32_t kNegInfKey = 0x007FFFFFu;
-  const float fq = lane <= L ? lq[lane][0] : -INFINITY;  // first entry of each offset
-  float n_score = 0.f;   // this node's score
-  int n_dn = 0;          // depth << 8 | rank of the offered child in list `depth`
-  int n_par = -1, n_rank = 0;
-  float c_score = lane == 0 ? fq : 0.f;  // the offered child's score
-  uint32_t c_hi = lane == 0 ? float_key(fq) - kNegInfKey : 0u;
-  float nx_q = lane == 0 ? lq[0][1] : -INFINITY;  // log q of the child after the offered one
-  float pend = -INFINITY;
-  bool upd = false;
+  auto okey = [](float v) { return 0x7F800000u - (__float_as_uint(v) & 0x7FFFFFFFu); };
+  const float fq = lane <= L ? lq[lane][0] : -INFINITY;  // first entry of each list
+  int st = 0;
+  float n_score = 0.f;
+  int n_par = -1;
+  uint32_t c_hi = lane == 0 ? okey(fq) : 0u;
+  float nx_q = lq[0][1];  // log q after the offered child (lane 0: the root's second child)
   int n_pop = 0;
   for (int i = 1; i <= N; ++i) {
     const uint32_t mh = wave_umax(c_hi);
     if (mh == 0u) break;
     unsigned long long cm = __ballot(c_hi == mh);
-    if (__popcll(cm) > 1) {  // equal scores: the smallest child depth, then the lowest lane
-      const uint32_t lo = (c_hi == mh) ? ~static_cast<uint32_t>(n_dn >> 8) : 0u;
+    if (__popcll(cm) > 1) {  // equal scores: the smallest depth, then the lowest lane
+      const uint32_t lo = (c_hi == mh) ? ~static_cast<uint32_t>(st >> 16) : 0u;
       const uint32_t ml = wave_umax(lo);
-      cm = __ballot(c_hi == mh && ~static_cast<uint32_t>(n_dn >> 8) == ml);
+      cm = __ballot(c_hi == mh && ~static_cast<uint32_t>(st >> 16) == ml);
     }
     const int p = __ffsll(static_cast<long long>(cm)) - 1;
-    const float w_score = readlane_f(c_score, p);
-    const int w_dn = readlane_i(n_dn, p);
-    const int w_depth = (w_dn >> 8) + 1;
-    const float q0 = readlane_f(fq, w_depth);
-    nx_q = upd ? pend : nx_q;
+    const int w_st = readlane_i(st, p);
+    const int dn = (w_st >> 16) + 1;                        // the new node's depth
+    const int new_st = (dn << 16) | ((w_st & 255) << 8);    // its own rank, first child offered
+    const float w_score = __uint_as_float((0x7F800000u - mh) | 0x80000000u);
+    const float q0 = readlane_f(fq, dn);
     const bool isp = lane == p, isi = lane == i;
-    // lane p: its next child; lane i: the new node's first child (a -inf log q,
-    // past a list's end or below depth L, gives key 0: no offer)
-    const float sp = n_score + nx_q;
-    const float si = w_score + q0;
-    const uint32_t kp = float_key(sp) - kNegInfKey;
-    const uint32_t ki = float_key(si) - kNegInfKey;
+    st = isi ? new_st : (isp ? w_st + 1 : st);
     n_score = isi ? w_score : n_score;
     n_par = isi ? p : n_par;
-    n_rank = isi ? (w_dn & 255) : n_rank;
-    n_dn = isi ? (w_depth << 8) : (isp ? n_dn + 1 : n_dn);
-    c_score = isi ? si : (isp ? sp : c_score);
-    c_hi = isi ? ki : (isp ? kp : c_hi);
-    // log q of the child after the new offer, used from the next iteration on
-    upd = isp || isi;
-    const int rr = (n_dn & 255) + 1;
-    pend = lq[n_dn >> 8][rr < kSlots ? rr : kSlots - 1];
+    const uint32_t k = okey(n_score + (isi ? q0 : nx_q));
+    c_hi = (isp || isi) ? k : c_hi;
+    nx_q = lq[st >> 16][(st & 255) + 1];
     n_pop = i;
   }
-  const int n_depth = n_dn >> 8;
 
-  // ---- breadth-first layout: rows by (depth, parent row, token id)
-  const int n_token = (lane >= 1 && lane <= n_pop) ? tk[n_depth - 1][n_rank] : -1;
+  // ---- breadth-first layout: rows by (depth, parent row, token id), level by
+  // level; a node's row and ancestor mask come from its parent's lane
+  const int n_depth = st >> 16;
+  const bool member = lane >= 1 && lane <= n_pop;
+  const int n_token = member ? tk[n_depth - 1][(st >> 8) & 255] : -1;
+  const int par_addr = (n_par < 0 ? 0 : n_par) * 4;
+  int row = 0, prow = -1;
+  unsigned long long anc = 1ull;
+  int base = 1;
+  for (int d = 1; d <= L; ++d) {
+    const bool in_level = member && n_depth == d;
+    const unsigned long long lvl = __ballot(in_level);
+    if (lvl == 0ull) break;
+    const int pr = __builtin_amdgcn_ds_bpermute(par_addr, row);
+    const uint32_t alo = __builtin_amdgcn_ds_bpermute(par_addr, static_cast<int>(anc));
+    const uint32_t ahi = __builtin_amdgcn_ds_bpermute(par_addr, static_cast<int>(anc >> 32));
+    const int key = (pr << 18) | (n_token & 0x3FFFF);  // token ids < 2^18
+    int rank = 0;
+    unsigned long long mm = lvl;
+    while (mm) {
+      const int jl = __ffsll(static_cast<long long>(mm)) - 1;
+      mm &= mm - 1;
+      rank += readlane_i(key, jl) < key ? 1 : 0;
+    }
+    if (in_level) {
+      row = base + rank;
+      prow = pr;
+      anc = ((static_cast<unsigned long long>(ahi) << 32) | alo) | (1ull << row);
+    }
+    base += __popcll(lvl);
+  }
   const size_t ob = static_cast<size_t>(s) * R;
   if (lane == 0) {
-    row_of_lane[0] = 0;
-    anc_row[0] = 1ull;
     parent[ob] = -1;
     depth_out[ob] = 0;
     token_out[ob] = root_token[s];
@@ -478,34 +523,12 @@ __global__ __launch_bounds__(kMaxChunks * kWave) void build_tree_kernel(
     score_out[ob] = 0.f;
     n_valid_out[s] = n_pop + 1;
   }
-  __builtin_amdgcn_wave_barrier();  // one wave: LDS is in order
-  int base = 1;
-  for (int d = 1; d <= L; ++d) {
-    const bool in_level = lane >= 1 && lane <= n_pop && n_depth == d;
-    const unsigned long long lvl = __ballot(in_level);
-    if (lvl == 0ull) break;
-    const int prow = in_level ? row_of_lane[n_par] : 0;
-    int rank = 0;
-    unsigned long long mm = lvl;
-    while (mm) {
-      const int jl = __ffsll(static_cast<long long>(mm)) - 1;
-      mm &= mm - 1;
-      const int op = readlane_i(prow, jl), ot = readlane_i(n_token, jl);
-      rank += (op < prow || (op == prow && ot < n_token)) ? 1 : 0;
-    }
-    if (in_level) {
-      const int r = base + rank;
-      row_of_lane[lane] = r;
-      const unsigned long long a = anc_row[prow] | (1ull << r);
-      anc_row[r] = a;
-      parent[ob + r] = prow;
-      depth_out[ob + r] = d;
-      token_out[ob + r] = n_token;
-      anc_out[ob + r] = a;
-      score_out[ob + r] = n_score;
-    }
-    base += __popcll(lvl);
-    __builtin_amdgcn_wave_barrier();  // one wave: LDS is in order
+  if (member) {
+    parent[ob + row] = prow;
+    depth_out[ob + row] = n_depth;
+    token_out[ob + row] = n_token;
+    anc_out[ob + row] = anc;
+    score_out[ob + row] = n_score;
   }
   for (int r = n_pop + 1 + lane; r < R; r += kWave) {
     parent[ob + r] = -1;
