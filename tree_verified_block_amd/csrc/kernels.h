@@ -12,8 +12,10 @@ namespace glance {
 
 // ------------------------------------------------------------------ tree.hip
 struct TreeWs {
-  // per-chunk (max, sum exp) [nseq*L][16] and sorted key lists [nseq*L][16][64]
-  size_t off_cstat = 0, off_clist = 0, bytes = 0;
+  // per-chunk (max, sum exp) [nseq*L][16], sorted key lists [nseq*L][16][64],
+  // merged rows (log q [nseq*L][64], token ids [nseq*L][64]) and the arrival
+  // counters of the rows [nseq*L] and sequences [nseq] (zero between calls)
+  size_t off_cstat = 0, off_clist = 0, off_lq = 0, off_tk = 0, off_row_cnt = 0, off_seq_cnt = 0, bytes = 0;
 };
 TreeWs tree_ws_layout(int nseq, int L, int V);
 glance_status launch_build_tree(const void* logits, int dtype, const int32_t* root, int nseq,

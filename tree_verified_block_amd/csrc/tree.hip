@@ -12,22 +12,19 @@
 // ancestors, all of which must also be in S.  So each offset keeps <= 63 tokens.
 // Tokens are ranked by the key (logit desc, token id asc); keys are distinct.
 //
-// Kernels
-//   lsm_row     grid (L, nseq) x 1024: one offset row per work-group.  Pass 1
-//               streams the row once from HBM (each thread's running max, sum of
-//               exp and best key); the K-th largest of the 1024 per-thread best
-//               keys, T, bounds the row's K-th largest key from below (K threads
-//               each hold a key >= T), and is found by sorting each wave's bests
-//               and merging the sorted lists pairwise.  Pass 2 re-reads the row
-//               from L2 and gathers the keys >= T (about K of them), ranked
-//               exactly by counting.  Output: log q_j(v) = (z_v - max) -
-//               ln(sum exp(z - max)) of the K best tokens, in rank order.
-//   build_tree  grid nseq x 256.  The ranked lists go to LDS; wave 0 runs
-//               best-first selection: lane 0 is the root and lane i the i-th
-//               selected node; every lane holds the best not-yet-selected child
-//               of its node, so a selection is one wave max and touches two
-//               lanes.  Finally the nodes are laid out breadth-first with their
-//               ancestor masks.
+// One launch, grid (chunk, offset row, sequence) x 256 threads, three phases:
+//   1. every work-group streams its chunk of an offset row once (every load
+//      issued up front): max, sum of exp, and the chunk's K best keys through a
+//      per-wave threshold and exact rank counting;
+//   2. the last chunk of a row to finish merges the row's chunk lists into the
+//      offset's K best tokens with log q_j(v) = (z_v - max) - ln(sum exp(z - max));
+//   3. the last row of a sequence to be merged runs best-first selection in one
+//      wavefront (lane 0 is the root, lane i the i-th selected node; every lane
+//      offers the best not-yet-selected child of its node, so a selection is one
+//      wave max and touches two lanes) and lays the nodes out breadth-first with
+//      their ancestor masks.
+// Work-groups meet through arrival counters (device-scope atomics); everything
+// they publish to each other is stored and loaded with device-coherent accesses.
 #include "common.h"
 #include "kernels.h"
 
@@ -124,21 +121,22 @@ __device__ __forceinline__ float load_logit<float>(const float* p) { return *p; 
 template <>
 __device__ __forceinline__ float load_logit<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
 
-// One chunk of an offset row: 256 threads x NV vectors of 16 bytes, every load
-// issued before any is used.  Writes the chunk's maximum and sum of
-// exp(z - max) and its K best keys, sorted descending (0 where fewer exist).
+// Phase 1, one chunk of an offset row: 256 threads x NV vectors of 16 bytes,
+// every load issued before any is used.  Publishes the chunk's maximum and sum
+// of exp(z - max) and its K best keys, sorted descending (0 where fewer exist),
+// with device-coherent stores.
 // Threshold: wave w sorts its 64 per-thread best keys and takes the k-th
 // largest, k = ceil(K/4); the minimum T over the four waves is a lower bound of
 // the chunk's K-th largest key (each wave holds k keys >= T).  Only keys >= T
 // (about K of them) are gathered to LDS and ranked exactly by counting; more
 // than kCap of them (massive ties) switches to an exact 8-bit radix select.
 template <typename T, int NV>
-__global__ __launch_bounds__(kChunkThreads) void lsm_chunk_kernel(
-    const T* __restrict__ logits, int L, int V, int N, int nch, float2* __restrict__ cstat,
-    unsigned long long* __restrict__ clist) {
+__device__ __forceinline__ void chunk_topk(const T* __restrict__ logits, int L, int V, int N, int nch,
+                                           unsigned long long* __restrict__ cstat,
+                                           unsigned long long* __restrict__ clist,
+                                           unsigned long long* cand) {
   constexpr int E = 16 / sizeof(T);
   constexpr int IPT = NV * E;
-  __shared__ __attribute__((aligned(16))) unsigned long long cand[kCap];
   __shared__ unsigned long long sel[kSlots];
   __shared__ unsigned long long wt[kChunkWaves];
   __shared__ int wcnt[kChunkWaves];
@@ -231,11 +229,12 @@ __global__ __launch_bounds__(kChunkThreads) void lsm_chunk_kernel(
     float S = 0.f;
     for (int i = 0; i < kChunkWaves; ++i)
       if (red_m[i] != -INFINITY) S += red_s[i] * __builtin_amdgcn_exp2f((red_m[i] - M) * 1.4426950408889634f);
-    cstat[static_cast<size_t>(row) * nch + c] = make_float2(M, S);
+    const unsigned long long ms = (static_cast<unsigned long long>(__float_as_uint(S)) << 32) | __float_as_uint(M);
+    __hip_atomic_store(cstat + static_cast<size_t>(row) * nch + c, ms, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   unsigned long long* out = clist + (static_cast<size_t>(row) * nch + c) * kSlots;
-  if (K <= 0) {
-    if (tid < kSlots) out[tid] = 0ull;
+  if (K <= 0) {  // (uniform) nothing of this offset can enter the tree
+    if (tid < kSlots) __hip_atomic_store(out + tid, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
   unsigned long long Tk = wt[0];
@@ -336,108 +335,113 @@ __global__ __launch_bounds__(kChunkThreads) void lsm_chunk_kernel(
     if (tid < K) sel[count_greater(cand, K, cand[tid])] = cand[tid];
   }
   __syncthreads();
-  if (tid < kSlots) out[tid] = sel[tid];
+  if (tid < kSlots) __hip_atomic_store(out + tid, sel[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__global__ __launch_bounds__(kMaxChunks * kWave) void build_tree_kernel(
-    const float2* __restrict__ cstat, const unsigned long long* __restrict__ clist, int nch,
-    const int32_t* __restrict__ root_token, int L, int V, int N, int32_t* __restrict__ parent,
-    int32_t* __restrict__ depth_out, int32_t* __restrict__ token_out,
-    uint64_t* __restrict__ anc_out, float* __restrict__ score_out,
-    int32_t* __restrict__ n_valid_out) {
-  // ranked log q per offset, -inf past the list (reads reach entry 65); row L is
-  // all -inf (depth-L nodes have no children)
-  __shared__ float lq[GLANCE_MAX_L + 1][kLqRow];
-  __shared__ int tk[GLANCE_MAX_L][kSlots];
-
-  const int s = blockIdx.x, lane = lane_id(), wv = threadIdx.x / kWave;
-
-  // ---- wave j ranks offset j from its chunk lists (sorted, lane l holds entry
-  // l of each).  With k = ceil(K / nch), the K-th largest of the lists' k
-  // leading entries, T, bounds the offset's K-th largest key from below (K
-  // keys >= T among them); the entries >= T, a prefix of each list, are
-  // gathered (about K) and ranked exactly by counting.
-  // per offset: up to 128 leading entries, then up to nch * 64 candidates
-  __shared__ __attribute__((aligned(16))) unsigned long long mcand[GLANCE_MAX_L][128 + kMaxChunks * kSlots];
-  __shared__ unsigned long long mthr[GLANCE_MAX_L];
-  if (wv == 0) {
-    lq[L][lane] = -INFINITY;
-    if (lane < kLqRow - kSlots) lq[L][kSlots + lane] = -INFINITY;
+// Phase 2, the last chunk of offset row `row` to finish: merge the row's chunk
+// lists into its K best tokens, ranked, with log q_j.  With k = ceil(K / nch),
+// the K-th largest of the lists' k leading entries, T, bounds the row's K-th
+// largest key from below (K keys >= T among them); the entries >= T, a prefix
+// of each list, are gathered and ranked exactly by counting.  Writes lq[row][64]
+// (log q in rank order, -inf past K) and tk[row][64] (token ids, -1 past K).
+__device__ __noinline__ void merge_row(const unsigned long long* __restrict__ cstat,
+                                       const unsigned long long* __restrict__ clist, int nch,
+                                       int row, int K, float* __restrict__ lq_out,
+                                       int* __restrict__ tk_out, unsigned long long* buf) {
+  __shared__ float s_lnS, s_M;
+  __shared__ unsigned long long s_thr;
+  __shared__ int wcnt[kChunkWaves];
+  __shared__ float lqr[kSlots];
+  __shared__ int tkr[kSlots];
+  const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+  unsigned long long* lead = buf;          // up to nch * k leading entries
+  unsigned long long* cs = buf + kCap / 2;  // up to nch * 64 candidates
+  constexpr int PER = kMaxChunks * kSlots / kChunkThreads;
+  unsigned long long key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = tid + i * kChunkThreads;
+    key[i] = (idx >> 6) < nch
+                 ? __hip_atomic_load(clist + static_cast<size_t>(row) * nch * kSlots + idx, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT)
+                 : 0ull;
   }
-  if (wv < L) {
-    const int j = wv;
-    const size_t row = static_cast<size_t>(s) * L + j;
-    const int K = k_of(N, V, j);
-    unsigned long long e[kMaxChunks];
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c)
-      e[c] = c < nch ? clist[(row * nch + c) * kSlots + lane] : 0ull;
-    const float2 st = lane < nch ? cstat[row * nch + lane] : make_float2(-INFINITY, 0.f);
-    const float M = wave_max(st.x);
-    float t = (M == -INFINITY || st.y <= 0.f) ? 0.f : st.y * __builtin_amdgcn_exp2f((st.x - M) * 1.4426950408889634f);
+  if (w == 0) {
+    const unsigned long long ms = lane < nch ? __hip_atomic_load(cstat + static_cast<size_t>(row) * nch + lane,
+                                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                             : 0ull;
+    const float m = lane < nch ? __uint_as_float(static_cast<uint32_t>(ms)) : -INFINITY;
+    const float sm = lane < nch ? __uint_as_float(static_cast<uint32_t>(ms >> 32)) : 0.f;
+    const float M = wave_max(m);
+    float t = (M == -INFINITY || sm <= 0.f) ? 0.f : sm * __builtin_amdgcn_exp2f((m - M) * 1.4426950408889634f);
     t = wave_sum(t);
-    const float lnS = logf(t);
-    unsigned long long* mc = mcand[j];
-    const int kc = K > 0 ? (K + nch - 1) / nch : 1;
-    const int n1 = nch * kc;
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c)
-      if (c < nch && lane < kc) mc[c * kc + lane] = e[c];
-    if (lane == 0) mthr[j] = 0ull;
-    __builtin_amdgcn_wave_barrier();  // one wave: LDS is in order
-    for (int x0 = 0; x0 < n1; x0 += 2 * kWave) {
-      const int xa = x0 + lane, xb = x0 + kWave + lane;
-      const unsigned long long va = xa < n1 ? mc[xa] : 0ull, vb = xb < n1 ? mc[xb] : 0ull;
-      int ra, rb;
-      if (x0 + kWave < n1) {
-        rank2(mc, n1, va, vb, ra, rb);
-      } else {  // one key per lane left
-        ra = count_greater(mc, n1, va);
-        rb = K;
-      }
-      if (xa < n1 && va != 0ull && ra == K - 1) mthr[j] = va;
-      if (xb < n1 && vb != 0ull && rb == K - 1) mthr[j] = vb;
+    if (lane == 0) {
+      s_M = M;
+      s_lnS = logf(t);
+      s_thr = 0ull;
     }
-    __builtin_amdgcn_wave_barrier();
-    const unsigned long long Tm = mthr[j];  // 0 when fewer than K leading entries: take all
-    unsigned long long* cs = mc + 128;
-    int C = 0;
+  }
+  if (tid < kSlots) {
+    lqr[tid] = -INFINITY;
+    tkr[tid] = -1;
+  }
+  const int kc = (K + nch - 1) / nch;
+  const int n1 = nch * kc;
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      const bool take = c < nch && e[c] != 0ull && e[c] >= Tm;
-      const unsigned long long bal = __ballot(take);
-      if (take) cs[C + __popcll(bal & ((1ull << lane) - 1ull))] = e[c];
-      C += __popcll(bal);
-    }
-    lq[j][lane] = -INFINITY;
-    if (lane < kLqRow - kSlots) lq[j][kSlots + lane] = -INFINITY;
-    tk[j][lane] = -1;
-    __builtin_amdgcn_wave_barrier();
-    for (int x0 = 0; x0 < C; x0 += 2 * kWave) {
-      const int xa = x0 + lane, xb = x0 + kWave + lane;
-      const unsigned long long va = xa < C ? cs[xa] : 0ull, vb = xb < C ? cs[xb] : 0ull;
-      int ra, rb;
-      if (x0 + kWave < C) {
-        rank2(cs, C, va, vb, ra, rb);
-      } else {
-        ra = count_greater(cs, C, va);
-        rb = K;
-      }
+  for (int i = 0; i < PER; ++i) {
+    const int idx = tid + i * kChunkThreads, c = idx >> 6, en = idx & 63;
+    if (c < nch && en < kc) lead[c * kc + en] = key[i];
+  }
+  __syncthreads();
+  for (int x = tid; x < n1; x += kChunkThreads) {
+    const unsigned long long v = lead[x];
+    if (v != 0ull && count_greater(lead, n1, v) == K - 1) s_thr = v;
+  }
+  __syncthreads();
+  const unsigned long long Tm = s_thr;  // 0 when fewer than K leading entries: take all
+  int cnt = 0;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const unsigned long long k = h ? vb : va;
-        const int rank = h ? rb : ra;
-        if ((h ? xb : xa) < C && rank < K) {
-          const float zz = key_float(static_cast<uint32_t>(k >> 32));
-          lq[j][rank] = (M == -INFINITY || zz == -INFINITY) ? -INFINITY : (zz - M) - lnS;
-          tk[j][rank] = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(k));
-        }
-      }
+  for (int i = 0; i < PER; ++i) cnt += (key[i] != 0ull && key[i] >= Tm) ? 1 : 0;
+  const int incl = wave_incl_sum(cnt);
+  if (lane == kWave - 1) wcnt[w] = incl;
+  __syncthreads();
+  int slot = incl - cnt, C = 0;
+#pragma unroll
+  for (int i = 0; i < kChunkWaves; ++i) {
+    slot += i < w ? wcnt[i] : 0;
+    C += wcnt[i];
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (key[i] != 0ull && key[i] >= Tm) cs[slot++] = key[i];
+  __syncthreads();
+  const float M = s_M, lnS = s_lnS;
+  for (int x = tid; x < C; x += kChunkThreads) {
+    const unsigned long long v = cs[x];
+    const int r = count_greater(cs, C, v);
+    if (r < K) {
+      const float zz = key_float(static_cast<uint32_t>(v >> 32));
+      lqr[r] = (M == -INFINITY || zz == -INFINITY) ? -INFINITY : (zz - M) - lnS;
+      tkr[r] = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(v));
     }
   }
   __syncthreads();
-  if (wv != 0) return;  // the rest is one wavefront; no block barrier follows
+  if (tid < kSlots) {
+    __hip_atomic_store(lq_out + static_cast<size_t>(row) * kSlots + tid, lqr[tid], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(tk_out + static_cast<size_t>(row) * kSlots + tid, tkr[tid], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
 
+// Phase 3, one wavefront, the last row of sequence s to be merged: best-first
+// selection over the ranked lists in LDS and the breadth-first layout.
+__device__ __forceinline__ void select_tree(const float (*lq)[kLqRow], const int (*tk)[kSlots], int s,
+                                         const int32_t* __restrict__ root_token, int L, int N,
+                                         int32_t* __restrict__ parent, int32_t* __restrict__ depth_out,
+                                         int32_t* __restrict__ token_out, uint64_t* __restrict__ anc_out,
+                                         float* __restrict__ score_out, int32_t* __restrict__ n_valid_out) {
+  const int lane = lane_id();
   // ---- best-first selection.  Lane 0 is the root, lane i the i-th selected
   // node; each lane offers the best not-yet-selected child of its node (the
   // next entry of the list of its depth).  Equal scores: smaller depth, then the
@@ -539,25 +543,104 @@ __global__ __launch_bounds__(kMaxChunks * kWave) void build_tree_kernel(
   }
 }
 
+// Arrival of this work-group at a counter shared by `total` work-groups: true
+// for the last one, which returns the counter to zero.  Every store the
+// work-group made before is complete (waited for) when it is counted.
+__device__ __forceinline__ bool arrive_last(unsigned* ctr, int total) {
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == static_cast<unsigned>(total - 1);
+    if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last;
+  }
+  __syncthreads();
+  return s_last != 0;
+}
+
+// The whole tree phase in one launch, grid (chunk, offset, sequence): every
+// work-group ranks its chunk (phase 1); the last chunk of each offset row to
+// finish merges the row (phase 2); the last row of each sequence to be merged
+// builds the tree (phase 3).  Work-groups meet only through device-scope
+// atomics: published values are stored and loaded with device-coherent
+// accesses and are complete before the arrival that announces them.
+template <typename T, int NV>
+__global__ __launch_bounds__(kChunkThreads) void tree_kernel(
+    const T* __restrict__ logits, int L, int V, int N, int nch, unsigned long long* __restrict__ cstat,
+    unsigned long long* __restrict__ clist, float* __restrict__ lq_g, int* __restrict__ tk_g,
+    unsigned* __restrict__ row_cnt, unsigned* __restrict__ seq_cnt, const int32_t* __restrict__ root_token,
+    int32_t* __restrict__ parent, int32_t* __restrict__ depth_out, int32_t* __restrict__ token_out,
+    uint64_t* __restrict__ anc_out, float* __restrict__ score_out, int32_t* __restrict__ n_valid_out) {
+  __shared__ __attribute__((aligned(16))) unsigned long long buf[kCap];
+  const int j = blockIdx.y, sq = blockIdx.z;
+  const int row = sq * L + j;
+  chunk_topk<T, NV>(logits, L, V, N, nch, cstat, clist, buf);
+  if (!arrive_last(row_cnt + row, nch)) return;
+  const int K = k_of(N, V, j);
+  if (K > 0) {
+    __syncthreads();  // buf is reused
+    merge_row(cstat, clist, nch, row, K, lq_g, tk_g, buf);
+  } else if (threadIdx.x < kSlots) {
+    __hip_atomic_store(lq_g + static_cast<size_t>(row) * kSlots + threadIdx.x, -INFINITY, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(tk_g + static_cast<size_t>(row) * kSlots + threadIdx.x, -1, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (!arrive_last(seq_cnt + sq, L)) return;
+  // ranked lists of every offset, -inf past each list (reads reach entry 65);
+  // row L is all -inf (depth-L nodes have no children)
+  __shared__ float lq[GLANCE_MAX_L + 1][kLqRow];
+  __shared__ int tk[GLANCE_MAX_L][kSlots];
+  for (int idx = threadIdx.x; idx < (L + 1) * kLqRow; idx += kChunkThreads) {
+    const int jj = idx / kLqRow, r = idx - jj * kLqRow;
+    float v = -INFINITY;
+    if (jj < L && r < kSlots) {
+      const size_t o = (static_cast<size_t>(sq) * L + jj) * kSlots + r;
+      v = __hip_atomic_load(lq_g + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      tk[jj][r] = __hip_atomic_load(tk_g + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    lq[jj][r] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x >= kWave) return;  // the rest is one wavefront
+  select_tree(lq, tk, sq, root_token, L, N, parent, depth_out, token_out, anc_out, score_out, n_valid_out);
+}
+
 }  // namespace
 
 // Host side -------------------------------------------------------------------
 namespace {
+struct TreeBufs {
+  unsigned long long* cstat;
+  unsigned long long* clist;
+  float* lq;
+  int* tk;
+  unsigned* row_cnt;
+  unsigned* seq_cnt;
+};
+
 template <typename T>
-void launch_chunks(int nv, dim3 ga, const T* logits, int L, int V, int N, int nch, float2* cstat,
-                   unsigned long long* clist, hipStream_t st) {
+void launch_tree(int nv, dim3 ga, const T* logits, int L, int V, int N, int nch, const TreeBufs& b,
+                 const int32_t* root, int32_t* parent, int32_t* depth, int32_t* token, uint64_t* anc,
+                 float* score, int32_t* n_valid, hipStream_t st) {
   switch (nv) {
-#define GLANCE_CHUNK_CASE(n) \
-  case n: lsm_chunk_kernel<T, n><<<ga, kChunkThreads, 0, st>>>(logits, L, V, N, nch, cstat, clist); break;
-    GLANCE_CHUNK_CASE(1)
-    GLANCE_CHUNK_CASE(2)
-    GLANCE_CHUNK_CASE(3)
-    GLANCE_CHUNK_CASE(4)
-    GLANCE_CHUNK_CASE(5)
-    GLANCE_CHUNK_CASE(6)
-    GLANCE_CHUNK_CASE(7)
-    GLANCE_CHUNK_CASE(8)
-#undef GLANCE_CHUNK_CASE
+#define GLANCE_TREE_CASE(n)                                                                         \
+  case n:                                                                                          \
+    tree_kernel<T, n><<<ga, kChunkThreads, 0, st>>>(logits, L, V, N, nch, b.cstat, b.clist, b.lq, b.tk, \
+                                                   b.row_cnt, b.seq_cnt, root, parent, depth, token, \
+                                                   anc, score, n_valid);                            \
+    break;
+    GLANCE_TREE_CASE(1)
+    GLANCE_TREE_CASE(2)
+    GLANCE_TREE_CASE(3)
+    GLANCE_TREE_CASE(4)
+    GLANCE_TREE_CASE(5)
+    GLANCE_TREE_CASE(6)
+    GLANCE_TREE_CASE(7)
+    GLANCE_TREE_CASE(8)
+#undef GLANCE_TREE_CASE
     default: break;
   }
 }
@@ -568,9 +651,19 @@ TreeWs tree_ws_layout(int nseq, int L, int V) {
   TreeWs w;
   const size_t r = static_cast<size_t>(nseq) * L;
   auto up = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
-  w.off_cstat = 0;
-  w.off_clist = up(r * kMaxChunks * sizeof(float2));
-  w.bytes = w.off_clist + up(r * kMaxChunks * kSlots * sizeof(unsigned long long));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += up(bytes);
+    return o;
+  };
+  w.off_cstat = take(r * kMaxChunks * sizeof(unsigned long long));
+  w.off_clist = take(r * kMaxChunks * kSlots * sizeof(unsigned long long));
+  w.off_lq = take(r * kSlots * sizeof(float));
+  w.off_tk = take(r * kSlots * sizeof(int));
+  w.off_row_cnt = take(r * sizeof(unsigned));
+  w.off_seq_cnt = take(static_cast<size_t>(nseq) * sizeof(unsigned));
+  w.bytes = off;
   return w;
 }
 
@@ -580,8 +673,13 @@ glance_status launch_build_tree(const void* logits, int dtype, const int32_t* ro
                                 int32_t* n_valid, void* ws, hipStream_t st) {
   const TreeWs w = tree_ws_layout(nseq, L, V);
   char* base = static_cast<char*>(ws);
-  float2* cstat = reinterpret_cast<float2*>(base + w.off_cstat);
-  unsigned long long* clist = reinterpret_cast<unsigned long long*>(base + w.off_clist);
+  TreeBufs b;
+  b.cstat = reinterpret_cast<unsigned long long*>(base + w.off_cstat);
+  b.clist = reinterpret_cast<unsigned long long*>(base + w.off_clist);
+  b.lq = reinterpret_cast<float*>(base + w.off_lq);
+  b.tk = reinterpret_cast<int*>(base + w.off_tk);
+  b.row_cnt = reinterpret_cast<unsigned*>(base + w.off_row_cnt);
+  b.seq_cnt = reinterpret_cast<unsigned*>(base + w.off_seq_cnt);
   // at most kMaxChunks chunks of 256 threads x nv vectors per offset row
   const int E = dtype == GLANCE_BF16 ? 8 : 4;
   const int per_vec = kChunkThreads * E;
@@ -591,12 +689,11 @@ glance_status launch_build_tree(const void* logits, int dtype, const int32_t* ro
   const int nch = (V + per_vec * nv - 1) / (per_vec * nv);
   const dim3 ga(nch, L, nseq);
   if (dtype == GLANCE_BF16)
-    launch_chunks<uint16_t>(nv, ga, static_cast<const uint16_t*>(logits), L, V, N, nch, cstat, clist, st);
+    launch_tree<uint16_t>(nv, ga, static_cast<const uint16_t*>(logits), L, V, N, nch, b, root, parent,
+                          depth, token, anc, score, n_valid, st);
   else
-    launch_chunks<float>(nv, ga, static_cast<const float*>(logits), L, V, N, nch, cstat, clist, st);
-  GLANCE_LAUNCH_CHECK();
-  build_tree_kernel<<<nseq, kMaxChunks * kWave, 0, st>>>(cstat, clist, nch, root, L, V, N, parent,
-                                                          depth, token, anc, score, n_valid);
+    launch_tree<float>(nv, ga, static_cast<const float*>(logits), L, V, N, nch, b, root, parent, depth,
+                       token, anc, score, n_valid, st);
   GLANCE_LAUNCH_CHECK();
   return GLANCE_OK;
 }
