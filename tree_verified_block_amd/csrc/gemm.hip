@@ -145,6 +145,55 @@ __device__ __forceinline__ const uint16_t* w_row_ptr(const GemmArgs& a, int row)
   return static_cast<const uint16_t*>(a.w.w[sidx]) + static_cast<size_t>(row - start) * a.K;
 }
 
+// Row statistics of one lane's logits acc[t][mb][v] (vocabulary row
+// blk[t]*16 + 4 lg + v, activation row 16 mb + l%16): per activation row the max,
+// its smallest token id and the best other logit in one select-only pass (rows
+// are visited in increasing token order, so a strict comparison keeps the
+// smallest id), then the two sums relative to that max through the hardware
+// exp2.  EDGE: some rows are past the vocabulary; they enter as -inf and d is
+// kept finite so that e * d is 0 for them (e = 0).
+template <int B, bool EDGE>
+__device__ __forceinline__ void head_row_stats(const f32x4 (&acc)[B][4], const int (&blk)[B],
+                                               const bool (&bval)[B], int lg, int N, HeadPart (&hp)[4]) {
+  bool nval[B][4];
+#pragma unroll
+  for (int t = 0; t < B; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) nval[t][v] = !EDGE || (bval[t] & (blk[t] * 16 + 4 * lg + v < N));
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    float mx = -INFINITY, m2 = -INFINITY;
+    int am = 0x7FFFFFFF;
+#pragma unroll
+    for (int t = 0; t < B; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float z = nval[t][v] ? acc[t][mb][v] : -INFINITY;
+        const bool gt = z > mx;
+        m2 = gt ? mx : fmaxf(m2, z);
+        am = gt ? blk[t] * 16 + 4 * lg + v : am;
+        mx = fmaxf(mx, z);
+      }
+    const float ms = EDGE && mx == -INFINITY ? 0.f : mx;
+    float sum = 0.f, tsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < B; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float z = nval[t][v] ? acc[t][mb][v] : -INFINITY;
+        const float d = EDGE ? fmaxf(z - ms, -1e30f) : z - ms;
+        const float e = __builtin_amdgcn_exp2f(d * 1.4426950408889634f);
+        sum += e;
+        tsum = fmaf(e, d, tsum);
+      }
+    hp[mb].m = mx;
+    hp[mb].am = am;
+    hp[mb].m2 = m2;
+    hp[mb].s = sum;
+    hp[mb].t = tsum;
+  }
+}
+
 // ------------------------------------------------------------------ LM head
 // Work-group = 4 waves over one 64-row activation tile; wave G owns blocks
 // G, G + NG, ... (B of them).  Each weight chunk (64 deep) of a block is loaded
@@ -274,49 +323,11 @@ __global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int
   }
 
   // acc[t][mb][v]: vocabulary row blk[t]*16 + 4 lg + v, activation row m0 + 16 mb + lr.
-  // Per lane and activation row: max, its smallest token id and the best other
-  // logit in one select-only pass (rows are visited in increasing token order, so
-  // a strict comparison keeps the smallest id; rows past the vocabulary enter as
-  // -inf), then the two sums relative to that max.
-  bool nval[B][4];
-#pragma unroll
-  for (int t = 0; t < B; ++t)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) nval[t][v] = bval[t] & (blk[t] * 16 + 4 * lg + v < a.N);
   HeadPart hp[4];
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    float mx = -INFINITY, m2 = -INFINITY;
-    int am = 0x7FFFFFFF;
-#pragma unroll
-    for (int t = 0; t < B; ++t)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float z = nval[t][v] ? acc[t][mb][v] : -INFINITY;
-        const bool gt = z > mx;
-        m2 = gt ? mx : fmaxf(m2, z);
-        am = gt ? blk[t] * 16 + 4 * lg + v : am;
-        mx = gt ? z : mx;
-      }
-    // d = z - max, kept finite so that e * d is 0 for absent rows (e = 0)
-    const float ms = mx == -INFINITY ? 0.f : mx;
-    float sum = 0.f, tsum = 0.f;
-#pragma unroll
-    for (int t = 0; t < B; ++t)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float z = nval[t][v] ? acc[t][mb][v] : -INFINITY;
-        const float d = fmaxf(z - ms, -1e30f);
-        const float e = __builtin_amdgcn_exp2f(d * 1.4426950408889634f);
-        sum += e;
-        tsum = fmaf(e, d, tsum);
-      }
-    hp[mb].m = mx;
-    hp[mb].am = am;
-    hp[mb].m2 = m2;
-    hp[mb].s = sum;
-    hp[mb].t = tsum;
-  }
+  if (bval[B - 1] && blk[B - 1] * 16 + 16 <= a.N)  // (wave-uniform) every row of the wave exists
+    head_row_stats<B, false>(acc, blk, bval, lg, a.N, hp);
+  else
+    head_row_stats<B, true>(acc, blk, bval, lg, a.N, hp);
   if (a.logits) {
 #pragma unroll
     for (int t = 0; t < B; ++t)
