@@ -129,10 +129,12 @@ __global__ __launch_bounds__(kAThreads) void tree_attn_bf16_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // ---- S^T = K Q^T: kKT keys x this wave's 32 queries
+  // ---- S^T = K Q^T: kKT keys x this wave's 32 queries (32-key blocks past the
+  // tile's keys are skipped: they are masked)
   f32x16 acc_s[kKT / 32] = {};
 #pragma unroll
   for (int kb = 0; kb < kKT / 32; ++kb) {
+    if (kb * 32 >= nk) break;  // (uniform)
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Ks[kb * 32 + j][ks * 16 + 8 * g]);
@@ -142,35 +144,46 @@ __global__ __launch_bounds__(kAThreads) void tree_attn_bf16_kernel(AttnArgs a) {
   // element v of acc_s[kb]: key kb*32 + 8 (v/4) + 4 g + v%4 of the tile, query j
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(kHD));
   float m = -INFINITY;
+  if (!tree_split && nk == kKT) {  // (uniform) a full prefix tile: every key visible
 #pragma unroll
-  for (int kb = 0; kb < kKT / 32; ++kb) {
+    for (int kb = 0; kb < kKT / 32; ++kb)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int key = kb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-      bool vis = key < nk;
-      if (tree_split) vis = vis && ((qanc >> key) & 1ull);
-      const float sv = vis ? acc_s[kb][v] * scale_log2 : -INFINITY;
-      acc_s[kb][v] = sv;
-      m = fmaxf(m, sv);
+      for (int v = 0; v < 16; ++v) {
+        acc_s[kb][v] *= scale_log2;
+        m = fmaxf(m, acc_s[kb][v]);
+      }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < kKT / 32; ++kb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = kb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+        bool vis = key < nk;
+        if (tree_split) vis = vis && ((qanc >> key) & 1ull);
+        const float sv = vis ? acc_s[kb][v] * scale_log2 : -INFINITY;
+        acc_s[kb][v] = sv;
+        m = fmaxf(m, sv);
+      }
     }
   }
   m = fmaxf(m, __shfl_xor(m, 32, kWave));
+  // P rounded to bf16 in pairs (hardware round-to-nearest-even); l sums the
+  // rounded values, so that it normalises exactly the P that enters O
+  const float mz = m == -INFINITY ? 0.f : m;  // (no visible key: every p is exp2(-inf) = 0)
   float lsum = 0.f;
 #pragma unroll
   for (int kb = 0; kb < kKT / 32; ++kb) {
 #pragma unroll
     for (int vg = 0; vg < 4; ++vg) {
-      uint16_t pb[4];
+      uint32_t pw[2];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float p = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(acc_s[kb][4 * vg + t] - m);
-        pb[t] = f32_to_bf16(p);
-        lsum += bf16_to_f32(pb[t]);
+      for (int t = 0; t < 2; ++t) {
+        const float p0 = __builtin_amdgcn_exp2f(acc_s[kb][4 * vg + 2 * t] - mz);
+        const float p1 = __builtin_amdgcn_exp2f(acc_s[kb][4 * vg + 2 * t + 1] - mz);
+        pw[t] = pack_bf16x2(p0, p1);
+        lsum += __uint_as_float(pw[t] << 16) + __uint_as_float(pw[t] & 0xFFFF0000u);
       }
-      uint2 u;
-      u.x = pb[0] | (static_cast<uint32_t>(pb[1]) << 16);
-      u.y = pb[2] | (static_cast<uint32_t>(pb[3]) << 16);
-      *reinterpret_cast<uint2*>(&Ps[w][j][kb * 32 + 8 * vg + 4 * g]) = u;
+      *reinterpret_cast<uint2*>(&Ps[w][j][kb * 32 + 8 * vg + 4 * g]) = make_uint2(pw[0], pw[1]);
     }
   }
   lsum += __shfl_xor(lsum, 32, kWave);
@@ -183,6 +196,7 @@ __global__ __launch_bounds__(kAThreads) void tree_attn_bf16_kernel(AttnArgs a) {
     const int dim = db * 32 + j;
 #pragma unroll
     for (int ks = 0; ks < kKT / 16; ++ks) {
+      if (ks * 16 >= nk) break;  // (uniform) keys past the tile have p = 0
       const int kblk = (ks * 16 + 8 * g) >> 3;
       const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Vt[dim][8 * (kblk ^ ((dim >> 3) & 15))]);
       const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&Ps[w][j][ks * 16 + 8 * g]);

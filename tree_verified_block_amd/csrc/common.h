@@ -38,6 +38,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ float rne_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
 
+// Two floats rounded to bf16 (nearest even) and packed, lo in the low half:
+// the hardware conversion (one instruction on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t h = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 // ------------------------------------------------------- order-preserving keys
 // Maps a float to an unsigned key whose unsigned order is the float order
 // (-0 sorts just below +0; NaN is not expected).

@@ -462,29 +462,31 @@ __device__ __forceinline__ void select_tree(const float (*lq)[kLqRow], const int
   uint32_t c_hi = lane == 0 ? okey(fq) : 0u;
   float nx_q = lq[0][1];  // log q after the offered child (lane 0: the root's second child)
   int n_pop = 0;
-  for (int i = 1; i <= N; ++i) {
-    const uint32_t mh = wave_umax(c_hi);
-    if (mh == 0u) break;
+  uint32_t mh = N >= 1 ? wave_umax(c_hi) : 0u;
+  for (int i = 1; mh != 0u;) {
     unsigned long long cm = __ballot(c_hi == mh);
     if (__popcll(cm) > 1) {  // equal scores: the smallest depth, then the lowest lane
       const uint32_t lo = (c_hi == mh) ? ~static_cast<uint32_t>(st >> 16) : 0u;
       const uint32_t ml = wave_umax(lo);
       cm = __ballot(c_hi == mh && ~static_cast<uint32_t>(st >> 16) == ml);
     }
-    const int p = __ffsll(static_cast<long long>(cm)) - 1;
+    const int p = __builtin_ctzll(cm);  // cm holds the lane of mh, never empty
     const int w_st = readlane_i(st, p);
     const int dn = (w_st >> 16) + 1;                        // the new node's depth
     const int new_st = (dn << 16) | ((w_st & 255) << 8);    // its own rank, first child offered
     const float w_score = __uint_as_float((0x7F800000u - mh) | 0x80000000u);
     const float q0 = readlane_f(fq, dn);
     const bool isp = lane == p, isi = lane == i;
-    st = isi ? new_st : (isp ? w_st + 1 : st);
+    st += isp ? 1 : 0;
+    st = isi ? new_st : st;
     n_score = isi ? w_score : n_score;
     n_par = isi ? p : n_par;
     const uint32_t k = okey(n_score + (isi ? q0 : nx_q));
-    c_hi = (isp || isi) ? k : c_hi;
+    c_hi = (isp | isi) ? k : c_hi;
     nx_q = lq[st >> 16][(st & 255) + 1];
     n_pop = i;
+    if (++i > N) break;
+    mh = wave_umax(c_hi);
   }
 
   // ---- breadth-first layout: rows by (depth, parent row, token id), level by
