@@ -205,6 +205,44 @@ glance_status glance_accept_walk(const int32_t* parent, const int32_t* token,
                                  float gap_flag, int32_t* n_accept, int32_t* out_tokens,
                                  int32_t* path_rows, int32_t* flagged, void* stream);
 
+/* ------------------------------------------------------- after step 5 --
+ * glance_commit_kv: append one round's accepted path to one layer's cache.
+ *
+ * Defines (paper §3.1; App. B.1, proof of Theorem 1: the next round conditions
+ * on x o b o Y_{1:A(S)}): the K and V entries of path rows 0..A (the root b and
+ * the A accepted nodes, at positions P..P+A, K already rotated by the verify
+ * pass) become cache rows P..P+A of the round's sequence, P = kv_offsets[1].
+ * Call it once per layer after glance_accept_walk, then glance_advance_round.
+ *
+ *   tree_k, tree_v    [n_rows][Hkv][D] dtype: this layer's tree-row K/V (the
+ *                     tree_k / tree_v outputs of its glance_tree_attn call)
+ *   path_rows, n_accept  glance_accept_walk outputs
+ *   kv_offsets        [2] int64: the sequence's prefix is cache rows
+ *                     [kv_offsets[0], kv_offsets[1]); read only here
+ *   k_cache, v_cache  [cap][Hkv][D] dtype: this layer's caches
+ *   cap               (host) rows the caches hold.  The caller keeps
+ *                     kv_offsets[1] + L + 1 <= cap; rows at or past cap are
+ *                     not written (never out of bounds).
+ * Limits: nseq == 1 (several packed sequences have no room to grow in place;
+ * other values return GLANCE_ERR_UNSUPPORTED); 1 <= L <= GLANCE_MAX_L;
+ * Hkv * D * element size a multiple of 16 bytes.
+ */
+glance_status glance_commit_kv(const void* tree_k, const void* tree_v, int32_t dtype,
+                               const int32_t* path_rows, const int32_t* n_accept, int32_t nseq,
+                               int32_t L, int32_t Hkv, int32_t D, const int64_t* kv_offsets,
+                               void* k_cache, void* v_cache, int64_t cap, void* stream);
+
+/* glance_advance_round: after every layer's glance_commit_kv, move the prefix
+ * end past the committed entries and install the emitted token as the next
+ * root: kv_offsets[1] += A + 1; root_token[0] = out_tokens[A] (paper §3.1: a
+ * round commits A(S) + 1 tokens, the last being the next round's root).
+ *   n_accept [1], out_tokens [L+1]: glance_accept_walk outputs
+ *   kv_offsets [2] int64, root_token [1] int32: updated in place
+ * Limits: nseq == 1.
+ */
+glance_status glance_advance_round(const int32_t* n_accept, const int32_t* out_tokens, int32_t nseq,
+                                   int64_t* kv_offsets, int32_t* root_token, void* stream);
+
 /* ------------------------------------------------------------------ helpers -- */
 const char* glance_status_string(int32_t status); /* static text (host)       */
 const char* glance_last_error(void);              /* this thread's last error */

@@ -92,3 +92,33 @@ def oracle_round(inp: dict, r: int = 0, exact: str = "beam", continuation_check=
             res["greedy"] = continuation(model, s, root, t["top"], cfg.L)
         out.append(res)
     return out
+
+
+def multi_round(model: mdl.TargetModel, s: int, root: int, draft_fn, n_rounds: int, dtype: str,
+                N: int, L: int):
+    """Rounds of the method chained by committing each round's accepted path
+    (paper §3.1: a round commits A(S) + 1 tokens, the last of which is the next
+    round's root; App. B.1: the next round conditions on x o b o Y_{1:A(S)}).
+
+    Round r builds its tree from draft_fn(r, stream) (stored draft logits
+    [L][V]) at the current root, evaluates every
+    node on its explicit sequence after the prefix and every token committed so
+    far, walks, and appends the walk's tokens to the stream.  Returns the stream
+    [b, t_1, t_2, ..] (the first root, then every committed token and later root
+    in order) and per round (A(S), the smallest top-2 gap on the walk)."""
+    stream = [int(root)]
+    rounds = []
+    for r in range(n_rounds):
+        z = draft_fn(r, stream)
+        b = stream[-1]
+        t = build_tree(z, dtype, b, N, "beam")
+        ctx = tuple(stream[1:])          # committed tokens after the first root, ending at b
+        order = t["order"]
+        paths = [ctx[:j] for j in range(len(ctx))] + [ctx + p for p in order]
+        ev = mdl.evaluate_paths(model, s, stream[0], paths)
+        zr = model.logits(ev["final"][len(ctx):])
+        am, _, gap, _ = mdl.row_stats(zr)
+        a, toks, rows = wk.walk(t["parent"], t["token"], t["n_valid"], am, L)
+        rounds.append((a, float(np.min(gap[rows]))))
+        stream.extend(int(x) for x in toks)
+    return stream, rounds

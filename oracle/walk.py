@@ -57,3 +57,20 @@ def walk(parent, token, n_valid: int, argmax_rows, L: int):
         if not kids or len(out) > L:
             return len(out) - 1, out, rows
         r = kids[0]
+
+
+def greedy_stream(model: TargetModel, s: int, root: int, n: int):
+    """Plain autoregressive greedy decoding after x o b (paper §3.1, the
+    temperature-0 reference that Theorem 1 says the method reproduces): the n
+    tokens Y_1..Y_n, Y_k = argmax p(. | x o b o Y_{1:k-1}), with the top-2 logit
+    gap of each step (how far each choice is from a tie)."""
+    dec = Decoder(model, s)
+    z = dec.extend(root)
+    out, gaps = [], []
+    for _ in range(n):
+        y = int(np.argmax(z))
+        top = np.partition(z, -2)[-2:]
+        out.append(y)
+        gaps.append(float(top[1] - top[0]))
+        z = dec.extend(y)
+    return out, gaps

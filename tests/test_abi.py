@@ -122,6 +122,30 @@ def test_accept_walk_rejects_bad_arguments(lib):
     assert lib.glance_accept_walk(p, p, p, p, p + 4, 1, 64, 15, 1e-3, p, p, p, p, None) == -2
 
 
+def test_commit_and_advance_reject_bad_arguments(lib):
+    p = OK_PTR
+    ok = dict(tk=p, tv=p, dtype=1, path=p, na=p, nseq=1, L=15, Hkv=8, D=128, kvo=p, kc=p, vc=p,
+              cap=2048)
+
+    def commit(**kw):
+        a = {**ok, **kw}
+        return lib.glance_commit_kv(a["tk"], a["tv"], a["dtype"], a["path"], a["na"], a["nseq"],
+                                    a["L"], a["Hkv"], a["D"], a["kvo"], a["kc"], a["vc"], a["cap"],
+                                    None)
+
+    assert commit(nseq=2) == -4
+    assert commit(dtype=7) == -1
+    assert commit(L=0) == -1
+    assert commit(L=17) == -1
+    assert commit(Hkv=1, D=2, dtype=0) == -1  # 8-byte rows
+    assert commit(cap=-1) == -1
+    assert commit(kc=None) == -1
+    assert commit(vc=p + 8) == -2
+    assert lib.glance_advance_round(p, p, 2, p, p, None) == -4
+    assert lib.glance_advance_round(p, None, 1, p, p, None) == -1
+    assert lib.glance_advance_round(p, p, 1, p + 4, p, None) == -2
+
+
 def test_binding_requires_built_library(tmp_path):
     """The binding never falls back: a missing library raises."""
     with pytest.raises(RuntimeError, match="missing"):

@@ -103,3 +103,19 @@ def glance_accept_walk(parent, token, n_valid, argmax, gap, nseq, n_rows, L, gap
     _lib.call("glance_accept_walk", _ptr(parent), _ptr(token), _ptr(n_valid), _ptr(argmax),
               _ptr(gap), nseq, n_rows, L, float(gap_flag), _ptr(n_accept), _ptr(out_tokens),
               _ptr(path_rows), _ptr(flagged), _stream(stream))
+
+
+# ---------------------------------------------------------------- after step 5
+def glance_commit_kv(tree_k, tree_v, path_rows, n_accept, L, kv_offsets, k_cache, v_cache,
+                     stream=None):
+    """Append one layer's accepted path entries to its cache (one sequence)."""
+    _, Hkv, D = tree_k.shape
+    _lib.call("glance_commit_kv", _ptr(tree_k), _ptr(tree_v), dtype_code(tree_k), _ptr(path_rows),
+              _ptr(n_accept), n_accept.shape[0], L, Hkv, D, _ptr(kv_offsets), _ptr(k_cache),
+              _ptr(v_cache), k_cache.shape[0], _stream(stream))
+
+
+def glance_advance_round(n_accept, out_tokens, kv_offsets, root_token, stream=None):
+    """Move the prefix end past the committed entries and set the next root."""
+    _lib.call("glance_advance_round", _ptr(n_accept), _ptr(out_tokens), n_accept.shape[0],
+              _ptr(kv_offsets), _ptr(root_token), _stream(stream))

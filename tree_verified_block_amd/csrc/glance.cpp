@@ -400,4 +400,41 @@ glance_status glance_accept_walk(const int32_t* parent, const int32_t* token,
                             static_cast<hipStream_t>(stream));
 }
 
+
+// -------------------------------------------------------------- after step 5
+glance_status glance_commit_kv(const void* tree_k, const void* tree_v, int32_t dtype,
+                               const int32_t* path_rows, const int32_t* n_accept, int32_t nseq,
+                               int32_t L, int32_t Hkv, int32_t D, const int64_t* kv_offsets,
+                               void* k_cache, void* v_cache, int64_t cap, void* stream) {
+  g_last_error.clear();
+  REQUIRE(dtype == GLANCE_F32 || dtype == GLANCE_BF16, "dtype = %d is not GLANCE_F32 or GLANCE_BF16", dtype);
+  if (nseq != 1) return fail(GLANCE_ERR_UNSUPPORTED, "nseq = %d: packed sequences cannot grow in place", nseq);
+  REQUIRE(L >= 1 && L <= GLANCE_MAX_L, "L = %d outside [1, %d]", L, GLANCE_MAX_L);
+  REQUIRE(Hkv >= 1 && D >= 1, "Hkv = %d, D = %d", Hkv, D);
+  REQUIRE(cap >= 0, "cap = %lld < 0", static_cast<long long>(cap));
+  const size_t row_bytes = static_cast<size_t>(Hkv) * D * (dtype == GLANCE_BF16 ? 2 : 4);
+  REQUIRE(row_bytes % 16 == 0, "Hkv * D * element size = %zu is not a multiple of 16", row_bytes);
+  REQUIRE_PTR(tree_k);
+  REQUIRE_PTR(tree_v);
+  REQUIRE_PTR(path_rows);
+  REQUIRE_PTR(n_accept);
+  REQUIRE_PTR(kv_offsets);
+  REQUIRE_PTR(k_cache);
+  REQUIRE_PTR(v_cache);
+  return launch_commit_kv(tree_k, tree_v, path_rows, n_accept, kv_offsets, cap, L, row_bytes,
+                          k_cache, v_cache, static_cast<hipStream_t>(stream));
+}
+
+glance_status glance_advance_round(const int32_t* n_accept, const int32_t* out_tokens, int32_t nseq,
+                                   int64_t* kv_offsets, int32_t* root_token, void* stream) {
+  g_last_error.clear();
+  if (nseq != 1) return fail(GLANCE_ERR_UNSUPPORTED, "nseq = %d: only one sequence advances in place", nseq);
+  REQUIRE_PTR(n_accept);
+  REQUIRE_PTR(out_tokens);
+  REQUIRE_PTR(kv_offsets);
+  REQUIRE_PTR(root_token);
+  return launch_advance_round(n_accept, out_tokens, kv_offsets, root_token,
+                              static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

@@ -113,5 +113,11 @@ glance_status launch_accept_walk(const int32_t* parent, const int32_t* token,
                                  const float* gap, int nseq, int n_rows, int L, float gap_flag,
                                  int32_t* n_accept, int32_t* out_tokens, int32_t* path_rows,
                                  int32_t* flagged, hipStream_t st);
+glance_status launch_commit_kv(const void* tree_k, const void* tree_v, const int32_t* path_rows,
+                               const int32_t* n_accept, const int64_t* kv_offsets, int64_t cap,
+                               int L, size_t row_bytes, void* k_cache, void* v_cache,
+                               hipStream_t st);
+glance_status launch_advance_round(const int32_t* n_accept, const int32_t* out_tokens,
+                                   int64_t* kv_offsets, int32_t* root, hipStream_t st);
 
 }  // namespace glance

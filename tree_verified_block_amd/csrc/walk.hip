@@ -4,6 +4,12 @@
 // and stop.  The walk visits at most L + 1 rows, so one wavefront per round
 // does it: lane c holds row c's parent and token, and a child lookup is one
 // ballot.
+//
+// After the walk (paper §3.1 and App. B.1: the next round conditions on
+// x o b o Y_{1:A}): the K/V entries of the path's rows (the root and the A
+// accepted nodes, rotated at positions P..P+A by the verify pass) are appended
+// to the cache, then the prefix end moves by A + 1 and the emitted token becomes
+// the next root, all on the device.
 #include "common.h"
 #include "kernels.h"
 
@@ -49,7 +55,52 @@ __global__ __launch_bounds__(kWave) void accept_walk_kernel(
   }
 }
 
+// Block k copies the K and V entries of path row k (k <= A) to cache row
+// kv_offsets[1] + k; rows at or past the cache's capacity are not written.
+__global__ __launch_bounds__(kWave) void commit_kv_kernel(
+    const uint4* __restrict__ tree_k, const uint4* __restrict__ tree_v,
+    const int32_t* __restrict__ path_rows, const int32_t* __restrict__ n_accept,
+    const int64_t* __restrict__ kv_offsets, int64_t cap, int row_vec, uint4* __restrict__ k_cache,
+    uint4* __restrict__ v_cache) {
+  const int k = blockIdx.x;
+  if (k > n_accept[0]) return;
+  const int64_t dst = kv_offsets[1] + k;
+  if (dst < 0 || dst >= cap) return;
+  const size_t src = static_cast<size_t>(path_rows[k]) * row_vec;
+  for (int i = threadIdx.x; i < row_vec; i += kWave) {
+    k_cache[static_cast<size_t>(dst) * row_vec + i] = tree_k[src + i];
+    v_cache[static_cast<size_t>(dst) * row_vec + i] = tree_v[src + i];
+  }
+}
+
+__global__ void advance_round_kernel(const int32_t* __restrict__ n_accept,
+                                     const int32_t* __restrict__ out_tokens,
+                                     int64_t* __restrict__ kv_offsets, int32_t* __restrict__ root) {
+  const int a = n_accept[0];
+  kv_offsets[1] += a + 1;
+  root[0] = out_tokens[a];
+}
+
 }  // namespace
+
+glance_status launch_commit_kv(const void* tree_k, const void* tree_v, const int32_t* path_rows,
+                               const int32_t* n_accept, const int64_t* kv_offsets, int64_t cap,
+                               int L, size_t row_bytes, void* k_cache, void* v_cache,
+                               hipStream_t st) {
+  commit_kv_kernel<<<L + 1, kWave, 0, st>>>(
+      static_cast<const uint4*>(tree_k), static_cast<const uint4*>(tree_v), path_rows, n_accept,
+      kv_offsets, cap, static_cast<int>(row_bytes / sizeof(uint4)), static_cast<uint4*>(k_cache),
+      static_cast<uint4*>(v_cache));
+  GLANCE_LAUNCH_CHECK();
+  return GLANCE_OK;
+}
+
+glance_status launch_advance_round(const int32_t* n_accept, const int32_t* out_tokens,
+                                   int64_t* kv_offsets, int32_t* root, hipStream_t st) {
+  advance_round_kernel<<<1, 1, 0, st>>>(n_accept, out_tokens, kv_offsets, root);
+  GLANCE_LAUNCH_CHECK();
+  return GLANCE_OK;
+}
 
 glance_status launch_accept_walk(const int32_t* parent, const int32_t* token,
                                  const int32_t* n_valid, const int32_t* argmax,

@@ -21,8 +21,12 @@ def to_device(x: np.ndarray, dtype: str, device) -> torch.Tensor:
 
 
 class DeviceRound:
+    """``capacity`` (one sequence only): the caches get room for that many rows and
+    every layer keeps its own tree-row K/V, so that ``commit()`` can append each
+    round's accepted path and chain rounds on the device."""
+
     def __init__(self, inp: dict, device="cuda", keep_layers: bool = False,
-                 want_logits: bool = False):
+                 want_logits: bool = False, capacity: int | None = None):
         cfg = inp["cfg"]
         self.cfg = cfg
         self.inp = inp
@@ -38,6 +42,20 @@ class DeviceRound:
         self.layers = [{k: to_device(v, dt, device) for k, v in lw.items()} for lw in inp["layers"]]
         self.kv_offsets = torch.from_numpy(inp["kv_offsets"].astype(np.int64)).to(device)
         self.max_prefix = int(inp["prefix_len"].max())
+        self.capacity = capacity
+        if capacity is not None:
+            if cfg.nseq != 1:
+                raise ValueError("chained rounds need one sequence")
+            P = int(inp["prefix_len"][0])
+            if capacity < P + cfg.L + 1:
+                raise ValueError("capacity below one round")
+            for lw in self.layers:
+                for name in ("k_cache", "v_cache"):
+                    c = lw[name]
+                    big = torch.zeros((capacity,) + tuple(c.shape[1:]), dtype=c.dtype, device=device)
+                    big[:c.shape[0]].copy_(c)
+                    lw[name] = big
+            self.max_prefix = capacity - cfg.L - 1
         self.rope_cos = torch.from_numpy(inp["rope_cos"]).to(device)
         self.rope_sin = torch.from_numpy(inp["rope_sin"]).to(device)
         self.tree = api.tree_outputs(self.nseq, self.N, device)
@@ -49,8 +67,10 @@ class DeviceRound:
         self.attn_out = [torch.empty((self.R, HD), dtype=torch.float32, device=device)
                          for _ in range(n_keep)]
         self.h_layers = [torch.empty((self.R, d), dtype=tdt, device=device) for _ in range(n_keep)]
-        self.tree_k = torch.empty((self.R, cfg.Hkv, cfg.D), dtype=tdt, device=device)
-        self.tree_v = torch.empty((self.R, cfg.Hkv, cfg.D), dtype=tdt, device=device)
+        n_kv = cfg.n_layers if capacity is not None else 1
+        self.tree_ks = [torch.empty((self.R, cfg.Hkv, cfg.D), dtype=tdt, device=device) for _ in range(n_kv)]
+        self.tree_vs = [torch.empty((self.R, cfg.Hkv, cfg.D), dtype=tdt, device=device) for _ in range(n_kv)]
+        self.tree_k, self.tree_v = self.tree_ks[-1], self.tree_vs[-1]
         self.argmax = torch.empty(self.R, dtype=torch.int32, device=device)
         self.top1 = torch.empty(self.R, dtype=torch.float32, device=device)
         self.gap = torch.empty(self.R, dtype=torch.float32, device=device)
@@ -98,7 +118,8 @@ class DeviceRound:
                                  self.rope_cos, self.rope_sin, self.nseq, self.n_rows,
                                  cfg.d_model, cfg.Hq, cfg.Hkv, cfg.D, self.ws_attn,
                                  attn_out=self.attn_out[li] if self.keep_layers else None,
-                                 tree_k=self.tree_k, tree_v=self.tree_v, stream=stream)
+                                 tree_k=self.tree_ks[min(li, len(self.tree_ks) - 1)],
+                                 tree_v=self.tree_vs[min(li, len(self.tree_vs) - 1)], stream=stream)
             if self.keep_layers:
                 self.h_layers[li].copy_(h_out)
 
@@ -121,6 +142,22 @@ class DeviceRound:
         self.step_attn(stream)
         self.step_head(stream)
         self.step_walk(stream)
+
+    def set_draft(self, draft_logits: np.ndarray, root: int | None = None):
+        """Next round's draft logits [1][L][V] (and, optionally, its root)."""
+        self.draft = to_device(draft_logits, self.cfg.dtype, self.device)
+        if root is not None:
+            self.root = torch.tensor([root], dtype=torch.int32, device=self.device)
+
+    def commit(self, stream=None):
+        """Append the round's accepted path to every layer's cache, move the prefix
+        end past it and make the emitted token the next root (on the device)."""
+        if self.capacity is None:
+            raise RuntimeError("commit needs a DeviceRound built with a capacity")
+        for li, lw in enumerate(self.layers):
+            api.glance_commit_kv(self.tree_ks[li], self.tree_vs[li], self.path_rows, self.n_accept,
+                                 self.L, self.kv_offsets, lw["k_cache"], lw["v_cache"], stream)
+        api.glance_advance_round(self.n_accept, self.out_tokens, self.kv_offsets, self.root, stream)
 
     def fetch(self) -> dict:
         torch.cuda.synchronize()
