@@ -80,6 +80,49 @@ def cpu_baseline(inp, budget_s: float = 10.0) -> dict:
             "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
+def chain_measure(inp, cfg, drafts, K: int, warm: int = 5) -> dict:
+    """Chained rounds on the device: each round's verify path, then the commit of
+    the accepted path into the cache and the advance of prefix and root (no host
+    round trip).  The prefix grows by A + 1 per round; the synthetic drafts do
+    not follow the target, so A is mostly 0 here.  HIP events on the launch
+    stream bracket the commit of every fourth round."""
+    import torch
+    from synth.gen import rope_tables
+    from tree_verified_block_amd.round import DeviceRound
+    P0 = int(inp["prefix_len"][0])
+    cap = P0 + (K + warm + 1) * (cfg.L + 1)
+    inp = dict(inp)  # rotary tables covering every position the chain reaches
+    inp["rope_cos"], inp["rope_sin"] = rope_tables(cap + 1, cfg.D, cfg.rope_theta)
+    dev = DeviceRound(inp, device="cuda", capacity=cap)
+    dev.set_round(0)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        dev.draft = drafts[i % len(drafts)]
+        dev.run()
+        if ev:
+            ev[0].record(stream)
+        dev.commit()
+        if ev:
+            ev[1].record(stream)
+
+    for i in range(warm):
+        step(i)
+    torch.cuda.synchronize()
+    p_start = int(dev.kv_offsets[1])
+    cev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for i in range(0, K, 4)}
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, cev.get(i))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    p_end = int(dev.kv_offsets[1])
+    return {"rounds_per_s": round(K / wall, 2), "ms_per_round": round(wall / K * 1e3, 4),
+            "commit_us": round(float(np.mean([e[0].elapsed_time(e[1]) for e in cev.values()])) * 1e3, 2),
+            "tokens_per_round": round((p_end - p_start) / K, 3), "prefix": [p_start, p_end],
+            "rounds": K}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -88,6 +131,8 @@ def main():
     ap.add_argument("--config", default="qwen8b_1layer")
     ap.add_argument("--seed", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chain-rounds", type=int, default=50,
+                    help="chained rounds (verify + KV commit + advance) to time; 0 skips")
     ap.add_argument("--probe-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -186,6 +231,10 @@ def main():
                      "frac": round(head_gbs / HBM_PEAK_GBS, 4),
                      "traffic": head_traffic(cfg)},
     }
+    if args.chain_rounds > 0 and cfg.nseq == 1 and drafts:
+        del dev
+        torch.cuda.empty_cache()
+        out["chain"] = chain_measure(inp, cfg, drafts, args.chain_rounds)
     if args.probe_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
