@@ -123,6 +123,43 @@ def chain_measure(inp, cfg, drafts, K: int, warm: int = 5) -> dict:
             "rounds": K}
 
 
+def sampled_measure(inp, cfg, drafts, K: int, T: float = 1.0, warm: int = 5) -> dict:
+    """Verify rounds that also draw one token per row at temperature T and walk
+    on the draws (a new Philox round id per round); HIP events bracket the LM
+    head of every fourth round."""
+    import torch
+    from tree_verified_block_amd.round import DeviceRound
+    dev = DeviceRound(inp, device="cuda", temperature=T, seed=1234)
+    dev.set_round(0)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        dev.draft = drafts[i % len(drafts)]
+        dev.round_id = i
+        dev.step_tree()
+        dev.step_attn()
+        if ev:
+            ev[0].record(stream)
+        dev.step_head()
+        if ev:
+            ev[1].record(stream)
+        dev.step_walk()
+
+    for i in range(warm):
+        step(i)
+    torch.cuda.synchronize()
+    hev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for i in range(0, K, 4)}
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, hev.get(i))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return {"temperature": T, "rounds_per_s": round(K / wall, 2),
+            "ms_per_round": round(wall / K * 1e3, 4),
+            "head_us": round(float(np.mean([e[0].elapsed_time(e[1]) for e in hev.values()])) * 1e3, 2),
+            "rounds": K}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +170,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chain-rounds", type=int, default=50,
                     help="chained rounds (verify + KV commit + advance) to time; 0 skips")
+    ap.add_argument("--sampled-rounds", type=int, default=50,
+                    help="verify rounds that sample at T = 1 to time; 0 skips")
     ap.add_argument("--probe-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -231,9 +270,12 @@ def main():
                      "frac": round(head_gbs / HBM_PEAK_GBS, 4),
                      "traffic": head_traffic(cfg)},
     }
-    if args.chain_rounds > 0 and cfg.nseq == 1 and drafts:
-        del dev
+    del dev
+    torch.cuda.empty_cache()
+    if args.sampled_rounds > 0 and drafts:
+        out["sampled"] = sampled_measure(inp, cfg, drafts, args.sampled_rounds)
         torch.cuda.empty_cache()
+    if args.chain_rounds > 0 and cfg.nseq == 1 and drafts:
         out["chain"] = chain_measure(inp, cfg, drafts, args.chain_rounds)
     if args.probe_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

@@ -178,6 +178,32 @@ glance_status glance_verify_head(const void* h, const void* w_head, int32_t dtyp
 
 size_t glance_verify_head_ws(int32_t R, int32_t V, int32_t d_model, int32_t dtype);
 
+/* glance_verify_head_sampled: the same head, and one token drawn per row from the
+ * target's own distribution at temperature T (paper §5.4, Table 3, and App. D:
+ * under sampling the committed tokens are the target's draws, so the output
+ * distribution is the target's).  Reading taken: row i draws
+ *   y_i = argmax_v (z_iv / T + G_iv),  G = -ln(-ln U)   (Gumbel-max rule),
+ * with U_iv from Philox4x32-10 (Salmon et al., SC 2011) under key (seed low,
+ * seed high 32 bits), counter (v / 4, i, round_id low, round_id high), output
+ * word v % 4, and U = ((word >> 9) + 1/2) / 2^23 (exact in float32, so the
+ * noise is never infinite).  Every row has its own stream,
+ * so a row's draw does not depend on the path that reaches it; pass the draws
+ * to glance_accept_walk in place of argmax (and sample_gap in place of gap).
+ *
+ *   temperature  finite, > 0 (the scores use 1/T in float32)
+ *   seed, round_id  Philox key and the round's counter words
+ *   sample_tok   [R] int32: y_i (the smallest token id on exact ties)
+ *   sample_gap   [R] float: best minus second-best perturbed score of row i
+ * All other arguments, the limits and the workspace are those of
+ * glance_verify_head (whose outputs this call also writes).
+ */
+glance_status glance_verify_head_sampled(const void* h, const void* w_head, int32_t dtype,
+                                         int32_t R, int32_t d_model, int32_t V,
+                                         float temperature, uint64_t seed, uint64_t round_id,
+                                         int32_t* argmax, float* top1, float* gap,
+                                         float* entropy, int32_t* sample_tok, float* sample_gap,
+                                         float* logits, void* ws, size_t ws_bytes, void* stream);
+
 /* -------------------------------------------------------------------- step 5 --
  * glance_accept_walk: the greedy accept walk of every round.
  *

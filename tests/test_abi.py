@@ -90,6 +90,31 @@ def test_verify_head_rejects_bad_arguments(lib):
     assert _head(lib, ws_bytes=100) == -3
 
 
+def _head_sampled(lib, **kw):
+    a = dict(h=OK_PTR, w=OK_PTR, dtype=1, R=64, d=4096, V=151936, T=1.0, out=OK_PTR,
+             tok=OK_PTR, sgap=OK_PTR, ws=OK_PTR * 16, ws_bytes=1 << 40)
+    a.update(kw)
+    o = a["out"]
+    return lib.glance_verify_head_sampled(a["h"], a["w"], a["dtype"], a["R"], a["d"], a["V"],
+                                          a["T"], (1 << 63) + 5, (1 << 40) + 3, o, o, o, o,
+                                          a["tok"], a["sgap"], None, a["ws"], a["ws_bytes"], None)
+
+
+def test_verify_head_sampled_rejects_bad_arguments(lib):
+    assert _head_sampled(lib, T=0.0) == -1
+    assert _head_sampled(lib, T=-1.0) == -1
+    assert _head_sampled(lib, T=float("nan")) == -1
+    assert _head_sampled(lib, T=float("inf")) == -1
+    assert _head_sampled(lib, tok=None) == -1
+    assert _head_sampled(lib, sgap=None) == -1
+    assert _head_sampled(lib, tok=OK_PTR + 2) == -2
+    assert _head_sampled(lib, R=0) == -1
+    assert _head_sampled(lib, d=4000) == -4
+    assert _head_sampled(lib, ws_bytes=100) == -3
+    # the workspace holds the sampled partials as well
+    assert lib.glance_verify_head_ws(64, 151936, 4096, 1) >= 64 * 8 * 4
+
+
 def _attn(lib, **kw):
     a = dict(dtype=1, embed=OK_PTR, h_in=None, nseq=1, n_rows=64, d=4096, Hq=32, Hkv=8, D=128,
              max_prefix=1024, n_pos=2048, ws=OK_PTR * 16, ws_bytes=1 << 40, layer=OK_PTR)

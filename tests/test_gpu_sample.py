@@ -1,0 +1,128 @@
+"""Sampling at temperature T on the GPU against the oracle's draws: every verify
+row's drawn token equals the oracle's Gumbel-max draw from the same Philox
+stream over the oracle's own logits, on the rows whose perturbed top-2 gap is
+above 2 e / T (e: the largest difference between the GPU's and the oracle's
+logits of the round, at least 1e-3; the two best scores can each move by e / T),
+the walk follows the drawn tokens, and the greedy statistics of the sampled
+call equal those of the greedy call."""
+import numpy as np
+import pytest
+
+from oracle import model as mdl, round as orr, sample as sp, walk as wk
+from synth import gen_round, make_config
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _sampled_round(inp, T, seed, rnd):
+    from tree_verified_block_amd.round import DeviceRound
+    dev = DeviceRound(inp, want_logits=True, temperature=T, seed=seed)
+    dev.round_id = rnd
+    dev.set_round(0)
+    dev.run()
+    out = dev.fetch()
+    greedy = DeviceRound(inp, want_logits=False)
+    greedy.set_round(0)
+    greedy.run()
+    return out, greedy.fetch()
+
+
+@pytest.mark.parametrize("name,seed,T,key,rnd", [
+    ("tiny_widehead", 1000, 1.0, 7, 0),
+    ("tiny_widehead", 1001, 0.6, (1 << 63) + 12345, (1 << 33) + 9),
+    ("mini_bf16", 1, 1.0, 42, 3),
+    ("mini_bf16_ragged", 3, 0.8, 0xDEADBEEFCAFEF00D, 77),
+])
+def test_sampled_round_matches_oracle_draws(name, seed, T, key, rnd):
+    inp = gen_round(make_config(name), seed)
+    cfg = inp["cfg"]
+    gpu, ref = _sampled_round(inp, T, key, rnd)
+    # the sampled call leaves the greedy statistics as the greedy call does
+    assert np.array_equal(gpu["argmax"], ref["argmax"])
+    for k in ("top1", "gap", "entropy"):
+        np.testing.assert_allclose(gpu[k], ref[k], rtol=1e-6, atol=1e-6)
+    model = mdl.TargetModel(inp)
+    rd = inp["rounds"][0]
+    n_rows = cfg.N + 1
+    report = {"rows": 0, "rows_flagged": 0, "walk_exact": 0, "walk_flagged": 0}
+    for s in range(cfg.nseq):
+        root = int(rd["root"][s])
+        paths = parity.gpu_paths(gpu["parent"][s], gpu["token"][s], gpu["n_valid"][s])
+        ev = mdl.evaluate_paths(model, s, root, paths)
+        z = model.logits(ev["final"])
+        nv = len(paths)
+        rows = s * n_rows + np.arange(nv)
+        e = float(np.abs(gpu["logits"][rows].astype(np.float64) - z).max())
+        assert e <= parity.tol_for(cfg.dtype) * np.abs(z).max(), e
+        flag = 2 * max(e, parity.GAP) / T
+        otok, ogap = sp.sample_rows(z, T, key, rnd, rows=rows)
+        sure = ogap > flag
+        report["rows"] += nv
+        report["rows_flagged"] += int((~sure).sum())
+        g_tok = gpu["sample_tok"][rows]
+        assert np.array_equal(g_tok[sure], otok[sure]), (g_tok, otok, ogap)
+        assert np.all((g_tok >= 0) & (g_tok < cfg.V))
+        # the GPU's gap is that of its own perturbed scores
+        np.testing.assert_allclose(gpu["sample_gap"][rows][sure], ogap[sure],
+                                   atol=flag + 1e-5, rtol=1e-5)
+        # walk on the drawn tokens
+        a = int(gpu["n_accept"][s])
+        toks = gpu["out_tokens"][s]
+        prow = gpu["path_rows"][s]
+        for k in range(a + 1):
+            assert toks[k] == gpu["sample_tok"][s * n_rows + prow[k]]
+            if k:
+                assert gpu["parent"][s][prow[k]] == prow[k - 1]
+                assert gpu["token"][s][prow[k]] == toks[k - 1]
+        oa, otoks, orows = wk.walk(gpu["parent"][s], gpu["token"][s], nv, otok, cfg.L)
+        if np.any(ogap[orows] <= flag):
+            report["walk_flagged"] += 1
+            continue
+        report["walk_exact"] += 1
+        assert a == oa and list(toks[:a + 1]) == otoks and list(prow[:a + 1]) == orows
+    print(f"[sample] {name} seed={seed} T={T}: {report} logit err {e:.2e}", flush=True)
+    assert report["rows"] > report["rows_flagged"]
+
+
+def test_sampled_draws_change_with_round_and_seed():
+    """Distinct (seed, round) give distinct streams; the same pair repeats."""
+    inp = gen_round(make_config("mini_bf16"), 2)
+    a, _ = _sampled_round(inp, 1.0, 5, 0)
+    b, _ = _sampled_round(inp, 1.0, 5, 0)
+    c, _ = _sampled_round(inp, 1.0, 5, 1)
+    d, _ = _sampled_round(inp, 1.0, 6, 0)
+    assert np.array_equal(a["sample_tok"], b["sample_tok"])
+    assert not np.array_equal(a["sample_tok"], c["sample_tok"])
+    assert not np.array_equal(a["sample_tok"], d["sample_tok"])
+
+
+def test_sampled_draws_follow_softmax_on_the_device():
+    """Device draws of one row over many rounds against softmax(z / T) of the
+    device's own logits (chi-square over the likeliest tokens, the rest pooled)."""
+    from scipy import stats
+    from tree_verified_block_amd.round import DeviceRound
+    inp = gen_round(make_config("tiny_widehead"), 1002)
+    T = 1.5
+    dev = DeviceRound(inp, want_logits=True, temperature=T, seed=99)
+    dev.set_round(0)
+    dev.step_tree()
+    dev.step_attn()
+    n = 4000
+    draws = np.empty((n, dev.R), dtype=np.int64)
+    for r in range(n):
+        dev.round_id = r
+        dev.step_head()
+        draws[r] = dev.sample_tok.cpu().numpy()
+    z = dev.logits.cpu().numpy().astype(np.float64)
+    for row in (0, dev.R // 2):
+        p = np.exp((z[row] - z[row].max()) / T)
+        p /= p.sum()
+        top = np.argsort(-p)[:12]
+        top = top[p[top] * n >= 20]
+        obs = np.array([np.sum(draws[:, row] == t) for t in top] + [0])
+        obs[-1] = n - obs[:-1].sum()
+        exp_ = np.concatenate([p[top], [1 - p[top].sum()]]) * n
+        keep = exp_ > 0
+        _, pval = stats.chisquare(obs[keep], exp_[keep] * obs[keep].sum() / exp_[keep].sum())
+        assert pval > 1e-4, (row, obs, exp_, pval)

@@ -23,6 +23,7 @@ _I = ctypes.c_int32
 _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
 _F = ctypes.c_float
+_U64 = ctypes.c_uint64
 
 
 class GlanceAttnLayer(ctypes.Structure):
@@ -39,6 +40,8 @@ SIGNATURES = {
     "glance_tree_attn_ws": (_SZ, [_I, _I, _I64, _I, _I, _I, _I]),
     "glance_verify_head": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "glance_verify_head_ws": (_SZ, [_I, _I, _I, _I]),
+    "glance_verify_head_sampled": (_I, [_P, _P, _I, _I, _I, _I, _F, _U64, _U64, _P, _P, _P, _P,
+                                        _P, _P, _P, _P, _SZ, _P]),
     "glance_accept_walk": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P]),
     "glance_commit_kv": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _I64, _P]),
     "glance_advance_round": (_I, [_P, _P, _I, _P, _P, _P]),

@@ -97,6 +97,17 @@ def glance_verify_head(h, w_head, argmax, top1, gap, entropy, ws, logits=None, s
               ws.numel(), _stream(stream))
 
 
+def glance_verify_head_sampled(h, w_head, temperature, seed, round_id, argmax, top1, gap,
+                               entropy, sample_tok, sample_gap, ws, logits=None, stream=None):
+    """The head with one token per row drawn from softmax(z / temperature)."""
+    R, d_model = h.shape
+    V = w_head.shape[0]
+    _lib.call("glance_verify_head_sampled", _ptr(h), _ptr(w_head), dtype_code(w_head), R,
+              d_model, V, float(temperature), int(seed), int(round_id), _ptr(argmax), _ptr(top1),
+              _ptr(gap), _ptr(entropy), _ptr(sample_tok), _ptr(sample_gap), _ptr(logits),
+              _ptr(ws), ws.numel(), _stream(stream))
+
+
 # ---------------------------------------------------------------------- step 5
 def glance_accept_walk(parent, token, n_valid, argmax, gap, nseq, n_rows, L, gap_flag,
                        n_accept, out_tokens, path_rows, flagged, stream=None):

@@ -89,6 +89,51 @@ __device__ __forceinline__ HeadPart head_elem(float z, int n) {
   return p;
 }
 
+// Philox4x32-10 (Salmon et al., SC 2011): round (c0, c1, c2, c3) ->
+// (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)); the key
+// grows by the Weyl increments before every round but the first.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+  }
+  return c;
+}
+
+// Gumbel noise -ln(-ln U) from a Philox word: U = (top 23 bits + 1/2) / 2^23.
+// Its numerator has at most 24 bits, so U is exact in float32 and never 0 or 1;
+// a finer grid would round near 1, where the winning draws' 1 - U lives.
+__device__ __forceinline__ float gumbel(uint32_t x) {
+  const float u = (static_cast<float>(x >> 9) + 0.5f) * (1.0f / 8388608.0f);
+  return -logf(-logf(u));
+}
+
+// A partial draw: the best perturbed score, its token (smallest on ties) and the
+// best score of any other token.
+struct Draw {
+  float m;
+  int tok;
+  float m2;
+};
+__device__ __forceinline__ Draw draw_empty() { return Draw{-INFINITY, 0x7FFFFFFF, -INFINITY}; }
+__device__ __forceinline__ Draw draw_combine(Draw a, Draw b) {
+  if (b.m > a.m || (b.m == a.m && b.tok < a.tok)) {
+    const Draw t = a;
+    a = b;
+    b = t;
+  }
+  return Draw{a.m, a.tok, fmaxf(a.m2, b.m)};
+}
+__device__ __forceinline__ Draw shfl_draw(const Draw& d, int src) {
+  return Draw{__shfl(d.m, src, kWave), __shfl(d.tok, src, kWave), __shfl(d.m2, src, kWave)};
+}
+
 __device__ __forceinline__ HeadPart shfl_part(const HeadPart& p, int src) {
   HeadPart r;
   r.m = __shfl(p.m, src, kWave);
@@ -210,7 +255,7 @@ __device__ __forceinline__ void head_row_stats(const f32x4 (&acc)[B][4], const i
 // loaded into a second register slot while chunk c is computed.
 __device__ __forceinline__ int swz(int row, int unit) { return row * kKc + 8 * (unit ^ (row & 7)); }
 
-template <int B, int SB>
+template <int B, int SB, bool SAMPLE>
 __global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int NB, int NG,
                                                                  int nWG, int nMT) {
   constexpr int XST = kTileM * kKc;  // one activation stage (elements)
@@ -348,6 +393,47 @@ __global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int
     hp[mb] = head_combine(hp[mb], shfl_part(hp[mb], l ^ 16));
     hp[mb] = head_combine(hp[mb], shfl_part(hp[mb], l ^ 32));
     if (lg == 0) hred[w][mb * 16 + lr] = hp[mb];
+  }
+  if constexpr (SAMPLE) {
+    // the draw of every activation row from softmax(z / T): Gumbel-max over this
+    // lane's tokens (one Philox call gives the noise of 4 consecutive tokens),
+    // then over lanes and waves as for the statistics
+    __shared__ Draw dred[4][kTileM];
+    Draw dp[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      dp[mb] = draw_empty();
+      const uint32_t row = static_cast<uint32_t>(m0 + mb * 16 + lr);
+#pragma unroll
+      for (int t = 0; t < B; ++t) {
+        const uint4 x = philox4x32_10(
+            make_uint4(static_cast<uint32_t>(blk[t] * 4 + lg), row, a.rnd_lo, a.rnd_hi), a.seed_lo,
+            a.seed_hi);
+        const uint32_t xs4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int n = blk[t] * 16 + 4 * lg + v;
+          const float sc = (bval[t] & (n < a.N)) ? fmaf(acc[t][mb][v], a.inv_temp, gumbel(xs4[v])) : -INFINITY;
+          const bool gt = sc > dp[mb].m;
+          dp[mb].m2 = gt ? dp[mb].m : fmaxf(dp[mb].m2, sc);
+          dp[mb].tok = gt ? n : dp[mb].tok;
+          dp[mb].m = fmaxf(dp[mb].m, sc);
+        }
+      }
+      dp[mb] = draw_combine(dp[mb], shfl_draw(dp[mb], l ^ 16));
+      dp[mb] = draw_combine(dp[mb], shfl_draw(dp[mb], l ^ 32));
+      if (lg == 0) dred[w][mb * 16 + lr] = dp[mb];
+    }
+    __syncthreads();
+    if (tid < kTileM && m0 + tid < a.M) {
+      Draw d = dred[0][tid];
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww) d = draw_combine(d, dred[ww][tid]);
+      float* o = a.spart + (static_cast<size_t>(m0 + tid) * nWG + wg) * 3;
+      o[0] = d.m;
+      o[1] = __int_as_float(d.tok);
+      o[2] = d.m2;
+    }
   }
   __syncthreads();
   if (tid < kTileM) {
@@ -581,10 +667,13 @@ __global__ __launch_bounds__(256) void head_merge_kernel(const float* __restrict
                                                          int32_t* __restrict__ argmax,
                                                          float* __restrict__ top1,
                                                          float* __restrict__ gap,
-                                                         float* __restrict__ entropy) {
+                                                         float* __restrict__ entropy,
+                                                         HeadDraw dr) {
   __shared__ HeadPart red[256];
+  __shared__ Draw dred[256];
   const int r = blockIdx.x, tid = threadIdx.x;
   HeadPart p = head_empty();
+  Draw d = draw_empty();
   for (int t = tid; t < nNT; t += 256) {
     const float* q = part + (static_cast<size_t>(r) * nNT + t) * 5;
     HeadPart e;
@@ -594,11 +683,19 @@ __global__ __launch_bounds__(256) void head_merge_kernel(const float* __restrict
     e.s = q[3];
     e.t = q[4];
     p = head_combine(p, e);
+    if (dr.tok) {
+      const float* u = dr.spart + (static_cast<size_t>(r) * nNT + t) * 3;
+      d = draw_combine(d, Draw{u[0], __float_as_int(u[1]), u[2]});
+    }
   }
   red[tid] = p;
+  dred[tid] = d;
   __syncthreads();
   for (int st = 128; st > 0; st >>= 1) {
-    if (tid < st) red[tid] = head_combine(red[tid], red[tid + st]);
+    if (tid < st) {
+      red[tid] = head_combine(red[tid], red[tid + st]);
+      dred[tid] = draw_combine(dred[tid], dred[tid + st]);
+    }
     __syncthreads();
   }
   if (tid == 0) {
@@ -607,6 +704,10 @@ __global__ __launch_bounds__(256) void head_merge_kernel(const float* __restrict
     top1[r] = f.m;
     gap[r] = f.m - f.m2;
     entropy[r] = logf(f.s) - f.t / f.s;
+    if (dr.tok) {
+      dr.tok[r] = dred[0].tok;
+      dr.gap[r] = dred[0].m - dred[0].m2;
+    }
   }
 }
 
@@ -647,16 +748,31 @@ __global__ __launch_bounds__(256) void head_rowstats_f32_kernel(const float* __r
                                                                 int V, int32_t* __restrict__ argmax,
                                                                 float* __restrict__ top1,
                                                                 float* __restrict__ gap,
-                                                                float* __restrict__ entropy) {
+                                                                float* __restrict__ entropy,
+                                                                HeadDraw dr) {
   __shared__ HeadPart red[256];
+  __shared__ Draw dred[256];
   const int r = blockIdx.x, tid = threadIdx.x;
   const float* z = logits + static_cast<size_t>(r) * V;
   HeadPart p = head_empty();
-  for (int n = tid; n < V; n += 256) p = head_combine(p, head_elem(z[n], n));
+  Draw d = draw_empty();
+  for (int n = tid; n < V; n += 256) {
+    p = head_combine(p, head_elem(z[n], n));
+    if (dr.tok) {
+      const uint4 x = philox4x32_10(make_uint4(static_cast<uint32_t>(n >> 2), static_cast<uint32_t>(r),
+                                               dr.rnd_lo, dr.rnd_hi), dr.seed_lo, dr.seed_hi);
+      const uint32_t w = (n & 3) == 0 ? x.x : (n & 3) == 1 ? x.y : (n & 3) == 2 ? x.z : x.w;
+      d = draw_combine(d, Draw{fmaf(z[n], dr.inv_temp, gumbel(w)), n, -INFINITY});
+    }
+  }
   red[tid] = p;
+  dred[tid] = d;
   __syncthreads();
   for (int st = 128; st > 0; st >>= 1) {
-    if (tid < st) red[tid] = head_combine(red[tid], red[tid + st]);
+    if (tid < st) {
+      red[tid] = head_combine(red[tid], red[tid + st]);
+      dred[tid] = draw_combine(dred[tid], dred[tid + st]);
+    }
     __syncthreads();
   }
   if (tid == 0) {
@@ -665,6 +781,10 @@ __global__ __launch_bounds__(256) void head_rowstats_f32_kernel(const float* __r
     top1[r] = f.m;
     gap[r] = f.m - f.m2;
     entropy[r] = logf(f.s) - f.t / f.s;
+    if (dr.tok) {
+      dr.tok[r] = dred[0].tok;
+      dr.gap[r] = dred[0].m - dred[0].m2;
+    }
   }
 }
 
@@ -725,7 +845,10 @@ glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   if (a.epi == EPI_HEAD) {
     const HeadGrid g = head_grid(a.N);
     const int grid = ((g.nWG + 7) / 8) * 8 * nMT;
-    head_bf16_kernel<kHeadB, 2><<<grid, kGThreads, 0, st>>>(a, g.NB, g.NG, g.nWG, nMT);
+    if (a.spart)
+      head_bf16_kernel<kHeadB, 2, true><<<grid, kGThreads, 0, st>>>(a, g.NB, g.NG, g.nWG, nMT);
+    else
+      head_bf16_kernel<kHeadB, 2, false><<<grid, kGThreads, 0, st>>>(a, g.NB, g.NG, g.nWG, nMT);
   } else {
     const int NB = proj_blocks(a);
     const int NGr = (NB + 3) / 4;
@@ -762,16 +885,17 @@ glance_status launch_gemm_f32(const GemmArgs& a, hipStream_t st) {
 }
 
 glance_status launch_head_merge(const float* part, int n_tiles, int R, int32_t* argmax,
-                                float* top1, float* gap, float* entropy, hipStream_t st) {
-  head_merge_kernel<<<R, 256, 0, st>>>(part, n_tiles, argmax, top1, gap, entropy);
+                                float* top1, float* gap, float* entropy, const HeadDraw& dr,
+                                hipStream_t st) {
+  head_merge_kernel<<<R, 256, 0, st>>>(part, n_tiles, argmax, top1, gap, entropy, dr);
   GLANCE_LAUNCH_CHECK();
   return GLANCE_OK;
 }
 
 glance_status launch_head_rowstats_f32(const float* logits, int R, int V, int32_t* argmax,
                                        float* top1, float* gap, float* entropy,
-                                       hipStream_t st) {
-  head_rowstats_f32_kernel<<<R, 256, 0, st>>>(logits, V, argmax, top1, gap, entropy);
+                                       const HeadDraw& dr, hipStream_t st) {
+  head_rowstats_f32_kernel<<<R, 256, 0, st>>>(logits, V, argmax, top1, gap, entropy, dr);
   GLANCE_LAUNCH_CHECK();
   return GLANCE_OK;
 }

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -326,16 +327,16 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
 size_t glance_verify_head_ws(int32_t R, int32_t V, int32_t d_model, int32_t dtype) {
   (void)d_model;
   if (R < 1 || V < 2) return 0;
+  // bf16: 5 floats of statistics and 3 of the sampled draw per row and partial
   if (dtype == GLANCE_BF16)
-    return round256(static_cast<size_t>(R) * gemm_bf16_head_parts(V) * 5 * sizeof(float));
+    return round256(static_cast<size_t>(R) * gemm_bf16_head_parts(V) * 8 * sizeof(float));
   return round256(static_cast<size_t>(R) * V * sizeof(float));
 }
 
-glance_status glance_verify_head(const void* h, const void* w_head, int32_t dtype, int32_t R,
+static glance_status verify_head(const void* h, const void* w_head, int32_t dtype, int32_t R,
                                  int32_t d_model, int32_t V, int32_t* argmax, float* top1,
                                  float* gap, float* entropy, float* logits, void* ws,
-                                 size_t ws_bytes, void* stream) {
-  g_last_error.clear();
+                                 size_t ws_bytes, HeadDraw dr, hipStream_t hs) {
   REQUIRE(dtype == GLANCE_F32 || dtype == GLANCE_BF16, "dtype %d is not GLANCE_F32/BF16", dtype);
   REQUIRE(R >= 1, "R = %d < 1", R);
   REQUIRE(V >= 2, "V = %d < 2", V);
@@ -352,7 +353,6 @@ glance_status glance_verify_head(const void* h, const void* w_head, int32_t dtyp
   const size_t need = glance_verify_head_ws(R, V, d_model, dtype);
   glance_status st = check_ws(ws, ws_bytes, need);
   if (st != GLANCE_OK) return st;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
   GemmArgs g{};
   g.x = h;
   g.w.w[0] = w_head;
@@ -363,16 +363,58 @@ glance_status glance_verify_head(const void* h, const void* w_head, int32_t dtyp
   g.K = d_model;
   g.epi = EPI_HEAD;
   if (dtype == GLANCE_BF16) {
+    const int parts = gemm_bf16_head_parts(V);
     g.part = static_cast<float*>(ws);
     g.logits = logits;
+    if (dr.tok) {
+      g.spart = g.part + static_cast<size_t>(R) * parts * 5;
+      g.inv_temp = dr.inv_temp;
+      g.seed_lo = dr.seed_lo;
+      g.seed_hi = dr.seed_hi;
+      g.rnd_lo = dr.rnd_lo;
+      g.rnd_hi = dr.rnd_hi;
+      dr.spart = g.spart;
+    }
     st = launch_gemm_bf16(g, hs);
     if (st != GLANCE_OK) return st;
-    return launch_head_merge(g.part, gemm_bf16_head_parts(V), R, argmax, top1, gap, entropy, hs);
+    return launch_head_merge(g.part, parts, R, argmax, top1, gap, entropy, dr, hs);
   }
   g.logits = logits ? logits : static_cast<float*>(ws);
   st = launch_gemm_f32(g, hs);
   if (st != GLANCE_OK) return st;
-  return launch_head_rowstats_f32(g.logits, R, V, argmax, top1, gap, entropy, hs);
+  return launch_head_rowstats_f32(g.logits, R, V, argmax, top1, gap, entropy, dr, hs);
+}
+
+glance_status glance_verify_head(const void* h, const void* w_head, int32_t dtype, int32_t R,
+                                 int32_t d_model, int32_t V, int32_t* argmax, float* top1,
+                                 float* gap, float* entropy, float* logits, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  return verify_head(h, w_head, dtype, R, d_model, V, argmax, top1, gap, entropy, logits, ws,
+                     ws_bytes, HeadDraw{}, static_cast<hipStream_t>(stream));
+}
+
+glance_status glance_verify_head_sampled(const void* h, const void* w_head, int32_t dtype,
+                                         int32_t R, int32_t d_model, int32_t V,
+                                         float temperature, uint64_t seed, uint64_t round_id,
+                                         int32_t* argmax, float* top1, float* gap,
+                                         float* entropy, int32_t* sample_tok, float* sample_gap,
+                                         float* logits, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  REQUIRE(std::isfinite(temperature) && temperature > 0.f,
+          "temperature = %g is not a finite positive number", static_cast<double>(temperature));
+  REQUIRE_PTR(sample_tok);
+  REQUIRE_PTR(sample_gap);
+  HeadDraw dr;
+  dr.tok = sample_tok;
+  dr.gap = sample_gap;
+  dr.inv_temp = 1.f / temperature;
+  dr.seed_lo = static_cast<uint32_t>(seed);
+  dr.seed_hi = static_cast<uint32_t>(seed >> 32);
+  dr.rnd_lo = static_cast<uint32_t>(round_id);
+  dr.rnd_hi = static_cast<uint32_t>(round_id >> 32);
+  return verify_head(h, w_head, dtype, R, d_model, V, argmax, top1, gap, entropy, logits, ws,
+                     ws_bytes, dr, static_cast<hipStream_t>(stream));
 }
 
 // ------------------------------------------------------------------- step 5

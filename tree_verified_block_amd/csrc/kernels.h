@@ -45,6 +45,11 @@ struct GemmArgs {
   void* out_res;           // EPI_RESID: [M][N] in the storage dtype
   float* part;             // EPI_HEAD: [M][n_part] partial statistics (5 floats)
   float* logits;           // EPI_HEAD: optional [M][N]
+  // EPI_HEAD, sampling at temperature T: [M][n_part] partial draws (3 floats:
+  // best perturbed score, its token, second best), 1/T, Philox key and round
+  float* spart;
+  float inv_temp;
+  uint32_t seed_lo, seed_hi, rnd_lo, rnd_hi;
   // EPI_QKV (bf16, head_dim 128): W = [Wq; Wk; Wv]; q and k rotated at the row's
   // position, everything rounded to bf16.
   int Hq, Hkv;
@@ -72,12 +77,22 @@ int proj_ksplit(int K, int NB);
 size_t proj_part_floats(int M, int NB, int K);
 size_t proj_counters(int M, int NB);
 glance_status launch_gemm_f32(const GemmArgs& a, hipStream_t st);
+// Sampling outputs of the head: token drawn per row and the gap between its
+// perturbed score and the next one (null when not sampling).
+struct HeadDraw {
+  int32_t* tok = nullptr;
+  float* gap = nullptr;
+  const float* spart = nullptr;  // bf16 path: partial draws
+  float inv_temp = 1.f;
+  uint32_t seed_lo = 0, seed_hi = 0, rnd_lo = 0, rnd_hi = 0;
+};
 // Row statistics of the head from bf16 partials, or from full fp32 logits.
 glance_status launch_head_merge(const float* part, int n_tiles, int R, int32_t* argmax,
-                                float* top1, float* gap, float* entropy, hipStream_t st);
+                                float* top1, float* gap, float* entropy, const HeadDraw& dr,
+                                hipStream_t st);
 glance_status launch_head_rowstats_f32(const float* logits, int R, int V, int32_t* argmax,
                                        float* top1, float* gap, float* entropy,
-                                       hipStream_t st);
+                                       const HeadDraw& dr, hipStream_t st);
 
 // ------------------------------------------------------------------ attn.hip
 struct AttnArgs {

@@ -23,10 +23,15 @@ def to_device(x: np.ndarray, dtype: str, device) -> torch.Tensor:
 class DeviceRound:
     """``capacity`` (one sequence only): the caches get room for that many rows and
     every layer keeps its own tree-row K/V, so that ``commit()`` can append each
-    round's accepted path and chain rounds on the device."""
+    round's accepted path and chain rounds on the device.
+
+    ``temperature``: every verify row also draws a token from softmax(z / T)
+    (Philox key ``seed``, counter round ``round_id``) and the walk runs on the
+    draws instead of the argmax; ``commit()`` moves to the next round id."""
 
     def __init__(self, inp: dict, device="cuda", keep_layers: bool = False,
-                 want_logits: bool = False, capacity: int | None = None):
+                 want_logits: bool = False, capacity: int | None = None,
+                 temperature: float | None = None, seed: int = 0):
         cfg = inp["cfg"]
         self.cfg = cfg
         self.inp = inp
@@ -77,6 +82,12 @@ class DeviceRound:
         self.entropy = torch.empty(self.R, dtype=torch.float32, device=device)
         self.logits = (torch.empty((self.R, self.V), dtype=torch.float32, device=device)
                        if want_logits else None)
+        self.temperature = temperature
+        self.seed = int(seed)
+        self.round_id = 0
+        if temperature is not None:
+            self.sample_tok = torch.empty(self.R, dtype=torch.int32, device=device)
+            self.sample_gap = torch.empty(self.R, dtype=torch.float32, device=device)
         self.n_accept = torch.empty(self.nseq, dtype=torch.int32, device=device)
         self.out_tokens = torch.empty((self.nseq, self.L + 1), dtype=torch.int32, device=device)
         self.path_rows = torch.empty((self.nseq, self.L + 1), dtype=torch.int32, device=device)
@@ -128,12 +139,20 @@ class DeviceRound:
         return self.h[(self.cfg.n_layers - 1) % 2]
 
     def step_head(self, stream=None):
-        api.glance_verify_head(self.h_final, self.w_head, self.argmax, self.top1, self.gap,
-                               self.entropy, self.ws_head, logits=self.logits, stream=stream)
+        if self.temperature is None:
+            api.glance_verify_head(self.h_final, self.w_head, self.argmax, self.top1, self.gap,
+                                   self.entropy, self.ws_head, logits=self.logits, stream=stream)
+        else:
+            api.glance_verify_head_sampled(self.h_final, self.w_head, self.temperature, self.seed,
+                                           self.round_id, self.argmax, self.top1, self.gap,
+                                           self.entropy, self.sample_tok, self.sample_gap,
+                                           self.ws_head, logits=self.logits, stream=stream)
 
     def step_walk(self, stream=None, gap_flag=GAP_FLAG):
         t = self.tree
-        api.glance_accept_walk(t["parent"], t["token"], t["n_valid"], self.argmax, self.gap,
+        tok, gap = ((self.argmax, self.gap) if self.temperature is None
+                    else (self.sample_tok, self.sample_gap))
+        api.glance_accept_walk(t["parent"], t["token"], t["n_valid"], tok, gap,
                                self.nseq, self.n_rows, self.L, gap_flag, self.n_accept,
                                self.out_tokens, self.path_rows, self.flagged, stream)
 
@@ -158,6 +177,7 @@ class DeviceRound:
             api.glance_commit_kv(self.tree_ks[li], self.tree_vs[li], self.path_rows, self.n_accept,
                                  self.L, self.kv_offsets, lw["k_cache"], lw["v_cache"], stream)
         api.glance_advance_round(self.n_accept, self.out_tokens, self.kv_offsets, self.root, stream)
+        self.round_id += 1
 
     def fetch(self) -> dict:
         torch.cuda.synchronize()
@@ -170,6 +190,9 @@ class DeviceRound:
         out["h_final"] = self.h_final.float().cpu().numpy()
         if self.logits is not None:
             out["logits"] = self.logits.cpu().numpy()
+        if self.temperature is not None:
+            out["sample_tok"] = self.sample_tok.cpu().numpy()
+            out["sample_gap"] = self.sample_gap.cpu().numpy()
         if self.keep_layers:
             out["attn_out"] = [a.cpu().numpy() for a in self.attn_out]
             out["h_layers"] = [h.float().cpu().numpy() for h in self.h_layers]
