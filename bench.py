@@ -80,7 +80,7 @@ def cpu_baseline(inp, budget_s: float = 10.0) -> dict:
             "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
-def chain_measure(inp, cfg, drafts, K: int, warm: int = 5) -> dict:
+def chain_measure(inp, cfg, drafts, K: int, warm: int = 5, packed: bool = False) -> dict:
     """Chained rounds on the device: each round's verify path, then the commit of
     the accepted path into the cache and the advance of prefix and root (no host
     round trip).  The prefix grows by A + 1 per round; the synthetic drafts do
@@ -93,7 +93,7 @@ def chain_measure(inp, cfg, drafts, K: int, warm: int = 5) -> dict:
     cap = P0 + (K + warm + 1) * (cfg.L + 1)
     inp = dict(inp)  # rotary tables covering every position the chain reaches
     inp["rope_cos"], inp["rope_sin"] = rope_tables(cap + 1, cfg.D, cfg.rope_theta)
-    dev = DeviceRound(inp, device="cuda", capacity=cap)
+    dev = DeviceRound(inp, device="cuda", capacity=cap, packed_head=packed)
     dev.set_round(0)
     stream = torch.cuda.current_stream()
 
@@ -123,13 +123,14 @@ def chain_measure(inp, cfg, drafts, K: int, warm: int = 5) -> dict:
             "rounds": K}
 
 
-def sampled_measure(inp, cfg, drafts, K: int, T: float = 1.0, warm: int = 5) -> dict:
+def sampled_measure(inp, cfg, drafts, K: int, T: float = 1.0, warm: int = 5,
+                    packed: bool = False) -> dict:
     """Verify rounds that also draw one token per row at temperature T and walk
     on the draws (a new Philox round id per round); HIP events bracket the LM
     head of every fourth round."""
     import torch
     from tree_verified_block_amd.round import DeviceRound
-    dev = DeviceRound(inp, device="cuda", temperature=T, seed=1234)
+    dev = DeviceRound(inp, device="cuda", temperature=T, seed=1234, packed_head=packed)
     dev.set_round(0)
     stream = torch.cuda.current_stream()
 
@@ -172,6 +173,8 @@ def main():
                     help="chained rounds (verify + KV commit + advance) to time; 0 skips")
     ap.add_argument("--sampled-rounds", type=int, default=50,
                     help="verify rounds that sample at T = 1 to time; 0 skips")
+    ap.add_argument("--row-major-head", action="store_true",
+                    help="LM head over the row-major weights instead of the packed copy")
     ap.add_argument("--probe-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -188,7 +191,8 @@ def main():
     inp = gen_round(cfg, args.seed)
     print(f"[bench] generated {cfg.name} in {time.perf_counter() - t0:.1f} s", file=sys.stderr,
           flush=True)
-    dev = DeviceRound(inp, device="cuda")
+    packed = cfg.dtype == "bf16" and not args.row_major_head
+    dev = DeviceRound(inp, device="cuda", packed_head=packed)
     dev.set_round(0)
     drafts = [to_device(rd["draft_logits"], cfg.dtype, "cuda") for rd in inp["rounds"]
               if "draft_logits" in rd]
@@ -261,7 +265,8 @@ def main():
         if cfg.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.n_layers} tree-attention layer(s), d_model "
                    f"{cfg.d_model}, {cfg.Hq}q/{cfg.Hkv}kv heads x {cfg.D}, V {cfg.V}, L {cfg.L}, "
-                   f"N {cfg.N}, prefix {P}, nseq {cfg.nseq}", "seed": args.seed},
+                   f"N {cfg.N}, prefix {P}, nseq {cfg.nseq}", "seed": args.seed,
+                   "head_weights": "packed tile order" if packed else "row-major"},
         "round_hbm_frac": round(total_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
         "round_bytes": total_bytes,
         "per_kernel": per_kernel,
@@ -273,10 +278,10 @@ def main():
     del dev
     torch.cuda.empty_cache()
     if args.sampled_rounds > 0 and drafts:
-        out["sampled"] = sampled_measure(inp, cfg, drafts, args.sampled_rounds)
+        out["sampled"] = sampled_measure(inp, cfg, drafts, args.sampled_rounds, packed=packed)
         torch.cuda.empty_cache()
     if args.chain_rounds > 0 and cfg.nseq == 1 and drafts:
-        out["chain"] = chain_measure(inp, cfg, drafts, args.chain_rounds)
+        out["chain"] = chain_measure(inp, cfg, drafts, args.chain_rounds, packed=packed)
     if args.probe_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)

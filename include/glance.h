@@ -204,6 +204,35 @@ glance_status glance_verify_head_sampled(const void* h, const void* w_head, int3
                                          float* entropy, int32_t* sample_tok, float* sample_gap,
                                          float* logits, void* ws, size_t ws_bytes, void* stream);
 
+/* glance_head_pack / glance_verify_head_packed: the same LM head (bf16) over
+ * weights reordered once, at load time, into the head kernel's own tile order:
+ * for every 64-deep chunk of d_model, every wave of the head grid and each of
+ * its vocabulary blocks, the 16 x 64 bf16 tile laid out as the matrix-core
+ * operand (16 bytes per lane, lanes consecutive).  The kernel then streams the
+ * weights from HBM straight into the matrix cores in contiguous kilobytes, with
+ * no transposition through LDS.  The layout depends only on (V, d_model); its
+ * size is glance_head_pack_bytes(V, d_model) (0 if unsupported), a little above
+ * V * d_model * 2 (vocabulary rows padded with zeros to whole wave blocks).
+ *
+ * glance_head_pack: w_head [V][d_model] bf16 row-major -> w_packed (device,
+ * 16-byte aligned, caller-owned, that many bytes).  Limits: V >= 2,
+ * d_model % 256 == 0.
+ * glance_verify_head_packed: glance_verify_head's outputs, workspace and limits
+ * for dtype bf16 (identical results: same products, same accumulation order),
+ * from w_packed; with sample_tok and sample_gap not NULL also the draws of
+ * glance_verify_head_sampled (temperature, seed and round_id as there; all three
+ * ignored when both are NULL).
+ */
+size_t glance_head_pack_bytes(int32_t V, int32_t d_model);
+glance_status glance_head_pack(const void* w_head, int32_t V, int32_t d_model, void* w_packed,
+                               void* stream);
+glance_status glance_verify_head_packed(const void* h, const void* w_packed, int32_t R,
+                                        int32_t d_model, int32_t V, float temperature,
+                                        uint64_t seed, uint64_t round_id, int32_t* argmax,
+                                        float* top1, float* gap, float* entropy,
+                                        int32_t* sample_tok, float* sample_gap, float* logits,
+                                        void* ws, size_t ws_bytes, void* stream);
+
 /* -------------------------------------------------------------------- step 5 --
  * glance_accept_walk: the greedy accept walk of every round.
  *

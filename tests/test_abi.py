@@ -115,6 +115,33 @@ def test_verify_head_sampled_rejects_bad_arguments(lib):
     assert lib.glance_verify_head_ws(64, 151936, 4096, 1) >= 64 * 8 * 4
 
 
+def test_head_pack_rejects_bad_arguments(lib):
+    p = OK_PTR
+    assert lib.glance_head_pack_bytes(151936, 4096) >= 151936 * 4096 * 2
+    assert lib.glance_head_pack_bytes(151936, 4000) == 0
+    assert lib.glance_head_pack_bytes(1, 4096) == 0
+    assert lib.glance_head_pack(p, 1, 4096, p, None) == -1
+    assert lib.glance_head_pack(p, 1000, 4000, p, None) == -4
+    assert lib.glance_head_pack(None, 1000, 256, p, None) == -1
+    assert lib.glance_head_pack(p, 1000, 256, p + 8, None) == -2
+
+    def packed(**kw):
+        a = dict(h=p, w=p, R=64, d=4096, V=151936, T=1.0, tok=None, sgap=None, ws=p * 16,
+                 ws_bytes=1 << 40)
+        a.update(kw)
+        return lib.glance_verify_head_packed(a["h"], a["w"], a["R"], a["d"], a["V"], a["T"], 1, 2,
+                                             p, p, p, p, a["tok"], a["sgap"], None, a["ws"],
+                                             a["ws_bytes"], None)
+
+    assert packed(w=None) == -1
+    assert packed(w=p + 4) == -2
+    assert packed(R=0) == -1
+    assert packed(d=4000) == -4
+    assert packed(ws_bytes=100) == -3
+    assert packed(tok=p, sgap=p, T=0.0) == -1      # sampling needs T > 0
+    assert packed(tok=p) == -1                     # both draw outputs or neither
+
+
 def _attn(lib, **kw):
     a = dict(dtype=1, embed=OK_PTR, h_in=None, nseq=1, n_rows=64, d=4096, Hq=32, Hkv=8, D=128,
              max_prefix=1024, n_pos=2048, ws=OK_PTR * 16, ws_bytes=1 << 40, layer=OK_PTR)

@@ -1,0 +1,99 @@
+"""The LM head over packed weights: the packed bytes follow the documented tile
+order (rebuilt here with NumPy from the row-major weights), and the packed call
+returns exactly what the row-major call returns (same products, same
+accumulation order), greedy and sampled, on ragged vocabularies, several
+activation tiles and the 8B-shaped head."""
+import numpy as np
+import pytest
+import torch
+
+from tree_verified_block_amd import api
+
+pytestmark = pytest.mark.gpu
+
+WAVES, BLOCKS = 2048, 5  # the head grid's target wave count and blocks per wave
+
+
+def _grid(V):
+    NB = (V + 15) // 16
+    per = min(-(-NB // WAVES), BLOCKS)
+    NG = -(-NB // per)
+    return NB, NG, per
+
+
+def _pack_numpy(w: np.ndarray) -> np.ndarray:
+    """[V][d] uint16 -> [d/64][NG][per][2][64 lanes][8] uint16, zero past V."""
+    V, d = w.shape
+    _, NG, per = _grid(V)
+    out = np.zeros((d // 64, NG, per, 2, 64, 8), dtype=np.uint16)
+    l = np.arange(64)
+    for t in range(per):
+        for G in range(NG):
+            rows = (G + t * NG) * 16 + (l & 15)
+            ok = rows < V
+            for s in range(2):
+                cols = 32 * s + 8 * (l >> 4)
+                for c in range(d // 64):
+                    idx = c * 64 + cols[:, None] + np.arange(8)[None, :]
+                    out[c, G, t, s][ok] = w[rows[ok][:, None], idx[ok]]
+    return out
+
+
+def _bf16(shape, scale, gen):
+    return (torch.randn(shape, generator=gen, device="cuda") * scale).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("V,d", [(1000, 256), (4099, 512)])
+def test_pack_layout(V, d):
+    g = torch.Generator(device="cuda").manual_seed(V)
+    w = _bf16((V, d), 1.0, g)
+    packed = api.glance_head_pack(w)
+    torch.cuda.synchronize()
+    assert packed.numel() == api.head_pack_bytes(V, d)
+    want = _pack_numpy(w.cpu().view(torch.int16).numpy().view(np.uint16))
+    got = packed.cpu().numpy().view(np.uint16).reshape(want.shape)
+    assert np.array_equal(got, want)
+
+
+def _heads(V, d, R, seed, sample=None):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    w = _bf16((V, d), 0.05, g)
+    h = _bf16((R, d), 1.0, g)
+    packed = api.glance_head_pack(w)
+    outs = []
+    for use_packed in (False, True):
+        o = {k: torch.empty(R, dtype=torch.float32, device="cuda") for k in ("top1", "gap", "H", "sgap")}
+        o["am"] = torch.empty(R, dtype=torch.int32, device="cuda")
+        o["tok"] = torch.empty(R, dtype=torch.int32, device="cuda")
+        o["logits"] = torch.empty((R, V), dtype=torch.float32, device="cuda")
+        ws = api.workspace(api.verify_head_ws_bytes(R, V, d, 1), "cuda")
+        if use_packed:
+            kw = {}
+            if sample:
+                kw = dict(temperature=sample[0], seed=sample[1], round_id=sample[2],
+                          sample_tok=o["tok"], sample_gap=o["sgap"])
+            api.glance_verify_head_packed(h, packed, V, o["am"], o["top1"], o["gap"], o["H"], ws,
+                                          logits=o["logits"], **kw)
+        elif sample:
+            api.glance_verify_head_sampled(h, w, sample[0], sample[1], sample[2], o["am"],
+                                           o["top1"], o["gap"], o["H"], o["tok"], o["sgap"], ws,
+                                           logits=o["logits"])
+        else:
+            api.glance_verify_head(h, w, o["am"], o["top1"], o["gap"], o["H"], ws,
+                                   logits=o["logits"])
+        torch.cuda.synchronize()
+        outs.append({k: v.cpu().numpy() for k, v in o.items()})
+    return outs
+
+
+@pytest.mark.parametrize("V,d,R", [(1000, 256, 64), (4099, 512, 100), (151936, 4096, 64)])
+def test_packed_head_equals_row_major(V, d, R):
+    ref, got = _heads(V, d, R, seed=V + R)
+    for k in ("am", "top1", "gap", "H", "logits"):
+        assert np.array_equal(ref[k], got[k]), k
+
+
+def test_packed_head_sampled_equals_row_major():
+    ref, got = _heads(151936, 4096, 64, seed=5, sample=(0.8, (1 << 40) + 7, 123))
+    for k in ("am", "top1", "gap", "H", "tok", "sgap"):
+        assert np.array_equal(ref[k], got[k]), k

@@ -42,6 +42,10 @@ SIGNATURES = {
     "glance_verify_head_ws": (_SZ, [_I, _I, _I, _I]),
     "glance_verify_head_sampled": (_I, [_P, _P, _I, _I, _I, _I, _F, _U64, _U64, _P, _P, _P, _P,
                                         _P, _P, _P, _P, _SZ, _P]),
+    "glance_head_pack_bytes": (_SZ, [_I, _I]),
+    "glance_head_pack": (_I, [_P, _I, _I, _P, _P]),
+    "glance_verify_head_packed": (_I, [_P, _P, _I, _I, _I, _F, _U64, _U64, _P, _P, _P, _P, _P, _P,
+                                       _P, _P, _SZ, _P]),
     "glance_accept_walk": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P]),
     "glance_commit_kv": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _I64, _P]),
     "glance_advance_round": (_I, [_P, _P, _I, _P, _P, _P]),

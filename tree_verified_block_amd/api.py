@@ -108,6 +108,32 @@ def glance_verify_head_sampled(h, w_head, temperature, seed, round_id, argmax, t
               _ptr(ws), ws.numel(), _stream(stream))
 
 
+def head_pack_bytes(V: int, d_model: int) -> int:
+    return _lib.load().glance_head_pack_bytes(V, d_model)
+
+
+def glance_head_pack(w_head, stream=None):
+    """bf16 LM-head weights [V][d_model] -> the head kernel's packed tile order
+    (a new uint8 device tensor; done once, when the weights are loaded)."""
+    V, d_model = w_head.shape
+    n = head_pack_bytes(V, d_model)
+    if n == 0:
+        raise ValueError(f"no packed layout for V={V}, d_model={d_model}")
+    out = torch.empty(n, dtype=torch.uint8, device=w_head.device)
+    _lib.call("glance_head_pack", _ptr(w_head), V, d_model, _ptr(out), _stream(stream))
+    return out
+
+
+def glance_verify_head_packed(h, w_packed, V, argmax, top1, gap, entropy, ws, logits=None,
+                              temperature=1.0, seed=0, round_id=0, sample_tok=None,
+                              sample_gap=None, stream=None):
+    R, d_model = h.shape
+    _lib.call("glance_verify_head_packed", _ptr(h), _ptr(w_packed), R, d_model, V,
+              float(temperature), int(seed), int(round_id), _ptr(argmax), _ptr(top1), _ptr(gap),
+              _ptr(entropy), _ptr(sample_tok), _ptr(sample_gap), _ptr(logits), _ptr(ws),
+              ws.numel(), _stream(stream))
+
+
 # ---------------------------------------------------------------------- step 5
 def glance_accept_walk(parent, token, n_valid, argmax, gap, nseq, n_rows, L, gap_flag,
                        n_accept, out_tokens, path_rows, flagged, stream=None):

@@ -253,14 +253,21 @@ __device__ __forceinline__ void head_row_stats(const f32x4 (&acc)[B][4], const i
 // LDS rows are 128 bytes, unpadded, with the 16-byte unit XOR-swizzled by the
 // row's low 3 bits against bank conflicts.  The weights of chunk c + 1 are
 // loaded into a second register slot while chunk c is computed.
+//
+// PACKED: W was reordered once into the head's own tile order (head_pack_kernel):
+// for chunk c, wave G, its t-th block (t < per) and half s, 1 KB holding lane l's
+// 16 bytes of the MFMA operand (row l%16, k = 64 c + 32 s + 8 (l/16)) at l * 16.
+// The weights then go from HBM straight into MFMA operands: no LDS tile, every
+// load a contiguous kilobyte, and all waves of chunk c read one contiguous band.
+// The freed LDS deepens the activation ring (the waves meet less often).
 __device__ __forceinline__ int swz(int row, int unit) { return row * kKc + 8 * (unit ^ (row & 7)); }
 
-template <int B, int SB, bool SAMPLE>
+template <int B, int SB, bool SAMPLE, bool PACKED>
 __global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int NB, int NG,
-                                                                 int nWG, int nMT) {
+                                                                 int nWG, int nMT, int per) {
   constexpr int XST = kTileM * kKc;  // one activation stage (elements)
   __shared__ __attribute__((aligned(16))) uint16_t xs[2 * SB * XST];
-  __shared__ __attribute__((aligned(16))) uint16_t wtile[4 * B * 16 * kKc];
+  __shared__ __attribute__((aligned(16))) uint16_t wtile[PACKED ? 8 : 4 * B * 16 * kKc];
   __shared__ HeadPart hred[4][kTileM];
 
   const int bid = blockIdx.x;
@@ -272,20 +279,35 @@ __global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
   const int G = wg * 4 + w;
   const int nck = a.K / kKc;
-  uint16_t* wt = wtile + w * B * 16 * kKc;
+  uint16_t* wt = PACKED ? wtile : wtile + w * B * 16 * kKc;
 
   int blk[B];
   bool bval[B];
   const uint16_t* wp[B][2];
+  // packed: one base per lane (the wave's first tile), wave-uniform tile offsets;
+  // consecutive chunks of a tile are a band (NG per tiles) apart.  Waves and
+  // blocks past the grid re-read a valid tile (their results are never stored).
+  const uint4* wq0 = nullptr;
+  int toff[B];
+  const size_t cstride = static_cast<size_t>(NG) * per * 128;
+  if constexpr (PACKED) {
+    const int gc = G < NG ? G : NG - 1;
+    wq0 = static_cast<const uint4*>(a.w_packed) + static_cast<size_t>(gc) * per * 128 + l;
+  }
 #pragma unroll
   for (int t = 0; t < B; ++t) {
     blk[t] = G + t * NG;
     bval[t] = G < NG && blk[t] < NB;
+    toff[t] = (t < per ? t : per - 1) * 128;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      int row = bval[t] ? blk[t] * 16 + 8 * i + (l >> 3) : 0;
-      if (row > a.N - 1) row = a.N - 1;
-      wp[t][i] = w_row_ptr(a, row) + 8 * (l & 7);
+      if constexpr (PACKED) {
+        wp[t][i] = nullptr;
+      } else {
+        int row = bval[t] ? blk[t] * 16 + 8 * i + (l >> 3) : 0;
+        if (row > a.N - 1) row = a.N - 1;
+        wp[t][i] = w_row_ptr(a, row) + 8 * (l & 7);
+      }
     }
   }
   // activation pieces this thread stages: 64 rows x 8 units of 16 B per chunk.
@@ -312,7 +334,12 @@ __global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int
 #pragma unroll
     for (int t = 0; t < B; ++t)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) dst[t][i] = load_stream(wp[t][i] + c * kKc);
+      for (int i = 0; i < 2; ++i) {
+        if constexpr (PACKED)
+          dst[t][i] = load_stream(wq0 + (c * cstride + toff[t] + i * 64));
+        else
+          dst[t][i] = load_stream(wp[t][i] + c * kKc);
+      }
   };
   auto xload = [&](int c, uint4 (&dst)[2]) {
 #pragma unroll
@@ -332,6 +359,51 @@ __global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int
   for (int j = 0; j < SB; ++j) xstore(j, xb[j]);
   wload(0, wbuf[0]);
   __syncthreads();
+  if constexpr (PACKED) {
+    static_assert(SB == 2, "the packed head computes two chunks per stage half");
+  // packed: the same schedule written out with named registers (no lambdas or
+  // arrays for the activation stage, which the compiler would otherwise keep in
+  // scratch memory).  An empty asm statement with a memory clobber after each
+  // chunk's weight loads keeps the scheduler from sinking them to their use
+  // (the loaded registers feed the matrix cores directly).  The next stage
+  // half was last read before the previous barrier, so it is written between
+  // the two chunks and its registers live across one chunk only.
+#define GLANCE_PACKED_CHUNK(U)                                                              \
+  {                                                                                         \
+    const int cn = min(c0 + (U) + 1, nck - 1);                                              \
+    _Pragma("unroll") for (int t = 0; t < B; ++t)                                           \
+      _Pragma("unroll") for (int i = 0; i < 2; ++i)                                         \
+        wbuf[((U) + 1) & 1][t][i] = load_stream(wq0 + (cn * cstride + toff[t] + i * 64));   \
+    asm volatile("" ::: "memory");                                                          \
+    const uint16_t* xq = xs + (half * 2 + (U)) * XST;                                       \
+    _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                         \
+      bf16x8 bx[4];                                                                         \
+      _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) bx[mb] =                             \
+          *reinterpret_cast<const bf16x8*>(xq + swz(mb * 16 + lr, 4 * s + lg));             \
+      _Pragma("unroll") for (int t = 0; t < B; ++t) {                                       \
+        const bf16x8 av = __builtin_bit_cast(bf16x8, wbuf[(U) & 1][t][s]);                  \
+        _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) acc[t][mb] =                       \
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bx[mb], acc[t][mb], 0, 0, 0);       \
+      }                                                                                     \
+    }                                                                                       \
+  }
+  for (int c0 = 0; c0 < nck; c0 += 2) {
+    const int half = (c0 / 2) & 1;
+    const int ca = min(c0 + 2, nck - 1), cb = min(c0 + 3, nck - 1);
+    const uint4 xa0 = *reinterpret_cast<const uint4*>(xr[0] + ca * kKc);
+    const uint4 xa1 = *reinterpret_cast<const uint4*>(xr[1] + ca * kKc);
+    const uint4 xb0 = *reinterpret_cast<const uint4*>(xr[0] + cb * kKc);
+    const uint4 xb1 = *reinterpret_cast<const uint4*>(xr[1] + cb * kKc);
+    GLANCE_PACKED_CHUNK(0)
+    *reinterpret_cast<uint4*>(&xs[((half ^ 1) * 2) * XST + xlds[0]]) = xa0;
+    *reinterpret_cast<uint4*>(&xs[((half ^ 1) * 2) * XST + xlds[1]]) = xa1;
+    *reinterpret_cast<uint4*>(&xs[((half ^ 1) * 2 + 1) * XST + xlds[0]]) = xb0;
+    *reinterpret_cast<uint4*>(&xs[((half ^ 1) * 2 + 1) * XST + xlds[1]]) = xb1;
+    GLANCE_PACKED_CHUNK(1)
+    __syncthreads();
+  }
+#undef GLANCE_PACKED_CHUNK
+  } else {
   for (int c0 = 0; c0 < nck; c0 += SB) {
     const int half = (c0 / SB) & 1;  // stage half holding chunks c0 .. c0 + SB - 1
 #pragma unroll
@@ -365,6 +437,7 @@ __global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int
 #pragma unroll
     for (int j = 0; j < SB; ++j) xstore((half ^ 1) * SB + j, xb[j]);
     __syncthreads();
+  }
   }
 
   // acc[t][mb][v]: vocabulary row blk[t]*16 + 4 lg + v, activation row m0 + 16 mb + lr.
@@ -795,7 +868,7 @@ constexpr int kHeadB = 5;      // weight blocks per wave in the LM head
 constexpr int kHeadWaves = 2048;  // waves the LM head grid aims for (256 CUs x 8)
 
 struct HeadGrid {
-  int NB, NG, nWG;
+  int NB, NG, nWG, per;
 };
 HeadGrid head_grid(int N) {
   // the fewest waves (at most kHeadWaves while blocks per wave <= kHeadB) that
@@ -804,13 +877,51 @@ HeadGrid head_grid(int N) {
   g.NB = (N + 15) / 16;
   int per = (g.NB + kHeadWaves - 1) / kHeadWaves;
   if (per > kHeadB) per = kHeadB;
+  g.per = per;
   g.NG = (g.NB + per - 1) / per;
   g.nWG = (g.NG + 3) / 4;
   return g;
 }
+
+// Packed LM-head weights: [K/64 chunks][NG waves][per blocks][2 halves][64 lanes]
+// x 16 bytes; block t of wave G is vocabulary block G + t NG; lane l of half s
+// holds row 16 (G + t NG) + l%16, columns 64 c + 32 s + 8 (l/16) .. + 8; rows
+// past N are zero.
+__global__ __launch_bounds__(256) void head_pack_kernel(const uint16_t* __restrict__ w, int N,
+                                                        int K, int NG, int per, size_t n16,
+                                                        uint4* __restrict__ out) {
+  for (size_t o = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; o < n16;
+       o += static_cast<size_t>(gridDim.x) * 256) {
+    const int l = static_cast<int>(o & 63), s = static_cast<int>((o >> 6) & 1);
+    size_t rest = o >> 7;
+    const int t = static_cast<int>(rest % per);
+    rest /= per;
+    const int G = static_cast<int>(rest % NG);
+    const int c = static_cast<int>(rest / NG);
+    const int row = (G + t * NG) * 16 + (l & 15);
+    const int col = c * kKc + 32 * s + 8 * (l >> 4);
+    out[o] = row < N ? *reinterpret_cast<const uint4*>(w + static_cast<size_t>(row) * K + col)
+                     : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
 }  // namespace
 
 int gemm_bf16_head_parts(int N) { return head_grid(N).nWG; }
+
+size_t head_pack_bytes(int N, int K) {
+  const HeadGrid g = head_grid(N);
+  return static_cast<size_t>(K / kKc) * g.NG * g.per * 2 * 64 * 16;
+}
+
+glance_status launch_head_pack(const void* w, int N, int K, void* w_packed, hipStream_t st) {
+  const HeadGrid g = head_grid(N);
+  const size_t n16 = head_pack_bytes(N, K) / 16;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  head_pack_kernel<<<static_cast<unsigned>(blocks), 256, 0, st>>>(
+      static_cast<const uint16_t*>(w), N, K, g.NG, g.per, n16, static_cast<uint4*>(w_packed));
+  return GLANCE_OK;
+}
 
 int proj_ksplit(int K, int NB) {
   // about one work-group per CU: S ~ 256 / (number of 4-block groups), taken as a
@@ -845,10 +956,16 @@ glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   if (a.epi == EPI_HEAD) {
     const HeadGrid g = head_grid(a.N);
     const int grid = ((g.nWG + 7) / 8) * 8 * nMT;
-    if (a.spart)
-      head_bf16_kernel<kHeadB, 2, true><<<grid, kGThreads, 0, st>>>(a, g.NB, g.NG, g.nWG, nMT);
-    else
-      head_bf16_kernel<kHeadB, 2, false><<<grid, kGThreads, 0, st>>>(a, g.NB, g.NG, g.nWG, nMT);
+    if (a.w_packed) {
+      if (a.spart)
+        head_bf16_kernel<kHeadB, 2, true, true><<<grid, kGThreads, 0, st>>>(a, g.NB, g.NG, g.nWG, nMT, g.per);
+      else
+        head_bf16_kernel<kHeadB, 2, false, true><<<grid, kGThreads, 0, st>>>(a, g.NB, g.NG, g.nWG, nMT, g.per);
+    } else if (a.spart) {
+      head_bf16_kernel<kHeadB, 2, true, false><<<grid, kGThreads, 0, st>>>(a, g.NB, g.NG, g.nWG, nMT, g.per);
+    } else {
+      head_bf16_kernel<kHeadB, 2, false, false><<<grid, kGThreads, 0, st>>>(a, g.NB, g.NG, g.nWG, nMT, g.per);
+    }
   } else {
     const int NB = proj_blocks(a);
     const int NGr = (NB + 3) / 4;

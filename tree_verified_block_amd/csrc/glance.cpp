@@ -333,10 +333,11 @@ size_t glance_verify_head_ws(int32_t R, int32_t V, int32_t d_model, int32_t dtyp
   return round256(static_cast<size_t>(R) * V * sizeof(float));
 }
 
-static glance_status verify_head(const void* h, const void* w_head, int32_t dtype, int32_t R,
-                                 int32_t d_model, int32_t V, int32_t* argmax, float* top1,
-                                 float* gap, float* entropy, float* logits, void* ws,
-                                 size_t ws_bytes, HeadDraw dr, hipStream_t hs) {
+static glance_status verify_head(const void* h, const void* w_head, const void* w_packed,
+                                 int32_t dtype, int32_t R, int32_t d_model, int32_t V,
+                                 int32_t* argmax, float* top1, float* gap, float* entropy,
+                                 float* logits, void* ws, size_t ws_bytes, HeadDraw dr,
+                                 hipStream_t hs) {
   REQUIRE(dtype == GLANCE_F32 || dtype == GLANCE_BF16, "dtype %d is not GLANCE_F32/BF16", dtype);
   REQUIRE(R >= 1, "R = %d < 1", R);
   REQUIRE(V >= 2, "V = %d < 2", V);
@@ -344,7 +345,10 @@ static glance_status verify_head(const void* h, const void* w_head, int32_t dtyp
   if (dtype == GLANCE_BF16 && d_model % 256 != 0)
     return fail(GLANCE_ERR_UNSUPPORTED, "bf16 head needs d_model %% 256 == 0 (got %d)", d_model);
   REQUIRE_PTR(h);
-  REQUIRE_PTR(w_head);
+  if (w_packed)
+    REQUIRE_PTR(w_packed);
+  else
+    REQUIRE_PTR(w_head);
   REQUIRE_PTR(argmax);
   REQUIRE_PTR(top1);
   REQUIRE_PTR(gap);
@@ -364,6 +368,7 @@ static glance_status verify_head(const void* h, const void* w_head, int32_t dtyp
   g.epi = EPI_HEAD;
   if (dtype == GLANCE_BF16) {
     const int parts = gemm_bf16_head_parts(V);
+    g.w_packed = w_packed;
     g.part = static_cast<float*>(ws);
     g.logits = logits;
     if (dr.tok) {
@@ -390,8 +395,8 @@ glance_status glance_verify_head(const void* h, const void* w_head, int32_t dtyp
                                  float* gap, float* entropy, float* logits, void* ws,
                                  size_t ws_bytes, void* stream) {
   g_last_error.clear();
-  return verify_head(h, w_head, dtype, R, d_model, V, argmax, top1, gap, entropy, logits, ws,
-                     ws_bytes, HeadDraw{}, static_cast<hipStream_t>(stream));
+  return verify_head(h, w_head, nullptr, dtype, R, d_model, V, argmax, top1, gap, entropy, logits,
+                     ws, ws_bytes, HeadDraw{}, static_cast<hipStream_t>(stream));
 }
 
 glance_status glance_verify_head_sampled(const void* h, const void* w_head, int32_t dtype,
@@ -413,8 +418,50 @@ glance_status glance_verify_head_sampled(const void* h, const void* w_head, int3
   dr.seed_hi = static_cast<uint32_t>(seed >> 32);
   dr.rnd_lo = static_cast<uint32_t>(round_id);
   dr.rnd_hi = static_cast<uint32_t>(round_id >> 32);
-  return verify_head(h, w_head, dtype, R, d_model, V, argmax, top1, gap, entropy, logits, ws,
-                     ws_bytes, dr, static_cast<hipStream_t>(stream));
+  return verify_head(h, w_head, nullptr, dtype, R, d_model, V, argmax, top1, gap, entropy, logits,
+                     ws, ws_bytes, dr, static_cast<hipStream_t>(stream));
+}
+
+size_t glance_head_pack_bytes(int32_t V, int32_t d_model) {
+  if (V < 2 || d_model < 256 || d_model % 256 != 0) return 0;
+  return head_pack_bytes(V, d_model);
+}
+
+glance_status glance_head_pack(const void* w_head, int32_t V, int32_t d_model, void* w_packed,
+                               void* stream) {
+  g_last_error.clear();
+  REQUIRE(V >= 2, "V = %d < 2", V);
+  if (d_model < 256 || d_model % 256 != 0)
+    return fail(GLANCE_ERR_UNSUPPORTED, "packed head needs d_model %% 256 == 0 (got %d)", d_model);
+  REQUIRE_PTR(w_head);
+  REQUIRE_PTR(w_packed);
+  return launch_head_pack(w_head, V, d_model, w_packed, static_cast<hipStream_t>(stream));
+}
+
+glance_status glance_verify_head_packed(const void* h, const void* w_packed, int32_t R,
+                                        int32_t d_model, int32_t V, float temperature,
+                                        uint64_t seed, uint64_t round_id, int32_t* argmax,
+                                        float* top1, float* gap, float* entropy,
+                                        int32_t* sample_tok, float* sample_gap, float* logits,
+                                        void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  HeadDraw dr;
+  if (sample_tok || sample_gap) {
+    REQUIRE(std::isfinite(temperature) && temperature > 0.f,
+            "temperature = %g is not a finite positive number", static_cast<double>(temperature));
+    REQUIRE_PTR(sample_tok);
+    REQUIRE_PTR(sample_gap);
+    dr.tok = sample_tok;
+    dr.gap = sample_gap;
+    dr.inv_temp = 1.f / temperature;
+    dr.seed_lo = static_cast<uint32_t>(seed);
+    dr.seed_hi = static_cast<uint32_t>(seed >> 32);
+    dr.rnd_lo = static_cast<uint32_t>(round_id);
+    dr.rnd_hi = static_cast<uint32_t>(round_id >> 32);
+  }
+  REQUIRE(w_packed != nullptr, "w_packed is NULL");
+  return verify_head(h, nullptr, w_packed, GLANCE_BF16, R, d_model, V, argmax, top1, gap, entropy,
+                     logits, ws, ws_bytes, dr, static_cast<hipStream_t>(stream));
 }
 
 // ------------------------------------------------------------------- step 5

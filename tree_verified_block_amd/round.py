@@ -27,11 +27,14 @@ class DeviceRound:
 
     ``temperature``: every verify row also draws a token from softmax(z / T)
     (Philox key ``seed``, counter round ``round_id``) and the walk runs on the
-    draws instead of the argmax; ``commit()`` moves to the next round id."""
+    draws instead of the argmax; ``commit()`` moves to the next round id.
+
+    ``packed_head`` (bf16): the LM-head weights are packed once into the head
+    kernel's tile order and every round's head reads the packed copy."""
 
     def __init__(self, inp: dict, device="cuda", keep_layers: bool = False,
                  want_logits: bool = False, capacity: int | None = None,
-                 temperature: float | None = None, seed: int = 0):
+                 temperature: float | None = None, seed: int = 0, packed_head: bool = False):
         cfg = inp["cfg"]
         self.cfg = cfg
         self.inp = inp
@@ -44,6 +47,11 @@ class DeviceRound:
         d = cfg.d_model
         self.embed = to_device(inp["embed"], dt, device)
         self.w_head = to_device(inp["w_head"], dt, device)
+        self.w_packed = None
+        if packed_head:
+            if dt != "bf16":
+                raise ValueError("the packed head is bf16 only")
+            self.w_packed = api.glance_head_pack(self.w_head)
         self.layers = [{k: to_device(v, dt, device) for k, v in lw.items()} for lw in inp["layers"]]
         self.kv_offsets = torch.from_numpy(inp["kv_offsets"].astype(np.int64)).to(device)
         self.max_prefix = int(inp["prefix_len"].max())
@@ -139,7 +147,15 @@ class DeviceRound:
         return self.h[(self.cfg.n_layers - 1) % 2]
 
     def step_head(self, stream=None):
-        if self.temperature is None:
+        if self.w_packed is not None:
+            kw = {}
+            if self.temperature is not None:
+                kw = dict(temperature=self.temperature, seed=self.seed, round_id=self.round_id,
+                          sample_tok=self.sample_tok, sample_gap=self.sample_gap)
+            api.glance_verify_head_packed(self.h_final, self.w_packed, self.V, self.argmax,
+                                          self.top1, self.gap, self.entropy, self.ws_head,
+                                          logits=self.logits, stream=stream, **kw)
+        elif self.temperature is None:
             api.glance_verify_head(self.h_final, self.w_head, self.argmax, self.top1, self.gap,
                                    self.entropy, self.ws_head, logits=self.logits, stream=stream)
         else:
