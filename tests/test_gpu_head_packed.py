@@ -97,3 +97,28 @@ def test_packed_head_sampled_equals_row_major():
     ref, got = _heads(151936, 4096, 64, seed=5, sample=(0.8, (1 << 40) + 7, 123))
     for k in ("am", "top1", "gap", "H", "tok", "sgap"):
         assert np.array_equal(ref[k], got[k]), k
+
+
+@pytest.mark.parametrize("name,seed,kw", [
+    ("mini_bf16", 1, {}),
+    ("mini_bf16_ragged", 9, dict(draft="topology", n_layers=3, nseq=2, N=63, L=15)),
+    ("qwen8b_1layer", 2000, {}),
+])
+def test_packed_round_equals_row_major(name, seed, kw):
+    """A whole round with the packed head weights: every output equals the
+    row-major round's (tree, hidden rows, new cache entries, head statistics,
+    walk)."""
+    from synth import gen_round, make_config
+    from tree_verified_block_amd.round import DeviceRound
+    inp = gen_round(make_config(name, **kw), seed)
+    outs = []
+    for packed in (False, True):
+        dev = DeviceRound(inp, packed_head=packed)
+        dev.set_round(0)
+        dev.run()
+        outs.append(dev.fetch())
+        del dev
+        torch.cuda.empty_cache()
+    ref, got = outs
+    for k in ref:
+        assert np.array_equal(ref[k], got[k]), k
