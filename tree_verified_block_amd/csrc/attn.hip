@@ -233,8 +233,11 @@ __global__ __launch_bounds__(kHD) void attn_combine_kernel(AttnArgs a) {
   const int G = a.Hq / a.Hkv;
   const int Qn = a.n_rows * G;
   const int h = qh / G, q = r * G + qh % G;
-  float o = 0.f;
-  if (a.token[grow] >= 0) {
+  // the records are read whatever the row's token (in bounds for every row), so
+  // that their loads do not wait for the token's; padding rows give 0
+  const bool live = a.token[grow] >= 0;
+  float o;
+  {
     const float* rec = a.part + ((static_cast<size_t>(s) * a.Hkv + h) * (a.n_split + 1) *
                                      static_cast<size_t>(Qn) + q) * kRec;
     const size_t stride = static_cast<size_t>(Qn) * kRec;
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(kHD) void attn_combine_kernel(AttnArgs a) {
       }
       M = Mb;
     }
-    o = acc / Ls;
+    o = live ? acc / Ls : 0.f;
   }
   const size_t off = static_cast<size_t>(grow) * a.Hq * kHD + qh * kHD + dim;
   if (a.attn_out) a.attn_out[off] = o;

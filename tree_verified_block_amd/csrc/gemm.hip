@@ -742,8 +742,8 @@ __global__ __launch_bounds__(256) void head_merge_kernel(const float* __restrict
                                                          float* __restrict__ gap,
                                                          float* __restrict__ entropy,
                                                          HeadDraw dr) {
-  __shared__ HeadPart red[256];
-  __shared__ Draw dred[256];
+  __shared__ HeadPart red[4];
+  __shared__ Draw dred[4];
   const int r = blockIdx.x, tid = threadIdx.x;
   HeadPart p = head_empty();
   Draw d = draw_empty();
@@ -761,25 +761,33 @@ __global__ __launch_bounds__(256) void head_merge_kernel(const float* __restrict
       d = draw_combine(d, Draw{u[0], __float_as_int(u[1]), u[2]});
     }
   }
-  red[tid] = p;
-  dred[tid] = d;
-  __syncthreads();
-  for (int st = 128; st > 0; st >>= 1) {
-    if (tid < st) {
-      red[tid] = head_combine(red[tid], red[tid + st]);
-      dred[tid] = draw_combine(dred[tid], dred[tid + st]);
-    }
-    __syncthreads();
+  // within each wave by lane exchanges, then the four waves in order
+  const int lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    p = head_combine(p, shfl_part(p, lane ^ off));
+    if (dr.tok) d = draw_combine(d, shfl_draw(d, lane ^ off));
   }
+  if (lane == 0) {
+    red[wv] = p;
+    dred[wv] = d;
+  }
+  __syncthreads();
   if (tid == 0) {
-    const HeadPart f = red[0];
+    HeadPart f = red[0];
+    Draw g = dred[0];
+#pragma unroll
+    for (int k = 1; k < 4; ++k) {
+      f = head_combine(f, red[k]);
+      g = draw_combine(g, dred[k]);
+    }
     argmax[r] = f.am;
     top1[r] = f.m;
     gap[r] = f.m - f.m2;
     entropy[r] = logf(f.s) - f.t / f.s;
     if (dr.tok) {
-      dr.tok[r] = dred[0].tok;
-      dr.gap[r] = dred[0].m - dred[0].m2;
+      dr.tok[r] = g.tok;
+      dr.gap[r] = g.m - g.m2;
     }
   }
 }

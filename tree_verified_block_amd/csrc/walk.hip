@@ -25,12 +25,19 @@ __global__ __launch_bounds__(kWave) void accept_walk_kernel(
     int32_t* __restrict__ path_rows, int32_t* __restrict__ flagged) {
   const int s = blockIdx.x, lane = lane_id();
   const size_t rb = static_cast<size_t>(s) * n_rows;
+  // every load issued at once (rows below n_rows exist whatever n_valid is); the
+  // rows past n_valid are masked afterwards
+  const int li = lane < n_rows ? lane : 0;
   const int nv = n_valid[s];
+  const int ld_parent = parent[rb + li];
+  const int ld_token = token[rb + li];
+  const int ld_arg = argmax[rb + li];
+  const float ld_gap = gap[rb + li];
   const bool mine = lane < nv && lane < n_rows;
-  const int my_parent = mine ? parent[rb + lane] : -2;
-  const int my_token = mine ? token[rb + lane] : -2;
-  const int my_arg = mine ? argmax[rb + lane] : -1;
-  const float my_gap = mine ? gap[rb + lane] : INFINITY;
+  const int my_parent = mine ? ld_parent : -2;
+  const int my_token = mine ? ld_token : -2;
+  const int my_arg = mine ? ld_arg : -1;
+  const float my_gap = mine ? ld_gap : INFINITY;
   int r = 0, a = 0, flag = 0;
   for (;;) {
     const int y = __shfl(my_arg, r, kWave);
@@ -62,11 +69,15 @@ __global__ __launch_bounds__(kWave) void commit_kv_kernel(
     const int32_t* __restrict__ path_rows, const int32_t* __restrict__ n_accept,
     const int64_t* __restrict__ kv_offsets, int64_t cap, int row_vec, uint4* __restrict__ k_cache,
     uint4* __restrict__ v_cache) {
+  // the three index loads are independent (path_rows has L + 1 >= gridDim.x
+  // entries), so they are issued together
   const int k = blockIdx.x;
-  if (k > n_accept[0]) return;
+  const int a = n_accept[0];
   const int64_t dst = kv_offsets[1] + k;
+  const int prow = path_rows[k];
+  if (k > a) return;
   if (dst < 0 || dst >= cap) return;
-  const size_t src = static_cast<size_t>(path_rows[k]) * row_vec;
+  const size_t src = static_cast<size_t>(prow) * row_vec;
   for (int i = threadIdx.x; i < row_vec; i += kWave) {
     k_cache[static_cast<size_t>(dst) * row_vec + i] = tree_k[src + i];
     v_cache[static_cast<size_t>(dst) * row_vec + i] = tree_v[src + i];
