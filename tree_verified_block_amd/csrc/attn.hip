@@ -7,9 +7,9 @@
 // anc[i]), which is the causal sequence x o b o y_{1:d(i)}.
 //
 // bf16 path (head_dim 128, gfx950 MFMA v_mfma_f32_32x32x16_bf16).  Grid
-// (prefix splits + 1, Hkv x query blocks, rounds), 512 threads: the queries of
-// one KV head are its Hq/Hkv query heads times the round's rows (<= 256 per
-// work-group, 32 per wave).  Split c takes prefix keys [c*128, (c+1)*128) as
+// (prefix splits + 1, Hkv x query blocks, rounds), 256 threads: the queries of
+// one KV head are its Hq/Hkv query heads times the round's rows (<= 128 per
+// work-group, 32 per wave; smaller blocks spread a round over more CUs).  Split c takes prefix keys [c*128, (c+1)*128) as
 // one tile: the query, K and V loads are all issued before any is used; K is
 // staged in LDS as [key][dim], V transposed as [dim][key]; each wave forms
 // S^T = K Q^T (one query per lane, so the row max and sum stay inside a lane
@@ -28,9 +28,9 @@ namespace glance {
 
 namespace {
 
-constexpr int kAThreads = 512;
+constexpr int kAThreads = 256;
 constexpr int kQWave = 32;
-constexpr int kQBlock = 256;
+constexpr int kQBlock = 128;
 constexpr int kKT = 128;         // keys per work-group tile (one prefix split)
 constexpr int kHD = 128;         // head_dim of the bf16 path
 constexpr int kTPad = 136;       // row stride of the K, V^T and P tiles (bf16)
@@ -67,7 +67,6 @@ __global__ __launch_bounds__(kAThreads) void tree_attn_bf16_kernel(AttnArgs a) {
   const int r = qvalid ? q / G : 0;
   const int qh = h * G + (qvalid ? q % G : 0);
   const int grow = s * a.n_rows + r;
-  const bool qlive = qvalid && a.token[grow] >= 0;
   const uint64_t qanc = qvalid ? a.anc[grow] : 0ull;
 
   int kbeg, kend;
@@ -80,16 +79,16 @@ __global__ __launch_bounds__(kAThreads) void tree_attn_bf16_kernel(AttnArgs a) {
   }
   const int nk = kend - kbeg;  // <= kKT keys in this tile
 
-  // ---- every load of the tile issued up front: the query, then K and V
+  // ---- every load of the tile issued up front: the query, then K and V.  The
+  // query is loaded for padding rows too (their records are never combined:
+  // each query's scores and output stay in its own lanes), so that its loads
+  // do not wait for the row's token
   bf16x8 qf[8];
   {
     const uint16_t* xq = static_cast<const uint16_t*>(a.q) + static_cast<size_t>(grow) * a.Hq * kHD + qh * kHD;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (qlive) u = *reinterpret_cast<const uint4*>(xq + ks * 16 + 8 * g);
-      qf[ks] = __builtin_bit_cast(bf16x8, u);
-    }
+    for (int ks = 0; ks < 8; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xq + ks * 16 + 8 * g));
   }
   constexpr int kPass = kKT * (kHD / 8) / kAThreads;  // 16-byte pieces per thread
   uint4 kb_[kPass], vb_[kPass];
