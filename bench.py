@@ -161,6 +161,60 @@ def sampled_measure(inp, cfg, drafts, K: int, T: float = 1.0, warm: int = 5,
             "rounds": K}
 
 
+def shared_measure(K: int, seed: int = 4, budget_per_seq: int = 31, n_max: int = 63,
+                   oracle: bool = True) -> dict:
+    """Steps 1-2 of an 8-sequence batch (8B vocabulary, L 15, mixed draft
+    entropies) under one shared node budget (8 x 31 nodes, at most 63 per
+    sequence), timed with HIP events around each call; beside it the
+    fixed-width build of the same batch (31 nodes each) and the CPU oracle of
+    the shared build."""
+    import torch
+    from synth import gen_round, make_config
+    from tree_verified_block_amd import api
+    from tree_verified_block_amd.round import to_device
+    cfg = make_config("qwen8b_ragged8")
+    inp = gen_round(cfg, seed, with_model=False)
+    rd = inp["rounds"][0]
+    nseq, L, V = rd["draft_logits"].shape
+    draft = to_device(rd["draft_logits"], cfg.dtype, "cuda")
+    root = torch.tensor(rd["root"].astype(np.int32), device="cuda")
+    w = np.random.default_rng(seed).normal(0.0, 1.0, nseq).astype(np.float32)
+    wd = torch.tensor(w, device="cuda")
+    B = nseq * budget_per_seq
+    out = api.tree_outputs(nseq, n_max, "cuda")
+    out_fixed = api.tree_outputs(nseq, budget_per_seq, "cuda")
+    ws = api.workspace(api.build_tree_ws_bytes(nseq, L, V, n_max), "cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for e in ev:
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e3)
+
+    us = timed(lambda: api.glance_build_tree_shared(draft, root, wd, n_max, B, out, ws))
+    us_fixed = timed(lambda: api.glance_build_tree(draft, root, budget_per_seq, out_fixed, ws))
+    n = (out["n_valid"].cpu().numpy() - 1).tolist()
+    nbytes = nseq * L * V * 2 + nseq * (n_max + 1) * 28
+    res = {"workload": f"qwen8b_ragged8 drafts: {nseq} sequences x L {L} x V {V} bf16, budget {B} "
+                       f"nodes (at most {n_max} per sequence), weights N(0, 1)",
+           "us_per_call": round(us, 2), "calls_per_s": round(1e6 / us, 1), "nodes": n,
+           "algorithmic_bytes": nbytes, "hbm_frac": round(nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
+           "fixed_width_us": round(us_fixed, 2)}
+    if oracle:
+        from oracle import shared as sh
+        t0 = time.perf_counter()
+        sh.build_trees([rd["draft_logits"][s] for s in range(nseq)], cfg.dtype, rd["root"],
+                       w.astype(np.float64), B, n_max)
+        res["oracle_s"] = round(time.perf_counter() - t0, 2)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +227,8 @@ def main():
                     help="chained rounds (verify + KV commit + advance) to time; 0 skips")
     ap.add_argument("--sampled-rounds", type=int, default=50,
                     help="verify rounds that sample at T = 1 to time; 0 skips")
+    ap.add_argument("--shared-calls", type=int, default=50,
+                    help="shared-budget tree builds of an 8-sequence batch to time; 0 skips")
     ap.add_argument("--row-major-head", action="store_true",
                     help="LM head over the row-major weights instead of the packed copy")
     ap.add_argument("--probe-copy", action="store_true",
@@ -282,6 +338,8 @@ def main():
         torch.cuda.empty_cache()
     if args.chain_rounds > 0 and cfg.nseq == 1 and drafts:
         out["chain"] = chain_measure(inp, cfg, drafts, args.chain_rounds, packed=packed)
+    if args.shared_calls > 0:
+        out["shared_budget"] = shared_measure(args.shared_calls, oracle=not args.no_cpu_baseline)
     if args.probe_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)

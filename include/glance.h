@@ -98,6 +98,37 @@ glance_status glance_build_tree(const void* draft_logits, int32_t dtype,
 
 size_t glance_build_tree_ws(int32_t nseq, int32_t L, int32_t V, int32_t N);
 
+/* glance_build_tree_shared: steps 1-2 for a batch of rounds that share one
+ * budget of tree nodes (paper App. B.5, Proposition 4 and Eq. 5: under a
+ * shared verifier budget the best allocation takes the globally highest node
+ * masses, each round's masses indexed by its value V(H)).
+ *
+ * Defines: sequence s's prefixes carry the key log_weight[s] + sum_j log q_j(y_j)
+ * (log_weight[s] = ln V(H_s), supplied by the caller: the value law's fitted
+ * constants are data, not part of the method).  The batch takes the `budget`
+ * highest keys, equal keys going to the lower sequence and, within a
+ * sequence, following the order of glance_build_tree (score, depth, parent,
+ * token); every sequence keeps at most n_max nodes, and keys below
+ * min_log_value (the stopping rule, log units; -INFINITY disables it) or equal
+ * to -inf are never taken.  Within a sequence the keys fall along that order,
+ * so each sequence keeps its own top-n_s tree (prefix-closed), laid out as
+ * glance_build_tree lays out a tree of n_max + 1 rows.
+ *
+ *   log_weight  [nseq] float32, device; not NaN
+ *   n_max       0 <= n_max <= GLANCE_MAX_ROWS - 1 (rows per sequence n_max + 1)
+ *   budget      >= 0 nodes over the batch (sum_s n_s <= budget)
+ *   outputs     as glance_build_tree with N = n_max; n_valid[s] = n_s + 1
+ * Limits: 1 <= nseq <= GLANCE_MAX_SHARED; the rest as glance_build_tree, whose
+ * workspace size (glance_build_tree_ws) also serves this call.
+ */
+#define GLANCE_MAX_SHARED 16
+glance_status glance_build_tree_shared(const void* draft_logits, int32_t dtype,
+                                       const int32_t* root_token, const float* log_weight,
+                                       int32_t nseq, int32_t L, int32_t V, int32_t n_max,
+                                       int32_t budget, float min_log_value, int32_t* parent,
+                                       int32_t* depth, int32_t* token, uint64_t* anc, float* score,
+                                       int32_t* n_valid, void* ws, size_t ws_bytes, void* stream);
+
 /* -------------------------------------------------------------------- step 3 --
  * glance_tree_attn: one target layer over every verify row of nseq rounds, as a
  * single packed pass with ancestor-only masking.

@@ -76,14 +76,18 @@ def build_trees(drafts_stored, dtype: str, roots, log_weight, B: int, n_max: int
     n, gap, tmargin = allocate(logqs, log_weight, B, n_max, tau)
     trees = []
     for s, logq in enumerate(logqs):
-        top, scores, _ = tr.level_beam_top_n(logq, n_max)
+        top, scores, nxt = tr.level_beam_top_n(logq, n_max)
         sel = top[:int(n[s])]
         parent, depth, token, anc, n_valid, order = tr.canonical_layout(sel, int(roots[s]), n_max)
         score = np.full(n_max + 1, -np.inf)
         score[0] = 0.0
         for i, p in enumerate(order[1:], start=1):
             score[i] = scores[p]
+        # a round cut at its cap has its own boundary (its n_max-th node against
+        # the next one); a cut by the budget or the threshold is the batch's
+        own = (scores[top[-1]] - nxt) if (int(n[s]) == n_max and n_max > 0 and len(top) == n_max) \
+            else np.inf
         trees.append({"logq": logq, "top": sel, "parent": parent, "depth": depth,
                       "token": token, "anc": anc, "score": score, "n_valid": n_valid,
-                      "order": order})
+                      "order": order, "boundary_gap": own})
     return trees, n, gap, tmargin

@@ -73,6 +73,31 @@ def test_build_tree_rejects_bad_arguments(lib):
     assert b"needed" in lib.glance_last_error()
 
 
+def test_build_tree_shared_rejects_bad_arguments(lib):
+    p = OK_PTR
+
+    def call(**kw):
+        a = dict(logits=p, dtype=1, root=p, w=p, nseq=4, L=15, V=151936, n_max=63, budget=126,
+                 tau=float("-inf"), out=p, ws=p * 16, ws_bytes=1 << 40)
+        a.update(kw)
+        o = a["out"]
+        return lib.glance_build_tree_shared(a["logits"], a["dtype"], a["root"], a["w"], a["nseq"],
+                                            a["L"], a["V"], a["n_max"], a["budget"], a["tau"], o, o,
+                                            o, o, o, o, a["ws"], a["ws_bytes"], None)
+
+    assert call(nseq=0) == -1
+    assert call(nseq=17) == -1
+    assert call(n_max=64) == -1
+    assert call(n_max=-1) == -1
+    assert call(budget=-1) == -1
+    assert call(tau=float("nan")) == -1
+    assert call(w=None) == -1
+    assert call(w=p + 4) == -2
+    assert call(L=17) == -1
+    assert call(ws_bytes=64) == -3
+    assert call(dtype=0, V=200000) == -4
+
+
 def _head(lib, **kw):
     a = dict(h=OK_PTR, w=OK_PTR, dtype=1, R=64, d=4096, V=151936, out=OK_PTR, ws=OK_PTR * 16,
              ws_bytes=1 << 40)

@@ -34,6 +34,8 @@ class GlanceAttnLayer(ctypes.Structure):
 SIGNATURES = {
     "glance_build_tree": (_I, [_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "glance_build_tree_ws": (_SZ, [_I, _I, _I, _I]),
+    "glance_build_tree_shared": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P,
+                                      _P, _P, _SZ, _P]),
     "glance_tree_attn": (_I, [ctypes.POINTER(GlanceAttnLayer), _I, _P, _P, _P, _P, _P, _I64,
                               _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ,
                               _P]),

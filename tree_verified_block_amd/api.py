@@ -66,6 +66,18 @@ def glance_build_tree(draft_logits, root_token, N, out, ws, stream=None):
     return out
 
 
+def glance_build_tree_shared(draft_logits, root_token, log_weight, n_max, budget, out, ws,
+                             min_log_value=float("-inf"), stream=None):
+    """Trees of a batch of rounds under one shared node budget (out as from
+    tree_outputs(nseq, n_max))."""
+    nseq, L, V = draft_logits.shape
+    _lib.call("glance_build_tree_shared", _ptr(draft_logits), dtype_code(draft_logits),
+              _ptr(root_token), _ptr(log_weight), nseq, L, V, n_max, budget, float(min_log_value),
+              _ptr(out["parent"]), _ptr(out["depth"]), _ptr(out["token"]), _ptr(out["anc"]),
+              _ptr(out["score"]), _ptr(out["n_valid"]), _ptr(ws), ws.numel(), _stream(stream))
+    return out
+
+
 # ---------------------------------------------------------------------- step 3
 def tree_attn_ws_bytes(nseq, n_rows, max_prefix, d_model, Hq, Hkv, D) -> int:
     return _lib.load().glance_tree_attn_ws(nseq, n_rows, max_prefix, d_model, Hq, Hkv, D)

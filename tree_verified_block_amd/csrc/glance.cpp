@@ -161,6 +161,40 @@ glance_status glance_build_tree(const void* draft_logits, int32_t dtype,
                            anc, score, n_valid, ws, static_cast<hipStream_t>(stream));
 }
 
+glance_status glance_build_tree_shared(const void* draft_logits, int32_t dtype,
+                                       const int32_t* root_token, const float* log_weight,
+                                       int32_t nseq, int32_t L, int32_t V, int32_t n_max,
+                                       int32_t budget, float min_log_value, int32_t* parent,
+                                       int32_t* depth, int32_t* token, uint64_t* anc, float* score,
+                                       int32_t* n_valid, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  REQUIRE(dtype == GLANCE_F32 || dtype == GLANCE_BF16, "dtype %d is not GLANCE_F32/BF16", dtype);
+  REQUIRE(nseq >= 1 && nseq <= GLANCE_MAX_SHARED, "nseq = %d outside [1, %d]", nseq, GLANCE_MAX_SHARED);
+  REQUIRE(L >= 1 && L <= GLANCE_MAX_L, "L = %d outside [1, %d]", L, GLANCE_MAX_L);
+  REQUIRE(V >= 2, "V = %d < 2", V);
+  REQUIRE(n_max >= 0 && n_max <= GLANCE_MAX_ROWS - 1, "n_max = %d outside [0, %d]", n_max,
+          GLANCE_MAX_ROWS - 1);
+  REQUIRE(budget >= 0, "budget = %d < 0", budget);
+  REQUIRE(!std::isnan(min_log_value), "min_log_value is NaN");
+  if (V > (dtype == GLANCE_BF16 ? (1 << 18) : (1 << 17)))
+    return fail(GLANCE_ERR_UNSUPPORTED, "V = %d above 2^18 (bf16) / 2^17 (fp32)", V);
+  REQUIRE_PTR(draft_logits);
+  REQUIRE_PTR(root_token);
+  REQUIRE_PTR(log_weight);
+  REQUIRE_PTR(parent);
+  REQUIRE_PTR(depth);
+  REQUIRE_PTR(token);
+  REQUIRE_PTR(anc);
+  REQUIRE_PTR(score);
+  REQUIRE_PTR(n_valid);
+  const TreeWs w = tree_ws_layout(nseq, L, V);
+  glance_status st = check_ws(ws, ws_bytes, w.bytes);
+  if (st != GLANCE_OK) return st;
+  return launch_build_tree(draft_logits, dtype, root_token, nseq, L, V, n_max, parent, depth, token,
+                           anc, score, n_valid, ws, static_cast<hipStream_t>(stream), log_weight,
+                           budget, min_log_value);
+}
+
 // ------------------------------------------------------------------- step 3
 size_t glance_tree_attn_ws(int32_t nseq, int32_t n_rows, int64_t max_prefix, int32_t d_model,
                            int32_t Hq, int32_t Hkv, int32_t D) {

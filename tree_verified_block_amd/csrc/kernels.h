@@ -13,15 +13,21 @@ namespace glance {
 // ------------------------------------------------------------------ tree.hip
 struct TreeWs {
   // per-chunk (max, sum exp) [nseq*L][16], sorted key lists [nseq*L][16][64],
-  // merged rows (log q [nseq*L][64], token ids [nseq*L][64]) and the arrival
-  // counters of the rows [nseq*L] and sequences [nseq] (zero between calls)
-  size_t off_cstat = 0, off_clist = 0, off_lq = 0, off_tk = 0, off_row_cnt = 0, off_seq_cnt = 0, bytes = 0;
+  // merged rows (log q [nseq*L][64], token ids [nseq*L][64]), the arrival
+  // counters of the rows [nseq*L] and sequences [nseq] (zero between calls), and
+  // for a shared budget the published selections [nseq][64] and the batch counter
+  size_t off_cstat = 0, off_clist = 0, off_lq = 0, off_tk = 0, off_row_cnt = 0, off_seq_cnt = 0,
+         off_pops = 0, off_batch_cnt = 0, bytes = 0;
 };
+// Sequences of one shared-budget batch (the cut keeps their keys in LDS).
+constexpr int kMaxShared = GLANCE_MAX_SHARED;
 TreeWs tree_ws_layout(int nseq, int L, int V);
 glance_status launch_build_tree(const void* logits, int dtype, const int32_t* root, int nseq,
                                 int L, int V, int N, int32_t* parent, int32_t* depth,
                                 int32_t* token, uint64_t* anc, float* score,
-                                int32_t* n_valid, void* ws, hipStream_t st);
+                                int32_t* n_valid, void* ws, hipStream_t st,
+                                const float* log_weight = nullptr, int budget = 0,
+                                float tau = 0.f);
 
 // ------------------------------------------------------------------ gemm.hip
 // C = X W^T with X [M][K] (rows optionally gathered by token id) and W the

@@ -434,26 +434,31 @@ __device__ __noinline__ void merge_row(const unsigned long long* __restrict__ cs
   }
 }
 
-// Phase 3, one wavefront, the last row of sequence s to be merged: best-first
-// selection over the ranked lists in LDS and the breadth-first layout.
-__device__ __forceinline__ void select_tree(const float (*lq)[kLqRow], const int (*tk)[kSlots], int s,
-                                         const int32_t* __restrict__ root_token, int L, int N,
-                                         int32_t* __restrict__ parent, int32_t* __restrict__ depth_out,
-                                         int32_t* __restrict__ token_out, uint64_t* __restrict__ anc_out,
-                                         float* __restrict__ score_out, int32_t* __restrict__ n_valid_out) {
+// A selected node as its lane holds it after the selection (lane i = the i-th
+// selected node): depth, token id, parent lane and plug-in log score.
+struct PopState {
+  int depth;
+  int token;
+  int par;
+  float score;
+};
+
+// Phase 3a, one wavefront: best-first selection of up to N nodes over the ranked
+// lists in LDS.  Returns the number of selected nodes (wave-uniform); lane i
+// (1 <= i <= that number) holds the i-th selected node.
+__device__ __forceinline__ int select_pops(const float (*lq)[kLqRow], const int (*tk)[kSlots], int L,
+                                           int N, PopState& ps) {
   const int lane = lane_id();
-  // ---- best-first selection.  Lane 0 is the root, lane i the i-th selected
-  // node; each lane offers the best not-yet-selected child of its node (the
-  // next entry of the list of its depth).  Equal scores: smaller depth, then the
-  // earlier-selected parent (smaller lane); a lane offers one child at a time.
-  // Scores are sums of log q <= 0, so the order key of a score v is
-  // 0x7F800000 - bits(|v|): larger scores give larger keys, -inf (no offer)
-  // gives 0, and the key maps back to -|v| on the scalar unit.  Per iteration
-  // only the winner p and the new node i change, from scalar values; every lane
-  // re-reads the log q after its offered child, so the read is issued one
-  // iteration ahead of its use.
+  // Lane 0 is the root, lane i the i-th selected node; each lane offers the
+  // best not-yet-selected child of its node (the next entry of the list of its
+  // depth).  Equal scores: smaller depth, then the earlier-selected parent
+  // (smaller lane); a lane offers one child at a time.  Scores are sums of
+  // log q <= 0, so the order key of a score v is 0x7F800000 - bits(|v|): larger
+  // scores give larger keys, -inf (no offer) gives 0, and the key maps back to
+  // -|v| on the scalar unit.  Per iteration only the winner p and the new node
+  // i change, from scalar values; every lane re-reads the log q after its
+  // offered child, so the read is issued one iteration ahead of its use.
   // Lane state: st = depth << 16 | own rank << 8 | rank of the offered child.
-  const int R = N + 1;
   auto okey = [](float v) { return 0x7F800000u - (__float_as_uint(v) & 0x7FFFFFFFu); };
   const float fq = lane <= L ? lq[lane][0] : -INFINITY;  // first entry of each list
   int st = 0;
@@ -488,13 +493,31 @@ __device__ __forceinline__ void select_tree(const float (*lq)[kLqRow], const int
     if (++i > N) break;
     mh = wave_umax(c_hi);
   }
-
-  // ---- breadth-first layout: rows by (depth, parent row, token id), level by
-  // level; a node's row and ancestor mask come from its parent's lane
   const int n_depth = st >> 16;
   const bool member = lane >= 1 && lane <= n_pop;
-  const int n_token = member ? tk[n_depth - 1][(st >> 8) & 255] : -1;
-  const int par_addr = (n_par < 0 ? 0 : n_par) * 4;
+  ps.depth = n_depth;
+  ps.token = member ? tk[n_depth - 1][(st >> 8) & 255] : -1;
+  ps.par = n_par;
+  ps.score = n_score;
+  return n_pop;
+}
+
+// Phase 3b, one wavefront: the breadth-first layout of the first n_use selected
+// nodes (any prefix of the selection order is prefix-closed) into rows
+// [s][0, R): rows by (depth, parent row, token id), level by level; a node's row
+// and ancestor mask come from its parent's lane.  Rows past n_use + 1 are padding.
+__device__ __forceinline__ void layout_tree(const PopState& ps, int n_use, int s, int root, int L,
+                                          int R, int32_t* __restrict__ parent,
+                                          int32_t* __restrict__ depth_out,
+                                          int32_t* __restrict__ token_out,
+                                          uint64_t* __restrict__ anc_out,
+                                          float* __restrict__ score_out,
+                                          int32_t* __restrict__ n_valid_out) {
+  const int lane = lane_id();
+  const int n_depth = ps.depth;
+  const bool member = lane >= 1 && lane <= n_use;
+  const int n_token = member ? ps.token : -1;
+  const int par_addr = (ps.par < 0 ? 0 : ps.par) * 4;
   int row = 0, prow = -1;
   unsigned long long anc = 1ull;
   int base = 1;
@@ -524,19 +547,19 @@ __device__ __forceinline__ void select_tree(const float (*lq)[kLqRow], const int
   if (lane == 0) {
     parent[ob] = -1;
     depth_out[ob] = 0;
-    token_out[ob] = root_token[s];
+    token_out[ob] = root;
     anc_out[ob] = 1ull;
     score_out[ob] = 0.f;
-    n_valid_out[s] = n_pop + 1;
+    n_valid_out[s] = n_use + 1;
   }
   if (member) {
     parent[ob + row] = prow;
     depth_out[ob + row] = n_depth;
     token_out[ob + row] = n_token;
     anc_out[ob + row] = anc;
-    score_out[ob + row] = n_score;
+    score_out[ob + row] = ps.score;
   }
-  for (int r = n_pop + 1 + lane; r < R; r += kWave) {
+  for (int r = n_use + 1 + lane; r < R; r += kWave) {
     parent[ob + r] = -1;
     depth_out[ob + r] = 0;
     token_out[ob + r] = -1;
@@ -568,13 +591,92 @@ __device__ __forceinline__ bool arrive_last(unsigned* ctr, int total) {
 // builds the tree (phase 3).  Work-groups meet only through device-scope
 // atomics: published values are stored and loaded with device-coherent
 // accesses and are complete before the arrival that announces them.
+// Shared budget over the batch (null log_weight: every sequence takes N nodes).
+struct SharedArgs {
+  const float* log_weight;  // [nseq] ln V(H_s), the value of sequence s's node masses
+  int budget;               // nodes over the batch
+  float tau;                // keys below it are not taken
+  int nseq;
+  int4* pops;               // [nseq][64] published selections (depth, token, parent, score)
+  unsigned* batch_cnt;      // arrivals of the sequences (zero between calls)
+};
+
+// The batch's cut and the trees, by the work-group of the last sequence to finish
+// its selection (all threads).  Sequence s's i-th selected node has the key
+// log_weight[s] + its score; keys are non-increasing in selection order, so a
+// candidate's rank among the admissible keys (>= tau, > -inf) of the batch,
+// ordered by (key desc, sequence, selection order), is its own index plus, for
+// every other sequence, a binary search in that sequence's keys.  The nodes of
+// rank < budget are taken: a prefix of each sequence's selection order.
+__device__ void shared_cut_and_layout(const SharedArgs& sh, int L, int N,
+                                      const int32_t* __restrict__ root_token,
+                                      int32_t* __restrict__ parent, int32_t* __restrict__ depth_out,
+                                      int32_t* __restrict__ token_out, uint64_t* __restrict__ anc_out,
+                                      float* __restrict__ score_out, int32_t* __restrict__ n_valid_out) {
+  __shared__ float keys[kMaxShared][kWave];
+  __shared__ int adm[kMaxShared], nsel[kMaxShared];
+  const int tid = threadIdx.x, nseq = sh.nseq;
+  for (int idx = tid; idx < nseq * kWave; idx += kChunkThreads) {
+    const int s = idx / kWave, l = idx - s * kWave;
+    const uint64_t* src = reinterpret_cast<const uint64_t*>(sh.pops + idx);
+    const uint64_t lo = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (l == 0) {
+      adm[s] = static_cast<int>(static_cast<uint32_t>(lo));  // lane 0 carries the count
+    } else {
+      keys[s][l - 1] = sh.log_weight[s] + __uint_as_float(static_cast<uint32_t>(hi >> 32));
+    }
+  }
+  __syncthreads();
+  if (tid < nseq) {
+    int a = 0;
+    const int n = adm[tid];
+    while (a < n && keys[tid][a] >= sh.tau && keys[tid][a] > -INFINITY) ++a;
+    adm[tid] = a;
+    nsel[tid] = 0;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < nseq * kWave; idx += kChunkThreads) {
+    const int s = idx / kWave, i = idx - s * kWave;
+    if (i >= adm[s]) continue;
+    const float key = keys[s][i];
+    int rank = i;
+    for (int s2 = 0; s2 < nseq; ++s2) {
+      if (s2 == s) continue;
+      int lo = 0, hi = adm[s2];
+      while (lo < hi) {  // entries of s2 ordered before (s, i): a prefix of its keys
+        const int mid = (lo + hi) >> 1;
+        const bool before = s2 < s ? keys[s2][mid] >= key : keys[s2][mid] > key;
+        if (before) lo = mid + 1; else hi = mid;
+      }
+      rank += lo;
+    }
+    if (rank < sh.budget) atomicMax(&nsel[s], i + 1);
+  }
+  __syncthreads();
+  const int w = tid / kWave, lane = tid - w * kWave;
+  for (int s = w; s < nseq; s += kChunkThreads / kWave) {
+    const uint64_t* src = reinterpret_cast<const uint64_t*>(sh.pops + s * kWave + lane);
+    const uint64_t lo = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    PopState ps;
+    ps.depth = lane == 0 ? 0 : static_cast<int>(static_cast<uint32_t>(lo));
+    ps.token = static_cast<int>(static_cast<uint32_t>(lo >> 32));
+    ps.par = static_cast<int>(static_cast<uint32_t>(hi));
+    ps.score = __uint_as_float(static_cast<uint32_t>(hi >> 32));
+    layout_tree(ps, nsel[s], s, root_token[s], L, N + 1, parent, depth_out, token_out, anc_out,
+                score_out, n_valid_out);
+  }
+}
+
 template <typename T, int NV>
 __global__ __launch_bounds__(kChunkThreads) void tree_kernel(
     const T* __restrict__ logits, int L, int V, int N, int nch, unsigned long long* __restrict__ cstat,
     unsigned long long* __restrict__ clist, float* __restrict__ lq_g, int* __restrict__ tk_g,
     unsigned* __restrict__ row_cnt, unsigned* __restrict__ seq_cnt, const int32_t* __restrict__ root_token,
     int32_t* __restrict__ parent, int32_t* __restrict__ depth_out, int32_t* __restrict__ token_out,
-    uint64_t* __restrict__ anc_out, float* __restrict__ score_out, int32_t* __restrict__ n_valid_out) {
+    uint64_t* __restrict__ anc_out, float* __restrict__ score_out, int32_t* __restrict__ n_valid_out,
+    SharedArgs sh) {
   __shared__ __attribute__((aligned(16))) unsigned long long buf[kCap];
   const int j = blockIdx.y, sq = blockIdx.z;
   const int row = sq * L + j;
@@ -606,8 +708,32 @@ __global__ __launch_bounds__(kChunkThreads) void tree_kernel(
     lq[jj][r] = v;
   }
   __syncthreads();
+  if (sh.log_weight) {
+    // shared budget: publish this sequence's selection (up to N nodes); the last
+    // sequence to arrive cuts the batch and lays out every tree
+    if (threadIdx.x < kWave) {
+      PopState ps;
+      const int n_pop = select_pops(lq, tk, L, N, ps);
+      const int lane = threadIdx.x;
+      const uint32_t d = lane == 0 ? static_cast<uint32_t>(n_pop) : static_cast<uint32_t>(ps.depth);
+      uint64_t* dst = reinterpret_cast<uint64_t*>(sh.pops + sq * kWave + lane);
+      __hip_atomic_store(dst, (static_cast<uint64_t>(static_cast<uint32_t>(ps.token)) << 32) | d,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(dst + 1,
+                         (static_cast<uint64_t>(__float_as_uint(ps.score)) << 32) |
+                             static_cast<uint32_t>(ps.par),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (!arrive_last(sh.batch_cnt, sh.nseq)) return;
+    shared_cut_and_layout(sh, L, N, root_token, parent, depth_out, token_out, anc_out, score_out,
+                          n_valid_out);
+    return;
+  }
   if (threadIdx.x >= kWave) return;  // the rest is one wavefront
-  select_tree(lq, tk, sq, root_token, L, N, parent, depth_out, token_out, anc_out, score_out, n_valid_out);
+  PopState ps;
+  const int n_pop = select_pops(lq, tk, L, N, ps);
+  layout_tree(ps, n_pop, sq, root_token[sq], L, N + 1, parent, depth_out, token_out, anc_out, score_out,
+              n_valid_out);
 }
 
 }  // namespace
@@ -626,13 +752,13 @@ struct TreeBufs {
 template <typename T>
 void launch_tree(int nv, dim3 ga, const T* logits, int L, int V, int N, int nch, const TreeBufs& b,
                  const int32_t* root, int32_t* parent, int32_t* depth, int32_t* token, uint64_t* anc,
-                 float* score, int32_t* n_valid, hipStream_t st) {
+                 float* score, int32_t* n_valid, const SharedArgs& sh, hipStream_t st) {
   switch (nv) {
 #define GLANCE_TREE_CASE(n)                                                                         \
   case n:                                                                                          \
     tree_kernel<T, n><<<ga, kChunkThreads, 0, st>>>(logits, L, V, N, nch, b.cstat, b.clist, b.lq, b.tk, \
                                                    b.row_cnt, b.seq_cnt, root, parent, depth, token, \
-                                                   anc, score, n_valid);                            \
+                                                   anc, score, n_valid, sh);                        \
     break;
     GLANCE_TREE_CASE(1)
     GLANCE_TREE_CASE(2)
@@ -665,6 +791,8 @@ TreeWs tree_ws_layout(int nseq, int L, int V) {
   w.off_tk = take(r * kSlots * sizeof(int));
   w.off_row_cnt = take(r * sizeof(unsigned));
   w.off_seq_cnt = take(static_cast<size_t>(nseq) * sizeof(unsigned));
+  w.off_pops = take(static_cast<size_t>(nseq) * kWave * sizeof(int4));
+  w.off_batch_cnt = take(sizeof(unsigned));
   w.bytes = off;
   return w;
 }
@@ -672,8 +800,16 @@ TreeWs tree_ws_layout(int nseq, int L, int V) {
 glance_status launch_build_tree(const void* logits, int dtype, const int32_t* root, int nseq,
                                 int L, int V, int N, int32_t* parent, int32_t* depth,
                                 int32_t* token, uint64_t* anc, float* score,
-                                int32_t* n_valid, void* ws, hipStream_t st) {
+                                int32_t* n_valid, void* ws, hipStream_t st,
+                                const float* log_weight, int budget, float tau) {
   const TreeWs w = tree_ws_layout(nseq, L, V);
+  SharedArgs sh{};
+  sh.log_weight = log_weight;
+  sh.budget = budget;
+  sh.tau = tau;
+  sh.nseq = nseq;
+  sh.pops = reinterpret_cast<int4*>(static_cast<char*>(ws) + w.off_pops);
+  sh.batch_cnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + w.off_batch_cnt);
   char* base = static_cast<char*>(ws);
   TreeBufs b;
   b.cstat = reinterpret_cast<unsigned long long*>(base + w.off_cstat);
@@ -692,10 +828,10 @@ glance_status launch_build_tree(const void* logits, int dtype, const int32_t* ro
   const dim3 ga(nch, L, nseq);
   if (dtype == GLANCE_BF16)
     launch_tree<uint16_t>(nv, ga, static_cast<const uint16_t*>(logits), L, V, N, nch, b, root, parent,
-                          depth, token, anc, score, n_valid, st);
+                          depth, token, anc, score, n_valid, sh, st);
   else
     launch_tree<float>(nv, ga, static_cast<const float*>(logits), L, V, N, nch, b, root, parent, depth,
-                       token, anc, score, n_valid, st);
+                       token, anc, score, n_valid, sh, st);
   GLANCE_LAUNCH_CHECK();
   return GLANCE_OK;
 }
