@@ -22,6 +22,18 @@ Storage points of bf16 runs (values that a real engine keeps in bf16): the
 K/V entry of every sequence position and each layer's output h'.  The oracle
 rounds there and computes in float64 everywhere else.
 
+Full layer (configs with an MLP; the pages name the target, Qwen3-VL-8B, but
+not its layer internals, so this is the public decoder-layer shape of that
+family):
+  x   = RMSNorm(h) * g_attn                       (stored)
+  q, k, v = x Wq^T, x Wk^T, x Wv^T; every q and k head normalised,
+        RMSNorm(q_head) * g_q, RMSNorm(k_head) * g_k, then rotated (k stored)
+  h1  = h + concat_g(a_g) Wo^T                    (stored)
+  x2  = RMSNorm(h1) * g_mlp                       (stored)
+  act = silu(x2 W_gate^T) * (x2 W_up^T)           (stored)
+  h'  = h1 + act W_down^T                         (stored)
+with RMSNorm(x) = x / sqrt(mean(x^2) + eps) and silu(z) = z / (1 + e^-z).
+
 Row statistics (paper §3.1 greedy argmax; App. B.1 top-2 gap; §6 and the
 project page's entropy law: next-token entropy H at the round root, in nats):
 argmax (lowest token id on exact ties), top-1 logit, gap = top-1 minus the best
@@ -46,6 +58,16 @@ def rope(x: np.ndarray, pos: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
 
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * g over the last axis."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * g
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
 class TargetModel:
     """Float64 view of the synthetic target's tensors, decoded on demand."""
 
@@ -56,6 +78,8 @@ class TargetModel:
         self.V, self.d = cfg.V, cfg.d_model
         self.Hq, self.Hkv, self.D = cfg.Hq, cfg.Hkv, cfg.D
         self.n_layers = cfg.n_layers
+        self.full = getattr(cfg, "mlp", 0) > 0
+        self.eps = getattr(cfg, "norm_eps", 1e-6)
         self._inp = inp
         self.kv_offsets = np.asarray(inp["kv_offsets"], dtype=np.int64)
         self.prefix_len = np.asarray(inp["prefix_len"], dtype=np.int64)
@@ -71,8 +95,10 @@ class TargetModel:
     def layer(self, li: int) -> dict:
         if li not in self._layer_cache:
             lw = self._inp["layers"][li]
-            self._layer_cache = {li: {k: decode(lw[k], self.dtype)
-                                      for k in ("wq", "wk", "wv", "wo")}}
+            names = ("wq", "wk", "wv", "wo")
+            if self.full:
+                names += ("g_attn", "g_q", "g_k", "g_mlp", "w_gate", "w_up", "w_down")
+            self._layer_cache = {li: {k: decode(lw[k], self.dtype) for k in names}}
         return self._layer_cache[li]
 
     def prefix_kv(self, li: int, s: int):
@@ -96,9 +122,13 @@ class TargetModel:
         """q (rotated), k (rotated, stored), v (stored) of rows h at positions pos."""
         w = self.layer(li)
         n = h.shape[0]
-        q = (h @ w["wq"].T).reshape(n, self.Hq, self.D)
-        k = (h @ w["wk"].T).reshape(n, self.Hkv, self.D)
-        v = (h @ w["wv"].T).reshape(n, self.Hkv, self.D)
+        x = store(rmsnorm(h, w["g_attn"], self.eps), self.dtype) if self.full else h
+        q = (x @ w["wq"].T).reshape(n, self.Hq, self.D)
+        k = (x @ w["wk"].T).reshape(n, self.Hkv, self.D)
+        v = (x @ w["wv"].T).reshape(n, self.Hkv, self.D)
+        if self.full:
+            q = rmsnorm(q, w["g_q"], self.eps)
+            k = rmsnorm(k, w["g_k"], self.eps)
         q = rope(q, pos, self.cos, self.sin)
         k = store(rope(k, pos, self.cos, self.sin), self.dtype)
         v = store(v, self.dtype)
@@ -119,7 +149,12 @@ class TargetModel:
 
     def residual(self, li: int, h: np.ndarray, a: np.ndarray) -> np.ndarray:
         w = self.layer(li)
-        return store(h + a.reshape(a.shape[0], -1) @ w["wo"].T, self.dtype)
+        h1 = store(h + a.reshape(a.shape[0], -1) @ w["wo"].T, self.dtype)
+        if not self.full:
+            return h1
+        x2 = store(rmsnorm(h1, w["g_mlp"], self.eps), self.dtype)
+        act = store(silu(x2 @ w["w_gate"].T) * (x2 @ w["w_up"].T), self.dtype)
+        return store(h1 + act @ w["w_down"].T, self.dtype)
 
 
 def evaluate_paths(model: TargetModel, s: int, root: int, paths: list,

@@ -31,7 +31,7 @@ from typing import Optional
 import numpy as np
 
 # Fixed order in which child streams are spawned from SeedSequence(seed).
-_STREAMS = ("draft", "root", "embed", "head", "layers", "kv", "prefix", "extra")
+_STREAMS = ("draft", "root", "embed", "head", "layers", "kv", "prefix", "extra", "mlp")
 _CHUNK = 1 << 22  # elements per generation chunk (bounded temporaries)
 
 
@@ -91,6 +91,10 @@ class RoundConfig:
     planted_alpha: float = 4.0      # "planted": strength of the head's bigram bias
     planted_rho: float = 0.852      # "planted": P(G >= l) = rho**l, G <= L
     mixed_top: float = 50.0         # "mixed": spike on the last sequence
+    mlp: int = 0                    # intermediate size of a full layer (0: attention only)
+    mlp_std: float = 0.02           # W_gate / W_up / W_down
+    gain_std: float = 0.1           # RMSNorm gains 1 + gain_std * N(0, 1)
+    norm_eps: float = 1e-6
 
     @property
     def rows(self) -> int:          # verify rows per sequence: root + N nodes
@@ -141,6 +145,15 @@ CONFIGS = {
         name="mini_bf16", dtype="bf16", V=20011, L=15, N=63, d_model=512,
         Hq=8, Hkv=2, D=128, prefix=("fixed", 333), draft="scaled",
         draft_scales=(3.0,), kv_std=1.0),
+    # a full layer (RMSNorm, QK-norm, SwiGLU MLP) at reduced and at 8B shapes
+    "mini_bf16_full": RoundConfig(
+        name="mini_bf16_full", dtype="bf16", V=20011, L=15, N=63, d_model=512,
+        Hq=4, Hkv=2, D=128, n_layers=2, mlp=1536, prefix=("fixed", 300), draft="scaled",
+        draft_scales=(3.0,), kv_std=1.0, w_std=0.05, mlp_std=0.05),
+    "qwen8b_full": RoundConfig(
+        name="qwen8b_full", dtype="bf16", V=151936, L=15, N=63, d_model=4096,
+        Hq=32, Hkv=8, D=128, mlp=12288, prefix=("fixed", 1024), draft="scaled",
+        draft_scales=C2_SCALES, n_rounds=len(C2_SCALES), kv_std=1.0),
     "mini_bf16_ragged": RoundConfig(
         name="mini_bf16_ragged", dtype="bf16", V=9001, L=7, N=40, d_model=256,
         Hq=4, Hkv=1, D=128, n_layers=2, nseq=3, prefix=("uniform", 1, 700),
@@ -396,6 +409,18 @@ def gen_round(cfg: RoundConfig, seed: int, with_model: bool = True) -> dict:
             "k_cache": _normal(rk, (sumP, cfg.Hkv, cfg.D), cfg.kv_std, dt),
             "v_cache": _normal(rk, (sumP, cfg.Hkv, cfg.D), cfg.kv_std, dt),
         })
+        if cfg.mlp > 0:
+            # full layer: RMSNorm gains (input, per q/k head, before the MLP) and
+            # the gate/up/down projections, from a stream of their own
+            rm = st.rng("mlp", li)
+            gain = lambda n: _store((1.0 + cfg.gain_std * rm.standard_normal(n)).astype(np.float32), dt)
+            layers[-1].update({
+                "g_attn": gain(cfg.d_model), "g_q": gain(cfg.D), "g_k": gain(cfg.D),
+                "g_mlp": gain(cfg.d_model),
+                "w_gate": _normal(rm, (cfg.mlp, cfg.d_model), cfg.mlp_std, dt),
+                "w_up": _normal(rm, (cfg.mlp, cfg.d_model), cfg.mlp_std, dt),
+                "w_down": _normal(rm, (cfg.d_model, cfg.mlp), cfg.mlp_std, dt),
+            })
     out["layers"] = layers
     n_pos = int(P.max()) + cfg.L + 1
     out["rope_cos"], out["rope_sin"] = rope_tables(n_pos, cfg.D, cfg.rope_theta)
