@@ -186,6 +186,49 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype,
 size_t glance_tree_attn_ws(int32_t nseq, int32_t n_rows, int64_t max_prefix,
                            int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D);
 
+/* glance_tree_layer: step 3 with a full decoder layer instead of the
+ * attention-only block (bf16).  The pages name the target family (Qwen3-VL-8B)
+ * but not its layer internals; this is that family's public decoder-layer
+ * shape:
+ *   x   = RMSNorm(h) * g_attn                                (bf16)
+ *   q, k, v = x Wq^T, x Wk^T, x Wv^T; each q and k head RMSNorm(.) * g_q / g_k,
+ *         then rotated as in glance_tree_attn (k and v: bf16 cache entries)
+ *   h1  = h + attention Wo^T                                 (bf16)
+ *   x2  = RMSNorm(h1) * g_mlp                                (bf16)
+ *   act = silu(x2 W_gate^T) * (x2 W_up^T)                    (bf16)
+ *   h'  = h1 + act W_down^T                                  (bf16, h_out)
+ * with RMSNorm(x) = x / sqrt(mean(x^2) + eps), silu(z) = z / (1 + e^-z) and the
+ * attention of glance_tree_attn (same masks, positions, caches).  Arguments as
+ * glance_tree_attn; layer->attn holds the attention weights and caches.
+ *   g_attn, g_mlp [d_model], g_q, g_k [D]          bf16 gains
+ *   w_gate, w_up  [inter][d_model], w_down [d_model][inter]   bf16
+ * Limits: D == 128; d_model, Hq*D and inter multiples of 256; eps >= 0.
+ * Workspace: glance_tree_layer_ws (zero-filled, as every workspace).
+ */
+typedef struct {
+  glance_attn_layer attn;
+  const void* g_attn;
+  const void* g_q;
+  const void* g_k;
+  const void* g_mlp;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  int32_t inter;
+  float eps;
+} glance_full_layer;
+
+glance_status glance_tree_layer(const glance_full_layer* layer, const void* embed,
+                                const int32_t* token, const void* h_in, void* h_out,
+                                const int64_t* kv_offsets, int64_t max_prefix, const int32_t* depth,
+                                const uint64_t* anc, const float* rope_cos, const float* rope_sin,
+                                int32_t n_pos, int32_t nseq, int32_t n_rows, int32_t d_model,
+                                int32_t Hq, int32_t Hkv, int32_t D, float* attn_out, void* tree_k,
+                                void* tree_v, void* ws, size_t ws_bytes, void* stream);
+
+size_t glance_tree_layer_ws(int32_t nseq, int32_t n_rows, int64_t max_prefix, int32_t d_model,
+                            int32_t Hq, int32_t Hkv, int32_t D, int32_t inter);
+
 /* -------------------------------------------------------------------- step 4 --
  * glance_verify_head: LM head of the verify rows with a fused row epilogue.
  *

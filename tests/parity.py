@@ -2,10 +2,15 @@
 
 Integer outputs (tree layout, argmax, walk) must match bit-exactly wherever the
 oracle's decision is not a near-tie (top-2 logit gap, or the tree's boundary
-gap, above 1e-3: the pages' uniqueness assumption of Theorem 1); near-ties are
-flagged, counted and checked for validity instead.  Float tensors are compared
-norm-wise, max|gpu - oracle| / max|oracle|, against 1e-5 (fp32 runs) or 1e-2
-(bf16 runs)."""
+gap, above 1e-3: the pages' uniqueness assumption of Theorem 1; for the argmax
+also above twice the largest difference between the GPU's and the oracle's
+logits of the round, since each of the two best logits can move by that much);
+near-ties are flagged, counted and checked for validity instead.  Float tensors
+are compared norm-wise, max|gpu - oracle| / max|oracle|, against 1e-5 (fp32
+runs), 1e-2 (bf16 runs) or 2e-2 (bf16 runs of full layers: five more bf16
+storage points per layer, where a rounding flip moves an element by one bf16
+ulp, up to 2^-7 of max|x| for the largest elements, and the next products carry
+it to every element; measured errors reach about 1% of max|h|)."""
 from __future__ import annotations
 
 import numpy as np
@@ -15,8 +20,10 @@ from oracle import draft, model as mdl, round as orr, tree as tr, walk as wk
 GAP = 1e-3
 
 
-def tol_for(dtype: str) -> float:
-    return 1e-5 if dtype == "f32" else 1e-2
+def tol_for(dtype: str, full: bool = False) -> float:
+    if dtype == "f32":
+        return 1e-5
+    return 2e-2 if full else 1e-2
 
 
 def rel_err(got, want) -> float:
@@ -81,9 +88,10 @@ def check_tree(gpu: dict, s: int, ora_tree: dict, logq: np.ndarray, N: int, L: i
 
 
 def check_rows(gpu: dict, ev: dict, z: np.ndarray, s: int, n_rows: int, dtype: str, report: dict,
-               rows=None):
-    """Verify rows of sequence s (the oracle evaluated on the GPU's own tree)."""
-    tol = tol_for(dtype)
+               rows=None, full: bool = False):
+    """Verify rows of sequence s (the oracle evaluated on the GPU's own tree).
+    Leaves the round's decision threshold in report["flag"] (see module doc)."""
+    tol = tol_for(dtype, full)
     sl = slice(s * n_rows, (s + 1) * n_rows)
     idx = np.arange(len(ev["final"])) if rows is None else np.asarray(rows)
     if "attn_out" in gpu:
@@ -95,17 +103,21 @@ def check_rows(gpu: dict, ev: dict, z: np.ndarray, s: int, n_rows: int, dtype: s
             report.setdefault("h_err", []).append(e)
             assert e <= tol, ("h", li, e)
     am, top1, gap, H = mdl.row_stats(z)
+    flag = GAP
     if "logits" in gpu:
         e = rel_err(gpu["logits"][sl][idx], z)
         report.setdefault("logit_err", []).append(e)
         assert e <= tol, ("logits", e)
+        e_abs = float(np.abs(gpu["logits"][sl][idx].astype(np.float64) - z).max())
+        flag = max(GAP, 2.0 * e_abs)
+    report["flag"] = max(report.get("flag", GAP), flag)
     e = rel_err(gpu["top1"][sl][idx], top1)
     assert e <= tol, ("top1", e)
     eH = np.max(np.abs(gpu["entropy"][sl][idx] - H) / np.maximum(1.0, H))
     report.setdefault("H_err", []).append(float(eH))
     assert eH <= tol, ("entropy", eH)
     g_am = gpu["argmax"][sl][idx]
-    sure = gap > GAP
+    sure = gap > flag
     report["rows"] = report.get("rows", 0) + len(idx)
     report["rows_flagged"] = report.get("rows_flagged", 0) + int((~sure).sum())
     assert np.array_equal(g_am[sure], am[sure]), "argmax mismatch on an unflagged row"
@@ -133,7 +145,7 @@ def check_walk(gpu: dict, s: int, paths, am, gap, L: int, report: dict, greedy=N
     token = gpu["token"][s]
     nv = int(gpu["n_valid"][s])
     oa, otoks, orows = wk.walk(parent, token, nv, am, L)
-    flagged = bool(np.any(gap[orows] <= GAP))
+    flagged = bool(np.any(gap[orows] <= report.get("flag", GAP)))
     if flagged:
         report["walk_flagged"] = report.get("walk_flagged", 0) + 1
         return

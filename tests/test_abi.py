@@ -179,6 +179,28 @@ def _attn(lib, **kw):
                                 a["ws_bytes"], None)
 
 
+def test_tree_layer_rejects_bad_arguments(lib):
+    p = OK_PTR
+
+    def call(inter=12288, eps=1e-6, D=128, d=4096, gate=p, ws_bytes=1 << 40):
+        attn = _lib.GlanceAttnLayer(*(p,) * 6)
+        full = _lib.GlanceFullLayer(attn, p, p, p, p, gate, p, p, inter, eps)
+        return lib.glance_tree_layer(ctypes.byref(full), p, p, None, p, p, 1024, p, p, p, p, 2048,
+                                     1, 64, d, 32, 8, D, None, None, None, p * 16, ws_bytes, None)
+
+    assert lib.glance_tree_layer_ws(1, 64, 1024, 4096, 32, 8, 128, 12288) > \
+        lib.glance_tree_attn_ws(1, 64, 1024, 4096, 32, 8, 128)
+    assert lib.glance_tree_layer_ws(1, 64, 1024, 4096, 32, 8, 64, 12288) == 0
+    assert call(inter=1000) == -4
+    assert call(D=64) == -4
+    assert call(d=4000) == -4
+    assert call(eps=float("nan")) == -1
+    assert call(eps=-1.0) == -1
+    assert call(gate=None) == -1
+    assert call(gate=p + 2) == -2
+    assert call(ws_bytes=1000) == -3
+
+
 def test_tree_attn_rejects_bad_arguments(lib):
     assert _attn(lib, n_rows=65) == -1
     assert _attn(lib, Hq=30) == -1            # not a multiple of Hkv

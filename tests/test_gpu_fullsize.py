@@ -8,6 +8,8 @@ times (the same DeviceRound path: one C-ABI call per step, bf16 storage).
                 run must be accepted whole (A = G) and the break token emitted
   ragged batch  8 rounds in one call, prefixes uniform in 512..6144; rows on
                 the walk plus a seeded sample per round, with their ancestors
+  full layer    the single-layer shapes with RMSNorm, QK-norm and a SwiGLU MLP
+                (intermediate 12288); sampled rows as for the ragged batch
   deep stack    36 layers over an 8192-token prefix, a given random topology;
                 every layer's attention output and hidden rows on a sampled
                 set of rows (and their ancestors), logits on the sample
@@ -66,7 +68,7 @@ def _check_walk_on_rows(gpu, s, n_rows, am_rows, gap_rows, rows, L, report):
     parent, token = gpu["parent"][s], gpu["token"][s]
     nv = int(gpu["n_valid"][s])
     pos = {r: i for i, r in enumerate(rows)}
-    if any(gap_rows[pos[r]] <= parity.GAP for r in path):
+    if any(gap_rows[pos[r]] <= report.get("flag", parity.GAP) for r in path):
         report["walk_flagged"] = report.get("walk_flagged", 0) + 1
         return
     for k, r in enumerate(path):
@@ -112,7 +114,8 @@ def _sampled_round(inp, model, dev, r, per_seq, seed, teacher_forced=False):
         else:
             ev = mdl.evaluate_paths(model, s, root, sel)
         z = model.logits(ev["final"])
-        am, gap = parity.check_rows(gpu, ev, z, s, n_rows, cfg.dtype, report, rows=rows)
+        am, gap = parity.check_rows(gpu, ev, z, s, n_rows, cfg.dtype, report, rows=rows,
+                                    full=cfg.mlp > 0)
         _check_walk_on_rows(gpu, s, n_rows, am, gap, rows, cfg.L, report)
     print(f"[full] {cfg.name} round={r}: {report}", flush=True)
     return gpu, report
@@ -171,6 +174,16 @@ def test_copy_regime_8b_accepts_planted_run(r):
 def test_ragged_batch_8b_sampled_rows():
     inp, model, dev = _workload("qwen8b_ragged8", 5000, cache_head=False)
     _sampled_round(inp, model, dev, 0, per_seq=4, seed=5000)
+
+
+# ---------------------------------------------------------------- full layer
+@pytest.mark.timeout(300)
+def test_full_layer_8b_sampled_rows():
+    """A full decoder layer (RMSNorm, QK-norm, SwiGLU MLP with intermediate
+    size 12288) at the 8B shapes: the attention output and hidden rows of a
+    seeded sample of rows (with their ancestors), their logits and the walk."""
+    inp, model, dev = _workload("qwen8b_full", 6000, cache_head=False)
+    _sampled_round(inp, model, dev, 0, per_seq=4, seed=6000)
 
 
 # ---------------------------------------------------------------- deep stack

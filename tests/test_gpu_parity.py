@@ -33,7 +33,8 @@ def _round_parity(inp, r, exact="beam", greedy=True):
             paths = parity.gpu_paths(gpu["parent"][s], gpu["token"][s], gpu["n_valid"][s])
         ev = mdl.evaluate_paths(model, s, root, paths)
         z = model.logits(ev["final"])
-        am, gap = parity.check_rows(gpu, ev, z, s, cfg.N + 1, cfg.dtype, report)
+        am, gap = parity.check_rows(gpu, ev, z, s, cfg.N + 1, cfg.dtype, report,
+                                    full=cfg.mlp > 0)
         g = orr.continuation(model, s, root, paths[1:], cfg.L) if greedy else None
         parity.check_walk(gpu, s, paths, am, gap, cfg.L, report, g)
     print(f"[parity] {cfg.name} seed={inp['seed']} round={r}: {report}", flush=True)
@@ -62,6 +63,13 @@ def test_tiny_empty_tree():
                                        ("mini_bf16_ragged", 3), ("mini_bf16_ragged", 4)])
 def test_mini_bf16_round(name, seed):
     _round_parity(gen_round(make_config(name), seed), 0)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_mini_full_layer_round(seed):
+    """Two full decoder layers (RMSNorm, QK-norm, SwiGLU MLP): every layer's
+    attention output and hidden rows, the logits, the statistics and the walk."""
+    _round_parity(gen_round(make_config("mini_bf16_full"), seed), 0)
 
 
 def test_mini_copy_regime_accepts_planted_run():

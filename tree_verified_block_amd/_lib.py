@@ -30,6 +30,11 @@ class GlanceAttnLayer(ctypes.Structure):
     _fields_ = [("wq", _P), ("wk", _P), ("wv", _P), ("wo", _P), ("k_cache", _P), ("v_cache", _P)]
 
 
+class GlanceFullLayer(ctypes.Structure):
+    _fields_ = [("attn", GlanceAttnLayer), ("g_attn", _P), ("g_q", _P), ("g_k", _P), ("g_mlp", _P),
+                ("w_gate", _P), ("w_up", _P), ("w_down", _P), ("inter", _I), ("eps", _F)]
+
+
 # name -> (restype, argtypes), exactly the declarations of include/glance.h
 SIGNATURES = {
     "glance_build_tree": (_I, [_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -40,6 +45,9 @@ SIGNATURES = {
                               _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ,
                               _P]),
     "glance_tree_attn_ws": (_SZ, [_I, _I, _I64, _I, _I, _I, _I]),
+    "glance_tree_layer": (_I, [ctypes.POINTER(GlanceFullLayer), _P, _P, _P, _P, _P, _I64, _P, _P,
+                               _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "glance_tree_layer_ws": (_SZ, [_I, _I, _I64, _I, _I, _I, _I, _I]),
     "glance_verify_head": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "glance_verify_head_ws": (_SZ, [_I, _I, _I, _I]),
     "glance_verify_head_sampled": (_I, [_P, _P, _I, _I, _I, _I, _F, _U64, _U64, _P, _P, _P, _P,

@@ -8,7 +8,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import GLANCE_BF16, GLANCE_F32, GlanceAttnLayer
+from ._lib import GLANCE_BF16, GLANCE_F32, GlanceAttnLayer, GlanceFullLayer
 
 
 def _ptr(t):
@@ -94,6 +94,29 @@ def glance_tree_attn(layer: dict, dtype: int, embed, token, h_in, h_out, kv_offs
               _ptr(anc), _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], nseq, n_rows,
               d_model, Hq, Hkv, D, _ptr(attn_out), _ptr(tree_k), _ptr(tree_v), _ptr(ws),
               ws.numel(), _stream(stream))
+
+
+def tree_layer_ws_bytes(nseq, n_rows, max_prefix, d_model, Hq, Hkv, D, inter) -> int:
+    return _lib.load().glance_tree_layer_ws(nseq, n_rows, max_prefix, d_model, Hq, Hkv, D, inter)
+
+
+def glance_tree_layer(layer: dict, eps: float, embed, token, h_in, h_out, kv_offsets,
+                      max_prefix: int, depth, anc, rope_cos, rope_sin, nseq: int, n_rows: int,
+                      d_model: int, Hq: int, Hkv: int, D: int, ws, attn_out=None, tree_k=None,
+                      tree_v=None, stream=None):
+    """One full decoder layer (RMSNorm, QK-norm, attention, SwiGLU MLP) over the
+    verify rows; ``layer`` holds wq/wk/wv/wo, the caches, g_attn/g_q/g_k/g_mlp and
+    w_gate/w_up/w_down (bf16)."""
+    attn = GlanceAttnLayer(_ptr(layer["wq"]), _ptr(layer["wk"]), _ptr(layer["wv"]),
+                           _ptr(layer["wo"]), _ptr(layer["k_cache"]), _ptr(layer["v_cache"]))
+    full = GlanceFullLayer(attn, _ptr(layer["g_attn"]), _ptr(layer["g_q"]), _ptr(layer["g_k"]),
+                           _ptr(layer["g_mlp"]), _ptr(layer["w_gate"]), _ptr(layer["w_up"]),
+                           _ptr(layer["w_down"]), layer["w_gate"].shape[0], float(eps))
+    _lib.call("glance_tree_layer", ctypes.byref(full), _ptr(embed), _ptr(token), _ptr(h_in),
+              _ptr(h_out), _ptr(kv_offsets), int(max_prefix), _ptr(depth), _ptr(anc),
+              _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], nseq, n_rows, d_model, Hq, Hkv,
+              D, _ptr(attn_out), _ptr(tree_k), _ptr(tree_v), _ptr(ws), ws.numel(),
+              _stream(stream))
 
 
 # ---------------------------------------------------------------------- step 4

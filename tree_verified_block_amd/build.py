@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libglance.so")
-SOURCES = ["glance.cpp", "tree.hip", "gemm.hip", "attn.hip", "walk.hip"]
+SOURCES = ["glance.cpp", "tree.hip", "gemm.hip", "attn.hip", "walk.hip", "layer.hip"]
 
 
 def hipcc() -> str:

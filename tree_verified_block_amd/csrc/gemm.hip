@@ -170,7 +170,10 @@ __device__ __forceinline__ uint4 mask4(uint4 v, uint32_t mask) {
 // 8j..8j+7 and 64+8j..64+8j+7.
 template <int EPI>
 __device__ __forceinline__ int block_row(const GemmArgs& a, int b, int i) {
-  if constexpr (EPI == EPI_QKV) {
+  if constexpr (EPI == EPI_SWIGLU) {
+    // rows i < 8: gate rows 8b + i; rows 8 + i: the matching up rows
+    return i < 8 ? 8 * b + i : a.N / 2 + 8 * b + (i - 8);
+  } else if constexpr (EPI == EPI_QKV) {
     const int nq = a.Hq * 8, nk = a.Hkv * 8;
     if (b < nq + nk) {
       const int base = b < nq ? 0 : a.Hq * 128;
@@ -556,6 +559,22 @@ __device__ __forceinline__ void proj_store(const GemmArgs& a, int b, int gm, con
     uint4* op = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out_res) + static_cast<size_t>(gm) * a.N + n);
     op[0] = o[0];
     op[1] = o[1];
+  } else if constexpr (EPI == EPI_STORE_F32) {
+    float4* op = reinterpret_cast<float4*>(a.out_f32 + static_cast<size_t>(gm) * a.N + b * 16);
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) op[k4] = make_float4(x[4 * k4], x[4 * k4 + 1], x[4 * k4 + 2], x[4 * k4 + 3]);
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    // x[i] the gate and x[8 + i] the up projection of intermediate unit 8b + i
+    uint32_t ow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float g0 = x[2 * j], g1 = x[2 * j + 1];
+      const float v0 = g0 / (1.f + expf(-g0)) * x[8 + 2 * j];
+      const float v1 = g1 / (1.f + expf(-g1)) * x[8 + 2 * j + 1];
+      ow[j] = pack_bf16x2(v0, v1);
+    }
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out_res) + static_cast<size_t>(gm) * (a.N / 2) + 8 * b) =
+        make_uint4(ow[0], ow[1], ow[2], ow[3]);
   } else {  // EPI_QKV
     const int nq = a.Hq * 8, nk = a.Hkv * 8;
     if (b < nq + nk) {
@@ -982,13 +1001,19 @@ glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
     // ring depth: the largest of 8, 4, 2 slots dividing the slice's chunk count
     const int nck = a.K / S / kKc;
     const int rs = nck % 8 == 0 ? 8 : nck % 4 == 0 ? 4 : 2;
+#define GLANCE_PROJ(E)                                                             \
+  if (rs == 8)                                                                     \
+    proj_bf16_kernel<E, 7><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);         \
+  else if (rs == 4)                                                                \
+    proj_bf16_kernel<E, 3><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);         \
+  else                                                                             \
+    proj_bf16_kernel<E, 1><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
     if (a.epi == EPI_QKV) {
-      if (rs == 8)
-        proj_bf16_kernel<EPI_QKV, 7><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
-      else if (rs == 4)
-        proj_bf16_kernel<EPI_QKV, 3><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
-      else
-        proj_bf16_kernel<EPI_QKV, 1><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
+      GLANCE_PROJ(EPI_QKV)
+    } else if (a.epi == EPI_SWIGLU) {
+      GLANCE_PROJ(EPI_SWIGLU)
+    } else if (a.epi == EPI_STORE_F32) {
+      GLANCE_PROJ(EPI_STORE_F32)
     } else {
       if (rs == 8)
         proj_bf16_kernel<EPI_RESID, 7><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
@@ -997,6 +1022,7 @@ glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
       else
         proj_bf16_kernel<EPI_RESID, 1><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
     }
+#undef GLANCE_PROJ
   }
   GLANCE_LAUNCH_CHECK();
   return GLANCE_OK;

@@ -62,10 +62,12 @@ struct AttnWs {
   int n_split = 0, split = 0;
   size_t off_qkv = 0, off_q = 0, off_k = 0, off_v = 0, off_part = 0, off_x = 0, bytes = 0;
   size_t off_kpart = 0, off_kcnt = 0;
+  // full layer (inter > 0): normalised rows, fp32 q/k/v, h1 and the MLP activation
+  size_t off_xn = 0, off_qkv32 = 0, off_h1 = 0, off_act = 0;
 };
 
 AttnWs attn_ws_layout(int dtype, int nseq, int n_rows, int64_t max_prefix, int d_model, int Hq,
-                      int Hkv, int D) {
+                      int Hkv, int D, int inter = 0) {
   AttnWs w;
   const size_t R = static_cast<size_t>(nseq) * n_rows;
   size_t off = 0;
@@ -82,13 +84,26 @@ AttnWs attn_ws_layout(int dtype, int nseq, int n_rows, int64_t max_prefix, int d
     w.n_split = static_cast<int>((max_prefix + w.split - 1) / w.split);
     w.off_part = take(attn_part_floats(nseq, n_rows, Hq, Hkv, D, w.n_split) * sizeof(float));
     w.off_x = take(R * Hq * D * 2);
-    // split-K scratch shared by the q/k/v and output projections
+    // split-K scratch shared by the projections (q/k/v, output and, in a full
+    // layer, gate/up and down)
     const int M = static_cast<int>(R);
     const int nb_qkv = (Hq + 2 * Hkv) * 8, nb_o = (d_model + 15) / 16;
-    const size_t pf = std::max(proj_part_floats(M, nb_qkv, d_model), proj_part_floats(M, nb_o, Hq * D));
+    size_t pf = std::max(proj_part_floats(M, nb_qkv, d_model), proj_part_floats(M, nb_o, Hq * D));
+    size_t nc = std::max(proj_counters(M, nb_qkv), proj_counters(M, nb_o));
+    if (inter > 0) {
+      const int nb_gu = 2 * inter / 16;
+      pf = std::max({pf, proj_part_floats(M, nb_gu, d_model), proj_part_floats(M, nb_o, inter)});
+      nc = std::max(nc, proj_counters(M, nb_gu));
+    }
     w.off_kpart = take(pf * sizeof(float));
     // arrival counters of the split-K groups (each projection returns them to zero)
-    w.off_kcnt = take(std::max(proj_counters(M, nb_qkv), proj_counters(M, nb_o)) * sizeof(unsigned));
+    w.off_kcnt = take(nc * sizeof(unsigned));
+    if (inter > 0) {
+      w.off_xn = take(R * d_model * 2);
+      w.off_qkv32 = take(R * static_cast<size_t>(Hq + 2 * Hkv) * D * sizeof(float));
+      w.off_h1 = take(R * d_model * 2);
+      w.off_act = take(R * static_cast<size_t>(inter) * 2);
+    }
   } else {
     w.off_qkv = take(R * static_cast<size_t>(Hq + 2 * Hkv) * D * sizeof(float));
     w.off_x = take(R * Hq * D * sizeof(float));
@@ -355,6 +370,193 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
   o.kpart = kpart;
   o.kcnt = kcnt;
   return dtype == GLANCE_BF16 ? launch_gemm_bf16(o, hs) : launch_gemm_f32(o, hs);
+}
+
+// --------------------------------------------------------- step 3, full layer
+size_t glance_tree_layer_ws(int32_t nseq, int32_t n_rows, int64_t max_prefix, int32_t d_model,
+                            int32_t Hq, int32_t Hkv, int32_t D, int32_t inter) {
+  if (nseq < 1 || n_rows < 1 || n_rows > GLANCE_MAX_ROWS || max_prefix < 0 || Hkv < 1 ||
+      Hq < Hkv || D != 128 || inter < 256 || d_model < 256)
+    return 0;
+  return attn_ws_layout(GLANCE_BF16, nseq, n_rows, max_prefix, d_model, Hq, Hkv, D, inter).bytes;
+}
+
+glance_status glance_tree_layer(const glance_full_layer* layer, const void* embed,
+                                const int32_t* token, const void* h_in, void* h_out,
+                                const int64_t* kv_offsets, int64_t max_prefix, const int32_t* depth,
+                                const uint64_t* anc, const float* rope_cos, const float* rope_sin,
+                                int32_t n_pos, int32_t nseq, int32_t n_rows, int32_t d_model,
+                                int32_t Hq, int32_t Hkv, int32_t D, float* attn_out, void* tree_k,
+                                void* tree_v, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  REQUIRE(layer != nullptr, "layer is NULL");
+  REQUIRE(nseq >= 1, "nseq = %d < 1", nseq);
+  REQUIRE(n_rows >= 1 && n_rows <= GLANCE_MAX_ROWS, "n_rows = %d outside [1, %d]", n_rows,
+          GLANCE_MAX_ROWS);
+  REQUIRE(Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
+  REQUIRE(d_model >= 1, "d_model = %d < 1", d_model);
+  REQUIRE(max_prefix >= 0, "max_prefix < 0");
+  REQUIRE(embed != nullptr || h_in != nullptr, "both embed and h_in are NULL");
+  REQUIRE(n_pos > max_prefix, "n_pos = %d must exceed max_prefix", n_pos);
+  REQUIRE(std::isfinite(layer->eps) && layer->eps >= 0.f, "eps = %g is not finite and >= 0",
+          static_cast<double>(layer->eps));
+  const int inter = layer->inter;
+  if (D != 128 || d_model % 256 != 0 || (Hq * D) % 256 != 0 || inter < 256 || inter % 256 != 0)
+    return fail(GLANCE_ERR_UNSUPPORTED,
+                "full layer needs D = 128 and d_model, Hq*D, inter multiples of 256 (got D %d, "
+                "d_model %d, Hq*D %d, inter %d)", D, d_model, Hq * D, inter);
+  const glance_attn_layer* at = &layer->attn;
+  REQUIRE_PTR(at->wq);
+  REQUIRE_PTR(at->wk);
+  REQUIRE_PTR(at->wv);
+  REQUIRE_PTR(at->wo);
+  REQUIRE_PTR(at->k_cache);
+  REQUIRE_PTR(at->v_cache);
+  REQUIRE_PTR(layer->g_attn);
+  REQUIRE_PTR(layer->g_q);
+  REQUIRE_PTR(layer->g_k);
+  REQUIRE_PTR(layer->g_mlp);
+  REQUIRE_PTR(layer->w_gate);
+  REQUIRE_PTR(layer->w_up);
+  REQUIRE_PTR(layer->w_down);
+  REQUIRE_ALIGNED_OR_NULL(embed);
+  REQUIRE_ALIGNED_OR_NULL(h_in);
+  REQUIRE_PTR(token);
+  REQUIRE_PTR(h_out);
+  REQUIRE_PTR(kv_offsets);
+  REQUIRE_PTR(depth);
+  REQUIRE_PTR(anc);
+  REQUIRE_PTR(rope_cos);
+  REQUIRE_PTR(rope_sin);
+  REQUIRE_ALIGNED_OR_NULL(attn_out);
+  REQUIRE_ALIGNED_OR_NULL(tree_k);
+  REQUIRE_ALIGNED_OR_NULL(tree_v);
+  const AttnWs w = attn_ws_layout(GLANCE_BF16, nseq, n_rows, max_prefix, d_model, Hq, Hkv, D, inter);
+  glance_status st = check_ws(ws, ws_bytes, w.bytes);
+  if (st != GLANCE_OK) return st;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  const int R = nseq * n_rows;
+  const int qd = Hq * D, kd = Hkv * D;
+  float* kpart = reinterpret_cast<float*>(base + w.off_kpart);
+  unsigned* kcnt = reinterpret_cast<unsigned*>(base + w.off_kcnt);
+  void* xn = base + w.off_xn;
+  void* h1 = base + w.off_h1;
+  void* act = base + w.off_act;
+  float* qkv32 = reinterpret_cast<float*>(base + w.off_qkv32);
+  if (tree_k == nullptr) tree_k = base + w.off_k;
+  if (tree_v == nullptr) tree_v = base + w.off_v;
+  const void* h0 = embed ? embed : h_in;
+
+  // 1. x = RMSNorm(h) g_attn; 2. q, k, v in fp32; 3. q/k head norms, RoPE, bf16
+  st = launch_rmsnorm(h0, embed ? token : nullptr, token, R, d_model, layer->g_attn, layer->eps, xn, hs);
+  if (st != GLANCE_OK) return st;
+  GemmArgs g{};
+  g.x = xn;
+  g.w.w[0] = at->wq;
+  g.w.w[1] = at->wk;
+  g.w.w[2] = at->wv;
+  g.w.n_end[0] = qd;
+  g.w.n_end[1] = qd + kd;
+  g.w.n_end[2] = qd + 2 * kd;
+  g.w.nseg = 3;
+  g.M = R;
+  g.N = qd + 2 * kd;
+  g.K = d_model;
+  g.epi = EPI_STORE_F32;
+  g.out_f32 = qkv32;
+  g.kpart = kpart;
+  g.kcnt = kcnt;
+  st = launch_gemm_bf16(g, hs);
+  if (st != GLANCE_OK) return st;
+  st = launch_qkv_finish(qkv32, R, Hq, Hkv, layer->g_q, layer->g_k, layer->eps, kv_offsets, depth,
+                         n_rows, rope_cos, rope_sin, n_pos, base + w.off_q, tree_k, tree_v, hs);
+  if (st != GLANCE_OK) return st;
+
+  // 4. attention over prefix + ancestors
+  AttnArgs a{};
+  a.dtype = GLANCE_BF16;
+  a.q = base + w.off_q;
+  a.k_cache = at->k_cache;
+  a.v_cache = at->v_cache;
+  a.kv_offsets = kv_offsets;
+  a.depth = depth;
+  a.anc = anc;
+  a.token = token;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.n_pos = n_pos;
+  a.nseq = nseq;
+  a.n_rows = n_rows;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.max_prefix = max_prefix;
+  a.split = w.split;
+  a.n_split = w.n_split;
+  a.part = reinterpret_cast<float*>(base + w.off_part);
+  a.attn_out = attn_out;
+  a.attn_x = base + w.off_x;
+  a.tree_k = tree_k;
+  a.tree_v = tree_v;
+  st = launch_tree_attention(a, hs);
+  if (st != GLANCE_OK) return st;
+
+  // 5. h1 = h + attn Wo^T
+  GemmArgs o{};
+  o.x = base + w.off_x;
+  o.w.w[0] = at->wo;
+  o.w.n_end[0] = d_model;
+  o.w.nseg = 1;
+  o.M = R;
+  o.N = d_model;
+  o.K = qd;
+  o.epi = EPI_RESID;
+  o.resid = h0;
+  o.resid_tok = token;
+  o.resid_by_token = embed != nullptr;
+  o.out_res = h1;
+  o.kpart = kpart;
+  o.kcnt = kcnt;
+  st = launch_gemm_bf16(o, hs);
+  if (st != GLANCE_OK) return st;
+
+  // 6. x2 = RMSNorm(h1) g_mlp; 7. act = silu(x2 Wg^T) * (x2 Wu^T); 8. h' = h1 + act Wd^T
+  st = launch_rmsnorm(h1, nullptr, token, R, d_model, layer->g_mlp, layer->eps, xn, hs);
+  if (st != GLANCE_OK) return st;
+  GemmArgs gu{};
+  gu.x = xn;
+  gu.w.w[0] = layer->w_gate;
+  gu.w.w[1] = layer->w_up;
+  gu.w.n_end[0] = inter;
+  gu.w.n_end[1] = 2 * inter;
+  gu.w.nseg = 2;
+  gu.M = R;
+  gu.N = 2 * inter;
+  gu.K = d_model;
+  gu.epi = EPI_SWIGLU;
+  gu.out_res = act;
+  gu.kpart = kpart;
+  gu.kcnt = kcnt;
+  st = launch_gemm_bf16(gu, hs);
+  if (st != GLANCE_OK) return st;
+  GemmArgs dn{};
+  dn.x = act;
+  dn.w.w[0] = layer->w_down;
+  dn.w.n_end[0] = d_model;
+  dn.w.nseg = 1;
+  dn.M = R;
+  dn.N = d_model;
+  dn.K = inter;
+  dn.epi = EPI_RESID;
+  dn.resid = h1;
+  dn.resid_tok = token;
+  dn.resid_by_token = false;
+  dn.out_res = h_out;
+  dn.kpart = kpart;
+  dn.kcnt = kcnt;
+  return launch_gemm_bf16(dn, hs);
 }
 
 // ------------------------------------------------------------------- step 4

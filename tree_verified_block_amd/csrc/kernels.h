@@ -37,7 +37,9 @@ struct GemmSeg {
   int n_end[3];  // cumulative row counts
   int nseg;
 };
-enum GemmEpi { EPI_STORE_F32 = 0, EPI_RESID = 1, EPI_HEAD = 2, EPI_QKV = 3 };
+// EPI_SWIGLU (bf16): W = [W_gate; W_up] (two segments of N/2 rows); the output
+// out_res [M][N/2] is silu(x W_gate^T) * (x W_up^T) rounded to bf16.
+enum GemmEpi { EPI_STORE_F32 = 0, EPI_RESID = 1, EPI_HEAD = 2, EPI_QKV = 3, EPI_SWIGLU = 4 };
 struct GemmArgs {
   const void* x;          // [M][K]
   const int32_t* gather;  // NULL or [M] token ids (row m of X = x[gather[m]], -1 = zero row)
@@ -134,6 +136,17 @@ struct AttnArgs {
 int attn_split_len(int64_t max_prefix, int nseq, int Hkv);
 size_t attn_part_floats(int nseq, int n_rows, int Hq, int Hkv, int D, int n_split);
 glance_status launch_tree_attention(const AttnArgs& a, hipStream_t st);
+
+// ----------------------------------------------------------------- layer.hip
+// out[m] = bf16(RMSNorm(x[gather ? gather[m] : m]) * g); rows with token[m] < 0 -> 0
+glance_status launch_rmsnorm(const void* x, const int32_t* gather, const int32_t* token, int M,
+                             int d, const void* g, float eps, void* out, hipStream_t st);
+// fp32 q/k/v [R][(Hq + 2 Hkv) 128] -> head-normalised, rotated bf16 q, k and bf16 v
+glance_status launch_qkv_finish(const float* qkv, int R, int Hq, int Hkv, const void* g_q,
+                                const void* g_k, float eps, const int64_t* kv_offsets,
+                                const int32_t* depth, int n_rows, const float* rope_cos,
+                                const float* rope_sin, int n_pos, void* q_out, void* k_out,
+                                void* v_out, hipStream_t st);
 
 // ------------------------------------------------------------------ walk.hip
 glance_status launch_accept_walk(const int32_t* parent, const int32_t* token,

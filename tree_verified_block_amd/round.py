@@ -101,8 +101,13 @@ class DeviceRound:
         self.path_rows = torch.empty((self.nseq, self.L + 1), dtype=torch.int32, device=device)
         self.flagged = torch.empty(self.nseq, dtype=torch.int32, device=device)
         self.ws_tree = api.workspace(api.build_tree_ws_bytes(self.nseq, self.L, self.V, self.N), device)
-        self.ws_attn = api.workspace(api.tree_attn_ws_bytes(self.nseq, self.n_rows, self.max_prefix, d,
-                                                            cfg.Hq, cfg.Hkv, cfg.D), device)
+        self.full = getattr(cfg, "mlp", 0) > 0
+        if self.full:
+            self.ws_attn = api.workspace(api.tree_layer_ws_bytes(self.nseq, self.n_rows, self.max_prefix,
+                                                                 d, cfg.Hq, cfg.Hkv, cfg.D, cfg.mlp), device)
+        else:
+            self.ws_attn = api.workspace(api.tree_attn_ws_bytes(self.nseq, self.n_rows, self.max_prefix, d,
+                                                                cfg.Hq, cfg.Hkv, cfg.D), device)
         self.ws_head = api.workspace(api.verify_head_ws_bytes(self.R, self.V, d, self.dt), device)
         self.draft = None
         self.root = None
@@ -132,6 +137,18 @@ class DeviceRound:
         for li, lw in enumerate(self.layers):
             h_in = None if li == 0 else self.h[(li - 1) % 2]
             h_out = self.h[li % 2]
+            if self.full:
+                api.glance_tree_layer(lw, cfg.norm_eps, self.embed if li == 0 else None, t["token"],
+                                      h_in, h_out, self.kv_offsets, self.max_prefix, t["depth"],
+                                      t["anc"], self.rope_cos, self.rope_sin, self.nseq, self.n_rows,
+                                      cfg.d_model, cfg.Hq, cfg.Hkv, cfg.D, self.ws_attn,
+                                      attn_out=self.attn_out[li] if self.keep_layers else None,
+                                      tree_k=self.tree_ks[min(li, len(self.tree_ks) - 1)],
+                                      tree_v=self.tree_vs[min(li, len(self.tree_vs) - 1)],
+                                      stream=stream)
+                if self.keep_layers:
+                    self.h_layers[li].copy_(h_out)
+                continue
             api.glance_tree_attn(lw, self.dt, self.embed if li == 0 else None, t["token"], h_in,
                                  h_out, self.kv_offsets, self.max_prefix, t["depth"], t["anc"],
                                  self.rope_cos, self.rope_sin, self.nseq, self.n_rows,
