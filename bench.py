@@ -215,6 +215,50 @@ def shared_measure(K: int, seed: int = 4, budget_per_seq: int = 31, n_max: int =
     return res
 
 
+def full_layer_measure(K: int, seed: int = 2000, deep: int = 36) -> dict:
+    """Rounds of the 8B-shaped workload with full decoder layers (RMSNorm,
+    QK-norm, SwiGLU MLP with intermediate 12288): one layer, and a stack of
+    `deep` layers whose weights and caches are copies of that layer's (every
+    layer still streams its own 386 MB of weights from HBM), with the packed
+    head; HIP events around each round."""
+    import torch
+    from synth import gen_round, make_config
+    from tree_verified_block_amd.round import DeviceRound, to_device
+    cfg = make_config("qwen8b_full")
+    inp = gen_round(cfg, seed)
+    drafts = [to_device(rd["draft_logits"], cfg.dtype, "cuda") for rd in inp["rounds"]]
+    lw = inp["layers"][0]
+    layer_bytes = sum(lw[k].nbytes for k in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"))
+    res = {"workload": f"qwen8b_full: d_model {cfg.d_model}, {cfg.Hq}q/{cfg.Hkv}kv heads x {cfg.D}, "
+                       f"MLP {cfg.mlp}, V {cfg.V}, L {cfg.L}, N {cfg.N}, prefix 1024",
+           "layer_weight_bytes": layer_bytes}
+    stream = torch.cuda.current_stream()
+    for n_layers in (1, deep):
+        sub = dict(inp)
+        sub["cfg"] = cfg.replace(n_layers=n_layers)
+        sub["layers"] = [lw] * n_layers
+        dev = DeviceRound(sub, device="cuda", packed_head=True)
+        dev.set_round(0)
+        for i in range(3):
+            dev.draft = drafts[i % len(drafts)]
+            dev.run()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for i, e in enumerate(ev):
+            dev.draft = drafts[i % len(drafts)]
+            e[0].record(stream)
+            dev.run()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        nbytes = n_layers * layer_bytes + cfg.V * cfg.d_model * 2
+        res[f"layers_{n_layers}"] = {"rounds_per_s": round(1e3 / ms, 1), "ms_per_round": round(ms, 4),
+                                     "weight_bytes": nbytes,
+                                     "hbm_frac": round(nbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)}
+        del dev
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,6 +273,8 @@ def main():
                     help="verify rounds that sample at T = 1 to time; 0 skips")
     ap.add_argument("--shared-calls", type=int, default=50,
                     help="shared-budget tree builds of an 8-sequence batch to time; 0 skips")
+    ap.add_argument("--full-rounds", type=int, default=20,
+                    help="rounds of the full-layer workload (1 and 36 layers) to time; 0 skips")
     ap.add_argument("--row-major-head", action="store_true",
                     help="LM head over the row-major weights instead of the packed copy")
     ap.add_argument("--probe-copy", action="store_true",
@@ -340,6 +386,8 @@ def main():
         out["chain"] = chain_measure(inp, cfg, drafts, args.chain_rounds, packed=packed)
     if args.shared_calls > 0:
         out["shared_budget"] = shared_measure(args.shared_calls, oracle=not args.no_cpu_baseline)
+    if args.full_rounds > 0:
+        out["full_layer"] = full_layer_measure(args.full_rounds)
     if args.probe_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)

@@ -216,6 +216,8 @@ typedef struct {
   const void* w_down;
   int32_t inter;
   float eps;
+  const void* mlp_packed; /* NULL, or w_gate/w_up/w_down as glance_mlp_pack wrote
+                             them (then those three are not read)         */
 } glance_full_layer;
 
 glance_status glance_tree_layer(const glance_full_layer* layer, const void* embed,
@@ -228,6 +230,20 @@ glance_status glance_tree_layer(const glance_full_layer* layer, const void* embe
 
 size_t glance_tree_layer_ws(int32_t nseq, int32_t n_rows, int64_t max_prefix, int32_t d_model,
                             int32_t Hq, int32_t Hkv, int32_t D, int32_t inter);
+
+/* glance_mlp_pack: the MLP weights of a full layer copied once, at load time,
+ * into the projection kernel's tile order: for every 64-deep chunk of the input
+ * and every block of 16 output rows (gate rows 8b..8b+7 with the matching up
+ * rows for the gate/up projection), the 16 x 64 tile laid out as the
+ * matrix-core operand, so that each weight load is a contiguous kilobyte.
+ * Gate/up first, then w_down at the next 256-byte boundary; size from
+ * glance_mlp_pack_bytes (0 if unsupported).  Results with the packed copy are
+ * identical to those with the row-major weights.  Limits: d_model and inter
+ * multiples of 256.
+ */
+size_t glance_mlp_pack_bytes(int32_t d_model, int32_t inter);
+glance_status glance_mlp_pack(const void* w_gate, const void* w_up, const void* w_down,
+                              int32_t d_model, int32_t inter, void* packed, void* stream);
 
 /* -------------------------------------------------------------------- step 4 --
  * glance_verify_head: LM head of the verify rows with a fused row epilogue.

@@ -201,6 +201,15 @@ def test_tree_layer_rejects_bad_arguments(lib):
     assert call(ws_bytes=1000) == -3
 
 
+def test_mlp_pack_rejects_bad_arguments(lib):
+    p = OK_PTR
+    assert lib.glance_mlp_pack_bytes(4096, 12288) >= 3 * 4096 * 12288 * 2
+    assert lib.glance_mlp_pack_bytes(4096, 1000) == 0
+    assert lib.glance_mlp_pack(p, p, p, 4096, 1000, p, None) == -4
+    assert lib.glance_mlp_pack(None, p, p, 4096, 12288, p, None) == -1
+    assert lib.glance_mlp_pack(p, p, p, 4096, 12288, p + 8, None) == -2
+
+
 def test_tree_attn_rejects_bad_arguments(lib):
     assert _attn(lib, n_rows=65) == -1
     assert _attn(lib, Hq=30) == -1            # not a multiple of Hkv

@@ -103,11 +103,12 @@ def test_packed_head_sampled_equals_row_major():
     ("mini_bf16", 1, {}),
     ("mini_bf16_ragged", 9, dict(draft="topology", n_layers=3, nseq=2, N=63, L=15)),
     ("qwen8b_1layer", 2000, {}),
+    ("mini_bf16_full", 3, {}),
 ])
 def test_packed_round_equals_row_major(name, seed, kw):
-    """A whole round with the packed head weights: every output equals the
-    row-major round's (tree, hidden rows, new cache entries, head statistics,
-    walk)."""
+    """A whole round with the packed head weights (and, for full layers, the
+    packed MLP weights): every output equals the row-major round's (tree, hidden
+    rows, new cache entries, head statistics, walk)."""
     from synth import gen_round, make_config
     from tree_verified_block_amd.round import DeviceRound
     inp = gen_round(make_config(name, **kw), seed)

@@ -32,7 +32,8 @@ class GlanceAttnLayer(ctypes.Structure):
 
 class GlanceFullLayer(ctypes.Structure):
     _fields_ = [("attn", GlanceAttnLayer), ("g_attn", _P), ("g_q", _P), ("g_k", _P), ("g_mlp", _P),
-                ("w_gate", _P), ("w_up", _P), ("w_down", _P), ("inter", _I), ("eps", _F)]
+                ("w_gate", _P), ("w_up", _P), ("w_down", _P), ("inter", _I), ("eps", _F),
+                ("mlp_packed", _P)]
 
 
 # name -> (restype, argtypes), exactly the declarations of include/glance.h
@@ -48,6 +49,8 @@ SIGNATURES = {
     "glance_tree_layer": (_I, [ctypes.POINTER(GlanceFullLayer), _P, _P, _P, _P, _P, _I64, _P, _P,
                                _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "glance_tree_layer_ws": (_SZ, [_I, _I, _I64, _I, _I, _I, _I, _I]),
+    "glance_mlp_pack_bytes": (_SZ, [_I, _I]),
+    "glance_mlp_pack": (_I, [_P, _P, _P, _I, _I, _P, _P]),
     "glance_verify_head": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "glance_verify_head_ws": (_SZ, [_I, _I, _I, _I]),
     "glance_verify_head_sampled": (_I, [_P, _P, _I, _I, _I, _I, _F, _U64, _U64, _P, _P, _P, _P,

@@ -111,12 +111,26 @@ def glance_tree_layer(layer: dict, eps: float, embed, token, h_in, h_out, kv_off
                            _ptr(layer["wo"]), _ptr(layer["k_cache"]), _ptr(layer["v_cache"]))
     full = GlanceFullLayer(attn, _ptr(layer["g_attn"]), _ptr(layer["g_q"]), _ptr(layer["g_k"]),
                            _ptr(layer["g_mlp"]), _ptr(layer["w_gate"]), _ptr(layer["w_up"]),
-                           _ptr(layer["w_down"]), layer["w_gate"].shape[0], float(eps))
+                           _ptr(layer["w_down"]), layer["w_gate"].shape[0], float(eps),
+                           _ptr(layer.get("mlp_packed")))
     _lib.call("glance_tree_layer", ctypes.byref(full), _ptr(embed), _ptr(token), _ptr(h_in),
               _ptr(h_out), _ptr(kv_offsets), int(max_prefix), _ptr(depth), _ptr(anc),
               _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], nseq, n_rows, d_model, Hq, Hkv,
               D, _ptr(attn_out), _ptr(tree_k), _ptr(tree_v), _ptr(ws), ws.numel(),
               _stream(stream))
+
+
+def glance_mlp_pack(layer: dict, stream=None):
+    """bf16 MLP weights of a full layer -> the projection kernel's packed tile
+    order (a new uint8 device tensor; done once, when the weights are loaded)."""
+    inter, d_model = layer["w_gate"].shape
+    n = _lib.load().glance_mlp_pack_bytes(d_model, inter)
+    if n == 0:
+        raise ValueError(f"no packed layout for d_model={d_model}, inter={inter}")
+    out = torch.empty(n, dtype=torch.uint8, device=layer["w_gate"].device)
+    _lib.call("glance_mlp_pack", _ptr(layer["w_gate"]), _ptr(layer["w_up"]), _ptr(layer["w_down"]),
+              d_model, inter, _ptr(out), _stream(stream))
+    return out
 
 
 # ---------------------------------------------------------------------- step 4

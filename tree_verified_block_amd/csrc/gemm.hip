@@ -643,9 +643,24 @@ __global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int
   const int kbase = q * Ks;
   const int nck = Ks / kKc;
 
-  int row = bv ? block_row<EPI>(a, b, lr) : 0;
-  if (row > a.N - 1) row = a.N - 1;
-  const uint16_t* wp = w_row_ptr(a, row) + kbase + 8 * lg;
+  // weight operand of chunk c, half i: wb + c * wcs + i * whs (bytes).  Row-major
+  // W: row block_row(b, l%16), columns 64 c + 32 i + 8 (l/16); packed W (see
+  // proj_pack_kernel): the same 16 bytes, each half a contiguous kilobyte.
+  const char* wb;
+  size_t wcs, whs;
+  if (a.w_packed) {
+    const int bc = bv ? b : NB - 1;
+    wb = static_cast<const char*>(a.w_packed) +
+         ((static_cast<size_t>(kbase / kKc) * NB + bc) * 128 + l) * 16;
+    wcs = static_cast<size_t>(NB) * 2048;
+    whs = 1024;
+  } else {
+    int row = bv ? block_row<EPI>(a, b, lr) : 0;
+    if (row > a.N - 1) row = a.N - 1;
+    wb = reinterpret_cast<const char*>(w_row_ptr(a, row) + kbase + 8 * lg);
+    wcs = kKc * 2;
+    whs = 64;
+  }
   const uint16_t* xr[2];
   uint32_t xm[2];
   int xlds[2];
@@ -667,7 +682,7 @@ __global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int
   uint4 xbuf[RS][2];
   auto wload = [&](int c, uint4 (&dst)[2]) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dst[i] = *reinterpret_cast<const uint4*>(wp + c * kKc + 32 * i);
+    for (int i = 0; i < 2; ++i) dst[i] = *reinterpret_cast<const uint4*>(wb + c * wcs + i * whs);
   };
   // raw loads; the row mask is applied when the chunk is written to LDS
   auto xload = [&](int c, uint4 (&dst)[2]) {
@@ -933,7 +948,42 @@ __global__ __launch_bounds__(256) void head_pack_kernel(const uint16_t* __restri
 }
 }  // namespace
 
+// Packed projection weights: [K/64 chunks][NB blocks][2 halves][64 lanes] x 16
+// bytes; lane l of half s of block b holds row block_row(b, l%16), columns
+// 64 c + 32 s + 8 (l/16) .. + 8 (the MFMA operand of that block and chunk).
+template <int EPI>
+__global__ __launch_bounds__(256) void proj_pack_kernel(GemmArgs a, int NB, size_t n16,
+                                                        uint4* __restrict__ out) {
+  for (size_t o = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; o < n16;
+       o += static_cast<size_t>(gridDim.x) * 256) {
+    const int l = static_cast<int>(o & 63), s = static_cast<int>((o >> 6) & 1);
+    const size_t rest = o >> 7;
+    const int b = static_cast<int>(rest % NB);
+    const int c = static_cast<int>(rest / NB);
+    const int row = block_row<EPI>(a, b, l & 15);
+    const int col = c * kKc + 32 * s + 8 * (l >> 4);
+    out[o] = *reinterpret_cast<const uint4*>(w_row_ptr(a, row) + col);
+  }
+}
+
 int gemm_bf16_head_parts(int N) { return head_grid(N).nWG; }
+
+size_t proj_pack_bytes(int N, int K) {
+  return static_cast<size_t>(K / kKc) * ((N + 15) / 16) * 2048;
+}
+
+glance_status launch_proj_pack(const GemmArgs& a, void* w_packed, hipStream_t st) {
+  const int NB = proj_blocks(a);
+  const size_t n16 = proj_pack_bytes(a.N, a.K) / 16;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (a.epi == EPI_SWIGLU)
+    proj_pack_kernel<EPI_SWIGLU><<<static_cast<unsigned>(blocks), 256, 0, st>>>(a, NB, n16, static_cast<uint4*>(w_packed));
+  else
+    proj_pack_kernel<EPI_RESID><<<static_cast<unsigned>(blocks), 256, 0, st>>>(a, NB, n16, static_cast<uint4*>(w_packed));
+  GLANCE_LAUNCH_CHECK();
+  return GLANCE_OK;
+}
 
 size_t head_pack_bytes(int N, int K) {
   const HeadGrid g = head_grid(N);

@@ -416,9 +416,13 @@ glance_status glance_tree_layer(const glance_full_layer* layer, const void* embe
   REQUIRE_PTR(layer->g_q);
   REQUIRE_PTR(layer->g_k);
   REQUIRE_PTR(layer->g_mlp);
-  REQUIRE_PTR(layer->w_gate);
-  REQUIRE_PTR(layer->w_up);
-  REQUIRE_PTR(layer->w_down);
+  if (layer->mlp_packed) {
+    REQUIRE_PTR(layer->mlp_packed);
+  } else {
+    REQUIRE_PTR(layer->w_gate);
+    REQUIRE_PTR(layer->w_up);
+    REQUIRE_PTR(layer->w_down);
+  }
   REQUIRE_ALIGNED_OR_NULL(embed);
   REQUIRE_ALIGNED_OR_NULL(h_in);
   REQUIRE_PTR(token);
@@ -536,6 +540,7 @@ glance_status glance_tree_layer(const glance_full_layer* layer, const void* embe
   gu.N = 2 * inter;
   gu.K = d_model;
   gu.epi = EPI_SWIGLU;
+  gu.w_packed = layer->mlp_packed;
   gu.out_res = act;
   gu.kpart = kpart;
   gu.kcnt = kcnt;
@@ -556,7 +561,46 @@ glance_status glance_tree_layer(const glance_full_layer* layer, const void* embe
   dn.out_res = h_out;
   dn.kpart = kpart;
   dn.kcnt = kcnt;
+  if (layer->mlp_packed)
+    dn.w_packed = static_cast<const char*>(layer->mlp_packed) + round256(proj_pack_bytes(2 * inter, d_model));
   return launch_gemm_bf16(dn, hs);
+}
+
+size_t glance_mlp_pack_bytes(int32_t d_model, int32_t inter) {
+  if (d_model < 256 || d_model % 256 != 0 || inter < 256 || inter % 256 != 0) return 0;
+  return round256(proj_pack_bytes(2 * inter, d_model)) + proj_pack_bytes(d_model, inter);
+}
+
+glance_status glance_mlp_pack(const void* w_gate, const void* w_up, const void* w_down,
+                              int32_t d_model, int32_t inter, void* packed, void* stream) {
+  g_last_error.clear();
+  if (glance_mlp_pack_bytes(d_model, inter) == 0)
+    return fail(GLANCE_ERR_UNSUPPORTED, "packed MLP needs d_model and inter multiples of 256 (got %d, %d)",
+                d_model, inter);
+  REQUIRE_PTR(w_gate);
+  REQUIRE_PTR(w_up);
+  REQUIRE_PTR(w_down);
+  REQUIRE_PTR(packed);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  GemmArgs gu{};
+  gu.w.w[0] = w_gate;
+  gu.w.w[1] = w_up;
+  gu.w.n_end[0] = inter;
+  gu.w.n_end[1] = 2 * inter;
+  gu.w.nseg = 2;
+  gu.N = 2 * inter;
+  gu.K = d_model;
+  gu.epi = EPI_SWIGLU;
+  glance_status st = launch_proj_pack(gu, packed, hs);
+  if (st != GLANCE_OK) return st;
+  GemmArgs dn{};
+  dn.w.w[0] = w_down;
+  dn.w.n_end[0] = d_model;
+  dn.w.nseg = 1;
+  dn.N = d_model;
+  dn.K = inter;
+  dn.epi = EPI_RESID;
+  return launch_proj_pack(dn, static_cast<char*>(packed) + round256(proj_pack_bytes(gu.N, d_model)), hs);
 }
 
 // ------------------------------------------------------------------- step 4

@@ -51,8 +51,8 @@ struct GemmArgs {
   const int32_t* resid_tok;  // EPI_RESID: [M] token ids; rows with token < 0 are written as 0
   bool resid_by_token;     // residual row m is resid[resid_tok[m]] (else resid[m])
   void* out_res;           // EPI_RESID: [M][N] in the storage dtype
-  // EPI_HEAD, bf16: W in the head's packed tile order (see head_pack_layout), or
-  // null for row-major W
+  // bf16: W in the kernel's packed tile order (glance_head_pack for the head,
+  // glance_mlp_pack for the MLP projections), or null for row-major W
   const void* w_packed;
   float* part;             // EPI_HEAD: [M][n_part] partial statistics (5 floats)
   float* logits;           // EPI_HEAD: optional [M][N]
@@ -84,6 +84,10 @@ int gemm_bf16_head_parts(int N);
 // packing kernel (row-major [N][K] -> packed tile order).
 size_t head_pack_bytes(int N, int K);
 glance_status launch_head_pack(const void* w, int N, int K, void* w_packed, hipStream_t st);
+// Bytes of a packed projection weight (N output rows of K, bf16) and its packing
+// kernel (in the block order of a.epi: EPI_SWIGLU pairs gate and up rows).
+size_t proj_pack_bytes(int N, int K);
+glance_status launch_proj_pack(const GemmArgs& a, void* w_packed, hipStream_t st);
 glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
 // Scratch of the bf16 projections: number of 16-row weight blocks, K-split,
 // partial floats and arrival counters for M activation rows.
