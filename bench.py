@@ -275,6 +275,8 @@ def main():
                     help="shared-budget tree builds of an 8-sequence batch to time; 0 skips")
     ap.add_argument("--full-rounds", type=int, default=20,
                     help="rounds of the full-layer workload (1 and 36 layers) to time; 0 skips")
+    ap.add_argument("--skip-main", action="store_true",
+                    help="run only the extra legs (shared budget, full layers) and print them")
     ap.add_argument("--row-major-head", action="store_true",
                     help="LM head over the row-major weights instead of the packed copy")
     ap.add_argument("--probe-copy", action="store_true",
@@ -285,6 +287,14 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.skip_main:
+        out = {}
+        if args.shared_calls > 0:
+            out["shared_budget"] = shared_measure(args.shared_calls, oracle=not args.no_cpu_baseline)
+        if args.full_rounds > 0:
+            out["full_layer"] = full_layer_measure(args.full_rounds)
+        print(json.dumps(out), flush=True)
+        return
     from synth import gen_round, make_config
     from tree_verified_block_amd.round import DeviceRound, to_device
 
