@@ -1007,6 +1007,7 @@ int proj_ksplit(int K, int NB) {
   const int NGr = (NB + 3) / 4;
   int target = 256 / NGr;
   if (target < 1) target = 1;
+  if (NGr > 256) target = 2;  // wide projections (MLP): two slices, up to 3 work-groups per CU
   int S = 1;
   for (int c = 1; c <= nch / 2; ++c)
     if ((nch / 2) % c == 0 && c <= target) S = c;
