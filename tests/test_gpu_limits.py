@@ -1,0 +1,73 @@
+"""Steps 1-2 at the limits the C ABI documents: L = GLANCE_MAX_L (16) offsets,
+vocabularies of 2^18 (bf16) and 2^17 (fp32) logits, N + 1 = GLANCE_MAX_ROWS
+rows, and a shared-budget batch of GLANCE_MAX_SHARED (16) sequences; every tree
+against the oracle's exact tree (exact layout unless its boundary is a
+near-tie)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import round as orr, shared as sh
+from synth import gen_round, make_config
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _build(drafts, dtype, roots, N):
+    from tree_verified_block_amd import api
+    from tree_verified_block_amd.round import to_device
+    nseq, L, V = drafts.shape
+    out = api.tree_outputs(nseq, N, "cuda")
+    ws = api.workspace(api.build_tree_ws_bytes(nseq, L, V, N), "cuda")
+    api.glance_build_tree(to_device(drafts, dtype, "cuda"),
+                          torch.tensor(np.asarray(roots, np.int32), device="cuda"), N, out, ws)
+    torch.cuda.synchronize()
+    res = {k: v.cpu().numpy() for k, v in out.items()}
+    res["anc"] = res["anc"].view(np.uint64)
+    return res
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype,V,draft", [("bf16", 1 << 18, "mixed"), ("f32", 1 << 17, "scaled")])
+def test_tree_at_the_size_limits(dtype, V, draft):
+    cfg = make_config("mini_bf16", dtype=dtype, V=V, L=16, N=63, nseq=2, draft=draft)
+    inp = gen_round(cfg, 17, with_model=False)
+    rd = inp["rounds"][0]
+    gpu = _build(rd["draft_logits"], dtype, rd["root"], cfg.N)
+    report = {}
+    for s in range(cfg.nseq):
+        ot = orr.build_tree(rd["draft_logits"][s], dtype, int(rd["root"][s]), cfg.N)
+        parity.check_tree(gpu, s, ot, ot["logq"], cfg.N, cfg.L, report)
+        assert int(gpu["depth"][s].max()) <= 16
+    print(f"[limits] {dtype} V={V} L=16: {report}", flush=True)
+
+
+@pytest.mark.timeout(300)
+def test_shared_budget_with_the_most_sequences():
+    from tree_verified_block_amd import api
+    from tree_verified_block_amd.round import to_device
+    cfg = make_config("mini_bf16", V=4099, L=8, nseq=16, draft="mixed")
+    inp = gen_round(cfg, 18, with_model=False)
+    rd = inp["rounds"][0]
+    w = np.random.default_rng(18).normal(0.0, 1.0, 16).astype(np.float32)
+    B, n_max = 16 * 20, 63
+    out = api.tree_outputs(16, n_max, "cuda")
+    ws = api.workspace(api.build_tree_ws_bytes(16, cfg.L, cfg.V, n_max), "cuda")
+    api.glance_build_tree_shared(to_device(rd["draft_logits"], cfg.dtype, "cuda"),
+                                 torch.tensor(rd["root"].astype(np.int32), device="cuda"),
+                                 torch.tensor(w, device="cuda"), n_max, B, out, ws)
+    torch.cuda.synchronize()
+    gpu = {k: v.cpu().numpy() for k, v in out.items()}
+    gpu["anc"] = gpu["anc"].view(np.uint64)
+    trees, n, gap, tm = sh.build_trees([rd["draft_logits"][s] for s in range(16)], cfg.dtype,
+                                       rd["root"], w.astype(np.float64), B, n_max)
+    got = gpu["n_valid"] - 1
+    assert got.sum() <= B
+    report = {}
+    if gap > parity.GAP:
+        assert got.tolist() == n.tolist()
+    for s in range(16):
+        if got[s] == n[s]:
+            parity.check_tree(gpu, s, trees[s], trees[s]["logq"], n_max, cfg.L, report)
+    print(f"[limits] shared 16 sequences: n={got.tolist()} gap={gap:.3g} {report}", flush=True)
