@@ -9,6 +9,7 @@ import torch
 
 from oracle import round as orr, shared as sh
 from synth import gen_round, make_config
+from synth.gen import bf16_bits, bf16_bits_to_f32
 from tests import parity
 
 pytestmark = pytest.mark.gpu
@@ -71,3 +72,32 @@ def test_shared_budget_with_the_most_sequences():
         if got[s] == n[s]:
             parity.check_tree(gpu, s, trees[s], trees[s]["logq"], n_max, cfg.L, report)
     print(f"[limits] shared 16 sequences: n={got.tolist()} gap={gap:.3g} {report}", flush=True)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype,V", [("bf16", 151936), ("f32", 1 << 17)])
+def test_tree_when_every_chunk_ends_in_ties(dtype, V):
+    """Rows of equal logits (0) with 100 spikes in [1, 7): the K best keys of
+    every chunk of a row end in a run of equal logits, ranked by token id (the
+    exact radix select), while each merged row keeps only spikes (in bf16 some
+    spikes are equal too, again ranked by token id)."""
+    rng = np.random.default_rng(19)
+    nseq, L, N = 2, 4, 63
+    z = np.zeros((nseq, L, V), np.float32)
+    for s in range(nseq):
+        for j in range(L):
+            z[s, j, rng.choice(V, 100, replace=False)] = rng.uniform(1.0, 7.0, 100)
+    if dtype == "bf16":   # the values the device sees
+        z = bf16_bits_to_f32(bf16_bits(z))
+    stored = z if dtype == "f32" else bf16_bits(z)
+    roots = np.array([3, 4], np.int64)
+    gpu = _build(stored, dtype, roots, N)
+    report = {}
+    for s in range(nseq):
+        ot = orr.build_tree(stored[s], dtype, int(roots[s]), N)
+        parity.check_tree(gpu, s, ot, ot["logq"], N, L, report)
+        # every node's token is one of its offset's spikes
+        nv = int(gpu["n_valid"][s])
+        for i in range(1, nv):
+            assert z[s, int(gpu["depth"][s][i]) - 1, int(gpu["token"][s][i])] >= 1.0
+    print(f"[limits] ties {dtype} V={V}: {report}", flush=True)

@@ -69,29 +69,6 @@ __device__ __forceinline__ int count_greater(const unsigned long long* a, int n,
   return rank;
 }
 
-// Ranks (numbers of larger keys) of two keys among n keys of an LDS array that
-// every lane reads in step (broadcast reads, 8 keys in flight).
-__device__ __forceinline__ void rank2(const unsigned long long* a, int n, unsigned long long x,
-                                      unsigned long long y, int& rx, int& ry) {
-  rx = 0;
-  ry = 0;
-  int o = 0;
-  for (; o + 8 <= n; o += 8) {
-    ulonglong2 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const ulonglong2*>(a + o + 2 * u);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      rx += (v[u].x > x ? 1 : 0) + (v[u].y > x ? 1 : 0);
-      ry += (v[u].x > y ? 1 : 0) + (v[u].y > y ? 1 : 0);
-    }
-  }
-  for (; o < n; ++o) {
-    rx += a[o] > x ? 1 : 0;
-    ry += a[o] > y ? 1 : 0;
-  }
-}
-
 __device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
   return a > b ? a : b;
 }
@@ -99,19 +76,75 @@ __device__ __forceinline__ unsigned long long umin64(unsigned long long a, unsig
   return a > b ? b : a;
 }
 
-// Descending sort of one wavefront's 64 keys (one per lane): bitonic network.
-__device__ __forceinline__ unsigned long long wave_sort_desc(unsigned long long key) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const unsigned long long o = __shfl_xor(key, j, kWave);
-      const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
-      key = keep_max ? umax64(key, o) : umin64(key, o);
-    }
+// Wave-wide float max and sum through DPP row shifts and row broadcasts: lane
+// 63 ends with the result over all 64 lanes (lanes that receive no source
+// combine with the identity), read back as a wave-uniform value.
+#define GLANCE_DPP_STEP(v, op, id, ctrl, rm) \
+  v = op(v, __int_as_float(__builtin_amdgcn_update_dpp(id, __float_as_int(v), ctrl, rm, 0xF, false)))
+__device__ __forceinline__ float fadd2(float a, float b) { return a + b; }
+__device__ __forceinline__ float wave_fmax_u(float v) {
+  constexpr int kNegInf = static_cast<int>(0xFF800000u);
+  GLANCE_DPP_STEP(v, fmaxf, kNegInf, 0x111, 0xF);
+  GLANCE_DPP_STEP(v, fmaxf, kNegInf, 0x112, 0xF);
+  GLANCE_DPP_STEP(v, fmaxf, kNegInf, 0x114, 0xF);
+  GLANCE_DPP_STEP(v, fmaxf, kNegInf, 0x118, 0xF);
+  GLANCE_DPP_STEP(v, fmaxf, kNegInf, 0x142, 0xA);
+  GLANCE_DPP_STEP(v, fmaxf, kNegInf, 0x143, 0xC);
+  return readlane_f(v, 63);
+}
+__device__ __forceinline__ float wave_fsum_u(float v) {
+  GLANCE_DPP_STEP(v, fadd2, 0, 0x111, 0xF);
+  GLANCE_DPP_STEP(v, fadd2, 0, 0x112, 0xF);
+  GLANCE_DPP_STEP(v, fadd2, 0, 0x114, 0xF);
+  GLANCE_DPP_STEP(v, fadd2, 0, 0x118, 0xF);
+  GLANCE_DPP_STEP(v, fadd2, 0, 0x142, 0xA);
+  GLANCE_DPP_STEP(v, fadd2, 0, 0x143, 0xC);
+  return readlane_f(v, 63);
+}
+#undef GLANCE_DPP_STEP
+
+// The value of lane (lane ^ J): DPP quad permutations for 1 and 2, a row
+// rotation by 8 for 8, a bit-mode swizzle (within 32 lanes) for 4 and 16, and
+// the half swap of the 32-lane permute for 32.
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  if constexpr (J == 1)
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false));
+  else if constexpr (J == 2)
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false));
+  else if constexpr (J == 8)
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xF, 0xF, false));
+  else if constexpr (J == 4 || J == 16)
+    return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), (J << 10) | 0x1F));
+  else {
+    static_assert(J == 32, "lane exchange distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return lane_id() < 32 ? r[1] : r[0];
   }
-  return key;
+}
+template <int J>
+__device__ __forceinline__ unsigned long long xor_lane64(unsigned long long v) {
+  const uint32_t lo = xor_lane<J>(static_cast<uint32_t>(v)), hi = xor_lane<J>(static_cast<uint32_t>(v >> 32));
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+template <int J>
+__device__ __forceinline__ unsigned long long cleave(unsigned long long v) {
+  const unsigned long long o = xor_lane64<J>(v);
+  return (lane_id() & J) ? umin64(v, o) : umax64(v, o);
+}
+
+// Top 64 of two descending 64-key lists, descending: lane l holds a = A[l] and
+// b = B[63 - l].  max(a, b) over the lanes is a bitonic sequence holding the 64
+// largest keys of A and B; six half-cleaner stages sort it.
+__device__ __forceinline__ unsigned long long merge_top64(unsigned long long a, unsigned long long b) {
+  unsigned long long v = umax64(a, b);
+  v = cleave<32>(v);
+  v = cleave<16>(v);
+  v = cleave<8>(v);
+  v = cleave<4>(v);
+  v = cleave<2>(v);
+  v = cleave<1>(v);
+  return v;
 }
 
 template <typename T>
@@ -125,11 +158,12 @@ __device__ __forceinline__ float load_logit<uint16_t>(const uint16_t* p) { retur
 // every load issued before any is used.  Publishes the chunk's maximum and sum
 // of exp(z - max) and its K best keys, sorted descending (0 where fewer exist),
 // with device-coherent stores.
-// Threshold: wave w sorts its 64 per-thread best keys and takes the k-th
-// largest, k = ceil(K/4); the minimum T over the four waves is a lower bound of
-// the chunk's K-th largest key (each wave holds k keys >= T).  Only keys >= T
-// (about K of them) are gathered to LDS and ranked exactly by counting; more
-// than kCap of them (massive ties) switches to an exact 8-bit radix select.
+// Threshold: each wave finds, on ballots, the largest 16-bit prefix that k =
+// ceil(K/4) of its per-thread best keys reach; the smallest over the four waves
+// is a lower bound of the chunk's K-th largest key (each wave holds k keys above
+// it).  Only the keys above it (about K of them) are gathered to LDS and ranked
+// exactly by counting; more than a wave's share of kCap of them (massive ties)
+// switches to an exact 8-bit radix select.
 template <typename T, int NV>
 __device__ __forceinline__ void chunk_topk(const T* __restrict__ logits, int L, int V, int N, int nch,
                                            unsigned long long* __restrict__ cstat,
@@ -138,7 +172,7 @@ __device__ __forceinline__ void chunk_topk(const T* __restrict__ logits, int L, 
   constexpr int E = 16 / sizeof(T);
   constexpr int IPT = NV * E;
   __shared__ unsigned long long sel[kSlots];
-  __shared__ unsigned long long wt[kChunkWaves];
+  __shared__ uint32_t wt[kChunkWaves];
   __shared__ int wcnt[kChunkWaves];
   __shared__ float red_m[kChunkWaves], red_s[kChunkWaves];
   __shared__ unsigned hist[256];
@@ -208,19 +242,28 @@ __device__ __forceinline__ void chunk_topk(const T* __restrict__ logits, int L, 
     for (int e = 0; e < IPT; ++e)
       if (ok[e]) s += __builtin_amdgcn_exp2f((z[e] - m) * 1.4426950408889634f);
   }
-  const unsigned long long best = bi >= 0 ? make_comp(bz, static_cast<uint32_t>(bi)) : 0ull;
-
-  const float wm = wave_max(m);
+  const float wm = wave_fmax_u(m);
   float part = (wm == -INFINITY || m == -INFINITY) ? 0.f : s * __builtin_amdgcn_exp2f((m - wm) * 1.4426950408889634f);
-  part = wave_sum(part);
-  // this wave's k-th largest best, k = ceil(K/4)
+  part = wave_fsum_u(part);
+  // this wave's threshold t: the largest value with zero low 16 bits that at
+  // least k = ceil(K/4) of the per-thread best keys (high 32 bits) reach, found
+  // bit by bit on ballots; the minimum T over the four waves is then reached by
+  // at least K keys of the chunk
   const int kw = (K + kChunkWaves - 1) / kChunkWaves;
-  const unsigned long long srt = wave_sort_desc(best);
+  const uint32_t kb = bi >= 0 ? float_key(bz) : 0u;
+  uint32_t t = 0u;
+  if (kw > 0) {
+#pragma unroll
+    for (int bit = 31; bit >= 16; --bit) {
+      const uint32_t c = t | (1u << bit);
+      if (__popcll(__ballot(kb >= c)) >= kw) t = c;
+    }
+  }
   if (lane == 0) {
     red_m[w] = wm;
     red_s[w] = part;
+    wt[w] = t;
   }
-  if (kw > 0 && lane == kw - 1) wt[w] = srt;
   if (tid < kSlots) sel[tid] = 0ull;
   __syncthreads();
   if (tid == 0) {
@@ -237,40 +280,53 @@ __device__ __forceinline__ void chunk_topk(const T* __restrict__ logits, int L, 
     if (tid < kSlots) __hip_atomic_store(out + tid, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  unsigned long long Tk = wt[0];
+  uint32_t thr = wt[0];
 #pragma unroll
-  for (int i = 1; i < kChunkWaves; ++i) Tk = umin64(Tk, wt[i]);
-  // (Tk == 0 when a wave holds fewer than k keys: every key is gathered)
-  // Slots: a wave-inclusive scan of the per-thread counts places each thread's
-  // keys after those of the lower lanes, the waves' totals after the lower waves.
-  int cnt = 0;
-#pragma unroll
-  for (int e = 0; e < IPT; ++e)
-    cnt += (ok[e] && make_comp(z[e], static_cast<uint32_t>(tok(e))) >= Tk) ? 1 : 0;
-  const int incl = wave_incl_sum(cnt);
-  if (lane == kWave - 1) wcnt[w] = incl;
-  __syncthreads();
-  int slot = incl - cnt, C = 0;
-#pragma unroll
-  for (int i = 0; i < kChunkWaves; ++i) {
-    slot += i < w ? wcnt[i] : 0;
-    C += wcnt[i];
-  }
+  for (int i = 1; i < kChunkWaves; ++i) thr = min(thr, wt[i]);
+  // Gather every key whose value reaches key_float(thr) (a superset of the keys
+  // with high part >= thr; thr = 0: every valid key) into this wave's region of
+  // the candidate array, at ballot offsets; a region that overflows sends the
+  // chunk to the radix select.
+  const float zT = thr == 0u ? -INFINITY : key_float(thr);
+  constexpr int RW = kCap / kChunkWaves;
+  unsigned long long* cw = cand + w * RW;
+  int run = 0;
 #pragma unroll
   for (int e = 0; e < IPT; ++e) {
-    if (ok[e]) {
-      const unsigned long long key = make_comp(z[e], static_cast<uint32_t>(tok(e)));
-      if (key >= Tk) {
-        if (slot < kCap) cand[slot] = key;
-        ++slot;
-      }
+    const bool pass = ok[e] && z[e] >= zT;
+    const unsigned long long mk = __ballot(pass);
+    if (mk != 0ull) {
+      const int pos = run + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                static_cast<uint32_t>(mk >> 32),
+                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mk), 0u)));
+      if (pass && pos < RW) cw[pos] = make_comp(z[e], static_cast<uint32_t>(tok(e)));
+      run += __popcll(mk);
     }
   }
+  if (lane == 0) wcnt[w] = run;
   __syncthreads();
-  if (C <= kCap) {
-    for (int e = tid; e < C; e += kChunkThreads) {
-      const unsigned long long k = cand[e];
-      const int rank = count_greater(cand, C, k);
+  int cn[kChunkWaves], C = 0;
+  bool over = false;
+#pragma unroll
+  for (int i = 0; i < kChunkWaves; ++i) {
+    cn[i] = wcnt[i];
+    over |= cn[i] > RW;
+    C += cn[i];
+  }
+  if (!over) {
+    // exact ranks by counting over the four regions
+    for (int x = tid; x < C; x += kChunkThreads) {
+      int r = 0, o = x;
+#pragma unroll
+      for (int i = 0; i < kChunkWaves - 1; ++i)
+        if (r == i && o >= cn[i]) {
+          o -= cn[i];
+          r = i + 1;
+        }
+      const unsigned long long k = cand[r * RW + o];
+      int rank = 0;
+#pragma unroll
+      for (int i = 0; i < kChunkWaves; ++i) rank += count_greater(cand + i * RW, cn[i], k);
       if (rank < K) sel[rank] = k;
     }
   } else {
@@ -339,23 +395,19 @@ __device__ __forceinline__ void chunk_topk(const T* __restrict__ logits, int L, 
 }
 
 // Phase 2, the last chunk of offset row `row` to finish: merge the row's chunk
-// lists into its K best tokens, ranked, with log q_j.  With k = ceil(K / nch),
-// the K-th largest of the lists' k leading entries, T, bounds the row's K-th
-// largest key from below (K keys >= T among them); the entries >= T, a prefix
-// of each list, are gathered and ranked exactly by counting.  Writes lq[row][64]
-// (log q in rank order, -inf past K) and tk[row][64] (token ids, -1 past K).
+// lists (each sorted descending, 0 past its end) into the row's K best tokens,
+// ranked, with log q_j(v) = (z_v - M) - ln S.  Wave w folds lists w, w + 4, ...
+// into a running top 64 held one key per lane (bitonic merges), then the four
+// waves' lists are merged pairwise.  Writes lq[row][64] (log q in rank order,
+// -inf past K) and tk[row][64] (token ids, -1 past K).
 __device__ __noinline__ void merge_row(const unsigned long long* __restrict__ cstat,
                                        const unsigned long long* __restrict__ clist, int nch,
                                        int row, int K, float* __restrict__ lq_out,
                                        int* __restrict__ tk_out, unsigned long long* buf) {
   __shared__ float s_lnS, s_M;
-  __shared__ unsigned long long s_thr;
-  __shared__ int wcnt[kChunkWaves];
-  __shared__ float lqr[kSlots];
-  __shared__ int tkr[kSlots];
   const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
-  unsigned long long* lead = buf;          // up to nch * k leading entries
-  unsigned long long* cs = buf + kCap / 2;  // up to nch * 64 candidates
+  unsigned long long* lists = buf;                          // [nch][64]
+  unsigned long long* part = buf + kMaxChunks * kSlots;     // [4][64] per-wave results
   constexpr int PER = kMaxChunks * kSlots / kChunkThreads;
   unsigned long long key[PER];
 #pragma unroll
@@ -378,58 +430,37 @@ __device__ __noinline__ void merge_row(const unsigned long long* __restrict__ cs
     if (lane == 0) {
       s_M = M;
       s_lnS = logf(t);
-      s_thr = 0ull;
     }
   }
-  if (tid < kSlots) {
-    lqr[tid] = -INFINITY;
-    tkr[tid] = -1;
-  }
-  const int kc = (K + nch - 1) / nch;
-  const int n1 = nch * kc;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int idx = tid + i * kChunkThreads, c = idx >> 6, en = idx & 63;
-    if (c < nch && en < kc) lead[c * kc + en] = key[i];
+    const int idx = tid + i * kChunkThreads;
+    if ((idx >> 6) < nch) lists[idx] = key[i];
   }
   __syncthreads();
-  for (int x = tid; x < n1; x += kChunkThreads) {
-    const unsigned long long v = lead[x];
-    if (v != 0ull && count_greater(lead, n1, v) == K - 1) s_thr = v;
+  unsigned long long v = w < nch ? lists[w * kSlots + lane] : 0ull;
+  for (int c = w + kChunkWaves; c < nch; c += kChunkWaves)
+    v = merge_top64(v, lists[c * kSlots + (kSlots - 1 - lane)]);
+  part[w * kSlots + lane] = v;
+  __syncthreads();
+  if (w < 2) {
+    v = merge_top64(v, part[(w + 2) * kSlots + (kSlots - 1 - lane)]);
+    part[w * kSlots + lane] = v;
   }
   __syncthreads();
-  const unsigned long long Tm = s_thr;  // 0 when fewer than K leading entries: take all
-  int cnt = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) cnt += (key[i] != 0ull && key[i] >= Tm) ? 1 : 0;
-  const int incl = wave_incl_sum(cnt);
-  if (lane == kWave - 1) wcnt[w] = incl;
-  __syncthreads();
-  int slot = incl - cnt, C = 0;
-#pragma unroll
-  for (int i = 0; i < kChunkWaves; ++i) {
-    slot += i < w ? wcnt[i] : 0;
-    C += wcnt[i];
-  }
-#pragma unroll
-  for (int i = 0; i < PER; ++i)
-    if (key[i] != 0ull && key[i] >= Tm) cs[slot++] = key[i];
-  __syncthreads();
-  const float M = s_M, lnS = s_lnS;
-  for (int x = tid; x < C; x += kChunkThreads) {
-    const unsigned long long v = cs[x];
-    const int r = count_greater(cs, C, v);
-    if (r < K) {
+  if (w == 0) {
+    v = merge_top64(v, part[kSlots + (kSlots - 1 - lane)]);
+    const float M = s_M, lnS = s_lnS;
+    float lq = -INFINITY;
+    int tk = -1;
+    if (lane < K && v != 0ull) {
       const float zz = key_float(static_cast<uint32_t>(v >> 32));
-      lqr[r] = (M == -INFINITY || zz == -INFINITY) ? -INFINITY : (zz - M) - lnS;
-      tkr[r] = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(v));
+      lq = (M == -INFINITY || zz == -INFINITY) ? -INFINITY : (zz - M) - lnS;
+      tk = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(v));
     }
-  }
-  __syncthreads();
-  if (tid < kSlots) {
-    __hip_atomic_store(lq_out + static_cast<size_t>(row) * kSlots + tid, lqr[tid], __ATOMIC_RELAXED,
+    __hip_atomic_store(lq_out + static_cast<size_t>(row) * kSlots + lane, lq, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(tk_out + static_cast<size_t>(row) * kSlots + tid, tkr[tid], __ATOMIC_RELAXED,
+    __hip_atomic_store(tk_out + static_cast<size_t>(row) * kSlots + lane, tk, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   }
 }
