@@ -133,6 +133,61 @@ __device__ __forceinline__ unsigned long long cleave(unsigned long long v) {
   return (lane_id() & J) ? umin64(v, o) : umax64(v, o);
 }
 
+// One step of the bitonic sorting network over the 64 lanes: blocks of size
+// K2 alternate direction (descending first), J is the exchange distance.
+template <int K2, int J>
+__device__ __forceinline__ unsigned long long bitonic_step(unsigned long long v) {
+  const unsigned long long o = xor_lane64<J>(v);
+  const int lane = lane_id();
+  const bool keep_max = ((lane & J) == 0) == ((lane & K2) == 0);
+  return keep_max ? umax64(v, o) : umin64(v, o);
+}
+
+// Descending sort of one key per lane (21 compare-exchange steps).
+__device__ __forceinline__ unsigned long long wave_sort64_desc(unsigned long long v) {
+  v = bitonic_step<2, 1>(v);
+  v = bitonic_step<4, 2>(v);
+  v = bitonic_step<4, 1>(v);
+  v = bitonic_step<8, 4>(v);
+  v = bitonic_step<8, 2>(v);
+  v = bitonic_step<8, 1>(v);
+  v = bitonic_step<16, 8>(v);
+  v = bitonic_step<16, 4>(v);
+  v = bitonic_step<16, 2>(v);
+  v = bitonic_step<16, 1>(v);
+  v = bitonic_step<32, 16>(v);
+  v = bitonic_step<32, 8>(v);
+  v = bitonic_step<32, 4>(v);
+  v = bitonic_step<32, 2>(v);
+  v = bitonic_step<32, 1>(v);
+  v = bitonic_step<64, 32>(v);
+  v = bitonic_step<64, 16>(v);
+  v = bitonic_step<64, 8>(v);
+  v = bitonic_step<64, 4>(v);
+  v = bitonic_step<64, 2>(v);
+  v = bitonic_step<64, 1>(v);
+  return v;
+}
+
+// z[e] for a lane-dependent e < N, by a binary tree of selects on the bits of e
+// (register arrays are never indexed dynamically).
+template <int N>
+__device__ __forceinline__ float select_elem(const float (&z)[N], int e) {
+  float t[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) t[k] = z[k];
+#pragma unroll
+  for (int bit = 0; bit < 7; ++bit) {
+    constexpr int one = 1;
+    const int step = one << bit;
+    if (step >= N) break;
+    const bool hi = ((e >> bit) & 1) != 0;
+#pragma unroll
+    for (int k = 0; k + step < N; k += 2 * step) t[k] = hi ? t[k + step] : t[k];
+  }
+  return t[0];
+}
+
 // Top 64 of two descending 64-key lists, descending: lane l holds a = A[l] and
 // b = B[63 - l].  max(a, b) over the lanes is a bitonic sequence holding the 64
 // largest keys of A and B; six half-cleaner stages sort it.
@@ -161,8 +216,10 @@ __device__ __forceinline__ float load_logit<uint16_t>(const uint16_t* p) { retur
 // Threshold: each wave finds, on ballots, the largest 16-bit prefix that k =
 // ceil(K/4) of its per-thread best keys reach; the smallest over the four waves
 // is a lower bound of the chunk's K-th largest key (each wave holds k keys above
-// it).  Only the keys above it (about K of them) are gathered to LDS and ranked
-// exactly by counting; more than a wave's share of kCap of them (massive ties)
+// it).  Only the keys above it (about K of them) are gathered to LDS.  When no
+// wave holds more than 64 of them, each wave sorts its keys (bitonic network)
+// and the four sorted lists are merged; otherwise they are ranked exactly by
+// counting, and more than a wave's share of kCap of them (massive ties)
 // switches to an exact 8-bit radix select.
 template <typename T, int NV>
 __device__ __forceinline__ void chunk_topk(const T* __restrict__ logits, int L, int V, int N, int nch,
@@ -290,30 +347,50 @@ __device__ __forceinline__ void chunk_topk(const T* __restrict__ logits, int L, 
   const float zT = thr == 0u ? -INFINITY : key_float(thr);
   constexpr int RW = kCap / kChunkWaves;
   unsigned long long* cw = cand + w * RW;
-  int run = 0;
+  // this thread's elements that reach zT as a bit mask, its slots from a wave
+  // prefix sum; only the set bits are visited
+  unsigned long long pm = 0ull;
 #pragma unroll
-  for (int e = 0; e < IPT; ++e) {
-    const bool pass = ok[e] && z[e] >= zT;
-    const unsigned long long mk = __ballot(pass);
-    if (mk != 0ull) {
-      const int pos = run + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
-                                static_cast<uint32_t>(mk >> 32),
-                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mk), 0u)));
-      if (pass && pos < RW) cw[pos] = make_comp(z[e], static_cast<uint32_t>(tok(e)));
-      run += __popcll(mk);
-    }
+  for (int e = 0; e < IPT; ++e)
+    if (ok[e] && z[e] >= zT) pm |= 1ull << e;
+  const int pc = __popcll(pm);
+  const int incl = wave_incl_sum(pc);
+  const int run = readlane_i(incl, kWave - 1);
+  int slot = incl - pc;
+  while (pm != 0ull) {
+    const int e = __builtin_ctzll(pm);
+    pm &= pm - 1ull;
+    if (slot < RW) cw[slot] = make_comp(select_elem(z, e), static_cast<uint32_t>(tok(e)));
+    ++slot;
   }
   if (lane == 0) wcnt[w] = run;
   __syncthreads();
   int cn[kChunkWaves], C = 0;
-  bool over = false;
+  bool over = false, small = true;
 #pragma unroll
   for (int i = 0; i < kChunkWaves; ++i) {
     cn[i] = wcnt[i];
     over |= cn[i] > RW;
+    small &= cn[i] <= kWave;
     C += cn[i];
   }
-  if (!over) {
+  if (small) {
+    // every wave sorts its candidates (one per lane); the four sorted lists are
+    // then merged pairwise
+    unsigned long long x = lane < cn[w] ? cw[lane] : 0ull;
+    x = wave_sort64_desc(x);
+    cw[lane] = x;
+    __syncthreads();
+    if (w < 2) {
+      x = merge_top64(x, cand[(w + 2) * RW + (kWave - 1 - lane)]);
+      cw[lane] = x;
+    }
+    __syncthreads();
+    if (w == 0) {
+      x = merge_top64(x, cand[RW + (kWave - 1 - lane)]);
+      sel[lane] = lane < K ? x : 0ull;
+    }
+  } else if (!over) {
     // exact ranks by counting over the four regions
     for (int x = tid; x < C; x += kChunkThreads) {
       int r = 0, o = x;
