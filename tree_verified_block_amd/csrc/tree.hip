@@ -103,20 +103,27 @@ __device__ __forceinline__ float wave_fsum_u(float v) {
 }
 #undef GLANCE_DPP_STEP
 
-// The value of lane (lane ^ J): DPP quad permutations for 1 and 2, a row
-// rotation by 8 for 8, a bit-mode swizzle (within 32 lanes) for 4 and 16, and
-// the half swap of the 32-lane permute for 32.
+// The value of lane (lane ^ J), on the vector ALU only: DPP quad permutations
+// for 1 and 2, row shifts by 4 (left for lanes with bit 2 clear, right
+// otherwise) for 4, a row rotation by 8 for 8, and the row-pair and half swaps
+// of the 16- and 32-lane permutes for 16 and 32.
 template <int J>
 __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  const int x = static_cast<int>(v);
   if constexpr (J == 1)
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false));
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
   else if constexpr (J == 2)
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false));
-  else if constexpr (J == 8)
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xF, 0xF, false));
-  else if constexpr (J == 4 || J == 16)
-    return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), (J << 10) | 0x1F));
-  else {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
+  else if constexpr (J == 4) {
+    const int up = __builtin_amdgcn_update_dpp(0, x, 0x104, 0xF, 0xF, false);    // row_shl:4
+    const int down = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    return static_cast<uint32_t>((lane_id() & 4) ? down : up);
+  } else if constexpr (J == 8)
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false));
+  else if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane_id() & 16) ? r[0] : r[1];
+  } else {
     static_assert(J == 32, "lane exchange distance");
     const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
     return lane_id() < 32 ? r[1] : r[0];
@@ -565,7 +572,9 @@ __device__ __forceinline__ int select_pops(const float (*lq)[kLqRow], const int 
   // scores give larger keys, -inf (no offer) gives 0, and the key maps back to
   // -|v| on the scalar unit.  Per iteration only the winner p and the new node
   // i change, from scalar values; every lane re-reads the log q after its
-  // offered child, so the read is issued one iteration ahead of its use.
+  // offered child and the first log q of the list below its offered child, so
+  // both reads are issued one iteration ahead of their use and the winner's
+  // two values come from two independent lane reads.
   // Lane state: st = depth << 16 | own rank << 8 | rank of the offered child.
   auto okey = [](float v) { return 0x7F800000u - (__float_as_uint(v) & 0x7FFFFFFFu); };
   const float fq = lane <= L ? lq[lane][0] : -INFINITY;  // first entry of each list
@@ -574,11 +583,12 @@ __device__ __forceinline__ int select_pops(const float (*lq)[kLqRow], const int 
   int n_par = -1;
   uint32_t c_hi = lane == 0 ? okey(fq) : 0u;
   float nx_q = lq[0][1];  // log q after the offered child (lane 0: the root's second child)
+  float fqn = lq[1][0];   // first log q below the offered child (lane 0: list 1)
   int n_pop = 0;
   uint32_t mh = N >= 1 ? wave_umax(c_hi) : 0u;
   for (int i = 1; mh != 0u;) {
     unsigned long long cm = __ballot(c_hi == mh);
-    if (__popcll(cm) > 1) {  // equal scores: the smallest depth, then the lowest lane
+    if (__builtin_expect((cm & (cm - 1ull)) != 0ull, 0)) {  // equal scores: the smallest depth, then the lowest lane
       const uint32_t lo = (c_hi == mh) ? ~static_cast<uint32_t>(st >> 16) : 0u;
       const uint32_t ml = wave_umax(lo);
       cm = __ballot(c_hi == mh && ~static_cast<uint32_t>(st >> 16) == ml);
@@ -588,7 +598,7 @@ __device__ __forceinline__ int select_pops(const float (*lq)[kLqRow], const int 
     const int dn = (w_st >> 16) + 1;                        // the new node's depth
     const int new_st = (dn << 16) | ((w_st & 255) << 8);    // its own rank, first child offered
     const float w_score = __uint_as_float((0x7F800000u - mh) | 0x80000000u);
-    const float q0 = readlane_f(fq, dn);
+    const float q0 = readlane_f(fqn, p);
     const bool isp = lane == p, isi = lane == i;
     st += isp ? 1 : 0;
     st = isi ? new_st : st;
@@ -597,6 +607,7 @@ __device__ __forceinline__ int select_pops(const float (*lq)[kLqRow], const int 
     const uint32_t k = okey(n_score + (isi ? q0 : nx_q));
     c_hi = (isp | isi) ? k : c_hi;
     nx_q = lq[st >> 16][(st & 255) + 1];
+    fqn = lq[min((st >> 16) + 1, L)][0];
     n_pop = i;
     if (++i > N) break;
     mh = wave_umax(c_hi);
