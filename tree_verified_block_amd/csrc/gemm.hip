@@ -529,22 +529,69 @@ __global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int
 }
 
 // -------------------------------------------------------------- projections
+// What the epilogue of block b reads for activation row gm besides the sums,
+// loaded ahead of the split-K hand-over: the q/k rows' RoPE position (or the
+// output projection's residual token) at the start of the kernel, the RoPE
+// values at that position (or the residual row) right after the K loop, so
+// that they arrive while the partial sums are stored and counted.
+struct EpiIn {
+  int key;           // q/k: RoPE position, residual: token (-1: none / zero row)
+  float c[8], sn[8];  // q/k: cos and sin of head dims j8 .. j8 + 7 at the position
+  uint4 r[2];        // residual: the 16 residual values of the block
+};
+
+template <int EPI>
+__device__ __forceinline__ int epi_key(const GemmArgs& a, int b, int gm) {
+  if constexpr (EPI == EPI_QKV) {
+    if (b >= (a.Hq + a.Hkv) * 8) return -1;
+    const int sq = gm / a.n_rows;
+    const int pos = static_cast<int>(a.kv_offsets[sq + 1] - a.kv_offsets[sq]) + a.depth[gm];
+    return pos > a.n_pos - 1 ? a.n_pos - 1 : pos;
+  } else if constexpr (EPI == EPI_RESID) {
+    return a.resid_tok[gm];
+  } else {
+    return -1;
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ void epi_load(const GemmArgs& a, int b, int gm, EpiIn& in) {
+  if constexpr (EPI == EPI_QKV) {
+    if (in.key >= 0) {
+      const int nq = a.Hq * 8;
+      const int j8 = ((b < nq ? b : b - nq) & 7) * 8;
+      const float* cp = a.rope_cos + static_cast<size_t>(in.key) * 64 + j8;
+      const float* sp = a.rope_sin + static_cast<size_t>(in.key) * 64 + j8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        in.c[i] = cp[i];
+        in.sn[i] = sp[i];
+      }
+    }
+  } else if constexpr (EPI == EPI_RESID) {
+    if (in.key >= 0) {
+      const uint16_t* rp = static_cast<const uint16_t*>(a.resid) +
+                           static_cast<size_t>(a.resid_by_token ? in.key : gm) * a.N + b * 16;
+      in.r[0] = *reinterpret_cast<const uint4*>(rp);
+      in.r[1] = *reinterpret_cast<const uint4*>(rp + 8);
+    }
+  }
+}
+
 // Epilogue of one 16-row weight block for activation row gm: x[i] is the
 // block's row i (of the summed K slices).  q/k blocks are rotated (rows i and
 // 8+i are RoPE partners), v rows copied, output-projection rows added to the
 // residual; everything is rounded to bf16.
 template <int EPI>
-__device__ __forceinline__ void proj_store(const GemmArgs& a, int b, int gm, const float (&x)[16]) {
+__device__ __forceinline__ void proj_store(const GemmArgs& a, int b, int gm, const float (&x)[16],
+                                           const EpiIn& in) {
   if constexpr (EPI == EPI_RESID) {
     const int n = b * 16;
     uint4 o[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-    const int tok = a.resid_tok[gm];
-    if (tok >= 0) {
-      const uint16_t* rp = static_cast<const uint16_t*>(a.resid) +
-                           static_cast<size_t>(a.resid_by_token ? tok : gm) * a.N + n;
+    if (in.key >= 0) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const uint4 r = *reinterpret_cast<const uint4*>(rp + 8 * h);
+        const uint4 r = in.r[h];
         const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
         uint32_t ow[4];
 #pragma unroll
@@ -581,9 +628,6 @@ __device__ __forceinline__ void proj_store(const GemmArgs& a, int b, int gm, con
       // rows i < 8 are head dims 8j + i, rows 8 + i their RoPE partners 64 + 8j + i
       const int bb = b < nq ? b : b - nq;
       const int head = bb >> 3, j8 = (bb & 7) * 8;
-      const int sq = gm / a.n_rows;
-      int pos = static_cast<int>(a.kv_offsets[sq + 1] - a.kv_offsets[sq]) + a.depth[gm];
-      if (pos > a.n_pos - 1) pos = a.n_pos - 1;
       uint32_t lw[4], hw[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -591,8 +635,8 @@ __device__ __forceinline__ void proj_store(const GemmArgs& a, int b, int gm, con
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int i = 2 * j + h;
-          const float c = a.rope_cos[static_cast<size_t>(pos) * 64 + j8 + i];
-          const float sn = a.rope_sin[static_cast<size_t>(pos) * 64 + j8 + i];
+          const float c = in.c[i];
+          const float sn = in.sn[i];
           lo[h] = x[i] * c - x[i + 8] * sn;
           hi[h] = x[i + 8] * c + x[i] * sn;
         }
@@ -642,6 +686,10 @@ __global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int
   const int Ks = a.K / S;
   const int kbase = q * Ks;
   const int nck = Ks / kKc;
+  // the epilogue's own inputs for activation row m0 + l (rows past M: the last)
+  const int gme = min(m0 + l, a.M - 1);
+  EpiIn ein;
+  ein.key = bv ? epi_key<EPI>(a, b, gme) : -1;
 
   // weight operand of chunk c, half i: wb + c * wcs + i * whs (bytes).  Row-major
   // W: row block_row(b, l%16), columns 64 c + 32 i + 8 (l/16); packed W (see
@@ -692,15 +740,16 @@ __global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int
 
   // nck is a multiple of RS; loads past the last chunk are clamped to it, so no
   // load is conditional (a conditional load would make the compiler's wait
-  // counts conservative and drain the ring every chunk)
+  // counts conservative and drain the ring every chunk).  The whole ring is in
+  // flight before the first activation chunk is waited for.
   xload(0, xbuf[0]);
-#pragma unroll
-  for (int e = 0; e < 2; ++e) *reinterpret_cast<uint4*>(&xs[xlds[e]]) = mask4(xbuf[0][e], xm[e]);
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) {
     if (d + 1 < DEPTH) xload(min(d + 1, nck - 1), xbuf[d + 1]);
     wload(min(d, nck - 1), wbuf[d]);
   }
+#pragma unroll
+  for (int e = 0; e < 2; ++e) *reinterpret_cast<uint4*>(&xs[xlds[e]]) = mask4(xbuf[0][e], xm[e]);
   for (int c0 = 0; c0 < nck; c0 += RS) {
 #pragma unroll
     for (int u = 0; u < RS; ++u) {
@@ -734,6 +783,7 @@ __global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int
   // counter and the partials are shared, both through device-scope atomic
   // accesses (write-through stores and coherent loads), and every store has
   // completed before the arrival is counted, so no cache write-back is needed.
+  if (bv) epi_load<EPI>(a, b, gme, ein);
   const size_t grp = static_cast<size_t>(mt) * NGr + g;
   float* pp = a.kpart + ((grp * S + q) * 4 + w) * 1024;
 #pragma unroll
@@ -767,7 +817,7 @@ __global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int
   }
   const int gm = m0 + l;
   if (gm >= a.M) return;
-  proj_store<EPI>(a, b, gm, x);
+  proj_store<EPI>(a, b, gm, x, ein);
 }
 
 __global__ __launch_bounds__(256) void head_merge_kernel(const float* __restrict__ part, int nNT,
