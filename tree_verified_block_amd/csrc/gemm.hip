@@ -807,13 +807,25 @@ __global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int
   float x[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) x[i] = 0.f;
-  for (int qq = 0; qq < S; ++qq) {
-    const float* src = a.kpart + ((grp * S + qq) * 4 + w) * 1024 + l;
-    float y[16];
+  // up to 8 slices' loads in flight at once (one round trip per 8 slices),
+  // summed in slice order
+  constexpr int kSB = 8;
+  for (int q0 = 0; q0 < S; q0 += kSB) {
+    float y[kSB][16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) y[i] = __hip_atomic_load(src + i * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int j = 0; j < kSB; ++j) {
+      if (q0 + j < S) {
+        const float* src = a.kpart + ((grp * S + q0 + j) * 4 + w) * 1024 + l;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] += y[i];
+        for (int i = 0; i < 16; ++i) y[j][i] = __hip_atomic_load(src + i * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kSB; ++j)
+      if (q0 + j < S) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] += y[j][i];
+      }
   }
   const int gm = m0 + l;
   if (gm >= a.M) return;
