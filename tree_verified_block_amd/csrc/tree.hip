@@ -319,8 +319,8 @@ __device__ __forceinline__ void chunk_topk(const T* __restrict__ logits, int L, 
   if (kw > 0) {
 #pragma unroll
     for (int bit = 31; bit >= 16; --bit) {
-      const uint32_t c = t | (1u << bit);
-      if (__popcll(__ballot(kb >= c)) >= kw) t = c;
+      const uint32_t tc = t | (1u << bit);
+      if (static_cast<int>(__popcll(__ballot(kb >= tc))) >= kw) t = tc;
     }
   }
   if (lane == 0) {
@@ -466,8 +466,8 @@ __device__ __forceinline__ void chunk_topk(const T* __restrict__ logits, int L, 
       if (ok[e]) {
         const unsigned long long key = make_comp(z[e], static_cast<uint32_t>(tok(e)));
         if (key >= prefix) {
-          const int slot = atomicAdd(&s_count, 1);
-          if (slot < kSlots) cand[slot] = key;
+          const int at = atomicAdd(&s_count, 1);
+          if (at < kSlots) cand[at] = key;
         }
       }
     }
