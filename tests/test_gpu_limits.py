@@ -101,3 +101,25 @@ def test_tree_when_every_chunk_ends_in_ties(dtype, V):
         for i in range(1, nv):
             assert z[s, int(gpu["depth"][s][i]) - 1, int(gpu["token"][s][i])] >= 1.0
     print(f"[limits] ties {dtype} V={V}: {report}", flush=True)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype,V,L,N", [
+    ("bf16", 151936, 1, 63),   # one offset: the tree is the root's 63 best children
+    ("bf16", 151936, 16, 1),   # a single node
+    ("bf16", 4099, 2, 5),      # V not a multiple of the 8-logit vector (scalar loads)
+    ("f32", 20011, 7, 40),     # V not a multiple of the 4-logit vector
+    ("f32", 3, 4, 63),         # fewer tokens than K: lists end early
+])
+def test_tree_at_edge_shapes(dtype, V, L, N):
+    rng = np.random.default_rng(20 + L + N)
+    nseq = 2
+    z = rng.normal(0.0, 2.0, (nseq, L, V)).astype(np.float32)
+    stored = z if dtype == "f32" else bf16_bits(z)
+    roots = np.array([5 % V, 7 % V], np.int64)
+    gpu = _build(stored, dtype, roots, N)
+    report = {}
+    for s in range(nseq):
+        ot = orr.build_tree(stored[s], dtype, int(roots[s]), N)
+        parity.check_tree(gpu, s, ot, ot["logq"], N, L, report)
+    print(f"[limits] edge {dtype} V={V} L={L} N={N}: {report}", flush=True)
