@@ -59,19 +59,32 @@ def rope(x: np.ndarray, pos: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np
 
 
 def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
-    """x / sqrt(mean(x^2) + eps) * g over the last axis."""
-    x = np.asarray(x, dtype=np.float64)
-    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * g
+    """x / sqrt(mean(x^2) + eps) * g over the last axis (in float32 when x is
+    float32, else float64)."""
+    x = np.asarray(x)
+    if x.dtype != np.float32:
+        x = x.astype(np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + x.dtype.type(eps)) * g.astype(x.dtype)
 
 
 def silu(z: np.ndarray) -> np.ndarray:
-    return z / (1.0 + np.exp(-z))
+    return z / (z.dtype.type(1) + np.exp(-z))
 
 
 class TargetModel:
-    """Float64 view of the synthetic target's tensors, decoded on demand."""
+    """Float64 view of the synthetic target's tensors, decoded on demand.
 
-    def __init__(self, inp: dict, cache_head: bool = False):
+    ``compute="f32"`` evaluates the same definition with every operation between
+    two storage points in float32 instead of float64 (the storage points, and the
+    order of operations, are unchanged).  It is a second valid evaluation of the
+    same model, used only to measure how far two correct implementations of a
+    bf16 stack can drift apart from rounding alone; the tolerances of the
+    comparisons are derived from that drift."""
+
+    def __init__(self, inp: dict, cache_head: bool = False, compute: str = "f64"):
+        if compute not in ("f64", "f32"):
+            raise ValueError(compute)
+        self.ft = np.float64 if compute == "f64" else np.float32
         cfg = inp["cfg"]
         self.cfg = cfg
         self.dtype = cfg.dtype
@@ -83,14 +96,22 @@ class TargetModel:
         self._inp = inp
         self.kv_offsets = np.asarray(inp["kv_offsets"], dtype=np.int64)
         self.prefix_len = np.asarray(inp["prefix_len"], dtype=np.int64)
-        self.cos = np.asarray(inp["rope_cos"], dtype=np.float64)
-        self.sin = np.asarray(inp["rope_sin"], dtype=np.float64)
-        self._head64 = decode(inp["w_head"], self.dtype) if cache_head else None
+        self.cos = np.asarray(inp["rope_cos"], dtype=self.ft)
+        self.sin = np.asarray(inp["rope_sin"], dtype=self.ft)
+        self._head64 = self._dec(inp["w_head"]) if cache_head else None
         self._layer_cache: dict = {}
 
     # ---------------------------------------------------------------- tensors
+    def _dec(self, x) -> np.ndarray:
+        """Stored tensor -> exact values in the compute type."""
+        return decode(x, self.dtype).astype(self.ft, copy=False)
+
+    def _store(self, x) -> np.ndarray:
+        """Storage point: round to the storage format, back in the compute type."""
+        return store(x, self.dtype).astype(self.ft, copy=False)
+
     def embed_rows(self, tokens) -> np.ndarray:
-        return decode(self._inp["embed"][np.asarray(tokens, dtype=np.int64)], self.dtype)
+        return self._dec(self._inp["embed"][np.asarray(tokens, dtype=np.int64)])
 
     def layer(self, li: int) -> dict:
         if li not in self._layer_cache:
@@ -98,22 +119,23 @@ class TargetModel:
             names = ("wq", "wk", "wv", "wo")
             if self.full:
                 names += ("g_attn", "g_q", "g_k", "g_mlp", "w_gate", "w_up", "w_down")
-            self._layer_cache = {li: {k: decode(lw[k], self.dtype) for k in names}}
+            self._layer_cache = {li: {k: self._dec(lw[k]) for k in names}}
         return self._layer_cache[li]
 
     def prefix_kv(self, li: int, s: int):
         lw = self._inp["layers"][li]
         a, b = int(self.kv_offsets[s]), int(self.kv_offsets[s + 1])
-        return decode(lw["k_cache"][a:b], self.dtype), decode(lw["v_cache"][a:b], self.dtype)
+        return self._dec(lw["k_cache"][a:b]), self._dec(lw["v_cache"][a:b])
 
     def logits(self, h: np.ndarray, chunk: int = 8192) -> np.ndarray:
-        """z = h W_head^T in float64, over vocabulary chunks."""
-        h = np.atleast_2d(np.asarray(h, dtype=np.float64))
+        """z = h W_head^T (float64, or float32 in the float32 mode; returned as
+        float64), over vocabulary chunks."""
+        h = np.atleast_2d(np.asarray(h, dtype=self.ft))
         z = np.empty((h.shape[0], self.V), dtype=np.float64)
         for a in range(0, self.V, chunk):
             b = min(a + chunk, self.V)
             w = self._head64[a:b] if self._head64 is not None else \
-                decode(self._inp["w_head"][a:b], self.dtype)
+                self._dec(self._inp["w_head"][a:b])
             z[:, a:b] = h @ w.T
         return z
 
@@ -121,8 +143,9 @@ class TargetModel:
     def project(self, li: int, h: np.ndarray, pos: np.ndarray):
         """q (rotated), k (rotated, stored), v (stored) of rows h at positions pos."""
         w = self.layer(li)
+        h = np.asarray(h, dtype=self.ft)
         n = h.shape[0]
-        x = store(rmsnorm(h, w["g_attn"], self.eps), self.dtype) if self.full else h
+        x = self._store(rmsnorm(h, w["g_attn"], self.eps)) if self.full else h
         q = (x @ w["wq"].T).reshape(n, self.Hq, self.D)
         k = (x @ w["wk"].T).reshape(n, self.Hkv, self.D)
         v = (x @ w["wv"].T).reshape(n, self.Hkv, self.D)
@@ -130,18 +153,18 @@ class TargetModel:
             q = rmsnorm(q, w["g_q"], self.eps)
             k = rmsnorm(k, w["g_k"], self.eps)
         q = rope(q, pos, self.cos, self.sin)
-        k = store(rope(k, pos, self.cos, self.sin), self.dtype)
-        v = store(v, self.dtype)
+        k = self._store(rope(k, pos, self.cos, self.sin))
+        v = self._store(v)
         return q, k, v
 
     def attend(self, q: np.ndarray, keys: np.ndarray, vals: np.ndarray) -> np.ndarray:
         """Softmax attention of one position's query heads q [Hq][D] over an
         explicit key/value sequence [T][Hkv][D]; returns [Hq][D]."""
         G = self.Hq // self.Hkv
-        out = np.empty((self.Hq, self.D))
+        out = np.empty((self.Hq, self.D), dtype=self.ft)
         for g in range(self.Hq):
             kv = g // G
-            sc = keys[:, kv, :] @ q[g] / np.sqrt(self.D)
+            sc = keys[:, kv, :] @ q[g] / self.ft(np.sqrt(self.D))
             p = np.exp(sc - sc.max())
             p /= p.sum()
             out[g] = p @ vals[:, kv, :]
@@ -149,12 +172,14 @@ class TargetModel:
 
     def residual(self, li: int, h: np.ndarray, a: np.ndarray) -> np.ndarray:
         w = self.layer(li)
-        h1 = store(h + a.reshape(a.shape[0], -1) @ w["wo"].T, self.dtype)
+        h = np.asarray(h, dtype=self.ft)
+        a = np.asarray(a, dtype=self.ft)
+        h1 = self._store(h + a.reshape(a.shape[0], -1) @ w["wo"].T)
         if not self.full:
             return h1
-        x2 = store(rmsnorm(h1, w["g_mlp"], self.eps), self.dtype)
-        act = store(silu(x2 @ w["w_gate"].T) * (x2 @ w["w_up"].T), self.dtype)
-        return store(h1 + act @ w["w_down"].T, self.dtype)
+        x2 = self._store(rmsnorm(h1, w["g_mlp"], self.eps))
+        act = self._store(silu(x2 @ w["w_gate"].T) * (x2 @ w["w_up"].T))
+        return self._store(h1 + act @ w["w_down"].T)
 
 
 def evaluate_paths(model: TargetModel, s: int, root: int, paths: list,
@@ -184,18 +209,18 @@ def evaluate_paths(model: TargetModel, s: int, root: int, paths: list,
     attn_all, h_all = [], []
     for li in range(model.n_layers):
         if layer_inputs is not None and li > 0 and layer_inputs[li] is not None:
-            h = np.asarray(layer_inputs[li], dtype=np.float64)
+            h = np.asarray(layer_inputs[li], dtype=model.ft)
         q, k, v = model.project(li, h, pos)
         Kp, Vp = model.prefix_kv(li, s)
-        a = np.empty((n, model.Hq, model.D))
+        a = np.empty((n, model.Hq, model.D), dtype=model.ft)
         for i in range(n):
             keys = np.concatenate([Kp, k[chains[i]]], axis=0)
             vals = np.concatenate([Vp, v[chains[i]]], axis=0)
             a[i] = model.attend(q[i], keys, vals)
-        attn_all.append(a.reshape(n, -1))
+        attn_all.append(a.reshape(n, -1).astype(np.float64))
         h = model.residual(li, h, a)
-        h_all.append(h)
-    return {"attn": attn_all, "h": h_all, "final": h}
+        h_all.append(h.astype(np.float64))
+    return {"attn": attn_all, "h": h_all, "final": h.astype(np.float64)}
 
 
 class Decoder:
