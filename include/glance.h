@@ -98,6 +98,17 @@ glance_status glance_build_tree(const void* draft_logits, int32_t dtype,
 
 size_t glance_build_tree_ws(int32_t nseq, int32_t L, int32_t V, int32_t N);
 
+/* glance_build_tree_flag_offset: byte offset, inside a glance_build_tree (or
+ * glance_build_tree_shared) workspace of these sizes, of a uint32 word that
+ * reports non-finite draft logits: every call ORs in bit 0 when a logit it read
+ * is NaN and bit 1 when one is +inf (a -inf logit is a token of probability 0,
+ * legal, and not reported).  The word is sticky: the library never clears it;
+ * it starts at 0 in a zero-filled workspace, and the caller resets it by
+ * writing 0.  The trees of a call that set it are unspecified (NaN has no
+ * place in the score order).  Host function, pure; 0 on invalid sizes (the
+ * word never sits at offset 0). */
+size_t glance_build_tree_flag_offset(int32_t nseq, int32_t L, int32_t V, int32_t N);
+
 /* glance_build_tree_shared: steps 1-2 for a batch of rounds that share one
  * budget of tree nodes (paper App. B.5, Proposition 4 and Eq. 5: under a
  * shared verifier budget the best allocation takes the globally highest node

@@ -45,6 +45,15 @@ def build_tree_ws_bytes(nseq: int, L: int, V: int, N: int) -> int:
     return _lib.load().glance_build_tree_ws(nseq, L, V, N)
 
 
+def build_tree_flags(ws: torch.Tensor, nseq: int, L: int, V: int, N: int) -> int:
+    """The workspace's sticky non-finite flag word (bit 0: a NaN draft logit was
+    read, bit 1: a +inf one) as a Python int; synchronises with the device."""
+    off = _lib.load().glance_build_tree_flag_offset(nseq, L, V, N)
+    if off == 0:
+        raise ValueError("invalid tree sizes")
+    return int(ws[off:off + 4].view(torch.int32).item()) & 0xFFFFFFFF
+
+
 def tree_outputs(nseq: int, N: int, device) -> dict:
     R = N + 1
     return {

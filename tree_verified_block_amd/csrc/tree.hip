@@ -232,7 +232,7 @@ template <typename T, int NV>
 __device__ __forceinline__ void chunk_topk(const T* __restrict__ logits, int L, int V, int N, int nch,
                                            unsigned long long* __restrict__ cstat,
                                            unsigned long long* __restrict__ clist,
-                                           unsigned long long* cand) {
+                                           unsigned long long* cand, unsigned* __restrict__ flag) {
   constexpr int E = 16 / sizeof(T);
   constexpr int IPT = NV * E;
   __shared__ unsigned long long sel[kSlots];
@@ -286,18 +286,27 @@ __device__ __forceinline__ void chunk_topk(const T* __restrict__ logits, int L, 
     }
   }
 
-  // running max and best (strict comparison: the smallest id wins a tie)
+  // running max and best (strict comparison: the smallest id wins a tie); NaN
+  // and +inf logits are reported in the flag word (bit 0 and bit 1)
   float m = -INFINITY, bz = -INFINITY;
   int bi = -1;
+  bool nan_seen = false, pinf_seen = false;
 #pragma unroll
   for (int e = 0; e < IPT; ++e) {
     if (ok[e]) {
       m = fmaxf(m, z[e]);
+      nan_seen |= z[e] != z[e];
+      pinf_seen |= z[e] == INFINITY;
       if (bi < 0 || z[e] > bz) {
         bz = z[e];
         bi = tok(e);
       }
     }
+  }
+  {
+    const bool bn = __ballot(nan_seen) != 0ull, bp = __ballot(pinf_seen) != 0ull;
+    if (lane == 0 && (bn || bp))
+      __hip_atomic_fetch_or(flag, (bn ? 1u : 0u) | (bp ? 2u : 0u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   // sum of exp(z - m) through the hardware exp2 (z - m <= 0)
   float s = 0.f;
@@ -313,8 +322,13 @@ __device__ __forceinline__ void chunk_topk(const T* __restrict__ logits, int L, 
   // least k = ceil(K/4) of the per-thread best keys (high 32 bits) reach, found
   // bit by bit on ballots; the minimum T over the four waves is then reached by
   // at least K keys of the chunk
+  // A -inf logit (a token of probability 0) never enters a tree: it takes no
+  // part in the threshold or the gather.  (Its key, float_key(-inf), sits just
+  // below every finite key; a threshold at its 16-bit prefix would map back to
+  // a NaN and gather nothing.)  Finite keys are >= 0x00800000, so the threshold
+  // is 0 or a finite value's prefix.
   const int kw = (K + kChunkWaves - 1) / kChunkWaves;
-  const uint32_t kb = bi >= 0 ? float_key(bz) : 0u;
+  const uint32_t kb = (bi >= 0 && bz > -INFINITY) ? float_key(bz) : 0u;
   uint32_t t = 0u;
   if (kw > 0) {
 #pragma unroll
@@ -359,7 +373,7 @@ __device__ __forceinline__ void chunk_topk(const T* __restrict__ logits, int L, 
   unsigned long long pm = 0ull;
 #pragma unroll
   for (int e = 0; e < IPT; ++e)
-    if (ok[e] && z[e] >= zT) pm |= 1ull << e;
+    if (ok[e] && z[e] >= zT && z[e] > -INFINITY) pm |= 1ull << e;
   const int pc = __popcll(pm);
   const int incl = wave_incl_sum(pc);
   const int run = readlane_i(incl, kWave - 1);
@@ -795,11 +809,11 @@ __global__ __launch_bounds__(kChunkThreads) void tree_kernel(
     unsigned* __restrict__ row_cnt, unsigned* __restrict__ seq_cnt, const int32_t* __restrict__ root_token,
     int32_t* __restrict__ parent, int32_t* __restrict__ depth_out, int32_t* __restrict__ token_out,
     uint64_t* __restrict__ anc_out, float* __restrict__ score_out, int32_t* __restrict__ n_valid_out,
-    SharedArgs sh) {
+    SharedArgs sh, unsigned* __restrict__ flag) {
   __shared__ __attribute__((aligned(16))) unsigned long long buf[kCap];
   const int j = blockIdx.y, sq = blockIdx.z;
   const int row = sq * L + j;
-  chunk_topk<T, NV>(logits, L, V, N, nch, cstat, clist, buf);
+  chunk_topk<T, NV>(logits, L, V, N, nch, cstat, clist, buf, flag);
   if (!arrive_last(row_cnt + row, nch)) return;
   const int K = k_of(N, V, j);
   if (K > 0) {
@@ -866,6 +880,7 @@ struct TreeBufs {
   int* tk;
   unsigned* row_cnt;
   unsigned* seq_cnt;
+  unsigned* flag;
 };
 
 template <typename T>
@@ -877,7 +892,7 @@ void launch_tree(int nv, dim3 ga, const T* logits, int L, int V, int N, int nch,
   case n:                                                                                          \
     tree_kernel<T, n><<<ga, kChunkThreads, 0, st>>>(logits, L, V, N, nch, b.cstat, b.clist, b.lq, b.tk, \
                                                    b.row_cnt, b.seq_cnt, root, parent, depth, token, \
-                                                   anc, score, n_valid, sh);                        \
+                                                   anc, score, n_valid, sh, b.flag);                \
     break;
     GLANCE_TREE_CASE(1)
     GLANCE_TREE_CASE(2)
@@ -912,6 +927,7 @@ TreeWs tree_ws_layout(int nseq, int L, int V) {
   w.off_seq_cnt = take(static_cast<size_t>(nseq) * sizeof(unsigned));
   w.off_pops = take(static_cast<size_t>(nseq) * kWave * sizeof(int4));
   w.off_batch_cnt = take(sizeof(unsigned));
+  w.off_flag = take(sizeof(unsigned));
   w.bytes = off;
   return w;
 }
@@ -937,6 +953,7 @@ glance_status launch_build_tree(const void* logits, int dtype, const int32_t* ro
   b.tk = reinterpret_cast<int*>(base + w.off_tk);
   b.row_cnt = reinterpret_cast<unsigned*>(base + w.off_row_cnt);
   b.seq_cnt = reinterpret_cast<unsigned*>(base + w.off_seq_cnt);
+  b.flag = reinterpret_cast<unsigned*>(base + w.off_flag);
   // at most kMaxChunks chunks of 256 threads x nv vectors per offset row
   const int E = dtype == GLANCE_BF16 ? 8 : 4;
   const int per_vec = kChunkThreads * E;
