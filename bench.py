@@ -92,7 +92,7 @@ def chain_measure(inp, cfg, drafts, K: int, warm: int = 5, packed: bool = False)
     P0 = int(inp["prefix_len"][0])
     cap = P0 + (K + warm + 1) * (cfg.L + 1)
     inp = dict(inp)  # rotary tables covering every position the chain reaches
-    inp["rope_cos"], inp["rope_sin"] = rope_tables(cap + 1, cfg.D, cfg.rope_theta)
+    inp["rope_cos"], inp["rope_sin"] = rope_tables(cap + cfg.N + 1, cfg.D, cfg.rope_theta)
     dev = DeviceRound(inp, device="cuda", capacity=cap, packed_head=packed)
     dev.set_round(0)
     stream = torch.cuda.current_stream()

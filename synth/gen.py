@@ -422,6 +422,8 @@ def gen_round(cfg: RoundConfig, seed: int, with_model: bool = True) -> dict:
                 "w_down": _normal(rm, (cfg.d_model, cfg.mlp), cfg.mlp_std, dt),
             })
     out["layers"] = layers
-    n_pos = int(P.max()) + cfg.L + 1
+    # a row of the table for every position P + depth a verify row can take
+    # (depth < N + 1 rows), so that tables cover max prefix + rows
+    n_pos = int(P.max()) + max(cfg.L, cfg.N) + 1
     out["rope_cos"], out["rope_sin"] = rope_tables(n_pos, cfg.D, cfg.rope_theta)
     return out

@@ -11,7 +11,7 @@ def chained_workload(name: str, seed: int, n_rounds: int, **overrides):
     cfg = make_config(name, **overrides)
     inp = gen_round(cfg, seed)
     P = int(inp["prefix_len"][0])
-    n_pos = P + (n_rounds + 1) * (cfg.L + 1) + 1
+    n_pos = P + (n_rounds + 1) * (cfg.L + 1) + cfg.N + 1
     inp["rope_cos"], inp["rope_sin"] = rope_tables(n_pos, cfg.D, cfg.rope_theta)
     return cfg, inp
 

@@ -1,29 +1,57 @@
 """Comparison rules between the HIP path's outputs and the CPU oracle.
 
 Integer outputs (tree layout, argmax, walk) must match bit-exactly wherever the
-oracle's decision is not a near-tie (top-2 logit gap, or the tree's boundary
-gap, above 1e-3: the pages' uniqueness assumption of Theorem 1; for the argmax
-also above twice the largest difference between the GPU's and the oracle's
-logits of the round, since each of the two best logits can move by that much);
-near-ties are flagged, counted and checked for validity instead.  Float tensors
-are compared norm-wise, max|gpu - oracle| / max|oracle|, against 1e-5 (fp32
-runs), 1e-2 (bf16 runs) or 2e-2 (bf16 runs of full layers: five more bf16
-storage points per layer, where a rounding flip moves an element by one bf16
-ulp, up to 2^-7 of max|x| for the largest elements, and the next products carry
-it to every element; measured errors reach about 1% of max|h|)."""
+oracle's decision is not a near-tie: the tree's boundary gap, or a row's top-2
+logit gap, above 1e-3 (the uniqueness assumption of Theorem 1, paper App. B.1).
+Near-ties are flagged, counted and checked for validity: a flagged tree must be
+a valid top-N set within 1e-3, a flagged row's token must be within the decision
+threshold of the oracle's best logit.
+
+The decision threshold of a row is max(1e-3, 2 dz) (fp32 runs: max(1e-6, 2 dz)),
+dz being the largest logit difference between the oracle's float64 and float32
+evaluations of the same workload (tests/golden/precision_bounds.json, written
+by the oracle alone): two correct implementations whose logits differ by at most
+dz can disagree only on a row whose gap is at most 2 dz.  For the attention-only
+workloads of one layer dz is far below 5e-4 and the threshold is exactly 1e-3;
+deep stacks and full decoder layers have a wider one.  Rows with
+1e-3 < gap <= threshold are the "near" bucket: counted and checked for validity.
+
+Float tensors are compared norm-wise, max|gpu - oracle| / max|oracle|, against
+1e-5 (fp32 runs) or 1e-2 (bf16 runs); the same file shows that two correct
+evaluations of every workload stay inside these bars."""
 from __future__ import annotations
+
+import json
+import os
 
 import numpy as np
 
-from oracle import draft, model as mdl, round as orr, tree as tr, walk as wk
+from oracle import model as mdl, tree as tr, walk as wk
 
-GAP = 1e-3
+GAP = 1e-3       # near-tie threshold of the pages' uniqueness assumption (logit units)
+GAP_F32 = 1e-6   # fp32 runs: argmax bit-exact down to this gap
+
+_BOUNDS_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                            "precision_bounds.json")
+_BOUNDS = None
 
 
-def tol_for(dtype: str, full: bool = False) -> float:
-    if dtype == "f32":
-        return 1e-5
-    return 2e-2 if full else 1e-2
+def bounds(name: str) -> dict:
+    """Float32-vs-float64 oracle drift of a workload (zeros when not recorded)."""
+    global _BOUNDS
+    if _BOUNDS is None:
+        with open(_BOUNDS_PATH) as f:
+            _BOUNDS = json.load(f)["workloads"]
+    return _BOUNDS.get(name, {"dz": 0.0, "logits": 0.0, "h": 0.0, "attn": 0.0})
+
+
+def tol_for(dtype: str) -> float:
+    return 1e-5 if dtype == "f32" else 1e-2
+
+
+def decide_threshold(dtype: str, name: str) -> float:
+    base = GAP_F32 if dtype == "f32" else GAP
+    return max(base, 2.0 * bounds(name)["dz"])
 
 
 def rel_err(got, want) -> float:
@@ -31,6 +59,14 @@ def rel_err(got, want) -> float:
     want = np.asarray(want, dtype=np.float64)
     den = np.abs(want).max()
     return float(np.abs(got - want).max() / (den if den > 0 else 1.0))
+
+
+def _add(report: dict, key: str, n: int = 1):
+    report[key] = report.get(key, 0) + n
+
+
+def _maxto(report: dict, key: str, v: float):
+    report[key] = max(report.get(key, 0.0), float(v))
 
 
 def gpu_paths(parent, token, n_valid):
@@ -66,9 +102,9 @@ def check_tree(gpu: dict, s: int, ora_tree: dict, logq: np.ndarray, N: int, L: i
             assert np.array_equal(gpu[k][s], ora_tree[k]), k
         assert np.array_equal(gpu["anc"][s], ora_tree["anc"])
         assert g_nv == ora_tree["n_valid"]
-        report["tree_exact"] = report.get("tree_exact", 0) + 1
+        _add(report, "tree_exact")
     else:
-        report["tree_flagged"] = report.get("tree_flagged", 0) + 1
+        _add(report, "tree_flagged")
         assert g_nv == ora_tree["n_valid"]
         in_scores = [sum(logq[j, t] for j, t in enumerate(p)) for p in paths[1:]]
         best_out = -np.inf
@@ -87,48 +123,66 @@ def check_tree(gpu: dict, s: int, ora_tree: dict, logq: np.ndarray, N: int, L: i
     return paths
 
 
-def check_rows(gpu: dict, ev: dict, z: np.ndarray, s: int, n_rows: int, dtype: str, report: dict,
-               rows=None, full: bool = False):
-    """Verify rows of sequence s (the oracle evaluated on the GPU's own tree).
-    Leaves the round's decision threshold in report["flag"] (see module doc)."""
-    tol = tol_for(dtype, full)
+def check_rows(gpu: dict, ev: dict, z: np.ndarray, s: int, n_rows: int, cfg, report: dict,
+               rows=None):
+    """Verify rows of sequence s (the oracle evaluated on the GPU's own tree, in
+    the order of ``rows``, default every row): float tensors norm-wise within the
+    bar, argmax bit-exact on decided rows, a valid near-argmax elsewhere.
+    Returns the oracle's argmax and top-2 gap of those rows."""
+    dtype = cfg.dtype
+    tol = tol_for(dtype)
+    thr = decide_threshold(dtype, cfg.name)
+    report["threshold"] = thr
     sl = slice(s * n_rows, (s + 1) * n_rows)
     idx = np.arange(len(ev["final"])) if rows is None else np.asarray(rows)
     if "attn_out" in gpu:
         for li in range(len(ev["attn"])):
             e = rel_err(gpu["attn_out"][li][sl][idx], ev["attn"][li])
-            report.setdefault("attn_err", []).append(e)
+            _maxto(report, "attn_err", e)
             assert e <= tol, ("attn", li, e)
             e = rel_err(gpu["h_layers"][li][sl][idx], ev["h"][li])
-            report.setdefault("h_err", []).append(e)
+            _maxto(report, "h_err", e)
             assert e <= tol, ("h", li, e)
     am, top1, gap, H = mdl.row_stats(z)
-    flag = GAP
     if "logits" in gpu:
-        e = rel_err(gpu["logits"][sl][idx], z)
-        report.setdefault("logit_err", []).append(e)
+        gz = gpu["logits"][sl][idx].astype(np.float64)
+        e = rel_err(gz, z)
+        _maxto(report, "logit_err", e)
+        _maxto(report, "logit_abs_err", np.abs(gz - z).max())
         assert e <= tol, ("logits", e)
-        e_abs = float(np.abs(gpu["logits"][sl][idx].astype(np.float64) - z).max())
-        flag = max(GAP, 2.0 * e_abs)
-    report["flag"] = max(report.get("flag", GAP), flag)
     e = rel_err(gpu["top1"][sl][idx], top1)
     assert e <= tol, ("top1", e)
-    eH = np.max(np.abs(gpu["entropy"][sl][idx] - H) / np.maximum(1.0, H))
-    report.setdefault("H_err", []).append(float(eH))
+    eH = float(np.max(np.abs(gpu["entropy"][sl][idx] - H) / np.maximum(1.0, H)))
+    _maxto(report, "H_err", eH)
     assert eH <= tol, ("entropy", eH)
-    g_am = gpu["argmax"][sl][idx]
-    sure = gap > flag
-    report["rows"] = report.get("rows", 0) + len(idx)
-    report["rows_flagged"] = report.get("rows_flagged", 0) + int((~sure).sum())
-    assert np.array_equal(g_am[sure], am[sure]), "argmax mismatch on an unflagged row"
-    # the GPU gap is the top-2 gap of its own logits
+    g_am = np.asarray(gpu["argmax"][sl][idx]).astype(np.int64)
+    decided = gap > thr
+    _add(report, "rows", len(idx))
+    _add(report, "rows_flagged", int((gap <= GAP).sum()))           # the pages' near-ties
+    _add(report, "rows_near", int(((gap > GAP) & ~decided).sum()))  # 1e-3 < gap <= thr
+    if dtype == "f32":
+        _add(report, "rows_flagged_1e-6", int((gap <= GAP_F32).sum()))
+    _add(report, "rows_exact", int(decided.sum()))
+    bad = np.nonzero(decided & (g_am != am))[0]
+    assert bad.size == 0, ("argmax mismatch on a decided row", bad, gap[bad])
+    # every other row: the GPU's token is a valid near-argmax of the oracle's logits
+    und = np.nonzero(~decided)[0]
+    if und.size:
+        zg = z[und, g_am[und]]
+        assert np.all(zg >= top1[und] - thr), ("invalid argmax on a flagged row", und, zg, top1[und])
+    _add(report, "rows_flag_valid", int(und.size))
     return am, gap
+
+
+def walk_flagged(gap_rows, thr) -> bool:
+    return bool(np.any(np.asarray(gap_rows) <= thr))
 
 
 def check_walk(gpu: dict, s: int, paths, am, gap, L: int, report: dict, greedy=None):
     """Walk of sequence s against the oracle's walk over the same rows (and the
-    independent greedy decode when given), exact unless a visited row is a
-    near-tie; always a valid root path whose tokens are row argmaxes."""
+    independent greedy decode when given), exact unless a visited row is
+    undecided; always a valid root path whose tokens are row argmaxes."""
+    thr = report.get("threshold", GAP)
     n_rows = len(gpu["parent"][s])
     a = int(gpu["n_accept"][s])
     toks = gpu["out_tokens"][s]
@@ -141,15 +195,28 @@ def check_walk(gpu: dict, s: int, paths, am, gap, L: int, report: dict, greedy=N
             assert gpu["parent"][s][rows[k]] == rows[k - 1]
             assert gpu["token"][s][rows[k]] == toks[k - 1]
     assert np.all(toks[a + 1:] == -1) and np.all(rows[a + 1:] == -1)
+    # the device's own flag: some row on its path has a top-2 gap <= 1e-3
+    g_gap = gpu["gap"][s * n_rows:(s + 1) * n_rows]
+    if "flagged" in gpu:
+        assert bool(gpu["flagged"][s]) == bool(np.any(g_gap[rows[:a + 1]] <= GAP))
     parent = gpu["parent"][s]
     token = gpu["token"][s]
     nv = int(gpu["n_valid"][s])
     oa, otoks, orows = wk.walk(parent, token, nv, am, L)
-    flagged = bool(np.any(gap[orows] <= report.get("flag", GAP)))
-    if flagged:
-        report["walk_flagged"] = report.get("walk_flagged", 0) + 1
+    if walk_flagged(gap[orows], thr):
+        _add(report, "walk_flagged")
         return
-    report["walk_exact"] = report.get("walk_exact", 0) + 1
+    _add(report, "walk_exact")
     assert a == oa and list(toks[:a + 1]) == otoks and list(rows[:a + 1]) == orows
-    if greedy is not None and not greedy["flagged"]:
+    if greedy is not None and not walk_flagged(greedy["Y_gaps"][:greedy["A"] + 1], thr):
         assert greedy["A"] == a and greedy["Y"][:a + 1] == otoks
+        _add(report, "greedy_exact")
+
+
+def record(tag: str, report: dict):
+    """Print the report; append it as one JSON line to $GLANCE_PARITY_LOG when set."""
+    print(f"[parity] {tag}: {report}", flush=True)
+    path = os.environ.get("GLANCE_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"case": tag, **{k: v for k, v in report.items()}}) + "\n")

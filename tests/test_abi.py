@@ -42,6 +42,9 @@ def test_helpers(lib):
     assert b"workspace" in lib.glance_status_string(-3)
     assert lib.glance_build_tree_ws(1, 15, 151936, 63) > 0
     assert lib.glance_build_tree_ws(0, 15, 151936, 63) == 0
+    off = lib.glance_build_tree_flag_offset(1, 15, 151936, 63)
+    assert 0 < off and off % 4 == 0 and off + 4 <= lib.glance_build_tree_ws(1, 15, 151936, 63)
+    assert lib.glance_build_tree_flag_offset(1, 0, 151936, 63) == 0
     assert lib.glance_verify_head_ws(64, 151936, 4096, 1) >= 64 * 5 * 4
     assert lib.glance_tree_attn_ws(1, 64, 1024, 4096, 32, 8, 128) > 0
 
@@ -216,6 +219,9 @@ def test_tree_attn_rejects_bad_arguments(lib):
     assert _attn(lib, D=64) == -4             # bf16 path is head_dim 128
     assert _attn(lib, embed=None) == -1       # neither embed nor h_in
     assert _attn(lib, n_pos=100) == -1
+    # every row's position P + depth (depth < n_rows) needs a table row
+    assert _attn(lib, max_prefix=1024, n_pos=1024 + 63) == -1
+    assert _attn(lib, max_prefix=1024, n_pos=1024 + 64, ws_bytes=1000) == -3
     assert _attn(lib, layer=OK_PTR + 2) == -2
     assert _attn(lib, dtype=0, max_prefix=9000, n_pos=10000) == -4
     assert _attn(lib, ws_bytes=1000) == -3

@@ -123,3 +123,38 @@ def test_tree_at_edge_shapes(dtype, V, L, N):
         ot = orr.build_tree(stored[s], dtype, int(roots[s]), N)
         parity.check_tree(gpu, s, ot, ot["logq"], N, L, report)
     print(f"[limits] edge {dtype} V={V} L={L} N={N}: {report}", flush=True)
+
+
+@pytest.mark.timeout(300)
+def test_nonfinite_logits_set_the_flag_word():
+    """The workspace's flag word reports NaN (bit 0) and +inf (bit 1) draft
+    logits; -inf logits are legal (probability 0) and leave it clear, and the
+    word is sticky until the caller clears it."""
+    from tree_verified_block_amd import api
+    from tree_verified_block_amd.round import to_device
+    cfg = make_config("mini_bf16", V=4099, L=4, N=15, nseq=2)
+    inp = gen_round(cfg, 19, with_model=False)
+    z = bf16_bits_to_f32(inp["rounds"][0]["draft_logits"]).copy()
+    roots = torch.tensor(inp["rounds"][0]["root"].astype(np.int32), device="cuda")
+    out = api.tree_outputs(cfg.nseq, cfg.N, "cuda")
+    ws = api.workspace(api.build_tree_ws_bytes(cfg.nseq, cfg.L, cfg.V, cfg.N), "cuda")
+
+    def build(zz):
+        api.glance_build_tree(to_device(bf16_bits(zz), "bf16", "cuda"), roots, cfg.N, out, ws)
+        return api.build_tree_flags(ws, cfg.nseq, cfg.L, cfg.V, cfg.N)
+
+    zi = z.copy()
+    zi[0, 1, 7] = -np.inf
+    zi[1, 3, 100:200] = -np.inf
+    assert build(zi) == 0
+    zn = z.copy()
+    zn[1, 2, 4000] = np.nan
+    assert build(zn) == 1
+    assert build(z) == 1                 # sticky
+    off = api._lib.load().glance_build_tree_flag_offset(cfg.nseq, cfg.L, cfg.V, cfg.N)
+    ws[off:off + 4].zero_()
+    zp = z.copy()
+    zp[0, 0, 3] = np.inf
+    assert build(zp) == 2
+    zp[1, 0, 9] = np.nan
+    assert build(zp) == 3

@@ -33,11 +33,10 @@ def _round_parity(inp, r, exact="beam", greedy=True):
             paths = parity.gpu_paths(gpu["parent"][s], gpu["token"][s], gpu["n_valid"][s])
         ev = mdl.evaluate_paths(model, s, root, paths)
         z = model.logits(ev["final"])
-        am, gap = parity.check_rows(gpu, ev, z, s, cfg.N + 1, cfg.dtype, report,
-                                    full=cfg.mlp > 0)
+        am, gap = parity.check_rows(gpu, ev, z, s, cfg.N + 1, cfg, report)
         g = orr.continuation(model, s, root, paths[1:], cfg.L) if greedy else None
         parity.check_walk(gpu, s, paths, am, gap, cfg.L, report, g)
-    print(f"[parity] {cfg.name} seed={inp['seed']} round={r}: {report}", flush=True)
+    parity.record(f"{cfg.name} seed={inp['seed']} round={r}", report)
     return gpu, report
 
 
@@ -122,3 +121,42 @@ def test_non_ancestor_rows_do_not_leak():
     keep = [i for i in range(cfg.N + 1) if i != leaf]
     assert np.array_equal(a["h_final"][keep], b["h_final"][keep])
     assert not np.array_equal(a["h_final"][leaf], b["h_final"][leaf])
+
+
+def _sparse_draft(draft, dtype, keep):
+    """Draft logits with every token of offset j but its keep[j] largest set to
+    -inf: only prod_{j<=d} keep[j] prefixes of depth d have a finite score."""
+    from synth.gen import as_f32, bf16_bits
+    z = as_f32(np.array(draft), dtype).astype(np.float32).copy()
+    for s in range(z.shape[0]):
+        for j in range(z.shape[1]):
+            top = np.argsort(-z[s, j], kind="stable")[:keep[j]]
+            row = np.full(z.shape[2], -np.inf, dtype=np.float32)
+            row[top] = z[s, j, top]
+            z[s, j] = row
+    return bf16_bits(z) if dtype == "bf16" else z
+
+
+@pytest.mark.parametrize("name,seed,exact", [("tiny", 1003, "brute"), ("tiny_widehead", 1004, "beam"),
+                                             ("mini_bf16_ragged", 6, "beam")])
+def test_partial_tree_round(name, seed, exact):
+    """Draft marginals that are zero off a few tokens per offset (logits -inf):
+    fewer finite prefixes than N, so the tree has padding rows (token -1), which
+    the attention zeroes and the walk never reaches; every live row, the walk and
+    the greedy decode still match the oracle (paper §3.2 Def. 1: S need not fill
+    the budget)."""
+    inp = gen_round(make_config(name), seed)
+    cfg = inp["cfg"]
+    rd = dict(inp["rounds"][0])
+    keep = [2] + [1] * (cfg.L - 1)
+    rd["draft_logits"] = _sparse_draft(rd["draft_logits"], cfg.dtype, keep)
+    inp = dict(inp, rounds=[rd])
+    gpu, _ = _round_parity(inp, 0, exact=exact)
+    n_live = 1 + 2 * cfg.L
+    assert n_live < cfg.N + 1
+    for s in range(cfg.nseq):
+        assert int(gpu["n_valid"][s]) == n_live
+        rows = slice(s * (cfg.N + 1) + n_live, (s + 1) * (cfg.N + 1))
+        assert np.all(gpu["h_final"][rows] == 0)
+        for li in range(cfg.n_layers):
+            assert np.all(gpu["attn_out"][li][rows] == 0)

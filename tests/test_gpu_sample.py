@@ -1,10 +1,12 @@
 """Sampling at temperature T on the GPU against the oracle's draws: every verify
 row's drawn token equals the oracle's Gumbel-max draw from the same Philox
 stream over the oracle's own logits, on the rows whose perturbed top-2 gap is
-above 2 e / T (e: the largest difference between the GPU's and the oracle's
-logits of the round, at least 1e-3; the two best scores can each move by e / T),
-the walk follows the drawn tokens, and the greedy statistics of the sampled
-call equal those of the greedy call."""
+above thr / T + 1e-5 (thr: the argmax decision threshold of the workload,
+max(1e-3, 2 dz) with dz the oracle-only float32-vs-float64 logit drift; 1e-5
+covers the float32 evaluation of the noise -ln(-ln U)); on the other rows the
+drawn token's perturbed score is within that margin of the best one.  The walk
+follows the drawn tokens, and the greedy statistics of the sampled call equal
+those of the greedy call."""
 import numpy as np
 import pytest
 
@@ -46,6 +48,7 @@ def test_sampled_round_matches_oracle_draws(name, seed, T, key, rnd):
     rd = inp["rounds"][0]
     n_rows = cfg.N + 1
     report = {"rows": 0, "rows_flagged": 0, "walk_exact": 0, "walk_flagged": 0}
+    flag = parity.decide_threshold(cfg.dtype, cfg.name) / T + 1e-5
     for s in range(cfg.nseq):
         root = int(rd["root"][s])
         paths = parity.gpu_paths(gpu["parent"][s], gpu["token"][s], gpu["n_valid"][s])
@@ -55,14 +58,17 @@ def test_sampled_round_matches_oracle_draws(name, seed, T, key, rnd):
         rows = s * n_rows + np.arange(nv)
         e = float(np.abs(gpu["logits"][rows].astype(np.float64) - z).max())
         assert e <= parity.tol_for(cfg.dtype) * np.abs(z).max(), e
-        flag = 2 * max(e, parity.GAP) / T
         otok, ogap = sp.sample_rows(z, T, key, rnd, rows=rows)
         sure = ogap > flag
         report["rows"] += nv
         report["rows_flagged"] += int((~sure).sum())
         g_tok = gpu["sample_tok"][rows]
-        assert np.array_equal(g_tok[sure], otok[sure]), (g_tok, otok, ogap)
         assert np.all((g_tok >= 0) & (g_tok < cfg.V))
+        assert np.array_equal(g_tok[sure], otok[sure]), (g_tok, otok, ogap)
+        # undecided rows: the GPU's draw is a valid near-best perturbed score
+        for i in np.nonzero(~sure)[0]:
+            sc = z[i] / T - np.log(-np.log(sp.uniforms(key, rnd, int(rows[i]), cfg.V)))
+            assert sc[int(g_tok[i])] >= sc.max() - flag, (i, sc[int(g_tok[i])], sc.max())
         # the GPU's gap is that of its own perturbed scores
         np.testing.assert_allclose(gpu["sample_gap"][rows][sure], ogap[sure],
                                    atol=flag + 1e-5, rtol=1e-5)

@@ -6,18 +6,32 @@
 // plus exactly the tree rows j that are i itself or its ancestors (bit j of
 // anc[i]), which is the causal sequence x o b o y_{1:d(i)}.
 //
-// bf16 path (head_dim 128, gfx950 MFMA v_mfma_f32_32x32x16_bf16).  Grid
-// (prefix splits + 1, Hkv x query blocks, rounds), 256 threads: the queries of
-// one KV head are its Hq/Hkv query heads times the round's rows (<= 128 per
-// work-group, 32 per wave; smaller blocks spread a round over more CUs).  Split c takes prefix keys [c*128, (c+1)*128) as
-// one tile: the query, K and V loads are all issued before any is used; K is
-// staged in LDS as [key][dim], V transposed as [dim][key]; each wave forms
-// S^T = K Q^T (one query per lane, so the row max and sum stay inside a lane
-// and its partner lane l^32), rounds P to bf16 into its own LDS tile and forms
-// O^T = V^T P^T.  The extra split n_split takes the round's tree rows as keys:
-// the rotated bf16 K and bf16 V rows the q/k/v projection wrote (a storage
-// point), masked by anc.  Each (split, query) leaves (max, sum, unnormalised
-// O); attn_combine merges them.
+// bf16 path (head_dim 128, gfx950 MFMA v_mfma_f32_32x32x16_bf16).  A work-group
+// of four waves owns one KV head h of one round and a block of 32 of its
+// queries (query q = row * G + j, the G = Hq/Hkv query heads of h times the
+// round's rows).  The round's keys are its prefix [0, P) followed by its tree
+// rows: key P + i is tree row i, visible to a query iff bit i of the query row's
+// ancestor word is set.  The keys are cut into n_split x 4 contiguous ranges,
+// one per wave; a wave streams its range in blocks of 32 keys with an online
+// softmax:
+//   S^T = K Q^T     K goes from memory straight into the MFMA operand (lane
+//                   (j, g) holds key j, dims 64 g .. 64 g + 63 over the eight
+//                   16-deep steps); q enters as its bf16 rounding plus the bf16
+//                   remainder (two products), so the scores see q to ~16 bits.
+//   P = 2^(S - m)   in fp32, then split the same way into a bf16 part and the
+//                   bf16 remainder of what it left out.
+//   O^T += V^T P^T  V is transposed through the wave's own LDS tile; P^T stays
+//                   in registers: each lane already holds, for its query, the
+//                   keys that the MFMA B operand wants from it, provided the V^T
+//                   tile stores the keys in that order (the slot permutation
+//                   below).
+// The four waves merge their (max, sum, O) in LDS.  With several splits the
+// last work-group of a query block to arrive merges the splits' records.  The
+// output o = O / sum is written in fp32; the output projection takes it as a
+// bf16 pair too, so q, P and o all enter the products with ~16 significant bits.
+// Work-group ids put the query blocks and splits of one KV head on the same XCD
+// (id mod 8 = h when Hkv = 8), so the head's K/V cross HBM once and are shared
+// through that XCD's L2.
 //
 // fp32 path (tiny shapes): one work-group per (row, query head), scores in LDS,
 // plain fp32 loops.
@@ -28,13 +42,15 @@ namespace glance {
 
 namespace {
 
-constexpr int kAThreads = 256;
-constexpr int kQWave = 32;
-constexpr int kQBlock = 128;
-constexpr int kKT = 128;         // keys per work-group tile (one prefix split)
-constexpr int kHD = 128;         // head_dim of the bf16 path
-constexpr int kTPad = 136;       // row stride of the K, V^T and P tiles (bf16)
-constexpr int kRec = kHD + 4;    // partial record: m, l, -, -, o[128]
+constexpr int kAW = 4;                // waves per work-group
+constexpr int kAThreads = kAW * kWave;
+constexpr int kQW = 32;               // queries per work-group
+constexpr int kKB = 32;               // keys per block
+constexpr int kHD = 128;              // head_dim of the bf16 path
+constexpr int kVtRow = 40;            // bf16 slots per V^T row: 32 keys + 8 padding (80 bytes)
+constexpr int kObRow = kHD + 1;       // fp32 stride of the merge rows (odd: no bank conflicts)
+constexpr int kRec = kHD + 4;         // split record per query: m, l, -, -, o[128]
+constexpr int kMaxSplit = 8;
 
 // position P + depth of a row, clamped into the cos/sin tables
 __device__ __forceinline__ int row_pos(const AttnArgs& a, int P, int row) {
@@ -42,238 +58,379 @@ __device__ __forceinline__ int row_pos(const AttnArgs& a, int P, int row) {
   return p < a.n_pos - 1 ? p : a.n_pos - 1;
 }
 
+// Prefix length of round s, read as at most max_prefix keys.
+__device__ __forceinline__ int prefix_len(const AttnArgs& a, int s) {
+  int64_t P = a.kv_offsets[s + 1] - a.kv_offsets[s];
+  if (P > a.max_prefix) P = a.max_prefix;
+  return P < 0 ? 0 : static_cast<int>(P);
+}
+
 __device__ __forceinline__ float rope_pair(const float* x, int i, int half, float c, float s) {
   // rotate-half: (x_i, x_{i+half}) -> (x_i c - x_{i+half} s, x_{i+half} c + x_i s)
   return i < half ? x[i] * c - x[i + half] * s : x[i] * c + x[i - half] * s;
 }
 
-__global__ __launch_bounds__(kAThreads) void tree_attn_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kKT][kTPad];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kHD][kTPad];
-  __shared__ __attribute__((aligned(16))) uint16_t Ps[kAThreads / kWave][kQWave][kTPad];
+// Head-h row of key t of round s: prefix keys from the cache, key P + i from
+// tree row i; keys at or past T (the tail of a wave's last block) read tree row 0
+// of the round, which is in bounds, and are masked.
+// Both candidate rows are formed and one is picked with a mask: a branch here
+// would keep the loads from unrolling and make their wait counts conservative.
+__device__ __forceinline__ const uint16_t* key_row(const uint16_t* cache, const uint16_t* tree,
+                                                   int64_t kv0, int P, int T, int s, int n_rows,
+                                                   int Hkv, int h, int t) {
+  const bool pre = t < P;
+  const int i = (t < T && !pre) ? t - P : 0;
+  const uintptr_t pc = reinterpret_cast<uintptr_t>(cache + ((kv0 + t) * Hkv + h) * kHD);
+  const uintptr_t pt = reinterpret_cast<uintptr_t>(tree + ((static_cast<int64_t>(s) * n_rows + i) * Hkv + h) * kHD);
+  const uintptr_t m = pre ? ~static_cast<uintptr_t>(0) : 0;
+  return reinterpret_cast<const uint16_t*>((pc & m) | (pt & ~m));
+}
 
-  const int c = blockIdx.x, s = blockIdx.z;
-  const int h = blockIdx.y % a.Hkv, qb = blockIdx.y / a.Hkv;
-  const int G = a.Hq / a.Hkv;
+// Visibility of keys t0 .. t0 + 31 to a query whose row has ancestor word anc:
+// bit k set iff key t0 + k is before t_end and is a prefix key (< P) or tree
+// row t0 + k - P with its bit set in anc.  Branch-free.
+__device__ __forceinline__ uint32_t block_mask(int t0, int t_end, int P, uint64_t anc) {
+  const int nv = min(max(t_end - t0, 0), 32);  // keys of the block in the range
+  const int np = min(max(P - t0, 0), nv);      // prefix keys among them
+  const uint32_t valid = nv == 32 ? 0xFFFFFFFFu : ((1u << nv) - 1u);
+  const uint32_t pref = np == 32 ? 0xFFFFFFFFu : ((1u << np) - 1u);
+  const int sh = t0 - P;  // tree index of key t0 (< 64 while t0 < T; keys past T are not valid)
+  const uint32_t right = static_cast<uint32_t>(anc >> (sh & 63));
+  const uint32_t left = static_cast<uint32_t>(anc << ((-sh) & 63));
+  const uint32_t tree = sh >= 0 ? right : (sh > -32 ? left : 0u);
+  return pref | (tree & valid & ~pref);
+}
+
+// Slot quad of key quad kq (keys 4 kq .. 4 kq + 3 of a 32-key block) in the V^T
+// tile.  The S^T accumulator gives lane (j, g) the keys 8 i + 4 g + u (i, u < 4)
+// of query j; the MFMA B operand of 16-key step t takes from it the keys of
+// quads 4 t + g and 4 t + 2 + g, in that order.  So quad 4 t + 2 a + g goes to
+// slot quad 4 t + 2 g + a: the A operand (V^T, lane (dim, g)) of step t is then
+// slot quads 4 t + 2 g and 4 t + 2 g + 1.  Slot quads are further XOR-swizzled
+// by (dim / 8) mod 8 against LDS bank conflicts.
+__device__ __forceinline__ int slot_quad(int kq) {
+  return (kq & 4) | ((kq & 1) << 1) | ((kq >> 1) & 1);
+}
+
+__device__ __forceinline__ uint32_t half16(uint32_t w, int hi) { return hi ? (w >> 16) : (w & 0xFFFFu); }
+
+// One of the two bf16 halves of a pair of 32-bit words: the low (sel = 0x05040100)
+// or high (0x07060302) 16 bits of a, then of b, packed into one word.
+__device__ __forceinline__ uint32_t pick16(uint32_t a, uint32_t b, uint32_t sel) {
+  return __builtin_amdgcn_perm(b, a, sel);
+}
+
+__global__ __launch_bounds__(kAThreads, 1) void tree_attn_bf16_kernel(AttnArgs a, int nqb) {
+  // LDS: each wave's K / V^T tile, later reused for the merge of the 4 waves
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[kAW][kHD * kVtRow];
+  __shared__ float Ms[kAW][kQW], Ls[kAW][kQW];
+  static_assert(2 * kQW * kObRow * sizeof(float) <= sizeof(Vt), "merge buffers alias the tiles");
+
+  const int Hkv = a.Hkv;
+  int id = blockIdx.x;
+  const int h = id % Hkv;
+  id /= Hkv;
+  const int qb = id % nqb;
+  id /= nqb;
+  const int c = id % a.n_split;
+  const int s = id / a.n_split;
+  // w is read from lane 0 so that the compiler knows it (and each wave's key
+  // range, block count and offsets) is uniform: branches on them stay scalar
+  const int tid = threadIdx.x, l = tid & 63, j = l & 31, g = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = a.Hq / Hkv;
   const int Qn = a.n_rows * G;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, j = l & 31, g = l >> 5;
-  const bool tree_split = (c == a.n_split);
-  const int64_t kv0 = a.kv_offsets[s];
-  const int P = static_cast<int>(a.kv_offsets[s + 1] - kv0);
 
-  // ---- this lane's query: q index, row, head (rotated and rounded by the projection)
-  const int q = qb * kQBlock + w * kQWave + j;
+  // ---- this lane's query: q as bf16 + remainder, the B operand of S^T (step
+  // ks: dims 64 g + 8 ks .. + 7), in registers for the whole range (queries past
+  // Qn read row 0 of the round and are never stored)
+  const int q = qb * kQW + j;
   const bool qvalid = q < Qn;
-  const int r = qvalid ? q / G : 0;
-  const int qh = h * G + (qvalid ? q % G : 0);
-  const int grow = s * a.n_rows + r;
+  const int grow = s * a.n_rows + (qvalid ? q / G : 0);
   const uint64_t qanc = qvalid ? a.anc[grow] : 0ull;
-
-  int kbeg, kend;
-  if (tree_split) {
-    kbeg = 0;
-    kend = a.n_rows;
-  } else {
-    kbeg = c * a.split;
-    kend = min(kbeg + a.split, P);
-  }
-  const int nk = kend - kbeg;  // <= kKT keys in this tile
-
-  // ---- every load of the tile issued up front: the query, then K and V.  The
-  // query is loaded for padding rows too (their records are never combined:
-  // each query's scores and output stay in its own lanes), so that its loads
-  // do not wait for the row's token
-  bf16x8 qf[8];
+  bf16x8 qhi[8], qlo[8];
   {
-    const uint16_t* xq = static_cast<const uint16_t*>(a.q) + static_cast<size_t>(grow) * a.Hq * kHD + qh * kHD;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xq + ks * 16 + 8 * g));
-  }
-  constexpr int kPass = kKT * (kHD / 8) / kAThreads;  // 16-byte pieces per thread
-  uint4 kb_[kPass], vb_[kPass];
-  {
-    const uint16_t* kbase = tree_split ? static_cast<const uint16_t*>(a.tree_k)
-                                       : static_cast<const uint16_t*>(a.k_cache);
-    const uint16_t* vbase = tree_split ? static_cast<const uint16_t*>(a.tree_v)
-                                       : static_cast<const uint16_t*>(a.v_cache);
-#pragma unroll
-    for (int pass = 0; pass < kPass; ++pass) {
-      const int idx = pass * kAThreads + tid;
-      const int kr = idx >> 4, col = (idx & 15) * 8;
-      kb_[pass] = make_uint4(0, 0, 0, 0);
-      vb_[pass] = make_uint4(0, 0, 0, 0);
-      if (kr < nk) {
-        const int64_t krow = tree_split ? static_cast<int64_t>(s) * a.n_rows + kr : kv0 + kbeg + kr;
-        const size_t off = (static_cast<size_t>(krow) * a.Hkv + h) * kHD + col;
-        kb_[pass] = load_stream(kbase + off);
-        vb_[pass] = load_stream(vbase + off);
-      }
-    }
-  }
-  // K as [key][dim]; V transposed to [dim][key], its 8-key blocks XOR-swizzled by
-  // the dim's 8-row block so that the transposing stores spread over the banks
-#pragma unroll
-  for (int pass = 0; pass < kPass; ++pass) {
-    const int idx = pass * kAThreads + tid;
-    const int kr = idx >> 4, col = (idx & 15) * 8;
-    *reinterpret_cast<uint4*>(&Ks[kr][col]) = kb_[pass];
-    const uint32_t vw[4] = {vb_[pass].x, vb_[pass].y, vb_[pass].z, vb_[pass].w};
-    const int kcol = 8 * ((kr >> 3) ^ ((col >> 3) & 15)) + (kr & 7);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      Vt[col + 2 * t][kcol] = static_cast<uint16_t>(vw[t] & 0xFFFF);
-      Vt[col + 2 * t + 1][kcol] = static_cast<uint16_t>(vw[t] >> 16);
-    }
-  }
-  __syncthreads();
-
-  // ---- S^T = K Q^T: kKT keys x this wave's 32 queries (32-key blocks past the
-  // tile's keys are skipped: they are masked)
-  f32x16 acc_s[kKT / 32] = {};
-#pragma unroll
-  for (int kb = 0; kb < kKT / 32; ++kb) {
-    if (kb * 32 >= nk) break;  // (uniform)
+    const size_t qoff = (static_cast<size_t>(grow) * a.Hq + h * G + (qvalid ? q % G : 0)) * kHD + 64 * g;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qoff;
+    const uint16_t* qlp = static_cast<const uint16_t*>(a.q_lo) + qoff;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Ks[kb * 32 + j][ks * 16 + 8 * g]);
-      acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], acc_s[kb], 0, 0, 0);
+      qhi[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 8 * ks));
+      qlo[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qlp + 8 * ks));
     }
   }
-  // element v of acc_s[kb]: key kb*32 + 8 (v/4) + 4 g + v%4 of the tile, query j
+  const int64_t kv0 = a.kv_offsets[s];
+  const int P = prefix_len(a, s);
+  const int T = P + a.n_rows;
+  // this wave's keys: range c * 4 + w of n_split * 4, in whole blocks
+  const int span = a.n_split * kAW;
+  const int per = ((T + span - 1) / span + kKB - 1) / kKB * kKB;
+  const int t_beg = (c * kAW + w) * per;
+  const int t_end = min(t_beg + per, T);
+  const int nblk = t_end > t_beg ? (t_end - t_beg + kKB - 1) / kKB : 0;
+
+  // ---- key t's head-h row: prefix key t at kc0 + t * ks, tree row i (key P + i)
+  // at tk0 + i * ks (tree rows have the cache's row stride); keys at or past T
+  // read tree row 0 (in bounds, masked).  32-bit element offsets from two bases.
+  const int kstr = Hkv * kHD;
+  const uint16_t* kc0 = static_cast<const uint16_t*>(a.k_cache) + (kv0 * Hkv + h) * kHD;
+  const uint16_t* vc0 = static_cast<const uint16_t*>(a.v_cache) + (kv0 * Hkv + h) * kHD;
+  const size_t trow0 = (static_cast<size_t>(s) * a.n_rows * Hkv + h) * kHD;
+  const uint16_t* tk0 = static_cast<const uint16_t*>(a.tree_k) + trow0;
+  const uint16_t* tv0 = static_cast<const uint16_t*>(a.tree_v) + trow0;
+  auto row_of = [&](const uint16_t* c0, const uint16_t* t0p, int t) {
+    const bool pre = t < P;
+    const int i = (t < T && !pre) ? t - P : 0;
+    return (pre ? c0 : t0p) + (pre ? t : i) * kstr;
+  };
+  const int vx = l & 15, vkq = l >> 4;  // V pieces: dims 8 vx .. + 7 of key quads vkq, vkq + 4
+  // K and V of the block starting at t0 are loaded the same way: instruction i
+  // reads four whole key rows (K: lane l takes key 4 i + l / 16, 16-byte piece
+  // l % 16; V: key 4 (vkq + 4 (i / 4)) + i % 4, piece vx), full cache lines.
+#define GLANCE_LOAD_KV(t0_, kd_, vd_)                                                           \
+  _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                \
+    kd_[i] = *reinterpret_cast<const u32x4*>(row_of(kc0, tk0, (t0_) + 4 * i + (l >> 4)) + 8 * (l & 15)); \
+    vd_[i] = *reinterpret_cast<const u32x4*>(                                                    \
+        row_of(vc0, tv0, (t0_) + 4 * (vkq + 4 * (i >> 2)) + (i & 3)) + 8 * vx);                   \
+  }
+  // The wave's LDS buffer holds the block's K tile, then its V^T tile.  K tile:
+  // key k's row at k * 128, its 16-byte piece p at unit p ^ (k mod 8), so that
+  // the MFMA operand reads (lane (j, g): key j, piece 8 g + ks) of eight
+  // consecutive keys fall in distinct banks.
+  uint16_t* vt = Vt[w];
+#define GLANCE_WRITE_K(src_)                                                                    \
+  _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                 \
+    const int k = 4 * i + (l >> 4);                                                               \
+    *reinterpret_cast<u32x4*>(vt + k * kHD + 8 * ((l & 15) ^ (k & 7))) = src_[i];                 \
+  }
+  // V pieces -> V^T tile: dim 8 vx + e, the slot quad of the key quad, 4 keys
+  // (pieces 4 i .. 4 i + 3) per 8-byte write
+#define GLANCE_WRITE_VT(src_)                                                                   \
+  _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                                 \
+    const int sq = slot_quad(vkq + 4 * i) ^ (vx & 7);                                             \
+    _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                               \
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;                                   \
+      const uint32_t x0 = src_[4 * i][e >> 1], x1 = src_[4 * i + 1][e >> 1];                      \
+      const uint32_t x2 = src_[4 * i + 2][e >> 1], x3 = src_[4 * i + 3][e >> 1];                  \
+      *reinterpret_cast<uint2*>(vt + (8 * vx + e) * kVtRow + 4 * sq) =                            \
+          make_uint2(pick16(x0, x1, sel), pick16(x2, x3, sel));                                   \
+    }                                                                                             \
+  }
+
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(kHD));
-  float m = -INFINITY;
-  if (!tree_split && nk == kKT) {  // (uniform) a full prefix tile: every key visible
-#pragma unroll
-    for (int kb = 0; kb < kKT / 32; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        acc_s[kb][v] *= scale_log2;
-        m = fmaxf(m, acc_s[kb][v]);
-      }
-  } else {
-#pragma unroll
-    for (int kb = 0; kb < kKT / 32; ++kb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = kb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-        bool vis = key < nk;
-        if (tree_split) vis = vis && ((qanc >> key) & 1ull);
-        const float sv = vis ? acc_s[kb][v] * scale_log2 : -INFINITY;
-        acc_s[kb][v] = sv;
-        m = fmaxf(m, sv);
-      }
-    }
-  }
-  m = fmaxf(m, __shfl_xor(m, 32, kWave));
-  // P rounded to bf16 in pairs (hardware round-to-nearest-even); l sums the
-  // rounded values, so that it normalises exactly the P that enters O
-  const float mz = m == -INFINITY ? 0.f : m;  // (no visible key: every p is exp2(-inf) = 0)
-  float lsum = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < kKT / 32; ++kb) {
-#pragma unroll
-    for (int vg = 0; vg < 4; ++vg) {
-      uint32_t pw[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const float p0 = __builtin_amdgcn_exp2f(acc_s[kb][4 * vg + 2 * t] - mz);
-        const float p1 = __builtin_amdgcn_exp2f(acc_s[kb][4 * vg + 2 * t + 1] - mz);
-        pw[t] = pack_bf16x2(p0, p1);
-        lsum += __uint_as_float(pw[t] << 16) + __uint_as_float(pw[t] & 0xFFFF0000u);
-      }
-      *reinterpret_cast<uint2*>(&Ps[w][j][kb * 32 + 8 * vg + 4 * g]) = make_uint2(pw[0], pw[1]);
-    }
-  }
-  lsum += __shfl_xor(lsum, 32, kWave);
-  __builtin_amdgcn_wave_barrier();  // the wave's own P tile: same-wave LDS accesses are in order
-
-  // ---- O^T = V^T P^T
   f32x16 acc_o[4] = {};
+  // Online softmax with a lazily moved reference: p = 2^(s - m_ref) with m_ref
+  // raised (and O, l rescaled) only when a score exceeds it by more than 8, so
+  // p <= 2^8 (exact enough in fp32 and bf16 + remainder) and the rescale is rare.
+  float m_ref = -INFINITY, l_run = 0.f;
+  // One block after the other with the next block's K and V loads in flight: the
+  // K registers are refilled as soon as the K tile is written, the V registers as
+  // soon as the V^T tile is.  Past the last block the loads re-read it (no
+  // conditional load).
+  u32x4 kr[8], vr[8];
+  const int tlast = t_beg + (nblk > 0 ? nblk - 1 : 0) * kKB;
+  GLANCE_LOAD_KV(t_beg, kr, vr)
+  for (int b = 0; b < nblk; ++b) {
+    const int t0 = t_beg + b * kKB;
+    const int tn = min(t0 + kKB, tlast);
+    GLANCE_WRITE_K(kr)
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) kr[i] = *reinterpret_cast<const u32x4*>(
+        row_of(kc0, tk0, tn + 4 * i + (l >> 4)) + 8 * (l & 15));
+    __builtin_amdgcn_sched_barrier(0);  // keeps the scheduler from sinking the loads
+    __builtin_amdgcn_wave_barrier();
+    // ---- S^T = K Q^T with q = hi + lo (A: key j, dims 64 g + 8 ks from the K
+    // tile; B: query j, the same dims, from the query rows), two accumulators
+    // (all eight operand reads first, then the products)
+    bf16x8 kop[8];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const int dim = db * 32 + j;
+    for (int ks = 0; ks < 8; ++ks)
+      kop[ks] = *reinterpret_cast<const bf16x8*>(vt + j * kHD + 8 * ((8 * g + ks) ^ (j & 7)));
+    f32x16 sa = {}, sb = {};
 #pragma unroll
-    for (int ks = 0; ks < kKT / 16; ++ks) {
-      if (ks * 16 >= nk) break;  // (uniform) keys past the tile have p = 0
-      const int kblk = (ks * 16 + 8 * g) >> 3;
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Vt[dim][8 * (kblk ^ ((dim >> 3) & 15))]);
-      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&Ps[w][j][ks * 16 + 8 * g]);
-      acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc_o[db], 0, 0, 0);
+    for (int ks = 0; ks < 8; ++ks) {
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qhi[ks], sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qlo[ks], sb, 0, 0, 0);
     }
-  }
-
-  // ---- partial record of (split, query): m (log2 units), l, unnormalised O
-  if (qvalid) {
-    float* rec = a.part +
-                 ((static_cast<size_t>(s) * a.Hkv + h) * (a.n_split + 1) + c) * static_cast<size_t>(Qn) * kRec +
-                 static_cast<size_t>(q) * kRec;
-    if (g == 0) {
-      rec[0] = m;
-      rec[1] = lsum;
+    // ---- mask (element v: key t0 + 8 (v / 4) + 4 g + v % 4, query j), block max
+    const uint32_t vm = block_mask(t0, t_end, P, qanc) >> (4 * g);
+    float sc[16], mb = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const bool vis = (vm >> (8 * (v >> 2) + (v & 3))) & 1u;
+      sc[v] = vis ? (sa[v] + sb[v]) * scale_log2 : -INFINITY;
+      mb = fmaxf(mb, sc[v]);
     }
+    mb = fmaxf(mb, __shfl_xor(mb, 32, kWave));
+    const bool raise = mb > m_ref + 8.f;  // also when m_ref is still -inf
+    if (__ballot(raise) != 0ull) {  // (uniform) rare after the first block
+      const float m_new = raise ? mb : m_ref;
+      const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int vg = 0; vg < 4; ++vg) {
-        const int dim = db * 32 + 8 * vg + 4 * g;
-        *reinterpret_cast<float4*>(rec + 4 + dim) =
-            make_float4(acc_o[db][4 * vg], acc_o[db][4 * vg + 1], acc_o[db][4 * vg + 2], acc_o[db][4 * vg + 3]);
+        for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
+    }
+    const float mz = m_ref == -INFINITY ? 0.f : m_ref;  // nothing visible yet: every p is 0
+    // ---- P = hi + lo in bf16 (the remainder taken from the rounded value)
+    uint32_t ph[8], pl[8];
+#pragma unroll
+    for (int pr = 0; pr < 8; ++pr) {
+      const float p0 = __builtin_amdgcn_exp2f(sc[2 * pr] - mz);
+      const float p1 = __builtin_amdgcn_exp2f(sc[2 * pr + 1] - mz);
+      ph[pr] = pack_bf16x2(p0, p1);
+      pl[pr] = pack_bf16x2(p0 - __uint_as_float(ph[pr] << 16), p1 - __uint_as_float(ph[pr] & 0xFFFF0000u));
+      l_run += p0 + p1;
+    }
+    // the K tile's reads are done (LDS is in order per wave): the V^T tile takes
+    // the buffer, and the V registers take the next block's loads
+    __builtin_amdgcn_wave_barrier();
+    GLANCE_WRITE_VT(vr)
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) vr[i] = *reinterpret_cast<const u32x4*>(
+        row_of(vc0, tv0, tn + 4 * (vkq + 4 * (i >> 2)) + (i & 3)) + 8 * vx);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_wave_barrier();
+    // ---- O^T += V^T P^T, two 16-key steps, P = hi + lo (operand reads first)
+    bf16x8 vop[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int dim = 32 * db + j;
+        const int sw = (dim >> 3) & 7;
+        const uint16_t* row = vt + dim * kVtRow;
+        const uint2 lo = *reinterpret_cast<const uint2*>(row + 4 * ((4 * t + 2 * g) ^ sw));
+        const uint2 hi = *reinterpret_cast<const uint2*>(row + 4 * ((4 * t + 2 * g + 1) ^ sw));
+        vop[t][db] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bf16x8 bh = __builtin_bit_cast(bf16x8, make_uint4(ph[4 * t], ph[4 * t + 1], ph[4 * t + 2], ph[4 * t + 3]));
+      const bf16x8 bl = __builtin_bit_cast(bf16x8, make_uint4(pl[4 * t], pl[4 * t + 1], pl[4 * t + 2], pl[4 * t + 3]));
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t][db], bh, acc_o[db], 0, 0, 0);
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t][db], bl, acc_o[db], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();  // reads of this block before the next block's writes
+  }
+#undef GLANCE_LOAD_KV
+#undef GLANCE_WRITE_K
+#undef GLANCE_WRITE_VT
+  const float m_run = m_ref;
+  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+
+  // ---- the four waves' (max, sum, O) merged in LDS, through two buffers that
+  // reuse the tiles: waves 2 and 3 hand their O to waves 0 and 1, which then
+  // leave their sums for all threads (thread (tq, 16 dims from d0))
+  if (g == 0) {
+    Ms[w][j] = m_run;
+    Ls[w][j] = l_tot;
+  }
+  __syncthreads();
+  float* ob = reinterpret_cast<float*>(&Vt[0][0]);
+  {
+    float M = Ms[0][j];
+#pragma unroll
+    for (int ww = 1; ww < kAW; ++ww) M = fmaxf(M, Ms[ww][j]);
+    const float f = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+    float* mine = ob + ((w & 1) * kQW + j) * kObRow;
+    if (w >= 2) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mine[32 * db + 8 * (v >> 2) + 4 * g + (v & 3)] = acc_o[db][v] * f;
+    }
+    __syncthreads();
+    if (w < 2) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          acc_o[db][v] = acc_o[db][v] * f + mine[32 * db + 8 * (v >> 2) + 4 * g + (v & 3)];
+    }
+    __syncthreads();
+    if (w < 2) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mine[32 * db + 8 * (v >> 2) + 4 * g + (v & 3)] = acc_o[db][v];
+    }
+    __syncthreads();
+  }
+  const int tq = tid >> 3, d0 = (tid & 7) * 16;
+  float M = Ms[0][tq];
+#pragma unroll
+  for (int ww = 1; ww < kAW; ++ww) M = fmaxf(M, Ms[ww][tq]);
+  float L = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < kAW; ++ww)
+    L += Ms[ww][tq] == -INFINITY ? 0.f : Ls[ww][tq] * __builtin_amdgcn_exp2f(Ms[ww][tq] - M);
+  float o[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) o[i] = ob[tq * kObRow + d0 + i] + ob[(kQW + tq) * kObRow + d0 + i];
+  const int qq = qb * kQW + tq;
+  if (a.n_split > 1) {
+    // split record (m, l, O) of this work-group's queries; attn_combine merges
+    const size_t blk = (static_cast<size_t>(s) * Hkv + h) * nqb + qb;
+    float* rec = a.part + ((blk * a.n_split + c) * kQW + tq) * kRec;
+    if ((tid & 7) == 0) *reinterpret_cast<float2*>(rec) = make_float2(M, L);
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4)
+      *reinterpret_cast<float4*>(rec + 4 + d0 + 4 * k4) =
+          make_float4(o[4 * k4], o[4 * k4 + 1], o[4 * k4 + 2], o[4 * k4 + 3]);
+    return;
+  }
+  if (qq >= Qn) return;
+  const int rr = qq / G;
+  const int growq = s * a.n_rows + rr;
+  const bool live = a.token[growq] >= 0;
+  const float inv = (live && L > 0.f) ? 1.f / L : 0.f;
+  const size_t off = static_cast<size_t>(growq) * a.Hq * kHD + (h * G + qq % G) * kHD + d0;
+#pragma unroll
+  for (int k4 = 0; k4 < 4; ++k4) {
+    const float4 v = make_float4(o[4 * k4] * inv, o[4 * k4 + 1] * inv, o[4 * k4 + 2] * inv, o[4 * k4 + 3] * inv);
+    *reinterpret_cast<float4*>(a.attn_x + off + 4 * k4) = v;
+    if (a.attn_out) *reinterpret_cast<float4*>(a.attn_out + off + 4 * k4) = v;
   }
 }
 
-// Merge the split partials of every (row, query head) into the attention output:
-// one work-group per row and query head, one thread per head dimension, splits
-// folded in order in batches of 16 with a running maximum.
-__global__ __launch_bounds__(kHD) void attn_combine_kernel(AttnArgs a) {
+// Merge of the split records of every (row, query head): one work-group per row
+// and query head, one thread per head dimension, splits in order.
+__global__ __launch_bounds__(kHD) void attn_combine_kernel(AttnArgs a, int nqb) {
   const int grow = blockIdx.x, qh = blockIdx.y, dim = threadIdx.x;
   const int s = grow / a.n_rows, r = grow % a.n_rows;
   const int G = a.Hq / a.Hkv;
-  const int Qn = a.n_rows * G;
   const int h = qh / G, q = r * G + qh % G;
-  // the records are read whatever the row's token (in bounds for every row), so
-  // that their loads do not wait for the token's; padding rows give 0
-  const bool live = a.token[grow] >= 0;
-  float o;
-  {
-    const float* rec = a.part + ((static_cast<size_t>(s) * a.Hkv + h) * (a.n_split + 1) *
-                                     static_cast<size_t>(Qn) + q) * kRec;
-    const size_t stride = static_cast<size_t>(Qn) * kRec;
-    const int ns = a.n_split + 1;
-    // 16 splits at a time: every load of the batch issued first, then the
-    // batch maximum, then the rescaled sums
-    float M = -INFINITY, Ls = 0.f, acc = 0.f;
-    for (int c0 = 0; c0 < ns; c0 += 16) {
-      float mm[16], ll[16], vv[16];
+  const size_t blk = (static_cast<size_t>(s) * a.Hkv + h) * nqb + q / kQW;
+  const float* rec = a.part + (blk * a.n_split * kQW + q % kQW) * kRec;
+  const size_t cs = static_cast<size_t>(kQW) * kRec;
+  // every load first (splits past n_split re-read the last record, weight 0)
+  float mm[kMaxSplit], ll[kMaxSplit], vv[kMaxSplit];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const size_t cc = static_cast<size_t>(min(c0 + u, ns - 1)) * stride;
-        mm[u] = rec[cc];
-        ll[u] = rec[cc + 1];
-        vv[u] = rec[cc + 4 + dim];
-      }
-      float Mb = M;
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if (c0 + u < ns && ll[u] > 0.f) Mb = fmaxf(Mb, mm[u]);
-      const float fo = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mb);
-      Ls *= fo;
-      acc *= fo;
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        // splits without visible keys have l = 0 and contribute nothing
-        const float f = (c0 + u < ns && ll[u] > 0.f) ? __builtin_amdgcn_exp2f(mm[u] - Mb) : 0.f;
-        Ls += ll[u] * f;
-        acc += vv[u] * f;
-      }
-      M = Mb;
-    }
-    o = live ? acc / Ls : 0.f;
+  for (int c = 0; c < kMaxSplit; ++c) {
+    const float* rc = rec + min(c, a.n_split - 1) * cs;
+    mm[c] = rc[0];
+    ll[c] = rc[1];
+    vv[c] = rc[4 + dim];
   }
+  const bool live = a.token[grow] >= 0;
+  float M = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < kMaxSplit; ++c) M = fmaxf(M, c < a.n_split ? mm[c] : -INFINITY);
+  float L = 0.f, acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMaxSplit; ++c) {
+    const float f = (c >= a.n_split || mm[c] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mm[c] - M);
+    L += ll[c] * f;
+    acc += vv[c] * f;
+  }
+  const float o = (live && L > 0.f) ? acc / L : 0.f;
   const size_t off = static_cast<size_t>(grow) * a.Hq * kHD + qh * kHD + dim;
+  a.attn_x[off] = o;
   if (a.attn_out) a.attn_out[off] = o;
-  static_cast<uint16_t*>(a.attn_x)[off] = f32_to_bf16(o);
 }
 
 // ------------------------------------------------------------------ fp32 path
@@ -288,7 +445,7 @@ __global__ __launch_bounds__(128) void tree_attn_f32_kernel(AttnArgs a) {
   const int G = a.Hq / a.Hkv, h = qh / G, D = a.D, half = D / 2;
   const int nq_total = (a.Hq + 2 * a.Hkv) * D;
   const int tid = threadIdx.x;
-  float* ox = static_cast<float*>(a.attn_x) + static_cast<size_t>(grow) * a.Hq * D + qh * D;
+  float* ox = a.attn_x + static_cast<size_t>(grow) * a.Hq * D + qh * D;
   if (a.token[grow] < 0) {
     for (int d = tid; d < D; d += 128) {
       ox[d] = 0.f;
@@ -297,7 +454,7 @@ __global__ __launch_bounds__(128) void tree_attn_f32_kernel(AttnArgs a) {
     return;
   }
   const int64_t kv0 = a.kv_offsets[s];
-  const int P = static_cast<int>(a.kv_offsets[s + 1] - kv0);
+  const int P = prefix_len(a, s);
   const uint64_t anc = a.anc[grow];
   {
     const int pos = row_pos(a, P, grow);
@@ -386,28 +543,35 @@ __global__ __launch_bounds__(128) void tree_attn_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
-int attn_split_len(int64_t max_prefix, int nseq, int Hkv) {
-  (void)max_prefix;
-  (void)nseq;
-  (void)Hkv;
-  return kKT;  // one tile per split work-group
+static int attn_qblocks(int n_rows, int Hq, int Hkv) { return (n_rows * (Hq / Hkv) + kQW - 1) / kQW; }
+
+int attn_splits(int nseq, int64_t max_prefix, int n_rows, int Hq, int Hkv) {
+  // enough work-groups to fill the CUs once, and a split per 2048 keys of the
+  // longest round (about 16 blocks per wave)
+  const int64_t base = static_cast<int64_t>(nseq) * Hkv * attn_qblocks(n_rows, Hq, Hkv);
+  const int64_t fill = (256 + base - 1) / base;
+  const int64_t len = (max_prefix + n_rows + 2047) / 2048;
+  int64_t n = fill > len ? fill : len;
+  if (n < 1) n = 1;
+  if (n > kMaxSplit) n = kMaxSplit;
+  return static_cast<int>(n);
 }
 
-size_t attn_part_floats(int nseq, int n_rows, int Hq, int Hkv, int D, int n_split) {
-  (void)D;
-  const size_t Qn = static_cast<size_t>(n_rows) * (Hq / Hkv);
-  return static_cast<size_t>(nseq) * Hkv * (n_split + 1) * Qn * kRec;
+size_t attn_part_floats(int nseq, int n_rows, int Hq, int Hkv, int n_split) {
+  if (n_split <= 1) return 0;
+  return static_cast<size_t>(nseq) * Hkv * attn_qblocks(n_rows, Hq, Hkv) * n_split * kQW * kRec;
 }
 
 glance_status launch_tree_attention(const AttnArgs& a, hipStream_t st) {
   if (a.dtype == GLANCE_BF16) {
-    const int Qn = a.n_rows * (a.Hq / a.Hkv);
-    const int nqb = (Qn + kQBlock - 1) / kQBlock;
-    dim3 grid(a.n_split + 1, a.Hkv * nqb, a.nseq);
-    tree_attn_bf16_kernel<<<grid, kAThreads, 0, st>>>(a);
+    const int nqb = attn_qblocks(a.n_rows, a.Hq, a.Hkv);
+    const int grid = a.nseq * a.n_split * nqb * a.Hkv;
+    tree_attn_bf16_kernel<<<grid, kAThreads, 0, st>>>(a, nqb);
     GLANCE_LAUNCH_CHECK();
-    attn_combine_kernel<<<dim3(a.nseq * a.n_rows, a.Hq), kHD, 0, st>>>(a);
-    GLANCE_LAUNCH_CHECK();
+    if (a.n_split > 1) {
+      attn_combine_kernel<<<dim3(a.nseq * a.n_rows, a.Hq), kHD, 0, st>>>(a, nqb);
+      GLANCE_LAUNCH_CHECK();
+    }
   } else {
     dim3 grid(a.nseq * a.n_rows, a.Hq);
     tree_attn_f32_kernel<<<grid, 128, 0, st>>>(a);

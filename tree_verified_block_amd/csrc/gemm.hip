@@ -628,7 +628,9 @@ __device__ __forceinline__ void proj_store(const GemmArgs& a, int b, int gm, con
       // rows i < 8 are head dims 8j + i, rows 8 + i their RoPE partners 64 + 8j + i
       const int bb = b < nq ? b : b - nq;
       const int head = bb >> 3, j8 = (bb & 7) * 8;
-      uint32_t lw[4], hw[4];
+      // lw/hw: the rotated pair rounded to bf16; lr/hr (q only): what the
+      // rounding left out, rounded to bf16 (q enters the scores as the sum)
+      uint32_t lw[4], hw[4], lr[4], hr[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float lo[2], hi[2];
@@ -642,12 +644,19 @@ __device__ __forceinline__ void proj_store(const GemmArgs& a, int b, int gm, con
         }
         lw[j] = static_cast<uint32_t>(f32_to_bf16(lo[0])) | (static_cast<uint32_t>(f32_to_bf16(lo[1])) << 16);
         hw[j] = static_cast<uint32_t>(f32_to_bf16(hi[0])) | (static_cast<uint32_t>(f32_to_bf16(hi[1])) << 16);
+        lr[j] = pack_bf16x2(lo[0] - __uint_as_float(lw[j] << 16), lo[1] - __uint_as_float(lw[j] & 0xFFFF0000u));
+        hr[j] = pack_bf16x2(hi[0] - __uint_as_float(hw[j] << 16), hi[1] - __uint_as_float(hw[j] & 0xFFFF0000u));
       }
-      uint16_t* op = b < nq ? static_cast<uint16_t*>(a.q_out) + static_cast<size_t>(gm) * a.Hq * 128
-                            : static_cast<uint16_t*>(a.k_out) + static_cast<size_t>(gm) * a.Hkv * 128;
-      op += head * 128 + j8;
+      const size_t ro = b < nq ? static_cast<size_t>(gm) * a.Hq * 128 + head * 128 + j8
+                               : static_cast<size_t>(gm) * a.Hkv * 128 + head * 128 + j8;
+      uint16_t* op = (b < nq ? static_cast<uint16_t*>(a.q_out) : static_cast<uint16_t*>(a.k_out)) + ro;
       *reinterpret_cast<uint4*>(op) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       *reinterpret_cast<uint4*>(op + 64) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      if (b < nq) {
+        uint16_t* rp = static_cast<uint16_t*>(a.q_lo_out) + ro;
+        *reinterpret_cast<uint4*>(rp) = make_uint4(lr[0], lr[1], lr[2], lr[3]);
+        *reinterpret_cast<uint4*>(rp + 64) = make_uint4(hr[0], hr[1], hr[2], hr[3]);
+      }
     } else {
       const int vr = (b - nq - nk) * 16;  // first v dim of the block
       uint32_t ow[8];
@@ -668,10 +677,16 @@ __device__ __forceinline__ void proj_store(const GemmArgs& a, int b, int gm, con
 // group's S work-groups to finish sums the partials, one thread per (block,
 // activation row), and applies the epilogue.  The S x nMT work-groups of a
 // group are dealt to the same XCD.
-template <int EPI, int DEPTH>
+//
+// XF: the activations are fp32 (the attention output) and enter as two bf16
+// matrices, their rounding and the rounded remainder, each chunk staged as both
+// and multiplied by the same weight operand (two products per step): the
+// output projection then sees its input to ~16 significant bits.
+template <int EPI, int DEPTH, bool XF>
 __global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int NB, int NGr,
                                                                  int S, int nMT) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2 * kXS];
+  constexpr int NX = XF ? 4 : 2;  // 16-byte activation loads per thread and chunk
+  __shared__ __attribute__((aligned(16))) uint16_t xs[(XF ? 4 : 2) * kXS];
 
   const int bid = blockIdx.x;
   const int xcd = bid & 7, kk = bid >> 3;
@@ -709,17 +724,25 @@ __global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int
     wcs = kKc * 2;
     whs = 64;
   }
-  const uint16_t* xr[2];
+  // piece e of this thread: 8 activations of row m0 + r, columns cc .. cc + 7 of the chunk
+  const char* xr[2];
   uint32_t xm[2];
   int xlds[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int idx = e * kGThreads + tid;
     const int r = idx >> 3, cc = (idx & 7) * 8;
-    x_row_masked(a, m0 + r, xr[e], xm[e]);
-    xr[e] += kbase + cc;
+    const uint16_t* p16;
+    x_row_masked(a, m0 + r, p16, xm[e]);
+    if constexpr (XF) {
+      const size_t row = static_cast<size_t>(p16 - static_cast<const uint16_t*>(a.x)) / a.K;
+      xr[e] = reinterpret_cast<const char*>(static_cast<const float*>(a.x) + row * a.K + kbase + cc);
+    } else {
+      xr[e] = reinterpret_cast<const char*>(p16 + kbase + cc);
+    }
     xlds[e] = r * kXP + cc;
   }
+  constexpr int xcs = XF ? kKc * 4 : kKc * 2;  // bytes per chunk along a row
 
   f32x4 acc[4];
 #pragma unroll
@@ -727,15 +750,40 @@ __global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int
   constexpr int RS = DEPTH + 1;
   static_assert(RS % 2 == 0, "ring slots and LDS stages must unroll together");
   uint4 wbuf[RS][2];
-  uint4 xbuf[RS][2];
+  uint4 xbuf[RS][NX];
   auto wload = [&](int c, uint4 (&dst)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) dst[i] = *reinterpret_cast<const uint4*>(wb + c * wcs + i * whs);
   };
   // raw loads; the row mask is applied when the chunk is written to LDS
-  auto xload = [&](int c, uint4 (&dst)[2]) {
+  auto xload = [&](int c, uint4 (&dst)[NX]) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e) dst[e] = *reinterpret_cast<const uint4*>(xr[e] + c * kKc);
+    for (int e = 0; e < NX; ++e)
+      dst[e] = *reinterpret_cast<const uint4*>(xr[e * 2 / NX] + c * xcs + (XF ? (e & 1) * 16 : 0));
+  };
+  // chunk pieces -> LDS stage st (bf16 rounding; with XF also the remainder in
+  // the second half of the stage ring)
+  auto xstage = [&](int st, const uint4 (&src)[NX]) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      if constexpr (XF) {
+        const uint4 f0 = mask4(src[2 * e], xm[e]), f1 = mask4(src[2 * e + 1], xm[e]);
+        const float v[8] = {__uint_as_float(f0.x), __uint_as_float(f0.y), __uint_as_float(f0.z),
+                            __uint_as_float(f0.w), __uint_as_float(f1.x), __uint_as_float(f1.y),
+                            __uint_as_float(f1.z), __uint_as_float(f1.w)};
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          hw[k] = pack_bf16x2(v[2 * k], v[2 * k + 1]);
+          lw[k] = pack_bf16x2(v[2 * k] - __uint_as_float(hw[k] << 16),
+                              v[2 * k + 1] - __uint_as_float(hw[k] & 0xFFFF0000u));
+        }
+        *reinterpret_cast<uint4*>(&xs[st * kXS + xlds[e]]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(&xs[(2 + st) * kXS + xlds[e]]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      } else {
+        *reinterpret_cast<uint4*>(&xs[st * kXS + xlds[e]]) = mask4(src[e], xm[e]);
+      }
+    }
   };
 
   // nck is a multiple of RS; loads past the last chunk are clamped to it, so no
@@ -748,8 +796,7 @@ __global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int
     if (d + 1 < DEPTH) xload(min(d + 1, nck - 1), xbuf[d + 1]);
     wload(min(d, nck - 1), wbuf[d]);
   }
-#pragma unroll
-  for (int e = 0; e < 2; ++e) *reinterpret_cast<uint4*>(&xs[xlds[e]]) = mask4(xbuf[0][e], xm[e]);
+  xstage(0, xbuf[0]);
   for (int c0 = 0; c0 < nck; c0 += RS) {
 #pragma unroll
     for (int u = 0; u < RS; ++u) {
@@ -765,14 +812,17 @@ __global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int
           const bf16x8 av = __builtin_bit_cast(bf16x8, wbuf[u][s]);
 #pragma unroll
           for (int mb = 0; mb < 4; ++mb) {
-            const bf16x8 bx = *reinterpret_cast<const bf16x8*>(xq + (mb * 16 + lr) * kXP + s * 32 + 8 * lg);
+            const int xo = (mb * 16 + lr) * kXP + s * 32 + 8 * lg;
+            const bf16x8 bx = *reinterpret_cast<const bf16x8*>(xq + xo);
             acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bx, acc[mb], 0, 0, 0);
+            if constexpr (XF) {
+              const bf16x8 bl = *reinterpret_cast<const bf16x8*>(xq + 2 * kXS + xo);
+              acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, acc[mb], 0, 0, 0);
+            }
           }
         }
         // (after the last chunk this stores a clamped copy nobody reads)
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          *reinterpret_cast<uint4*>(&xs[((u + 1) & 1) * kXS + xlds[e]]) = mask4(xbuf[(u + 1) % RS][e], xm[e]);
+        xstage((u + 1) & 1, xbuf[(u + 1) % RS]);
       }
     }
   }
@@ -1114,26 +1164,28 @@ glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
     // ring depth: the largest of 8, 4, 2 slots dividing the slice's chunk count
     const int nck = a.K / S / kKc;
     const int rs = nck % 8 == 0 ? 8 : nck % 4 == 0 ? 4 : 2;
-#define GLANCE_PROJ(E)                                                             \
-  if (rs == 8)                                                                     \
-    proj_bf16_kernel<E, 7><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);         \
-  else if (rs == 4)                                                                \
-    proj_bf16_kernel<E, 3><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);         \
-  else                                                                             \
-    proj_bf16_kernel<E, 1><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
+#define GLANCE_PROJ(E)                                                               \
+  if (rs == 8)                                                                       \
+    proj_bf16_kernel<E, 7, false><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);    \
+  else if (rs == 4)                                                                  \
+    proj_bf16_kernel<E, 3, false><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);    \
+  else                                                                               \
+    proj_bf16_kernel<E, 1, false><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
     if (a.epi == EPI_QKV) {
       GLANCE_PROJ(EPI_QKV)
     } else if (a.epi == EPI_SWIGLU) {
       GLANCE_PROJ(EPI_SWIGLU)
     } else if (a.epi == EPI_STORE_F32) {
       GLANCE_PROJ(EPI_STORE_F32)
-    } else {
+    } else if (a.x_f32) {
       if (rs == 8)
-        proj_bf16_kernel<EPI_RESID, 7><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
+        proj_bf16_kernel<EPI_RESID, 7, true><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
       else if (rs == 4)
-        proj_bf16_kernel<EPI_RESID, 3><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
+        proj_bf16_kernel<EPI_RESID, 3, true><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
       else
-        proj_bf16_kernel<EPI_RESID, 1><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
+        proj_bf16_kernel<EPI_RESID, 1, true><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
+    } else {
+      GLANCE_PROJ(EPI_RESID)
     }
 #undef GLANCE_PROJ
   }

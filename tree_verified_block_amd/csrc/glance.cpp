@@ -59,8 +59,9 @@ glance_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
 
 // ---------------------------------------------------------------- tree_attn ws
 struct AttnWs {
-  int n_split = 0, split = 0;
-  size_t off_qkv = 0, off_q = 0, off_k = 0, off_v = 0, off_part = 0, off_x = 0, bytes = 0;
+  int n_split = 0;
+  size_t off_qkv = 0, off_q = 0, off_qlo = 0, off_k = 0, off_v = 0, off_part = 0, off_x = 0,
+         bytes = 0;
   size_t off_kpart = 0, off_kcnt = 0;
   // full layer (inter > 0): normalised rows, fp32 q/k/v, h1 and the MLP activation
   size_t off_xn = 0, off_qkv32 = 0, off_h1 = 0, off_act = 0;
@@ -78,12 +79,12 @@ AttnWs attn_ws_layout(int dtype, int nseq, int n_rows, int64_t max_prefix, int d
   };
   if (dtype == GLANCE_BF16) {
     w.off_q = take(R * Hq * D * 2);
+    w.off_qlo = take(R * Hq * D * 2);
     w.off_k = take(R * Hkv * D * 2);
     w.off_v = take(R * Hkv * D * 2);
-    w.split = attn_split_len(max_prefix, nseq, Hkv);
-    w.n_split = static_cast<int>((max_prefix + w.split - 1) / w.split);
-    w.off_part = take(attn_part_floats(nseq, n_rows, Hq, Hkv, D, w.n_split) * sizeof(float));
-    w.off_x = take(R * Hq * D * 2);
+    w.n_split = attn_splits(nseq, max_prefix, n_rows, Hq, Hkv);
+    w.off_part = take(attn_part_floats(nseq, n_rows, Hq, Hkv, w.n_split) * sizeof(float));
+    w.off_x = take(R * Hq * D * sizeof(float));
     // split-K scratch shared by the projections (q/k/v, output and, in a full
     // layer, gate/up and down)
     const int M = static_cast<int>(R);
@@ -146,6 +147,11 @@ size_t glance_build_tree_ws(int32_t nseq, int32_t L, int32_t V, int32_t N) {
   (void)N;
   if (nseq < 1 || L < 1 || L > GLANCE_MAX_L || V < 2 || V > (1 << 18)) return 0;
   return tree_ws_layout(nseq, L, V).bytes;
+}
+
+size_t glance_build_tree_flag_offset(int32_t nseq, int32_t L, int32_t V, int32_t N) {
+  if (glance_build_tree_ws(nseq, L, V, N) == 0) return 0;
+  return tree_ws_layout(nseq, L, V).off_flag;
 }
 
 glance_status glance_build_tree(const void* draft_logits, int32_t dtype,
@@ -240,7 +246,9 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
   REQUIRE(d_model >= 1, "d_model = %d < 1", d_model);
   REQUIRE(max_prefix >= 0, "max_prefix < 0");
   REQUIRE(embed != nullptr || h_in != nullptr, "both embed and h_in are NULL");
-  REQUIRE(n_pos > max_prefix, "n_pos = %d must exceed max_prefix", n_pos);
+  REQUIRE(n_pos >= max_prefix + n_rows, "n_pos = %d is below max_prefix + n_rows = %lld (every "
+          "row's position P + depth needs a table row)", n_pos,
+          static_cast<long long>(max_prefix + n_rows));
   if (dtype == GLANCE_BF16) {
     if (D != 128) return fail(GLANCE_ERR_UNSUPPORTED, "bf16 tree attention needs D = 128 (got %d)", D);
     if (d_model % 256 != 0 || (Hq * D) % 256 != 0)
@@ -275,7 +283,7 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
-  void* attn_x = base + w.off_x;
+  float* attn_x = reinterpret_cast<float*>(base + w.off_x);
   const int R = nseq * n_rows;
   const int qd = Hq * D, kd = Hkv * D;
   float* kpart = reinterpret_cast<float*>(base + w.off_kpart);
@@ -304,6 +312,7 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
     g.Hq = Hq;
     g.Hkv = Hkv;
     g.q_out = base + w.off_q;
+    g.q_lo_out = base + w.off_qlo;
     g.k_out = tree_k;
     g.v_out = tree_v;
     g.kv_offsets = kv_offsets;
@@ -327,6 +336,7 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
   a.dtype = dtype;
   a.qkv = reinterpret_cast<const float*>(base + w.off_qkv);
   a.q = base + w.off_q;
+  a.q_lo = base + w.off_qlo;
   a.k_cache = layer->k_cache;
   a.v_cache = layer->v_cache;
   a.kv_offsets = kv_offsets;
@@ -342,7 +352,6 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
   a.Hkv = Hkv;
   a.D = D;
   a.max_prefix = max_prefix;
-  a.split = w.split;
   a.n_split = w.n_split;
   a.part = reinterpret_cast<float*>(base + w.off_part);
   a.attn_out = attn_out;
@@ -352,9 +361,11 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
   st = launch_tree_attention(a, hs);
   if (st != GLANCE_OK) return st;
 
-  // 3. h_out = h_in + attn Wo^T (padding rows -> 0)
+  // 3. h_out = h_in + attn Wo^T (padding rows -> 0); the fp32 attention output
+  // enters the bf16 products as its rounding plus the rounded remainder
   GemmArgs o{};
   o.x = attn_x;
+  o.x_f32 = dtype == GLANCE_BF16;
   o.gather = nullptr;
   o.w.w[0] = layer->wo;
   o.w.n_end[0] = d_model;
@@ -397,7 +408,9 @@ glance_status glance_tree_layer(const glance_full_layer* layer, const void* embe
   REQUIRE(d_model >= 1, "d_model = %d < 1", d_model);
   REQUIRE(max_prefix >= 0, "max_prefix < 0");
   REQUIRE(embed != nullptr || h_in != nullptr, "both embed and h_in are NULL");
-  REQUIRE(n_pos > max_prefix, "n_pos = %d must exceed max_prefix", n_pos);
+  REQUIRE(n_pos >= max_prefix + n_rows, "n_pos = %d is below max_prefix + n_rows = %lld (every "
+          "row's position P + depth needs a table row)", n_pos,
+          static_cast<long long>(max_prefix + n_rows));
   REQUIRE(std::isfinite(layer->eps) && layer->eps >= 0.f, "eps = %g is not finite and >= 0",
           static_cast<double>(layer->eps));
   const int inter = layer->inter;
@@ -475,13 +488,15 @@ glance_status glance_tree_layer(const glance_full_layer* layer, const void* embe
   st = launch_gemm_bf16(g, hs);
   if (st != GLANCE_OK) return st;
   st = launch_qkv_finish(qkv32, R, Hq, Hkv, layer->g_q, layer->g_k, layer->eps, kv_offsets, depth,
-                         n_rows, rope_cos, rope_sin, n_pos, base + w.off_q, tree_k, tree_v, hs);
+                         n_rows, rope_cos, rope_sin, n_pos, base + w.off_q, base + w.off_qlo,
+                         tree_k, tree_v, hs);
   if (st != GLANCE_OK) return st;
 
   // 4. attention over prefix + ancestors
   AttnArgs a{};
   a.dtype = GLANCE_BF16;
   a.q = base + w.off_q;
+  a.q_lo = base + w.off_qlo;
   a.k_cache = at->k_cache;
   a.v_cache = at->v_cache;
   a.kv_offsets = kv_offsets;
@@ -497,11 +512,10 @@ glance_status glance_tree_layer(const glance_full_layer* layer, const void* embe
   a.Hkv = Hkv;
   a.D = D;
   a.max_prefix = max_prefix;
-  a.split = w.split;
   a.n_split = w.n_split;
   a.part = reinterpret_cast<float*>(base + w.off_part);
   a.attn_out = attn_out;
-  a.attn_x = base + w.off_x;
+  a.attn_x = reinterpret_cast<float*>(base + w.off_x);
   a.tree_k = tree_k;
   a.tree_v = tree_v;
   st = launch_tree_attention(a, hs);
@@ -510,6 +524,7 @@ glance_status glance_tree_layer(const glance_full_layer* layer, const void* embe
   // 5. h1 = h + attn Wo^T
   GemmArgs o{};
   o.x = base + w.off_x;
+  o.x_f32 = true;
   o.w.w[0] = at->wo;
   o.w.n_end[0] = d_model;
   o.w.nseg = 1;

@@ -14,10 +14,11 @@ namespace glance {
 struct TreeWs {
   // per-chunk (max, sum exp) [nseq*L][16], sorted key lists [nseq*L][16][64],
   // merged rows (log q [nseq*L][64], token ids [nseq*L][64]), the arrival
-  // counters of the rows [nseq*L] and sequences [nseq] (zero between calls), and
-  // for a shared budget the published selections [nseq][64] and the batch counter
+  // counters of the rows [nseq*L] and sequences [nseq] (zero between calls),
+  // for a shared budget the published selections [nseq][64] and the batch
+  // counter, and the sticky non-finite flag word (bit 0 NaN, bit 1 +inf logits)
   size_t off_cstat = 0, off_clist = 0, off_lq = 0, off_tk = 0, off_row_cnt = 0, off_seq_cnt = 0,
-         off_pops = 0, off_batch_cnt = 0, bytes = 0;
+         off_pops = 0, off_batch_cnt = 0, off_flag = 0, bytes = 0;
 };
 // Sequences of one shared-budget batch (the cut keeps their keys in LDS).
 constexpr int kMaxShared = GLANCE_MAX_SHARED;
@@ -41,7 +42,9 @@ struct GemmSeg {
 // out_res [M][N/2] is silu(x W_gate^T) * (x W_up^T) rounded to bf16.
 enum GemmEpi { EPI_STORE_F32 = 0, EPI_RESID = 1, EPI_HEAD = 2, EPI_QKV = 3, EPI_SWIGLU = 4 };
 struct GemmArgs {
-  const void* x;          // [M][K]
+  const void* x;          // [M][K] in the storage dtype, or fp32 when x_f32
+  bool x_f32;             // bf16 projections: X is fp32, used as the sum of two bf16
+                          // matrices (its bf16 rounding and the remainder)
   const int32_t* gather;  // NULL or [M] token ids (row m of X = x[gather[m]], -1 = zero row)
   GemmSeg w;
   int M, N, K;
@@ -62,9 +65,10 @@ struct GemmArgs {
   float inv_temp;
   uint32_t seed_lo, seed_hi, rnd_lo, rnd_hi;
   // EPI_QKV (bf16, head_dim 128): W = [Wq; Wk; Wv]; q and k rotated at the row's
-  // position, everything rounded to bf16.
+  // position, everything rounded to bf16; q also leaves its rounding remainder.
   int Hq, Hkv;
   void* q_out;             // [M][Hq*128]
+  void* q_lo_out;          // [M][Hq*128]: q - bf16(q), rounded to bf16
   void* k_out;             // [M][Hkv][128]
   void* v_out;             // [M][Hkv][128]
   const int64_t* kv_offsets;
@@ -117,7 +121,8 @@ glance_status launch_head_rowstats_f32(const float* logits, int R, int V, int32_
 struct AttnArgs {
   int dtype;
   const float* qkv;        // fp32 path: [R][(Hq + 2 Hkv) D] projections (before RoPE)
-  const void* q;           // bf16 path: [R][Hq D] rotated queries (tree K/V in tree_k/v)
+  const void* q;           // bf16 path: [R][Hq D] rotated queries rounded to bf16 (tree K/V in tree_k/v)
+  const void* q_lo;        // bf16 path: [R][Hq D] the rounding remainder q - bf16(q), in bf16
   const void* k_cache;     // [sum P][Hkv][D]
   const void* v_cache;
   const int64_t* kv_offsets;
@@ -126,31 +131,33 @@ struct AttnArgs {
   const int32_t* token;    // -1 marks padding rows
   const float* rope_cos;
   const float* rope_sin;
-  int n_pos;               // table rows; positions past the table are clamped to its end
+  int n_pos;               // table rows (the host checks max_prefix + n_rows <= n_pos)
   int nseq, n_rows, Hq, Hkv, D;
-  int64_t max_prefix;
-  int split;               // prefix keys per split work-group
-  int n_split;             // prefix splits (the tree keys form split n_split)
-  float* part;             // partial (m, l, o[D]) per split and query
+  int64_t max_prefix;      // prefixes longer than this are read as this long
+  int n_split;             // bf16: key splits per (sequence, KV head, query block)
+  float* part;             // bf16, n_split > 1: partial (m, l, o[D]) per split and query
   float* attn_out;         // NULL or [R][Hq D] fp32
-  void* attn_x;            // [R][Hq D] storage dtype: input of the output projection
+  float* attn_x;           // [R][Hq D] fp32: input of the output projection
   void* tree_k;            // [R][Hkv][D]: written by the fp32 path (if not NULL), read by bf16
   void* tree_v;
 };
-int attn_split_len(int64_t max_prefix, int nseq, int Hkv);
-size_t attn_part_floats(int nseq, int n_rows, int Hq, int Hkv, int D, int n_split);
+// Key splits of the bf16 attention (from the grid and the longest prefix), and
+// the floats of its split records.
+int attn_splits(int nseq, int64_t max_prefix, int n_rows, int Hq, int Hkv);
+size_t attn_part_floats(int nseq, int n_rows, int Hq, int Hkv, int n_split);
 glance_status launch_tree_attention(const AttnArgs& a, hipStream_t st);
 
 // ----------------------------------------------------------------- layer.hip
 // out[m] = bf16(RMSNorm(x[gather ? gather[m] : m]) * g); rows with token[m] < 0 -> 0
 glance_status launch_rmsnorm(const void* x, const int32_t* gather, const int32_t* token, int M,
                              int d, const void* g, float eps, void* out, hipStream_t st);
-// fp32 q/k/v [R][(Hq + 2 Hkv) 128] -> head-normalised, rotated bf16 q, k and bf16 v
+// fp32 q/k/v [R][(Hq + 2 Hkv) 128] -> head-normalised, rotated bf16 q (and its
+// rounding remainder), k and bf16 v
 glance_status launch_qkv_finish(const float* qkv, int R, int Hq, int Hkv, const void* g_q,
                                 const void* g_k, float eps, const int64_t* kv_offsets,
                                 const int32_t* depth, int n_rows, const float* rope_cos,
-                                const float* rope_sin, int n_pos, void* q_out, void* k_out,
-                                void* v_out, hipStream_t st);
+                                const float* rope_sin, int n_pos, void* q_out, void* q_lo_out,
+                                void* k_out, void* v_out, hipStream_t st);
 
 // ------------------------------------------------------------------ walk.hip
 glance_status launch_accept_walk(const int32_t* parent, const int32_t* token,

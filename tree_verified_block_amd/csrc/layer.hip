@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kNormThreads) void qkv_finish_kernel(
     const uint16_t* __restrict__ g_k, float eps, const int64_t* __restrict__ kv_offsets,
     const int32_t* __restrict__ depth, int n_rows, const float* __restrict__ rope_cos,
     const float* __restrict__ rope_sin, int n_pos, uint16_t* __restrict__ q_out,
-    uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out) {
+    uint16_t* __restrict__ q_lo_out, uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out) {
   const int nh = Hq + 2 * Hkv;
   const int item = blockIdx.x * (kNormThreads / kWave) + threadIdx.x / kWave;
   if (item >= R * nh) return;  // (wave-uniform)
@@ -91,10 +91,16 @@ __global__ __launch_bounds__(kNormThreads) void qkv_finish_kernel(
     if (p > n_pos - 1) p = n_pos - 1;
     const float c = rope_cos[static_cast<size_t>(p) * 64 + l], sn = rope_sin[static_cast<size_t>(p) * 64 + l];
     const float ra = a * c - b * sn, rb = b * c + a * sn;
-    uint16_t* dst = head < Hq ? q_out + (static_cast<size_t>(row) * Hq + head) * 128
-                              : k_out + (static_cast<size_t>(row) * Hkv + (head - Hq)) * 128;
-    dst[l] = f32_to_bf16(ra);
-    dst[l + 64] = f32_to_bf16(rb);
+    const size_t o = head < Hq ? (static_cast<size_t>(row) * Hq + head) * 128
+                               : (static_cast<size_t>(row) * Hkv + (head - Hq)) * 128;
+    uint16_t* dst = (head < Hq ? q_out : k_out) + o;
+    const uint16_t qa = f32_to_bf16(ra), qb = f32_to_bf16(rb);
+    dst[l] = qa;
+    dst[l + 64] = qb;
+    if (head < Hq) {  // q also leaves its rounding remainder (q = hi + lo in the scores)
+      q_lo_out[o + l] = f32_to_bf16(ra - bf16_to_f32(qa));
+      q_lo_out[o + l + 64] = f32_to_bf16(rb - bf16_to_f32(qb));
+    }
   } else {
     uint16_t* dst = v_out + (static_cast<size_t>(row) * Hkv + (head - Hq - Hkv)) * 128;
     dst[l] = f32_to_bf16(a);
@@ -116,14 +122,14 @@ glance_status launch_rmsnorm(const void* x, const int32_t* gather, const int32_t
 glance_status launch_qkv_finish(const float* qkv, int R, int Hq, int Hkv, const void* g_q,
                                 const void* g_k, float eps, const int64_t* kv_offsets,
                                 const int32_t* depth, int n_rows, const float* rope_cos,
-                                const float* rope_sin, int n_pos, void* q_out, void* k_out,
-                                void* v_out, hipStream_t st) {
+                                const float* rope_sin, int n_pos, void* q_out, void* q_lo_out,
+                                void* k_out, void* v_out, hipStream_t st) {
   const int items = R * (Hq + 2 * Hkv);
   const int per = kNormThreads / kWave;
   qkv_finish_kernel<<<(items + per - 1) / per, kNormThreads, 0, st>>>(
       qkv, R, Hq, Hkv, static_cast<const uint16_t*>(g_q), static_cast<const uint16_t*>(g_k), eps,
       kv_offsets, depth, n_rows, rope_cos, rope_sin, n_pos, static_cast<uint16_t*>(q_out),
-      static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out));
+      static_cast<uint16_t*>(q_lo_out), static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out));
   GLANCE_LAUNCH_CHECK();
   return GLANCE_OK;
 }
