@@ -334,6 +334,24 @@ glance_status glance_verify_head_packed(const void* h, const void* w_packed, int
                                         int32_t* sample_tok, float* sample_gap, float* logits,
                                         void* ws, size_t ws_bytes, void* stream);
 
+/* glance_verify_head_packed_noalloc: glance_verify_head_packed without a
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The head's partial statistics go to a fixed device array of
+ * 8 MiB inside the library (one per GPU, held until the process ends, found on
+ * the first call on each device); the call allocates nothing.  Limit:
+ * glance_verify_head_ws(R, V, d_model, GLANCE_BF16) <= 8 MiB (R <= 551 rows at
+ * V = 151936); larger sizes return GLANCE_ERR_UNSUPPORTED.  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (concurrent streams,
+ * threads) race and must be serialised by the caller.  Arguments, outputs and
+ * results are those of glance_verify_head_packed. */
+glance_status glance_verify_head_packed_noalloc(const void* h, const void* w_packed, int32_t R,
+                                                int32_t d_model, int32_t V, float temperature,
+                                                uint64_t seed, uint64_t round_id, int32_t* argmax,
+                                                float* top1, float* gap, float* entropy,
+                                                int32_t* sample_tok, float* sample_gap,
+                                                float* logits, void* stream);
+
 /* -------------------------------------------------------------------- step 5 --
  * glance_accept_walk: the greedy accept walk of every round.
  *

@@ -169,6 +169,17 @@ def test_head_pack_rejects_bad_arguments(lib):
     assert packed(tok=p, sgap=p, T=0.0) == -1      # sampling needs T > 0
     assert packed(tok=p) == -1                     # both draw outputs or neither
 
+    def noalloc(R):
+        return lib.glance_verify_head_packed_noalloc(p, p, R, 4096, 151936, 1.0, 1, 2, p, p, p, p,
+                                                     None, None, None, None)
+
+    # rows are checked, and sizes beyond the fixed scratch rejected, before any device call
+    assert noalloc(0) == -1
+    assert lib.glance_verify_head_ws(551, 151936, 4096, 1) <= 8 << 20
+    assert lib.glance_verify_head_ws(552, 151936, 4096, 1) > 8 << 20
+    assert noalloc(552) == -4
+    assert b"scratch" in lib.glance_last_error()
+
 
 def _attn(lib, **kw):
     a = dict(dtype=1, embed=OK_PTR, h_in=None, nseq=1, n_rows=64, d=4096, Hq=32, Hkv=8, D=128,

@@ -60,6 +60,8 @@ SIGNATURES = {
     "glance_head_pack": (_I, [_P, _I, _I, _P, _P]),
     "glance_verify_head_packed": (_I, [_P, _P, _I, _I, _I, _F, _U64, _U64, _P, _P, _P, _P, _P, _P,
                                        _P, _P, _SZ, _P]),
+    "glance_verify_head_packed_noalloc": (_I, [_P, _P, _I, _I, _I, _F, _U64, _U64, _P, _P, _P, _P,
+                                               _P, _P, _P, _P]),
     "glance_accept_walk": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P]),
     "glance_commit_kv": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _I64, _P]),
     "glance_advance_round": (_I, [_P, _P, _I, _P, _P, _P]),

@@ -192,6 +192,17 @@ def glance_verify_head_packed(h, w_packed, V, argmax, top1, gap, entropy, ws, lo
               ws.numel(), _stream(stream))
 
 
+def glance_verify_head_packed_noalloc(h, w_packed, V, argmax, top1, gap, entropy, logits=None,
+                                      temperature=1.0, seed=0, round_id=0, sample_tok=None,
+                                      sample_gap=None, stream=None):
+    """The packed head with the library's fixed device scratch in place of a
+    workspace (no allocation); calls that overlap on one GPU race."""
+    R, d_model = h.shape
+    _lib.call("glance_verify_head_packed_noalloc", _ptr(h), _ptr(w_packed), R, d_model, V,
+              float(temperature), int(seed), int(round_id), _ptr(argmax), _ptr(top1), _ptr(gap),
+              _ptr(entropy), _ptr(sample_tok), _ptr(sample_gap), _ptr(logits), _stream(stream))
+
+
 # ---------------------------------------------------------------------- step 5
 def glance_accept_walk(parent, token, n_valid, argmax, gap, nseq, n_rows, L, gap_flag,
                        n_accept, out_tokens, path_rows, flagged, stream=None):

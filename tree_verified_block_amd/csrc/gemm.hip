@@ -25,6 +25,8 @@
 // over all waves of the grid (9496 blocks over 2048 waves for V = 151936), and
 // the M-tiles of one weight range are placed on the same XCD back to back so
 // that the weights are fetched from HBM once per XCD L2.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -1079,6 +1081,32 @@ __global__ __launch_bounds__(256) void proj_pack_kernel(GemmArgs a, int NB, size
 }
 
 int gemm_bf16_head_parts(int N) { return head_grid(N).nWG; }
+
+// ------------------------------------------------- head without a workspace
+// Scratch of glance_verify_head_packed_noalloc: the head's per-row partial
+// statistics (and draws) live in this array instead of a caller workspace.
+// Each GPU the library runs on holds its own copy until the process ends; host
+// code must not pass the array's name to a kernel (on the host it is only a
+// stand-in symbol), but the device address looked up for the current device.
+static __device__ __align__(256) float scratch[kHeadScratchFloats];
+
+glance_status head_scratch_ptr(float** out) {
+  static std::mutex mu;
+  static float* per_device[64] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= 64) return GLANCE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_device[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    per_device[dev] = static_cast<float*>(p);
+  }
+  *out = per_device[dev];
+  return GLANCE_OK;
+}
 
 size_t proj_pack_bytes(int N, int K) {
   return static_cast<size_t>(K / kKc) * ((N + 15) / 16) * 2048;

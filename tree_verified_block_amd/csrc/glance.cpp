@@ -759,6 +759,28 @@ glance_status glance_verify_head_packed(const void* h, const void* w_packed, int
                      logits, ws, ws_bytes, dr, static_cast<hipStream_t>(stream));
 }
 
+glance_status glance_verify_head_packed_noalloc(const void* h, const void* w_packed, int32_t R,
+                                                int32_t d_model, int32_t V, float temperature,
+                                                uint64_t seed, uint64_t round_id, int32_t* argmax,
+                                                float* top1, float* gap, float* entropy,
+                                                int32_t* sample_tok, float* sample_gap,
+                                                float* logits, void* stream) {
+  g_last_error.clear();
+  REQUIRE(R >= 1, "R = %d < 1", R);
+  REQUIRE(V >= 2, "V = %d < 2", V);
+  const size_t need = glance_verify_head_ws(R, V, d_model, GLANCE_BF16);
+  if (need > kHeadScratchFloats * sizeof(float))
+    return fail(GLANCE_ERR_UNSUPPORTED,
+                "R = %d rows of V = %d need %zu bytes of head scratch; the fixed array holds %zu",
+                R, V, need, kHeadScratchFloats * sizeof(float));
+  float* scratch = nullptr;
+  const glance_status st = head_scratch_ptr(&scratch);
+  if (st != GLANCE_OK) return st;
+  return glance_verify_head_packed(h, w_packed, R, d_model, V, temperature, seed, round_id, argmax,
+                                   top1, gap, entropy, sample_tok, sample_gap, logits, scratch,
+                                   kHeadScratchFloats * sizeof(float), stream);
+}
+
 // ------------------------------------------------------------------- step 5
 glance_status glance_accept_walk(const int32_t* parent, const int32_t* token,
                                  const int32_t* n_valid, const int32_t* argmax, const float* gap,

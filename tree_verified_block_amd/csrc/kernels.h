@@ -84,6 +84,10 @@ struct GemmArgs {
 };
 // Number of per-row partial records the bf16 LM-head GEMM leaves (the merge input).
 int gemm_bf16_head_parts(int N);
+// The head's scratch for callers that cannot allocate: a fixed device array of
+// kHeadScratchFloats floats (8 MiB), its address on the current device.
+constexpr size_t kHeadScratchFloats = size_t(1) << 21;
+glance_status head_scratch_ptr(float** out);
 // Bytes of the packed LM-head weights for N vocabulary rows of K (bf16), and the
 // packing kernel (row-major [N][K] -> packed tile order).
 size_t head_pack_bytes(int N, int K);
