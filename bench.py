@@ -3,10 +3,14 @@
 A step is one whole round (steps 1-5: tree build, one packed tree-attention
 layer, LM head with its epilogue, accept walk) over device-resident synthetic
 inputs of the 8B-shaped single-layer workload: d_model 4096, 32 query / 8 KV
-heads, head_dim 128, V 151936, L 15, N 63, a 1024-token prefix, bf16 storage.
-Prints one JSON line: rounds/s, per-step microseconds and HBM fractions
-(HIP events on the launch stream), the roofline of the dominant kernel (the LM
-head) and the CPU oracle timed on a sample of the same workload.
+heads, head_dim 128, V 151936, L 15, N 63, a 1024-token prefix, bf16 storage,
+packed head and attention weights.  Prints one JSON line: rounds/s of K rounds
+launched on one stream (the headline), the per-round distribution, the same
+rounds replayed from HIP graphs, per-step microseconds and HBM fractions (HIP
+events on the launch stream), the roofline of the dominant kernel (the LM head),
+the other workloads (tiny fp32, copy regime, ragged batch of 8, 36-layer
+stack), sampled and chained rounds, the shared-budget build, full decoder
+layers, a plain device copy, and the CPU oracle on a sample of the workload.
 """
 from __future__ import annotations
 
@@ -24,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verify rounds/s at N=63, L=15, V=151936 (8B shape); % of HBM peak per kernel"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
 def step_bytes(cfg, P: int) -> dict:
@@ -57,27 +62,157 @@ def head_traffic(cfg):
     return rec.get("traffic_bytes")
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(inp, budget_s: float = 10.0) -> dict:
     """The CPU oracle as it stands, on whole rounds of the same workload (log-
     softmax, exact top-N tree, every verify row by unpacked evaluation, head
     statistics and the walk; the independent greedy re-decode is left out), run
-    round after round until about budget_s seconds of work."""
-    from threadpoolctl import threadpool_info
+    round after round until about budget_s seconds of work: once with the BLAS
+    pool limited to one thread, once with all the host's cores."""
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import round as orr
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     n_avail = len(inp["rounds"])
-    n = 0
+
+    def timed(limit):
+        with threadpool_limits(limits=limit):
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+            n = 0
+            t0 = time.perf_counter()
+            while True:
+                orr.oracle_round(inp, n % n_avail, exact="beam", continuation_check=False)
+                n += 1
+                dt = time.perf_counter() - t0
+                if dt >= budget_s or n >= 4 * n_avail:
+                    break
+        return n, dt, threads
+
+    n1, dt1, _ = timed(1)
+    na, dta, threads = timed(None)
+    return {"value": round(na / dta, 4), "unit": "rounds/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{na} rounds of {inp['cfg'].name} (steps 1-5, float64 NumPy), {dta:.1f} s",
+            "one_thread": {"value": round(n1 / dt1, 4), "cores": 1,
+                           "sample": f"{n1} rounds, {dt1:.1f} s"},
+            "host_cpu": _cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def graph_replays(dev, drafts, K: int, warm: int = 3, dist: int = 0) -> dict:
+    """Rounds replayed from HIP graphs: one graph per draft (each captures the
+    whole round reading that draft's tensor; a given-topology workload has one),
+    replayed in turn.  Times exactly K replays between two synchronisations;
+    with dist > 0 also `dist` replays bracketed one by one with events on the
+    replay stream (median, p10, p90 of the per-round time)."""
+    import torch
+    graphs = []
+    for d in (drafts or [None]):
+        if d is not None:
+            dev.draft = d
+        dev.run()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            dev.run()
+        graphs.append(g)
+    for i in range(warm):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    while True:
-        orr.oracle_round(inp, n % n_avail, exact="beam", continuation_check=False)
-        n += 1
-        dt = time.perf_counter() - t0
-        if dt >= budget_s or n >= 4 * n_avail:
-            break
-    return {"value": n / dt, "unit": "rounds/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} rounds of {inp['cfg'].name} (steps 1-5, float64 NumPy), {dt:.1f} s",
-            "host_cpu": platform.processor() or platform.machine(),
-            "affinity_cpus": len(os.sched_getaffinity(0))}
+    for i in range(K):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    out = {"rounds_per_s": round(K / wall, 2), "us_per_round": round(wall / K * 1e6, 2),
+           "replays": K, "graphs": len(graphs)}
+    if dist > 0:
+        stream = torch.cuda.current_stream()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(dist)]
+        for i, e in enumerate(ev):
+            e[0].record(stream)
+            graphs[i % len(graphs)].replay()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        us = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in ev])
+        out["per_round_us"] = {"median": round(float(np.median(us)), 2),
+                               "p10": round(float(np.percentile(us, 10)), 2),
+                               "p90": round(float(np.percentile(us, 90)), 2), "n": dist}
+    del graphs
+    return out
+
+
+def config_leg(name: str, K: int, seed: int, model: dict | None = None, layer_copies: int = 0,
+               head_peak: bool = False) -> dict:
+    """Graph-replayed rounds of another workload (packed weights when bf16).
+    ``model``: an 8B-shaped workload whose embedding, head and layer weights are
+    reused (its prefix caches, drafts and trees are this config's own).
+    layer_copies > 0: the config's layer count built from copies of its first
+    layer's weights and cache (each layer still its own device copy, streamed
+    from HBM every round), which keeps generation on the host short."""
+    import torch
+    from synth import gen_round, make_config
+    from tree_verified_block_amd.round import DeviceRound, to_device
+    cfg = make_config(name)
+    t0 = time.perf_counter()
+    if layer_copies:
+        inp = gen_round(cfg.replace(n_layers=1), seed, model=model)
+        inp["layers"] = [inp["layers"][0]] * layer_copies
+        inp["cfg"] = cfg
+    else:
+        inp = gen_round(cfg, seed, model=model)
+    gen_s = time.perf_counter() - t0
+    bf16 = cfg.dtype == "bf16"
+    dev = DeviceRound(inp, device="cuda", packed_head=bf16)
+    dev.set_round(0)
+    drafts = [to_device(rd["draft_logits"], cfg.dtype, "cuda") for rd in inp["rounds"]
+              if "draft_logits" in rd]
+    res = {"workload": f"{cfg.name}: {cfg.n_layers} layer(s), d_model {cfg.d_model}, "
+                       f"{cfg.Hq}q/{cfg.Hkv}kv x {cfg.D}, V {cfg.V}, L {cfg.L}, N {cfg.N}, "
+                       f"nseq {cfg.nseq}, prefix {cfg.prefix}, {cfg.dtype}",
+           "host_generation_s": round(gen_s, 1)}
+    res.update(graph_replays(dev, drafts, K))
+    # eager per-step split of one round (HIP events on the launch stream)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    if drafts:
+        dev.draft = drafts[0]
+    ev[0].record(stream)
+    dev.step_tree()
+    ev[1].record(stream)
+    dev.step_attn()
+    ev[2].record(stream)
+    dev.step_head()
+    ev[3].record(stream)
+    dev.step_walk()
+    ev[4].record(stream)
+    torch.cuda.synchronize()
+    names = ["build_tree", "tree_attn", "verify_head", "accept_walk"]
+    res["eager_step_us"] = {n: round(ev[k].elapsed_time(ev[k + 1]) * 1e3, 2) for k, n in enumerate(names)}
+    P = int(inp["prefix_len"].max())
+    nbytes = step_bytes(cfg, P) if bf16 else None
+    if nbytes:
+        res["round_bytes"] = sum(nbytes.values())
+        res["round_hbm_frac"] = round(res["round_bytes"] / (res["us_per_round"] * 1e-6) /
+                                      (HBM_PEAK_GBS * 1e9), 4)
+        la = res["eager_step_us"]["tree_attn"]
+        res["tree_attn_hbm_frac"] = round(nbytes["tree_attn"] / (la * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)
+    if head_peak:
+        R = cfg.nseq * (cfg.N + 1)
+        flops = 2.0 * R * cfg.d_model * cfg.V
+        hu = res["eager_step_us"]["verify_head"]
+        res["verify_head_tflops"] = round(flops / (hu * 1e-6) / 1e12, 1)
+        res["verify_head_mfma_frac"] = round(flops / (hu * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4)
+        res["verify_head_hbm_frac"] = round(nbytes["verify_head"] / (hu * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)
+    del dev
+    torch.cuda.empty_cache()
+    return res
 
 
 def chain_measure(inp, cfg, drafts, K: int, warm: int = 5, packed: bool = False) -> dict:
@@ -280,7 +415,13 @@ def main():
     ap.add_argument("--row-major-head", action="store_true",
                     help="LM head over the row-major weights instead of the packed copy")
     ap.add_argument("--probe-copy", action="store_true",
-                    help="also run a 1 GiB device copy (counter calibration)")
+                    help="accepted for older command lines: the 1 GiB device copy (the counter "
+                         "calibration and hbm_probe) always runs")
+    ap.add_argument("--leg-rounds", type=int, default=50,
+                    help="graph-replayed rounds of each other workload (tiny fp32, copy regime, "
+                         "ragged batch of 8; the 36-layer stack takes a fifth); 0 skips them")
+    ap.add_argument("--dist-rounds", type=int, default=200,
+                    help="rounds timed one by one for the per-round distribution")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
@@ -336,27 +477,41 @@ def main():
         one_step(i)
     torch.cuda.synchronize()
 
-    # timed region: K whole rounds; HIP events on the launch stream bracket the
-    # LM-head call of every fourth round (the dominant kernel's live duration;
-    # each recorded event costs a few microseconds of the round it sits in)
-    every = 4
-    hev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-           for i in range(0, args.steps, every)}
+    # timed region: exactly K whole rounds launched call by call on one stream,
+    # a synchronisation on both sides and nothing else in between
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        one_step(i, head_ev=hev.get(i))
+        one_step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    head_us = float(np.mean([e[0].elapsed_time(e[1]) for e in hev.values()]) * 1e3)
 
-    # per-step breakdown, outside the timed region (events between all steps
-    # cost a few microseconds per round of their own)
+    # the LM-head call's live duration (HIP events on the launch stream around it,
+    # in K further rounds; the dominant kernel's roofline is taken from these)
+    hev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        one_step(i, head_ev=hev[i])
+    torch.cuda.synchronize()
+    head_us = float(np.mean([e[0].elapsed_time(e[1]) for e in hev]) * 1e3)
+
+    # per-step breakdown (events between all steps cost a few microseconds per
+    # round of their own) and the per-round distribution (events between rounds)
     nd = min(args.steps, 50)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(nd)]
     for i in range(nd):
         one_step(i, evs[i])
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    rev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.dist_rounds)]
+    for i, e in enumerate(rev):
+        e[0].record(stream)
+        one_step(i)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    rus = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in rev]) if rev else None
+
+    # the same rounds replayed from HIP graphs (one graph per draft)
+    gr = graph_replays(dev, drafts, args.steps, warm=args.warmup, dist=args.dist_rounds)
 
     names = ["build_tree", "tree_attn", "verify_head", "accept_walk"]
     us = {n: float(np.mean([e[k].elapsed_time(e[k + 1]) for e in evs]) * 1e3)
@@ -370,6 +525,10 @@ def main():
     total_bytes = sum(nbytes.values())
     ms = wall / args.steps * 1e3
     head_gbs = nbytes["verify_head"] / (head_us * 1e-6) / 1e9
+    dist = None
+    if rus is not None:
+        dist = {"median": round(float(np.median(rus)), 2), "p10": round(float(np.percentile(rus, 10)), 2),
+                "p90": round(float(np.percentile(rus, 90)), 2), "n": len(rus)}
     out = {
         "metric": METRIC, "value": round(args.steps / wall, 2), "unit": "rounds/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -378,7 +537,11 @@ def main():
         "config": {"workload": f"{cfg.name}: {cfg.n_layers} tree-attention layer(s), d_model "
                    f"{cfg.d_model}, {cfg.Hq}q/{cfg.Hkv}kv heads x {cfg.D}, V {cfg.V}, L {cfg.L}, "
                    f"N {cfg.N}, prefix {P}, nseq {cfg.nseq}", "seed": args.seed,
-                   "head_weights": "packed tile order" if packed else "row-major"},
+                   "head_weights": "packed tile order" if packed else "row-major",
+                   "timing": f"{args.steps} rounds launched call by call on one stream, "
+                             f"drafts cycling over {len(drafts)}"},
+        "per_round_us": dist,
+        "graph": dict(gr, note="the same rounds replayed from HIP graphs, one per draft"),
         "round_hbm_frac": round(total_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
         "round_bytes": total_bytes,
         "per_kernel": per_kernel,
@@ -398,12 +561,39 @@ def main():
         out["shared_budget"] = shared_measure(args.shared_calls, oracle=not args.no_cpu_baseline)
     if args.full_rounds > 0:
         out["full_layer"] = full_layer_measure(args.full_rounds)
-    if args.probe_copy:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
+    if args.leg_rounds > 0 and cfg.name == "qwen8b_1layer":
+        K = args.leg_rounds
+        legs = {}
+        for key, name, seed, kw in (
+                ("tiny_f32", "tiny", 1000, {}),
+                ("copy_regime", "qwen8b_copy", 3000, dict(model=inp)),
+                ("ragged8", "qwen8b_ragged8", 4, dict(model=inp, head_peak=True)),
+                ("deep36", "qwen8b_deep36", 4000, dict(model=inp, layer_copies=36))):
+            k = max(5, K // 5) if key == "deep36" else K
+            legs[key] = config_leg(name, k, seed, **kw)
+            print(f"[bench] leg {key}: {legs[key]['us_per_round']} us per round", file=sys.stderr,
+                  flush=True)
+        out["configs"] = legs
+    # plain device copy of 1 GiB (read + write bytes over the event-timed copy):
+    # what this machine's HBM sustains outside the path's kernels
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    stream = torch.cuda.current_stream()
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ce[0].record(stream)
+    for _ in range(5):
+        b.copy_(a)
+    ce[1].record(stream)
+    torch.cuda.synchronize()
+    copy_us = ce[0].elapsed_time(ce[1]) * 1e3 / 5
+    out["hbm_probe"] = {"kind": "device copy, 1 GiB read + 1 GiB written (torch copy_)",
+                        "us": round(copy_us, 1),
+                        "GB/s": round(2 * (1 << 30) / (copy_us * 1e-6) / 1e9, 1),
+                        "frac_of_peak": round(2 * (1 << 30) / (copy_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    del a, b
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(out), flush=True)

@@ -183,6 +183,8 @@ typedef struct {
   const void* wo;      /* [d_model][Hq*D]                         */
   const void* k_cache; /* [sum P][Hkv][D], keys already rotated   */
   const void* v_cache; /* [sum P][Hkv][D]                         */
+  const void* packed;  /* NULL, or wq/wk/wv/wo as glance_attn_pack wrote them
+                          (bf16; then those four are not read)     */
 } glance_attn_layer;
 
 glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype,
@@ -242,11 +244,29 @@ glance_status glance_tree_layer(const glance_full_layer* layer, const void* embe
 size_t glance_tree_layer_ws(int32_t nseq, int32_t n_rows, int64_t max_prefix, int32_t d_model,
                             int32_t Hq, int32_t Hkv, int32_t D, int32_t inter);
 
+/* glance_attn_pack: the attention weights of a layer (wq, wk, wv, wo, bf16)
+ * copied once, at load time, into the projection kernel's tile order, for
+ * glance_tree_attn and glance_tree_layer alike: for every block of 16 output
+ * rows and 64-deep chunk of the input, the 16 x 64 tile laid out as the
+ * matrix-core operand (each weight load a contiguous kilobyte), the tiles of
+ * four consecutive blocks side by side and those of one group of four blocks
+ * contiguous over all chunks (a work-group's weights are one stream).  The
+ * q/k/v blocks pair each head's dims 8j..8j+7 with their rotary partners
+ * 64+8j..64+8j+7 (v blocks: 16 consecutive rows).  q/k/v first, then wo at the
+ * next 256-byte boundary; size from glance_attn_pack_bytes (0 if unsupported).
+ * Results with the packed copy are identical to those with the row-major
+ * weights.  Limits: D == 128, Hq % Hkv == 0, d_model and Hq*D multiples of 256.
+ */
+size_t glance_attn_pack_bytes(int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D);
+glance_status glance_attn_pack(const void* wq, const void* wk, const void* wv, const void* wo,
+                               int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D, void* packed,
+                               void* stream);
+
 /* glance_mlp_pack: the MLP weights of a full layer copied once, at load time,
- * into the projection kernel's tile order: for every 64-deep chunk of the input
- * and every block of 16 output rows (gate rows 8b..8b+7 with the matching up
- * rows for the gate/up projection), the 16 x 64 tile laid out as the
- * matrix-core operand, so that each weight load is a contiguous kilobyte.
+ * into the projection kernel's tile order (as glance_attn_pack: 16 x 64
+ * matrix-core tiles, groups of four 16-row blocks contiguous over the input
+ * chunks), the gate/up blocks pairing gate rows 8b..8b+7 with the matching up
+ * rows.
  * Gate/up first, then w_down at the next 256-byte boundary; size from
  * glance_mlp_pack_bytes (0 if unsupported).  Results with the packed copy are
  * identical to those with the row-major weights.  Limits: d_model and inter

@@ -307,13 +307,18 @@ def random_tree(rng: np.random.Generator, N: int, L: int, V: int, root: int):
 
 
 # ------------------------------------------------------------------------ rounds
-def gen_round(cfg: RoundConfig, seed: int, with_model: bool = True) -> dict:
+def gen_round(cfg: RoundConfig, seed: int, with_model: bool = True, model: dict | None = None) -> dict:
     """Draw every input of ``cfg.n_rounds`` verify rounds that share one model.
 
     Returns a dict with the model tensors (``embed``, ``w_head``, ``layers``,
     ``kv_offsets``, ``prefix_len``, ``rope_cos``, ``rope_sin``) and a list
     ``rounds`` of per-round dicts (``draft_logits`` or a given tree, ``root``,
-    plus recipe metadata such as the draft scale or the planted run)."""
+    plus recipe metadata such as the draft scale or the planted run).
+
+    ``model``: the output of an earlier call for a config of the same shapes and
+    weight distributions; its embedding, head and layer weights are reused (the
+    layers cyclically) instead of drawn again, and only the prefix caches, the
+    rounds and, in the copy regime, the biased head rows (on a copy) are new."""
     st = _Streams(seed)
     dt = cfg.dtype
     out: dict = {"cfg": cfg, "seed": seed}
@@ -382,8 +387,14 @@ def gen_round(cfg: RoundConfig, seed: int, with_model: bool = True) -> dict:
     if not with_model:
         return out
 
-    out["embed"] = _normal(st.rng("embed"), (cfg.V, cfg.d_model), cfg.embed_std, dt)
-    w_head = _normal(st.rng("head"), (cfg.V, cfg.d_model), cfg.head_std, dt)
+    if model is not None:
+        assert model["embed"].shape == (cfg.V, cfg.d_model) and model["embed"].dtype == _store(
+            np.zeros((1, 1), np.float32), dt).dtype, "the reused model has other shapes"
+        out["embed"] = model["embed"]
+        w_head = model["w_head"].copy() if plant_bias else model["w_head"]
+    else:
+        out["embed"] = _normal(st.rng("embed"), (cfg.V, cfg.d_model), cfg.embed_std, dt)
+        w_head = _normal(st.rng("head"), (cfg.V, cfg.d_model), cfg.head_std, dt)
     if plant_bias:
         # Bigram bias of the copy regime: row t_{k+1} of the head gains
         # alpha * E[t_k] / |E[t_k]|^2, so the greedy continuation follows the run.
@@ -401,6 +412,13 @@ def gen_round(cfg: RoundConfig, seed: int, with_model: bool = True) -> dict:
     for li in range(cfg.n_layers):
         rw = st.rng("layers", li)
         rk = st.rng("kv", li)
+        if model is not None:
+            src = model["layers"][li % len(model["layers"])]
+            assert src["wq"].shape == (qd, cfg.d_model), "the reused model has other shapes"
+            layers.append({k: v for k, v in src.items() if k not in ("k_cache", "v_cache")})
+            layers[-1]["k_cache"] = _normal(rk, (sumP, cfg.Hkv, cfg.D), cfg.kv_std, dt)
+            layers[-1]["v_cache"] = _normal(rk, (sumP, cfg.Hkv, cfg.D), cfg.kv_std, dt)
+            continue
         layers.append({
             "wq": _normal(rw, (qd, cfg.d_model), cfg.w_std, dt),
             "wk": _normal(rw, (kd, cfg.d_model), cfg.w_std, dt),

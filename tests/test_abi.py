@@ -181,11 +181,29 @@ def test_head_pack_rejects_bad_arguments(lib):
     assert b"scratch" in lib.glance_last_error()
 
 
+def test_attn_pack_rejects_bad_arguments(lib):
+    p = OK_PTR
+    qkv = ((32 + 16) * 128 // 16) * (4096 // 64) * 2048
+    wo = (4096 // 16) * (32 * 128 // 64) * 2048
+    assert lib.glance_attn_pack_bytes(4096, 32, 8, 128) == ((qkv + 255) // 256) * 256 + wo
+    assert lib.glance_attn_pack_bytes(4000, 32, 8, 128) == 0
+    assert lib.glance_attn_pack_bytes(4096, 32, 8, 64) == 0
+    assert lib.glance_attn_pack_bytes(4096, 30, 8, 128) == 0
+    assert lib.glance_attn_pack(p, p, p, p, 4096, 32, 8, 64, p, None) == -4
+    assert lib.glance_attn_pack(None, p, p, p, 4096, 32, 8, 128, p, None) == -1
+    assert lib.glance_attn_pack(p, p, p, p + 8, 4096, 32, 8, 128, p, None) == -2
+    assert lib.glance_attn_pack(p, p, p, p, 4096, 32, 8, 128, None, None) == -1
+    # a packed copy is bf16 only, and replaces the four row-major pointers
+    assert _attn(lib, dtype=0, D=64, packed=p) == -4
+    assert _attn(lib, layer=None, packed=p, ws_bytes=100) == -3
+
+
 def _attn(lib, **kw):
     a = dict(dtype=1, embed=OK_PTR, h_in=None, nseq=1, n_rows=64, d=4096, Hq=32, Hkv=8, D=128,
-             max_prefix=1024, n_pos=2048, ws=OK_PTR * 16, ws_bytes=1 << 40, layer=OK_PTR)
+             max_prefix=1024, n_pos=2048, ws=OK_PTR * 16, ws_bytes=1 << 40, layer=OK_PTR,
+             packed=None)
     a.update(kw)
-    lay = _lib.GlanceAttnLayer(*(a["layer"],) * 6)
+    lay = _lib.GlanceAttnLayer(*(a["layer"],) * 4, OK_PTR, OK_PTR, a["packed"])
     p = OK_PTR
     return lib.glance_tree_attn(ctypes.byref(lay), a["dtype"], a["embed"], p, a["h_in"], p, p,
                                 a["max_prefix"], p, p, p, p, a["n_pos"], a["nseq"], a["n_rows"],

@@ -1,4 +1,4 @@
-"""The LM head over packed weights: the packed bytes follow the documented tile
+"""The LM head and attention over packed weights: the packed bytes follow the documented tile
 order (rebuilt here with NumPy from the row-major weights), and the packed call
 returns exactly what the row-major call returns (same products, same
 accumulation order), greedy and sampled, on ragged vocabularies, several
@@ -55,6 +55,52 @@ def test_pack_layout(V, d):
     assert np.array_equal(got, want)
 
 
+def _pack_attn_numpy(wq, wk, wv, wo, Hq, Hkv):
+    """Packed q/k/v then wo (at the next 256-byte boundary), uint16, as
+    [16-row blocks / 4][64-deep chunks][4 blocks][2 halves][64 lanes][8]: lane l
+    of half s of block b, chunk c holds row block_row(b, l%16), columns
+    64c + 32s + 8(l/16) .. + 8."""
+    def pack(w, rows_of):
+        N, K = w.shape
+        NB = N // 16
+        out = np.zeros((NB // 4, K // 64, 4, 2, 64, 8), dtype=np.uint16)
+        l = np.arange(64)
+        for b in range(NB):
+            rows = rows_of(b, l & 15)
+            for s in range(2):
+                for c in range(K // 64):
+                    cols = 64 * c + 32 * s + 8 * (l >> 4)
+                    out[b // 4, c, b % 4, s] = w[rows[:, None], cols[:, None] + np.arange(8)[None, :]]
+        return out.reshape(-1)
+
+    nq, nk = Hq * 8, Hkv * 8
+
+    def qkv_row(b, i):
+        if b < nq + nk:
+            base, bb = (0, b) if b < nq else (Hq * 128, b - nq)
+            dim = np.where(i < 8, 8 * (bb & 7) + i, 64 + 8 * (bb & 7) + (i - 8))
+            return base + (bb >> 3) * 128 + dim
+        return (Hq + Hkv) * 128 + (b - nq - nk) * 16 + i
+
+    a = pack(np.concatenate([wq, wk, wv]), qkv_row)
+    pad = (-a.size) % 128  # 256 bytes
+    return np.concatenate([a, np.zeros(pad, np.uint16), pack(wo, lambda b, i: 16 * b + i)])
+
+
+def test_attn_pack_layout():
+    Hq, Hkv, d = 8, 2, 512
+    g = torch.Generator(device="cuda").manual_seed(11)
+    lw = {"wq": _bf16((Hq * 128, d), 1.0, g), "wk": _bf16((Hkv * 128, d), 1.0, g),
+          "wv": _bf16((Hkv * 128, d), 1.0, g), "wo": _bf16((d, Hq * 128), 1.0, g)}
+    packed = api.glance_attn_pack(lw, Hq, Hkv)
+    torch.cuda.synchronize()
+    u16 = {k: v.cpu().view(torch.int16).numpy().view(np.uint16) for k, v in lw.items()}
+    want = _pack_attn_numpy(u16["wq"], u16["wk"], u16["wv"], u16["wo"], Hq, Hkv)
+    got = packed.cpu().numpy().view(np.uint16)
+    assert got.size == want.size
+    assert np.array_equal(got, want)
+
+
 def _heads(V, d, R, seed, sample=None):
     g = torch.Generator(device="cuda").manual_seed(seed)
     w = _bf16((V, d), 0.05, g)
@@ -106,9 +152,9 @@ def test_packed_head_sampled_equals_row_major():
     ("mini_bf16_full", 3, {}),
 ])
 def test_packed_round_equals_row_major(name, seed, kw):
-    """A whole round with the packed head weights (and, for full layers, the
-    packed MLP weights): every output equals the row-major round's (tree, hidden
-    rows, new cache entries, head statistics, walk)."""
+    """A whole round with the packed head and attention weights (and, for full
+    layers, the packed MLP weights): every output equals the row-major round's
+    (tree, hidden rows, new cache entries, head statistics, walk)."""
     from synth import gen_round, make_config
     from tree_verified_block_amd.round import DeviceRound
     inp = gen_round(make_config(name, **kw), seed)

@@ -27,7 +27,8 @@ _U64 = ctypes.c_uint64
 
 
 class GlanceAttnLayer(ctypes.Structure):
-    _fields_ = [("wq", _P), ("wk", _P), ("wv", _P), ("wo", _P), ("k_cache", _P), ("v_cache", _P)]
+    _fields_ = [("wq", _P), ("wk", _P), ("wv", _P), ("wo", _P), ("k_cache", _P), ("v_cache", _P),
+                ("packed", _P)]
 
 
 class GlanceFullLayer(ctypes.Structure):
@@ -58,6 +59,8 @@ SIGNATURES = {
                                         _P, _P, _P, _P, _SZ, _P]),
     "glance_head_pack_bytes": (_SZ, [_I, _I]),
     "glance_head_pack": (_I, [_P, _I, _I, _P, _P]),
+    "glance_attn_pack_bytes": (_SZ, [_I, _I, _I, _I]),
+    "glance_attn_pack": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "glance_verify_head_packed": (_I, [_P, _P, _I, _I, _I, _F, _U64, _U64, _P, _P, _P, _P, _P, _P,
                                        _P, _P, _SZ, _P]),
     "glance_verify_head_packed_noalloc": (_I, [_P, _P, _I, _I, _I, _F, _U64, _U64, _P, _P, _P, _P,

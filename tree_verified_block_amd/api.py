@@ -97,7 +97,8 @@ def glance_tree_attn(layer: dict, dtype: int, embed, token, h_in, h_out, kv_offs
                      d_model: int, Hq: int, Hkv: int, D: int, ws, attn_out=None, tree_k=None,
                      tree_v=None, stream=None):
     lay = GlanceAttnLayer(_ptr(layer["wq"]), _ptr(layer["wk"]), _ptr(layer["wv"]),
-                          _ptr(layer["wo"]), _ptr(layer["k_cache"]), _ptr(layer["v_cache"]))
+                          _ptr(layer["wo"]), _ptr(layer["k_cache"]), _ptr(layer["v_cache"]),
+                          _ptr(layer.get("attn_packed")))
     _lib.call("glance_tree_attn", ctypes.byref(lay), dtype, _ptr(embed), _ptr(token),
               _ptr(h_in), _ptr(h_out), _ptr(kv_offsets), int(max_prefix), _ptr(depth),
               _ptr(anc), _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], nseq, n_rows,
@@ -117,7 +118,8 @@ def glance_tree_layer(layer: dict, eps: float, embed, token, h_in, h_out, kv_off
     verify rows; ``layer`` holds wq/wk/wv/wo, the caches, g_attn/g_q/g_k/g_mlp and
     w_gate/w_up/w_down (bf16)."""
     attn = GlanceAttnLayer(_ptr(layer["wq"]), _ptr(layer["wk"]), _ptr(layer["wv"]),
-                           _ptr(layer["wo"]), _ptr(layer["k_cache"]), _ptr(layer["v_cache"]))
+                           _ptr(layer["wo"]), _ptr(layer["k_cache"]), _ptr(layer["v_cache"]),
+                           _ptr(layer.get("attn_packed")))
     full = GlanceFullLayer(attn, _ptr(layer["g_attn"]), _ptr(layer["g_q"]), _ptr(layer["g_k"]),
                            _ptr(layer["g_mlp"]), _ptr(layer["w_gate"]), _ptr(layer["w_up"]),
                            _ptr(layer["w_down"]), layer["w_gate"].shape[0], float(eps),
@@ -127,6 +129,20 @@ def glance_tree_layer(layer: dict, eps: float, embed, token, h_in, h_out, kv_off
               _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], nseq, n_rows, d_model, Hq, Hkv,
               D, _ptr(attn_out), _ptr(tree_k), _ptr(tree_v), _ptr(ws), ws.numel(),
               _stream(stream))
+
+
+def glance_attn_pack(layer: dict, Hq: int, Hkv: int, stream=None):
+    """bf16 attention weights (wq/wk/wv/wo) -> the projection kernel's packed tile
+    order (a new uint8 device tensor; done once, when the weights are loaded)."""
+    qd, d_model = layer["wq"].shape
+    D = qd // Hq
+    n = _lib.load().glance_attn_pack_bytes(d_model, Hq, Hkv, D)
+    if n == 0:
+        raise ValueError(f"no packed layout for d_model={d_model}, Hq={Hq}, Hkv={Hkv}, D={D}")
+    out = torch.empty(n, dtype=torch.uint8, device=layer["wq"].device)
+    _lib.call("glance_attn_pack", _ptr(layer["wq"]), _ptr(layer["wk"]), _ptr(layer["wv"]),
+              _ptr(layer["wo"]), d_model, Hq, Hkv, D, _ptr(out), _stream(stream))
+    return out
 
 
 def glance_mlp_pack(layer: dict, stream=None):

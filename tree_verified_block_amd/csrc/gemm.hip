@@ -175,7 +175,10 @@ __device__ __forceinline__ int block_row(const GemmArgs& a, int b, int i) {
   if constexpr (EPI == EPI_SWIGLU) {
     // rows i < 8: gate rows 8b + i; rows 8 + i: the matching up rows
     return i < 8 ? 8 * b + i : a.N / 2 + 8 * b + (i - 8);
-  } else if constexpr (EPI == EPI_QKV) {
+  } else if constexpr (EPI == EPI_QKV || EPI == EPI_STORE_F32) {
+    // q and k blocks pair head dims 8j + i with their RoPE partners 64 + 8j + i
+    // (the fp32 store of full layers keeps the same order, so that one packed
+    // copy of the weights serves both)
     const int nq = a.Hq * 8, nk = a.Hkv * 8;
     if (b < nq + nk) {
       const int base = b < nq ? 0 : a.Hq * 128;
@@ -609,9 +612,14 @@ __device__ __forceinline__ void proj_store(const GemmArgs& a, int b, int gm, con
     op[0] = o[0];
     op[1] = o[1];
   } else if constexpr (EPI == EPI_STORE_F32) {
-    float4* op = reinterpret_cast<float4*>(a.out_f32 + static_cast<size_t>(gm) * a.N + b * 16);
+    // rows i < 8 and 8 + i are two runs of 8 columns (block_row)
+    float* orow = a.out_f32 + static_cast<size_t>(gm) * a.N;
 #pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) op[k4] = make_float4(x[4 * k4], x[4 * k4 + 1], x[4 * k4 + 2], x[4 * k4 + 3]);
+    for (int h = 0; h < 2; ++h) {
+      float4* op = reinterpret_cast<float4*>(orow + block_row<EPI>(a, b, 8 * h));
+      op[0] = make_float4(x[8 * h], x[8 * h + 1], x[8 * h + 2], x[8 * h + 3]);
+      op[1] = make_float4(x[8 * h + 4], x[8 * h + 5], x[8 * h + 6], x[8 * h + 7]);
+    }
   } else if constexpr (EPI == EPI_SWIGLU) {
     // x[i] the gate and x[8 + i] the up projection of intermediate unit 8b + i
     uint32_t ow[4];
@@ -684,11 +692,16 @@ __device__ __forceinline__ void proj_store(const GemmArgs& a, int b, int gm, con
 // matrices, their rounding and the rounded remainder, each chunk staged as both
 // and multiplied by the same weight operand (two products per step): the
 // output projection then sees its input to ~16 significant bits.
-template <int EPI, int DEPTH, bool XF>
-__global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int NB, int NGr,
-                                                                 int S, int nMT) {
+//
+// KW = 2: eight waves, the four blocks times two halves of the slice, each half
+// staging its own activation chunks; the halves' sums meet in LDS before the
+// epilogue (two waves per SIMD at one work-group per CU, no more partials).
+template <int EPI, int DEPTH, bool XF, int KW>
+__global__ __launch_bounds__(kGThreads * KW, (XF || DEPTH > 7 || KW > 1) ? 1 : 2) void proj_bf16_kernel(
+    GemmArgs a, int NB, int NGr, int S, int nMT) {
   constexpr int NX = XF ? 4 : 2;  // 16-byte activation loads per thread and chunk
-  __shared__ __attribute__((aligned(16))) uint16_t xs[(XF ? 4 : 2) * kXS];
+  constexpr int XH = (XF ? 4 : 2) * kXS;  // one half's stage ring (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t xs_all[KW * XH];
 
   const int bid = blockIdx.x;
   const int xcd = bid & 7, kk = bid >> 3;
@@ -697,12 +710,16 @@ __global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int
   const int g = (kk / (nMT * S)) * 8 + xcd;
   if (g >= NGr) return;
   const int m0 = mt * kTileM;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+  const int tid_all = threadIdx.x, l = tid_all & 63, lr = l & 15, lg = l >> 4;
+  const int w = (tid_all >> 6) & 3;  // block of the group
+  const int wk = tid_all >> 8;       // half of the slice (KW = 2)
+  const int tid = tid_all & (kGThreads - 1);
+  uint16_t* xs = xs_all + wk * XH;
   const int b = g * 4 + w;
   const bool bv = b < NB;
   const int Ks = a.K / S;
-  const int kbase = q * Ks;
-  const int nck = Ks / kKc;
+  const int kbase = q * Ks + wk * (Ks / KW);
+  const int nck = Ks / KW / kKc;
   // the epilogue's own inputs for activation row m0 + l (rows past M: the last)
   const int gme = min(m0 + l, a.M - 1);
   EpiIn ein;
@@ -714,10 +731,10 @@ __global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int
   const char* wb;
   size_t wcs, whs;
   if (a.w_packed) {
-    const int bc = bv ? b : NB - 1;
+    // group g's four blocks are one contiguous stream over the chunks
     wb = static_cast<const char*>(a.w_packed) +
-         ((static_cast<size_t>(kbase / kKc) * NB + bc) * 128 + l) * 16;
-    wcs = static_cast<size_t>(NB) * 2048;
+         (((static_cast<size_t>(g) * (a.K / kKc) + kbase / kKc) * 4 + w) * 128 + l) * 16;
+    wcs = 4 * 2048;
     whs = 1024;
   } else {
     int row = bv ? block_row<EPI>(a, b, lr) : 0;
@@ -809,19 +826,28 @@ __global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int
         wload(cn, wbuf[(u + DEPTH) % RS]);
         __syncthreads();
         const uint16_t* xq = xs + (u & 1) * kXS;
+        // every activation operand of the chunk is read from LDS before the
+        // first product, so the reads overlap instead of each product waiting
+        // on its own read
+        constexpr int NV = XF ? 2 : 1;
+        bf16x8 bx[2][4][NV];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+              bx[s][mb][v] = *reinterpret_cast<const bf16x8*>(
+                  xq + 2 * v * kXS + (mb * 16 + lr) * kXP + s * 32 + 8 * lg);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           const bf16x8 av = __builtin_bit_cast(bf16x8, wbuf[u][s]);
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb) {
-            const int xo = (mb * 16 + lr) * kXP + s * 32 + 8 * lg;
-            const bf16x8 bx = *reinterpret_cast<const bf16x8*>(xq + xo);
-            acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bx, acc[mb], 0, 0, 0);
-            if constexpr (XF) {
-              const bf16x8 bl = *reinterpret_cast<const bf16x8*>(xq + 2 * kXS + xo);
-              acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, acc[mb], 0, 0, 0);
-            }
-          }
+          for (int v = 0; v < NV; ++v)
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+              acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bx[s][mb][v], acc[mb], 0, 0, 0);
         }
         // (after the last chunk this stores a clamped copy nobody reads)
         xstage((u + 1) & 1, xbuf[(u + 1) % RS]);
@@ -835,26 +861,65 @@ __global__ __launch_bounds__(kGThreads, 2) void proj_bf16_kernel(GemmArgs a, int
   // counter and the partials are shared, both through device-scope atomic
   // accesses (write-through stores and coherent loads), and every store has
   // completed before the arrival is counted, so no cache write-back is needed.
+  if constexpr (KW > 1) {
+    // the second half's sums join the first's (same lane layout) through LDS
+    float* hp = reinterpret_cast<float*>(xs_all) + w * 1024 + l;
+    __syncthreads();
+    if (wk == 1) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) hp[(mb * 4 + v) * 64] = acc[mb][v];
+    }
+    __syncthreads();
+    if (wk == 0) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[mb][v] += hp[(mb * 4 + v) * 64];
+    }
+  }
   if (bv) epi_load<EPI>(a, b, gme, ein);
+  if (S == 1) {
+    // no other slice: the block's 16 x 64 result goes through LDS (the stage
+    // ring is free after the barrier) to one thread per activation row
+    float* tr = reinterpret_cast<float*>(xs_all) + w * 1024;
+    __syncthreads();
+    if (wk == 0) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) tr[(4 * lg + v) * 64 + mb * 16 + lr] = acc[mb][v];
+    }
+    __syncthreads();
+    if (wk != 0 || !bv || m0 + l >= a.M) return;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = tr[i * 64 + l];
+    proj_store<EPI>(a, b, m0 + l, x, ein);
+    return;
+  }
   const size_t grp = static_cast<size_t>(mt) * NGr + g;
   float* pp = a.kpart + ((grp * S + q) * 4 + w) * 1024;
+  if (wk == 0) {
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-      __hip_atomic_store(pp + (4 * lg + v) * 64 + mb * 16 + lr, acc[mb][v], __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      for (int v = 0; v < 4; ++v)
+        __hip_atomic_store(pp + (4 * lg + v) * 64 + mb * 16 + lr, acc[mb][v], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __shared__ int s_last;
   __syncthreads();
-  if (tid == 0) {
+  if (tid_all == 0) {
     const unsigned old = __hip_atomic_fetch_add(a.kcnt + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = old == static_cast<unsigned>(S - 1);
     if (last) __hip_atomic_store(a.kcnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = last;
   }
   __syncthreads();
-  if (!s_last || !bv) return;
+  if (!s_last || !bv || wk != 0) return;
   // thread (w, l): activation row m0 + l of block b
   float x[16];
 #pragma unroll
@@ -1062,18 +1127,26 @@ __global__ __launch_bounds__(256) void head_pack_kernel(const uint16_t* __restri
 }
 }  // namespace
 
-// Packed projection weights: [K/64 chunks][NB blocks][2 halves][64 lanes] x 16
-// bytes; lane l of half s of block b holds row block_row(b, l%16), columns
-// 64 c + 32 s + 8 (l/16) .. + 8 (the MFMA operand of that block and chunk).
+// Packed projection weights: [NB/4 groups][K/64 chunks][4 blocks][2 halves]
+// [64 lanes] x 16 bytes, so that the four blocks one work-group multiplies are
+// a single contiguous stream; lane l of half s of block b = 4 g + j holds row
+// block_row(b, l%16), columns 64 c + 32 s + 8 (l/16) .. + 8 (the MFMA operand
+// of that block and chunk).  Blocks past NB are zero.
 template <int EPI>
 __global__ __launch_bounds__(256) void proj_pack_kernel(GemmArgs a, int NB, size_t n16,
                                                         uint4* __restrict__ out) {
+  const int nch = a.K / kKc;
   for (size_t o = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; o < n16;
        o += static_cast<size_t>(gridDim.x) * 256) {
     const int l = static_cast<int>(o & 63), s = static_cast<int>((o >> 6) & 1);
     const size_t rest = o >> 7;
-    const int b = static_cast<int>(rest % NB);
-    const int c = static_cast<int>(rest / NB);
+    const int j = static_cast<int>(rest & 3);
+    const int c = static_cast<int>((rest >> 2) % nch);
+    const int b = static_cast<int>((rest >> 2) / nch) * 4 + j;
+    if (b >= NB) {
+      out[o] = make_uint4(0u, 0u, 0u, 0u);
+      continue;
+    }
     const int row = block_row<EPI>(a, b, l & 15);
     const int col = c * kKc + 32 * s + 8 * (l >> 4);
     out[o] = *reinterpret_cast<const uint4*>(w_row_ptr(a, row) + col);
@@ -1109,7 +1182,7 @@ glance_status head_scratch_ptr(float** out) {
 }
 
 size_t proj_pack_bytes(int N, int K) {
-  return static_cast<size_t>(K / kKc) * ((N + 15) / 16) * 2048;
+  return static_cast<size_t>(K / kKc) * (((N + 15) / 16 + 3) / 4) * 4 * 2048;
 }
 
 glance_status launch_proj_pack(const GemmArgs& a, void* w_packed, hipStream_t st) {
@@ -1119,6 +1192,8 @@ glance_status launch_proj_pack(const GemmArgs& a, void* w_packed, hipStream_t st
   if (blocks > 8192) blocks = 8192;
   if (a.epi == EPI_SWIGLU)
     proj_pack_kernel<EPI_SWIGLU><<<static_cast<unsigned>(blocks), 256, 0, st>>>(a, NB, n16, static_cast<uint4*>(w_packed));
+  else if (a.epi == EPI_QKV)
+    proj_pack_kernel<EPI_QKV><<<static_cast<unsigned>(blocks), 256, 0, st>>>(a, NB, n16, static_cast<uint4*>(w_packed));
   else
     proj_pack_kernel<EPI_RESID><<<static_cast<unsigned>(blocks), 256, 0, st>>>(a, NB, n16, static_cast<uint4*>(w_packed));
   GLANCE_LAUNCH_CHECK();
@@ -1140,14 +1215,18 @@ glance_status launch_head_pack(const void* w, int N, int K, void* w_packed, hipS
   return GLANCE_OK;
 }
 
+#ifndef GLANCE_PROJ_WGS
+#define GLANCE_PROJ_WGS 256
+#endif
 int proj_ksplit(int K, int NB) {
   // about one work-group per CU: S ~ 256 / (number of 4-block groups), taken as a
-  // divisor of half the chunk count (each slice an even number of chunks)
+  // divisor of half the chunk count (each slice an even number of chunks).  Wide
+  // projections (more groups than CUs, the MLP) take no split: every work-group
+  // is resident at two per CU and no partial sums cross work-groups.
   const int nch = K / kKc;
   const int NGr = (NB + 3) / 4;
-  int target = 256 / NGr;
+  int target = GLANCE_PROJ_WGS / NGr;
   if (target < 1) target = 1;
-  if (NGr > 256) target = 2;  // wide projections (MLP): two slices, up to 3 work-groups per CU
   int S = 1;
   for (int c = 1; c <= nch / 2; ++c)
     if ((nch / 2) % c == 0 && c <= target) S = c;
@@ -1189,32 +1268,47 @@ glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
     const int NGr = (NB + 3) / 4;
     const int S = proj_ksplit(a.K, NB);
     const int grid = ((NGr + 7) / 8) * 8 * S * nMT;
-    // ring depth: the largest of 8, 4, 2 slots dividing the slice's chunk count
-    const int nck = a.K / S / kKc;
-    const int rs = nck % 8 == 0 ? 8 : nck % 4 == 0 ? 4 : 2;
-#define GLANCE_PROJ(E)                                                               \
+    // at most one work-group per CU: eight waves splitting the slice in two
+    // halves (two waves per SIMD); wider grids: four waves.  Ring depth: the
+    // largest of 8, 4, 2 slots dividing the chunk count of a wave's range (4 at
+    // most for fp32 activations in eight-wave groups, for registers).
+    const int kw = grid <= 256 && (a.K / S / kKc) % 4 == 0 ? 2 : 1;
+    const int nck = a.K / S / kw / kKc;
+    int rs = nck % 8 == 0 ? 8 : nck % 4 == 0 ? 4 : 2;
+    if (kw == 2 && a.x_f32 && rs > 4) rs = 4;
+    const unsigned nthr = kGThreads * kw;
+#define GLANCE_PROJ_KW(E, X, KW)                                                      \
   if (rs == 8)                                                                       \
-    proj_bf16_kernel<E, 7, false><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);    \
+    proj_bf16_kernel<E, 7, X, KW><<<grid, nthr, 0, st>>>(a, NB, NGr, S, nMT);         \
   else if (rs == 4)                                                                  \
-    proj_bf16_kernel<E, 3, false><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);    \
+    proj_bf16_kernel<E, 3, X, KW><<<grid, nthr, 0, st>>>(a, NB, NGr, S, nMT);         \
   else                                                                               \
-    proj_bf16_kernel<E, 1, false><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
+    proj_bf16_kernel<E, 1, X, KW><<<grid, nthr, 0, st>>>(a, NB, NGr, S, nMT);
+#define GLANCE_PROJ(E, X)    \
+  if (kw == 2) {             \
+    GLANCE_PROJ_KW(E, X, 2)  \
+  } else {                   \
+    GLANCE_PROJ_KW(E, X, 1)  \
+  }
     if (a.epi == EPI_QKV) {
-      GLANCE_PROJ(EPI_QKV)
+      GLANCE_PROJ(EPI_QKV, false)
     } else if (a.epi == EPI_SWIGLU) {
-      GLANCE_PROJ(EPI_SWIGLU)
+      GLANCE_PROJ(EPI_SWIGLU, false)
     } else if (a.epi == EPI_STORE_F32) {
-      GLANCE_PROJ(EPI_STORE_F32)
+      GLANCE_PROJ(EPI_STORE_F32, false)
     } else if (a.x_f32) {
-      if (rs == 8)
-        proj_bf16_kernel<EPI_RESID, 7, true><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
-      else if (rs == 4)
-        proj_bf16_kernel<EPI_RESID, 3, true><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
-      else
-        proj_bf16_kernel<EPI_RESID, 1, true><<<grid, kGThreads, 0, st>>>(a, NB, NGr, S, nMT);
+      if (kw == 2) {
+        if (rs == 4)
+          proj_bf16_kernel<EPI_RESID, 3, true, 2><<<grid, nthr, 0, st>>>(a, NB, NGr, S, nMT);
+        else
+          proj_bf16_kernel<EPI_RESID, 1, true, 2><<<grid, nthr, 0, st>>>(a, NB, NGr, S, nMT);
+      } else {
+        GLANCE_PROJ_KW(EPI_RESID, true, 1)
+      }
     } else {
-      GLANCE_PROJ(EPI_RESID)
+      GLANCE_PROJ(EPI_RESID, false)
     }
+#undef GLANCE_PROJ_KW
 #undef GLANCE_PROJ
   }
   GLANCE_LAUNCH_CHECK();

@@ -32,6 +32,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
+// The output-projection part of a glance_attn_pack copy (after the q/k/v part).
+const void* packed_wo(const void* packed, int d_model, int Hq, int Hkv, int D) {
+  return static_cast<const char*>(packed) + round256(proj_pack_bytes((Hq + 2 * Hkv) * D, d_model));
+}
+
 #define REQUIRE(cond, ...)                                               \
   do {                                                                   \
     if (!(cond)) return fail(GLANCE_ERR_INVALID_ARG, __VA_ARGS__);       \
@@ -258,11 +263,17 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
       return fail(GLANCE_ERR_UNSUPPORTED, "fp32 tree attention needs even D <= 128 (got %d)", D);
     if (max_prefix > 8192)
       return fail(GLANCE_ERR_UNSUPPORTED, "fp32 tree attention needs max_prefix <= 8192");
+    if (layer->packed)
+      return fail(GLANCE_ERR_UNSUPPORTED, "packed attention weights are bf16 only");
   }
-  REQUIRE_PTR(layer->wq);
-  REQUIRE_PTR(layer->wk);
-  REQUIRE_PTR(layer->wv);
-  REQUIRE_PTR(layer->wo);
+  if (layer->packed) {
+    REQUIRE_PTR(layer->packed);
+  } else {
+    REQUIRE_PTR(layer->wq);
+    REQUIRE_PTR(layer->wk);
+    REQUIRE_PTR(layer->wv);
+    REQUIRE_PTR(layer->wo);
+  }
   REQUIRE_PTR(layer->k_cache);
   REQUIRE_PTR(layer->v_cache);
   REQUIRE_ALIGNED_OR_NULL(embed);
@@ -309,6 +320,7 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
   g.K = d_model;
   if (dtype == GLANCE_BF16) {
     g.epi = EPI_QKV;
+    g.w_packed = layer->packed;
     g.Hq = Hq;
     g.Hkv = Hkv;
     g.q_out = base + w.off_q;
@@ -380,6 +392,7 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
   o.out_res = h_out;
   o.kpart = kpart;
   o.kcnt = kcnt;
+  if (layer->packed) o.w_packed = packed_wo(layer->packed, d_model, Hq, Hkv, D);
   return dtype == GLANCE_BF16 ? launch_gemm_bf16(o, hs) : launch_gemm_f32(o, hs);
 }
 
@@ -419,10 +432,14 @@ glance_status glance_tree_layer(const glance_full_layer* layer, const void* embe
                 "full layer needs D = 128 and d_model, Hq*D, inter multiples of 256 (got D %d, "
                 "d_model %d, Hq*D %d, inter %d)", D, d_model, Hq * D, inter);
   const glance_attn_layer* at = &layer->attn;
-  REQUIRE_PTR(at->wq);
-  REQUIRE_PTR(at->wk);
-  REQUIRE_PTR(at->wv);
-  REQUIRE_PTR(at->wo);
+  if (at->packed) {
+    REQUIRE_PTR(at->packed);
+  } else {
+    REQUIRE_PTR(at->wq);
+    REQUIRE_PTR(at->wk);
+    REQUIRE_PTR(at->wv);
+    REQUIRE_PTR(at->wo);
+  }
   REQUIRE_PTR(at->k_cache);
   REQUIRE_PTR(at->v_cache);
   REQUIRE_PTR(layer->g_attn);
@@ -482,6 +499,9 @@ glance_status glance_tree_layer(const glance_full_layer* layer, const void* embe
   g.N = qd + 2 * kd;
   g.K = d_model;
   g.epi = EPI_STORE_F32;
+  g.w_packed = at->packed;
+  g.Hq = Hq;
+  g.Hkv = Hkv;
   g.out_f32 = qkv32;
   g.kpart = kpart;
   g.kcnt = kcnt;
@@ -538,6 +558,7 @@ glance_status glance_tree_layer(const glance_full_layer* layer, const void* embe
   o.out_res = h1;
   o.kpart = kpart;
   o.kcnt = kcnt;
+  if (at->packed) o.w_packed = packed_wo(at->packed, d_model, Hq, Hkv, D);
   st = launch_gemm_bf16(o, hs);
   if (st != GLANCE_OK) return st;
 
@@ -579,6 +600,54 @@ glance_status glance_tree_layer(const glance_full_layer* layer, const void* embe
   if (layer->mlp_packed)
     dn.w_packed = static_cast<const char*>(layer->mlp_packed) + round256(proj_pack_bytes(2 * inter, d_model));
   return launch_gemm_bf16(dn, hs);
+}
+
+size_t glance_attn_pack_bytes(int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D) {
+  if (d_model < 256 || d_model % 256 != 0 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0 || D != 128)
+    return 0;
+  const int qd = Hq * D, kd = Hkv * D;
+  if (qd % 256 != 0) return 0;
+  return round256(proj_pack_bytes(qd + 2 * kd, d_model)) + proj_pack_bytes(d_model, qd);
+}
+
+glance_status glance_attn_pack(const void* wq, const void* wk, const void* wv, const void* wo,
+                               int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D, void* packed,
+                               void* stream) {
+  g_last_error.clear();
+  if (glance_attn_pack_bytes(d_model, Hq, Hkv, D) == 0)
+    return fail(GLANCE_ERR_UNSUPPORTED, "packed attention weights need D = 128, Hq a multiple of "
+                "Hkv and d_model, Hq*D multiples of 256 (got d_model %d, Hq %d, Hkv %d, D %d)",
+                d_model, Hq, Hkv, D);
+  REQUIRE_PTR(wq);
+  REQUIRE_PTR(wk);
+  REQUIRE_PTR(wv);
+  REQUIRE_PTR(wo);
+  REQUIRE_PTR(packed);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int qd = Hq * D, kd = Hkv * D;
+  GemmArgs g{};
+  g.w.w[0] = wq;
+  g.w.w[1] = wk;
+  g.w.w[2] = wv;
+  g.w.n_end[0] = qd;
+  g.w.n_end[1] = qd + kd;
+  g.w.n_end[2] = qd + 2 * kd;
+  g.w.nseg = 3;
+  g.N = qd + 2 * kd;
+  g.K = d_model;
+  g.epi = EPI_QKV;
+  g.Hq = Hq;
+  g.Hkv = Hkv;
+  glance_status st = launch_proj_pack(g, packed, hs);
+  if (st != GLANCE_OK) return st;
+  GemmArgs o{};
+  o.w.w[0] = wo;
+  o.w.n_end[0] = d_model;
+  o.w.nseg = 1;
+  o.N = d_model;
+  o.K = qd;
+  o.epi = EPI_RESID;
+  return launch_proj_pack(o, const_cast<void*>(packed_wo(packed, d_model, Hq, Hkv, D)), hs);
 }
 
 size_t glance_mlp_pack_bytes(int32_t d_model, int32_t inter) {

@@ -29,9 +29,9 @@ class DeviceRound:
     (Philox key ``seed``, counter round ``round_id``) and the walk runs on the
     draws instead of the argmax; ``commit()`` moves to the next round id.
 
-    ``packed_head`` (bf16): the LM-head weights (and the MLP weights of full
-    layers) are packed once into their kernels' tile orders and every round
-    reads the packed copies."""
+    ``packed_head`` (bf16): the LM-head weights, the attention weights (and the
+    MLP weights of full layers) are packed once into their kernels' tile orders
+    and every round reads the packed copies."""
 
     def __init__(self, inp: dict, device="cuda", keep_layers: bool = False,
                  want_logits: bool = False, capacity: int | None = None,
@@ -54,9 +54,11 @@ class DeviceRound:
                 raise ValueError("the packed head is bf16 only")
             self.w_packed = api.glance_head_pack(self.w_head)
         self.layers = [{k: to_device(v, dt, device) for k, v in lw.items()} for lw in inp["layers"]]
-        if packed_head and getattr(cfg, "mlp", 0) > 0:
+        if packed_head:
             for lw in self.layers:
-                lw["mlp_packed"] = api.glance_mlp_pack(lw)
+                lw["attn_packed"] = api.glance_attn_pack(lw, cfg.Hq, cfg.Hkv)
+                if getattr(cfg, "mlp", 0) > 0:
+                    lw["mlp_packed"] = api.glance_mlp_pack(lw)
         self.kv_offsets = torch.from_numpy(inp["kv_offsets"].astype(np.int64)).to(device)
         self.max_prefix = int(inp["prefix_len"].max())
         self.capacity = capacity
