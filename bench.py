@@ -300,9 +300,11 @@ def shared_measure(K: int, seed: int = 4, budget_per_seq: int = 31, n_max: int =
                    oracle: bool = True) -> dict:
     """Steps 1-2 of an 8-sequence batch (8B vocabulary, L 15, mixed draft
     entropies) under one shared node budget (8 x 31 nodes, at most 63 per
-    sequence), timed with HIP events around each call; beside it the
-    fixed-width build of the same batch (31 nodes each) and the CPU oracle of
-    the shared build."""
+    sequence), each round keyed by ln V(H) of its root entropy through the
+    entropy law (pooled fit b0 0.96, b1 0.63, horizon L; root entropies drawn
+    uniform over the pages' 0.1-6 nat span), timed with HIP events around the
+    two calls; beside it the fixed-width build of the same batch (31 nodes
+    each) and the CPU oracle of the shared build."""
     import torch
     from synth import gen_round, make_config
     from tree_verified_block_amd import api
@@ -313,8 +315,10 @@ def shared_measure(K: int, seed: int = 4, budget_per_seq: int = 31, n_max: int =
     nseq, L, V = rd["draft_logits"].shape
     draft = to_device(rd["draft_logits"], cfg.dtype, "cuda")
     root = torch.tensor(rd["root"].astype(np.int32), device="cuda")
-    w = np.random.default_rng(seed).normal(0.0, 1.0, nseq).astype(np.float32)
-    wd = torch.tensor(w, device="cuda")
+    b0, b1 = 0.96, 0.63
+    Hroot = np.random.default_rng(seed).uniform(0.1, 6.0, nseq).astype(np.float32)
+    Hd = torch.tensor(Hroot, device="cuda")
+    wd = torch.empty(nseq, dtype=torch.float32, device="cuda")
     B = nseq * budget_per_seq
     out = api.tree_outputs(nseq, n_max, "cuda")
     out_fixed = api.tree_outputs(nseq, budget_per_seq, "cuda")
@@ -332,20 +336,26 @@ def shared_measure(K: int, seed: int = 4, budget_per_seq: int = 31, n_max: int =
         torch.cuda.synchronize()
         return float(np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e3)
 
-    us = timed(lambda: api.glance_build_tree_shared(draft, root, wd, n_max, B, out, ws))
+    def keyed():
+        api.glance_entropy_log_value(Hd, b0, b1, L, wd)
+        api.glance_build_tree_shared(draft, root, wd, n_max, B, out, ws)
+
+    us = timed(keyed)
     us_fixed = timed(lambda: api.glance_build_tree(draft, root, budget_per_seq, out_fixed, ws))
     n = (out["n_valid"].cpu().numpy() - 1).tolist()
     nbytes = nseq * L * V * 2 + nseq * (n_max + 1) * 28
     res = {"workload": f"qwen8b_ragged8 drafts: {nseq} sequences x L {L} x V {V} bf16, budget {B} "
-                       f"nodes (at most {n_max} per sequence), weights N(0, 1)",
+                       f"nodes (at most {n_max} per sequence), weights ln V(H) of root entropies "
+                       f"U(0.1, 6) nats (b0 {b0}, b1 {b1}, horizon {L})",
            "us_per_call": round(us, 2), "calls_per_s": round(1e6 / us, 1), "nodes": n,
            "algorithmic_bytes": nbytes, "hbm_frac": round(nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
            "fixed_width_us": round(us_fixed, 2)}
     if oracle:
         from oracle import shared as sh
         t0 = time.perf_counter()
+        w = sh.log_value(Hroot.astype(np.float64), b0, b1, L).astype(np.float32).astype(np.float64)
         sh.build_trees([rd["draft_logits"][s] for s in range(nseq)], cfg.dtype, rd["root"],
-                       w.astype(np.float64), B, n_max)
+                       w, B, n_max)
         res["oracle_s"] = round(time.perf_counter() - t0, 2)
     return res
 

@@ -115,8 +115,8 @@ size_t glance_build_tree_flag_offset(int32_t nseq, int32_t L, int32_t V, int32_t
  * masses, each round's masses indexed by its value V(H)).
  *
  * Defines: sequence s's prefixes carry the key log_weight[s] + sum_j log q_j(y_j)
- * (log_weight[s] = ln V(H_s), supplied by the caller: the value law's fitted
- * constants are data, not part of the method).  The batch takes the `budget`
+ * (log_weight[s] = ln V(H_s), e.g. from glance_entropy_log_value; any finite or
+ * -inf weights are accepted).  The batch takes the `budget`
  * highest keys, equal keys going to the lower sequence and, within a
  * sequence, following the order of glance_build_tree (score, depth, parent,
  * token); every sequence keeps at most n_max nodes, and keys below
@@ -132,6 +132,30 @@ size_t glance_build_tree_flag_offset(int32_t nseq, int32_t L, int32_t V, int32_t
  * Limits: 1 <= nseq <= GLANCE_MAX_SHARED; the rest as glance_build_tree, whose
  * workspace size (glance_build_tree_ws) also serves this call.
  */
+/* glance_entropy_log_value: the per-round log weights of glance_build_tree_shared
+ * from each round's root entropy, through the entropy law of draftability
+ * (paper §6, Eq. 2; App. B; App. B.5, Eq. 5 and Proposition 4; project page
+ * "An Entropy Law of Draftability"):
+ *   p_m(H)   = 1 / (1 + exp(-(b0 - b1 H)))         match probability at the root
+ *   E[a | H] = sum_{l=1}^{L} p_m^l                  accepted length, horizon L
+ *   V(H)     = E[a | H] (1 - p_m(H)) = p_m (1 - p_m^L)
+ *   log_weight[s] = ln V(H_s)                       float32
+ * (V is defined up to a factor common to all rounds, which leaves the
+ * allocation unchanged.)  V is largest at intermediate entropy: rounds whose
+ * acceptance is hopeless or already deep gain least from more width.
+ *
+ *   entropy     device float32, H_s = entropy[s * stride] in nats (e.g. the
+ *               entropy output of glance_verify_head with stride n_rows, row 0
+ *               of each sequence); a NaN entropy gives -inf (no width)
+ *   nseq >= 1, stride >= 1
+ *   b0, b1      the law's intercept and slope (finite; the pages fit b1 > 0)
+ *   L >= 1      block horizon (the tree depth)
+ *   log_weight  [nseq] device float32 output
+ * Pointers 4-byte aligned.  Asynchronous on `stream`.
+ */
+glance_status glance_entropy_log_value(const float* entropy, int32_t nseq, int32_t stride, float b0,
+                                       float b1, int32_t L, float* log_weight, void* stream);
+
 #define GLANCE_MAX_SHARED 16
 glance_status glance_build_tree_shared(const void* draft_logits, int32_t dtype,
                                        const int32_t* root_token, const float* log_weight,

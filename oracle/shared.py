@@ -6,8 +6,9 @@ length is global best-first over node masses, each round's masses indexed by
 its value V(H) (Eq. 5), until the marginal mass falls below the exchange rate.
 
 Reading used here.  Round s (one sequence of the batch) gives its prefixes the
-key  omega_s + sum_j log q_j(y_j),  with omega_s = ln V(H_s) supplied by the
-caller (the law's fitted constants are data, not part of the method), and
+key  omega_s + sum_j log q_j(y_j),  with omega_s = ln V(H_s) (``log_value``:
+the law's fitted constants b0, b1 and the horizon L are inputs, and the
+entropy H_s of each round's root comes with the round), and
   * the budget B is the total number of tree nodes over the batch,
   * every round keeps at most n_max nodes (its verify rows),
   * a node whose key is below tau (the stopping rule, in log units) or -inf is
@@ -24,6 +25,34 @@ import numpy as np
 
 from . import draft, tree as tr
 from .numerics import decode
+
+
+def log_match_probability(H, b0: float, b1: float):
+    """ln p_m(H) and ln(1 - p_m(H)) with p_m(H) = sigma(b0 - b1 H): the law's
+    affine match logit (paper §6, Eq. 2; project page "An Entropy Law of
+    Draftability"), in logs so that no entropy underflows them."""
+    x = b0 - b1 * np.asarray(H, dtype=np.float64)
+    with np.errstate(invalid="ignore"):  # a NaN entropy stays NaN here
+        return -np.logaddexp(0.0, -x), -np.logaddexp(0.0, x)
+
+
+def log_expected_accept(H, b0: float, b1: float, L: int):
+    """ln E[a | H] with E[a | H] ~ sum_{l=1}^{L} p_m^l, the survival sum truncated
+    at the block horizon L (paper App. B, the slowly varying step; project page,
+    the same sum in closed form)."""
+    lnp, _ = log_match_probability(H, b0, b1)
+    return np.logaddexp.reduce(np.stack([l * lnp for l in range(1, L + 1)]), axis=0)
+
+
+def log_value(H, b0: float, b1: float, L: int):
+    """ln V(H) with V(H) = E[a | H] (1 - p_m(H)) (paper App. B.5, Eq. 5: the
+    round's marginal value of width, up to a constant factor that is the same
+    for every round and so leaves the allocation unchanged).  A NaN entropy
+    gives -inf (the round receives no width)."""
+    H = np.asarray(H, dtype=np.float64)
+    _, ln1mp = log_match_probability(H, b0, b1)
+    v = log_expected_accept(H, b0, b1, L) + ln1mp
+    return np.where(np.isnan(H), -np.inf, v)
 
 
 def allocate(logqs, log_weight, B: int, n_max: int, tau: float = -np.inf):

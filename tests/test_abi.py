@@ -181,6 +181,18 @@ def test_head_pack_rejects_bad_arguments(lib):
     assert b"scratch" in lib.glance_last_error()
 
 
+def test_entropy_log_value_rejects_bad_arguments(lib):
+    p = OK_PTR
+    assert lib.glance_entropy_log_value(p, 0, 1, 0.96, 0.63, 15, p, None) == -1
+    assert lib.glance_entropy_log_value(p, 4, 0, 0.96, 0.63, 15, p, None) == -1
+    assert lib.glance_entropy_log_value(p, 4, 1, 0.96, 0.63, 0, p, None) == -1
+    assert lib.glance_entropy_log_value(p, 4, 1, float("nan"), 0.63, 15, p, None) == -1
+    assert lib.glance_entropy_log_value(p, 4, 1, 0.96, float("inf"), 15, p, None) == -1
+    assert lib.glance_entropy_log_value(None, 4, 1, 0.96, 0.63, 15, p, None) == -1
+    assert lib.glance_entropy_log_value(p, 4, 1, 0.96, 0.63, 15, None, None) == -1
+    assert lib.glance_entropy_log_value(p + 2, 4, 1, 0.96, 0.63, 15, p, None) == -2
+
+
 def test_attn_pack_rejects_bad_arguments(lib):
     p = OK_PTR
     qkv = ((32 + 16) * 128 // 16) * (4096 // 64) * 2048

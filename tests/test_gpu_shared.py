@@ -26,17 +26,19 @@ def _run(drafts, dtype, roots, w, B, n_max, tau=float("-inf")):
     nseq, L, V = drafts.shape
     out = api.tree_outputs(nseq, n_max, "cuda")
     ws = api.workspace(api.build_tree_ws_bytes(nseq, L, V, n_max), "cuda")
+    wd = w if torch.is_tensor(w) else torch.tensor(np.asarray(w, np.float32), device="cuda")
     api.glance_build_tree_shared(_device_draft(drafts, dtype),
                                  torch.tensor(np.asarray(roots, np.int32), device="cuda"),
-                                 torch.tensor(np.asarray(w, np.float32), device="cuda"),
-                                 n_max, B, out, ws, min_log_value=tau)
+                                 wd, n_max, B, out, ws, min_log_value=tau)
     torch.cuda.synchronize()
     res = {k: v.cpu().numpy() for k, v in out.items()}
     res["anc"] = res["anc"].view(np.uint64)
     return res
 
 
-def _case(name, seed, B, n_max, tau=float("-inf"), w=None, **over):
+def _case(name, seed, B, n_max, tau=float("-inf"), w=None, w_gpu=None, **over):
+    """w: the oracle's weights (rounded to float32, the boundary's type); w_gpu:
+    the device's own weights when they come from a device computation."""
     cfg = make_config(name, **over)
     inp = gen_round(cfg, seed, with_model=False)
     rd = inp["rounds"][0]
@@ -45,7 +47,7 @@ def _case(name, seed, B, n_max, tau=float("-inf"), w=None, **over):
     if w is None:
         w = rng.normal(0.0, 1.0, cfg.nseq)
     w = np.asarray(w, np.float32).astype(np.float64)   # the key adds the float32 weight
-    gpu = _run(drafts, cfg.dtype, roots, w, B, n_max, tau)
+    gpu = _run(drafts, cfg.dtype, roots, w if w_gpu is None else w_gpu, B, n_max, tau)
     trees, n, gap, tmargin = sh.build_trees([drafts[s] for s in range(cfg.nseq)], cfg.dtype, roots,
                                             w, B, n_max, tau)
     report = {}
@@ -99,3 +101,55 @@ def test_unbinding_budget_equals_fixed_width():
     for k, v in out.items():
         assert np.array_equal(v.cpu().numpy().view(gpu[k].dtype) if k == "anc" else v.cpu().numpy(),
                               gpu[k]), k
+
+
+# ------------------------------------------------- entropy-keyed weights (f2)
+# paper §6 Eq. 2, App. B and B.5 Eq. 5: ln V(H) from each round's root entropy
+LAW = [(0.96, 0.63, 15), (1.226, 0.95, 15), (0.96, 1.71, 1), (2.0, 0.46, 7)]
+
+
+def _log_value_gpu(H, b0, b1, L, stride=1):
+    from tree_verified_block_amd import api
+    Ht = torch.tensor(np.asarray(H, np.float32), device="cuda")
+    n = Ht.numel() // stride
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    api.glance_entropy_log_value(Ht, b0, b1, L, out, stride=stride)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("b0,b1,L", LAW)
+def test_entropy_log_value_matches_oracle(b0, b1, L):
+    rng = np.random.default_rng(int(b1 * 100) + L)
+    H = np.concatenate([[0.0, 1e-6, b0 / b1, 6.0, 30.0, 1e4, np.nan, -1e-7],
+                        rng.uniform(0.0, 8.0, 300)]).astype(np.float32)
+    got = _log_value_gpu(H, b0, b1, L).cpu().numpy().astype(np.float64)
+    want = sh.log_value(H.astype(np.float64), b0, b1, L)
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isfinite(got), fin)
+    assert np.all(got[~fin] == want[~fin])
+    err = np.abs(got[fin] - want[fin]) / np.maximum(1.0, np.abs(want[fin]))
+    assert err.max() <= 1e-5, err.max()
+    # strided input: every n_rows-th entry (row 0 of each sequence)
+    n_rows = 64
+    Hs = np.full((len(H), n_rows), 99.0, np.float32)
+    Hs[:, 0] = H
+    got_s = _log_value_gpu(Hs.reshape(-1), b0, b1, L, stride=n_rows).cpu().numpy()
+    assert np.array_equal(got_s, got.astype(np.float32), equal_nan=True)
+
+
+@pytest.mark.parametrize("name,seed,B,n_max,over", [
+    ("mini_bf16", 11, 120, 63, dict(nseq=6, draft="mixed")),
+    ("qwen8b_ragged8", 12, 248, 63, {}),
+])
+def test_entropy_keyed_shared_budget(name, seed, B, n_max, over):
+    """Root entropies over the pages' span (0.1-6 nats) -> ln V on the device ->
+    the shared build, against the oracle's ln V and allocation."""
+    b0, b1, L = 0.96, 0.63, 15
+    nseq = make_config(name, **over).nseq
+    H = np.random.default_rng(seed).uniform(0.1, 6.0, nseq).astype(np.float32)
+    lw_gpu = _log_value_gpu(H, b0, b1, L)
+    lw = sh.log_value(H.astype(np.float64), b0, b1, L)
+    gpu, n, cfg, *_ = _case(name, seed, B, n_max, w=lw, w_gpu=lw_gpu, **over)
+    # the intermediate-entropy rounds get the width: V peaks at intermediate H
+    assert int(np.argmax(lw)) == int(np.argmax(lw_gpu.cpu().numpy()))

@@ -109,3 +109,62 @@ def test_equal_keys_go_to_the_lower_round():
     logq = _random_logqs(rng, 1, 3, 4)[0]
     n, _, _ = sh.allocate([logq, logq.copy()], np.zeros(2), 5, 10)
     assert n.tolist() == [3, 2]
+
+
+# --------------------------------------------------------------- entropy keying
+# ln V(H) of the entropy law (paper §6 Eq. 2, App. B and B.5 Eq. 5), pinned to
+# closed forms that a dropped term, a sign or a wrong horizon breaks.
+
+def test_log_value_at_half_match_probability():
+    # H = b0 / b1 gives p_m = 1/2: E[a|H] = 1 - 2^-L, V = (1 - 2^-L) / 2
+    b0, b1 = 0.96, 0.63
+    for L in (1, 2, 15):
+        got = sh.log_value(b0 / b1, b0, b1, L)
+        assert got == pytest.approx(np.log((1 - 2.0 ** -L) / 2), abs=1e-13)
+
+
+def test_log_value_one_offset_and_infinite_horizon():
+    rng = np.random.default_rng(3)
+    b0, b1 = 1.226, 0.95
+    H = rng.uniform(0.0, 8.0, 50)
+    x = b0 - b1 * H
+    # L = 1: V = p (1 - p) = sigma(x) sigma(-x)
+    want1 = -np.logaddexp(0.0, -x) - np.logaddexp(0.0, x)
+    assert np.allclose(sh.log_value(H, b0, b1, 1), want1, atol=1e-12)
+    # long horizon: E[a|H] -> p / (1 - p), so V -> p = sigma(x)
+    want_inf = -np.logaddexp(0.0, -x)
+    assert np.allclose(sh.log_value(H, b0, b1, 400), want_inf, atol=1e-9)
+
+
+def test_log_value_peaks_at_intermediate_entropy():
+    # Prop. 4: small when acceptance is hopeless (large H) or already deep
+    # (H -> 0, with a horizon long enough that 1 - p_m dominates), largest in
+    # between; the truncated value p (1 - p^L) peaks where p = (L + 1)^(-1/L)
+    b0, b1, L = 6.0, 1.0, 15
+    H = np.linspace(0.0, 12.0, 4801)
+    v = sh.log_value(H, b0, b1, L)
+    i = int(np.argmax(v))
+    assert 0 < i < len(H) - 1
+    p_star = (L + 1.0) ** (-1.0 / L)
+    H_star = (b0 - np.log(p_star / (1 - p_star))) / b1
+    assert abs(H[i] - H_star) < 2 * (H[1] - H[0])
+    assert np.all(np.diff(v[:i]) >= 0) and np.all(np.diff(v[i:]) <= 0)
+    # large H: ln V ~ ln p ~ b0 - b1 H
+    assert sh.log_value(40.0, b0, b1, L) == pytest.approx(b0 - b1 * 40.0, abs=1e-9)
+
+
+def test_log_value_special_inputs():
+    assert sh.log_value(np.nan, 0.96, 0.63, 15) == -np.inf
+    assert np.isfinite(sh.log_value(0.0, 0.96, 0.63, 15))
+    # a huge entropy: p itself would underflow, ln V still follows b0 - b1 H
+    assert sh.log_value(1e4, 0.96, 0.63, 15) == pytest.approx(0.96 - 0.63e4, abs=1e-9)
+
+
+def test_log_value_matches_the_plain_product_where_it_is_representable():
+    # the log-domain steps equal ln( (sum_l p^l) (1 - p) ) computed directly
+    rng = np.random.default_rng(9)
+    b0, b1, L = 0.96, 0.63, 15
+    H = rng.uniform(0.0, 20.0, 200)
+    p = 1.0 / (1.0 + np.exp(-(b0 - b1 * H)))
+    plain = np.log(sum(p ** l for l in range(1, L + 1)) * (1.0 - p))
+    assert np.allclose(sh.log_value(H, b0, b1, L), plain, rtol=1e-12, atol=1e-12)

@@ -42,6 +42,7 @@ SIGNATURES = {
     "glance_build_tree": (_I, [_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "glance_build_tree_ws": (_SZ, [_I, _I, _I, _I]),
     "glance_build_tree_flag_offset": (_SZ, [_I, _I, _I, _I]),
+    "glance_entropy_log_value": (_I, [_P, _I, _I, _F, _F, _I, _P, _P]),
     "glance_build_tree_shared": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P,
                                       _P, _P, _SZ, _P]),
     "glance_tree_attn": (_I, [ctypes.POINTER(GlanceAttnLayer), _I, _P, _P, _P, _P, _P, _I64,

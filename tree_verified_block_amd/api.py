@@ -87,6 +87,15 @@ def glance_build_tree_shared(draft_logits, root_token, log_weight, n_max, budget
     return out
 
 
+def glance_entropy_log_value(entropy, b0: float, b1: float, L: int, log_weight, nseq=None,
+                             stride: int = 1, stream=None):
+    """ln V(H) of the entropy law for each round's root entropy (float32 device
+    tensors; H_s = entropy.flatten()[s * stride])."""
+    n = log_weight.numel() if nseq is None else nseq
+    _lib.call("glance_entropy_log_value", _ptr(entropy), n, stride, float(b0), float(b1), int(L),
+              _ptr(log_weight), _stream(stream))
+
+
 # ---------------------------------------------------------------------- step 3
 def tree_attn_ws_bytes(nseq, n_rows, max_prefix, d_model, Hq, Hkv, D) -> int:
     return _lib.load().glance_tree_attn_ws(nseq, n_rows, max_prefix, d_model, Hq, Hkv, D)

@@ -221,6 +221,22 @@ glance_status glance_build_tree_shared(const void* draft_logits, int32_t dtype,
                            budget, min_log_value);
 }
 
+glance_status glance_entropy_log_value(const float* entropy, int32_t nseq, int32_t stride, float b0,
+                                       float b1, int32_t L, float* log_weight, void* stream) {
+  g_last_error.clear();
+  REQUIRE(nseq >= 1, "nseq = %d < 1", nseq);
+  REQUIRE(stride >= 1, "stride = %d < 1", stride);
+  REQUIRE(L >= 1, "L = %d < 1", L);
+  REQUIRE(std::isfinite(b0) && std::isfinite(b1), "b0 = %g, b1 = %g are not both finite",
+          static_cast<double>(b0), static_cast<double>(b1));
+  REQUIRE(entropy != nullptr, "entropy is NULL");
+  REQUIRE(log_weight != nullptr, "log_weight is NULL");
+  if ((reinterpret_cast<uintptr_t>(entropy) & 3u) || (reinterpret_cast<uintptr_t>(log_weight) & 3u))
+    return fail(GLANCE_ERR_ALIGNMENT, "entropy and log_weight must be 4-byte aligned");
+  return launch_entropy_log_value(entropy, nseq, stride, b0, b1, L, log_weight,
+                                  static_cast<hipStream_t>(stream));
+}
+
 // ------------------------------------------------------------------- step 3
 size_t glance_tree_attn_ws(int32_t nseq, int32_t n_rows, int64_t max_prefix, int32_t d_model,
                            int32_t Hq, int32_t Hkv, int32_t D) {

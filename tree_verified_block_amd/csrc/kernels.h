@@ -82,6 +82,9 @@ struct GemmArgs {
   float* kpart;
   unsigned* kcnt;
 };
+// ln V(H) of the entropy law for nseq entropies H[s * stride].
+glance_status launch_entropy_log_value(const float* H, int nseq, int stride, float b0, float b1,
+                                       int L, float* out, hipStream_t st);
 // Number of per-row partial records the bf16 LM-head GEMM leaves (the merge input).
 int gemm_bf16_head_parts(int N);
 // The head's scratch for callers that cannot allocate: a fixed device array of

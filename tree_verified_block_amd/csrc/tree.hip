@@ -871,6 +871,27 @@ __global__ __launch_bounds__(kChunkThreads) void tree_kernel(
 
 }  // namespace
 
+// ln V(H) of each sequence's root entropy under the entropy law: the match
+// probability p = sigma(b0 - b1 H) (paper §6, Eq. 2), the expected accepted
+// length truncated at the horizon, sum_{l<=L} p^l = p (1 - p^L) / (1 - p) (App.
+// B), and the value V = E[a|H] (1 - p) = p (1 - p^L) (App. B.5, Eq. 5), taken
+// in the log domain as ln p + ln(1 - p^L) with ln p = -softplus(-x) and
+// 1 - p^L = -expm1(L ln p), both without cancellation.  NaN entropy: -inf.
+__global__ __launch_bounds__(256) void entropy_log_value_kernel(const float* __restrict__ H, int nseq,
+                                                                int stride, float b0, float b1, int L,
+                                                                float* __restrict__ out) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s >= nseq) return;
+  const float h = H[static_cast<size_t>(s) * stride];
+  if (h != h) {
+    out[s] = -INFINITY;
+    return;
+  }
+  const float x = b0 - b1 * h;
+  const float lnp = -(fmaxf(-x, 0.f) + log1pf(expf(-fabsf(x))));
+  out[s] = lnp + logf(-expm1f(static_cast<float>(L) * lnp));
+}
+
 // Host side -------------------------------------------------------------------
 namespace {
 struct TreeBufs {
@@ -968,6 +989,13 @@ glance_status launch_build_tree(const void* logits, int dtype, const int32_t* ro
   else
     launch_tree<float>(nv, ga, static_cast<const float*>(logits), L, V, N, nch, b, root, parent, depth,
                        token, anc, score, n_valid, sh, st);
+  GLANCE_LAUNCH_CHECK();
+  return GLANCE_OK;
+}
+
+glance_status launch_entropy_log_value(const float* H, int nseq, int stride, float b0, float b1,
+                                       int L, float* out, hipStream_t st) {
+  entropy_log_value_kernel<<<(nseq + 255) / 256, 256, 0, st>>>(H, nseq, stride, b0, b1, L, out);
   GLANCE_LAUNCH_CHECK();
   return GLANCE_OK;
 }
