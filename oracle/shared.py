@@ -41,7 +41,8 @@ def log_expected_accept(H, b0: float, b1: float, L: int):
     at the block horizon L (paper App. B, the slowly varying step; project page,
     the same sum in closed form)."""
     lnp, _ = log_match_probability(H, b0, b1)
-    return np.logaddexp.reduce(np.stack([l * lnp for l in range(1, L + 1)]), axis=0)
+    with np.errstate(invalid="ignore"):  # NaN entropies stay NaN
+        return np.logaddexp.reduce(np.stack([l * lnp for l in range(1, L + 1)]), axis=0)
 
 
 def log_value(H, b0: float, b1: float, L: int):
