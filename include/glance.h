@@ -408,7 +408,7 @@ glance_status glance_verify_head_packed_noalloc(const void* h, const void* w_pac
  *
  *   parent, token [nseq*n_rows], n_valid [nseq]: tree outputs
  *   argmax, gap   [nseq*n_rows]: verify-head outputs
- *   gap_flag      a round is flagged when a visited row has gap <= gap_flag
+ *   gap_flag      a round is flagged when a visited row has gap <= gap_flag (not NaN)
  *                 (near-ties, where packed and unpacked evaluation may pick
  *                 different tokens; paper Theorem 1); <= 0 disables flagging
  * Outputs: n_accept [nseq] = A(S); out_tokens [nseq][L+1] (entries 0..A-1 the

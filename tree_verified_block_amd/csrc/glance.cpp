@@ -62,6 +62,25 @@ glance_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
   return GLANCE_OK;
 }
 
+// Shape bounds that keep every size and grid computation inside 32-bit ints
+// (entry points return GLANCE_ERR_UNSUPPORTED beyond them, sizers 0).
+constexpr int32_t kMaxSeqs = 1 << 16;
+constexpr int32_t kMaxDModel = 1 << 16;
+constexpr int32_t kMaxHeads = 1024;
+constexpr int32_t kMaxInter = 1 << 20;
+constexpr int32_t kMaxHeadVocab = 1 << 24;
+constexpr int32_t kMaxHeadRows = 1 << 20;
+constexpr int64_t kMaxPrefix = (int64_t(1) << 31) - 1 - GLANCE_MAX_ROWS;
+
+bool attn_in_bounds(int nseq, int64_t max_prefix, int d_model, int Hq, int inter) {
+  return nseq <= kMaxSeqs && max_prefix <= kMaxPrefix && d_model <= kMaxDModel && Hq <= kMaxHeads &&
+         inter <= kMaxInter;
+}
+
+bool head_in_bounds(int R, int V, int d_model) {
+  return R <= kMaxHeadRows && V <= kMaxHeadVocab && d_model <= kMaxDModel;
+}
+
 // ---------------------------------------------------------------- tree_attn ws
 struct AttnWs {
   int n_split = 0;
@@ -241,7 +260,7 @@ glance_status glance_entropy_log_value(const float* entropy, int32_t nseq, int32
 size_t glance_tree_attn_ws(int32_t nseq, int32_t n_rows, int64_t max_prefix, int32_t d_model,
                            int32_t Hq, int32_t Hkv, int32_t D) {
   if (nseq < 1 || n_rows < 1 || n_rows > GLANCE_MAX_ROWS || max_prefix < 0 || Hkv < 1 ||
-      Hq < Hkv || D < 2)
+      Hq < Hkv || D < 2 || D > 128 || d_model < 1 || !attn_in_bounds(nseq, max_prefix, d_model, Hq, 0))
     return 0;
   // the larger of the two dtypes' layouts, so one size fits either
   const AttnWs a = attn_ws_layout(GLANCE_BF16, nseq, n_rows, max_prefix, d_model, Hq, Hkv, D);
@@ -267,9 +286,9 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
   REQUIRE(d_model >= 1, "d_model = %d < 1", d_model);
   REQUIRE(max_prefix >= 0, "max_prefix < 0");
   REQUIRE(embed != nullptr || h_in != nullptr, "both embed and h_in are NULL");
-  REQUIRE(n_pos >= max_prefix + n_rows, "n_pos = %d is below max_prefix + n_rows = %lld (every "
-          "row's position P + depth needs a table row)", n_pos,
-          static_cast<long long>(max_prefix + n_rows));
+  REQUIRE(max_prefix <= static_cast<int64_t>(n_pos) - n_rows,
+          "n_pos = %d is below max_prefix %lld + n_rows %d (every row's position P + depth "
+          "needs a table row)", n_pos, static_cast<long long>(max_prefix), n_rows);
   if (dtype == GLANCE_BF16) {
     if (D != 128) return fail(GLANCE_ERR_UNSUPPORTED, "bf16 tree attention needs D = 128 (got %d)", D);
     if (d_model % 256 != 0 || (Hq * D) % 256 != 0)
@@ -304,6 +323,10 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
   REQUIRE_ALIGNED_OR_NULL(attn_out);
   REQUIRE_ALIGNED_OR_NULL(tree_k);
   REQUIRE_ALIGNED_OR_NULL(tree_v);
+  if (!attn_in_bounds(nseq, max_prefix, d_model, Hq, 0))
+    return fail(GLANCE_ERR_UNSUPPORTED, "shape beyond the library's bounds (nseq <= %d, max_prefix "
+                "<= %lld, d_model <= %d, Hq <= %d)", kMaxSeqs, static_cast<long long>(kMaxPrefix),
+                kMaxDModel, kMaxHeads);
   const AttnWs w = attn_ws_layout(dtype, nseq, n_rows, max_prefix, d_model, Hq, Hkv, D);
   glance_status st = check_ws(ws, ws_bytes, w.bytes);
   if (st != GLANCE_OK) return st;
@@ -416,7 +439,8 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
 size_t glance_tree_layer_ws(int32_t nseq, int32_t n_rows, int64_t max_prefix, int32_t d_model,
                             int32_t Hq, int32_t Hkv, int32_t D, int32_t inter) {
   if (nseq < 1 || n_rows < 1 || n_rows > GLANCE_MAX_ROWS || max_prefix < 0 || Hkv < 1 ||
-      Hq < Hkv || D != 128 || inter < 256 || d_model < 256)
+      Hq < Hkv || D != 128 || inter < 256 || d_model < 256 ||
+      !attn_in_bounds(nseq, max_prefix, d_model, Hq, inter))
     return 0;
   return attn_ws_layout(GLANCE_BF16, nseq, n_rows, max_prefix, d_model, Hq, Hkv, D, inter).bytes;
 }
@@ -437,9 +461,9 @@ glance_status glance_tree_layer(const glance_full_layer* layer, const void* embe
   REQUIRE(d_model >= 1, "d_model = %d < 1", d_model);
   REQUIRE(max_prefix >= 0, "max_prefix < 0");
   REQUIRE(embed != nullptr || h_in != nullptr, "both embed and h_in are NULL");
-  REQUIRE(n_pos >= max_prefix + n_rows, "n_pos = %d is below max_prefix + n_rows = %lld (every "
-          "row's position P + depth needs a table row)", n_pos,
-          static_cast<long long>(max_prefix + n_rows));
+  REQUIRE(max_prefix <= static_cast<int64_t>(n_pos) - n_rows,
+          "n_pos = %d is below max_prefix %lld + n_rows %d (every row's position P + depth "
+          "needs a table row)", n_pos, static_cast<long long>(max_prefix), n_rows);
   REQUIRE(std::isfinite(layer->eps) && layer->eps >= 0.f, "eps = %g is not finite and >= 0",
           static_cast<double>(layer->eps));
   const int inter = layer->inter;
@@ -481,6 +505,10 @@ glance_status glance_tree_layer(const glance_full_layer* layer, const void* embe
   REQUIRE_ALIGNED_OR_NULL(attn_out);
   REQUIRE_ALIGNED_OR_NULL(tree_k);
   REQUIRE_ALIGNED_OR_NULL(tree_v);
+  if (!attn_in_bounds(nseq, max_prefix, d_model, Hq, inter))
+    return fail(GLANCE_ERR_UNSUPPORTED, "shape beyond the library's bounds (nseq <= %d, max_prefix "
+                "<= %lld, d_model <= %d, Hq <= %d, inter <= %d)", kMaxSeqs,
+                static_cast<long long>(kMaxPrefix), kMaxDModel, kMaxHeads, kMaxInter);
   const AttnWs w = attn_ws_layout(GLANCE_BF16, nseq, n_rows, max_prefix, d_model, Hq, Hkv, D, inter);
   glance_status st = check_ws(ws, ws_bytes, w.bytes);
   if (st != GLANCE_OK) return st;
@@ -619,7 +647,8 @@ glance_status glance_tree_layer(const glance_full_layer* layer, const void* embe
 }
 
 size_t glance_attn_pack_bytes(int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D) {
-  if (d_model < 256 || d_model % 256 != 0 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0 || D != 128)
+  if (d_model < 256 || d_model % 256 != 0 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0 || D != 128 ||
+      d_model > kMaxDModel || Hq > kMaxHeads)
     return 0;
   const int qd = Hq * D, kd = Hkv * D;
   if (qd % 256 != 0) return 0;
@@ -667,7 +696,9 @@ glance_status glance_attn_pack(const void* wq, const void* wk, const void* wv, c
 }
 
 size_t glance_mlp_pack_bytes(int32_t d_model, int32_t inter) {
-  if (d_model < 256 || d_model % 256 != 0 || inter < 256 || inter % 256 != 0) return 0;
+  if (d_model < 256 || d_model % 256 != 0 || inter < 256 || inter % 256 != 0 ||
+      d_model > kMaxDModel || inter > kMaxInter)
+    return 0;
   return round256(proj_pack_bytes(2 * inter, d_model)) + proj_pack_bytes(d_model, inter);
 }
 
@@ -705,8 +736,7 @@ glance_status glance_mlp_pack(const void* w_gate, const void* w_up, const void* 
 
 // ------------------------------------------------------------------- step 4
 size_t glance_verify_head_ws(int32_t R, int32_t V, int32_t d_model, int32_t dtype) {
-  (void)d_model;
-  if (R < 1 || V < 2) return 0;
+  if (R < 1 || V < 2 || !head_in_bounds(R, V, d_model)) return 0;
   // bf16: 5 floats of statistics and 3 of the sampled draw per row and partial
   if (dtype == GLANCE_BF16)
     return round256(static_cast<size_t>(R) * gemm_bf16_head_parts(V) * 8 * sizeof(float));
@@ -724,6 +754,9 @@ static glance_status verify_head(const void* h, const void* w_head, const void* 
   REQUIRE(d_model >= 1, "d_model = %d < 1", d_model);
   if (dtype == GLANCE_BF16 && d_model % 256 != 0)
     return fail(GLANCE_ERR_UNSUPPORTED, "bf16 head needs d_model %% 256 == 0 (got %d)", d_model);
+  if (!head_in_bounds(R, V, d_model))
+    return fail(GLANCE_ERR_UNSUPPORTED, "head beyond the library's bounds (R <= %d, V <= %d, "
+                "d_model <= %d)", kMaxHeadRows, kMaxHeadVocab, kMaxDModel);
   REQUIRE_PTR(h);
   if (w_packed)
     REQUIRE_PTR(w_packed);
@@ -803,7 +836,7 @@ glance_status glance_verify_head_sampled(const void* h, const void* w_head, int3
 }
 
 size_t glance_head_pack_bytes(int32_t V, int32_t d_model) {
-  if (V < 2 || d_model < 256 || d_model % 256 != 0) return 0;
+  if (V < 2 || d_model < 256 || d_model % 256 != 0 || !head_in_bounds(1, V, d_model)) return 0;
   return head_pack_bytes(V, d_model);
 }
 
@@ -811,8 +844,9 @@ glance_status glance_head_pack(const void* w_head, int32_t V, int32_t d_model, v
                                void* stream) {
   g_last_error.clear();
   REQUIRE(V >= 2, "V = %d < 2", V);
-  if (d_model < 256 || d_model % 256 != 0)
-    return fail(GLANCE_ERR_UNSUPPORTED, "packed head needs d_model %% 256 == 0 (got %d)", d_model);
+  if (d_model < 256 || d_model % 256 != 0 || !head_in_bounds(1, V, d_model))
+    return fail(GLANCE_ERR_UNSUPPORTED, "packed head needs d_model %% 256 == 0, d_model <= %d and "
+                "V <= %d (got %d, %d)", kMaxDModel, kMaxHeadVocab, d_model, V);
   REQUIRE_PTR(w_head);
   REQUIRE_PTR(w_packed);
   return launch_head_pack(w_head, V, d_model, w_packed, static_cast<hipStream_t>(stream));
@@ -854,6 +888,9 @@ glance_status glance_verify_head_packed_noalloc(const void* h, const void* w_pac
   REQUIRE(R >= 1, "R = %d < 1", R);
   REQUIRE(V >= 2, "V = %d < 2", V);
   const size_t need = glance_verify_head_ws(R, V, d_model, GLANCE_BF16);
+  if (need == 0)
+    return fail(GLANCE_ERR_UNSUPPORTED, "head beyond the library's bounds (R <= %d, V <= %d, "
+                "d_model <= %d)", kMaxHeadRows, kMaxHeadVocab, kMaxDModel);
   if (need > kHeadScratchFloats * sizeof(float))
     return fail(GLANCE_ERR_UNSUPPORTED,
                 "R = %d rows of V = %d need %zu bytes of head scratch; the fixed array holds %zu",
@@ -877,6 +914,7 @@ glance_status glance_accept_walk(const int32_t* parent, const int32_t* token,
   REQUIRE(n_rows >= 1 && n_rows <= GLANCE_MAX_ROWS, "n_rows = %d outside [1, %d]", n_rows,
           GLANCE_MAX_ROWS);
   REQUIRE(L >= 1 && L <= GLANCE_MAX_L, "L = %d outside [1, %d]", L, GLANCE_MAX_L);
+  REQUIRE(!std::isnan(gap_flag), "gap_flag is NaN");
   REQUIRE_PTR(parent);
   REQUIRE_PTR(token);
   REQUIRE_PTR(n_valid);
