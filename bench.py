@@ -261,8 +261,8 @@ def chain_measure(inp, cfg, drafts, K: int, warm: int = 5, packed: bool = False)
 def sampled_measure(inp, cfg, drafts, K: int, T: float = 1.0, warm: int = 5,
                     packed: bool = False) -> dict:
     """Verify rounds that also draw one token per row at temperature T and walk
-    on the draws (a new Philox round id per round); HIP events bracket the LM
-    head of every fourth round."""
+    on the draws (a new Philox round id per round; steps 4-5 in one call); HIP
+    events bracket the LM head of every fourth round (then called on its own)."""
     import torch
     from tree_verified_block_amd.round import DeviceRound
     dev = DeviceRound(inp, device="cuda", temperature=T, seed=1234, packed_head=packed)
@@ -274,11 +274,12 @@ def sampled_measure(inp, cfg, drafts, K: int, T: float = 1.0, warm: int = 5,
         dev.round_id = i
         dev.step_tree()
         dev.step_attn()
-        if ev:
-            ev[0].record(stream)
+        if ev is None:
+            dev.step_verify()
+            return
+        ev[0].record(stream)
         dev.step_head()
-        if ev:
-            ev[1].record(stream)
+        ev[1].record(stream)
         dev.step_walk()
 
     for i in range(warm):
@@ -404,6 +405,25 @@ def full_layer_measure(K: int, seed: int = 2000, deep: int = 36) -> dict:
     return res
 
 
+def run_legs(args, model_inp) -> dict:
+    """The other workloads (``--legs``), the 8B ones reusing model_inp's weights."""
+    K = args.leg_rounds
+    want = set(args.legs.split(","))
+    legs = {}
+    for key, name, seed, kw in (
+            ("tiny_f32", "tiny", 1000, {}),
+            ("copy_regime", "qwen8b_copy", 3000, dict(model=model_inp)),
+            ("ragged8", "qwen8b_ragged8", 4, dict(model=model_inp, head_peak=True)),
+            ("deep36", "qwen8b_deep36", 4000, dict(model=model_inp, layer_copies=36))):
+        if key not in want:
+            continue
+        k = max(5, K // 5) if key == "deep36" else K
+        legs[key] = config_leg(name, k, seed, **kw)
+        print(f"[bench] leg {key}: {legs[key]['us_per_round']} us per round", file=sys.stderr,
+              flush=True)
+    return legs
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -432,6 +452,8 @@ def main():
                          "ragged batch of 8; the 36-layer stack takes a fifth); 0 skips them")
     ap.add_argument("--dist-rounds", type=int, default=200,
                     help="rounds timed one by one for the per-round distribution")
+    ap.add_argument("--legs", default="tiny_f32,copy_regime,ragged8,deep36",
+                    help="which other workloads to run (comma-separated)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
@@ -444,6 +466,9 @@ def main():
             out["shared_budget"] = shared_measure(args.shared_calls, oracle=not args.no_cpu_baseline)
         if args.full_rounds > 0:
             out["full_layer"] = full_layer_measure(args.full_rounds)
+        if args.leg_rounds > 0 and args.legs:
+            from synth import gen_round, make_config
+            out["configs"] = run_legs(args, gen_round(make_config(args.config), args.seed))
         print(json.dumps(out), flush=True)
         return
     from synth import gen_round, make_config
@@ -464,6 +489,12 @@ def main():
     def one_step(i, ev=None, head_ev=None):
         if drafts:
             dev.draft = drafts[i % len(drafts)]
+        if ev is None and head_ev is None:
+            # the production round: steps 4-5 in one call (the head's last row walks)
+            dev.step_tree()
+            dev.step_attn()
+            dev.step_verify()
+            return
         if ev:
             ev[0].record(stream)
         dev.step_tree()
@@ -487,15 +518,6 @@ def main():
         one_step(i)
     torch.cuda.synchronize()
 
-    # timed region: exactly K whole rounds launched call by call on one stream,
-    # a synchronisation on both sides and nothing else in between
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        one_step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
     # the LM-head call's live duration (HIP events on the launch stream around it,
     # in K further rounds; the dominant kernel's roofline is taken from these)
     hev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
@@ -511,7 +533,18 @@ def main():
     for i in range(nd):
         one_step(i, evs[i])
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
+    # steps 4-5 as the timed rounds run them (one fused call)
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nd)]
+    for i in range(nd):
+        if drafts:
+            dev.draft = drafts[i % len(drafts)]
+        dev.step_tree()
+        dev.step_attn()
+        fev[i][0].record(stream)
+        dev.step_verify()
+        fev[i][1].record(stream)
+    torch.cuda.synchronize()
+    fused_us = float(np.mean([e[0].elapsed_time(e[1]) for e in fev]) * 1e3)
     rev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.dist_rounds)]
     for i, e in enumerate(rev):
         e[0].record(stream)
@@ -519,6 +552,16 @@ def main():
         e[1].record(stream)
     torch.cuda.synchronize()
     rus = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in rev]) if rev else None
+
+    # timed region: exactly K whole rounds launched call by call on one stream,
+    # a synchronisation on both sides and nothing else in between (it runs after
+    # the untimed measurement passes above, so the GPU has left its idle state)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
 
     # the same rounds replayed from HIP graphs (one graph per draft)
     gr = graph_replays(dev, drafts, args.steps, warm=args.warmup, dist=args.dist_rounds)
@@ -532,6 +575,10 @@ def main():
     per_kernel = {n: {"us": round(us[n], 2), "bytes": nbytes[n],
                       "hbm_frac": round(nbytes[n] / (us[n] * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)}
                   for n in names}
+    vb = nbytes["verify_head"] + nbytes["accept_walk"]
+    per_kernel["verify_head+accept_walk (fused, as timed)"] = {
+        "us": round(fused_us, 2), "bytes": vb,
+        "hbm_frac": round(vb / (fused_us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)}
     total_bytes = sum(nbytes.values())
     ms = wall / args.steps * 1e3
     head_gbs = nbytes["verify_head"] / (head_us * 1e-6) / 1e9
@@ -549,7 +596,8 @@ def main():
                    f"N {cfg.N}, prefix {P}, nseq {cfg.nseq}", "seed": args.seed,
                    "head_weights": "packed tile order" if packed else "row-major",
                    "timing": f"{args.steps} rounds launched call by call on one stream, "
-                             f"drafts cycling over {len(drafts)}"},
+                             f"drafts cycling over {len(drafts)}, timed after the warm-up and "
+                             "the untimed per-step, head and per-round passes"},
         "per_round_us": dist,
         "graph": dict(gr, note="the same rounds replayed from HIP graphs, one per draft"),
         "round_hbm_frac": round(total_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
@@ -571,19 +619,8 @@ def main():
         out["shared_budget"] = shared_measure(args.shared_calls, oracle=not args.no_cpu_baseline)
     if args.full_rounds > 0:
         out["full_layer"] = full_layer_measure(args.full_rounds)
-    if args.leg_rounds > 0 and cfg.name == "qwen8b_1layer":
-        K = args.leg_rounds
-        legs = {}
-        for key, name, seed, kw in (
-                ("tiny_f32", "tiny", 1000, {}),
-                ("copy_regime", "qwen8b_copy", 3000, dict(model=inp)),
-                ("ragged8", "qwen8b_ragged8", 4, dict(model=inp, head_peak=True)),
-                ("deep36", "qwen8b_deep36", 4000, dict(model=inp, layer_copies=36))):
-            k = max(5, K // 5) if key == "deep36" else K
-            legs[key] = config_leg(name, k, seed, **kw)
-            print(f"[bench] leg {key}: {legs[key]['us_per_round']} us per round", file=sys.stderr,
-                  flush=True)
-        out["configs"] = legs
+    if args.leg_rounds > 0 and args.legs and cfg.name == "qwen8b_1layer":
+        out["configs"] = run_legs(args, inp)
     # plain device copy of 1 GiB (read + write bytes over the event-timed copy):
     # what this machine's HBM sustains outside the path's kernels
     a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

@@ -378,6 +378,36 @@ glance_status glance_verify_head_packed(const void* h, const void* w_packed, int
                                         int32_t* sample_tok, float* sample_gap, float* logits,
                                         void* ws, size_t ws_bytes, void* stream);
 
+/* glance_verify_head_walk: glance_verify_head_packed followed by
+ * glance_accept_walk in the same launches: the head's last row to finish runs
+ * the walk of every round (greedy: over argmax and gap; sampling: over
+ * sample_tok and sample_gap), so the round needs no separate walk launch.
+ * Results equal the two calls made in turn.  `walk` gives the walk's inputs and
+ * outputs as glance_accept_walk takes them; R must be walk->nseq *
+ * walk->n_rows.  The workspace (glance_verify_head_ws, zero-filled once) holds
+ * the arrival word, which every call returns to zero; calls that overlap on
+ * one workspace race. */
+typedef struct {
+  const int32_t* parent;   /* [nseq*n_rows] tree outputs */
+  const int32_t* token;
+  const int32_t* n_valid;  /* [nseq] */
+  int32_t nseq;
+  int32_t n_rows;
+  int32_t L;
+  float gap_flag;          /* as glance_accept_walk (not NaN) */
+  int32_t* n_accept;       /* [nseq] */
+  int32_t* out_tokens;     /* [nseq][L+1] */
+  int32_t* path_rows;      /* [nseq][L+1] */
+  int32_t* flagged;        /* [nseq] */
+} glance_walk;
+
+glance_status glance_verify_head_walk(const void* h, const void* w_packed, int32_t R,
+                                      int32_t d_model, int32_t V, float temperature, uint64_t seed,
+                                      uint64_t round_id, int32_t* argmax, float* top1, float* gap,
+                                      float* entropy, int32_t* sample_tok, float* sample_gap,
+                                      float* logits, const glance_walk* walk, void* ws,
+                                      size_t ws_bytes, void* stream);
+
 /* glance_verify_head_packed_noalloc: glance_verify_head_packed without a
  * workspace argument, for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid

@@ -169,3 +169,34 @@ def test_packed_round_equals_row_major(name, seed, kw):
     ref, got = outs
     for k in ref:
         assert np.array_equal(ref[k], got[k]), k
+
+
+@pytest.mark.parametrize("name,seed,kw,T", [
+    ("mini_bf16_ragged", 9, dict(nseq=3), None),
+    ("mini_bf16_ragged", 10, dict(nseq=3), 0.7),
+    ("qwen8b_ragged8", 5001, {}, None),
+])
+def test_fused_walk_equals_head_then_walk(name, seed, kw, T):
+    """glance_verify_head_walk (the head's last row to finish walks every round)
+    returns what glance_verify_head_packed followed by glance_accept_walk returns,
+    greedy and sampled, over several sequences, call after call (the arrival word
+    returns to zero)."""
+    from synth import gen_round, make_config
+    from tree_verified_block_amd.round import DeviceRound
+    inp = gen_round(make_config(name, **kw), seed)
+    dev = DeviceRound(inp, packed_head=True, temperature=T, seed=77)
+    outs = []
+    for rep in range(3):
+        dev.set_round(0)
+        dev.round_id = 5
+        dev.step_tree()
+        dev.step_attn()
+        if rep == 0:
+            dev.step_head()
+            dev.step_walk()
+        else:
+            dev.step_verify()
+        outs.append(dev.fetch())
+    for got in outs[1:]:
+        for k in outs[0]:
+            assert np.array_equal(np.asarray(got[k]), np.asarray(outs[0][k])), k

@@ -37,6 +37,12 @@ class GlanceFullLayer(ctypes.Structure):
                 ("mlp_packed", _P)]
 
 
+class GlanceWalk(ctypes.Structure):
+    _fields_ = [("parent", _P), ("token", _P), ("n_valid", _P), ("nseq", _I), ("n_rows", _I),
+                ("L", _I), ("gap_flag", _F), ("n_accept", _P), ("out_tokens", _P),
+                ("path_rows", _P), ("flagged", _P)]
+
+
 # name -> (restype, argtypes), exactly the declarations of include/glance.h
 SIGNATURES = {
     "glance_build_tree": (_I, [_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -64,6 +70,8 @@ SIGNATURES = {
     "glance_attn_pack": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "glance_verify_head_packed": (_I, [_P, _P, _I, _I, _I, _F, _U64, _U64, _P, _P, _P, _P, _P, _P,
                                        _P, _P, _SZ, _P]),
+    "glance_verify_head_walk": (_I, [_P, _P, _I, _I, _I, _F, _U64, _U64, _P, _P, _P, _P, _P, _P,
+                                     _P, ctypes.POINTER(GlanceWalk), _P, _SZ, _P]),
     "glance_verify_head_packed_noalloc": (_I, [_P, _P, _I, _I, _I, _F, _U64, _U64, _P, _P, _P, _P,
                                                _P, _P, _P, _P]),
     "glance_accept_walk": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P]),

@@ -8,7 +8,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import GLANCE_BF16, GLANCE_F32, GlanceAttnLayer, GlanceFullLayer
+from ._lib import GLANCE_BF16, GLANCE_F32, GlanceAttnLayer, GlanceFullLayer, GlanceWalk
 
 
 def _ptr(t):
@@ -214,6 +214,21 @@ def glance_verify_head_packed(h, w_packed, V, argmax, top1, gap, entropy, ws, lo
     _lib.call("glance_verify_head_packed", _ptr(h), _ptr(w_packed), R, d_model, V,
               float(temperature), int(seed), int(round_id), _ptr(argmax), _ptr(top1), _ptr(gap),
               _ptr(entropy), _ptr(sample_tok), _ptr(sample_gap), _ptr(logits), _ptr(ws),
+              ws.numel(), _stream(stream))
+
+
+def glance_verify_head_walk(h, w_packed, V, argmax, top1, gap, entropy, ws, parent, token, n_valid,
+                            nseq, n_rows, L, gap_flag, n_accept, out_tokens, path_rows, flagged,
+                            logits=None, temperature=1.0, seed=0, round_id=0, sample_tok=None,
+                            sample_gap=None, stream=None):
+    """The packed head and the accept walk of every round in one call (the
+    head's last row to finish walks)."""
+    R, d_model = h.shape
+    walk = GlanceWalk(_ptr(parent), _ptr(token), _ptr(n_valid), nseq, n_rows, L, float(gap_flag),
+                      _ptr(n_accept), _ptr(out_tokens), _ptr(path_rows), _ptr(flagged))
+    _lib.call("glance_verify_head_walk", _ptr(h), _ptr(w_packed), R, d_model, V, float(temperature),
+              int(seed), int(round_id), _ptr(argmax), _ptr(top1), _ptr(gap), _ptr(entropy),
+              _ptr(sample_tok), _ptr(sample_gap), _ptr(logits), ctypes.byref(walk), _ptr(ws),
               ws.numel(), _stream(stream))
 
 

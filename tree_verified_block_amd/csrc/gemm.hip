@@ -29,6 +29,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "walk_impl.h"
 
 namespace glance {
 
@@ -949,12 +950,18 @@ __global__ __launch_bounds__(kGThreads * KW, (XF || DEPTH > 7 || KW > 1) ? 1 : 2
   proj_store<EPI>(a, b, gm, x, ein);
 }
 
+// WALK: the row outputs are published with a release increment of an arrival
+// counter; the last row to arrive acquires all of them and runs the accept walk
+// of every round (the step that follows the head) in its first wave, then
+// returns the counter to zero.
+template <bool WALK>
 __global__ __launch_bounds__(256) void head_merge_kernel(const float* __restrict__ part, int nNT,
                                                          int32_t* __restrict__ argmax,
                                                          float* __restrict__ top1,
                                                          float* __restrict__ gap,
                                                          float* __restrict__ entropy,
-                                                         HeadDraw dr) {
+                                                         HeadDraw dr, WalkArgs wk,
+                                                         unsigned* __restrict__ arrivals) {
   __shared__ HeadPart red[4];
   __shared__ Draw dred[4];
   const int r = blockIdx.x, tid = threadIdx.x;
@@ -1002,6 +1009,25 @@ __global__ __launch_bounds__(256) void head_merge_kernel(const float* __restrict
       dr.tok[r] = g.tok;
       dr.gap[r] = g.m - g.m2;
     }
+  }
+  if constexpr (WALK) {
+    __shared__ int s_last;
+    if (tid == 0) {
+      // release: this thread's row outputs above; acquire: every earlier row's
+      const unsigned old = __hip_atomic_fetch_add(arrivals, 1u, __ATOMIC_ACQ_REL,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = old == gridDim.x - 1u;
+      if (last) __hip_atomic_store(arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last;
+    }
+    __syncthreads();
+    if (!s_last || tid >= kWave) return;
+    // the walking wave's own loads of the other rows' outputs come after an
+    // acquire of its own (the increment above acquired for thread 0 only)
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const int32_t* pick = dr.tok ? dr.tok : argmax;
+    const float* pgap = dr.tok ? dr.gap : gap;
+    for (int s = 0; s < wk.nseq; ++s) walk_round(wk, pick, pgap, s);
   }
 }
 
@@ -1325,7 +1351,17 @@ glance_status launch_gemm_f32(const GemmArgs& a, hipStream_t st) {
 glance_status launch_head_merge(const float* part, int n_tiles, int R, int32_t* argmax,
                                 float* top1, float* gap, float* entropy, const HeadDraw& dr,
                                 hipStream_t st) {
-  head_merge_kernel<<<R, 256, 0, st>>>(part, n_tiles, argmax, top1, gap, entropy, dr);
+  head_merge_kernel<false><<<R, 256, 0, st>>>(part, n_tiles, argmax, top1, gap, entropy, dr,
+                                              WalkArgs{}, nullptr);
+  GLANCE_LAUNCH_CHECK();
+  return GLANCE_OK;
+}
+
+glance_status launch_head_merge_walk(const float* part, int n_tiles, int R, int32_t* argmax,
+                                     float* top1, float* gap, float* entropy, const HeadDraw& dr,
+                                     const WalkArgs& wk, unsigned* arrivals, hipStream_t st) {
+  head_merge_kernel<true><<<R, 256, 0, st>>>(part, n_tiles, argmax, top1, gap, entropy, dr, wk,
+                                             arrivals);
   GLANCE_LAUNCH_CHECK();
   return GLANCE_OK;
 }

@@ -11,6 +11,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "walk_impl.h"
 
 namespace glance {
 
@@ -737,9 +738,10 @@ glance_status glance_mlp_pack(const void* w_gate, const void* w_up, const void* 
 // ------------------------------------------------------------------- step 4
 size_t glance_verify_head_ws(int32_t R, int32_t V, int32_t d_model, int32_t dtype) {
   if (R < 1 || V < 2 || !head_in_bounds(R, V, d_model)) return 0;
-  // bf16: 5 floats of statistics and 3 of the sampled draw per row and partial
+  // bf16: 5 floats of statistics and 3 of the sampled draw per row and partial,
+  // then the arrival counter of glance_verify_head_walk
   if (dtype == GLANCE_BF16)
-    return round256(static_cast<size_t>(R) * gemm_bf16_head_parts(V) * 8 * sizeof(float));
+    return round256(static_cast<size_t>(R) * gemm_bf16_head_parts(V) * 8 * sizeof(float)) + 256;
   return round256(static_cast<size_t>(R) * V * sizeof(float));
 }
 
@@ -747,7 +749,7 @@ static glance_status verify_head(const void* h, const void* w_head, const void* 
                                  int32_t dtype, int32_t R, int32_t d_model, int32_t V,
                                  int32_t* argmax, float* top1, float* gap, float* entropy,
                                  float* logits, void* ws, size_t ws_bytes, HeadDraw dr,
-                                 hipStream_t hs) {
+                                 hipStream_t hs, const WalkArgs* wk = nullptr) {
   REQUIRE(dtype == GLANCE_F32 || dtype == GLANCE_BF16, "dtype %d is not GLANCE_F32/BF16", dtype);
   REQUIRE(R >= 1, "R = %d < 1", R);
   REQUIRE(V >= 2, "V = %d < 2", V);
@@ -795,6 +797,11 @@ static glance_status verify_head(const void* h, const void* w_head, const void* 
     }
     st = launch_gemm_bf16(g, hs);
     if (st != GLANCE_OK) return st;
+    if (wk) {
+      unsigned* arrivals = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + need - 256);
+      return launch_head_merge_walk(g.part, parts, R, argmax, top1, gap, entropy, dr, *wk, arrivals,
+                                    hs);
+    }
     return launch_head_merge(g.part, parts, R, argmax, top1, gap, entropy, dr, hs);
   }
   g.logits = logits ? logits : static_cast<float*>(ws);
@@ -876,6 +883,59 @@ glance_status glance_verify_head_packed(const void* h, const void* w_packed, int
   REQUIRE(w_packed != nullptr, "w_packed is NULL");
   return verify_head(h, nullptr, w_packed, GLANCE_BF16, R, d_model, V, argmax, top1, gap, entropy,
                      logits, ws, ws_bytes, dr, static_cast<hipStream_t>(stream));
+}
+
+glance_status glance_verify_head_walk(const void* h, const void* w_packed, int32_t R,
+                                      int32_t d_model, int32_t V, float temperature, uint64_t seed,
+                                      uint64_t round_id, int32_t* argmax, float* top1, float* gap,
+                                      float* entropy, int32_t* sample_tok, float* sample_gap,
+                                      float* logits, const glance_walk* walk, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  REQUIRE(walk != nullptr, "walk is NULL");
+  REQUIRE(walk->nseq >= 1, "nseq = %d < 1", walk->nseq);
+  REQUIRE(walk->n_rows >= 1 && walk->n_rows <= GLANCE_MAX_ROWS, "n_rows = %d outside [1, %d]",
+          walk->n_rows, GLANCE_MAX_ROWS);
+  REQUIRE(static_cast<int64_t>(walk->nseq) * walk->n_rows == R,
+          "R = %d is not nseq %d x n_rows %d", R, walk->nseq, walk->n_rows);
+  REQUIRE(walk->L >= 1 && walk->L <= GLANCE_MAX_L, "L = %d outside [1, %d]", walk->L, GLANCE_MAX_L);
+  REQUIRE(!std::isnan(walk->gap_flag), "gap_flag is NaN");
+  REQUIRE_PTR(walk->parent);
+  REQUIRE_PTR(walk->token);
+  REQUIRE_PTR(walk->n_valid);
+  REQUIRE_PTR(walk->n_accept);
+  REQUIRE_PTR(walk->out_tokens);
+  REQUIRE_PTR(walk->path_rows);
+  REQUIRE_PTR(walk->flagged);
+  HeadDraw dr;
+  if (sample_tok || sample_gap) {
+    REQUIRE(std::isfinite(temperature) && temperature > 0.f,
+            "temperature = %g is not a finite positive number", static_cast<double>(temperature));
+    REQUIRE_PTR(sample_tok);
+    REQUIRE_PTR(sample_gap);
+    dr.tok = sample_tok;
+    dr.gap = sample_gap;
+    dr.inv_temp = 1.f / temperature;
+    dr.seed_lo = static_cast<uint32_t>(seed);
+    dr.seed_hi = static_cast<uint32_t>(seed >> 32);
+    dr.rnd_lo = static_cast<uint32_t>(round_id);
+    dr.rnd_hi = static_cast<uint32_t>(round_id >> 32);
+  }
+  REQUIRE(w_packed != nullptr, "w_packed is NULL");
+  WalkArgs wk;
+  wk.parent = walk->parent;
+  wk.token = walk->token;
+  wk.n_valid = walk->n_valid;
+  wk.nseq = walk->nseq;
+  wk.n_rows = walk->n_rows;
+  wk.L = walk->L;
+  wk.gap_flag = walk->gap_flag;
+  wk.n_accept = walk->n_accept;
+  wk.out_tokens = walk->out_tokens;
+  wk.path_rows = walk->path_rows;
+  wk.flagged = walk->flagged;
+  return verify_head(h, nullptr, w_packed, GLANCE_BF16, R, d_model, V, argmax, top1, gap, entropy,
+                     logits, ws, ws_bytes, dr, static_cast<hipStream_t>(stream), &wk);
 }
 
 glance_status glance_verify_head_packed_noalloc(const void* h, const void* w_packed, int32_t R,

@@ -120,6 +120,12 @@ struct HeadDraw {
 glance_status launch_head_merge(const float* part, int n_tiles, int R, int32_t* argmax,
                                 float* top1, float* gap, float* entropy, const HeadDraw& dr,
                                 hipStream_t st);
+struct WalkArgs;
+// The merge with the accept walk of every round fused behind it (the last row
+// to arrive walks); `arrivals` is a zero word the kernel returns to zero.
+glance_status launch_head_merge_walk(const float* part, int n_tiles, int R, int32_t* argmax,
+                                     float* top1, float* gap, float* entropy, const HeadDraw& dr,
+                                     const WalkArgs& wk, unsigned* arrivals, hipStream_t st);
 glance_status launch_head_rowstats_f32(const float* logits, int R, int V, int32_t* argmax,
                                        float* top1, float* gap, float* entropy,
                                        const HeadDraw& dr, hipStream_t st);

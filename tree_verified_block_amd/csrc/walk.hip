@@ -12,54 +12,15 @@
 // the next root, all on the device.
 #include "common.h"
 #include "kernels.h"
+#include "walk_impl.h"
 
 namespace glance {
 
 namespace {
 
-__global__ __launch_bounds__(kWave) void accept_walk_kernel(
-    const int32_t* __restrict__ parent, const int32_t* __restrict__ token,
-    const int32_t* __restrict__ n_valid, const int32_t* __restrict__ argmax,
-    const float* __restrict__ gap, int n_rows, int L, float gap_flag,
-    int32_t* __restrict__ n_accept, int32_t* __restrict__ out_tokens,
-    int32_t* __restrict__ path_rows, int32_t* __restrict__ flagged) {
-  const int s = blockIdx.x, lane = lane_id();
-  const size_t rb = static_cast<size_t>(s) * n_rows;
-  // every load issued at once (rows below n_rows exist whatever n_valid is); the
-  // rows past n_valid are masked afterwards
-  const int li = lane < n_rows ? lane : 0;
-  const int nv = n_valid[s];
-  const int ld_parent = parent[rb + li];
-  const int ld_token = token[rb + li];
-  const int ld_arg = argmax[rb + li];
-  const float ld_gap = gap[rb + li];
-  const bool mine = lane < nv && lane < n_rows;
-  const int my_parent = mine ? ld_parent : -2;
-  const int my_token = mine ? ld_token : -2;
-  const int my_arg = mine ? ld_arg : -1;
-  const float my_gap = mine ? ld_gap : INFINITY;
-  int r = 0, a = 0, flag = 0;
-  for (;;) {
-    const int y = __shfl(my_arg, r, kWave);
-    const float gp = __shfl(my_gap, r, kWave);
-    if (gap_flag > 0.f && gp <= gap_flag) flag = 1;
-    if (lane == 0) {
-      out_tokens[static_cast<size_t>(s) * (L + 1) + a] = y;
-      path_rows[static_cast<size_t>(s) * (L + 1) + a] = r;
-    }
-    const unsigned long long hit = __ballot(lane > 0 && my_parent == r && my_token == y);
-    if (hit == 0ull || a >= L) break;
-    r = __ffsll(static_cast<long long>(hit)) - 1;
-    ++a;
-  }
-  for (int k = a + 1 + lane; k <= L; k += kWave) {
-    out_tokens[static_cast<size_t>(s) * (L + 1) + k] = -1;
-    path_rows[static_cast<size_t>(s) * (L + 1) + k] = -1;
-  }
-  if (lane == 0) {
-    n_accept[s] = a;
-    flagged[s] = flag;
-  }
+__global__ __launch_bounds__(kWave) void accept_walk_kernel(WalkArgs w, const int32_t* __restrict__ argmax,
+                                                            const float* __restrict__ gap) {
+  walk_round(w, argmax, gap, blockIdx.x);
 }
 
 // Block k copies the K and V entries of path row k (k <= A) to cache row
@@ -118,9 +79,19 @@ glance_status launch_accept_walk(const int32_t* parent, const int32_t* token,
                                  const float* gap, int nseq, int n_rows, int L, float gap_flag,
                                  int32_t* n_accept, int32_t* out_tokens, int32_t* path_rows,
                                  int32_t* flagged, hipStream_t st) {
-  accept_walk_kernel<<<nseq, kWave, 0, st>>>(parent, token, n_valid, argmax, gap, n_rows, L,
-                                              gap_flag, n_accept, out_tokens, path_rows,
-                                              flagged);
+  WalkArgs w;
+  w.parent = parent;
+  w.token = token;
+  w.n_valid = n_valid;
+  w.nseq = nseq;
+  w.n_rows = n_rows;
+  w.L = L;
+  w.gap_flag = gap_flag;
+  w.n_accept = n_accept;
+  w.out_tokens = out_tokens;
+  w.path_rows = path_rows;
+  w.flagged = flagged;
+  accept_walk_kernel<<<nseq, kWave, 0, st>>>(w, argmax, gap);
   GLANCE_LAUNCH_CHECK();
   return GLANCE_OK;
 }

@@ -195,11 +195,28 @@ class DeviceRound:
                                self.nseq, self.n_rows, self.L, gap_flag, self.n_accept,
                                self.out_tokens, self.path_rows, self.flagged, stream)
 
+    def step_verify(self, stream=None, gap_flag=GAP_FLAG):
+        """Steps 4-5: with packed head weights one call (the head's last row to
+        finish walks), else the head and the walk in turn."""
+        if self.w_packed is None:
+            self.step_head(stream)
+            self.step_walk(stream, gap_flag)
+            return
+        kw = {}
+        if self.temperature is not None:
+            kw = dict(temperature=self.temperature, seed=self.seed, round_id=self.round_id,
+                      sample_tok=self.sample_tok, sample_gap=self.sample_gap)
+        t = self.tree
+        api.glance_verify_head_walk(self.h_final, self.w_packed, self.V, self.argmax, self.top1,
+                                    self.gap, self.entropy, self.ws_head, t["parent"], t["token"],
+                                    t["n_valid"], self.nseq, self.n_rows, self.L, gap_flag,
+                                    self.n_accept, self.out_tokens, self.path_rows, self.flagged,
+                                    logits=self.logits, stream=stream, **kw)
+
     def run(self, stream=None):
         self.step_tree(stream)
         self.step_attn(stream)
-        self.step_head(stream)
-        self.step_walk(stream)
+        self.step_verify(stream)
 
     def set_draft(self, draft_logits: np.ndarray, root: int | None = None):
         """Next round's draft logits [1][L][V] (and, optionally, its root)."""
