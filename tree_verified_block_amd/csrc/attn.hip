@@ -6,35 +6,40 @@
 // plus exactly the tree rows j that are i itself or its ancestors (bit j of
 // anc[i]), which is the causal sequence x o b o y_{1:d(i)}.
 //
-// bf16 path (head_dim 128, gfx950 MFMA v_mfma_f32_32x32x16_bf16).  A work-group
-// of four waves owns one KV head h of one round and a block of 32 of its
-// queries (query q = row * G + j, the G = Hq/Hkv query heads of h times the
-// round's rows).  The round's keys are its prefix [0, P) followed by its tree
-// rows: key P + i is tree row i, visible to a query iff bit i of the query row's
-// ancestor word is set.  The keys are cut into n_split x 4 contiguous ranges,
-// one per wave; a wave streams its range in blocks of 32 keys with an online
-// softmax:
-//   S^T = K Q^T     K goes from memory straight into the MFMA operand (lane
-//                   (j, g) holds key j, dims 64 g .. 64 g + 63 over the eight
-//                   16-deep steps); q enters as its bf16 rounding plus the bf16
-//                   remainder (two products), so the scores see q to ~16 bits.
+// bf16 path (head_dim 128, gfx950 MFMA v_mfma_f32_32x32x16_bf16).  A wave owns
+// one KV head h of one round and a block of 32 of its queries (query q = row * G
+// + j, the G = Hq/Hkv query heads of h times the round's rows).  The round's
+// keys are its prefix [0, P) followed by its tree rows: key P + i is tree row i,
+// visible to a query iff bit i of the query row's ancestor word is set.  Keys
+// are streamed in blocks of 32 with an online softmax:
+//   S^T = K Q^T     K from an LDS tile (lane (j, g) holds key j, dims 64 g ..
+//                   64 g + 63 over the eight 16-deep steps); q enters as its
+//                   bf16 rounding plus the bf16 remainder (two products), so
+//                   the scores see q to ~16 bits.
 //   P = 2^(S - m)   in fp32, then split the same way into a bf16 part and the
 //                   bf16 remainder of what it left out.
-//   O^T += V^T P^T  V is transposed through the wave's own LDS tile; P^T stays
-//                   in registers: each lane already holds, for its query, the
-//                   keys that the MFMA B operand wants from it, provided the V^T
-//                   tile stores the keys in that order (the slot permutation
-//                   below).
-// The four waves merge their (max, sum, O) in LDS.  With several splits the
-// last work-group of a query block to arrive merges the splits' records.  The
-// output o = O / sum is written in fp32; the output projection takes it as a
-// bf16 pair too, so q, P and o all enter the products with ~16 significant bits.
-// Work-group ids put the query blocks and splits of one KV head on the same XCD
-// (id mod 8 = h when Hkv = 8), so the head's K/V cross HBM once and are shared
-// through that XCD's L2.
+//   O^T += V^T P^T  V through an LDS tile stored transposed; P^T stays in
+//                   registers: each lane already holds, for its query, the keys
+//                   that the MFMA B operand wants from it, provided the V^T tile
+//                   stores the keys in that order (the slot permutation below).
+// Default kernel (tree_attn_tile_kernel): the four waves of a work-group own
+// four consecutive query blocks of one head and one key split, and share each
+// 32-key K / V^T tile, loaded once per work-group, two blocks ahead, into a
+// double-buffered LDS pair.  The number of splits fills the CUs once but keeps
+// every split at least 8 blocks long, since each split costs a 528-byte record
+// (max, sum, O) per query; attn_combine_kernel merges the records in split
+// order.  Work-group ids put the query groups and splits of one KV head on the
+// same XCD (id mod 8 = h when Hkv = 8), so the head's K/V cross HBM once and
+// are shared through that XCD's L2.  The older per-wave kernel (each wave its
+// own key range and tiles, the four waves merged in LDS) stays selectable at
+// build time.  The output o = O / sum is written in fp32; the output projection
+// takes it as a bf16 pair too, so q, P and o all enter the products with ~16
+// significant bits.
 //
 // fp32 path (tiny shapes): one work-group per (row, query head), scores in LDS,
 // plain fp32 loops.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -50,7 +55,7 @@ constexpr int kHD = 128;              // head_dim of the bf16 path
 constexpr int kVtRow = 40;            // bf16 slots per V^T row: 32 keys + 8 padding (80 bytes)
 constexpr int kObRow = kHD + 1;       // fp32 stride of the merge rows (odd: no bank conflicts)
 constexpr int kRec = kHD + 4;         // split record per query: m, l, -, -, o[128]
-constexpr int kMaxSplit = 8;
+constexpr int kMaxSplit = 16;
 
 // position P + depth of a row, clamped into the cos/sin tables
 __device__ __forceinline__ int row_pos(const AttnArgs& a, int P, int row) {
@@ -159,6 +164,7 @@ __global__ __launch_bounds__(kAThreads, 1) void tree_attn_bf16_kernel(AttnArgs a
       qlo[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qlp + 8 * ks));
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // query loads done before the K/V stream starts
   const int64_t kv0 = a.kv_offsets[s];
   const int P = prefix_len(a, s);
   const int T = P + a.n_rows;
@@ -397,6 +403,269 @@ __global__ __launch_bounds__(kAThreads, 1) void tree_attn_bf16_kernel(AttnArgs a
   }
 }
 
+// Shared-tile variant: the W waves of a work-group own W consecutive blocks of
+// 32 queries of one KV head and all keys of one key split.  Every 32-key block
+// is loaded once per work-group, cooperatively (threads below 128 take the V
+// pieces, the rest, or the same threads when W = 2, the K pieces), two blocks
+// ahead of its use, into a double-buffered pair of LDS tiles (K rows with the
+// XOR swizzle, V^T in the slot order of the P operand), and read by every wave.
+// One barrier per block.  Each wave then does the per-block work of the
+// per-wave kernel above for its own queries (S^T = K Q^T with q as a bf16 pair,
+// the lazy online softmax, P as a bf16 pair, O^T += V^T P^T) and, at the end,
+// writes its queries' split records (or, with one split, their outputs).
+template <int W>
+__global__ __launch_bounds__(W * kWave, 1) void tree_attn_tile_kernel(AttnArgs a, int nqb) {
+  constexpr int KT = kKB * kHD;        // K tile (elements)
+  constexpr int VT = kHD * kVtRow;     // V^T tile (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][KT + VT];
+
+  const int Hkv = a.Hkv;
+  int id = blockIdx.x;
+  const int h = id % Hkv;
+  id /= Hkv;
+  const int nqg = (nqb + W - 1) / W;
+  const int qg = id % nqg;
+  id /= nqg;
+  const int c = id % a.n_split;
+  const int s = id / a.n_split;
+  const int tid = threadIdx.x, l = tid & 63, j = l & 31, g = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = a.Hq / Hkv;
+  const int Qn = a.n_rows * G;
+  const int qb = qg * W + w;  // this wave's query block (past nqb: no queries, still loads)
+
+  // ---- this lane's query as bf16 + remainder (queries past Qn read row 0 and
+  // are never stored)
+  const int q = qb * kQW + j;
+  const bool qvalid = qb < nqb && q < Qn;
+  const int grow = s * a.n_rows + (qvalid ? q / G : 0);
+  const uint64_t qanc = qvalid ? a.anc[grow] : 0ull;
+  bf16x8 qhi[8], qlo[8];
+  {
+    const size_t qoff = (static_cast<size_t>(grow) * a.Hq + h * G + (qvalid ? q % G : 0)) * kHD + 64 * g;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qoff;
+    const uint16_t* qlp = static_cast<const uint16_t*>(a.q_lo) + qoff;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      qhi[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 8 * ks));
+      qlo[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qlp + 8 * ks));
+    }
+  }
+  // the query loads complete here, before any K/V load is issued: otherwise the
+  // loop's first use of q waits on every load in flight, prefetches included
+  __builtin_amdgcn_s_waitcnt(0);
+  const int64_t kv0 = a.kv_offsets[s];
+  const int P = prefix_len(a, s);
+  const int T = P + a.n_rows;
+  // this work-group's keys: split c of n_split, in whole blocks
+  const int per = ((T + a.n_split - 1) / a.n_split + kKB - 1) / kKB * kKB;
+  const int t_beg = c * per;
+  const int t_end = min(t_beg + per, T);
+  const int nblk = t_end > t_beg ? (t_end - t_beg + kKB - 1) / kKB : 0;
+
+  const int kstr = Hkv * kHD;
+  const uint16_t* kc0 = static_cast<const uint16_t*>(a.k_cache) + (kv0 * Hkv + h) * kHD;
+  const uint16_t* vc0 = static_cast<const uint16_t*>(a.v_cache) + (kv0 * Hkv + h) * kHD;
+  const size_t trow0 = (static_cast<size_t>(s) * a.n_rows * Hkv + h) * kHD;
+  const uint16_t* tk0 = static_cast<const uint16_t*>(a.tree_k) + trow0;
+  const uint16_t* tv0 = static_cast<const uint16_t*>(a.tree_v) + trow0;
+  auto row_of = [&](const uint16_t* c0, const uint16_t* t0p, int t) {
+    const bool pre = t < P;
+    const int i = (t < T && !pre) ? t - P : 0;
+    return (pre ? c0 : t0p) + (pre ? t : i) * kstr;
+  };
+  // loading roles, per 32-key block: 512 K pieces (key pi / 16, 16-byte unit
+  // pi % 16; thread lt takes pi = lt + 128 i) and 128 V pieces (dims 8 vx .. + 7
+  // of the four keys of quad kq).  With four waves, waves 0-1 load V and waves
+  // 2-3 load K (one register set each); with two, every thread loads both.
+  const bool vrole = W == 4 ? w < 2 : true;
+  const bool krole = W == 4 ? w >= 2 : true;
+  constexpr int NP = W == 4 ? 4 : 8;   // 16-byte pieces per thread and block
+  constexpr int VO = W == 4 ? 0 : 4;   // index of the first V piece
+  const int lt = tid & 127;
+  const int vx = lt & 15, kq = lt >> 4;
+  // The loads are unconditional (the role picks the address): a load under a
+  // branch would make the compiler wait for every load in flight before the
+  // tile stores.
+  auto load = [&](int t0, u32x4 (&d)[NP]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t* kp = row_of(kc0, tk0, t0 + (lt >> 4) + 8 * i) + 8 * (lt & 15);
+      const uint16_t* vp = row_of(vc0, tv0, t0 + 4 * kq + i) + 8 * vx;
+      if (W == 4) {
+        d[i] = *reinterpret_cast<const u32x4*>(krole ? kp : vp);
+      } else {
+        d[i] = *reinterpret_cast<const u32x4*>(kp);
+        d[VO + i] = *reinterpret_cast<const u32x4*>(vp);
+      }
+    }
+  };
+  // K tile: key k's row at k * 128, its 16-byte unit p at unit p ^ (k mod 8);
+  // V^T tile: dim 8 vx + e, the slot quad of key quad kq, four keys per write
+  auto store = [&](int buf, const u32x4 (&d)[NP]) {
+    uint16_t* kt = tiles[buf];
+    uint16_t* vt = tiles[buf] + KT;
+    if (krole) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = (lt >> 4) + 8 * i;
+        *reinterpret_cast<u32x4*>(kt + k * kHD + 8 * ((lt & 15) ^ (k & 7))) = d[i];
+      }
+    }
+    if (vrole) {
+      const int sq = slot_quad(kq) ^ (vx & 7);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t x0 = d[VO][e >> 1], x1 = d[VO + 1][e >> 1];
+        const uint32_t x2 = d[VO + 2][e >> 1], x3 = d[VO + 3][e >> 1];
+        *reinterpret_cast<uint2*>(vt + (8 * vx + e) * kVtRow + 4 * sq) =
+            make_uint2(pick16(x0, x1, sel), pick16(x2, x3, sel));
+      }
+    }
+  };
+
+  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(kHD));
+  f32x16 acc_o[4] = {};
+  float m_ref = -INFINITY, l_run = 0.f;
+  // blocks 0 and 1 in flight; block 0 into tile 0.  Loads past the last block
+  // re-read it (no conditional load).
+  const int tlast = t_beg + (nblk > 0 ? nblk - 1 : 0) * kKB;
+  u32x4 pf[2][NP];
+  load(t_beg, pf[0]);
+  load(min(t_beg + kKB, tlast), pf[1]);
+  store(0, pf[0]);
+  load(min(t_beg + 2 * kKB, tlast), pf[0]);
+  __syncthreads();
+  // block b of the range; cur = b mod 2 is a compile-time constant so that the
+  // register set of the block after next is named statically
+  auto block = [&](int b, auto par) {
+    constexpr int cur = decltype(par)::value;
+    const int t0 = t_beg + b * kKB;
+    const uint16_t* kt = tiles[cur];
+    const uint16_t* vt = tiles[cur] + KT;
+    // ---- S^T = K Q^T with q = hi + lo (all eight operand reads first)
+    bf16x8 kop[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      kop[ks] = *reinterpret_cast<const bf16x8*>(kt + j * kHD + 8 * ((8 * g + ks) ^ (j & 7)));
+    f32x16 sa = {}, sb = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qhi[ks], sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qlo[ks], sb, 0, 0, 0);
+    }
+    // ---- the next block's tiles into the other buffer (its reads ended at the
+    // previous barrier), then the loads of the block after it
+    if (b + 1 < nblk) store(cur ^ 1, pf[cur ^ 1]);
+    load(min(t0 + 3 * kKB, tlast), pf[cur ^ 1]);
+    // ---- mask (element v: key t0 + 8 (v / 4) + 4 g + v % 4, query j), block max
+    float sc[16], mb = -INFINITY;
+    if (t0 + kKB <= min(P, t_end)) {  // (uniform) every key of the block is a visible prefix key
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        sc[v] = (sa[v] + sb[v]) * scale_log2;
+        mb = fmaxf(mb, sc[v]);
+      }
+    } else {
+      const uint32_t vm = block_mask(t0, t_end, P, qanc) >> (4 * g);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const bool vis = (vm >> (8 * (v >> 2) + (v & 3))) & 1u;
+        sc[v] = vis ? (sa[v] + sb[v]) * scale_log2 : -INFINITY;
+        mb = fmaxf(mb, sc[v]);
+      }
+    }
+    mb = fmaxf(mb, __shfl_xor(mb, 32, kWave));
+    const bool raise = mb > m_ref + 8.f;  // also when m_ref is still -inf
+    if (__ballot(raise) != 0ull) {  // (uniform per wave) rare after the first block
+      const float m_new = raise ? mb : m_ref;
+      const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
+    }
+    const float mz = m_ref == -INFINITY ? 0.f : m_ref;
+    uint32_t ph[8], pl[8];
+#pragma unroll
+    for (int pr = 0; pr < 8; ++pr) {
+      const float p0 = __builtin_amdgcn_exp2f(sc[2 * pr] - mz);
+      const float p1 = __builtin_amdgcn_exp2f(sc[2 * pr + 1] - mz);
+      ph[pr] = pack_bf16x2(p0, p1);
+      pl[pr] = pack_bf16x2(p0 - __uint_as_float(ph[pr] << 16), p1 - __uint_as_float(ph[pr] & 0xFFFF0000u));
+      l_run += p0 + p1;
+    }
+    // ---- O^T += V^T P^T, two 16-key steps (operand reads first)
+    bf16x8 vop[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int dim = 32 * db + j;
+        const int sw = (dim >> 3) & 7;
+        const uint16_t* row = vt + dim * kVtRow;
+        const uint2 lo = *reinterpret_cast<const uint2*>(row + 4 * ((4 * t + 2 * g) ^ sw));
+        const uint2 hi = *reinterpret_cast<const uint2*>(row + 4 * ((4 * t + 2 * g + 1) ^ sw));
+        vop[t][db] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bf16x8 bh = __builtin_bit_cast(bf16x8, make_uint4(ph[4 * t], ph[4 * t + 1], ph[4 * t + 2], ph[4 * t + 3]));
+      const bf16x8 bl = __builtin_bit_cast(bf16x8, make_uint4(pl[4 * t], pl[4 * t + 1], pl[4 * t + 2], pl[4 * t + 3]));
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t][db], bh, acc_o[db], 0, 0, 0);
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t][db], bl, acc_o[db], 0, 0, 0);
+      }
+    }
+    // every wave's reads of this block end before the next iteration stores
+    // into this buffer; the stores of the next block are visible after it
+    __syncthreads();
+  };
+  // whole pairs, then the last block alone: every back edge follows an odd block
+  // (a loop with the odd block optional would make the compiler wait for the
+  // loads just issued)
+  int b = 0;
+  for (; b + 1 < nblk; b += 2) {
+    block(b, std::integral_constant<int, 0>{});
+    block(b + 1, std::integral_constant<int, 1>{});
+  }
+  if (b < nblk) block(b, std::integral_constant<int, 0>{});
+  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  if (!qvalid) return;
+  // lane (j, g) holds dims 32 db + 8 i + 4 g + u (u < 4 consecutive) of query j
+  if (a.n_split > 1) {
+    const size_t blk = (static_cast<size_t>(s) * Hkv + h) * nqb + qb;
+    float* rec = a.part + ((blk * a.n_split + c) * kQW + j) * kRec;
+    if (g == 0) *reinterpret_cast<float2*>(rec) = make_float2(m_ref, l_tot);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<float4*>(rec + 4 + 32 * db + 8 * i + 4 * g) =
+            make_float4(acc_o[db][4 * i], acc_o[db][4 * i + 1], acc_o[db][4 * i + 2], acc_o[db][4 * i + 3]);
+    return;
+  }
+  const int rr = q / G;
+  const int growq = s * a.n_rows + rr;
+  const bool live = a.token[growq] >= 0;
+  const float inv = (live && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  const size_t off = static_cast<size_t>(growq) * a.Hq * kHD + (h * G + q % G) * kHD;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 32 * db + 8 * i + 4 * g;
+      const float4 v = make_float4(acc_o[db][4 * i] * inv, acc_o[db][4 * i + 1] * inv,
+                                   acc_o[db][4 * i + 2] * inv, acc_o[db][4 * i + 3] * inv);
+      *reinterpret_cast<float4*>(a.attn_x + off + d) = v;
+      if (a.attn_out) *reinterpret_cast<float4*>(a.attn_out + off + d) = v;
+    }
+}
+
 // Merge of the split records of every (row, query head): one work-group per row
 // and query head, one thread per head dimension, splits in order.
 __global__ __launch_bounds__(kHD) void attn_combine_kernel(AttnArgs a, int nqb) {
@@ -545,13 +814,36 @@ __global__ __launch_bounds__(128) void tree_attn_f32_kernel(AttnArgs a) {
 
 static int attn_qblocks(int n_rows, int Hq, int Hkv) { return (n_rows * (Hq / Hkv) + kQW - 1) / kQW; }
 
+// Waves per work-group of the shared-tile kernel (0: the per-wave kernel).
+#ifndef GLANCE_ATTN_TILE
+#define GLANCE_ATTN_TILE 4
+#endif
+// Split policy: enough work-groups to fill the CUs once, but no split shorter
+// than GLANCE_ATTN_MINBLK blocks of 32 keys (each split adds a 528-byte record
+// per query and KV head).
+#ifndef GLANCE_ATTN_FILL
+#define GLANCE_ATTN_FILL 256
+#endif
+#ifndef GLANCE_ATTN_MINBLK
+#define GLANCE_ATTN_MINBLK 8
+#endif
+
 int attn_splits(int nseq, int64_t max_prefix, int n_rows, int Hq, int Hkv) {
-  // enough work-groups to fill the CUs once, and a split per 2048 keys of the
-  // longest round (about 16 blocks per wave)
-  const int64_t base = static_cast<int64_t>(nseq) * Hkv * attn_qblocks(n_rows, Hq, Hkv);
-  const int64_t fill = (256 + base - 1) / base;
-  const int64_t len = (max_prefix + n_rows + 2047) / 2048;
-  int64_t n = fill > len ? fill : len;
+  const int nqb = attn_qblocks(n_rows, Hq, Hkv);
+  if (GLANCE_ATTN_TILE == 0) {
+    // per-wave kernel: fill the CUs once, and a split per 2048 keys
+    const int64_t base = static_cast<int64_t>(nseq) * Hkv * nqb;
+    const int64_t fill = (256 + base - 1) / base;
+    const int64_t len = (max_prefix + n_rows + 2047) / 2048;
+    int64_t n = fill > len ? fill : len;
+    if (n < 1) n = 1;
+    if (n > 8) n = 8;
+    return static_cast<int>(n);
+  }
+  const int64_t base = static_cast<int64_t>(nseq) * Hkv * ((nqb + GLANCE_ATTN_TILE - 1) / GLANCE_ATTN_TILE);
+  const int64_t fill = (GLANCE_ATTN_FILL + base - 1) / base;
+  const int64_t len = (max_prefix + n_rows) / (kKB * GLANCE_ATTN_MINBLK);
+  int64_t n = fill < len ? fill : len;
   if (n < 1) n = 1;
   if (n > kMaxSplit) n = kMaxSplit;
   return static_cast<int>(n);
@@ -565,8 +857,14 @@ size_t attn_part_floats(int nseq, int n_rows, int Hq, int Hkv, int n_split) {
 glance_status launch_tree_attention(const AttnArgs& a, hipStream_t st) {
   if (a.dtype == GLANCE_BF16) {
     const int nqb = attn_qblocks(a.n_rows, a.Hq, a.Hkv);
-    const int grid = a.nseq * a.n_split * nqb * a.Hkv;
-    tree_attn_bf16_kernel<<<grid, kAThreads, 0, st>>>(a, nqb);
+    if (GLANCE_ATTN_TILE == 0) {
+      const int grid = a.nseq * a.n_split * nqb * a.Hkv;
+      tree_attn_bf16_kernel<<<grid, kAThreads, 0, st>>>(a, nqb);
+    } else {
+      constexpr int W = GLANCE_ATTN_TILE == 0 ? 4 : GLANCE_ATTN_TILE;
+      const int grid = a.nseq * a.n_split * ((nqb + W - 1) / W) * a.Hkv;
+      tree_attn_tile_kernel<W><<<grid, W * kWave, 0, st>>>(a, nqb);
+    }
     GLANCE_LAUNCH_CHECK();
     if (a.n_split > 1) {
       attn_combine_kernel<<<dim3(a.nseq * a.n_rows, a.Hq), kHD, 0, st>>>(a, nqb);
