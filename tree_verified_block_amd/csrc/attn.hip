@@ -814,9 +814,9 @@ __global__ __launch_bounds__(128) void tree_attn_f32_kernel(AttnArgs a) {
 
 static int attn_qblocks(int n_rows, int Hq, int Hkv) { return (n_rows * (Hq / Hkv) + kQW - 1) / kQW; }
 
-// Waves per work-group of the shared-tile kernel (0: the per-wave kernel).
+// Shared-tile kernel (the default) or the per-wave kernel (GLANCE_ATTN_TILE=0).
 #ifndef GLANCE_ATTN_TILE
-#define GLANCE_ATTN_TILE 4
+#define GLANCE_ATTN_TILE 1
 #endif
 // Split policy: enough work-groups to fill the CUs once, but no split shorter
 // than GLANCE_ATTN_MINBLK blocks of 32 keys (each split adds a 528-byte record
@@ -825,10 +825,29 @@ static int attn_qblocks(int n_rows, int Hq, int Hkv) { return (n_rows * (Hq / Hk
 #define GLANCE_ATTN_FILL 256
 #endif
 #ifndef GLANCE_ATTN_MINBLK
-#define GLANCE_ATTN_MINBLK 8
+#define GLANCE_ATTN_MINBLK 4
 #endif
 
-int attn_splits(int nseq, int64_t max_prefix, int n_rows, int Hq, int Hkv) {
+namespace {
+struct AttnPlan {
+  int waves;  // waves per work-group of the shared-tile kernel (4 or 2)
+  int n_split;
+};
+
+int tile_splits(int nseq, int64_t max_prefix, int nqb, int Hkv, int W) {
+  const int64_t base = static_cast<int64_t>(nseq) * Hkv * ((nqb + W - 1) / W);
+  const int64_t fill = (GLANCE_ATTN_FILL + base - 1) / base;
+  const int64_t len = max_prefix / (kKB * GLANCE_ATTN_MINBLK);
+  int64_t n = fill < len ? fill : len;
+  if (n < 1) n = 1;
+  if (n > kMaxSplit) n = kMaxSplit;
+  return static_cast<int>(n);
+}
+
+// Four waves per work-group share each tile four ways; when the rounds are too
+// short for four-wave groups to fill the CUs (splits kept >= the minimum
+// length), two-wave groups give twice the work-groups for the same splits.
+AttnPlan attn_plan(int nseq, int64_t max_prefix, int n_rows, int Hq, int Hkv) {
   const int nqb = attn_qblocks(n_rows, Hq, Hkv);
   if (GLANCE_ATTN_TILE == 0) {
     // per-wave kernel: fill the CUs once, and a split per 2048 keys
@@ -838,15 +857,18 @@ int attn_splits(int nseq, int64_t max_prefix, int n_rows, int Hq, int Hkv) {
     int64_t n = fill > len ? fill : len;
     if (n < 1) n = 1;
     if (n > 8) n = 8;
-    return static_cast<int>(n);
+    return {4, static_cast<int>(n)};
   }
-  const int64_t base = static_cast<int64_t>(nseq) * Hkv * ((nqb + GLANCE_ATTN_TILE - 1) / GLANCE_ATTN_TILE);
-  const int64_t fill = (GLANCE_ATTN_FILL + base - 1) / base;
-  const int64_t len = (max_prefix + n_rows) / (kKB * GLANCE_ATTN_MINBLK);
-  int64_t n = fill < len ? fill : len;
-  if (n < 1) n = 1;
-  if (n > kMaxSplit) n = kMaxSplit;
-  return static_cast<int>(n);
+  const int64_t T = max_prefix + n_rows;
+  const int n4 = tile_splits(nseq, T, nqb, Hkv, 4);
+  const int64_t wg4 = static_cast<int64_t>(nseq) * Hkv * ((nqb + 3) / 4) * n4;
+  if (wg4 >= GLANCE_ATTN_FILL || nqb <= 2) return {4, n4};
+  return {2, tile_splits(nseq, T, nqb, Hkv, 2)};
+}
+}  // namespace
+
+int attn_splits(int nseq, int64_t max_prefix, int n_rows, int Hq, int Hkv) {
+  return attn_plan(nseq, max_prefix, n_rows, Hq, Hkv).n_split;
 }
 
 size_t attn_part_floats(int nseq, int n_rows, int Hq, int Hkv, int n_split) {
@@ -861,9 +883,14 @@ glance_status launch_tree_attention(const AttnArgs& a, hipStream_t st) {
       const int grid = a.nseq * a.n_split * nqb * a.Hkv;
       tree_attn_bf16_kernel<<<grid, kAThreads, 0, st>>>(a, nqb);
     } else {
-      constexpr int W = GLANCE_ATTN_TILE == 0 ? 4 : GLANCE_ATTN_TILE;
-      const int grid = a.nseq * a.n_split * ((nqb + W - 1) / W) * a.Hkv;
-      tree_attn_tile_kernel<W><<<grid, W * kWave, 0, st>>>(a, nqb);
+      // the plan that sized the workspace's split records
+      const AttnPlan pl = attn_plan(a.nseq, a.max_prefix, a.n_rows, a.Hq, a.Hkv);
+      if (pl.n_split != a.n_split) return GLANCE_ERR_INVALID_ARG;
+      const int grid = a.nseq * a.n_split * ((nqb + pl.waves - 1) / pl.waves) * a.Hkv;
+      if (pl.waves == 4)
+        tree_attn_tile_kernel<4><<<grid, 4 * kWave, 0, st>>>(a, nqb);
+      else
+        tree_attn_tile_kernel<2><<<grid, 2 * kWave, 0, st>>>(a, nqb);
     }
     GLANCE_LAUNCH_CHECK();
     if (a.n_split > 1) {
