@@ -414,7 +414,7 @@ __global__ __launch_bounds__(kAThreads, 1) void tree_attn_bf16_kernel(AttnArgs a
 // the lazy online softmax, P as a bf16 pair, O^T += V^T P^T) and, at the end,
 // writes its queries' split records (or, with one split, their outputs).
 template <int W>
-__global__ __launch_bounds__(W * kWave, 1) void tree_attn_tile_kernel(AttnArgs a, int nqb) {
+__global__ __launch_bounds__(W * kWave, 1) void tree_attn_tile_kernel(AttnArgs a, int nqb, int fuse) {
   constexpr int KT = kKB * kHD;        // K tile (elements)
   constexpr int VT = kHD * kVtRow;     // V^T tile (elements)
   __shared__ __attribute__((aligned(16))) uint16_t tiles[2][KT + VT];
@@ -440,20 +440,8 @@ __global__ __launch_bounds__(W * kWave, 1) void tree_attn_tile_kernel(AttnArgs a
   const bool qvalid = qb < nqb && q < Qn;
   const int grow = s * a.n_rows + (qvalid ? q / G : 0);
   const uint64_t qanc = qvalid ? a.anc[grow] : 0ull;
-  bf16x8 qhi[8], qlo[8];
-  {
-    const size_t qoff = (static_cast<size_t>(grow) * a.Hq + h * G + (qvalid ? q % G : 0)) * kHD + 64 * g;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qoff;
-    const uint16_t* qlp = static_cast<const uint16_t*>(a.q_lo) + qoff;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      qhi[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 8 * ks));
-      qlo[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qlp + 8 * ks));
-    }
-  }
-  // the query loads complete here, before any K/V load is issued: otherwise the
-  // loop's first use of q waits on every load in flight, prefetches included
-  __builtin_amdgcn_s_waitcnt(0);
+  bf16x8 qhi[8], qlo[8];  // loaded below, behind the first K/V blocks
+  const size_t qoff = (static_cast<size_t>(grow) * a.Hq + h * G + (qvalid ? q % G : 0)) * kHD + 64 * g;
   const int64_t kv0 = a.kv_offsets[s];
   const int P = prefix_len(a, s);
   const int T = P + a.n_rows;
@@ -534,13 +522,29 @@ __global__ __launch_bounds__(W * kWave, 1) void tree_attn_tile_kernel(AttnArgs a
   u32x4 pf[2][NP];
   load(t_beg, pf[0]);
   load(min(t_beg + kKB, tlast), pf[1]);
+  // the query (bf16 pair, the B operand of S^T: dims 64 g + 8 ks .. + 7) in
+  // flight behind the first two blocks
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qoff;
+    const uint16_t* qlp = static_cast<const uint16_t*>(a.q_lo) + qoff;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      qhi[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 8 * ks));
+      qlo[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qlp + 8 * ks));
+    }
+  }
   store(0, pf[0]);
   load(min(t_beg + 2 * kKB, tlast), pf[0]);
   __syncthreads();
   // block b of the range; cur = b mod 2 is a compile-time constant so that the
   // register set of the block after next is named statically
-  auto block = [&](int b, auto par) {
+  auto block = [&](int b, auto par, auto first) {
     constexpr int cur = decltype(par)::value;
+    if constexpr (decltype(first)::value) {
+      // in flight here: block 0, block 1, the 16 query loads, block 2 (NP loads
+      // each, completing in order); the query is complete once at most NP remain
+      __builtin_amdgcn_s_waitcnt(0x0F70 | NP);  // vmcnt(NP), expcnt and lgkmcnt not waited
+    }
     const int t0 = t_beg + b * kKB;
     const uint16_t* kt = tiles[cur];
     const uint16_t* vt = tiles[cur] + KT;
@@ -625,30 +629,99 @@ __global__ __launch_bounds__(W * kWave, 1) void tree_attn_tile_kernel(AttnArgs a
     // into this buffer; the stores of the next block are visible after it
     __syncthreads();
   };
-  // whole pairs, then the last block alone: every back edge follows an odd block
-  // (a loop with the odd block optional would make the compiler wait for the
-  // loads just issued)
-  int b = 0;
-  for (; b + 1 < nblk; b += 2) {
-    block(b, std::integral_constant<int, 0>{});
-    block(b + 1, std::integral_constant<int, 1>{});
+  // Block 0 alone (its products are the first use of q, so only it waits for
+  // the query loads), then whole pairs, then the last block alone: every back
+  // edge follows an even block, and no loop iteration waits for q or for the
+  // loads just issued (an optional second block, or q still pending at the loop
+  // entry, would make the compiler's waits drain the prefetch).
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using First = std::true_type;
+  using Later = std::false_type;
+  if (nblk > 0) {  // (the loop is reachable only through block 0)
+    block(0, C0{}, First{});
+    int b = 1;
+    for (; b + 1 < nblk; b += 2) {
+      block(b, C1{}, Later{});
+      block(b + 1, C0{}, Later{});
+    }
+    if (b < nblk) block(b, C1{}, Later{});
   }
-  if (b < nblk) block(b, std::integral_constant<int, 0>{});
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
-  if (!qvalid) return;
   // lane (j, g) holds dims 32 db + 8 i + 4 g + u (u < 4 consecutive) of query j
   if (a.n_split > 1) {
     const size_t blk = (static_cast<size_t>(s) * Hkv + h) * nqb + qb;
-    float* rec = a.part + ((blk * a.n_split + c) * kQW + j) * kRec;
-    if (g == 0) *reinterpret_cast<float2*>(rec) = make_float2(m_ref, l_tot);
+    const size_t cs = static_cast<size_t>(kQW) * kRec;  // one split's records of a query block
+    float* rec0 = a.part + (blk * a.n_split * kQW + j) * kRec;  // split 0 of this lane's query
+    if (qvalid) {
+      float* rec = rec0 + c * cs;
+      if (g == 0) *reinterpret_cast<float2*>(rec) = make_float2(m_ref, l_tot);
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<float4*>(rec + 4 + 32 * db + 8 * i + 4 * g) =
-            make_float4(acc_o[db][4 * i], acc_o[db][4 * i + 1], acc_o[db][4 * i + 2], acc_o[db][4 * i + 3]);
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<float4*>(rec + 4 + 32 * db + 8 * i + 4 * g) =
+              make_float4(acc_o[db][4 * i], acc_o[db][4 * i + 1], acc_o[db][4 * i + 2], acc_o[db][4 * i + 3]);
+    }
+    if (!fuse) return;  // attn_combine_kernel merges
+    // In-kernel merge: the records reach L2 (every wave waits for its stores),
+    // the group's counter is raised with release ordering (the L2 write-back
+    // makes the whole work-group's records visible device-wide), and the last
+    // of the group's n_split work-groups to arrive acquires them and merges,
+    // with attn_combine_kernel's arithmetic in the same order.
+    __builtin_amdgcn_s_waitcnt(0);
+    __shared__ int s_last;
+    __syncthreads();
+    if (tid == 0) {
+      unsigned* cnt = a.arrivals + (static_cast<size_t>(s) * Hkv + h) * nqg + qg;
+      const unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = old == static_cast<unsigned>(a.n_split - 1);
+      if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last;
+    }
+    __syncthreads();
+    if (!s_last || !qvalid) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // lane (j, g): query qb * 32 + j, dims 64 g .. 64 g + 63
+    float M = -INFINITY;
+    for (int cc = 0; cc < a.n_split; ++cc) M = fmaxf(M, rec0[cc * cs]);
+    float L = 0.f;
+    float acc[64];
+#pragma unroll
+    for (int d = 0; d < 64; ++d) acc[d] = 0.f;
+    for (int cc = 0; cc < a.n_split; ++cc) {
+      const float* rc = rec0 + cc * cs;
+      const float mc = rc[0];
+      const float f = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);
+      L += rc[1] * f;
+      float4 v[16];
+#pragma unroll
+      for (int d4 = 0; d4 < 16; ++d4) v[d4] = *reinterpret_cast<const float4*>(rc + 4 + 64 * g + 4 * d4);
+#pragma unroll
+      for (int d4 = 0; d4 < 16; ++d4) {
+        acc[4 * d4] += v[d4].x * f;
+        acc[4 * d4 + 1] += v[d4].y * f;
+        acc[4 * d4 + 2] += v[d4].z * f;
+        acc[4 * d4 + 3] += v[d4].w * f;
+      }
+    }
+    const int rr = q / G;
+    const int growq = s * a.n_rows + rr;
+    const bool live = a.token[growq] >= 0;
+    const size_t off = static_cast<size_t>(growq) * a.Hq * kHD + (h * G + q % G) * kHD + 64 * g;
+#pragma unroll
+    for (int d4 = 0; d4 < 16; ++d4) {
+      float4 o;
+      o.x = (live && L > 0.f) ? acc[4 * d4] / L : 0.f;
+      o.y = (live && L > 0.f) ? acc[4 * d4 + 1] / L : 0.f;
+      o.z = (live && L > 0.f) ? acc[4 * d4 + 2] / L : 0.f;
+      o.w = (live && L > 0.f) ? acc[4 * d4 + 3] / L : 0.f;
+      *reinterpret_cast<float4*>(a.attn_x + off + 4 * d4) = o;
+      if (a.attn_out) *reinterpret_cast<float4*>(a.attn_out + off + 4 * d4) = o;
+    }
     return;
   }
+  if (!qvalid) return;
   const int rr = q / G;
   const int growq = s * a.n_rows + rr;
   const bool live = a.token[growq] >= 0;
@@ -667,7 +740,9 @@ __global__ __launch_bounds__(W * kWave, 1) void tree_attn_tile_kernel(AttnArgs a
 }
 
 // Merge of the split records of every (row, query head): one work-group per row
-// and query head, one thread per head dimension, splits in order.
+// and query head, one thread per head dimension, splits in order.  NS >=
+// n_split is the unrolled load count.
+template <int NS>
 __global__ __launch_bounds__(kHD) void attn_combine_kernel(AttnArgs a, int nqb) {
   const int grow = blockIdx.x, qh = blockIdx.y, dim = threadIdx.x;
   const int s = grow / a.n_rows, r = grow % a.n_rows;
@@ -677,9 +752,9 @@ __global__ __launch_bounds__(kHD) void attn_combine_kernel(AttnArgs a, int nqb) 
   const float* rec = a.part + (blk * a.n_split * kQW + q % kQW) * kRec;
   const size_t cs = static_cast<size_t>(kQW) * kRec;
   // every load first (splits past n_split re-read the last record, weight 0)
-  float mm[kMaxSplit], ll[kMaxSplit], vv[kMaxSplit];
+  float mm[NS], ll[NS], vv[NS];
 #pragma unroll
-  for (int c = 0; c < kMaxSplit; ++c) {
+  for (int c = 0; c < NS; ++c) {
     const float* rc = rec + min(c, a.n_split - 1) * cs;
     mm[c] = rc[0];
     ll[c] = rc[1];
@@ -688,10 +763,10 @@ __global__ __launch_bounds__(kHD) void attn_combine_kernel(AttnArgs a, int nqb) 
   const bool live = a.token[grow] >= 0;
   float M = -INFINITY;
 #pragma unroll
-  for (int c = 0; c < kMaxSplit; ++c) M = fmaxf(M, c < a.n_split ? mm[c] : -INFINITY);
+  for (int c = 0; c < NS; ++c) M = fmaxf(M, c < a.n_split ? mm[c] : -INFINITY);
   float L = 0.f, acc = 0.f;
 #pragma unroll
-  for (int c = 0; c < kMaxSplit; ++c) {
+  for (int c = 0; c < NS; ++c) {
     const float f = (c >= a.n_split || mm[c] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mm[c] - M);
     L += ll[c] * f;
     acc += vv[c] * f;
@@ -827,11 +902,15 @@ static int attn_qblocks(int n_rows, int Hq, int Hkv) { return (n_rows * (Hq / Hk
 #ifndef GLANCE_ATTN_MINBLK
 #define GLANCE_ATTN_MINBLK 4
 #endif
+#ifndef GLANCE_ATTN_FUSE
+#define GLANCE_ATTN_FUSE 8
+#endif
 
 namespace {
 struct AttnPlan {
   int waves;  // waves per work-group of the shared-tile kernel (4 or 2)
   int n_split;
+  bool fuse;  // the last split of a query group merges the records (no attn_combine)
 };
 
 int tile_splits(int nseq, int64_t max_prefix, int nqb, int Hkv, int W) {
@@ -857,18 +936,26 @@ AttnPlan attn_plan(int nseq, int64_t max_prefix, int n_rows, int Hq, int Hkv) {
     int64_t n = fill > len ? fill : len;
     if (n < 1) n = 1;
     if (n > 8) n = 8;
-    return {4, static_cast<int>(n)};
+    return {4, static_cast<int>(n), false};
   }
   const int64_t T = max_prefix + n_rows;
   const int n4 = tile_splits(nseq, T, nqb, Hkv, 4);
   const int64_t wg4 = static_cast<int64_t>(nseq) * Hkv * ((nqb + 3) / 4) * n4;
-  if (wg4 >= GLANCE_ATTN_FILL || nqb <= 2) return {4, n4};
-  return {2, tile_splits(nseq, T, nqb, Hkv, 2)};
+  AttnPlan p{4, n4, false};
+  if (wg4 < GLANCE_ATTN_FILL && nqb > 2) p = AttnPlan{2, tile_splits(nseq, T, nqb, Hkv, 2), false};
+  // in-kernel merge when a query group's records are few: the last work-group
+  // to arrive reads n_split x waves x 32 records of 528 bytes
+  p.fuse = p.n_split > 1 && p.n_split * p.waves <= GLANCE_ATTN_FUSE;
+  return p;
 }
 }  // namespace
 
 int attn_splits(int nseq, int64_t max_prefix, int n_rows, int Hq, int Hkv) {
   return attn_plan(nseq, max_prefix, n_rows, Hq, Hkv).n_split;
+}
+
+size_t attn_arrival_words(int nseq, int n_rows, int Hq, int Hkv) {
+  return static_cast<size_t>(nseq) * Hkv * attn_qblocks(n_rows, Hq, Hkv);
 }
 
 size_t attn_part_floats(int nseq, int n_rows, int Hq, int Hkv, int n_split) {
@@ -887,14 +974,23 @@ glance_status launch_tree_attention(const AttnArgs& a, hipStream_t st) {
       const AttnPlan pl = attn_plan(a.nseq, a.max_prefix, a.n_rows, a.Hq, a.Hkv);
       if (pl.n_split != a.n_split) return GLANCE_ERR_INVALID_ARG;
       const int grid = a.nseq * a.n_split * ((nqb + pl.waves - 1) / pl.waves) * a.Hkv;
+      const int fuse = pl.fuse && a.arrivals != nullptr;
       if (pl.waves == 4)
-        tree_attn_tile_kernel<4><<<grid, 4 * kWave, 0, st>>>(a, nqb);
+        tree_attn_tile_kernel<4><<<grid, 4 * kWave, 0, st>>>(a, nqb, fuse);
       else
-        tree_attn_tile_kernel<2><<<grid, 2 * kWave, 0, st>>>(a, nqb);
+        tree_attn_tile_kernel<2><<<grid, 2 * kWave, 0, st>>>(a, nqb, fuse);
+      GLANCE_LAUNCH_CHECK();
+      if (fuse) return GLANCE_OK;
     }
     GLANCE_LAUNCH_CHECK();
     if (a.n_split > 1) {
-      attn_combine_kernel<<<dim3(a.nseq * a.n_rows, a.Hq), kHD, 0, st>>>(a, nqb);
+      const dim3 cg(a.nseq * a.n_rows, a.Hq);
+      if (a.n_split <= 4)
+        attn_combine_kernel<4><<<cg, kHD, 0, st>>>(a, nqb);
+      else if (a.n_split <= 8)
+        attn_combine_kernel<8><<<cg, kHD, 0, st>>>(a, nqb);
+      else
+        attn_combine_kernel<kMaxSplit><<<cg, kHD, 0, st>>>(a, nqb);
       GLANCE_LAUNCH_CHECK();
     }
   } else {

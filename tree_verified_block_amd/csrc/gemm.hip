@@ -699,7 +699,7 @@ __device__ __forceinline__ void proj_store(const GemmArgs& a, int b, int gm, con
 // epilogue (two waves per SIMD at one work-group per CU, no more partials).
 template <int EPI, int DEPTH, bool XF, int KW>
 __global__ __launch_bounds__(kGThreads * KW, (XF || DEPTH > 7 || KW > 1) ? 1 : 2) void proj_bf16_kernel(
-    GemmArgs a, int NB, int NGr, int S, int nMT) {
+    GemmArgs a, int NB, int NGr, int S, int nMT, int bpg) {
   constexpr int NX = XF ? 4 : 2;  // 16-byte activation loads per thread and chunk
   constexpr int XH = (XF ? 4 : 2) * kXS;  // one half's stage ring (elements)
   __shared__ __attribute__((aligned(16))) uint16_t xs_all[KW * XH];
@@ -716,8 +716,11 @@ __global__ __launch_bounds__(kGThreads * KW, (XF || DEPTH > 7 || KW > 1) ? 1 : 2
   const int wk = tid_all >> 8;       // half of the slice (KW = 2)
   const int tid = tid_all & (kGThreads - 1);
   uint16_t* xs = xs_all + wk * XH;
-  const int b = g * 4 + w;
-  const bool bv = b < NB;
+  // block of this wave: the group's w-th of bpg (3 or 4) blocks; with bpg = 3
+  // the fourth wave re-reads the group's first block (its sums are dropped) so
+  // that its loads need no branch
+  const int b = g * bpg + (w < bpg ? w : 0);
+  const bool bv = w < bpg && b < NB;
   const int Ks = a.K / S;
   const int kbase = q * Ks + wk * (Ks / KW);
   const int nck = Ks / KW / kKc;
@@ -732,13 +735,15 @@ __global__ __launch_bounds__(kGThreads * KW, (XF || DEPTH > 7 || KW > 1) ? 1 : 2
   const char* wb;
   size_t wcs, whs;
   if (a.w_packed) {
-    // group g's four blocks are one contiguous stream over the chunks
+    // the packed layout keeps four consecutive blocks as one contiguous stream
+    // over the chunks; block b is entry b % 4 of quad b / 4
+    const int bb = b < NB ? b : NB - 1;
     wb = static_cast<const char*>(a.w_packed) +
-         (((static_cast<size_t>(g) * (a.K / kKc) + kbase / kKc) * 4 + w) * 128 + l) * 16;
+         (((static_cast<size_t>(bb >> 2) * (a.K / kKc) + kbase / kKc) * 4 + (bb & 3)) * 128 + l) * 16;
     wcs = 4 * 2048;
     whs = 1024;
   } else {
-    int row = bv ? block_row<EPI>(a, b, lr) : 0;
+    int row = b < NB ? block_row<EPI>(a, b, lr) : 0;
     if (row > a.N - 1) row = a.N - 1;
     wb = reinterpret_cast<const char*>(w_row_ptr(a, row) + kbase + 8 * lg);
     wcs = kKc * 2;
@@ -1244,19 +1249,31 @@ glance_status launch_head_pack(const void* w, int N, int K, void* w_packed, hipS
 #ifndef GLANCE_PROJ_WGS
 #define GLANCE_PROJ_WGS 256
 #endif
-int proj_ksplit(int K, int NB) {
-  // about one work-group per CU: S ~ 256 / (number of 4-block groups), taken as a
-  // divisor of half the chunk count (each slice an even number of chunks).  Wide
-  // projections (more groups than CUs, the MLP) take no split: every work-group
-  // is resident at two per CU and no partial sums cross work-groups.
+#ifndef GLANCE_PROJ_MINBPG
+#define GLANCE_PROJ_MINBPG 3
+#endif
+// Work-groups of a projection: NGr groups of bpg 16-row blocks times S K-slices
+// (S a divisor of half the chunk count, so each slice is an even number of
+// chunks).  The most work-groups up to about one per CU, from groups of four
+// blocks or of three (three-block groups let 384 blocks fill 256 CUs exactly);
+// wide projections (more groups than CUs, the MLP) take groups of four and no
+// split: every work-group is resident at two per CU and no partial sums cross
+// work-groups.
+ProjGrid proj_grid(int K, int NB) {
   const int nch = K / kKc;
-  const int NGr = (NB + 3) / 4;
-  int target = GLANCE_PROJ_WGS / NGr;
-  if (target < 1) target = 1;
-  int S = 1;
-  for (int c = 1; c <= nch / 2; ++c)
-    if ((nch / 2) % c == 0 && c <= target) S = c;
-  return S;
+  ProjGrid best{4, (NB + 3) / 4, 1};
+  int best_wgs = 0;
+  for (int bpg = 4; bpg >= GLANCE_PROJ_MINBPG; --bpg) {
+    const int NGr = (NB + bpg - 1) / bpg;
+    int S = 1;
+    for (int c = 1; c <= nch / 2; ++c)
+      if ((nch / 2) % c == 0 && NGr * c <= GLANCE_PROJ_WGS) S = c;
+    if (NGr * S <= GLANCE_PROJ_WGS && NGr * S > best_wgs) {
+      best = ProjGrid{bpg, NGr, S};
+      best_wgs = NGr * S;
+    }
+  }
+  return best;
 }
 
 int proj_blocks(const GemmArgs& a) {
@@ -1265,13 +1282,13 @@ int proj_blocks(const GemmArgs& a) {
 
 size_t proj_part_floats(int M, int NB, int K) {
   const int nMT = (M + kTileM - 1) / kTileM;
-  const int NGr = (NB + 3) / 4;
-  return static_cast<size_t>(nMT) * NGr * proj_ksplit(K, NB) * 4 * 1024;
+  const ProjGrid pg = proj_grid(K, NB);
+  return static_cast<size_t>(nMT) * pg.NGr * pg.S * 4 * 1024;
 }
 
-size_t proj_counters(int M, int NB) {
+size_t proj_counters(int M, int NB, int K) {
   const int nMT = (M + kTileM - 1) / kTileM;
-  return static_cast<size_t>(nMT) * ((NB + 3) / 4);
+  return static_cast<size_t>(nMT) * proj_grid(K, NB).NGr;
 }
 
 glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
@@ -1291,8 +1308,8 @@ glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
     }
   } else {
     const int NB = proj_blocks(a);
-    const int NGr = (NB + 3) / 4;
-    const int S = proj_ksplit(a.K, NB);
+    const ProjGrid pg = proj_grid(a.K, NB);
+    const int NGr = pg.NGr, S = pg.S, bpg = pg.bpg;
     const int grid = ((NGr + 7) / 8) * 8 * S * nMT;
     // at most one work-group per CU: eight waves splitting the slice in two
     // halves (two waves per SIMD); wider grids: four waves.  Ring depth: the
@@ -1305,11 +1322,11 @@ glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
     const unsigned nthr = kGThreads * kw;
 #define GLANCE_PROJ_KW(E, X, KW)                                                      \
   if (rs == 8)                                                                       \
-    proj_bf16_kernel<E, 7, X, KW><<<grid, nthr, 0, st>>>(a, NB, NGr, S, nMT);         \
+    proj_bf16_kernel<E, 7, X, KW><<<grid, nthr, 0, st>>>(a, NB, NGr, S, nMT, bpg);         \
   else if (rs == 4)                                                                  \
-    proj_bf16_kernel<E, 3, X, KW><<<grid, nthr, 0, st>>>(a, NB, NGr, S, nMT);         \
+    proj_bf16_kernel<E, 3, X, KW><<<grid, nthr, 0, st>>>(a, NB, NGr, S, nMT, bpg);         \
   else                                                                               \
-    proj_bf16_kernel<E, 1, X, KW><<<grid, nthr, 0, st>>>(a, NB, NGr, S, nMT);
+    proj_bf16_kernel<E, 1, X, KW><<<grid, nthr, 0, st>>>(a, NB, NGr, S, nMT, bpg);
 #define GLANCE_PROJ(E, X)    \
   if (kw == 2) {             \
     GLANCE_PROJ_KW(E, X, 2)  \
@@ -1325,9 +1342,9 @@ glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
     } else if (a.x_f32) {
       if (kw == 2) {
         if (rs == 4)
-          proj_bf16_kernel<EPI_RESID, 3, true, 2><<<grid, nthr, 0, st>>>(a, NB, NGr, S, nMT);
+          proj_bf16_kernel<EPI_RESID, 3, true, 2><<<grid, nthr, 0, st>>>(a, NB, NGr, S, nMT, bpg);
         else
-          proj_bf16_kernel<EPI_RESID, 1, true, 2><<<grid, nthr, 0, st>>>(a, NB, NGr, S, nMT);
+          proj_bf16_kernel<EPI_RESID, 1, true, 2><<<grid, nthr, 0, st>>>(a, NB, NGr, S, nMT, bpg);
       } else {
         GLANCE_PROJ_KW(EPI_RESID, true, 1)
       }

@@ -87,7 +87,7 @@ struct AttnWs {
   int n_split = 0;
   size_t off_qkv = 0, off_q = 0, off_qlo = 0, off_k = 0, off_v = 0, off_part = 0, off_x = 0,
          bytes = 0;
-  size_t off_kpart = 0, off_kcnt = 0;
+  size_t off_kpart = 0, off_kcnt = 0, off_acnt = 0;
   // full layer (inter > 0): normalised rows, fp32 q/k/v, h1 and the MLP activation
   size_t off_xn = 0, off_qkv32 = 0, off_h1 = 0, off_act = 0;
 };
@@ -109,17 +109,19 @@ AttnWs attn_ws_layout(int dtype, int nseq, int n_rows, int64_t max_prefix, int d
     w.off_v = take(R * Hkv * D * 2);
     w.n_split = attn_splits(nseq, max_prefix, n_rows, Hq, Hkv);
     w.off_part = take(attn_part_floats(nseq, n_rows, Hq, Hkv, w.n_split) * sizeof(float));
+    // arrival counters of the attention's in-kernel split merge (returned to zero)
+    w.off_acnt = take(attn_arrival_words(nseq, n_rows, Hq, Hkv) * sizeof(unsigned));
     w.off_x = take(R * Hq * D * sizeof(float));
     // split-K scratch shared by the projections (q/k/v, output and, in a full
     // layer, gate/up and down)
     const int M = static_cast<int>(R);
     const int nb_qkv = (Hq + 2 * Hkv) * 8, nb_o = (d_model + 15) / 16;
     size_t pf = std::max(proj_part_floats(M, nb_qkv, d_model), proj_part_floats(M, nb_o, Hq * D));
-    size_t nc = std::max(proj_counters(M, nb_qkv), proj_counters(M, nb_o));
+    size_t nc = std::max(proj_counters(M, nb_qkv, d_model), proj_counters(M, nb_o, Hq * D));
     if (inter > 0) {
       const int nb_gu = 2 * inter / 16;
       pf = std::max({pf, proj_part_floats(M, nb_gu, d_model), proj_part_floats(M, nb_o, inter)});
-      nc = std::max(nc, proj_counters(M, nb_gu));
+      nc = std::max({nc, proj_counters(M, nb_gu, d_model), proj_counters(M, nb_o, inter)});
     }
     w.off_kpart = take(pf * sizeof(float));
     // arrival counters of the split-K groups (each projection returns them to zero)
@@ -406,6 +408,7 @@ glance_status glance_tree_attn(const glance_attn_layer* layer, int32_t dtype, co
   a.max_prefix = max_prefix;
   a.n_split = w.n_split;
   a.part = reinterpret_cast<float*>(base + w.off_part);
+  a.arrivals = reinterpret_cast<unsigned*>(base + w.off_acnt);
   a.attn_out = attn_out;
   a.attn_x = attn_x;
   a.tree_k = tree_k;
@@ -579,6 +582,7 @@ glance_status glance_tree_layer(const glance_full_layer* layer, const void* embe
   a.max_prefix = max_prefix;
   a.n_split = w.n_split;
   a.part = reinterpret_cast<float*>(base + w.off_part);
+  a.arrivals = reinterpret_cast<unsigned*>(base + w.off_acnt);
   a.attn_out = attn_out;
   a.attn_x = reinterpret_cast<float*>(base + w.off_x);
   a.tree_k = tree_k;

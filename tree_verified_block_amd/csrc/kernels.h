@@ -103,9 +103,14 @@ glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
 // Scratch of the bf16 projections: number of 16-row weight blocks, K-split,
 // partial floats and arrival counters for M activation rows.
 int proj_blocks(const GemmArgs& a);
-int proj_ksplit(int K, int NB);
+struct ProjGrid {
+  int bpg;  // 16-row blocks per group (4 or 3)
+  int NGr;  // groups
+  int S;    // K-slices
+};
+ProjGrid proj_grid(int K, int NB);
 size_t proj_part_floats(int M, int NB, int K);
-size_t proj_counters(int M, int NB);
+size_t proj_counters(int M, int NB, int K);
 glance_status launch_gemm_f32(const GemmArgs& a, hipStream_t st);
 // Sampling outputs of the head: token drawn per row and the gap between its
 // perturbed score and the next one (null when not sampling).
@@ -153,11 +158,14 @@ struct AttnArgs {
   float* attn_x;           // [R][Hq D] fp32: input of the output projection
   void* tree_k;            // [R][Hkv][D]: written by the fp32 path (if not NULL), read by bf16
   void* tree_v;
+  unsigned* arrivals;      // bf16: arrival counters of the in-kernel split merge (zero-filled,
+                           // returned to zero), attn_arrival_words of them
 };
 // Key splits of the bf16 attention (from the grid and the longest prefix), and
 // the floats of its split records.
 int attn_splits(int nseq, int64_t max_prefix, int n_rows, int Hq, int Hkv);
 size_t attn_part_floats(int nseq, int n_rows, int Hq, int Hkv, int n_split);
+size_t attn_arrival_words(int nseq, int n_rows, int Hq, int Hkv);
 glance_status launch_tree_attention(const AttnArgs& a, hipStream_t st);
 
 // ----------------------------------------------------------------- layer.hip
