@@ -79,6 +79,25 @@ def test_mini_copy_regime_accepts_planted_run():
         assert int(gpu["out_tokens"][0][rd["G"]]) == rd["break_token"]
 
 
+@pytest.mark.parametrize("prefix,seed", [(300, 21), (600, 22), (1500, 23)])
+def test_attention_split_paths(prefix, seed):
+    """Two query blocks per KV head and longer prefixes: four-wave tile groups
+    with two key splits merged inside the attention kernel (prefix 300), with
+    four splits merged by the separate merge kernel (600), and with more than
+    eight (1500); every output against the oracle, and a second and third
+    launch give the same bits (the merge's arrival counters return to zero)."""
+    from tree_verified_block_amd.round import DeviceRound
+    inp = gen_round(make_config("mini_bf16_copy", prefix=("fixed", prefix), n_rounds=1), seed)
+    first, _ = _round_parity(inp, 0)
+    dev = DeviceRound(inp, keep_layers=True, want_logits=True)
+    dev.set_round(0)
+    for _ in range(2):
+        dev.run()
+        again = dev.fetch()
+        for k in ("attn_out", "h_final", "logits", "argmax", "n_accept", "out_tokens"):
+            assert np.array_equal(np.asarray(again[k]), np.asarray(first[k])), k
+
+
 def test_mini_given_topology_multilayer():
     """Random prefix-closed topology (no draft), three stacked layers."""
     cfg = make_config("mini_bf16_ragged", draft="topology", n_layers=3, nseq=2, N=63, L=15)

@@ -472,19 +472,44 @@ __global__ __launch_bounds__(W * kWave, 1) void tree_attn_tile_kernel(AttnArgs a
   constexpr int VO = W == 4 ? 0 : 4;   // index of the first V piece
   const int lt = tid & 127;
   const int vx = lt & 15, kq = lt >> 4;
-  // The loads are unconditional (the role picks the address): a load under a
-  // branch would make the compiler wait for every load in flight before the
-  // tile stores.
-  auto load = [&](int t0, u32x4 (&d)[NP]) {
+  // Byte offsets of this thread's pieces from the start of a block, the same
+  // for every block (K piece i: key lt / 16 + 8 i, unit lt % 16; V piece i: key
+  // 4 kq + i, dims 8 vx ..); with four waves a thread's offsets are its role's.
+  uint32_t koff[4], voff[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint16_t* kp = row_of(kc0, tk0, t0 + (lt >> 4) + 8 * i) + 8 * (lt & 15);
-      const uint16_t* vp = row_of(vc0, tv0, t0 + 4 * kq + i) + 8 * vx;
-      if (W == 4) {
-        d[i] = *reinterpret_cast<const u32x4*>(krole ? kp : vp);
-      } else {
-        d[i] = *reinterpret_cast<const u32x4*>(kp);
-        d[VO + i] = *reinterpret_cast<const u32x4*>(vp);
+  for (int i = 0; i < 4; ++i) {
+    koff[i] = 2u * static_cast<uint32_t>(((lt >> 4) + 8 * i) * kstr + 8 * (lt & 15));
+    voff[i] = 2u * static_cast<uint32_t>((4 * kq + i) * kstr + 8 * vx);
+    if (W == 4 && !krole) koff[i] = voff[i];
+  }
+  // A block of prefix keys is one base address plus those offsets; a block that
+  // reaches the tree rows or the end picks each key's row.  Either way every
+  // load is issued (the role picks the address): a load under a branch that the
+  // other side lacks would make the compiler wait for every load in flight.
+  auto load = [&](int t0, u32x4 (&d)[NP]) {
+    if (t0 + kKB <= P) {  // (uniform)
+      const char* kb = reinterpret_cast<const char*>(kc0 + static_cast<int64_t>(t0) * kstr);
+      const char* vb = reinterpret_cast<const char*>(vc0 + static_cast<int64_t>(t0) * kstr);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (W == 4) {
+          d[i] = *reinterpret_cast<const u32x4*>((krole ? kb : vb) + koff[i]);
+        } else {
+          d[i] = *reinterpret_cast<const u32x4*>(kb + koff[i]);
+          d[VO + i] = *reinterpret_cast<const u32x4*>(vb + voff[i]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t* kp = row_of(kc0, tk0, t0 + (lt >> 4) + 8 * i) + 8 * (lt & 15);
+        const uint16_t* vp = row_of(vc0, tv0, t0 + 4 * kq + i) + 8 * vx;
+        if (W == 4) {
+          d[i] = *reinterpret_cast<const u32x4*>(krole ? kp : vp);
+        } else {
+          d[i] = *reinterpret_cast<const u32x4*>(kp);
+          d[VO + i] = *reinterpret_cast<const u32x4*>(vp);
+        }
       }
     }
   };
@@ -553,34 +578,36 @@ __global__ __launch_bounds__(W * kWave, 1) void tree_attn_tile_kernel(AttnArgs a
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
       kop[ks] = *reinterpret_cast<const bf16x8*>(kt + j * kHD + 8 * ((8 * g + ks) ^ (j & 7)));
-    f32x16 sa = {}, sb = {};
+    // one accumulator: each 16-deep step adds its q-part and remainder products
+    f32x16 sa = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qhi[ks], sa, 0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qlo[ks], sb, 0, 0, 0);
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qlo[ks], sa, 0, 0, 0);
     }
-    // ---- the next block's tiles into the other buffer (its reads ended at the
-    // previous barrier), then the loads of the block after it
     if (b + 1 < nblk) store(cur ^ 1, pf[cur ^ 1]);
     load(min(t0 + 3 * kKB, tlast), pf[cur ^ 1]);
-    // ---- mask (element v: key t0 + 8 (v / 4) + 4 g + v % 4, query j), block max
-    float sc[16], mb = -INFINITY;
+    // ---- mask (element v: key t0 + 8 (v / 4) + 4 g + v % 4, query j), block
+    // maximum of the raw scores, scaled once (the scale is positive, so the
+    // maximum commutes with it)
+    float sc[16], mraw = -INFINITY;
     if (t0 + kKB <= min(P, t_end)) {  // (uniform) every key of the block is a visible prefix key
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        sc[v] = (sa[v] + sb[v]) * scale_log2;
-        mb = fmaxf(mb, sc[v]);
+        sc[v] = sa[v];
+        mraw = fmaxf(mraw, sc[v]);
       }
     } else {
       const uint32_t vm = block_mask(t0, t_end, P, qanc) >> (4 * g);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const bool vis = (vm >> (8 * (v >> 2) + (v & 3))) & 1u;
-        sc[v] = vis ? (sa[v] + sb[v]) * scale_log2 : -INFINITY;
-        mb = fmaxf(mb, sc[v]);
+        sc[v] = vis ? sa[v] : -INFINITY;
+        mraw = fmaxf(mraw, sc[v]);
       }
     }
-    mb = fmaxf(mb, __shfl_xor(mb, 32, kWave));
+    mraw = fmaxf(mraw, __shfl_xor(mraw, 32, kWave));
+    const float mb = mraw * scale_log2;
     const bool raise = mb > m_ref + 8.f;  // also when m_ref is still -inf
     if (__ballot(raise) != 0ull) {  // (uniform per wave) rare after the first block
       const float m_new = raise ? mb : m_ref;
@@ -596,8 +623,8 @@ __global__ __launch_bounds__(W * kWave, 1) void tree_attn_tile_kernel(AttnArgs a
     uint32_t ph[8], pl[8];
 #pragma unroll
     for (int pr = 0; pr < 8; ++pr) {
-      const float p0 = __builtin_amdgcn_exp2f(sc[2 * pr] - mz);
-      const float p1 = __builtin_amdgcn_exp2f(sc[2 * pr + 1] - mz);
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[2 * pr], scale_log2, -mz));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[2 * pr + 1], scale_log2, -mz));
       ph[pr] = pack_bf16x2(p0, p1);
       pl[pr] = pack_bf16x2(p0 - __uint_as_float(ph[pr] << 16), p1 - __uint_as_float(ph[pr] & 0xFFFF0000u));
       l_run += p0 + p1;
