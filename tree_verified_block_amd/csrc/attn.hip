@@ -106,6 +106,18 @@ __device__ __forceinline__ uint32_t block_mask(int t0, int t_end, int P, uint64_
   return pref | (tree & valid & ~pref);
 }
 
+// The other half of a wave (lane l ^ 32) without an LDS round trip: with both
+// operands the same register, v_permlane32_swap leaves a lane's own value in one
+// result and its partner's in the other, so their max (or sum) is the pair's.
+__device__ __forceinline__ float max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Slot quad of key quad kq (keys 4 kq .. 4 kq + 3 of a 32-key block) in the V^T
 // tile.  The S^T accumulator gives lane (j, g) the keys 8 i + 4 g + u (i, u < 4)
 // of query j; the MFMA B operand of 16-key step t takes from it the keys of
@@ -606,7 +618,7 @@ __global__ __launch_bounds__(W * kWave, 1) void tree_attn_tile_kernel(AttnArgs a
         mraw = fmaxf(mraw, sc[v]);
       }
     }
-    mraw = fmaxf(mraw, __shfl_xor(mraw, 32, kWave));
+    mraw = max_halves(mraw);
     const float mb = mraw * scale_log2;
     const bool raise = mb > m_ref + 8.f;  // also when m_ref is still -inf
     if (__ballot(raise) != 0ull) {  // (uniform per wave) rare after the first block
@@ -674,7 +686,7 @@ __global__ __launch_bounds__(W * kWave, 1) void tree_attn_tile_kernel(AttnArgs a
     }
     if (b < nblk) block(b, C1{}, Later{});
   }
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  const float l_tot = sum_halves(l_run);
   // lane (j, g) holds dims 32 db + 8 i + 4 g + u (u < 4 consecutive) of query j
   if (a.n_split > 1) {
     const size_t blk = (static_cast<size_t>(s) * Hkv + h) * nqb + qb;
