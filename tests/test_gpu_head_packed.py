@@ -132,15 +132,20 @@ def _heads(V, d, R, seed, sample=None):
     return outs
 
 
-@pytest.mark.parametrize("V,d,R", [(1000, 256, 64), (4099, 512, 100), (151936, 4096, 64)])
+# Rows beyond 64 take the packed kernel's two-tile work-groups (each weight chunk
+# applied to 128 activation rows): 100 and 150 rows leave the last pair of tiles
+# partly or wholly empty, 512 rows are the ragged 8-round batch.
+@pytest.mark.parametrize("V,d,R", [(1000, 256, 64), (4099, 512, 100), (4099, 512, 150),
+                                   (151936, 4096, 64), (151936, 4096, 512)])
 def test_packed_head_equals_row_major(V, d, R):
     ref, got = _heads(V, d, R, seed=V + R)
     for k in ("am", "top1", "gap", "H", "logits"):
         assert np.array_equal(ref[k], got[k]), k
 
 
-def test_packed_head_sampled_equals_row_major():
-    ref, got = _heads(151936, 4096, 64, seed=5, sample=(0.8, (1 << 40) + 7, 123))
+@pytest.mark.parametrize("R", [64, 130])
+def test_packed_head_sampled_equals_row_major(R):
+    ref, got = _heads(151936, 4096, R, seed=5, sample=(0.8, (1 << 40) + 7, 123))
     for k in ("am", "top1", "gap", "H", "tok", "sgap"):
         assert np.array_equal(ref[k], got[k]), k
 

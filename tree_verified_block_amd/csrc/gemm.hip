@@ -26,6 +26,7 @@
 // the M-tiles of one weight range are placed on the same XCD back to back so
 // that the weights are fetched from HBM once per XCD L2.
 #include <mutex>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -271,11 +272,16 @@ __device__ __forceinline__ void head_row_stats(const f32x4 (&acc)[B][4], const i
 // The freed LDS deepens the activation ring (the waves meet less often).
 __device__ __forceinline__ int swz(int row, int unit) { return row * kKc + 8 * (unit ^ (row & 7)); }
 
-template <int B, int SB, bool SAMPLE, bool PACKED>
-__global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int NB, int NG,
-                                                                 int nWG, int nMT, int per) {
+// MT > 1 (packed weights only): each work-group applies every weight chunk to
+// MT tiles of 64 activation rows (nMT counts groups of MT tiles), so that rows
+// past the first 64 re-use the weights from registers instead of re-reading
+// them through the caches.
+template <int B, int SB, bool SAMPLE, bool PACKED, int MT = 1>
+__global__ __launch_bounds__(kGThreads, MT == 1 ? 2 : 1) void head_bf16_kernel(GemmArgs a, int NB, int NG,
+                                                                              int nWG, int nMT, int per) {
+  static_assert(MT == 1 || (PACKED && MT == 2), "two activation tiles per work-group, packed weights only");
   constexpr int XST = kTileM * kKc;  // one activation stage (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2 * SB * XST];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2 * SB * XST * MT];
   __shared__ __attribute__((aligned(16))) uint16_t wtile[PACKED ? 8 : 4 * B * 16 * kKc];
   __shared__ HeadPart hred[4][kTileM];
 
@@ -284,7 +290,7 @@ __global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int
   const int mt = kk % nMT;
   const int wg = (kk / nMT) * 8 + xcd;
   if (wg >= nWG) return;
-  const int m0 = mt * kTileM;
+  const int m0 = mt * MT * kTileM;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
   const int G = wg * 4 + w;
   const int nck = a.K / kKc;
@@ -321,24 +327,31 @@ __global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int
   }
   // activation pieces this thread stages: 64 rows x 8 units of 16 B per chunk.
   // Rows past M read row 0 unmasked: their results are never stored.
-  const uint16_t* xr[2];
+  // (tile mm of MT: rows m0 + 64 mm ..; stage st of tile mm at (st * MT + mm) * XST)
+  const uint16_t* xr[MT][2];
   int xlds[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int idx = e * kGThreads + tid;
     const int r = idx >> 3, cc = idx & 7;
-    const int row = m0 + r < a.M ? m0 + r : 0;
-    xr[e] = static_cast<const uint16_t*>(a.x) + static_cast<size_t>(row) * a.K + 8 * cc;
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) {
+      const int rr = m0 + mm * kTileM + r;
+      const int row = rr < a.M ? rr : 0;
+      xr[mm][e] = static_cast<const uint16_t*>(a.x) + static_cast<size_t>(row) * a.K + 8 * cc;
+    }
     xlds[e] = swz(r, cc);
   }
 
-  f32x4 acc[B][4];
+  f32x4 acc[MT][B][4];
 #pragma unroll
-  for (int t = 0; t < B; ++t)
+  for (int mm = 0; mm < MT; ++mm)
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) acc[t][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < B; ++t)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) acc[mm][t][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   uint4 wbuf[2][B][2];
-  uint4 xb[SB][2];
+  uint4 xb[SB][MT][2];
   auto wload = [&](int c, uint4 (&dst)[B][2]) {
 #pragma unroll
     for (int t = 0; t < B; ++t)
@@ -350,13 +363,17 @@ __global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int
           dst[t][i] = load_stream(wp[t][i] + c * kKc);
       }
   };
-  auto xload = [&](int c, uint4 (&dst)[2]) {
+  auto xload = [&](int c, uint4 (&dst)[MT][2]) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e) dst[e] = *reinterpret_cast<const uint4*>(xr[e] + c * kKc);
+    for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) dst[mm][e] = *reinterpret_cast<const uint4*>(xr[mm][e] + c * kKc);
   };
-  auto xstore = [&](int stage, const uint4 (&src)[2]) {
+  auto xstore = [&](int stage, const uint4 (&src)[MT][2]) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e) *reinterpret_cast<uint4*>(&xs[stage * XST + xlds[e]]) = src[e];
+    for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) *reinterpret_cast<uint4*>(&xs[(stage * MT + mm) * XST + xlds[e]]) = src[mm][e];
   };
 
   // nck is a multiple of SB; loads past the last chunk are clamped to it, so no
@@ -384,30 +401,46 @@ __global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int
       _Pragma("unroll") for (int i = 0; i < 2; ++i)                                         \
         wbuf[((U) + 1) & 1][t][i] = load_stream(wq0 + (cn * cstride + toff[t] + i * 64));   \
     asm volatile("" ::: "memory");                                                          \
-    const uint16_t* xq = xs + (half * 2 + (U)) * XST;                                       \
-    _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                         \
-      bf16x8 bx[4];                                                                         \
-      _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) bx[mb] =                             \
-          *reinterpret_cast<const bf16x8*>(xq + swz(mb * 16 + lr, 4 * s + lg));             \
-      _Pragma("unroll") for (int t = 0; t < B; ++t) {                                       \
-        const bf16x8 av = __builtin_bit_cast(bf16x8, wbuf[(U) & 1][t][s]);                  \
-        _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) acc[t][mb] =                       \
-            __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bx[mb], acc[t][mb], 0, 0, 0);       \
+    _Pragma("unroll") for (int mm = 0; mm < MT; ++mm) {                                     \
+      const uint16_t* xq = xs + ((half * 2 + (U)) * MT + mm) * XST;                         \
+      _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                       \
+        bf16x8 bx[4];                                                                       \
+        _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) bx[mb] =                           \
+            *reinterpret_cast<const bf16x8*>(xq + swz(mb * 16 + lr, 4 * s + lg));           \
+        _Pragma("unroll") for (int t = 0; t < B; ++t) {                                     \
+          const bf16x8 av = __builtin_bit_cast(bf16x8, wbuf[(U) & 1][t][s]);                \
+          _Pragma("unroll") for (int mb = 0; mb < 4; ++mb) acc[mm][t][mb] =                 \
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bx[mb], acc[mm][t][mb], 0, 0, 0); \
+        }                                                                                   \
       }                                                                                     \
     }                                                                                       \
   }
   for (int c0 = 0; c0 < nck; c0 += 2) {
     const int half = (c0 / 2) & 1;
     const int ca = min(c0 + 2, nck - 1), cb = min(c0 + 3, nck - 1);
-    const uint4 xa0 = *reinterpret_cast<const uint4*>(xr[0] + ca * kKc);
-    const uint4 xa1 = *reinterpret_cast<const uint4*>(xr[1] + ca * kKc);
-    const uint4 xb0 = *reinterpret_cast<const uint4*>(xr[0] + cb * kKc);
-    const uint4 xb1 = *reinterpret_cast<const uint4*>(xr[1] + cb * kKc);
+    // named registers (tile 0: x*, tile 1: y*), no arrays: see above
+    const uint4 xa0 = *reinterpret_cast<const uint4*>(xr[0][0] + ca * kKc);
+    const uint4 xa1 = *reinterpret_cast<const uint4*>(xr[0][1] + ca * kKc);
+    const uint4 xb0 = *reinterpret_cast<const uint4*>(xr[0][0] + cb * kKc);
+    const uint4 xb1 = *reinterpret_cast<const uint4*>(xr[0][1] + cb * kKc);
+    uint4 ya0, ya1, yb0, yb1;
+    if constexpr (MT == 2) {
+      ya0 = *reinterpret_cast<const uint4*>(xr[MT - 1][0] + ca * kKc);
+      ya1 = *reinterpret_cast<const uint4*>(xr[MT - 1][1] + ca * kKc);
+      yb0 = *reinterpret_cast<const uint4*>(xr[MT - 1][0] + cb * kKc);
+      yb1 = *reinterpret_cast<const uint4*>(xr[MT - 1][1] + cb * kKc);
+    }
     GLANCE_PACKED_CHUNK(0)
-    *reinterpret_cast<uint4*>(&xs[((half ^ 1) * 2) * XST + xlds[0]]) = xa0;
-    *reinterpret_cast<uint4*>(&xs[((half ^ 1) * 2) * XST + xlds[1]]) = xa1;
-    *reinterpret_cast<uint4*>(&xs[((half ^ 1) * 2 + 1) * XST + xlds[0]]) = xb0;
-    *reinterpret_cast<uint4*>(&xs[((half ^ 1) * 2 + 1) * XST + xlds[1]]) = xb1;
+    *reinterpret_cast<uint4*>(&xs[(((half ^ 1) * 2) * MT) * XST + xlds[0]]) = xa0;
+    *reinterpret_cast<uint4*>(&xs[(((half ^ 1) * 2) * MT) * XST + xlds[1]]) = xa1;
+    *reinterpret_cast<uint4*>(&xs[(((half ^ 1) * 2 + 1) * MT) * XST + xlds[0]]) = xb0;
+    *reinterpret_cast<uint4*>(&xs[(((half ^ 1) * 2 + 1) * MT) * XST + xlds[1]]) = xb1;
+    if constexpr (MT == 2) {
+      *reinterpret_cast<uint4*>(&xs[(((half ^ 1) * 2) * MT + 1) * XST + xlds[0]]) = ya0;
+      *reinterpret_cast<uint4*>(&xs[(((half ^ 1) * 2) * MT + 1) * XST + xlds[1]]) = ya1;
+      *reinterpret_cast<uint4*>(&xs[(((half ^ 1) * 2 + 1) * MT + 1) * XST + xlds[0]]) = yb0;
+      *reinterpret_cast<uint4*>(&xs[(((half ^ 1) * 2 + 1) * MT + 1) * XST + xlds[1]]) = yb1;
+    }
     GLANCE_PACKED_CHUNK(1)
     __syncthreads();
   }
@@ -437,7 +470,7 @@ __global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int
           const bf16x8 av = *reinterpret_cast<const bf16x8*>(wt + swz(t * 16 + lr, 4 * s + lg));
 #pragma unroll
           for (int mb = 0; mb < 4; ++mb)
-            acc[t][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bx[mb], acc[t][mb], 0, 0, 0);
+            acc[0][t][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bx[mb], acc[0][t][mb], 0, 0, 0);
         }
       }
     }
@@ -449,88 +482,100 @@ __global__ __launch_bounds__(kGThreads, 2) void head_bf16_kernel(GemmArgs a, int
   }
   }
 
-  // acc[t][mb][v]: vocabulary row blk[t]*16 + 4 lg + v, activation row m0 + 16 mb + lr.
-  HeadPart hp[4];
-  if (bval[B - 1] && blk[B - 1] * 16 + 16 <= a.N)  // (wave-uniform) every row of the wave exists
-    head_row_stats<B, false>(acc, blk, bval, lg, a.N, hp);
-  else
-    head_row_stats<B, true>(acc, blk, bval, lg, a.N, hp);
-  if (a.logits) {
-#pragma unroll
-    for (int t = 0; t < B; ++t)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int n = blk[t] * 16 + 4 * lg + v;
-        if (bval[t] && n < a.N) {
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb) {
-            const int m = m0 + mb * 16 + lr;
-            if (m < a.M) a.logits[static_cast<size_t>(m) * a.N + n] = acc[t][mb][v];
-          }
-        }
-      }
-  }
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    hp[mb] = head_combine(hp[mb], shfl_part(hp[mb], l ^ 16));
-    hp[mb] = head_combine(hp[mb], shfl_part(hp[mb], l ^ 32));
-    if (lg == 0) hred[w][mb * 16 + lr] = hp[mb];
-  }
-  if constexpr (SAMPLE) {
-    // the draw of every activation row from softmax(z / T): Gumbel-max over this
-    // lane's tokens (one Philox call gives the noise of 4 consecutive tokens),
-    // then over lanes and waves as for the statistics
-    __shared__ Draw dred[4][kTileM];
-    Draw dp[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      dp[mb] = draw_empty();
-      const uint32_t row = static_cast<uint32_t>(m0 + mb * 16 + lr);
-#pragma unroll
-      for (int t = 0; t < B; ++t) {
-        const uint4 x = philox4x32_10(
-            make_uint4(static_cast<uint32_t>(blk[t] * 4 + lg), row, a.rnd_lo, a.rnd_hi), a.seed_lo,
-            a.seed_hi);
-        const uint32_t xs4[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
+  // per activation tile: the statistics of its 64 rows (the LDS reduction
+  // buffers are reused tile after tile); the tile index is a compile-time
+  // constant so that the accumulators stay in registers
+  auto epilogue = [&](auto mmc) {
+    constexpr int mm = decltype(mmc)::value;
+    const int mt0 = m0 + mm * kTileM;
+    // acc[mm][t][mb][v]: vocabulary row blk[t]*16 + 4 lg + v, activation row mt0 + 16 mb + lr.
+    HeadPart hp[4];
+    if (bval[B - 1] && blk[B - 1] * 16 + 16 <= a.N)  // (wave-uniform) every row of the wave exists
+      head_row_stats<B, false>(acc[mm], blk, bval, lg, a.N, hp);
+    else
+      head_row_stats<B, true>(acc[mm], blk, bval, lg, a.N, hp);
+    if (a.logits) {
+  #pragma unroll
+      for (int t = 0; t < B; ++t)
+  #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int n = blk[t] * 16 + 4 * lg + v;
-          const float sc = (bval[t] & (n < a.N)) ? fmaf(acc[t][mb][v], a.inv_temp, gumbel(xs4[v])) : -INFINITY;
-          const bool gt = sc > dp[mb].m;
-          dp[mb].m2 = gt ? dp[mb].m : fmaxf(dp[mb].m2, sc);
-          dp[mb].tok = gt ? n : dp[mb].tok;
-          dp[mb].m = fmaxf(dp[mb].m, sc);
+          if (bval[t] && n < a.N) {
+  #pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+              const int m = mt0 + mb * 16 + lr;
+              if (m < a.M) a.logits[static_cast<size_t>(m) * a.N + n] = acc[mm][t][mb][v];
+            }
+          }
         }
+    }
+  #pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      hp[mb] = head_combine(hp[mb], shfl_part(hp[mb], l ^ 16));
+      hp[mb] = head_combine(hp[mb], shfl_part(hp[mb], l ^ 32));
+      if (lg == 0) hred[w][mb * 16 + lr] = hp[mb];
+    }
+    if constexpr (SAMPLE) {
+      // the draw of every activation row from softmax(z / T): Gumbel-max over this
+      // lane's tokens (one Philox call gives the noise of 4 consecutive tokens),
+      // then over lanes and waves as for the statistics
+      __shared__ Draw dred[4][kTileM];
+      Draw dp[4];
+  #pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        dp[mb] = draw_empty();
+        const uint32_t row = static_cast<uint32_t>(mt0 + mb * 16 + lr);
+  #pragma unroll
+        for (int t = 0; t < B; ++t) {
+          const uint4 x = philox4x32_10(
+              make_uint4(static_cast<uint32_t>(blk[t] * 4 + lg), row, a.rnd_lo, a.rnd_hi), a.seed_lo,
+              a.seed_hi);
+          const uint32_t xs4[4] = {x.x, x.y, x.z, x.w};
+  #pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int n = blk[t] * 16 + 4 * lg + v;
+            const float sc = (bval[t] & (n < a.N)) ? fmaf(acc[mm][t][mb][v], a.inv_temp, gumbel(xs4[v])) : -INFINITY;
+            const bool gt = sc > dp[mb].m;
+            dp[mb].m2 = gt ? dp[mb].m : fmaxf(dp[mb].m2, sc);
+            dp[mb].tok = gt ? n : dp[mb].tok;
+            dp[mb].m = fmaxf(dp[mb].m, sc);
+          }
+        }
+        dp[mb] = draw_combine(dp[mb], shfl_draw(dp[mb], l ^ 16));
+        dp[mb] = draw_combine(dp[mb], shfl_draw(dp[mb], l ^ 32));
+        if (lg == 0) dred[w][mb * 16 + lr] = dp[mb];
       }
-      dp[mb] = draw_combine(dp[mb], shfl_draw(dp[mb], l ^ 16));
-      dp[mb] = draw_combine(dp[mb], shfl_draw(dp[mb], l ^ 32));
-      if (lg == 0) dred[w][mb * 16 + lr] = dp[mb];
+      __syncthreads();
+      if (tid < kTileM && mt0 + tid < a.M) {
+        Draw d = dred[0][tid];
+  #pragma unroll
+        for (int ww = 1; ww < 4; ++ww) d = draw_combine(d, dred[ww][tid]);
+        float* o = a.spart + (static_cast<size_t>(mt0 + tid) * nWG + wg) * 3;
+        o[0] = d.m;
+        o[1] = __int_as_float(d.tok);
+        o[2] = d.m2;
+      }
     }
     __syncthreads();
-    if (tid < kTileM && m0 + tid < a.M) {
-      Draw d = dred[0][tid];
-#pragma unroll
-      for (int ww = 1; ww < 4; ++ww) d = draw_combine(d, dred[ww][tid]);
-      float* o = a.spart + (static_cast<size_t>(m0 + tid) * nWG + wg) * 3;
-      o[0] = d.m;
-      o[1] = __int_as_float(d.tok);
-      o[2] = d.m2;
+    if (tid < kTileM) {
+      HeadPart p = hred[0][tid];
+  #pragma unroll
+      for (int ww = 1; ww < 4; ++ww) p = head_combine(p, hred[ww][tid]);
+      const int m = mt0 + tid;
+      if (m < a.M) {
+        float* o = a.part + (static_cast<size_t>(m) * nWG + wg) * 5;
+        o[0] = p.m;
+        o[1] = __int_as_float(p.am);
+        o[2] = p.m2;
+        o[3] = p.s;
+        o[4] = p.t;
+      }
     }
-  }
-  __syncthreads();
-  if (tid < kTileM) {
-    HeadPart p = hred[0][tid];
-#pragma unroll
-    for (int ww = 1; ww < 4; ++ww) p = head_combine(p, hred[ww][tid]);
-    const int m = m0 + tid;
-    if (m < a.M) {
-      float* o = a.part + (static_cast<size_t>(m) * nWG + wg) * 5;
-      o[0] = p.m;
-      o[1] = __int_as_float(p.am);
-      o[2] = p.m2;
-      o[3] = p.s;
-      o[4] = p.t;
-    }
+  };
+  epilogue(std::integral_constant<int, 0>{});
+  if constexpr (MT == 2) {
+    __syncthreads();
+    epilogue(std::integral_constant<int, MT - 1>{});
   }
 }
 
@@ -1296,7 +1341,15 @@ glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   if (a.epi == EPI_HEAD) {
     const HeadGrid g = head_grid(a.N);
     const int grid = ((g.nWG + 7) / 8) * 8 * nMT;
-    if (a.w_packed) {
+    if (a.w_packed && nMT >= 2) {
+      // two activation tiles per work-group (weights applied from registers twice)
+      const int nMT2 = (nMT + 1) / 2;
+      const int grid2 = ((g.nWG + 7) / 8) * 8 * nMT2;
+      if (a.spart)
+        head_bf16_kernel<kHeadB, 2, true, true, 2><<<grid2, kGThreads, 0, st>>>(a, g.NB, g.NG, g.nWG, nMT2, g.per);
+      else
+        head_bf16_kernel<kHeadB, 2, false, true, 2><<<grid2, kGThreads, 0, st>>>(a, g.NB, g.NG, g.nWG, nMT2, g.per);
+    } else if (a.w_packed) {
       if (a.spart)
         head_bf16_kernel<kHeadB, 2, true, true><<<grid, kGThreads, 0, st>>>(a, g.NB, g.NG, g.nWG, nMT, g.per);
       else
