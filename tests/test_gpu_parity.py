@@ -64,6 +64,14 @@ def test_mini_bf16_round(name, seed):
     _round_parity(gen_round(make_config(name), seed), 0)
 
 
+@pytest.mark.parametrize("nseq,seed", [(4, 31), (7, 32)])
+def test_projection_row_tiles(nseq, seed):
+    """More rows than one 64-row tile: the projections take several tiles per
+    work-group, and 164 or 287 rows leave the last group of tiles partly empty;
+    every round output against the oracle."""
+    _round_parity(gen_round(make_config("mini_bf16_ragged", nseq=nseq), seed), 0)
+
+
 @pytest.mark.parametrize("seed", [1, 2])
 def test_mini_full_layer_round(seed):
     """Two full decoder layers (RMSNorm, QK-norm, SwiGLU MLP): every layer's

@@ -742,12 +742,17 @@ __device__ __forceinline__ void proj_store(const GemmArgs& a, int b, int gm, con
 // KW = 2: eight waves, the four blocks times two halves of the slice, each half
 // staging its own activation chunks; the halves' sums meet in LDS before the
 // epilogue (two waves per SIMD at one work-group per CU, no more partials).
-template <int EPI, int DEPTH, bool XF, int KW>
-__global__ __launch_bounds__(kGThreads * KW, (XF || DEPTH > 7 || KW > 1) ? 1 : 2) void proj_bf16_kernel(
+//
+// MT > 1 (more than 64 activation rows, K split over work-groups, four waves):
+// each work-group applies its weight stream to MT tiles of 64 rows (nMT then
+// counts groups of MT tiles), so the weights are loaded once for MT tiles.
+template <int EPI, int DEPTH, bool XF, int KW, int MT = 1>
+__global__ __launch_bounds__(kGThreads * KW, (XF || DEPTH > 7 || KW > 1 || MT > 2) ? 1 : 2) void proj_bf16_kernel(
     GemmArgs a, int NB, int NGr, int S, int nMT, int bpg) {
+  static_assert(MT == 1 || KW == 1, "activation tiles per work-group with one wave group per slice");
   constexpr int NX = XF ? 4 : 2;  // 16-byte activation loads per thread and chunk
-  constexpr int XH = (XF ? 4 : 2) * kXS;  // one half's stage ring (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t xs_all[KW * XH];
+  constexpr int XH = (XF ? 4 : 2) * kXS;  // one half's stage ring (elements), per tile
+  __shared__ __attribute__((aligned(16))) uint16_t xs_all[KW * XH * MT];
 
   const int bid = blockIdx.x;
   const int xcd = bid & 7, kk = bid >> 3;
@@ -755,12 +760,12 @@ __global__ __launch_bounds__(kGThreads * KW, (XF || DEPTH > 7 || KW > 1) ? 1 : 2
   const int q = (kk / nMT) % S;
   const int g = (kk / (nMT * S)) * 8 + xcd;
   if (g >= NGr) return;
-  const int m0 = mt * kTileM;
+  const int m0 = mt * MT * kTileM;
   const int tid_all = threadIdx.x, l = tid_all & 63, lr = l & 15, lg = l >> 4;
   const int w = (tid_all >> 6) & 3;  // block of the group
   const int wk = tid_all >> 8;       // half of the slice (KW = 2)
   const int tid = tid_all & (kGThreads - 1);
-  uint16_t* xs = xs_all + wk * XH;
+  uint16_t* xs = xs_all + wk * XH;  // tile mm's stages at xs + mm * XH
   // block of this wave: the group's w-th of bpg (3 or 4) blocks; with bpg = 3
   // the fourth wave re-reads the group's first block (its sums are dropped) so
   // that its loads need no branch
@@ -794,50 +799,61 @@ __global__ __launch_bounds__(kGThreads * KW, (XF || DEPTH > 7 || KW > 1) ? 1 : 2
     wcs = kKc * 2;
     whs = 64;
   }
-  // piece e of this thread: 8 activations of row m0 + r, columns cc .. cc + 7 of the chunk
-  const char* xr[2];
-  uint32_t xm[2];
+  // piece e of this thread: 8 activations of row m0 + 64 mm + r, columns cc .. cc + 7 of the chunk
+  const char* xr[MT][2];
+  uint32_t xm[MT][2];
   int xlds[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int idx = e * kGThreads + tid;
     const int r = idx >> 3, cc = (idx & 7) * 8;
-    const uint16_t* p16;
-    x_row_masked(a, m0 + r, p16, xm[e]);
-    if constexpr (XF) {
-      const size_t row = static_cast<size_t>(p16 - static_cast<const uint16_t*>(a.x)) / a.K;
-      xr[e] = reinterpret_cast<const char*>(static_cast<const float*>(a.x) + row * a.K + kbase + cc);
-    } else {
-      xr[e] = reinterpret_cast<const char*>(p16 + kbase + cc);
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) {
+      const uint16_t* p16;
+      x_row_masked(a, m0 + mm * kTileM + r, p16, xm[mm][e]);
+      if constexpr (XF) {
+        const size_t row = static_cast<size_t>(p16 - static_cast<const uint16_t*>(a.x)) / a.K;
+        xr[mm][e] = reinterpret_cast<const char*>(static_cast<const float*>(a.x) + row * a.K + kbase + cc);
+      } else {
+        xr[mm][e] = reinterpret_cast<const char*>(p16 + kbase + cc);
+      }
     }
     xlds[e] = r * kXP + cc;
   }
   constexpr int xcs = XF ? kKc * 4 : kKc * 2;  // bytes per chunk along a row
 
-  f32x4 acc[4];
+  f32x4 acc[MT][4];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[mm][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr int RS = DEPTH + 1;
   static_assert(RS % 2 == 0, "ring slots and LDS stages must unroll together");
   uint4 wbuf[RS][2];
-  uint4 xbuf[RS][NX];
+  uint4 xbuf[RS][MT][NX];
   auto wload = [&](int c, uint4 (&dst)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) dst[i] = *reinterpret_cast<const uint4*>(wb + c * wcs + i * whs);
   };
   // raw loads; the row mask is applied when the chunk is written to LDS
-  auto xload = [&](int c, uint4 (&dst)[NX]) {
+  auto xload = [&](int c, uint4 (&dst)[MT][NX]) {
 #pragma unroll
-    for (int e = 0; e < NX; ++e)
-      dst[e] = *reinterpret_cast<const uint4*>(xr[e * 2 / NX] + c * xcs + (XF ? (e & 1) * 16 : 0));
+    for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+      for (int e = 0; e < NX; ++e)
+        dst[mm][e] = *reinterpret_cast<const uint4*>(xr[mm][e * 2 / NX] + c * xcs + (XF ? (e & 1) * 16 : 0));
   };
   // chunk pieces -> LDS stage st (bf16 rounding; with XF also the remainder in
   // the second half of the stage ring)
-  auto xstage = [&](int st, const uint4 (&src)[NX]) {
+  auto xstage = [&](int st, const uint4 (&srcs)[MT][NX]) {
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm)
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
+      const uint4 (&src)[NX] = srcs[mm];
+      uint16_t* xt = xs + mm * XH;
       if constexpr (XF) {
-        const uint4 f0 = mask4(src[2 * e], xm[e]), f1 = mask4(src[2 * e + 1], xm[e]);
+        const uint4 f0 = mask4(src[2 * e], xm[mm][e]), f1 = mask4(src[2 * e + 1], xm[mm][e]);
         const float v[8] = {__uint_as_float(f0.x), __uint_as_float(f0.y), __uint_as_float(f0.z),
                             __uint_as_float(f0.w), __uint_as_float(f1.x), __uint_as_float(f1.y),
                             __uint_as_float(f1.z), __uint_as_float(f1.w)};
@@ -848,10 +864,10 @@ __global__ __launch_bounds__(kGThreads * KW, (XF || DEPTH > 7 || KW > 1) ? 1 : 2
           lw[k] = pack_bf16x2(v[2 * k] - __uint_as_float(hw[k] << 16),
                               v[2 * k + 1] - __uint_as_float(hw[k] & 0xFFFF0000u));
         }
-        *reinterpret_cast<uint4*>(&xs[st * kXS + xlds[e]]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        *reinterpret_cast<uint4*>(&xs[(2 + st) * kXS + xlds[e]]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        *reinterpret_cast<uint4*>(&xt[st * kXS + xlds[e]]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(&xt[(2 + st) * kXS + xlds[e]]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       } else {
-        *reinterpret_cast<uint4*>(&xs[st * kXS + xlds[e]]) = mask4(src[e], xm[e]);
+        *reinterpret_cast<uint4*>(&xt[st * kXS + xlds[e]]) = mask4(src[e], xm[mm][e]);
       }
     }
   };
@@ -876,29 +892,32 @@ __global__ __launch_bounds__(kGThreads * KW, (XF || DEPTH > 7 || KW > 1) ? 1 : 2
         xload(cn, xbuf[(u + DEPTH) % RS]);
         wload(cn, wbuf[(u + DEPTH) % RS]);
         __syncthreads();
-        const uint16_t* xq = xs + (u & 1) * kXS;
-        // every activation operand of the chunk is read from LDS before the
-        // first product, so the reads overlap instead of each product waiting
-        // on its own read
-        constexpr int NV = XF ? 2 : 1;
-        bf16x8 bx[2][4][NV];
+        // every activation operand of a tile's chunk is read from LDS before
+        // the tile's first product, so the reads overlap instead of each
+        // product waiting on its own read
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int mm = 0; mm < MT; ++mm) {
+          const uint16_t* xq = xs + mm * XH + (u & 1) * kXS;
+          constexpr int NV = XF ? 2 : 1;
+          bf16x8 bx[2][4][NV];
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int v = 0; v < NV; ++v)
-              bx[s][mb][v] = *reinterpret_cast<const bf16x8*>(
-                  xq + 2 * v * kXS + (mb * 16 + lr) * kXP + s * 32 + 8 * lg);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const bf16x8 av = __builtin_bit_cast(bf16x8, wbuf[u][s]);
-#pragma unroll
-          for (int v = 0; v < NV; ++v)
+          for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
-              acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bx[s][mb][v], acc[mb], 0, 0, 0);
+#pragma unroll
+              for (int v = 0; v < NV; ++v)
+                bx[s][mb][v] = *reinterpret_cast<const bf16x8*>(
+                    xq + 2 * v * kXS + (mb * 16 + lr) * kXP + s * 32 + 8 * lg);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const bf16x8 av = __builtin_bit_cast(bf16x8, wbuf[u][s]);
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+              for (int mb = 0; mb < 4; ++mb)
+                acc[mm][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bx[s][mb][v], acc[mm][mb], 0, 0, 0);
+          }
         }
         // (after the last chunk this stores a clamped copy nobody reads)
         xstage((u + 1) & 1, xbuf[(u + 1) % RS]);
@@ -906,98 +925,160 @@ __global__ __launch_bounds__(kGThreads * KW, (XF || DEPTH > 7 || KW > 1) ? 1 : 2
     }
   }
 
-  // partial of this wave's block: [16 block rows][64 activation rows], stored
-  // with device-coherent stores; the group's last work-group to arrive sums the
-  // S slices in slice order (deterministic) and applies the epilogue.  Only the
-  // counter and the partials are shared, both through device-scope atomic
-  // accesses (write-through stores and coherent loads), and every store has
-  // completed before the arrival is counted, so no cache write-back is needed.
-  if constexpr (KW > 1) {
-    // the second half's sums join the first's (same lane layout) through LDS
-    float* hp = reinterpret_cast<float*>(xs_all) + w * 1024 + l;
-    __syncthreads();
-    if (wk == 1) {
+  if constexpr (MT > 1) {
+    // K is split (S > 1): every tile's partial is stored, one arrival counts the
+    // work-group's tiles, and the last work-group of the group sums each tile's
+    // slices in slice order and applies the epilogue (same hand-over as below)
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) {
+      if (m0 + mm * kTileM >= a.M) break;  // (uniform) a tile past the rows: no partial
+      const size_t grp = static_cast<size_t>(mt * MT + mm) * NGr + g;
+      float* pp = a.kpart + ((grp * S + q) * 4 + w) * 1024;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) hp[(mb * 4 + v) * 64] = acc[mb][v];
+        for (int v = 0; v < 4; ++v)
+          __hip_atomic_store(pp + (4 * lg + v) * 64 + mb * 16 + lr, acc[mm][mb][v], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __shared__ int s_last_t;
+    __syncthreads();
+    if (tid_all == 0) {
+      unsigned* cnt = a.kcnt + static_cast<size_t>(mt) * NGr + g;
+      const unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = old == static_cast<unsigned>(S - 1);
+      if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last_t = last;
     }
     __syncthreads();
+    if (!s_last_t || !bv) return;
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) {
+      if (m0 + mm * kTileM >= a.M) break;  // (uniform) no rows in this tile
+      // thread (w, l): activation row m0 + 64 mm + l of block b
+      const int gm = m0 + mm * kTileM + l;
+      EpiIn et;
+      et.key = epi_key<EPI>(a, b, min(gm, a.M - 1));
+      epi_load<EPI>(a, b, min(gm, a.M - 1), et);
+      const size_t grp = static_cast<size_t>(mt * MT + mm) * NGr + g;
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = 0.f;
+      constexpr int kSB = 8;
+      for (int q0 = 0; q0 < S; q0 += kSB) {
+        float y[kSB][16];
+#pragma unroll
+        for (int j = 0; j < kSB; ++j) {
+          if (q0 + j < S) {
+            const float* src = a.kpart + ((grp * S + q0 + j) * 4 + w) * 1024 + l;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) y[j][i] = __hip_atomic_load(src + i * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kSB; ++j)
+          if (q0 + j < S) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[i] += y[j][i];
+          }
+      }
+      if (gm < a.M) proj_store<EPI>(a, b, gm, x, et);
+    }
+  } else {
+    // partial of this wave's block: [16 block rows][64 activation rows], stored
+    // with device-coherent stores; the group's last work-group to arrive sums the
+    // S slices in slice order (deterministic) and applies the epilogue.  Only the
+    // counter and the partials are shared, both through device-scope atomic
+    // accesses (write-through stores and coherent loads), and every store has
+    // completed before the arrival is counted, so no cache write-back is needed.
+    if constexpr (KW > 1) {
+      // the second half's sums join the first's (same lane layout) through LDS
+      float* hp = reinterpret_cast<float*>(xs_all) + w * 1024 + l;
+      __syncthreads();
+      if (wk == 1) {
+  #pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+  #pragma unroll
+          for (int v = 0; v < 4; ++v) hp[(mb * 4 + v) * 64] = acc[0][mb][v];
+      }
+      __syncthreads();
+      if (wk == 0) {
+  #pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+  #pragma unroll
+          for (int v = 0; v < 4; ++v) acc[0][mb][v] += hp[(mb * 4 + v) * 64];
+      }
+    }
+    if (bv) epi_load<EPI>(a, b, gme, ein);
+    if (S == 1) {
+      // no other slice: the block's 16 x 64 result goes through LDS (the stage
+      // ring is free after the barrier) to one thread per activation row
+      float* tr = reinterpret_cast<float*>(xs_all) + w * 1024;
+      __syncthreads();
+      if (wk == 0) {
+  #pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+  #pragma unroll
+          for (int v = 0; v < 4; ++v) tr[(4 * lg + v) * 64 + mb * 16 + lr] = acc[0][mb][v];
+      }
+      __syncthreads();
+      if (wk != 0 || !bv || m0 + l >= a.M) return;
+      float x[16];
+  #pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = tr[i * 64 + l];
+      proj_store<EPI>(a, b, m0 + l, x, ein);
+      return;
+    }
+    const size_t grp = static_cast<size_t>(mt) * NGr + g;
+    float* pp = a.kpart + ((grp * S + q) * 4 + w) * 1024;
     if (wk == 0) {
-#pragma unroll
+  #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[mb][v] += hp[(mb * 4 + v) * 64];
+  #pragma unroll
+        for (int v = 0; v < 4; ++v)
+          __hip_atomic_store(pp + (4 * lg + v) * 64 + mb * 16 + lr, acc[0][mb][v], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
     }
-  }
-  if (bv) epi_load<EPI>(a, b, gme, ein);
-  if (S == 1) {
-    // no other slice: the block's 16 x 64 result goes through LDS (the stage
-    // ring is free after the barrier) to one thread per activation row
-    float* tr = reinterpret_cast<float*>(xs_all) + w * 1024;
+    __builtin_amdgcn_s_waitcnt(0);
+    __shared__ int s_last;
     __syncthreads();
-    if (wk == 0) {
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) tr[(4 * lg + v) * 64 + mb * 16 + lr] = acc[mb][v];
+    if (tid_all == 0) {
+      const unsigned old = __hip_atomic_fetch_add(a.kcnt + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = old == static_cast<unsigned>(S - 1);
+      if (last) __hip_atomic_store(a.kcnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last;
     }
     __syncthreads();
-    if (wk != 0 || !bv || m0 + l >= a.M) return;
+    if (!s_last || !bv || wk != 0) return;
+    // thread (w, l): activation row m0 + l of block b
     float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = tr[i * 64 + l];
-    proj_store<EPI>(a, b, m0 + l, x, ein);
-    return;
-  }
-  const size_t grp = static_cast<size_t>(mt) * NGr + g;
-  float* pp = a.kpart + ((grp * S + q) * 4 + w) * 1024;
-  if (wk == 0) {
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        __hip_atomic_store(pp + (4 * lg + v) * 64 + mb * 16 + lr, acc[mb][v], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __shared__ int s_last;
-  __syncthreads();
-  if (tid_all == 0) {
-    const unsigned old = __hip_atomic_fetch_add(a.kcnt + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = old == static_cast<unsigned>(S - 1);
-    if (last) __hip_atomic_store(a.kcnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = last;
-  }
-  __syncthreads();
-  if (!s_last || !bv || wk != 0) return;
-  // thread (w, l): activation row m0 + l of block b
-  float x[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = 0.f;
-  // up to 8 slices' loads in flight at once (one round trip per 8 slices),
-  // summed in slice order
-  constexpr int kSB = 8;
-  for (int q0 = 0; q0 < S; q0 += kSB) {
-    float y[kSB][16];
-#pragma unroll
-    for (int j = 0; j < kSB; ++j) {
-      if (q0 + j < S) {
-        const float* src = a.kpart + ((grp * S + q0 + j) * 4 + w) * 1024 + l;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) y[j][i] = __hip_atomic_load(src + i * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  #pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = 0.f;
+    // up to 8 slices' loads in flight at once (one round trip per 8 slices),
+    // summed in slice order
+    constexpr int kSB = 8;
+    for (int q0 = 0; q0 < S; q0 += kSB) {
+      float y[kSB][16];
+  #pragma unroll
+      for (int j = 0; j < kSB; ++j) {
+        if (q0 + j < S) {
+          const float* src = a.kpart + ((grp * S + q0 + j) * 4 + w) * 1024 + l;
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) y[j][i] = __hip_atomic_load(src + i * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
+  #pragma unroll
+      for (int j = 0; j < kSB; ++j)
+        if (q0 + j < S) {
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] += y[j][i];
+        }
     }
-#pragma unroll
-    for (int j = 0; j < kSB; ++j)
-      if (q0 + j < S) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] += y[j][i];
-      }
+    const int gm = m0 + l;
+    if (gm >= a.M) return;
+    proj_store<EPI>(a, b, gm, x, ein);
   }
-  const int gm = m0 + l;
-  if (gm >= a.M) return;
-  proj_store<EPI>(a, b, gm, x, ein);
 }
 
 // WALK: the row outputs are published with a release increment of an arrival
@@ -1297,6 +1378,10 @@ glance_status launch_head_pack(const void* w, int N, int K, void* w_packed, hipS
 #ifndef GLANCE_PROJ_MINBPG
 #define GLANCE_PROJ_MINBPG 3
 #endif
+// 64-row tiles per work-group of the q/k/v projection above 64 rows (1, 2 or 4)
+#ifndef GLANCE_PROJ_QKV_TILES
+#define GLANCE_PROJ_QKV_TILES 2
+#endif
 // Work-groups of a projection: NGr groups of bpg 16-row blocks times S K-slices
 // (S a divisor of half the chunk count, so each slice is an even number of
 // chunks).  The most work-groups up to about one per CU, from groups of four
@@ -1326,7 +1411,8 @@ int proj_blocks(const GemmArgs& a) {
 }
 
 size_t proj_part_floats(int M, int NB, int K) {
-  const int nMT = (M + kTileM - 1) / kTileM;
+  // tiles of 64 rows, rounded up to a multiple of the most tiles a work-group takes
+  const int nMT = ((M + kTileM - 1) / kTileM + 3) / 4 * 4;
   const ProjGrid pg = proj_grid(K, NB);
   return static_cast<size_t>(nMT) * pg.NGr * pg.S * 4 * 1024;
 }
@@ -1363,6 +1449,32 @@ glance_status launch_gemm_bf16(const GemmArgs& a, hipStream_t st) {
     const int NB = proj_blocks(a);
     const ProjGrid pg = proj_grid(a.K, NB);
     const int NGr = pg.NGr, S = pg.S, bpg = pg.bpg;
+    // more than 64 rows with K split: several 64-row tiles per work-group (four
+    // for the q/k/v projection, two for the fp32-input output projection), a
+    // ring of 4 chunks (2 when a slice has fewer)
+    const bool tiled = nMT >= 2 && S > 1 &&
+                       ((a.epi == EPI_QKV && GLANCE_PROJ_QKV_TILES > 1) || (a.epi == EPI_RESID && a.x_f32));
+    if (tiled) {
+      const int nckt = a.K / S / kKc;
+      const bool r4 = nckt % 4 == 0;
+      const int mtt = (a.epi == EPI_QKV && nMT >= 4 && GLANCE_PROJ_QKV_TILES == 4) ? 4 : 2;
+      const int nMTg = (nMT + mtt - 1) / mtt;
+      const int gridt = ((NGr + 7) / 8) * 8 * S * nMTg;
+      if (a.epi == EPI_QKV) {
+        if (mtt == 4) {
+          if (r4) proj_bf16_kernel<EPI_QKV, 3, false, 1, 4><<<gridt, kGThreads, 0, st>>>(a, NB, NGr, S, nMTg, bpg);
+          else proj_bf16_kernel<EPI_QKV, 1, false, 1, 4><<<gridt, kGThreads, 0, st>>>(a, NB, NGr, S, nMTg, bpg);
+        } else {
+          if (r4) proj_bf16_kernel<EPI_QKV, 3, false, 1, 2><<<gridt, kGThreads, 0, st>>>(a, NB, NGr, S, nMTg, bpg);
+          else proj_bf16_kernel<EPI_QKV, 1, false, 1, 2><<<gridt, kGThreads, 0, st>>>(a, NB, NGr, S, nMTg, bpg);
+        }
+      } else {
+        if (r4) proj_bf16_kernel<EPI_RESID, 3, true, 1, 2><<<gridt, kGThreads, 0, st>>>(a, NB, NGr, S, nMTg, bpg);
+        else proj_bf16_kernel<EPI_RESID, 1, true, 1, 2><<<gridt, kGThreads, 0, st>>>(a, NB, NGr, S, nMTg, bpg);
+      }
+      GLANCE_LAUNCH_CHECK();
+      return GLANCE_OK;
+    }
     const int grid = ((NGr + 7) / 8) * 8 * S * nMT;
     // at most one work-group per CU: eight waves splitting the slice in two
     // halves (two waves per SIMD); wider grids: four waves.  Ring depth: the
