@@ -10,7 +10,12 @@ import torch
 pytestmark = pytest.mark.gpu
 
 
+# mini_bf16 merges its attention splits inside the attention kernel (arrival
+# counters that must return to zero between replays); mini_bf16_ragged has 123
+# rows, so its projections and head take two 64-row tiles per work-group.
 @pytest.mark.parametrize("name,seed,packed,kw", [("mini_bf16_copy", 5, True, {}),
+                                                 ("mini_bf16", 6, True, dict(n_rounds=2, draft_scales=(3.0, 4.0))),
+                                                 ("mini_bf16_ragged", 8, True, dict(n_rounds=2)),
                                                  ("qwen8b_1layer", 2000, True, {}),
                                                  ("tiny", 7, False, dict(n_rounds=2))])
 def test_graph_replay_equals_eager(name, seed, packed, kw):
