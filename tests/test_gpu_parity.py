@@ -64,6 +64,13 @@ def test_mini_bf16_round(name, seed):
     _round_parity(gen_round(make_config(name), seed), 0)
 
 
+def test_eight_query_heads_per_kv_head():
+    """Eight query heads share one KV head (G = 8): 8 x 41 queries per round
+    and KV head, query blocks that straddle rows; two ragged rounds."""
+    cfg = make_config("mini_bf16_ragged", Hq=8, Hkv=1, d_model=512, nseq=2)
+    _round_parity(gen_round(cfg, 33), 0)
+
+
 @pytest.mark.parametrize("nseq,seed", [(4, 31), (7, 32)])
 def test_projection_row_tiles(nseq, seed):
     """More rows than one 64-row tile: the projections take several tiles per

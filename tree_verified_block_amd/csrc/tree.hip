@@ -618,12 +618,16 @@ __device__ __forceinline__ int select_pops(const float (*lq)[kLqRow], const int 
     st = isi ? new_st : st;
     n_score = isi ? w_score : n_score;
     n_par = isi ? p : n_par;
+    n_pop = i;
+    if (++i > N) break;  // (the offers and reads below serve only a next pop)
     const uint32_t k = okey(n_score + (isi ? q0 : nx_q));
     c_hi = (isp | isi) ? k : c_hi;
+    // the old log q is dead here: the next reads may load straight into its
+    // register (issued above this point, they would land in a temporary whose
+    // copy at the end of the iteration waits for them)
+    __builtin_amdgcn_sched_barrier(0);
     nx_q = lq[st >> 16][(st & 255) + 1];
     fqn = lq[min((st >> 16) + 1, L)][0];
-    n_pop = i;
-    if (++i > N) break;
     mh = wave_umax(c_hi);
   }
   const int n_depth = st >> 16;
