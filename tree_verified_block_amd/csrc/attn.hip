@@ -816,6 +816,52 @@ __global__ __launch_bounds__(kHD) void attn_combine_kernel(AttnArgs a, int nqb) 
   if (a.attn_out) a.attn_out[off] = o;
 }
 
+// The same merge with 16-byte loads: a work-group of 128 threads takes four
+// query heads of one row, a thread four consecutive dimensions (Hq % 4 == 0);
+// per element the arithmetic and its order are those of attn_combine_kernel.
+template <int NS>
+__global__ __launch_bounds__(128) void attn_combine4_kernel(AttnArgs a, int nqb) {
+  const int grow = blockIdx.x, tid = threadIdx.x;
+  const int qh = blockIdx.y * 4 + (tid >> 5), d0 = (tid & 31) * 4;
+  const int s = grow / a.n_rows, r = grow % a.n_rows;
+  const int G = a.Hq / a.Hkv;
+  const int h = qh / G, q = r * G + qh % G;
+  const size_t blk = (static_cast<size_t>(s) * a.Hkv + h) * nqb + q / kQW;
+  const float* rec = a.part + (blk * a.n_split * kQW + q % kQW) * kRec;
+  const size_t cs = static_cast<size_t>(kQW) * kRec;
+  float mm[NS], ll[NS];
+  float4 vv[NS];
+#pragma unroll
+  for (int c = 0; c < NS; ++c) {
+    const float* rc = rec + min(c, a.n_split - 1) * cs;
+    const float2 ml = *reinterpret_cast<const float2*>(rc);
+    mm[c] = ml.x;
+    ll[c] = ml.y;
+    vv[c] = *reinterpret_cast<const float4*>(rc + 4 + d0);
+  }
+  const bool live = a.token[grow] >= 0;
+  float M = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < NS; ++c) M = fmaxf(M, c < a.n_split ? mm[c] : -INFINITY);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int c = 0; c < NS; ++c) {
+    const float f = (c >= a.n_split || mm[c] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mm[c] - M);
+    L += ll[c] * f;
+    acc.x += vv[c].x * f;
+    acc.y += vv[c].y * f;
+    acc.z += vv[c].z * f;
+    acc.w += vv[c].w * f;
+  }
+  const bool ok = live && L > 0.f;
+  const float4 o = make_float4(ok ? acc.x / L : 0.f, ok ? acc.y / L : 0.f, ok ? acc.z / L : 0.f,
+                               ok ? acc.w / L : 0.f);
+  const size_t off = static_cast<size_t>(grow) * a.Hq * kHD + qh * kHD + d0;
+  *reinterpret_cast<float4*>(a.attn_x + off) = o;
+  if (a.attn_out) *reinterpret_cast<float4*>(a.attn_out + off) = o;
+}
+
 // ------------------------------------------------------------------ fp32 path
 constexpr int kF32MaxKeys = 8192 + GLANCE_MAX_ROWS;
 
@@ -1023,13 +1069,23 @@ glance_status launch_tree_attention(const AttnArgs& a, hipStream_t st) {
     }
     GLANCE_LAUNCH_CHECK();
     if (a.n_split > 1) {
-      const dim3 cg(a.nseq * a.n_rows, a.Hq);
-      if (a.n_split <= 4)
-        attn_combine_kernel<4><<<cg, kHD, 0, st>>>(a, nqb);
-      else if (a.n_split <= 8)
-        attn_combine_kernel<8><<<cg, kHD, 0, st>>>(a, nqb);
-      else
-        attn_combine_kernel<kMaxSplit><<<cg, kHD, 0, st>>>(a, nqb);
+      if (a.Hq % 4 == 0) {
+        const dim3 cg(a.nseq * a.n_rows, a.Hq / 4);
+        if (a.n_split <= 4)
+          attn_combine4_kernel<4><<<cg, 128, 0, st>>>(a, nqb);
+        else if (a.n_split <= 8)
+          attn_combine4_kernel<8><<<cg, 128, 0, st>>>(a, nqb);
+        else
+          attn_combine4_kernel<kMaxSplit><<<cg, 128, 0, st>>>(a, nqb);
+      } else {
+        const dim3 cg(a.nseq * a.n_rows, a.Hq);
+        if (a.n_split <= 4)
+          attn_combine_kernel<4><<<cg, kHD, 0, st>>>(a, nqb);
+        else if (a.n_split <= 8)
+          attn_combine_kernel<8><<<cg, kHD, 0, st>>>(a, nqb);
+        else
+          attn_combine_kernel<kMaxSplit><<<cg, kHD, 0, st>>>(a, nqb);
+      }
       GLANCE_LAUNCH_CHECK();
     }
   } else {
