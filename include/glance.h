@@ -184,7 +184,11 @@ glance_status glance_build_tree_shared(const void* draft_logits, int32_t dtype,
  *   layer        weights and prefix cache of this layer (struct below)
  *   embed        [V][d_model] dtype or NULL.  If not NULL the layer input of row
  *                i is embed[token[i]] (first layer) and h_in is ignored.
- *   token        [nseq*n_rows] int32 (tree output; -1 marks a padding row)
+ *   token        [nseq*n_rows] int32 (tree output; -1 marks a padding row).
+ *                Every other value must lie in [0, V): with embed, row i reads
+ *                embed[token[i]] unchecked (V is not an argument), so the tree
+ *                outputs must hold a built tree, or at least every row marked
+ *                as padding, before this call
  *   h_in         [nseq*n_rows][d_model] dtype, or NULL when embed is given
  *   h_out        [nseq*n_rows][d_model] dtype; padding rows are written as 0
  *   kv_offsets   [nseq+1] int64: round s's prefix is cache rows
@@ -193,7 +197,7 @@ glance_status glance_build_tree_shared(const void* draft_logits, int32_t dtype,
  *   depth, anc   [nseq*n_rows] tree outputs
  *   rope_cos/sin [n_pos][D/2] float32 cos/sin of the rotary angles; they must
  *                cover every position P_s + depth (n_pos > max_prefix is checked;
- *                positions past the table are clamped to its last row)
+ *                positions outside the table are clamped into it)
  *   attn_out     [nseq*n_rows][Hq*D] float32 or NULL: concat_g(a_g) per row
  *   tree_k/v     [nseq*n_rows][Hkv][D] dtype or NULL: the rows' new cache
  *                entries (k after RoPE)

@@ -113,6 +113,33 @@ def test_attention_split_paths(prefix, seed):
             assert np.array_equal(np.asarray(again[k]), np.asarray(first[k])), k
 
 
+@pytest.mark.parametrize("prefix", [300, 600, 1500])
+@pytest.mark.parametrize("excess", [40.0, 200.0])
+def test_attention_score_far_above_first_block(prefix, excess):
+    """One prefix key (position 40, the second 32-key block of the first key
+    split) is set along the root row's first query head, so that its score for
+    that query lies `excess` (base-2 units) above every score of the split's
+    first block: the running maximum jumps by far more than the kernel's
+    rescaling threshold, and a weight taken against the old maximum would
+    overflow float32 at 200.  Every round output matches the oracle."""
+    from synth import bf16_bits, bf16_bits_to_f32
+    inp = gen_round(make_config("mini_bf16_copy", prefix=("fixed", prefix), n_rounds=1), 21)
+    cfg = inp["cfg"]
+    probe = mdl.TargetModel(inp)
+    root = int(inp["rounds"][0]["root"][0])
+    q, _, _ = probe.project(0, probe.embed_rows([root]), np.array([prefix]))
+    qh = q[0, 0]
+    K, _ = probe.prefix_kv(0, 0)
+    to_log2 = np.log2(np.e) / np.sqrt(cfg.D)
+    first = float((K[:32, 0, :] @ qh).max()) * to_log2
+    key = (first + excess) / to_log2 * qh / float(qh @ qh)
+    kc = inp["layers"][0]["k_cache"]
+    kc[int(inp["kv_offsets"][0]) + 40, 0] = bf16_bits(key.astype(np.float32))
+    planted = float(bf16_bits_to_f32(kc[int(inp["kv_offsets"][0]) + 40, 0]) @ qh) * to_log2
+    assert planted - first > excess - 1.0
+    _round_parity(inp, 0)
+
+
 def test_mini_given_topology_multilayer():
     """Random prefix-closed topology (no draft), three stacked layers."""
     cfg = make_config("mini_bf16_ragged", draft="topology", n_layers=3, nseq=2, N=63, L=15)

@@ -25,6 +25,8 @@ def _run(drafts, dtype, roots, w, B, n_max, tau=float("-inf")):
     from tree_verified_block_amd import api
     nseq, L, V = drafts.shape
     out = api.tree_outputs(nseq, n_max, "cuda")
+    for v in out.values():
+        v.fill_(7)  # a value the kernel must overwrite everywhere
     ws = api.workspace(api.build_tree_ws_bytes(nseq, L, V, n_max), "cuda")
     wd = w if torch.is_tensor(w) else torch.tensor(np.asarray(w, np.float32), device="cuda")
     api.glance_build_tree_shared(_device_draft(drafts, dtype),

@@ -55,14 +55,16 @@ def build_tree_flags(ws: torch.Tensor, nseq: int, L: int, V: int, N: int) -> int
 
 
 def tree_outputs(nseq: int, N: int, device) -> dict:
+    """The tree outputs, allocated as an empty tree (every row padding), so that
+    a layer call before the first tree build reads only valid tokens."""
     R = N + 1
     return {
-        "parent": torch.empty((nseq, R), dtype=torch.int32, device=device),
-        "depth": torch.empty((nseq, R), dtype=torch.int32, device=device),
-        "token": torch.empty((nseq, R), dtype=torch.int32, device=device),
-        "anc": torch.empty((nseq, R), dtype=torch.int64, device=device),
-        "score": torch.empty((nseq, R), dtype=torch.float32, device=device),
-        "n_valid": torch.empty((nseq,), dtype=torch.int32, device=device),
+        "parent": torch.full((nseq, R), -1, dtype=torch.int32, device=device),
+        "depth": torch.zeros((nseq, R), dtype=torch.int32, device=device),
+        "token": torch.full((nseq, R), -1, dtype=torch.int32, device=device),
+        "anc": torch.zeros((nseq, R), dtype=torch.int64, device=device),
+        "score": torch.zeros((nseq, R), dtype=torch.float32, device=device),
+        "n_valid": torch.zeros((nseq,), dtype=torch.int32, device=device),
     }
 
 

@@ -60,7 +60,7 @@ constexpr int kMaxSplit = 16;
 // position P + depth of a row, clamped into the cos/sin tables
 __device__ __forceinline__ int row_pos(const AttnArgs& a, int P, int row) {
   const int p = P + a.depth[row];
-  return p < a.n_pos - 1 ? p : a.n_pos - 1;
+  return p < 0 ? 0 : (p < a.n_pos - 1 ? p : a.n_pos - 1);
 }
 
 // Prefix length of round s, read as at most max_prefix keys.

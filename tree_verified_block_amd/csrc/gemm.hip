@@ -597,7 +597,7 @@ __device__ __forceinline__ int epi_key(const GemmArgs& a, int b, int gm) {
     if (b >= (a.Hq + a.Hkv) * 8) return -1;
     const int sq = gm / a.n_rows;
     const int pos = static_cast<int>(a.kv_offsets[sq + 1] - a.kv_offsets[sq]) + a.depth[gm];
-    return pos > a.n_pos - 1 ? a.n_pos - 1 : pos;
+    return pos < 0 ? 0 : (pos > a.n_pos - 1 ? a.n_pos - 1 : pos);
   } else if constexpr (EPI == EPI_RESID) {
     return a.resid_tok[gm];
   } else {

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kNormThreads) void qkv_finish_kernel(
     b *= r * bf16_to_f32(g[l + 64]);
     const int s = row / n_rows;
     int p = static_cast<int>(kv_offsets[s + 1] - kv_offsets[s]) + depth[row];
-    if (p > n_pos - 1) p = n_pos - 1;
+    p = p < 0 ? 0 : (p > n_pos - 1 ? n_pos - 1 : p);
     const float c = rope_cos[static_cast<size_t>(p) * 64 + l], sn = rope_sin[static_cast<size_t>(p) * 64 + l];
     const float ra = a * c - b * sn, rb = b * c + a * sn;
     const size_t o = head < Hq ? (static_cast<size_t>(row) * Hq + head) * 128
