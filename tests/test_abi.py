@@ -310,3 +310,15 @@ def test_binding_requires_built_library(tmp_path):
             _lib.load(str(tmp_path / "nope.so"))
         finally:
             _lib._lib = saved
+
+
+def test_tree_outputs_start_as_an_empty_tree():
+    """The binding allocates the tree outputs as a tree of padding rows, so that
+    a layer call made before any tree build (the layer gathers embed[token]
+    without a bound on the token) reads only the padding marker."""
+    from tree_verified_block_amd import api
+    out = api.tree_outputs(3, 7, "cpu")
+    assert set(out) == {"parent", "depth", "token", "anc", "score", "n_valid"}
+    assert out["token"].shape == (3, 8) and bool((out["token"] == -1).all())
+    assert bool((out["parent"] == -1).all()) and bool((out["depth"] == 0).all())
+    assert bool((out["anc"] == 0).all()) and bool((out["n_valid"] == 0).all())

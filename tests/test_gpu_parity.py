@@ -140,6 +140,22 @@ def test_attention_score_far_above_first_block(prefix, excess):
     _round_parity(inp, 0)
 
 
+@pytest.mark.parametrize("name", ["mini_bf16", "tiny"])
+def test_layer_before_any_tree_build(name):
+    """A round whose drafts are loaded but whose tree was never built: its tree
+    outputs are the binding's empty tree, so the attention layer sees only
+    padding rows and writes them as zeros."""
+    from tree_verified_block_amd.round import DeviceRound
+    inp = gen_round(make_config(name), 3)
+    dev = DeviceRound(inp, keep_layers=True)
+    dev.set_round(0)
+    dev.step_attn()
+    out = dev.fetch()
+    assert np.all(out["token"] == -1)
+    assert np.all(out["h_final"] == 0.0)
+    assert all(np.all(a == 0.0) for a in out["attn_out"])
+
+
 def test_mini_given_topology_multilayer():
     """Random prefix-closed topology (no draft), three stacked layers."""
     cfg = make_config("mini_bf16_ragged", draft="topology", n_layers=3, nseq=2, N=63, L=15)
