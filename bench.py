@@ -525,6 +525,23 @@ def main():
         one_step(i, head_ev=hev[i])
     torch.cuda.synchronize()
     head_us = float(np.mean([e[0].elapsed_time(e[1]) for e in hev]) * 1e3)
+    # the dominant kernel alone, the LM-head GEMM: the library records a pair of
+    # events on the launch stream right around it (glance_head_timing), in K
+    # further production rounds; the roofline line is taken from these
+    from tree_verified_block_amd import api
+    gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in gev:  # torch creates an event at its first record
+        e[0].record(stream)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    try:
+        for i in range(args.steps):
+            api.glance_head_timing(gev[i][0], gev[i][1])
+            one_step(i)
+    finally:
+        api.glance_head_timing(None, None)
+    torch.cuda.synchronize()
+    gemm_us = float(np.mean([e[0].elapsed_time(e[1]) for e in gev]) * 1e3)
 
     # per-step breakdown (events between all steps cost a few microseconds per
     # round of their own) and the per-round distribution (events between rounds)
@@ -581,7 +598,10 @@ def main():
         "hbm_frac": round(vb / (fused_us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)}
     total_bytes = sum(nbytes.values())
     ms = wall / args.steps * 1e3
-    head_gbs = nbytes["verify_head"] / (head_us * 1e-6) / 1e9
+    es = 2 if cfg.dtype == "bf16" else 4
+    R = cfg.nseq * (cfg.N + 1)
+    gemm_bytes = (cfg.V + R) * cfg.d_model * es  # head weights + activation rows
+    head_gbs = gemm_bytes / (gemm_us * 1e-6) / 1e9
     dist = None
     if rus is not None:
         dist = {"median": round(float(np.median(rus)), 2), "p10": round(float(np.percentile(rus, 10)), 2),
@@ -603,10 +623,13 @@ def main():
         "round_hbm_frac": round(total_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
         "round_bytes": total_bytes,
         "per_kernel": per_kernel,
-        "roofline": {"bound": "hbm", "kernel": "verify_head (LM-head GEMM + row merge)",
+        "roofline": {"bound": "hbm", "kernel": "LM-head GEMM ("
+                     + ("bf16, packed weights)" if packed else f"{cfg.dtype}, row-major weights)"),
                      "achieved": round(head_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(head_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": head_traffic(cfg)},
+                     "traffic": head_traffic(cfg), "kernel_us": round(gemm_us, 2),
+                     "algorithmic_bytes": gemm_bytes,
+                     "head_call_us": round(head_us, 2)},
     }
     del dev
     torch.cuda.empty_cache()

@@ -495,6 +495,18 @@ glance_status glance_commit_kv(const void* tree_k, const void* tree_v, int32_t d
 glance_status glance_advance_round(const int32_t* n_accept, const int32_t* out_tokens, int32_t nseq,
                                    int64_t* kv_offsets, int32_t* root_token, void* stream);
 
+/* glance_head_timing: a measurement hook for the LM-head GEMM, the kernel that
+ * streams the head weights in the verify-head calls above.  start and stop are
+ * hipEvent_t handles that the caller created (and keeps alive), or both NULL to
+ * stop.  While they are set, every verify-head call records start on its stream
+ * just before the head GEMM kernel and stop just after it (before the row merge
+ * and the walk), so that hipEventElapsedTime(start, stop) after the call is
+ * that kernel's duration.  The setting is process-wide and not synchronised:
+ * set it from the thread that makes the calls.  Errors: GLANCE_ERR_INVALID_ARG
+ * when exactly one of the two is NULL; a failed record makes the verify-head
+ * call return GLANCE_ERR_HIP. */
+glance_status glance_head_timing(void* start, void* stop);
+
 /* ------------------------------------------------------------------ helpers -- */
 const char* glance_status_string(int32_t status); /* static text (host)       */
 const char* glance_last_error(void);              /* this thread's last error */

@@ -322,3 +322,10 @@ def test_tree_outputs_start_as_an_empty_tree():
     assert out["token"].shape == (3, 8) and bool((out["token"] == -1).all())
     assert bool((out["parent"] == -1).all()) and bool((out["depth"] == 0).all())
     assert bool((out["anc"] == 0).all()) and bool((out["n_valid"] == 0).all())
+
+
+def test_head_timing_rejects_a_single_event(lib):
+    p = ctypes.c_void_p(64)
+    assert lib.glance_head_timing(p, None) == -1
+    assert lib.glance_head_timing(None, p) == -1
+    assert lib.glance_head_timing(None, None) == 0

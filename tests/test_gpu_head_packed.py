@@ -205,3 +205,43 @@ def test_fused_walk_equals_head_then_walk(name, seed, kw, T):
     for got in outs[1:]:
         for k in outs[0]:
             assert np.array_equal(np.asarray(got[k]), np.asarray(outs[0][k])), k
+
+
+def test_head_timing_events_bracket_the_gemm():
+    """glance_head_timing: the two events land around the head GEMM (a positive
+    span, shorter than the whole call with its row merge), recording changes no
+    output, and clearing the hook stops the recording."""
+    V, d, R = 4099, 512, 64
+    g = torch.Generator(device="cuda").manual_seed(5)
+    w = _bf16((V, d), 0.05, g)
+    h = _bf16((R, d), 1.0, g)
+    packed = api.glance_head_pack(w)
+    st = torch.cuda.current_stream()
+    outs = []
+    for timed in (False, True, False):
+        o = {k: torch.empty(R, dtype=torch.float32, device="cuda") for k in ("top1", "gap", "H")}
+        o["am"] = torch.empty(R, dtype=torch.int32, device="cuda")
+        ws = api.workspace(api.verify_head_ws_bytes(R, V, d, 1), "cuda")
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for e in ev:
+            e.record(st)
+        torch.cuda.synchronize()
+        if timed:
+            api.glance_head_timing(ev[1], ev[2])
+        ev[0].record(st)
+        try:
+            api.glance_verify_head_packed(h, packed, V, o["am"], o["top1"], o["gap"], o["H"], ws)
+        finally:
+            api.glance_head_timing(None, None)
+        ev[3].record(st)
+        torch.cuda.synchronize()
+        if timed:
+            inner, outer = ev[1].elapsed_time(ev[2]), ev[0].elapsed_time(ev[3])
+            assert 0.0 < inner < outer
+            assert ev[0].elapsed_time(ev[1]) >= 0.0 and ev[2].elapsed_time(ev[3]) > 0.0
+        else:
+            # untimed: the events were recorded before the call only
+            assert ev[1].elapsed_time(ev[0]) >= 0.0
+        outs.append({k: v.cpu().numpy() for k, v in o.items()})
+    for k in outs[0]:
+        assert np.array_equal(outs[0][k], outs[1][k]) and np.array_equal(outs[0][k], outs[2][k]), k

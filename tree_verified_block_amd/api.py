@@ -246,6 +246,19 @@ def glance_verify_head_packed_noalloc(h, w_packed, V, argmax, top1, gap, entropy
 
 
 # ---------------------------------------------------------------------- step 5
+def glance_head_timing(start=None, stop=None):
+    """Record two torch.cuda.Event objects around the LM-head GEMM of every later
+    verify-head call (both None: stop recording)."""
+    if (start is None) != (stop is None):
+        raise ValueError("start and stop must both be events or both be None")
+    if start is None:
+        _lib.call("glance_head_timing", None, None)
+        return
+    if not start.cuda_event or not stop.cuda_event:
+        raise ValueError("record each event once before handing it over (torch creates it lazily)")
+    _lib.call("glance_head_timing", ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event))
+
+
 def glance_accept_walk(parent, token, n_valid, argmax, gap, nseq, n_rows, L, gap_flag,
                        n_accept, out_tokens, path_rows, flagged, stream=None):
     _lib.call("glance_accept_walk", _ptr(parent), _ptr(token), _ptr(n_valid), _ptr(argmax),

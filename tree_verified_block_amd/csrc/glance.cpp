@@ -749,6 +749,17 @@ size_t glance_verify_head_ws(int32_t R, int32_t V, int32_t d_model, int32_t dtyp
   return round256(static_cast<size_t>(R) * V * sizeof(float));
 }
 
+// Events of glance_head_timing (process-wide; null: not recorded).
+static hipEvent_t g_head_ev_start = nullptr;
+static hipEvent_t g_head_ev_stop = nullptr;
+
+// One of the timing events on the head GEMM's stream, when the hook is set.
+static glance_status head_event(hipEvent_t ev, hipStream_t hs) {
+  if (!ev) return GLANCE_OK;
+  const hipError_t e = hipEventRecord(ev, hs);
+  return e == hipSuccess ? GLANCE_OK : hip_fail(e);
+}
+
 static glance_status verify_head(const void* h, const void* w_head, const void* w_packed,
                                  int32_t dtype, int32_t R, int32_t d_model, int32_t V,
                                  int32_t* argmax, float* top1, float* gap, float* entropy,
@@ -799,7 +810,10 @@ static glance_status verify_head(const void* h, const void* w_head, const void* 
       g.rnd_hi = dr.rnd_hi;
       dr.spart = g.spart;
     }
-    st = launch_gemm_bf16(g, hs);
+    const hipEvent_t e0 = g_head_ev_start, e1 = g_head_ev_stop;
+    st = head_event(e0, hs);
+    if (st == GLANCE_OK) st = launch_gemm_bf16(g, hs);
+    if (st == GLANCE_OK) st = head_event(e1, hs);
     if (st != GLANCE_OK) return st;
     if (wk) {
       unsigned* arrivals = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + need - 256);
@@ -809,7 +823,10 @@ static glance_status verify_head(const void* h, const void* w_head, const void* 
     return launch_head_merge(g.part, parts, R, argmax, top1, gap, entropy, dr, hs);
   }
   g.logits = logits ? logits : static_cast<float*>(ws);
-  st = launch_gemm_f32(g, hs);
+  const hipEvent_t e0 = g_head_ev_start, e1 = g_head_ev_stop;
+  st = head_event(e0, hs);
+  if (st == GLANCE_OK) st = launch_gemm_f32(g, hs);
+  if (st == GLANCE_OK) st = head_event(e1, hs);
   if (st != GLANCE_OK) return st;
   return launch_head_rowstats_f32(g.logits, R, V, argmax, top1, gap, entropy, dr, hs);
 }
@@ -965,6 +982,14 @@ glance_status glance_verify_head_packed_noalloc(const void* h, const void* w_pac
   return glance_verify_head_packed(h, w_packed, R, d_model, V, temperature, seed, round_id, argmax,
                                    top1, gap, entropy, sample_tok, sample_gap, logits, scratch,
                                    kHeadScratchFloats * sizeof(float), stream);
+}
+
+glance_status glance_head_timing(void* start, void* stop) {
+  g_last_error.clear();
+  REQUIRE((start == nullptr) == (stop == nullptr), "start and stop must both be set or both be NULL");
+  g_head_ev_start = static_cast<hipEvent_t>(start);
+  g_head_ev_stop = static_cast<hipEvent_t>(stop);
+  return GLANCE_OK;
 }
 
 // ------------------------------------------------------------------- step 5
