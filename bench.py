@@ -149,7 +149,7 @@ def graph_replays(dev, drafts, K: int, warm: int = 3, dist: int = 0) -> dict:
 
 
 def config_leg(name: str, K: int, seed: int, model: dict | None = None, layer_copies: int = 0,
-               head_peak: bool = False) -> dict:
+               head_peak: bool = False, overrides: dict | None = None) -> dict:
     """Graph-replayed rounds of another workload (packed weights when bf16).
     ``model``: an 8B-shaped workload whose embedding, head and layer weights are
     reused (its prefix caches, drafts and trees are this config's own).
@@ -159,7 +159,7 @@ def config_leg(name: str, K: int, seed: int, model: dict | None = None, layer_co
     import torch
     from synth import gen_round, make_config
     from tree_verified_block_amd.round import DeviceRound, to_device
-    cfg = make_config(name)
+    cfg = make_config(name, **(overrides or {}))
     t0 = time.perf_counter()
     if layer_copies:
         inp = gen_round(cfg.replace(n_layers=1), seed, model=model)
@@ -421,6 +421,14 @@ def run_legs(args, model_inp) -> dict:
         legs[key] = config_leg(name, k, seed, **kw)
         print(f"[bench] leg {key}: {legs[key]['us_per_round']} us per round", file=sys.stderr,
               flush=True)
+    if "budget_sweep" in want:
+        # the single-layer 8B round at the pages' smaller node budgets (N = 63 is
+        # the headline), same weights, prefix and draft temperatures
+        for n in (15, 31, 47):
+            key = f"budget_N{n}"
+            legs[key] = config_leg("qwen8b_1layer", K, 2000, model=model_inp, overrides={"N": n})
+            print(f"[bench] leg {key}: {legs[key]['us_per_round']} us per round", file=sys.stderr,
+                  flush=True)
     return legs
 
 
@@ -452,7 +460,7 @@ def main():
                          "ragged batch of 8; the 36-layer stack takes a fifth); 0 skips them")
     ap.add_argument("--dist-rounds", type=int, default=200,
                     help="rounds timed one by one for the per-round distribution")
-    ap.add_argument("--legs", default="tiny_f32,copy_regime,ragged8,deep36",
+    ap.add_argument("--legs", default="tiny_f32,copy_regime,ragged8,deep36,budget_sweep",
                     help="which other workloads to run (comma-separated)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -663,6 +671,29 @@ def main():
                         "GB/s": round(2 * (1 << 30) / (copy_us * 1e-6) / 1e9, 1),
                         "frac_of_peak": round(2 * (1 << 30) / (copy_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     del a, b
+    torch.cuda.empty_cache()
+    # streaming read of 2 GiB with the head's own load kind (glance_read_probe,
+    # 2048 work-groups, median of 10 event-timed passes): the read bandwidth the
+    # box delivers, beside which the head GEMM's achieved figure is also given
+    from tree_verified_block_amd import api
+    rb = torch.empty(1 << 31, dtype=torch.uint8, device="cuda")
+    rb.zero_()
+    rout = torch.empty(2048, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        api.glance_read_probe(rb, rout, 2048)
+    re_ = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(10)]
+    for e in re_:
+        e[0].record(stream)
+        api.glance_read_probe(rb, rout, 2048)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    read_us = float(np.median([e[0].elapsed_time(e[1]) for e in re_])) * 1e3
+    read_gbs = (1 << 31) / (read_us * 1e-6) / 1e9
+    out["hbm_read_probe"] = {"kind": "streaming read, 2 GiB, 16-byte non-temporal loads (glance_read_probe)",
+                             "us": round(read_us, 1), "GB/s": round(read_gbs, 1),
+                             "frac_of_peak": round(read_gbs / HBM_PEAK_GBS, 4)}
+    out["roofline"]["frac_of_read_probe"] = round(out["roofline"]["achieved"] / read_gbs, 4)
+    del rb, rout
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)

@@ -507,6 +507,20 @@ glance_status glance_advance_round(const int32_t* n_accept, const int32_t* out_t
  * call return GLANCE_ERR_HIP. */
 glance_status glance_head_timing(void* start, void* stop);
 
+/* glance_read_probe: a calibration pass that measures the read bandwidth the
+ * device actually delivers to the load kind the LM head streams its weights
+ * with (16-byte non-temporal loads), the figure the head's achieved bandwidth
+ * is set against beside the nominal peak.  Every 16-byte word of
+ * buf[0, bytes) is read once by n_wg work-groups of 256 threads in a
+ * grid-stride loop; work-group w writes the XOR of every 32-bit word it read to
+ * out[w], so the XOR over out[0, n_wg) is the XOR of the whole buffer.
+ *   buf    device pointer; bytes a positive multiple of 16
+ *   n_wg   1 .. 65536;  out: n_wg uint32 (device)
+ * buf and out 16-byte aligned.
+ * Errors: GLANCE_ERR_INVALID_ARG (sizes, NULL), GLANCE_ERR_ALIGNMENT. */
+glance_status glance_read_probe(const void* buf, size_t bytes, int32_t n_wg, uint32_t* out,
+                                void* stream);
+
 /* ------------------------------------------------------------------ helpers -- */
 const char* glance_status_string(int32_t status); /* static text (host)       */
 const char* glance_last_error(void);              /* this thread's last error */

@@ -329,3 +329,15 @@ def test_head_timing_rejects_a_single_event(lib):
     assert lib.glance_head_timing(p, None) == -1
     assert lib.glance_head_timing(None, p) == -1
     assert lib.glance_head_timing(None, None) == 0
+
+
+def test_read_probe_rejects_bad_arguments(lib):
+    p = ctypes.c_void_p(256)
+    assert lib.glance_read_probe(p, 0, 1, p, None) == -1
+    assert lib.glance_read_probe(p, 24, 1, p, None) == -1
+    assert lib.glance_read_probe(p, 32, 0, p, None) == -1
+    assert lib.glance_read_probe(p, 32, 65537, p, None) == -1
+    assert lib.glance_read_probe(None, 32, 1, p, None) == -1
+    assert lib.glance_read_probe(p, 32, 1, None, None) == -1
+    assert lib.glance_read_probe(ctypes.c_void_p(264), 32, 1, p, None) == -2
+

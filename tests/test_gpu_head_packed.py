@@ -245,3 +245,19 @@ def test_head_timing_events_bracket_the_gemm():
         outs.append({k: v.cpu().numpy() for k, v in o.items()})
     for k in outs[0]:
         assert np.array_equal(outs[0][k], outs[1][k]) and np.array_equal(outs[0][k], outs[2][k]), k
+
+
+@pytest.mark.parametrize("nbytes,n_wg", [(16, 1), (4096 + 48, 3), (1 << 22, 257)])
+def test_read_probe_reads_every_word(nbytes, n_wg):
+    """glance_read_probe reads each 16-byte word once: the XOR of the
+    work-groups' words is the XOR of the whole buffer (ragged last step and
+    grids larger than the buffer included)."""
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).cuda()
+    out = torch.zeros(n_wg, dtype=torch.int32, device="cuda")
+    api.glance_read_probe(buf, out, n_wg)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(host)
+

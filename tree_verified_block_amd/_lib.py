@@ -78,6 +78,7 @@ SIGNATURES = {
     "glance_commit_kv": (_I, [_P, _P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _I64, _P]),
     "glance_advance_round": (_I, [_P, _P, _I, _P, _P, _P]),
     "glance_head_timing": (_I, [_P, _P]),
+    "glance_read_probe": (_I, [_P, _SZ, _I, _P, _P]),
     "glance_status_string": (ctypes.c_char_p, [_I]),
     "glance_last_error": (ctypes.c_char_p, []),
     "glance_abi_version": (_I, []),

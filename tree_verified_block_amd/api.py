@@ -246,6 +246,12 @@ def glance_verify_head_packed_noalloc(h, w_packed, V, argmax, top1, gap, entropy
 
 
 # ---------------------------------------------------------------------- step 5
+def glance_read_probe(buf, out, n_wg: int, stream=None):
+    """One calibration read of every byte of ``buf`` (XOR per work-group into ``out``)."""
+    _lib.call("glance_read_probe", _ptr(buf), buf.numel() * buf.element_size(), n_wg, _ptr(out),
+              _stream(stream))
+
+
 def glance_head_timing(start=None, stop=None):
     """Record two torch.cuda.Event objects around the LM-head GEMM of every later
     verify-head call (both None: stop recording)."""

@@ -984,6 +984,16 @@ glance_status glance_verify_head_packed_noalloc(const void* h, const void* w_pac
                                    kHeadScratchFloats * sizeof(float), stream);
 }
 
+glance_status glance_read_probe(const void* buf, size_t bytes, int32_t n_wg, uint32_t* out,
+                                void* stream) {
+  g_last_error.clear();
+  REQUIRE(bytes >= 16 && bytes % 16 == 0, "bytes = %zu is not a positive multiple of 16", bytes);
+  REQUIRE(n_wg >= 1 && n_wg <= 65536, "n_wg = %d outside [1, 65536]", n_wg);
+  REQUIRE_PTR(buf);
+  REQUIRE_PTR(out);
+  return launch_read_probe(buf, bytes, n_wg, out, static_cast<hipStream_t>(stream));
+}
+
 glance_status glance_head_timing(void* start, void* stop) {
   g_last_error.clear();
   REQUIRE((start == nullptr) == (stop == nullptr), "start and stop must both be set or both be NULL");

@@ -192,5 +192,7 @@ glance_status launch_commit_kv(const void* tree_k, const void* tree_v, const int
                                hipStream_t st);
 glance_status launch_advance_round(const int32_t* n_accept, const int32_t* out_tokens,
                                    int64_t* kv_offsets, int32_t* root, hipStream_t st);
+glance_status launch_read_probe(const void* buf, size_t bytes, int n_wg, uint32_t* out,
+                                hipStream_t st);
 
 }  // namespace glance

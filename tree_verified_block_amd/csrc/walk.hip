@@ -74,6 +74,40 @@ glance_status launch_advance_round(const int32_t* n_accept, const int32_t* out_t
   return GLANCE_OK;
 }
 
+// Read-bandwidth calibration: a grid-stride pass over n16 16-byte words with
+// the LM head's non-temporal loads, four words per thread in flight per step
+// (an index past the end re-reads the last word and adds nothing), the XOR of
+// each work-group's words into out[work-group].
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ p, size_t n16,
+                                                         uint32_t* __restrict__ out) {
+  constexpr int U = 4;
+  const size_t stride = static_cast<size_t>(gridDim.x) * 256 * U;
+  uint32_t acc = 0;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * 256 * U + threadIdx.x; i < n16; i += stride) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t k = i + static_cast<size_t>(u) * 256;
+      v[u] = load_stream(p + (k < n16 ? k : n16 - 1));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i + static_cast<size_t>(u) * 256 < n16) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  __shared__ uint32_t red[256 / kWave];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc ^= static_cast<uint32_t>(__shfl_xor(static_cast<int>(acc), off, kWave));
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+glance_status launch_read_probe(const void* buf, size_t bytes, int n_wg, uint32_t* out, hipStream_t st) {
+  read_probe_kernel<<<n_wg, 256, 0, st>>>(static_cast<const uint4*>(buf), bytes / 16, out);
+  GLANCE_LAUNCH_CHECK();
+  return GLANCE_OK;
+}
+
 glance_status launch_accept_walk(const int32_t* parent, const int32_t* token,
                                  const int32_t* n_valid, const int32_t* argmax,
                                  const float* gap, int nseq, int n_rows, int L, float gap_flag,
