@@ -22,19 +22,19 @@
 //                   registers: each lane already holds, for its query, the keys
 //                   that the MFMA B operand wants from it, provided the V^T tile
 //                   stores the keys in that order (the slot permutation below).
-// Default kernel (tree_attn_tile_kernel): the four waves of a work-group own
-// four consecutive query blocks of one head and one key split, and share each
+// Kernel (tree_attn_tile_kernel): the four (or two) waves of a work-group own
+// consecutive query blocks of one head and one key split, and share each
 // 32-key K / V^T tile, loaded once per work-group, two blocks ahead, into a
 // double-buffered LDS pair.  The number of splits fills the CUs once but keeps
-// every split at least 8 blocks long, since each split costs a 528-byte record
-// (max, sum, O) per query; attn_combine_kernel merges the records in split
-// order.  Work-group ids put the query groups and splits of one KV head on the
-// same XCD (id mod 8 = h when Hkv = 8), so the head's K/V cross HBM once and
-// are shared through that XCD's L2.  The older per-wave kernel (each wave its
-// own key range and tiles, the four waves merged in LDS) stays selectable at
-// build time.  The output o = O / sum is written in fp32; the output projection
-// takes it as a bf16 pair too, so q, P and o all enter the products with ~16
-// significant bits.
+// every split at least GLANCE_ATTN_MINBLK blocks long, since each split costs
+// a 528-byte record (max, sum, O) per query; the split records are merged in
+// split order, by the last work-group of a query group to finish when the
+// records are few, else by attn_combine4_kernel (attn_combine_kernel when Hq
+// is not a multiple of 4).  Work-group ids put the query groups and splits of
+// one KV head on the same XCD (id mod 8 = h when Hkv = 8), so the head's K/V
+// cross HBM once and are shared through that XCD's L2.  The output o = O / sum
+// is written in fp32; the output projection takes it as a bf16 pair too, so
+// q, P and o all enter the products with ~16 significant bits.
 //
 // fp32 path (tiny shapes): one work-group per (row, query head), scores in LDS,
 // plain fp32 loops.
@@ -47,13 +47,10 @@ namespace glance {
 
 namespace {
 
-constexpr int kAW = 4;                // waves per work-group
-constexpr int kAThreads = kAW * kWave;
 constexpr int kQW = 32;               // queries per work-group
 constexpr int kKB = 32;               // keys per block
 constexpr int kHD = 128;              // head_dim of the bf16 path
 constexpr int kVtRow = 40;            // bf16 slots per V^T row: 32 keys + 8 padding (80 bytes)
-constexpr int kObRow = kHD + 1;       // fp32 stride of the merge rows (odd: no bank conflicts)
 constexpr int kRec = kHD + 4;         // split record per query: m, l, -, -, o[128]
 constexpr int kMaxSplit = 16;
 
@@ -73,22 +70,6 @@ __device__ __forceinline__ int prefix_len(const AttnArgs& a, int s) {
 __device__ __forceinline__ float rope_pair(const float* x, int i, int half, float c, float s) {
   // rotate-half: (x_i, x_{i+half}) -> (x_i c - x_{i+half} s, x_{i+half} c + x_i s)
   return i < half ? x[i] * c - x[i + half] * s : x[i] * c + x[i - half] * s;
-}
-
-// Head-h row of key t of round s: prefix keys from the cache, key P + i from
-// tree row i; keys at or past T (the tail of a wave's last block) read tree row 0
-// of the round, which is in bounds, and are masked.
-// Both candidate rows are formed and one is picked with a mask: a branch here
-// would keep the loads from unrolling and make their wait counts conservative.
-__device__ __forceinline__ const uint16_t* key_row(const uint16_t* cache, const uint16_t* tree,
-                                                   int64_t kv0, int P, int T, int s, int n_rows,
-                                                   int Hkv, int h, int t) {
-  const bool pre = t < P;
-  const int i = (t < T && !pre) ? t - P : 0;
-  const uintptr_t pc = reinterpret_cast<uintptr_t>(cache + ((kv0 + t) * Hkv + h) * kHD);
-  const uintptr_t pt = reinterpret_cast<uintptr_t>(tree + ((static_cast<int64_t>(s) * n_rows + i) * Hkv + h) * kHD);
-  const uintptr_t m = pre ? ~static_cast<uintptr_t>(0) : 0;
-  return reinterpret_cast<const uint16_t*>((pc & m) | (pt & ~m));
 }
 
 // Visibility of keys t0 .. t0 + 31 to a query whose row has ancestor word anc:
@@ -129,302 +110,22 @@ __device__ __forceinline__ int slot_quad(int kq) {
   return (kq & 4) | ((kq & 1) << 1) | ((kq >> 1) & 1);
 }
 
-__device__ __forceinline__ uint32_t half16(uint32_t w, int hi) { return hi ? (w >> 16) : (w & 0xFFFFu); }
-
 // One of the two bf16 halves of a pair of 32-bit words: the low (sel = 0x05040100)
 // or high (0x07060302) 16 bits of a, then of b, packed into one word.
 __device__ __forceinline__ uint32_t pick16(uint32_t a, uint32_t b, uint32_t sel) {
   return __builtin_amdgcn_perm(b, a, sel);
 }
 
-__global__ __launch_bounds__(kAThreads, 1) void tree_attn_bf16_kernel(AttnArgs a, int nqb) {
-  // LDS: each wave's K / V^T tile, later reused for the merge of the 4 waves
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kAW][kHD * kVtRow];
-  __shared__ float Ms[kAW][kQW], Ls[kAW][kQW];
-  static_assert(2 * kQW * kObRow * sizeof(float) <= sizeof(Vt), "merge buffers alias the tiles");
-
-  const int Hkv = a.Hkv;
-  int id = blockIdx.x;
-  const int h = id % Hkv;
-  id /= Hkv;
-  const int qb = id % nqb;
-  id /= nqb;
-  const int c = id % a.n_split;
-  const int s = id / a.n_split;
-  // w is read from lane 0 so that the compiler knows it (and each wave's key
-  // range, block count and offsets) is uniform: branches on them stay scalar
-  const int tid = threadIdx.x, l = tid & 63, j = l & 31, g = l >> 5;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = a.Hq / Hkv;
-  const int Qn = a.n_rows * G;
-
-  // ---- this lane's query: q as bf16 + remainder, the B operand of S^T (step
-  // ks: dims 64 g + 8 ks .. + 7), in registers for the whole range (queries past
-  // Qn read row 0 of the round and are never stored)
-  const int q = qb * kQW + j;
-  const bool qvalid = q < Qn;
-  const int grow = s * a.n_rows + (qvalid ? q / G : 0);
-  const uint64_t qanc = qvalid ? a.anc[grow] : 0ull;
-  bf16x8 qhi[8], qlo[8];
-  {
-    const size_t qoff = (static_cast<size_t>(grow) * a.Hq + h * G + (qvalid ? q % G : 0)) * kHD + 64 * g;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qoff;
-    const uint16_t* qlp = static_cast<const uint16_t*>(a.q_lo) + qoff;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      qhi[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 8 * ks));
-      qlo[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qlp + 8 * ks));
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // query loads done before the K/V stream starts
-  const int64_t kv0 = a.kv_offsets[s];
-  const int P = prefix_len(a, s);
-  const int T = P + a.n_rows;
-  // this wave's keys: range c * 4 + w of n_split * 4, in whole blocks
-  const int span = a.n_split * kAW;
-  const int per = ((T + span - 1) / span + kKB - 1) / kKB * kKB;
-  const int t_beg = (c * kAW + w) * per;
-  const int t_end = min(t_beg + per, T);
-  const int nblk = t_end > t_beg ? (t_end - t_beg + kKB - 1) / kKB : 0;
-
-  // ---- key t's head-h row: prefix key t at kc0 + t * ks, tree row i (key P + i)
-  // at tk0 + i * ks (tree rows have the cache's row stride); keys at or past T
-  // read tree row 0 (in bounds, masked).  32-bit element offsets from two bases.
-  const int kstr = Hkv * kHD;
-  const uint16_t* kc0 = static_cast<const uint16_t*>(a.k_cache) + (kv0 * Hkv + h) * kHD;
-  const uint16_t* vc0 = static_cast<const uint16_t*>(a.v_cache) + (kv0 * Hkv + h) * kHD;
-  const size_t trow0 = (static_cast<size_t>(s) * a.n_rows * Hkv + h) * kHD;
-  const uint16_t* tk0 = static_cast<const uint16_t*>(a.tree_k) + trow0;
-  const uint16_t* tv0 = static_cast<const uint16_t*>(a.tree_v) + trow0;
-  auto row_of = [&](const uint16_t* c0, const uint16_t* t0p, int t) {
-    const bool pre = t < P;
-    const int i = (t < T && !pre) ? t - P : 0;
-    return (pre ? c0 : t0p) + (pre ? t : i) * kstr;
-  };
-  const int vx = l & 15, vkq = l >> 4;  // V pieces: dims 8 vx .. + 7 of key quads vkq, vkq + 4
-  // K and V of the block starting at t0 are loaded the same way: instruction i
-  // reads four whole key rows (K: lane l takes key 4 i + l / 16, 16-byte piece
-  // l % 16; V: key 4 (vkq + 4 (i / 4)) + i % 4, piece vx), full cache lines.
-#define GLANCE_LOAD_KV(t0_, kd_, vd_)                                                           \
-  _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                \
-    kd_[i] = *reinterpret_cast<const u32x4*>(row_of(kc0, tk0, (t0_) + 4 * i + (l >> 4)) + 8 * (l & 15)); \
-    vd_[i] = *reinterpret_cast<const u32x4*>(                                                    \
-        row_of(vc0, tv0, (t0_) + 4 * (vkq + 4 * (i >> 2)) + (i & 3)) + 8 * vx);                   \
-  }
-  // The wave's LDS buffer holds the block's K tile, then its V^T tile.  K tile:
-  // key k's row at k * 128, its 16-byte piece p at unit p ^ (k mod 8), so that
-  // the MFMA operand reads (lane (j, g): key j, piece 8 g + ks) of eight
-  // consecutive keys fall in distinct banks.
-  uint16_t* vt = Vt[w];
-#define GLANCE_WRITE_K(src_)                                                                    \
-  _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                 \
-    const int k = 4 * i + (l >> 4);                                                               \
-    *reinterpret_cast<u32x4*>(vt + k * kHD + 8 * ((l & 15) ^ (k & 7))) = src_[i];                 \
-  }
-  // V pieces -> V^T tile: dim 8 vx + e, the slot quad of the key quad, 4 keys
-  // (pieces 4 i .. 4 i + 3) per 8-byte write
-#define GLANCE_WRITE_VT(src_)                                                                   \
-  _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                                 \
-    const int sq = slot_quad(vkq + 4 * i) ^ (vx & 7);                                             \
-    _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                               \
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;                                   \
-      const uint32_t x0 = src_[4 * i][e >> 1], x1 = src_[4 * i + 1][e >> 1];                      \
-      const uint32_t x2 = src_[4 * i + 2][e >> 1], x3 = src_[4 * i + 3][e >> 1];                  \
-      *reinterpret_cast<uint2*>(vt + (8 * vx + e) * kVtRow + 4 * sq) =                            \
-          make_uint2(pick16(x0, x1, sel), pick16(x2, x3, sel));                                   \
-    }                                                                                             \
-  }
-
-  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(kHD));
-  f32x16 acc_o[4] = {};
-  // Online softmax with a lazily moved reference: p = 2^(s - m_ref) with m_ref
-  // raised (and O, l rescaled) only when a score exceeds it by more than 8, so
-  // p <= 2^8 (exact enough in fp32 and bf16 + remainder) and the rescale is rare.
-  float m_ref = -INFINITY, l_run = 0.f;
-  // One block after the other with the next block's K and V loads in flight: the
-  // K registers are refilled as soon as the K tile is written, the V registers as
-  // soon as the V^T tile is.  Past the last block the loads re-read it (no
-  // conditional load).
-  u32x4 kr[8], vr[8];
-  const int tlast = t_beg + (nblk > 0 ? nblk - 1 : 0) * kKB;
-  GLANCE_LOAD_KV(t_beg, kr, vr)
-  for (int b = 0; b < nblk; ++b) {
-    const int t0 = t_beg + b * kKB;
-    const int tn = min(t0 + kKB, tlast);
-    GLANCE_WRITE_K(kr)
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) kr[i] = *reinterpret_cast<const u32x4*>(
-        row_of(kc0, tk0, tn + 4 * i + (l >> 4)) + 8 * (l & 15));
-    __builtin_amdgcn_sched_barrier(0);  // keeps the scheduler from sinking the loads
-    __builtin_amdgcn_wave_barrier();
-    // ---- S^T = K Q^T with q = hi + lo (A: key j, dims 64 g + 8 ks from the K
-    // tile; B: query j, the same dims, from the query rows), two accumulators
-    // (all eight operand reads first, then the products)
-    bf16x8 kop[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      kop[ks] = *reinterpret_cast<const bf16x8*>(vt + j * kHD + 8 * ((8 * g + ks) ^ (j & 7)));
-    f32x16 sa = {}, sb = {};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qhi[ks], sa, 0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qlo[ks], sb, 0, 0, 0);
-    }
-    // ---- mask (element v: key t0 + 8 (v / 4) + 4 g + v % 4, query j), block max
-    const uint32_t vm = block_mask(t0, t_end, P, qanc) >> (4 * g);
-    float sc[16], mb = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const bool vis = (vm >> (8 * (v >> 2) + (v & 3))) & 1u;
-      sc[v] = vis ? (sa[v] + sb[v]) * scale_log2 : -INFINITY;
-      mb = fmaxf(mb, sc[v]);
-    }
-    mb = fmaxf(mb, __shfl_xor(mb, 32, kWave));
-    const bool raise = mb > m_ref + 8.f;  // also when m_ref is still -inf
-    if (__ballot(raise) != 0ull) {  // (uniform) rare after the first block
-      const float m_new = raise ? mb : m_ref;
-      const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-      m_ref = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
-    }
-    const float mz = m_ref == -INFINITY ? 0.f : m_ref;  // nothing visible yet: every p is 0
-    // ---- P = hi + lo in bf16 (the remainder taken from the rounded value)
-    uint32_t ph[8], pl[8];
-#pragma unroll
-    for (int pr = 0; pr < 8; ++pr) {
-      const float p0 = __builtin_amdgcn_exp2f(sc[2 * pr] - mz);
-      const float p1 = __builtin_amdgcn_exp2f(sc[2 * pr + 1] - mz);
-      ph[pr] = pack_bf16x2(p0, p1);
-      pl[pr] = pack_bf16x2(p0 - __uint_as_float(ph[pr] << 16), p1 - __uint_as_float(ph[pr] & 0xFFFF0000u));
-      l_run += p0 + p1;
-    }
-    // the K tile's reads are done (LDS is in order per wave): the V^T tile takes
-    // the buffer, and the V registers take the next block's loads
-    __builtin_amdgcn_wave_barrier();
-    GLANCE_WRITE_VT(vr)
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) vr[i] = *reinterpret_cast<const u32x4*>(
-        row_of(vc0, tv0, tn + 4 * (vkq + 4 * (i >> 2)) + (i & 3)) + 8 * vx);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_wave_barrier();
-    // ---- O^T += V^T P^T, two 16-key steps, P = hi + lo (operand reads first)
-    bf16x8 vop[2][4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int dim = 32 * db + j;
-        const int sw = (dim >> 3) & 7;
-        const uint16_t* row = vt + dim * kVtRow;
-        const uint2 lo = *reinterpret_cast<const uint2*>(row + 4 * ((4 * t + 2 * g) ^ sw));
-        const uint2 hi = *reinterpret_cast<const uint2*>(row + 4 * ((4 * t + 2 * g + 1) ^ sw));
-        vop[t][db] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-      }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const bf16x8 bh = __builtin_bit_cast(bf16x8, make_uint4(ph[4 * t], ph[4 * t + 1], ph[4 * t + 2], ph[4 * t + 3]));
-      const bf16x8 bl = __builtin_bit_cast(bf16x8, make_uint4(pl[4 * t], pl[4 * t + 1], pl[4 * t + 2], pl[4 * t + 3]));
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t][db], bh, acc_o[db], 0, 0, 0);
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t][db], bl, acc_o[db], 0, 0, 0);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();  // reads of this block before the next block's writes
-  }
-#undef GLANCE_LOAD_KV
-#undef GLANCE_WRITE_K
-#undef GLANCE_WRITE_VT
-  const float m_run = m_ref;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
-
-  // ---- the four waves' (max, sum, O) merged in LDS, through two buffers that
-  // reuse the tiles: waves 2 and 3 hand their O to waves 0 and 1, which then
-  // leave their sums for all threads (thread (tq, 16 dims from d0))
-  if (g == 0) {
-    Ms[w][j] = m_run;
-    Ls[w][j] = l_tot;
-  }
-  __syncthreads();
-  float* ob = reinterpret_cast<float*>(&Vt[0][0]);
-  {
-    float M = Ms[0][j];
-#pragma unroll
-    for (int ww = 1; ww < kAW; ++ww) M = fmaxf(M, Ms[ww][j]);
-    const float f = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-    float* mine = ob + ((w & 1) * kQW + j) * kObRow;
-    if (w >= 2) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mine[32 * db + 8 * (v >> 2) + 4 * g + (v & 3)] = acc_o[db][v] * f;
-    }
-    __syncthreads();
-    if (w < 2) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          acc_o[db][v] = acc_o[db][v] * f + mine[32 * db + 8 * (v >> 2) + 4 * g + (v & 3)];
-    }
-    __syncthreads();
-    if (w < 2) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mine[32 * db + 8 * (v >> 2) + 4 * g + (v & 3)] = acc_o[db][v];
-    }
-    __syncthreads();
-  }
-  const int tq = tid >> 3, d0 = (tid & 7) * 16;
-  float M = Ms[0][tq];
-#pragma unroll
-  for (int ww = 1; ww < kAW; ++ww) M = fmaxf(M, Ms[ww][tq]);
-  float L = 0.f;
-#pragma unroll
-  for (int ww = 0; ww < kAW; ++ww)
-    L += Ms[ww][tq] == -INFINITY ? 0.f : Ls[ww][tq] * __builtin_amdgcn_exp2f(Ms[ww][tq] - M);
-  float o[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) o[i] = ob[tq * kObRow + d0 + i] + ob[(kQW + tq) * kObRow + d0 + i];
-  const int qq = qb * kQW + tq;
-  if (a.n_split > 1) {
-    // split record (m, l, O) of this work-group's queries; attn_combine merges
-    const size_t blk = (static_cast<size_t>(s) * Hkv + h) * nqb + qb;
-    float* rec = a.part + ((blk * a.n_split + c) * kQW + tq) * kRec;
-    if ((tid & 7) == 0) *reinterpret_cast<float2*>(rec) = make_float2(M, L);
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4)
-      *reinterpret_cast<float4*>(rec + 4 + d0 + 4 * k4) =
-          make_float4(o[4 * k4], o[4 * k4 + 1], o[4 * k4 + 2], o[4 * k4 + 3]);
-    return;
-  }
-  if (qq >= Qn) return;
-  const int rr = qq / G;
-  const int growq = s * a.n_rows + rr;
-  const bool live = a.token[growq] >= 0;
-  const float inv = (live && L > 0.f) ? 1.f / L : 0.f;
-  const size_t off = static_cast<size_t>(growq) * a.Hq * kHD + (h * G + qq % G) * kHD + d0;
-#pragma unroll
-  for (int k4 = 0; k4 < 4; ++k4) {
-    const float4 v = make_float4(o[4 * k4] * inv, o[4 * k4 + 1] * inv, o[4 * k4 + 2] * inv, o[4 * k4 + 3] * inv);
-    *reinterpret_cast<float4*>(a.attn_x + off + 4 * k4) = v;
-    if (a.attn_out) *reinterpret_cast<float4*>(a.attn_out + off + 4 * k4) = v;
-  }
-}
-
-// Shared-tile variant: the W waves of a work-group own W consecutive blocks of
-// 32 queries of one KV head and all keys of one key split.  Every 32-key block
-// is loaded once per work-group, cooperatively (threads below 128 take the V
-// pieces, the rest, or the same threads when W = 2, the K pieces), two blocks
-// ahead of its use, into a double-buffered pair of LDS tiles (K rows with the
-// XOR swizzle, V^T in the slot order of the P operand), and read by every wave.
-// One barrier per block.  Each wave then does the per-block work of the
-// per-wave kernel above for its own queries (S^T = K Q^T with q as a bf16 pair,
-// the lazy online softmax, P as a bf16 pair, O^T += V^T P^T) and, at the end,
-// writes its queries' split records (or, with one split, their outputs).
+// The W waves of a work-group own W consecutive blocks of 32 queries of one KV
+// head and all keys of one key split.  Every 32-key block is loaded once per
+// work-group, cooperatively (threads below 128 take the V pieces, the rest, or
+// the same threads when W = 2, the K pieces), two blocks ahead of its use, into
+// a double-buffered pair of LDS tiles (K rows with the XOR swizzle, V^T in the
+// slot order of the P operand), and read by every wave.  One barrier per block.
+// Each wave then does the per-block work for its own queries (S^T = K Q^T with
+// q as a bf16 pair, the lazy online softmax, P as a bf16 pair, O^T += V^T P^T)
+// and, at the end, writes its queries' split records (or, with one split, their
+// outputs).
 template <int W>
 __global__ __launch_bounds__(W * kWave, 1) void tree_attn_tile_kernel(AttnArgs a, int nqb, int fuse) {
   constexpr int KT = kKB * kHD;        // K tile (elements)
@@ -974,10 +675,6 @@ __global__ __launch_bounds__(128) void tree_attn_f32_kernel(AttnArgs a) {
 
 static int attn_qblocks(int n_rows, int Hq, int Hkv) { return (n_rows * (Hq / Hkv) + kQW - 1) / kQW; }
 
-// Shared-tile kernel (the default) or the per-wave kernel (GLANCE_ATTN_TILE=0).
-#ifndef GLANCE_ATTN_TILE
-#define GLANCE_ATTN_TILE 1
-#endif
 // Split policy: enough work-groups to fill the CUs once, but no split shorter
 // than GLANCE_ATTN_MINBLK blocks of 32 keys (each split adds a 528-byte record
 // per query and KV head).
@@ -1013,16 +710,6 @@ int tile_splits(int nseq, int64_t max_prefix, int nqb, int Hkv, int W) {
 // length), two-wave groups give twice the work-groups for the same splits.
 AttnPlan attn_plan(int nseq, int64_t max_prefix, int n_rows, int Hq, int Hkv) {
   const int nqb = attn_qblocks(n_rows, Hq, Hkv);
-  if (GLANCE_ATTN_TILE == 0) {
-    // per-wave kernel: fill the CUs once, and a split per 2048 keys
-    const int64_t base = static_cast<int64_t>(nseq) * Hkv * nqb;
-    const int64_t fill = (256 + base - 1) / base;
-    const int64_t len = (max_prefix + n_rows + 2047) / 2048;
-    int64_t n = fill > len ? fill : len;
-    if (n < 1) n = 1;
-    if (n > 8) n = 8;
-    return {4, static_cast<int>(n), false};
-  }
   const int64_t T = max_prefix + n_rows;
   const int n4 = tile_splits(nseq, T, nqb, Hkv, 4);
   const int64_t wg4 = static_cast<int64_t>(nseq) * Hkv * ((nqb + 3) / 4) * n4;
@@ -1051,23 +738,17 @@ size_t attn_part_floats(int nseq, int n_rows, int Hq, int Hkv, int n_split) {
 glance_status launch_tree_attention(const AttnArgs& a, hipStream_t st) {
   if (a.dtype == GLANCE_BF16) {
     const int nqb = attn_qblocks(a.n_rows, a.Hq, a.Hkv);
-    if (GLANCE_ATTN_TILE == 0) {
-      const int grid = a.nseq * a.n_split * nqb * a.Hkv;
-      tree_attn_bf16_kernel<<<grid, kAThreads, 0, st>>>(a, nqb);
-    } else {
-      // the plan that sized the workspace's split records
-      const AttnPlan pl = attn_plan(a.nseq, a.max_prefix, a.n_rows, a.Hq, a.Hkv);
-      if (pl.n_split != a.n_split) return GLANCE_ERR_INVALID_ARG;
-      const int grid = a.nseq * a.n_split * ((nqb + pl.waves - 1) / pl.waves) * a.Hkv;
-      const int fuse = pl.fuse && a.arrivals != nullptr;
-      if (pl.waves == 4)
-        tree_attn_tile_kernel<4><<<grid, 4 * kWave, 0, st>>>(a, nqb, fuse);
-      else
-        tree_attn_tile_kernel<2><<<grid, 2 * kWave, 0, st>>>(a, nqb, fuse);
-      GLANCE_LAUNCH_CHECK();
-      if (fuse) return GLANCE_OK;
-    }
+    // the plan that sized the workspace's split records
+    const AttnPlan pl = attn_plan(a.nseq, a.max_prefix, a.n_rows, a.Hq, a.Hkv);
+    if (pl.n_split != a.n_split) return GLANCE_ERR_INVALID_ARG;
+    const int grid = a.nseq * a.n_split * ((nqb + pl.waves - 1) / pl.waves) * a.Hkv;
+    const int fuse = pl.fuse && a.arrivals != nullptr;
+    if (pl.waves == 4)
+      tree_attn_tile_kernel<4><<<grid, 4 * kWave, 0, st>>>(a, nqb, fuse);
+    else
+      tree_attn_tile_kernel<2><<<grid, 2 * kWave, 0, st>>>(a, nqb, fuse);
     GLANCE_LAUNCH_CHECK();
+    if (fuse) return GLANCE_OK;
     if (a.n_split > 1) {
       if (a.Hq % 4 == 0) {
         const dim3 cg(a.nseq * a.n_rows, a.Hq / 4);
