@@ -1030,6 +1030,11 @@ __global__ __launch_bounds__(kGThreads * KW, (XF || DEPTH > 7 || KW > 1 || MT > 
       proj_store<EPI>(a, b, m0 + l, x, ein);
       return;
     }
+    // Hand-over to the group's last work-group.  Invariant: the partials are
+    // written and read only with device-scope atomic accesses (performed at
+    // the device-coherent level, never in a per-XCD cache), every store is
+    // complete (s_waitcnt 0) before this work-group's arrival increment, and
+    // the last work-group loads them only after it has seen the final count.
     const size_t grp = static_cast<size_t>(mt) * NGr + g;
     float* pp = a.kpart + ((grp * S + q) * 4 + w) * 1024;
     if (wk == 0) {
