@@ -17,29 +17,33 @@ from tests import parity
 pytestmark = pytest.mark.gpu
 
 
-def _sampled_round(inp, T, seed, rnd):
+def _sampled_round(inp, T, seed, rnd, packed=False):
     from tree_verified_block_amd.round import DeviceRound
-    dev = DeviceRound(inp, want_logits=True, temperature=T, seed=seed)
+    dev = DeviceRound(inp, want_logits=True, temperature=T, seed=seed, packed_head=packed)
     dev.round_id = rnd
     dev.set_round(0)
     dev.run()
     out = dev.fetch()
-    greedy = DeviceRound(inp, want_logits=False)
+    del dev
+    greedy = DeviceRound(inp, want_logits=False, packed_head=packed)
     greedy.set_round(0)
     greedy.run()
     return out, greedy.fetch()
 
 
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("name,seed,T,key,rnd", [
     ("tiny_widehead", 1000, 1.0, 7, 0),
     ("tiny_widehead", 1001, 0.6, (1 << 63) + 12345, (1 << 33) + 9),
     ("mini_bf16", 1, 1.0, 42, 3),
     ("mini_bf16_ragged", 3, 0.8, 0xDEADBEEFCAFEF00D, 77),
+    # the 8B shapes through the packed head, as the benchmark's sampled rounds
+    ("qwen8b_1layer", 2000, 1.0, 20261202, 5),
 ])
 def test_sampled_round_matches_oracle_draws(name, seed, T, key, rnd):
-    inp = gen_round(make_config(name), seed)
+    inp = gen_round(make_config(name, n_rounds=1) if name.startswith("qwen8b") else make_config(name), seed)
     cfg = inp["cfg"]
-    gpu, ref = _sampled_round(inp, T, key, rnd)
+    gpu, ref = _sampled_round(inp, T, key, rnd, packed=cfg.V > 100000)
     # the sampled call leaves the greedy statistics as the greedy call does
     assert np.array_equal(gpu["argmax"], ref["argmax"])
     for k in ("top1", "gap", "entropy"):
