@@ -105,6 +105,46 @@ def cpu_baseline(inp, budget_s: float = 10.0) -> dict:
             "host_cpu": _cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
+def cache_residency(dev, drafts, K: int, copies: int = 4) -> dict:
+    """The single-layer round with its layer's weights and prefix cache rotated
+    over ``copies`` device copies (4 x 88 MB, more than the 256 MB Infinity
+    Cache) against one copy: a round-time difference would mean that the one
+    copy is served from that cache between rounds."""
+    import torch
+    base = dev.layers[0]
+    sets = [base] + [{k: (v.clone() if torch.is_tensor(v) else v) for k, v in base.items()}
+                     for _ in range(copies - 1)]
+    stream = torch.cuda.current_stream()
+
+    def run(rotate: bool) -> float:
+        for i in range(K + 3):
+            if i == 3:
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            dev.layers[0] = sets[i % copies] if rotate else base
+            if drafts:
+                dev.draft = drafts[i % len(drafts)]
+            dev.step_tree()
+            dev.step_attn()
+            dev.step_verify()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / K
+
+    try:
+        one, rot = run(False), run(True)
+        one2 = run(False)
+    finally:
+        dev.layers[0] = base
+    del sets
+    torch.cuda.empty_cache()
+    return {"copies": copies, "one_copy_us": round(min(one, one2), 2), "rotated_us": round(rot, 2),
+            "note": "rounds launched call by call, K each; the layer's packed weights and prefix "
+                    "cache rotated over the copies"}
+
+
 def graph_replays(dev, drafts, K: int, warm: int = 3, dist: int = 0) -> dict:
     """Rounds replayed from HIP graphs: one graph per draft (each captures the
     whole round reading that draft's tensor; a given-topology workload has one),
@@ -590,6 +630,7 @@ def main():
 
     # the same rounds replayed from HIP graphs (one graph per draft)
     gr = graph_replays(dev, drafts, args.steps, warm=args.warmup, dist=args.dist_rounds)
+    residency = cache_residency(dev, drafts, 50) if packed and cfg.n_layers == 1 else None
 
     names = ["build_tree", "tree_attn", "verify_head", "accept_walk"]
     us = {n: float(np.mean([e[k].elapsed_time(e[k + 1]) for e in evs]) * 1e3)
@@ -628,6 +669,7 @@ def main():
                              "the untimed per-step, head and per-round passes"},
         "per_round_us": dist,
         "graph": dict(gr, note="the same rounds replayed from HIP graphs, one per draft"),
+        "cache_residency": residency,
         "round_hbm_frac": round(total_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
         "round_bytes": total_bytes,
         "per_kernel": per_kernel,
