@@ -17,8 +17,8 @@ per workload, as maxima over its rounds:
 The comparison rules take two things from this file.  An argmax is decided
 (bit-exact required) when the reference top-2 gap exceeds max(1e-3, 2 dz):
 two evaluations whose logits differ by at most dz can only disagree on a row
-whose gap is at most 2 dz.  And the float tolerances of the benchmark spec (1e-5
-fp32, 1e-2 bf16) stand as long as the recorded drift stays below them.
+whose gap is at most 2 dz.  And the parity tolerances for floating point
+(1e-5 fp32, 1e-2 bf16) stand as long as the recorded drift stays below them.
 
 Run:  python -m tests.golden.make_precision_bounds   (about 15 minutes, ~20 GB)
 """
