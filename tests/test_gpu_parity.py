@@ -94,13 +94,15 @@ def test_mini_copy_regime_accepts_planted_run():
         assert int(gpu["out_tokens"][0][rd["G"]]) == rd["break_token"]
 
 
-@pytest.mark.parametrize("prefix,seed", [(300, 21), (600, 22), (1500, 23)])
+@pytest.mark.parametrize("prefix,seed", [(300, 21), (600, 22), (1500, 23), (20000, 24)])
 def test_attention_split_paths(prefix, seed):
     """Two query blocks per KV head and longer prefixes: four-wave tile groups
     with two key splits merged inside the attention kernel (prefix 300), with
-    four splits merged by the separate merge kernel (600), and with more than
-    eight (1500); every output against the oracle, and a second and third
-    launch give the same bits (the merge's arrival counters return to zero)."""
+    four splits merged by the separate merge kernel (600), with more than
+    eight (1500), and at the cap of sixteen splits of about forty 32-key
+    blocks each (20000); every output against the oracle, and a second and
+    third launch give the same bits (the merge's arrival counters return to
+    zero)."""
     from tree_verified_block_amd.round import DeviceRound
     inp = gen_round(make_config("mini_bf16_copy", prefix=("fixed", prefix), n_rounds=1), seed)
     first, _ = _round_parity(inp, 0)
