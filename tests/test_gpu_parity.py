@@ -71,6 +71,17 @@ def test_eight_query_heads_per_kv_head():
     _round_parity(gen_round(cfg, 33), 0)
 
 
+@pytest.mark.parametrize("Hq,Hkv,seed", [(2, 2, 41), (6, 2, 42)])
+def test_query_heads_not_a_multiple_of_four(Hq, Hkv, seed):
+    """One query head per KV head (plain multi-head attention) and three per KV
+    head: query counts that leave the last query block partly empty, and split
+    records merged by the one-dimension-per-thread merge kernel (the 16-byte
+    merge needs a multiple of four query heads); a 600-token prefix gives
+    several splits."""
+    cfg = make_config("mini_bf16_copy", Hq=Hq, Hkv=Hkv, prefix=("fixed", 600), n_rounds=1)
+    _round_parity(gen_round(cfg, seed), 0)
+
+
 @pytest.mark.parametrize("nseq,seed", [(4, 31), (7, 32)])
 def test_projection_row_tiles(nseq, seed):
     """More rows than one 64-row tile: the projections take several tiles per
